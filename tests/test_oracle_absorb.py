@@ -1,0 +1,146 @@
+"""Pins for the oracle's Gram statistics, ridge absorb, reconstruction error and selection (CPU only).
+
+The ridge pins reach the minimiser of the page's objective by other routes:
+scikit-learn's Ridge (sum-of-squares objective, no intercept), numpy's
+least-squares (SVD) on the stacked system [A_loc; sqrt(lambda) I] X =
+[(A_full - A_loc) W; 0], the exact-linear-relation limit, the lambda -> inf
+limit, and the convexity of the objective (any perturbation raises it).
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from kv_cache_absorption_ispa_amd import inputs
+
+
+def _rows(seed, n, d, noise=0.3):
+    g = np.random.default_rng(seed)
+    a_loc = g.standard_normal((n, d)) * (0.2 * 10 ** (-g.random(d)))
+    a_full = a_loc * (1 + 0.1 * g.standard_normal(d)) + noise * 0.05 * g.standard_normal((n, d))
+    return a_loc, a_full
+
+
+def test_gram_symmetric_psd_and_chunk_additive():
+    a_loc, a_full = _rows(1, 400, 24)
+    G, C = oracle.gram(a_loc, a_full)
+    assert np.array_equal(G, G.T) or np.max(np.abs(G - G.T)) <= 1e-13 * np.abs(G).max()
+    assert np.linalg.eigvalsh(G).min() > 0
+    chunks = [(a_loc[i:i + 100], a_full[i:i + 100]) for i in range(0, 400, 100)]
+    G4, C4 = oracle.gram_from_chunks(chunks)
+    assert np.max(np.abs(G4 - G)) <= 1e-13 * np.abs(G).max()
+    assert np.max(np.abs(C4 - C)) <= 1e-13 * np.abs(C).max()
+
+
+def test_gram_brute_force_entries():
+    a_loc, a_full = _rows(2, 30, 5)
+    G, C = oracle.gram(a_loc, a_full)
+    for i in range(5):
+        for j in range(5):
+            g = math.fsum(a_loc[r, i] * a_loc[r, j] for r in range(30))
+            c = math.fsum(a_loc[r, i] * (a_full[r, j] - a_loc[r, j]) for r in range(30))
+            assert abs(G[i, j] - g) <= 1e-13
+            assert abs(C[i, j] - c) <= 1e-13
+
+
+def test_zero_update_when_streams_agree():
+    a_loc, _ = _rows(3, 200, 16)
+    W = np.random.default_rng(4).standard_normal((16, 16)) / 4
+    G, C = oracle.gram(a_loc, a_loc)
+    dW = oracle.ridge_solve(G, C, W, 1e-2)
+    assert np.all(dW == 0.0)
+
+
+@pytest.mark.parametrize("lam", [1e-2, 1.0, 30.0])
+def test_ridge_matches_sklearn(lam):
+    """scikit-learn's Ridge minimises ||Y - X B||^2 + alpha ||B||^2 (sums, no intercept)."""
+    from sklearn.linear_model import Ridge
+
+    a_loc, a_full = _rows(5, 300, 20)
+    W = np.random.default_rng(6).standard_normal((20, 12)) / math.sqrt(20)
+    G, C = oracle.gram(a_loc, a_full)
+    dW = oracle.ridge_solve(G, C, W, lam)
+    y = (a_full - a_loc) @ W
+    ref = Ridge(alpha=lam, fit_intercept=False, solver="svd").fit(a_loc, y).coef_.T
+    assert np.linalg.norm(dW - ref) / np.linalg.norm(ref) <= 1e-10
+
+
+def test_ridge_matches_stacked_lstsq():
+    a_loc, a_full = _rows(7, 500, 32)
+    lam = 1e-2
+    W = np.random.default_rng(8).standard_normal((32, 32)) / math.sqrt(32)
+    G, C = oracle.gram(a_loc, a_full)
+    dW = oracle.ridge_solve(G, C, W, lam)
+    X = np.vstack([a_loc, math.sqrt(lam) * np.eye(32)])
+    Y = np.vstack([(a_full - a_loc) @ W, np.zeros((32, 32))])
+    ref = np.linalg.lstsq(X, Y, rcond=None)[0]
+    assert np.linalg.norm(dW - ref) / np.linalg.norm(ref) <= 1e-10
+
+
+def test_exact_linear_relation_recovered_as_lambda_vanishes():
+    """A_full = A_loc M  =>  dW -> (M - I) W as lambda -> 0 (A_loc full column rank)."""
+    g = np.random.default_rng(9)
+    a_loc = g.standard_normal((200, 10))
+    M = np.eye(10) + 0.2 * g.standard_normal((10, 10))
+    W = g.standard_normal((10, 7))
+    G, C = oracle.gram(a_loc, a_loc @ M)
+    target = (M - np.eye(10)) @ W
+    errs = [np.linalg.norm(oracle.ridge_solve(G, C, W, lam) - target) for lam in (1.0, 1e-3, 1e-7)]
+    assert errs[0] > errs[1] > errs[2]
+    assert errs[2] / np.linalg.norm(target) <= 1e-8
+
+
+def test_large_lambda_limit():
+    """lambda -> inf  =>  lambda dW -> C W."""
+    a_loc, a_full = _rows(10, 100, 8)
+    W = np.random.default_rng(11).standard_normal((8, 8))
+    G, C = oracle.gram(a_loc, a_full)
+    lam = 1e9
+    r = lam * oracle.ridge_solve(G, C, W, lam)
+    assert np.linalg.norm(r - C @ W) / np.linalg.norm(C @ W) <= 1e-7
+
+
+def test_solution_minimises_objective():
+    a_loc, a_full = _rows(12, 150, 12)
+    W = np.random.default_rng(13).standard_normal((12, 6))
+    lam = 0.05
+    G, C = oracle.gram(a_loc, a_full)
+    dW = oracle.ridge_solve(G, C, W, lam)
+    f0 = oracle.objective(a_loc, a_full, W, dW, lam)
+    g = np.random.default_rng(14)
+    for _ in range(20):
+        P = 1e-3 * g.standard_normal(dW.shape)
+        assert oracle.objective(a_loc, a_full, W, dW + P, lam) > f0
+    # and it beats doing nothing (dW = 0) whenever the streams differ
+    assert f0 < oracle.objective(a_loc, a_full, W, np.zeros_like(dW), lam)
+
+
+def test_reconstruction_error_closed_form():
+    """eps from the rows equals the Gram-statistics form
+    <Q_ff - C - C^T - G, W W^T> - <dW, C W> - lambda ||dW||^2 (with Q_ff = A_full^T A_full)."""
+    a_loc, a_full = _rows(15, 400, 16)
+    W = np.random.default_rng(16).standard_normal((16, 16)) / 4
+    lam = 1e-2
+    G, C = oracle.gram(a_loc, a_full)
+    dW = oracle.ridge_solve(G, C, W, lam)
+    eps, eps_rel = oracle.reconstruction_error(a_loc, a_full, W, dW)
+    Qff = a_full.T @ a_full
+    cf = np.sum((Qff - C - C.T - G) * (W @ W.T)) - np.sum(dW * (C @ W)) - lam * np.sum(dW * dW)
+    assert abs(eps - cf) <= 1e-11 * abs(eps)
+    assert abs(eps_rel - eps / np.sum((a_full @ W) ** 2)) <= 1e-15
+    # the post-fit error is below the pre-fit discrepancy ||(A_full - A_loc) W||^2
+    assert eps < np.sum(((a_full - a_loc) @ W) ** 2)
+
+
+def test_selection_order_and_ties():
+    assert oracle.select_layers([0.5, 0.1, 0.3, 0.1, 0.9], 3) == [1, 3, 2]
+    assert oracle.select_layers([1.0, 1.0, 1.0], 2) == [0, 1]
+
+
+def test_standin_rows_conditioning():
+    """The stand-in rows give G + lambda I conditioned like measured attention rows (1e4..1e6)."""
+    a_loc, a_full = inputs.absorb_rows(1, 0, 4000, 256, "bf16")
+    G, _ = oracle.gram(a_loc.f64, a_full.f64)
+    ev = np.linalg.eigvalsh(G + 1e-2 * np.eye(256))
+    assert 1e3 < ev[-1] / ev[0] < 1e7
