@@ -1,0 +1,272 @@
+"""Benchmark of the ISPA hot path on one MI355X.
+
+One step = the whole warmup-and-absorb path of one Wan-1.3B-shaped attention
+layer: for each of the 4 warmup chunks, ispa_decomp_attn (local branch,
+history branch, fused LSE merge) then ispa_gram_accum on (A_loc, A_full);
+then ispa_absorb_solve (dW for the layer).  Inputs are seeded synthetic data
+already resident in HBM when timing starts.
+
+Prints ONE JSON line.  `value` is decomposable-attention TFLOP/s over the
+whole step (attention matmul FLOPs of the 4 chunks / step time); the per-kernel
+numbers, the absorb ms/layer, the roofline of the dominant kernel and the
+oracle's CPU rate are reported beside it.
+
+    python bench.py [--steps K] [--warmup W] [--config 1] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decomposable-attn TFLOP/s (% bf16 MFMA peak) + absorb ms/layer, 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", type=int, default=1, help="layer shape (1: Wan-1.3B, 2: long history, 3: Wan-14B)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU seconds for the oracle sample")
+    ap.add_argument("--traffic", type=str, default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="measured HBM traffic of the attention kernel (from rocprofv3 counters), if present")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only: the hot path is one layer on one device; "
+                                   "see the design notes for how it would shard"}), flush=True)
+        sys.exit(2)
+
+    import torch
+
+    from kv_cache_absorption_ispa_amd import inputs, ispa
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    ispa.load_library()
+    ispa.ispa_device_check(0)
+    cfg = inputs.CONFIGS[args.config]
+    H, D, d = cfg.heads, cfg.head_dim, cfg.d
+
+    def dev(t):
+        return torch.from_numpy(t.raw.view(np.int16)).view(torch.bfloat16).cuda()
+
+    # ---- inputs resident in HBM: 4 warmup chunks (different Q / chunk K,V / history K,V each)
+    log(f"[bench] generating inputs for {cfg.name}")
+    chunks = []
+    for c in range(cfg.n_chunks):
+        x = inputs.chunk_inputs(cfg, 0, c)
+        chunks.append(dict(q=dev(x.q), kl=dev(x.k_loc), vl=dev(x.v_loc), kh=dev(x.k_hist), vh=dev(x.v_hist)))
+    W = torch.from_numpy(inputs.weight(cfg, 0)).cuda()
+    nq = cfg.n_q
+    o_loc = torch.empty(nq, H, D, dtype=torch.bfloat16, device="cuda")
+    o_hist = torch.empty_like(o_loc)
+    o_full = torch.empty_like(o_loc)
+    lse = [torch.empty(H, nq, device="cuda") for _ in range(3)]
+    G = torch.empty(d, d, device="cuda")
+    C = torch.empty(d, d, device="cuda")
+    dW = torch.empty(d, d, device="cuda")
+    info = torch.empty(1, dtype=torch.int32, device="cuda")
+    gws = ispa.workspace(ispa.ispa_gram_workspace_size(nq, d, torch.bfloat16))
+    atws = ispa.workspace(ispa.ispa_decomp_attn_workspace_size(chunks[0]["q"], cfg.n_loc, cfg.n_hist))
+    aws = ispa.workspace(ispa.ispa_absorb_workspace_size(d, d, 1))
+    torch.cuda.synchronize()
+
+    n_ev = 2 * cfg.n_chunks + 1
+
+    def step(events=None):
+        for c, ch in enumerate(chunks):
+            if events is not None:
+                events[2 * c][0].record()
+            ispa.ispa_decomp_attn(ch["q"], ch["kl"], ch["vl"], ch["kh"], ch["vh"], o_loc=o_loc, lse_loc=lse[0],
+                                  o_hist=o_hist, lse_hist=lse[1], o_full=o_full, lse_full=lse[2], workspace=atws)
+            if events is not None:
+                events[2 * c][1].record()
+                events[2 * c + 1][0].record()
+            ispa.ispa_gram_accum(o_loc, o_full, G, C, accumulate=c > 0, workspace=gws)
+            if events is not None:
+                events[2 * c + 1][1].record()
+        if events is not None:
+            events[-1][0].record()
+        ispa.ispa_absorb_solve(G, C, W, cfg.lam, dW, info, workspace=aws)
+        if events is not None:
+            events[-1][1].record()
+
+    log(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if info.item() != 0:
+        raise RuntimeError(f"absorb failed, info = {info.item()}")
+
+    # ---- timed region: exactly K steps, whole-job wall clock
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    # ---- per-kernel durations with events on the launch stream (separate pass, same work)
+    attn_ms, gram_ms, solve_ms = [], [], []
+    for _ in range(args.steps):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
+        step(ev)
+        torch.cuda.synchronize()
+        for c in range(cfg.n_chunks):
+            attn_ms.append(ev[2 * c][0].elapsed_time(ev[2 * c][1]))
+            gram_ms.append(ev[2 * c + 1][0].elapsed_time(ev[2 * c + 1][1]))
+        solve_ms.append(ev[-1][0].elapsed_time(ev[-1][1]))
+
+    # ---- single-pass attention over the concatenated keys (the comparison pass)
+    ch = chunks[0]
+    kcat = torch.cat([ch["kl"], ch["kh"]])
+    vcat = torch.cat([ch["vl"], ch["vh"]])
+    o_single = torch.empty_like(o_loc)
+    lse_single = torch.empty(H, nq, device="cuda")
+    for _ in range(2):
+        ispa.ispa_full_attn(ch["q"], kcat, vcat, o=o_single, lse=lse_single)
+    full_ms = []
+    for _ in range(max(args.steps, 3)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        ispa.ispa_full_attn(ch["q"], kcat, vcat, o=o_single, lse=lse_single)
+        e1.record()
+        torch.cuda.synchronize()
+        full_ms.append(e0.elapsed_time(e1))
+    del kcat, vcat
+
+    attn_flops = cfg.attn_flops()
+    step_attn_flops = attn_flops * cfg.n_chunks
+    attn_avg = float(np.mean(attn_ms))
+    achieved = attn_flops / (attn_avg * 1e-3) / 1e12
+    value = step_attn_flops / (ms_per_step * 1e-3) / 1e12
+
+    traffic = None
+    if os.path.exists(args.traffic):
+        try:
+            with open(args.traffic) as f:
+                t = json.load(f)
+            if t.get("kernel_source_sha") == kernel_source_sha():
+                traffic = t.get("bytes_per_launch")
+        except Exception:
+            traffic = None
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q/K/V, 8 sink keys at 4x norm; random-init W)",
+        "config": {
+            "workload": f"{cfg.name}: {H} heads x {D}, {nq} queries/chunk, {cfg.n_sink} sink + {cfg.n_chunk} chunk "
+                        f"local keys, {cfg.n_hist} history keys, {cfg.n_chunks} warmup chunks, absorb d={d}",
+            "global_batch": cfg.n_chunks * nq,
+            "seq_len": cfg.n_loc + cfg.n_hist,
+            "parallelism": "single GPU",
+        },
+        "attn_tflops_kernel": round(achieved, 2),
+        "attn_pct_bf16_peak": round(100 * achieved / PEAK_BF16_TFLOPS, 2),
+        "attn_ms_per_chunk": round(attn_avg, 4),
+        "single_pass_ms": round(float(np.median(full_ms)), 4),
+        "ratio_decomp_vs_single_pass": round(attn_avg / float(np.median(full_ms)), 4),
+        "gram_ms_per_chunk": round(float(np.mean(gram_ms)), 4),
+        "absorb_ms_per_layer": round(float(np.mean(solve_ms)), 4),
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "attn_bf16_kernel (ispa_decomp_attn)",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "algorithmic_flops_per_launch": attn_flops,
+        },
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def kernel_source_sha() -> str:
+    import hashlib
+
+    p = os.path.join(ROOT, "kv_cache_absorption_ispa_amd", "csrc", "attn_kernels.hip")
+    with open(p, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def cpu_baseline(cfg, target_s: float):
+    """The oracle (float64 numpy, as it stands) on a bounded sample of the same workload:
+    decomposable attention of a subset of one chunk's queries over all local and history keys."""
+    import oracle
+    from kv_cache_absorption_ispa_amd import inputs
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    x = inputs.chunk_inputs(cfg, 0, 0)
+    q, kl, vl, kh, vh = x.q.f64, x.k_loc.f64, x.v_loc.f64, x.k_hist.f64, x.v_hist.f64
+    def decomposed(qs):
+        o_l, l_l = oracle.attention(qs, kl, vl, cfg.scale)
+        o_h, l_h = oracle.attention(qs, kh, vh, cfg.scale)
+        return oracle.merge(o_l, l_l, o_h, l_h)
+
+    n = 32
+    t = 0.0
+    while True:  # grow the sample until one run takes a measurable time
+        t0 = time.perf_counter()
+        decomposed(q[:n])
+        t = time.perf_counter() - t0
+        if t > 0.5 or n >= cfg.n_q:
+            break
+        n = min(cfg.n_q, n * 4)
+    n_final = int(min(cfg.n_q, max(n, n * target_s / max(t, 1e-3))))
+    t0 = time.perf_counter()
+    decomposed(q[:n_final])
+    t = time.perf_counter() - t0
+    flops = 4.0 * n_final * (cfg.n_loc + cfg.n_hist) * cfg.head_dim * cfg.heads
+    return {
+        "value": round(flops / t / 1e12, 5),
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{n_final} of {cfg.n_q} queries of one chunk, all {cfg.heads} heads, "
+                  f"{cfg.n_loc}+{cfg.n_hist} keys; {t:.1f} s",
+    }
+
+
+if __name__ == "__main__":
+    main()

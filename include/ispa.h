@@ -1,0 +1,218 @@
+/*
+ * ispa.h — C ABI of the ISPA hot path on AMD MI355X (gfx950).
+ *
+ * Instance-Specific Parametric Absorption converts some full-attention layers
+ * of an autoregressive video model to local attention after a short warmup,
+ * absorbing the lost history into the attention output projection.  This
+ * library implements the warmup's dual-stream attention and the closed-form
+ * absorb that follows it:
+ *
+ *   ispa_decomp_attn   local and historical attention branches plus their
+ *                      log-sum-exp merge (A_loc and A_full rows),
+ *   ispa_gram_accum    G = A_loc^T A_loc and C = A_loc^T (A_full - A_loc),
+ *   ispa_absorb_solve  dW = (G + lambda I)^-1 C W  (Cholesky + triangular solves),
+ *   ispa_layer_eps     the post-fit reconstruction error used to rank layers,
+ *   ispa_full_attn     one softmax pass over all keys (the comparison pass),
+ *   ispa_lse_merge     standalone N-way merge of (O, LSE) partial results.
+ *
+ * Sources: "Technical Summary: Instance-Specific Parametric Absorption (ISPA)
+ * for Memory-Efficient Video Generation" (gist.science), section 2
+ * "Methodology" (Dual-Stream Warmup, Layer Absorb, Memory-Efficient Inference,
+ * Dynamic Layer Selection) and section 3 "Key Contributions" (online softmax);
+ * "Towards Memory-Efficient Autoregressive Video Generation via
+ * Instance-Specific Parametric Absorption" (mlsanity.com), "Abstract (arXiv)".
+ *
+ * Conventions for every call
+ * --------------------------
+ * - Every buffer is DEVICE memory owned by the caller.  The library never
+ *   allocates or frees in these calls; scratch space is a caller-provided
+ *   workspace whose size is queried first.
+ * - Calls only enqueue work on `stream` (a hipStream_t; NULL = default
+ *   stream) and return; results are valid once the stream is synchronised.
+ * - Inputs must not alias outputs (the one exception is W_new == W).
+ * - Layouts: Q, K, V and O are [tokens, heads, head_dim] contiguous, so an O
+ *   buffer is also the row-major [tokens, d] matrix A with d = heads*head_dim
+ *   and column h*head_dim + e.  LSE is [heads, tokens] float32, natural log,
+ *   scale included.  G, C, Q_ff, W, dW, W_new are row-major float32.
+ * - bf16 tensors are passed as 16-bit patterns (uint16 storage).
+ * - Return value: ISPA_OK, or an error status with detail in
+ *   ispa_last_error() (thread-local).  Nothing throws, aborts or exits.
+ *   Validation errors are returned before anything is enqueued.
+ * - Non-finite inputs propagate (a NaN in a Q row makes that row's outputs
+ *   NaN); they are not checked.
+ */
+#ifndef ISPA_H
+#define ISPA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ISPA_OK = 0,
+  ISPA_E_INVALID_ARG = 1, /* null required pointer, bad size, misaligned pointer, unsupported shape */
+  ISPA_E_UNSUPPORTED = 2, /* the current device is not gfx950 */
+  ISPA_E_WORKSPACE = 3,   /* workspace missing or smaller than the queried size */
+  ISPA_E_HIP = 4          /* a HIP runtime / launch error */
+} ispa_status_t;
+
+typedef enum { ISPA_F32 = 0, ISPA_BF16 = 1 } ispa_dtype_t;
+
+/* Shape of one attention call. */
+typedef struct {
+  int32_t heads;    /* H >= 1 */
+  int32_t head_dim; /* D in {64, 128} */
+  int64_t n_q;      /* queries, >= 0 */
+  int64_t n_loc;    /* local keys (sink rows then current-chunk rows), >= 1 */
+  int64_t n_hist;   /* history keys, >= 0; 0 = local-attention (L-layer) mode */
+  float scale;      /* softmax scale, usually 1/sqrt(head_dim); > 0 */
+  int32_t dtype;    /* ispa_dtype_t of Q, K, V and O */
+} ispa_attn_desc_t;
+
+/*
+ * ispa_decomp_attn — decomposable attention of one chunk (one launch).
+ *
+ * Source: ISPA technical summary, section 2 "Methodology", step 1
+ * "Dual-Stream Warmup": the local stream attends to the current chunk plus the
+ * sink tokens, the full stream to the entire context; the decomposable form
+ * runs a local and a historical branch, each an online-softmax pass that keeps
+ * its log-sum-exp state, and fuses them afterwards.  Reading used: scores are
+ * scale*<q,k> with no mask; the merge is LSE = logaddexp(LSE_loc, LSE_hist),
+ * O_full = e^(LSE_loc-LSE) O_loc + e^(LSE_hist-LSE) O_hist, and is computed in
+ * the history branch's epilogue from the float32 branch outputs (O_loc is
+ * parked in the workspace between the branches), so O_full is rounded once.
+ *
+ *   Q       [n_q,  H, D]      K_loc, V_loc [n_loc, H, D]   K_hist, V_hist [n_hist, H, D]
+ *   O_loc, O_hist, O_full [n_q, H, D] (dtype)   LSE_* [H, n_q] float32
+ *
+ * Every output pointer may be NULL (that output is not written).  With
+ * n_hist == 0, K_hist/V_hist are ignored, LSE_hist = -inf, O_hist = 0, and
+ * O_full is bitwise equal to O_loc.  Pointers must be 16-byte aligned.
+ * `workspace` (device, >= ispa_decomp_attn_workspace_size bytes) is required
+ * when O_full is requested with n_hist > 0 in bf16, else may be NULL;
+ * ISPA_E_WORKSPACE otherwise.
+ * dtype BF16 computes QK^T and PV on bf16 matrix cores with float32
+ * accumulation and float32 softmax state; F32 computes everything in float32.
+ */
+ispa_status_t ispa_decomp_attn(const ispa_attn_desc_t* desc, const void* Q, const void* K_loc,
+                               const void* V_loc, const void* K_hist, const void* V_hist, void* O_loc,
+                               float* LSE_loc, void* O_hist, float* LSE_hist, void* O_full,
+                               float* LSE_full, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes ispa_decomp_attn needs for this shape: n_q*H*D*4 for bf16
+ * with history keys (the float32 O_loc the merge reads), else 0.  Needed only
+ * when O_full is requested. */
+size_t ispa_decomp_attn_workspace_size(const ispa_attn_desc_t* desc);
+
+/*
+ * ispa_full_attn — one online-softmax pass over n_loc + n_hist keys given as a
+ * single concatenated K, V ([n_loc + n_hist, H, D]).  This is the
+ * single-stream attention the decomposable pass is compared against (same
+ * kernel family, one phase).  O / LSE may be NULL.
+ */
+ispa_status_t ispa_full_attn(const ispa_attn_desc_t* desc, const void* Q, const void* K, const void* V,
+                             void* O, float* LSE, void* stream);
+
+/*
+ * ispa_lse_merge — merge n_parts partial attention results over disjoint key
+ * sets into the result over their union: LSE = log sum_p exp(LSE_p),
+ * O = sum_p exp(LSE_p - LSE) O_p.  Source: ISPA technical summary, section 2,
+ * step 1 (branches fused after the fact from their LSE states).
+ * O_parts / LSE_parts are HOST arrays of n_parts DEVICE pointers
+ * (O_p [n_q,H,D] dtype, LSE_p [H,n_q] float32).  1 <= n_parts <= 16.
+ * A part with LSE = -inf contributes nothing.  LSE_out may be NULL.
+ */
+ispa_status_t ispa_lse_merge(int32_t n_parts, const void* const* O_parts, const float* const* LSE_parts,
+                             int64_t n_q, int32_t heads, int32_t head_dim, int32_t dtype, void* O_out,
+                             float* LSE_out, void* stream);
+
+/* Workspace bytes ispa_gram_accum needs for these sizes (0 is possible). */
+size_t ispa_gram_workspace_size(int64_t n_rows, int32_t d, int32_t dtype);
+
+/*
+ * ispa_gram_accum — stream warmup rows into the absorb's sufficient statistics.
+ *
+ * Source: ISPA technical summary, section 2, step 2 "Layer Absorb": the
+ * closed form needs only A_loc^T A_loc and A_loc^T (A_full - A_loc) over the
+ * warmup rows.  Computed as G += A_loc^T A_loc, C += A_loc^T A_full -
+ * A_loc^T A_loc from the exact stored operands (mathematically identical to
+ * the page's form; it avoids rounding A_full - A_loc to bf16).
+ *
+ *   A_loc, A_full [n_rows, d] (dtype), row-major (an O buffer of
+ *   ispa_decomp_attn is such a matrix).  G, C, Q_ff [d, d] float32.
+ *   accumulate = 0 overwrites G, C (and Q_ff); 1 adds to them.
+ *   Q_ff may be NULL; if given, Q_ff (+)= A_full^T A_full (for ispa_layer_eps).
+ *   G and Q_ff are written in full (both triangles).  d must be a multiple of
+ *   128 (bf16) or 64 (float32); n_rows >= 0 (0 rows with accumulate = 0 writes zeros).  The result is
+ *   deterministic: no atomics, fixed reduction order.
+ */
+ispa_status_t ispa_gram_accum(int64_t n_rows, int32_t d, int32_t dtype, const void* A_loc,
+                              const void* A_full, float* G, float* C, float* Q_ff, int32_t accumulate,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes ispa_absorb_solve needs for these sizes. */
+size_t ispa_absorb_workspace_size(int32_t d, int32_t d_out, int32_t batch);
+
+/*
+ * ispa_absorb_solve — closed-form absorb for `batch` layers.
+ *
+ * Source: ISPA technical summary, section 2, step 2 "Layer Absorb" (ridge
+ * objective and its closed-form minimiser, non-iterative) and step 3
+ * "Memory-Efficient Inference" (W_new = W + dW).  Computes, per batch entry,
+ * M = G + lambda I, M = L L^T (blocked Cholesky, float32), R = C W,
+ * L Y = R, L^T dW = Y.
+ *
+ *   G, C [batch, d, d]; W [batch, d, d_out]; dW [batch, d, d_out]; all float32.
+ *   W_new [batch, d, d_out] may be NULL or equal to W (in-place absorb).
+ *   info [batch] int32 DEVICE: 0 = success; k > 0 = the leading minor of
+ *   order k of G + lambda I is not positive definite (LAPACK potrf
+ *   convention); then dW[b] is all NaN and W_new[b] is left untouched.
+ *   G and C are read only (the factor lives in the workspace).
+ *   d and d_out must be multiples of 64; lambda >= 0; batch >= 1.
+ */
+ispa_status_t ispa_absorb_solve(int32_t d, int32_t d_out, int32_t batch, const float* G, const float* C,
+                                const float* W, float lambda, float* dW, float* W_new, int32_t* info,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes ispa_layer_eps needs. */
+size_t ispa_eps_workspace_size(int32_t d, int32_t d_out, int32_t batch);
+
+/*
+ * ispa_layer_eps — reconstruction error of each absorbed layer, for ranking.
+ *
+ * Source: ISPA technical summary, section 2 "Dynamic Layer Selection" (layers
+ * ranked by reconstruction error after warmup, lowest converted).  Reading:
+ * eps = ||A_loc (W + dW) - A_full W||_F^2 over the warmup rows (the lambda
+ * term excluded), evaluated from the Gram statistics with D = A_full - A_loc:
+ *   eps = <Q_ff - C - C^T - G, W W^T> - <dW, C W> - lambda ||dW||^2
+ *       = <Q_ff W, W> - 2 <C W, W> - <G W, W> - <dW, C W> - lambda ||dW||^2,
+ * eps_rel = eps / <Q_ff W, W>  (= eps / ||A_full W||_F^2).
+ * Products in float32, the inner products reduced in float64.
+ *   G, C, Q_ff [batch, d, d]; W, dW [batch, d, d_out]; eps_abs, eps_rel
+ *   [batch] float64 DEVICE.
+ */
+ispa_status_t ispa_layer_eps(int32_t d, int32_t d_out, int32_t batch, const float* G, const float* C,
+                             const float* Q_ff, const float* W, const float* dW, float lambda,
+                             double* eps_abs, double* eps_rel, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* ispa_status_string(ispa_status_t status);
+
+/* Detail of the last error on the calling thread ("" if none). */
+const char* ispa_last_error(void);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int32_t ispa_version(void);
+
+/* ISPA_OK if `device` is a gfx950 GPU, else ISPA_E_UNSUPPORTED (or ISPA_E_HIP). */
+ispa_status_t ispa_device_check(int32_t device);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ISPA_H */

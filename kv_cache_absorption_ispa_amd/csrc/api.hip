@@ -1,0 +1,256 @@
+// C ABI of the ISPA library: argument validation, device check, error state.
+// The declarations and their documentation are in include/ispa.h.
+#include <mutex>
+#include <string>
+
+#include "ispa_internal.h"
+
+namespace ispa {
+
+static thread_local std::string g_last_error;
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+
+ispa_status_t hip_check(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ISPA_OK;
+  g_last_error = std::string(what) + ": " + hipGetErrorString(e);
+  return ISPA_E_HIP;
+}
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_dev_once[kMaxDevices];
+int g_dev_ok[kMaxDevices];  // 1 = gfx950, 0 = other, -1 = query failed
+
+ispa_status_t check_device(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) {
+    set_error("device index out of range");
+    return ISPA_E_UNSUPPORTED;
+  }
+  std::call_once(g_dev_once[dev], [dev]() {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      g_dev_ok[dev] = -1;
+      return;
+    }
+    g_dev_ok[dev] = std::string(prop.gcnArchName).rfind("gfx950", 0) == 0 ? 1 : 0;
+  });
+  if (g_dev_ok[dev] == 1) return ISPA_OK;
+  if (g_dev_ok[dev] == -1) {
+    set_error("hipGetDeviceProperties failed");
+    return ISPA_E_HIP;
+  }
+  set_error("device is not gfx950 (MI355X)");
+  return ISPA_E_UNSUPPORTED;
+}
+
+ispa_status_t check_current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    set_error("hipGetDevice failed");
+    return ISPA_E_HIP;
+  }
+  return check_device(dev);
+}
+
+ispa_status_t invalid(const std::string& msg) {
+  set_error(msg);
+  return ISPA_E_INVALID_ARG;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Required pointer: non-null and 16-byte aligned.  Optional: null or aligned.
+bool req(const void* p) { return p != nullptr && aligned16(p); }
+bool opt(const void* p) { return p == nullptr || aligned16(p); }
+
+ispa_status_t check_attn_desc(const ispa_attn_desc_t* d, bool allow_hist) {
+  if (d == nullptr) return invalid("desc is NULL");
+  if (d->heads < 1) return invalid("heads must be >= 1");
+  if (d->head_dim != 64 && d->head_dim != 128) return invalid("head_dim must be 64 or 128");
+  if (d->n_q < 0 || d->n_loc < 1 || d->n_hist < 0) return invalid("need n_q >= 0, n_loc >= 1, n_hist >= 0");
+  if (!allow_hist && d->n_hist != 0) return invalid("n_hist must be 0 here");
+  if (!(d->scale > 0.f) || d->scale == INFINITY) return invalid("scale must be finite and > 0");
+  if (d->dtype != ISPA_F32 && d->dtype != ISPA_BF16) return invalid("dtype must be ISPA_F32 or ISPA_BF16");
+  const int64_t hd = (int64_t)d->heads * d->head_dim;
+  const int64_t lim = (int64_t)1 << 31;
+  if (d->n_q * hd >= lim || (d->n_loc + d->n_hist) * hd >= lim || (int64_t)d->heads * d->n_q >= lim)
+    return invalid("tensor too large (2^31 elements per tensor)");
+  return ISPA_OK;
+}
+
+}  // namespace
+}  // namespace ispa
+
+using namespace ispa;
+
+extern "C" {
+
+size_t ispa_decomp_attn_workspace_size(const ispa_attn_desc_t* desc) {
+  if (desc == nullptr || desc->n_q < 0 || desc->heads < 1 || desc->n_hist < 0) return 0;
+  return attention_workspace_size(desc->n_q, desc->heads, desc->head_dim, desc->n_hist, desc->dtype);
+}
+
+ispa_status_t ispa_decomp_attn(const ispa_attn_desc_t* desc, const void* Q, const void* K_loc, const void* V_loc,
+                               const void* K_hist, const void* V_hist, void* O_loc, float* LSE_loc, void* O_hist,
+                               float* LSE_hist, void* O_full, float* LSE_full, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  ispa_status_t st = check_attn_desc(desc, true);
+  if (st != ISPA_OK) return st;
+  if ((desc->n_q > 0 && !req(Q)) || !req(K_loc) || !req(V_loc))
+    return invalid("Q, K_loc, V_loc must be non-NULL and 16-byte aligned");
+  if (desc->n_hist > 0 && (!req(K_hist) || !req(V_hist)))
+    return invalid("K_hist, V_hist must be non-NULL and 16-byte aligned when n_hist > 0");
+  if (!opt(O_loc) || !opt(LSE_loc) || !opt(O_hist) || !opt(LSE_hist) || !opt(O_full) || !opt(LSE_full) ||
+      !opt(workspace))
+    return invalid("output and workspace pointers must be 16-byte aligned");
+  const size_t ws_need = ispa_decomp_attn_workspace_size(desc);
+  if (O_full != nullptr && ws_need > 0 && (workspace == nullptr || workspace_bytes < ws_need)) {
+    set_error("ispa_decomp_attn: workspace smaller than ispa_decomp_attn_workspace_size()");
+    return ISPA_E_WORKSPACE;
+  }
+  st = check_current_device();
+  if (st != ISPA_OK) return st;
+  AttnArgs a;
+  a.Q = Q;
+  a.Kl = K_loc;
+  a.Vl = V_loc;
+  a.Kh = desc->n_hist > 0 ? K_hist : nullptr;
+  a.Vh = desc->n_hist > 0 ? V_hist : nullptr;
+  a.O_loc = O_loc;
+  a.LSE_loc = LSE_loc;
+  a.O_hist = O_hist;
+  a.LSE_hist = LSE_hist;
+  a.O_full = O_full;
+  a.LSE_full = LSE_full;
+  a.n_q = desc->n_q;
+  a.n_loc = desc->n_loc;
+  a.n_hist = desc->n_hist;
+  a.heads = desc->heads;
+  a.head_dim = desc->head_dim;
+  a.scale = desc->scale;
+  a.dtype = desc->dtype;
+  a.ws = workspace;
+  a.ws_bytes = workspace_bytes;
+  return launch_attention(a, (hipStream_t)stream);
+}
+
+ispa_status_t ispa_full_attn(const ispa_attn_desc_t* desc, const void* Q, const void* K, const void* V, void* O,
+                             float* LSE, void* stream) {
+  ispa_status_t st = check_attn_desc(desc, true);
+  if (st != ISPA_OK) return st;
+  if ((desc->n_q > 0 && !req(Q)) || !req(K) || !req(V)) return invalid("Q, K, V must be non-NULL and 16-byte aligned");
+  if (!opt(O) || !opt(LSE)) return invalid("output pointers must be 16-byte aligned");
+  st = check_current_device();
+  if (st != ISPA_OK) return st;
+  AttnArgs a = {};
+  a.Q = Q;
+  a.Kl = K;
+  a.Vl = V;
+  a.O_loc = O;
+  a.LSE_loc = LSE;
+  a.n_q = desc->n_q;
+  a.n_loc = desc->n_loc + desc->n_hist;
+  a.n_hist = 0;
+  a.heads = desc->heads;
+  a.head_dim = desc->head_dim;
+  a.scale = desc->scale;
+  a.dtype = desc->dtype;
+  return launch_attention(a, (hipStream_t)stream);
+}
+
+ispa_status_t ispa_lse_merge(int32_t n_parts, const void* const* O_parts, const float* const* LSE_parts, int64_t n_q,
+                             int32_t heads, int32_t head_dim, int32_t dtype, void* O_out, float* LSE_out,
+                             void* stream) {
+  if (n_parts < 1 || n_parts > 16) return invalid("n_parts must be in [1, 16]");
+  if (O_parts == nullptr || LSE_parts == nullptr) return invalid("O_parts / LSE_parts is NULL");
+  if (n_q < 0 || heads < 1 || (head_dim != 64 && head_dim != 128)) return invalid("bad shape");
+  if (dtype != ISPA_F32 && dtype != ISPA_BF16) return invalid("bad dtype");
+  for (int i = 0; i < n_parts && n_q > 0; ++i)
+    if (!req(O_parts[i]) || !req(LSE_parts[i])) return invalid("part pointers must be non-NULL and 16-byte aligned");
+  if ((n_q > 0 && !req(O_out)) || !opt(LSE_out)) return invalid("O_out must be non-NULL; outputs 16-byte aligned");
+  ispa_status_t st = check_current_device();
+  if (st != ISPA_OK) return st;
+  return launch_lse_merge(n_parts, O_parts, LSE_parts, n_q, heads, head_dim, dtype, O_out, LSE_out,
+                          (hipStream_t)stream);
+}
+
+size_t ispa_gram_workspace_size(int64_t n_rows, int32_t d, int32_t dtype) {
+  if (n_rows < 0 || d <= 0) return 0;
+  return gram_workspace_size(n_rows, d, dtype);
+}
+
+ispa_status_t ispa_gram_accum(int64_t n_rows, int32_t d, int32_t dtype, const void* A_loc, const void* A_full, float* G,
+                              float* C, float* Q_ff, int32_t accumulate, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  if (n_rows < 0) return invalid("n_rows must be >= 0");
+  if (dtype != ISPA_F32 && dtype != ISPA_BF16) return invalid("bad dtype");
+  if (d <= 0 || (dtype == ISPA_BF16 && d % 128 != 0) || (dtype == ISPA_F32 && d % 64 != 0))
+    return invalid("d must be a multiple of 128 (bf16) or 64 (f32)");
+  if (accumulate != 0 && accumulate != 1) return invalid("accumulate must be 0 or 1");
+  if ((n_rows > 0 && (!req(A_loc) || !req(A_full))) || !req(G) || !req(C) || !opt(Q_ff))
+    return invalid("A_loc, A_full, G, C must be non-NULL and 16-byte aligned");
+  if (n_rows * (int64_t)d >= ((int64_t)1 << 40)) return invalid("too many rows");
+  ispa_status_t st = check_current_device();
+  if (st != ISPA_OK) return st;
+  return launch_gram(n_rows, d, dtype, A_loc, A_full, G, C, Q_ff, accumulate, workspace, workspace_bytes,
+                     (hipStream_t)stream);
+}
+
+size_t ispa_absorb_workspace_size(int32_t d, int32_t d_out, int32_t batch) {
+  if (d <= 0 || d_out <= 0 || batch <= 0) return 0;
+  return absorb_workspace_size(d, d_out, batch);
+}
+
+ispa_status_t ispa_absorb_solve(int32_t d, int32_t d_out, int32_t batch, const float* G, const float* C,
+                                const float* W, float lambda, float* dW, float* W_new, int32_t* info, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (d <= 0 || d % 64 != 0 || d_out <= 0 || d_out % 64 != 0) return invalid("d and d_out must be multiples of 64");
+  if (batch < 1 || batch > 65535) return invalid("batch must be in [1, 65535]");
+  if (!(lambda >= 0.f) || lambda == INFINITY) return invalid("lambda must be finite and >= 0");
+  if (!req(G) || !req(C) || !req(W) || !req(dW) || !req(info) || !opt(W_new))
+    return invalid("G, C, W, dW, info must be non-NULL and 16-byte aligned");
+  ispa_status_t st = check_current_device();
+  if (st != ISPA_OK) return st;
+  return launch_absorb(d, d_out, batch, G, C, W, lambda, dW, W_new, info, workspace, workspace_bytes,
+                       (hipStream_t)stream);
+}
+
+size_t ispa_eps_workspace_size(int32_t d, int32_t d_out, int32_t batch) {
+  if (d <= 0 || d_out <= 0 || batch <= 0) return 0;
+  return eps_workspace_size(d, d_out, batch);
+}
+
+ispa_status_t ispa_layer_eps(int32_t d, int32_t d_out, int32_t batch, const float* G, const float* C, const float* Q_ff,
+                             const float* W, const float* dW, float lambda, double* eps_abs, double* eps_rel,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  if (d <= 0 || d % 64 != 0 || d_out <= 0 || d_out % 64 != 0) return invalid("d and d_out must be multiples of 64");
+  if (batch < 1 || batch > 65535) return invalid("batch must be in [1, 65535]");
+  if (!(lambda >= 0.f) || lambda == INFINITY) return invalid("lambda must be finite and >= 0");
+  if (!req(G) || !req(C) || !req(Q_ff) || !req(W) || !req(dW) || !req(eps_abs) || !req(eps_rel))
+    return invalid("all pointers must be non-NULL and 16-byte aligned");
+  ispa_status_t st = check_current_device();
+  if (st != ISPA_OK) return st;
+  return launch_eps(d, d_out, batch, G, C, Q_ff, W, dW, lambda, eps_abs, eps_rel, workspace, workspace_bytes,
+                    (hipStream_t)stream);
+}
+
+const char* ispa_status_string(ispa_status_t s) {
+  switch (s) {
+    case ISPA_OK: return "ISPA_OK";
+    case ISPA_E_INVALID_ARG: return "ISPA_E_INVALID_ARG";
+    case ISPA_E_UNSUPPORTED: return "ISPA_E_UNSUPPORTED";
+    case ISPA_E_WORKSPACE: return "ISPA_E_WORKSPACE";
+    case ISPA_E_HIP: return "ISPA_E_HIP";
+  }
+  return "ISPA_E_UNKNOWN";
+}
+
+const char* ispa_last_error(void) { return g_last_error.c_str(); }
+
+int32_t ispa_version(void) { return 100; }
+
+ispa_status_t ispa_device_check(int32_t device) { return check_device(device); }
+
+}  // extern "C"

@@ -1,0 +1,614 @@
+// Decomposable attention on gfx950: local branch, history branch and their
+// log-sum-exp merge in one launch; plus the single-pass comparison attention
+// and a standalone N-way merge.
+//
+// Source: "Technical Summary: Instance-Specific Parametric Absorption (ISPA)
+// for Memory-Efficient Video Generation", section 2 "Methodology", step 1
+// "Dual-Stream Warmup" (local stream = sink + current chunk, full stream =
+// entire context, decomposed into local and historical branches that keep
+// log-sum-exp states and are fused afterwards) and section 3 (online softmax).
+//
+// bf16 kernel design (one workgroup = NW waves, one head, NW*32 queries):
+//  * Each wave owns 32 queries and computes S^T = K Q^T with
+//    v_mfma_f32_32x32x16_bf16, so a lane holds scores of ONE query (column
+//    lane%32) for 16 keys: the softmax row max and row sum are in-lane, plus
+//    one exchange between the two 32-lane halves.
+//  * O^T = V^T P^T accumulates on the same MFMA; P goes from the score
+//    accumulator straight into the B operand (no LDS round trip).  V is
+//    stored transposed in LDS with the keys of each 16-key group permuted
+//    (bits 2 and 3 of the key index swapped) so that the 8 keys a lane's P
+//    register holds are 8 contiguous LDS elements: one ds_read_b128.
+//  * K and V^T tiles of 64 keys are double-buffered in LDS; the next tile's
+//    global loads are issued before the current tile's MFMAs.
+//  * Local tiles then history tiles form one tile sequence (the pipeline does
+//    not drain at the branch switch).  At the switch the local branch is
+//    normalised and written (O_loc, LSE_loc); its float32 values go to the
+//    caller's workspace (each lane later reads back exactly what it wrote, so
+//    no synchronisation is needed).  After the last history tile the merge
+//    runs in registers from the float32 O_loc and O_full is rounded once.
+//  * Scores are scaled by scale*log2(e) and exponentiated with v_exp_f32
+//    (2^x); LSE is exported in natural log.
+#include "ispa_internal.h"
+
+namespace ispa {
+namespace {
+
+constexpr int BN = 64;  // keys per tile
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+struct AttnKParams {
+  const uint16_t* Q;
+  const uint16_t* Kl;
+  const uint16_t* Vl;
+  const uint16_t* Kh;
+  const uint16_t* Vh;
+  uint16_t* O_loc;
+  float* LSE_loc;
+  uint16_t* O_hist;
+  float* LSE_hist;
+  uint16_t* O_full;
+  float* LSE_full;
+  float* stash;  // float32 O_loc kept for the merge ([n_q, H, D]); used when O_full and history exist
+  int n_q, n_loc, n_hist, heads;
+  float c2;  // scale * log2(e)
+  int n_qtiles, nblocks;
+};
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnKParams p) {
+  constexpr int NT = NW * 64;
+  constexpr int KS = D + 8;   // K tile row stride (elements): rows 16 B apart in bank space
+  constexpr int VS = BN + 8;  // V^T tile row stride (elements)
+  constexpr int KK = D / 16;  // MFMA k-steps of S^T
+  constexpr int DB = D / 32;  // 32-row blocks of O^T
+  constexpr int NKB = BN / 32;
+  constexpr int KC = BN * D / 8 / NT;  // 16-byte K chunks per thread per tile
+  static_assert(KC >= 1 && KC * NT * 8 == BN * D, "K tile split");
+  constexpr int VITEMS = (BN / 8) * (D / 4);  // (8 keys x 4 dims) V items per tile
+  constexpr int VI = (VITEMS + NT - 1) / NT;
+
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * VS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const uint32_t unit = xcd_remap(blockIdx.x, p.nblocks);
+  const int head = unit / p.n_qtiles, qt = unit % p.n_qtiles;
+  const size_t HD = (size_t)p.heads * D;
+  const int myq = qt * (NW * 32) + wave * 32 + l32;
+  const bool qvalid = myq < p.n_q;
+  const int Tl = (p.n_loc + BN - 1) / BN;
+  const int Th = (p.n_hist + BN - 1) / BN;
+  const int T = Tl + Th;
+
+  // Q^T fragments (B operand of S^T = K Q^T): lane holds q[myq][16kk + 8hh .. +7].
+  bf16x8 qf[KK];
+  {
+    const uint16_t* qp = p.Q + (size_t)(qvalid ? myq : 0) * HD + head * D + 8 * hh;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      u32x4 v = qvalid ? *(const u32x4*)(qp + 16 * kk) : u32x4{0, 0, 0, 0};
+      qf[kk] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  u32x4 kreg[KC];
+  u32x2 vreg[VI][8];
+
+  auto load_tile = [&](int t) {
+    const uint16_t* Kp;
+    const uint16_t* Vp;
+    int key0, nvalid;
+    if (t < Tl) {
+      Kp = p.Kl; Vp = p.Vl; key0 = t * BN; nvalid = p.n_loc;
+    } else {
+      Kp = p.Kh; Vp = p.Vh; key0 = (t - Tl) * BN; nvalid = p.n_hist;
+    }
+#pragma unroll
+    for (int i = 0; i < KC; ++i) {
+      const int c = tid + i * NT;
+      const int row = c / (D / 8), col8 = c % (D / 8);
+      const int key = key0 + row;
+      kreg[i] = key < nvalid ? *(const u32x4*)(Kp + (size_t)key * HD + head * D + col8 * 8) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < VI; ++i) {
+      const int it = tid + i * NT;
+      const int kg = it % (BN / 8), dq = it / (BN / 8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int key = key0 + kg * 8 + e;
+        vreg[i][e] = (it < VITEMS && key < nvalid) ? *(const u32x2*)(Vp + (size_t)key * HD + head * D + dq * 4)
+                                                    : u32x2{0, 0};
+      }
+    }
+  };
+
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < KC; ++i) {
+      const int c = tid + i * NT;
+      const int row = c / (D / 8), col8 = c % (D / 8);
+      *(u32x4*)(&sK[buf][row * KS + col8 * 8]) = kreg[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VI; ++i) {
+      const int it = tid + i * NT;
+      if (it < VITEMS) {
+        const int kg = it % (BN / 8), dq = it / (BN / 8);
+        // Key 8kg+e of the tile goes to position sigma(8kg+e); sigma swaps bits
+        // 2 and 3 inside each 16-key group, so keys e=0..3 land at pos0+0..3
+        // and keys e=4..7 at pos0+8..11.
+        const int pos0 = (kg >> 1) * 16 + (kg & 1) * 4;
+#pragma unroll
+        for (int dd = 0; dd < 4; ++dd) {
+          uint32_t w[4];
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            const uint32_t a = (dd < 2) ? vreg[i][2 * x].x : vreg[i][2 * x].y;
+            const uint32_t b = (dd < 2) ? vreg[i][2 * x + 1].x : vreg[i][2 * x + 1].y;
+            w[x] = (dd & 1) ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
+          }
+          uint16_t* row = &sV[buf][(dq * 4 + dd) * VS];
+          *(u32x2*)(row + pos0) = u32x2{w[0], w[1]};
+          *(u32x2*)(row + pos0 + 8) = u32x2{w[2], w[3]};
+        }
+      }
+    }
+  };
+
+  // Online-softmax state of the current branch (log2 domain).
+  f32x16 acc[DB];
+  float m = -INFINITY, l = 0.f;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{0};
+
+  auto compute_tile = [&](int buf, int t) {
+    const int key0 = (t < Tl ? t : t - Tl) * BN;
+    const int nvalid = t < Tl ? p.n_loc : p.n_hist;
+    f32x16 s[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      s[kb] = f32x16{0};
+      const uint16_t* kr = &sK[buf][(kb * 32 + l32) * KS + 8 * hh];
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const bf16x8 kf = __builtin_bit_cast(bf16x8, *(const u32x4*)(kr + 16 * kk));
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s[kb], 0, 0, 0);
+      }
+    }
+    // Accumulator element v of lane (query, hh) in key block kb is key
+    // kb*32 + 8*(v/4) + 4*hh + v%4.  Mask keys past the branch's end.
+    if (key0 + BN > nvalid) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = key0 + kb * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
+          if (key >= nvalid) s[kb][v] = -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mnew = fmaxf(m, mx * p.c2);
+    const float alpha = fast_exp2(m - mnew);
+    m = mnew;
+    float ls = 0.f;
+    u32x4 pk[NKB][2];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm) {
+        uint32_t w[4];
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+          const float p0 = fast_exp2(fmaf(s[kb][8 * mm + j], p.c2, -mnew));
+          const float p1 = fast_exp2(fmaf(s[kb][8 * mm + j + 1], p.c2, -mnew));
+          ls += p0 + p1;
+          const bf16x2 b = {(__bf16)p0, (__bf16)p1};
+          w[j >> 1] = __builtin_bit_cast(uint32_t, b);
+        }
+        pk[kb][mm] = u32x4{w[0], w[1], w[2], w[3]};
+      }
+    l = fmaf(l, alpha, ls);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const uint16_t* vr = &sV[buf][(db * 32 + l32) * VS + 8 * hh];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm) {
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, *(const u32x4*)(vr + kb * 32 + 16 * mm));
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, __builtin_bit_cast(bf16x8, pk[kb][mm]), acc[db],
+                                                            0, 0, 0);
+        }
+    }
+  };
+
+  // O^T accumulator element v of lane (query, hh) in block db is dim 32db + 8(v/4) + 4hh + v%4.
+  auto write_o = [&](uint16_t* O, const u32x2 (&vals)[DB][4]) {
+    if (O == nullptr || !qvalid) return;
+    uint16_t* op = O + (size_t)myq * HD + head * D + 4 * hh;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) *(u32x2*)(op + 32 * db + 8 * g) = vals[db][g];
+  };
+  auto pack_acc = [&](u32x2 (&out)[DB][4], float scale_by) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const bf16x2 a = {(__bf16)(acc[db][4 * g] * scale_by), (__bf16)(acc[db][4 * g + 1] * scale_by)};
+        const bf16x2 b = {(__bf16)(acc[db][4 * g + 2] * scale_by), (__bf16)(acc[db][4 * g + 3] * scale_by)};
+        out[db][g] = u32x2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
+      }
+  };
+
+  float lse2_loc = -INFINITY;
+  float* const stash = p.stash + (size_t)(qvalid ? myq : 0) * HD + head * D + 4 * hh;
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  for (int t = 0; t < T; ++t) {
+    if (t + 1 < T) load_tile(t + 1);
+    compute_tile(t & 1, t);
+    if (t == Tl - 1) {
+      // local branch done: normalise, write O_loc / LSE_loc, keep float32 O_loc for the merge
+      const float lt = l + __shfl_xor(l, 32);
+      const float inv = 1.0f / lt;
+      lse2_loc = m + __log2f(lt);
+      u32x2 oloc[DB][4];
+      pack_acc(oloc, inv);
+      write_o(p.O_loc, oloc);
+      if (p.LSE_loc && hh == 0 && qvalid) p.LSE_loc[(size_t)head * p.n_q + myq] = lse2_loc * LN2;
+      if (Th == 0) {
+        // local-attention mode: the full output is the local one, bit for bit
+        write_o(p.O_full, oloc);
+        if (p.LSE_full && hh == 0 && qvalid) p.LSE_full[(size_t)head * p.n_q + myq] = lse2_loc * LN2;
+      } else if (p.O_full && qvalid) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            *(f32x4*)(stash + 32 * db + 8 * g) = f32x4{acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv,
+                                                      acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv};
+      }
+      m = -INFINITY;
+      l = 0.f;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc[db] = f32x16{0};
+    }
+    if (t + 1 < T) store_tile((t + 1) & 1);
+    __syncthreads();
+  }
+
+  if (Th > 0) {
+    const float lt = l + __shfl_xor(l, 32);
+    const float inv = 1.0f / lt;
+    const float lse2_hist = m + __log2f(lt);
+    if (p.O_hist) {
+      u32x2 oh[DB][4];
+      pack_acc(oh, inv);
+      write_o(p.O_hist, oh);
+    }
+    if (p.LSE_hist && hh == 0 && qvalid) p.LSE_hist[(size_t)head * p.n_q + myq] = lse2_hist * LN2;
+    // merge: LSE = logaddexp(LSE_loc, LSE_hist); O = w_loc O_loc + w_hist O_hist
+    const float mx = fmaxf(lse2_loc, lse2_hist);
+    const float lse2 = mx + __log2f(fast_exp2(lse2_loc - mx) + fast_exp2(lse2_hist - mx));
+    const float wl = fast_exp2(lse2_loc - lse2);
+    const float wh = fast_exp2(lse2_hist - lse2) * inv;
+    if (p.O_full && qvalid) {
+      u32x2 of[DB][4];
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 ol = *(const f32x4*)(stash + 32 * db + 8 * g);
+          float x[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = fmaf(wl, ol[e], wh * acc[db][4 * g + e]);
+          const bf16x2 a = {(__bf16)x[0], (__bf16)x[1]};
+          const bf16x2 b = {(__bf16)x[2], (__bf16)x[3]};
+          of[db][g] = u32x2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
+        }
+      write_o(p.O_full, of);
+    }
+    if (p.LSE_full && hh == 0 && qvalid) p.LSE_full[(size_t)head * p.n_q + myq] = lse2 * LN2;
+  } else if (p.O_hist) {
+    u32x2 z[DB][4];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) z[db][g] = u32x2{0, 0};
+    write_o(p.O_hist, z);
+  }
+  if (Th == 0 && p.LSE_hist && hh == 0 && qvalid) p.LSE_hist[(size_t)head * p.n_q + myq] = -INFINITY;
+}
+
+// ----------------------------------------------------------------------------
+// float32 path: one thread per (query, head); K/V tiles of 32 keys in LDS.
+// Used for the float32 configuration (parity-grade, not a performance path).
+// ----------------------------------------------------------------------------
+struct AttnF32Params {
+  const float* Q;
+  const float* Kl;
+  const float* Vl;
+  const float* Kh;
+  const float* Vh;
+  float* O_loc;
+  float* LSE_loc;
+  float* O_hist;
+  float* LSE_hist;
+  float* O_full;
+  float* LSE_full;
+  int n_q, n_loc, n_hist, heads;
+  float c2;
+  int n_qtiles;
+};
+
+constexpr int F32_NT = 128;
+constexpr int F32_BN = 32;
+
+template <int D>
+__global__ __launch_bounds__(F32_NT) void attn_f32_kernel(AttnF32Params p) {
+  __shared__ float sK[F32_BN][D];
+  __shared__ float sV[F32_BN][D];
+  __shared__ float stash[D][F32_NT];  // normalised O_loc of each thread's query
+  const int tid = threadIdx.x;
+  const int head = blockIdx.x / p.n_qtiles, qt = blockIdx.x % p.n_qtiles;
+  const size_t HD = (size_t)p.heads * D;
+  const int myq = qt * F32_NT + tid;
+  const bool qvalid = myq < p.n_q;
+  float q[D];
+  for (int e = 0; e < D; ++e) q[e] = qvalid ? p.Q[(size_t)myq * HD + head * D + e] : 0.f;
+
+  float lse2_loc = -INFINITY, lse2_hist = -INFINITY, inv_hist = 0.f;
+  float acc[D];
+  for (int br = 0; br < 2; ++br) {
+    const float* Kp = br == 0 ? p.Kl : p.Kh;
+    const float* Vp = br == 0 ? p.Vl : p.Vh;
+    const int n = br == 0 ? p.n_loc : p.n_hist;
+    float m = -INFINITY, l = 0.f;
+    for (int e = 0; e < D; ++e) acc[e] = 0.f;
+    for (int k0 = 0; k0 < n; k0 += F32_BN) {
+      __syncthreads();
+      for (int i = tid; i < F32_BN * D; i += F32_NT) {
+        const int r = i / D, c = i % D;
+        const int key = k0 + r;
+        sK[r][c] = key < n ? Kp[(size_t)key * HD + head * D + c] : 0.f;
+        sV[r][c] = key < n ? Vp[(size_t)key * HD + head * D + c] : 0.f;
+      }
+      __syncthreads();
+      const int nk = min(F32_BN, n - k0);
+      float s[F32_BN];
+      float mx = -INFINITY;
+      for (int j = 0; j < F32_BN; ++j) {
+        float a = 0.f;
+        for (int e = 0; e < D; ++e) a = fmaf(q[e], sK[j][e], a);
+        s[j] = j < nk ? a * p.c2 : -INFINITY;
+        mx = fmaxf(mx, s[j]);
+      }
+      const float mnew = fmaxf(m, mx);
+      const float alpha = exp2f(m - mnew);
+      m = mnew;
+      l *= alpha;
+      for (int e = 0; e < D; ++e) acc[e] *= alpha;
+      for (int j = 0; j < F32_BN; ++j) {
+        const float pj = exp2f(s[j] - mnew);
+        l += pj;
+        for (int e = 0; e < D; ++e) acc[e] = fmaf(pj, sV[j][e], acc[e]);
+      }
+    }
+    if (br == 0) {
+      const float inv = 1.0f / l;
+      lse2_loc = m + log2f(l);
+      for (int e = 0; e < D; ++e) stash[e][tid] = acc[e] * inv;
+      if (qvalid) {
+        if (p.O_loc)
+          for (int e = 0; e < D; ++e) p.O_loc[(size_t)myq * HD + head * D + e] = stash[e][tid];
+        if (p.LSE_loc) p.LSE_loc[(size_t)head * p.n_q + myq] = lse2_loc * LN2;
+      }
+    } else if (n > 0) {
+      inv_hist = 1.0f / l;
+      lse2_hist = m + log2f(l);
+    }
+  }
+  if (!qvalid) return;
+  float* ob = nullptr;
+  if (p.O_hist) {
+    ob = p.O_hist + (size_t)myq * HD + head * D;
+    for (int e = 0; e < D; ++e) ob[e] = p.n_hist > 0 ? acc[e] * inv_hist : 0.f;
+  }
+  if (p.LSE_hist) p.LSE_hist[(size_t)head * p.n_q + myq] = lse2_hist * LN2;
+  float lse2 = lse2_loc, wl = 1.f, wh = 0.f;
+  if (p.n_hist > 0) {
+    const float mx = fmaxf(lse2_loc, lse2_hist);
+    lse2 = mx + log2f(exp2f(lse2_loc - mx) + exp2f(lse2_hist - mx));
+    wl = exp2f(lse2_loc - lse2);
+    wh = exp2f(lse2_hist - lse2) * inv_hist;
+  }
+  if (p.O_full) {
+    float* of = p.O_full + (size_t)myq * HD + head * D;
+    for (int e = 0; e < D; ++e) of[e] = p.n_hist > 0 ? fmaf(wl, stash[e][tid], wh * acc[e]) : stash[e][tid];
+  }
+  if (p.LSE_full) p.LSE_full[(size_t)head * p.n_q + myq] = lse2 * LN2;
+}
+
+// ----------------------------------------------------------------------------
+// N-way LSE merge (memory bound): one thread per (query, head, 8 dims).
+// ----------------------------------------------------------------------------
+constexpr int MAX_PARTS = 16;
+struct MergeParams {
+  const void* O[MAX_PARTS];
+  const float* LSE[MAX_PARTS];
+  int n_parts;
+  int64_t n_q;
+  int heads, head_dim;
+  void* O_out;
+  float* LSE_out;
+};
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void lse_merge_kernel(MergeParams p) {
+  const int chunks = p.head_dim / 8;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = p.n_q * p.heads * chunks;
+  if (idx >= total) return;
+  const int c = idx % chunks;
+  const int64_t qh = idx / chunks;
+  const int h = qh % p.heads;
+  const int64_t q = qh / p.heads;
+  float lse[MAX_PARTS];
+  float mx = -INFINITY;
+  for (int i = 0; i < p.n_parts; ++i) {
+    lse[i] = p.LSE[i][(size_t)h * p.n_q + q];
+    mx = fmaxf(mx, lse[i]);
+  }
+  float sum = 0.f;
+  for (int i = 0; i < p.n_parts; ++i) sum += (lse[i] == -INFINITY) ? 0.f : __expf(lse[i] - mx);
+  const float lse_out = (mx == -INFINITY) ? -INFINITY : mx + __logf(sum);
+  float out[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  const size_t off = (size_t)qh * p.head_dim + c * 8;
+  for (int i = 0; i < p.n_parts; ++i) {
+    if (lse[i] == -INFINITY) continue;
+    const float w = __expf(lse[i] - lse_out);
+    if (BF16) {
+      const u32x4 v = *(const u32x4*)((const uint16_t*)p.O[i] + off);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        out[2 * e] = fmaf(w, __builtin_bit_cast(float, v[e] << 16), out[2 * e]);
+        out[2 * e + 1] = fmaf(w, __builtin_bit_cast(float, v[e] & 0xFFFF0000u), out[2 * e + 1]);
+      }
+    } else {
+      const f32x4 a = *(const f32x4*)((const float*)p.O[i] + off);
+      const f32x4 b = *(const f32x4*)((const float*)p.O[i] + off + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        out[e] = fmaf(w, a[e], out[e]);
+        out[4 + e] = fmaf(w, b[e], out[4 + e]);
+      }
+    }
+  }
+  if (BF16) {
+    u32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bf16x2 b = {(__bf16)out[2 * e], (__bf16)out[2 * e + 1]};
+      v[e] = __builtin_bit_cast(uint32_t, b);
+    }
+    *(u32x4*)((uint16_t*)p.O_out + off) = v;
+  } else {
+    *(f32x4*)((float*)p.O_out + off) = f32x4{out[0], out[1], out[2], out[3]};
+    *(f32x4*)((float*)p.O_out + off + 4) = f32x4{out[4], out[5], out[6], out[7]};
+  }
+  if (p.LSE_out && c == 0) p.LSE_out[(size_t)h * p.n_q + q] = lse_out;
+}
+
+}  // namespace
+
+constexpr int ATTN_NW = 4;
+
+ispa_status_t launch_attention(const AttnArgs& a, hipStream_t s) {
+  if (a.n_q == 0) return ISPA_OK;
+  if (a.dtype == ISPA_BF16) {
+    AttnKParams p;
+    p.Q = (const uint16_t*)a.Q;
+    p.Kl = (const uint16_t*)a.Kl;
+    p.Vl = (const uint16_t*)a.Vl;
+    p.Kh = (const uint16_t*)a.Kh;
+    p.Vh = (const uint16_t*)a.Vh;
+    p.O_loc = (uint16_t*)a.O_loc;
+    p.LSE_loc = a.LSE_loc;
+    p.O_hist = (uint16_t*)a.O_hist;
+    p.LSE_hist = a.LSE_hist;
+    p.O_full = (uint16_t*)a.O_full;
+    p.LSE_full = a.LSE_full;
+    p.stash = (float*)a.ws;
+    p.n_q = (int)a.n_q;
+    p.n_loc = (int)a.n_loc;
+    p.n_hist = (int)a.n_hist;
+    p.heads = a.heads;
+    p.c2 = a.scale * LOG2E;
+    const size_t ws_need = attention_workspace_size(a.n_q, a.heads, a.head_dim, a.n_hist, a.dtype);
+    if (a.O_full && ws_need > 0 && (a.ws == nullptr || a.ws_bytes < ws_need)) {
+      set_error("ispa_decomp_attn: workspace too small for the merge (query ispa_decomp_attn_workspace_size)");
+      return ISPA_E_WORKSPACE;
+    }
+    const int bm = ATTN_NW * 32;
+    p.n_qtiles = (int)((a.n_q + bm - 1) / bm);
+    p.nblocks = p.n_qtiles * a.heads;
+    const dim3 grid(p.nblocks), block(ATTN_NW * 64);
+    if (a.head_dim == 128)
+      hipLaunchKernelGGL((attn_bf16_kernel<128, ATTN_NW>), grid, block, 0, s, p);
+    else
+      hipLaunchKernelGGL((attn_bf16_kernel<64, ATTN_NW>), grid, block, 0, s, p);
+    return hip_check(hipGetLastError(), "attn_bf16_kernel launch");
+  }
+  AttnF32Params p;
+  p.Q = (const float*)a.Q;
+  p.Kl = (const float*)a.Kl;
+  p.Vl = (const float*)a.Vl;
+  p.Kh = (const float*)a.Kh;
+  p.Vh = (const float*)a.Vh;
+  p.O_loc = (float*)a.O_loc;
+  p.LSE_loc = a.LSE_loc;
+  p.O_hist = (float*)a.O_hist;
+  p.LSE_hist = a.LSE_hist;
+  p.O_full = (float*)a.O_full;
+  p.LSE_full = a.LSE_full;
+  p.n_q = (int)a.n_q;
+  p.n_loc = (int)a.n_loc;
+  p.n_hist = (int)a.n_hist;
+  p.heads = a.heads;
+  p.c2 = a.scale * LOG2E;
+  p.n_qtiles = (int)((a.n_q + F32_NT - 1) / F32_NT);
+  const dim3 grid(p.n_qtiles * a.heads), block(F32_NT);
+  if (a.head_dim == 128)
+    hipLaunchKernelGGL((attn_f32_kernel<128>), grid, block, 0, s, p);
+  else
+    hipLaunchKernelGGL((attn_f32_kernel<64>), grid, block, 0, s, p);
+  return hip_check(hipGetLastError(), "attn_f32_kernel launch");
+}
+
+size_t attention_workspace_size(int64_t n_q, int32_t heads, int32_t head_dim, int64_t n_hist, int32_t dtype) {
+  if (dtype != ISPA_BF16 || n_hist == 0) return 0;
+  return (size_t)n_q * heads * head_dim * sizeof(float);
+}
+
+ispa_status_t launch_lse_merge(int32_t n_parts, const void* const* O, const float* const* LSE, int64_t n_q,
+                               int32_t heads, int32_t head_dim, int32_t dtype, void* O_out, float* LSE_out,
+                               hipStream_t s) {
+  if (n_q == 0) return ISPA_OK;
+  MergeParams p;
+  for (int i = 0; i < n_parts; ++i) {
+    p.O[i] = O[i];
+    p.LSE[i] = LSE[i];
+  }
+  p.n_parts = n_parts;
+  p.n_q = n_q;
+  p.heads = heads;
+  p.head_dim = head_dim;
+  p.O_out = O_out;
+  p.LSE_out = LSE_out;
+  const int64_t total = n_q * heads * (head_dim / 8);
+  const dim3 grid((unsigned)((total + 255) / 256)), block(256);
+  if (dtype == ISPA_BF16)
+    hipLaunchKernelGGL((lse_merge_kernel<true>), grid, block, 0, s, p);
+  else
+    hipLaunchKernelGGL((lse_merge_kernel<false>), grid, block, 0, s, p);
+  return hip_check(hipGetLastError(), "lse_merge_kernel launch");
+}
+
+}  // namespace ispa

@@ -1,0 +1,82 @@
+// Internal declarations shared by the ISPA HIP translation units (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string>
+
+#include "../../include/ispa.h"
+
+namespace ispa {
+
+// ---------------------------------------------------------------- vector types
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------- error state
+void set_error(const std::string& msg);
+ispa_status_t hip_check(hipError_t e, const char* what);
+
+// ---------------------------------------------------------------- launchers
+struct AttnArgs {
+  const void* Q;
+  const void* Kl;
+  const void* Vl;
+  const void* Kh;
+  const void* Vh;
+  void* O_loc;
+  float* LSE_loc;
+  void* O_hist;
+  float* LSE_hist;
+  void* O_full;
+  float* LSE_full;
+  int64_t n_q, n_loc, n_hist;
+  int32_t heads, head_dim;
+  float scale;
+  int32_t dtype;
+  void* ws;
+  size_t ws_bytes;
+};
+size_t attention_workspace_size(int64_t n_q, int32_t heads, int32_t head_dim, int64_t n_hist, int32_t dtype);
+ispa_status_t launch_attention(const AttnArgs& a, hipStream_t s);
+
+ispa_status_t launch_lse_merge(int32_t n_parts, const void* const* O, const float* const* LSE, int64_t n_q,
+                               int32_t heads, int32_t head_dim, int32_t dtype, void* O_out, float* LSE_out,
+                               hipStream_t s);
+
+size_t gram_workspace_size(int64_t n_rows, int32_t d, int32_t dtype);
+ispa_status_t launch_gram(int64_t n_rows, int32_t d, int32_t dtype, const void* A_loc, const void* A_full,
+                          float* G, float* C, float* Qff, int32_t accumulate, void* ws, size_t ws_bytes,
+                          hipStream_t s);
+
+size_t absorb_workspace_size(int32_t d, int32_t d_out, int32_t batch);
+ispa_status_t launch_absorb(int32_t d, int32_t d_out, int32_t batch, const float* G, const float* C,
+                            const float* W, float lambda, float* dW, float* W_new, int32_t* info, void* ws,
+                            size_t ws_bytes, hipStream_t s);
+
+size_t eps_workspace_size(int32_t d, int32_t d_out, int32_t batch);
+ispa_status_t launch_eps(int32_t d, int32_t d_out, int32_t batch, const float* G, const float* C,
+                         const float* Qff, const float* W, const float* dW, float lambda, double* eps_abs,
+                         double* eps_rel, void* ws, size_t ws_bytes, hipStream_t s);
+
+// ---------------------------------------------------------------- device helpers
+// Map a linear workgroup id so that ids dispatched to the same XCD (the
+// hardware deals workgroups round-robin over the 8 XCDs) get consecutive
+// logical ids: tiles that share operands then share one XCD's L2.
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t bid, uint32_t nblocks) {
+  constexpr uint32_t NXCD = 8;
+  const uint32_t xcd = bid % NXCD;
+  const uint32_t slot = bid / NXCD;
+  const uint32_t q = nblocks / NXCD, r = nblocks % NXCD;
+  // XCDs < r hold q+1 blocks, the rest hold q.
+  const uint32_t base = xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q;
+  return base + slot;
+}
+
+}  // namespace ispa

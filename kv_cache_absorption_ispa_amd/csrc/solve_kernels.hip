@@ -1,0 +1,457 @@
+// Closed-form absorb on gfx950: dW = (G + lambda I)^-1 (C W) by a blocked
+// float32 Cholesky factorisation and blocked triangular solves, batched over
+// layers; and the Gram-form reconstruction error used to rank layers.
+//
+// Source: "Technical Summary: Instance-Specific Parametric Absorption (ISPA)
+// for Memory-Efficient Video Generation", section 2 "Methodology", step 2
+// "Layer Absorb" (ridge objective, closed-form minimiser, non-iterative),
+// step 3 "Memory-Efficient Inference" (W_new = W + dW) and "Dynamic Layer
+// Selection" (rank layers by reconstruction error).
+//
+// Structure (nb = 64 column panels, right-looking):
+//   M = G + lambda I                                   (init kernel)
+//   R = C W, accumulated in float64                    (float64 GEMM)
+//   for each panel k:
+//     factor M_kk = L_kk L_kk^T in LDS, form L_kk^-1  (one workgroup per layer)
+//     L_ik = M_ik L_kk^-T                             (GEMM, in place)
+//     M_ij -= L_ik L_jk^T  (lower tiles only)         (GEMM)
+//   forward:  Y_k = L_kk^-1 Y_k ; Y_i -= L_ik Y_k      (GEMMs)
+//   backward: X_k = L_kk^-T Y_k ; Y_i -= L_ki^T X_k    (GEMMs)
+//   one refinement step: r = R - G X - lambda X in float64, solve again with
+//   the same factor, dW = X + correction.
+// The float32 factorisation alone loses about kappa * 2^-24 (about 1e-3 at the
+// conditioning warmup statistics have, 1e5); the refinement step with a
+// float64 residual brings dW to the accuracy of its float32 inputs.
+// The factor and solve GEMMs run on v_mfma_f32_32x32x2_f32 with 64x64 tiles;
+// the float64-accumulated products run on the float64 VALU.  A layer whose
+// pivot fails records info = column + 1 and is skipped by later kernels; its
+// dW is set to NaN at the end and its W_new is left alone.
+#include "ispa_internal.h"
+
+namespace ispa {
+namespace {
+
+constexpr int NB = 64;  // panel width
+
+struct GemmParams {
+  const float* A;
+  const float* B;
+  const float* Cin;
+  float* D;
+  int M, N, K;
+  int lda, ldb, ldc, ldd;
+  size_t sA, sB, sC, sD;  // batch strides (elements)
+  float alpha, beta;
+  int lower_only;         // skip 64x64 tiles strictly above the diagonal
+  const int32_t* info;    // skip batch entries with info != 0 (nullable)
+};
+
+// D = alpha * op(A) op(B) + beta * Cin; op(A) is MxK, op(B) is KxN.
+// TA: A stored KxM (op(A) = A^T); TB: B stored NxK (op(B) = B^T).
+// M, N multiples of 64; K multiple of 16.  Cin may equal D.
+template <bool TA, bool TB>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
+  const int b = blockIdx.z;
+  if (p.info && p.info[b] != 0) return;
+  const int tm = blockIdx.y, tn = blockIdx.x;
+  if (p.lower_only && tm < tn) return;
+  const int m0 = tm * 64, n0 = tn * 64;
+  __shared__ float As[16][64 + 4];  // [k][m]
+  __shared__ float Bs[16][64 + 4];  // [k][n]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
+  const float* A = p.A + b * p.sA;
+  const float* B = p.B + b * p.sB;
+  f32x16 acc = f32x16{0};
+  for (int k0 = 0; k0 < p.K; k0 += 16) {
+    if (!TA) {
+      const int m = tid >> 2, kq = tid & 3;
+      const f32x4 v = *(const f32x4*)(A + (size_t)(m0 + m) * p.lda + k0 + 4 * kq);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) As[4 * kq + e][m] = v[e];
+    } else {
+      const int k = tid >> 4, mq = tid & 15;
+      *(f32x4*)(&As[k][4 * mq]) = *(const f32x4*)(A + (size_t)(k0 + k) * p.lda + m0 + 4 * mq);
+    }
+    if (TB) {
+      const int n = tid >> 2, kq = tid & 3;
+      const f32x4 v = *(const f32x4*)(B + (size_t)(n0 + n) * p.ldb + k0 + 4 * kq);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Bs[4 * kq + e][n] = v[e];
+    } else {
+      const int k = tid >> 4, nq = tid & 15;
+      *(f32x4*)(&Bs[k][4 * nq]) = *(const f32x4*)(B + (size_t)(k0 + k) * p.ldb + n0 + 4 * nq);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(As[2 * kk + hh][wm + l32], Bs[2 * kk + hh][wn + l32], acc, 0, 0, 0);
+    __syncthreads();
+  }
+  const float* Cin = p.Cin ? p.Cin + b * p.sC : nullptr;
+  float* D = p.D + b * p.sD;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int i = m0 + wm + 8 * (v >> 2) + 4 * hh + (v & 3);
+    const int j = n0 + wn + l32;
+    float r = p.alpha * acc[v];
+    if (Cin && p.beta != 0.f) r = fmaf(p.beta, Cin[(size_t)i * p.ldc + j], r);
+    D[(size_t)i * p.ldd + j] = r;
+  }
+}
+
+struct GemmDParams {
+  const float* A;      // M x K, row-major (lda)
+  const float* B;      // K x N, row-major (ldb)
+  const double* Cin;   // M x N float64 (ldc), nullable
+  const float* X;      // M x N float32 (ldx), nullable
+  double* D64;         // nullable
+  float* D32;          // nullable
+  int M, N, K;
+  int lda, ldb, ldc, ldx, ldd;
+  size_t sA, sB, sC, sX, sD;
+  double alpha, beta, gamma;
+  const int32_t* info;
+};
+
+// D = alpha * A B + beta * Cin + gamma * X with float64 accumulation of the
+// (exact) products of float32 operands, on the float64 VALU (full rate on this
+// GPU): each thread owns a 4x4 block of the 64x64 tile.  M, N multiples of 64,
+// K of 16.
+__global__ __launch_bounds__(256) void gemm_f64acc_kernel(GemmDParams p) {
+  const int b = blockIdx.z;
+  if (p.info && p.info[b] != 0) return;
+  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  __shared__ __attribute__((aligned(16))) float As[16][64 + 4];
+  __shared__ __attribute__((aligned(16))) float Bs[16][64 + 4];
+  const int tid = threadIdx.x;
+  const int ty = tid >> 4, tx = tid & 15;
+  const float* A = p.A + b * p.sA;
+  const float* B = p.B + b * p.sB;
+  double acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+  for (int k0 = 0; k0 < p.K; k0 += 16) {
+    {
+      const int m = tid >> 2, kq = tid & 3;
+      const f32x4 v = *(const f32x4*)(A + (size_t)(m0 + m) * p.lda + k0 + 4 * kq);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) As[4 * kq + e][m] = v[e];
+      const int k = tid >> 4, nq = tid & 15;
+      *(f32x4*)(&Bs[k][4 * nq]) = *(const f32x4*)(B + (size_t)(k0 + k) * p.ldb + n0 + 4 * nq);
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int k = 0; k < 16; ++k) {
+      const f32x4 a = *(const f32x4*)(&As[k][4 * ty]);
+      const f32x4 bb = *(const f32x4*)(&Bs[k][4 * tx]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fma((double)a[i], (double)bb[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = m0 + 4 * ty + i;
+      const int c = n0 + 4 * tx + j;
+      double x = p.alpha * acc[i][j];
+      if (p.Cin) x += p.beta * p.Cin[b * p.sC + (size_t)r * p.ldc + c];
+      if (p.X) x += p.gamma * (double)p.X[b * p.sX + (size_t)r * p.ldx + c];
+      if (p.D64) p.D64[b * p.sD + (size_t)r * p.ldd + c] = x;
+      if (p.D32) p.D32[b * p.sD + (size_t)r * p.ldd + c] = (float)x;
+    }
+}
+
+// M = G + lambda I (full matrix); info = 0.
+__global__ __launch_bounds__(256) void init_shift_kernel(const float* __restrict__ G, float* M, int d, float lambda,
+                                                         int32_t* info) {
+  const int b = blockIdx.y;
+  const size_t dd = (size_t)d * d;
+  const size_t i4 = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (blockIdx.x == 0 && threadIdx.x == 0) info[b] = 0;
+  if (i4 >= dd) return;
+  f32x4 v = *(const f32x4*)(G + b * dd + i4);
+  const int row = (int)(i4 / d), col = (int)(i4 % d);
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (col + e == row) v[e] += lambda;
+  *(f32x4*)(M + b * dd + i4) = v;
+}
+
+// Factor the 64x64 diagonal block at (k0, k0) of each layer's M in LDS and
+// form its inverse.  The lower triangle of M's block is overwritten by L_kk.
+__global__ __launch_bounds__(256) void potrf_diag_kernel(float* M, int d, int k0, float* Linv, int32_t* info) {
+  const int b = blockIdx.x;
+  if (info[b] != 0) return;
+  __shared__ float L[NB][NB + 1];
+  __shared__ float X[NB][NB + 1];
+  __shared__ int fail_col;
+  const int tid = threadIdx.x;
+  float* Mb = M + (size_t)b * d * d;
+  for (int e = tid; e < NB * NB; e += 256) {
+    const int i = e / NB, j = e % NB;
+    L[i][j] = j <= i ? Mb[(size_t)(k0 + i) * d + k0 + j] : 0.f;
+  }
+  if (tid == 0) fail_col = -1;
+  __syncthreads();
+  for (int j = 0; j < NB; ++j) {
+    if (tid == 0) {
+      const float dj = L[j][j];
+      if (!(dj > 0.f)) fail_col = j;
+      L[j][j] = sqrtf(dj);
+    }
+    __syncthreads();
+    if (fail_col >= 0) break;
+    const float piv = L[j][j];
+    for (int i = j + 1 + tid; i < NB; i += 256) L[i][j] /= piv;
+    __syncthreads();
+    const int w = NB - 1 - j;
+    for (int e = tid; e < w * w; e += 256) {
+      const int i = j + 1 + e / w, c = j + 1 + e % w;
+      if (c <= i) L[i][c] = fmaf(-L[i][j], L[c][j], L[i][c]);
+    }
+    __syncthreads();
+  }
+  if (fail_col >= 0) {
+    if (tid == 0) info[b] = k0 + fail_col + 1;
+    return;
+  }
+  // inverse of the lower-triangular L by forward substitution, one column per thread
+  if (tid < NB) {
+    const int c = tid;
+    for (int i = 0; i < NB; ++i) {
+      if (i < c) {
+        X[i][c] = 0.f;
+        continue;
+      }
+      float s = (i == c) ? 1.f : 0.f;
+      for (int m = c; m < i; ++m) s = fmaf(-L[i][m], X[m][c], s);
+      X[i][c] = s / L[i][i];
+    }
+  }
+  __syncthreads();
+  float* Lv = Linv + ((size_t)b * (d / NB) + k0 / NB) * NB * NB;
+  for (int e = tid; e < NB * NB; e += 256) {
+    const int i = e / NB, j = e % NB;
+    Lv[e] = X[i][j];
+    if (j <= i) Mb[(size_t)(k0 + i) * d + k0 + j] = L[i][j];
+  }
+}
+
+// dW = X + correction, or NaN for failed layers; W_new = W + dW for the others (W_new may be W).
+__global__ __launch_bounds__(256) void finalize_kernel(const float* W, float* dW, const float* corr, float* Wn,
+                                                       size_t n, const int32_t* info) {
+  const int b = blockIdx.y;
+  const size_t i4 = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (i4 >= n) return;
+  float* dw = dW + b * n + i4;
+  if (info[b] != 0) {
+    *(f32x4*)dw = f32x4{NAN, NAN, NAN, NAN};
+    return;
+  }
+  const f32x4 x = *(const f32x4*)dw + *(const f32x4*)(corr + b * n + i4);
+  *(f32x4*)dw = x;
+  if (Wn) *(f32x4*)(Wn + b * n + i4) = *(const f32x4*)(W + b * n + i4) + x;
+}
+
+// Inner products for the reconstruction error, reduced in float64 in a fixed order.
+__global__ __launch_bounds__(256) void eps_reduce_kernel(const float* W, const float* dW, const float* QW,
+                                                         const float* CW, const float* GW, size_t n, float lambda,
+                                                         double* eps_abs, double* eps_rel) {
+  const int b = blockIdx.x;
+  const size_t off = (size_t)b * n;
+  double s[5] = {0, 0, 0, 0, 0};
+  for (size_t i = threadIdx.x; i < n; i += 256) {
+    const double w = W[off + i], dw = dW[off + i], cw = CW[off + i];
+    s[0] += (double)QW[off + i] * w;
+    s[1] += cw * w;
+    s[2] += (double)GW[off + i] * w;
+    s[3] += dw * cw;
+    s[4] += dw * dw;
+  }
+  __shared__ double red[5][256];
+  for (int k = 0; k < 5; ++k) red[k][threadIdx.x] = s[k];
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w)
+      for (int k = 0; k < 5; ++k) red[k][threadIdx.x] += red[k][threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const double e = red[0][0] - 2.0 * red[1][0] - red[2][0] - red[3][0] - (double)lambda * red[4][0];
+    eps_abs[b] = e;
+    eps_rel[b] = e / red[0][0];
+  }
+}
+
+template <bool TA, bool TB>
+ispa_status_t gemm(hipStream_t s, int batch, int M, int N, int K, const float* A, int lda, size_t sA, const float* B,
+                   int ldb, size_t sB, const float* Cin, int ldc, size_t sC, float* D, int ldd, size_t sD, float alpha,
+                   float beta, bool lower_only, const int32_t* info) {
+  if (M <= 0 || N <= 0 || K <= 0) return ISPA_OK;
+  GemmParams p;
+  p.A = A; p.B = B; p.Cin = Cin; p.D = D;
+  p.M = M; p.N = N; p.K = K;
+  p.lda = lda; p.ldb = ldb; p.ldc = ldc; p.ldd = ldd;
+  p.sA = sA; p.sB = sB; p.sC = sC; p.sD = sD;
+  p.alpha = alpha; p.beta = beta;
+  p.lower_only = lower_only ? 1 : 0;
+  p.info = info;
+  const dim3 grid(N / 64, M / 64, batch), block(256);
+  hipLaunchKernelGGL((gemm_f32_kernel<TA, TB>), grid, block, 0, s, p);
+  return hip_check(hipGetLastError(), "gemm_f32_kernel launch");
+}
+
+ispa_status_t gemm_d(hipStream_t s, int batch, int M, int N, int K, const float* A, int lda, size_t sA,
+                     const float* B, int ldb, size_t sB, const double* Cin, int ldc, size_t sC, const float* X,
+                     int ldx, size_t sX, double* D64, float* D32, int ldd, size_t sD, double alpha, double beta,
+                     double gamma, const int32_t* info) {
+  GemmDParams p;
+  p.A = A; p.B = B; p.Cin = Cin; p.X = X; p.D64 = D64; p.D32 = D32;
+  p.M = M; p.N = N; p.K = K;
+  p.lda = lda; p.ldb = ldb; p.ldc = ldc; p.ldx = ldx; p.ldd = ldd;
+  p.sA = sA; p.sB = sB; p.sC = sC; p.sX = sX; p.sD = sD;
+  p.alpha = alpha; p.beta = beta; p.gamma = gamma;
+  p.info = info;
+  hipLaunchKernelGGL(gemm_f64acc_kernel, dim3(N / 64, M / 64, batch), dim3(256), 0, s, p);
+  return hip_check(hipGetLastError(), "gemm_f64acc_kernel launch");
+}
+
+#define ISPA_TRY(x)                       \
+  do {                                    \
+    ispa_status_t st_ = (x);              \
+    if (st_ != ISPA_OK) return st_;       \
+  } while (0)
+
+}  // namespace
+
+size_t absorb_workspace_size(int32_t d, int32_t d_out, int32_t batch) {
+  const size_t b = (size_t)batch;
+  return b * d * d * sizeof(float)               // factor
+         + b * d * NB * sizeof(float)            // inverses of the diagonal blocks
+         + b * d * d_out * sizeof(double)        // R = C W in float64
+         + b * d * d_out * sizeof(float);        // residual / correction
+}
+
+namespace {
+
+// Y <- (L L^T)^-1 Y in place, with the blocked factor L (lower triangle of M) and
+// the inverses of its diagonal blocks.
+ispa_status_t chol_solve_inplace(hipStream_t s, int batch, int d, int d_out, const float* M, const float* Linv,
+                                 float* Y, const int32_t* info) {
+  const size_t dd = (size_t)d * d, dn = (size_t)d * d_out;
+  const int nblk = d / NB;
+  const size_t sL = (size_t)nblk * NB * NB;
+  for (int k = 0; k < nblk; ++k) {  // forward: L Z = Y
+    const int k0 = k * NB;
+    float* Yk = Y + (size_t)k0 * d_out;
+    const float* Lkk_inv = Linv + (size_t)k * NB * NB;
+    ISPA_TRY((gemm<false, false>(s, batch, NB, d_out, NB, Lkk_inv, NB, sL, Yk, d_out, dn, nullptr, 0, 0, Yk, d_out,
+                                 dn, 1.f, 0.f, false, info)));
+    const int rest = d - k0 - NB;
+    if (rest > 0) {
+      const float* Lik = M + (size_t)(k0 + NB) * d + k0;
+      float* Yi = Y + (size_t)(k0 + NB) * d_out;
+      ISPA_TRY((gemm<false, false>(s, batch, rest, d_out, NB, Lik, d, dd, Yk, d_out, dn, Yi, d_out, dn, Yi, d_out, dn,
+                                   -1.f, 1.f, false, info)));
+    }
+  }
+  for (int k = nblk - 1; k >= 0; --k) {  // backward: L^T X = Z
+    const int k0 = k * NB;
+    float* Xk = Y + (size_t)k0 * d_out;
+    const float* Lkk_inv = Linv + (size_t)k * NB * NB;
+    ISPA_TRY((gemm<true, false>(s, batch, NB, d_out, NB, Lkk_inv, NB, sL, Xk, d_out, dn, nullptr, 0, 0, Xk, d_out, dn,
+                                1.f, 0.f, false, info)));
+    if (k0 > 0) {
+      const float* Lki = M + (size_t)k0 * d;  // rows k0..k0+63, cols 0..k0-1; used transposed
+      ISPA_TRY((gemm<true, false>(s, batch, k0, d_out, NB, Lki, d, dd, Xk, d_out, dn, Y, d_out, dn, Y, d_out, dn, -1.f,
+                                  1.f, false, info)));
+    }
+  }
+  return ISPA_OK;
+}
+
+}  // namespace
+
+ispa_status_t launch_absorb(int32_t d, int32_t d_out, int32_t batch, const float* G, const float* C, const float* W,
+                            float lambda, float* dW, float* W_new, int32_t* info, void* ws, size_t ws_bytes,
+                            hipStream_t s) {
+  const size_t need = absorb_workspace_size(d, d_out, batch);
+  if (ws == nullptr || ws_bytes < need) {
+    set_error("ispa_absorb_solve: workspace too small");
+    return ISPA_E_WORKSPACE;
+  }
+  const size_t dd = (size_t)d * d, dn = (size_t)d * d_out;
+  float* M = (float*)ws;
+  float* Linv = M + (size_t)batch * dd;
+  double* R64 = (double*)(Linv + (size_t)batch * d * NB);
+  float* Rr = (float*)(R64 + (size_t)batch * dn);
+  const int nblk = d / NB;
+
+  hipLaunchKernelGGL(init_shift_kernel, dim3((unsigned)((dd / 4 + 255) / 256), batch), dim3(256), 0, s, G, M, d,
+                     lambda, info);
+  ISPA_TRY(hip_check(hipGetLastError(), "init_shift_kernel launch"));
+  // R = C W (float64 accumulation), kept in float64 and rounded into dW as the first right-hand side
+  ISPA_TRY(gemm_d(s, batch, d, d_out, d, C, d, dd, W, d_out, dn, nullptr, 0, 0, nullptr, 0, 0, R64, dW, d_out, dn,
+                  1.0, 0.0, 0.0, nullptr));
+  // Cholesky
+  for (int k = 0; k < nblk; ++k) {
+    const int k0 = k * NB;
+    hipLaunchKernelGGL(potrf_diag_kernel, dim3(batch), dim3(256), 0, s, M, d, k0, Linv, info);
+    ISPA_TRY(hip_check(hipGetLastError(), "potrf_diag_kernel launch"));
+    const int rest = d - k0 - NB;
+    if (rest <= 0) break;
+    float* panel = M + (size_t)(k0 + NB) * d + k0;
+    const float* Lkk_inv = Linv + (size_t)k * NB * NB;
+    // L_ik = M_ik L_kk^-T (in place)
+    ISPA_TRY((gemm<false, true>(s, batch, rest, NB, NB, panel, d, dd, Lkk_inv, NB, (size_t)nblk * NB * NB, nullptr,
+                                0, 0, panel, d, dd, 1.f, 0.f, false, info)));
+    // trailing update, lower tiles
+    float* trail = M + (size_t)(k0 + NB) * d + k0 + NB;
+    ISPA_TRY((gemm<false, true>(s, batch, rest, rest, NB, panel, d, dd, panel, d, dd, trail, d, dd, trail, d, dd, -1.f,
+                                1.f, true, info)));
+  }
+  // X = (L L^T)^-1 R
+  ISPA_TRY(chol_solve_inplace(s, batch, d, d_out, M, Linv, dW, info));
+  // refinement: r = R - G X - lambda X (float64), correction = (L L^T)^-1 r
+  ISPA_TRY(gemm_d(s, batch, d, d_out, d, G, d, dd, dW, d_out, dn, R64, d_out, dn, dW, d_out, dn, nullptr, Rr, d_out,
+                  dn, -1.0, 1.0, -(double)lambda, info));
+  ISPA_TRY(chol_solve_inplace(s, batch, d, d_out, M, Linv, Rr, info));
+  hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)((dn / 4 + 255) / 256), batch), dim3(256), 0, s, W, dW,
+                     (const float*)Rr, W_new, dn, (const int32_t*)info);
+  return hip_check(hipGetLastError(), "finalize_kernel launch");
+}
+
+size_t eps_workspace_size(int32_t d, int32_t d_out, int32_t batch) {
+  return 3 * (size_t)batch * d * d_out * sizeof(float);
+}
+
+ispa_status_t launch_eps(int32_t d, int32_t d_out, int32_t batch, const float* G, const float* C, const float* Qff,
+                         const float* W, const float* dW, float lambda, double* eps_abs, double* eps_rel, void* ws,
+                         size_t ws_bytes, hipStream_t s) {
+  if (ws == nullptr || ws_bytes < eps_workspace_size(d, d_out, batch)) {
+    set_error("ispa_layer_eps: workspace too small");
+    return ISPA_E_WORKSPACE;
+  }
+  const size_t dd = (size_t)d * d, dn = (size_t)d * d_out;
+  float* QW = (float*)ws;
+  float* CW = QW + (size_t)batch * dn;
+  float* GW = CW + (size_t)batch * dn;
+  ISPA_TRY((gemm<false, false>(s, batch, d, d_out, d, Qff, d, dd, W, d_out, dn, nullptr, 0, 0, QW, d_out, dn, 1.f, 0.f,
+                               false, nullptr)));
+  ISPA_TRY((gemm<false, false>(s, batch, d, d_out, d, C, d, dd, W, d_out, dn, nullptr, 0, 0, CW, d_out, dn, 1.f, 0.f,
+                               false, nullptr)));
+  ISPA_TRY((gemm<false, false>(s, batch, d, d_out, d, G, d, dd, W, d_out, dn, nullptr, 0, 0, GW, d_out, dn, 1.f, 0.f,
+                               false, nullptr)));
+  hipLaunchKernelGGL(eps_reduce_kernel, dim3(batch), dim3(256), 0, s, W, dW, QW, CW, GW, dn, lambda, eps_abs, eps_rel);
+  return hip_check(hipGetLastError(), "eps_reduce_kernel launch");
+}
+
+}  // namespace ispa

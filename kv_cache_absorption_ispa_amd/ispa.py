@@ -1,0 +1,275 @@
+"""Thin ctypes binding of libispa.so (argument marshalling only).
+
+Every function has the name of the C entry point it calls (see include/ispa.h
+for the semantics).  Tensors are torch tensors on the current HIP device;
+torch provides device memory and the stream, nothing else: all computation is
+in the library's HIP kernels.  There is no fallback: if the library is not
+built, or the device is not gfx950, calls raise :class:`IspaError`.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libispa.so")
+
+ISPA_OK, ISPA_E_INVALID_ARG, ISPA_E_UNSUPPORTED, ISPA_E_WORKSPACE, ISPA_E_HIP = range(5)
+ISPA_F32, ISPA_BF16 = 0, 1
+
+EXPORTS = [
+    "ispa_decomp_attn", "ispa_decomp_attn_workspace_size", "ispa_full_attn", "ispa_lse_merge", "ispa_gram_workspace_size", "ispa_gram_accum",
+    "ispa_absorb_workspace_size", "ispa_absorb_solve", "ispa_eps_workspace_size", "ispa_layer_eps",
+    "ispa_status_string", "ispa_last_error", "ispa_version", "ispa_device_check",
+]
+
+
+class IspaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [
+        ("heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("n_q", ctypes.c_int64),
+        ("n_loc", ctypes.c_int64),
+        ("n_hist", ctypes.c_int64),
+        ("scale", ctypes.c_float),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libispa.so and declare its signatures (no GPU needed to load)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise IspaError(-1, f"{path} is not built; run `python -m kv_cache_absorption_ispa_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I32, I64, SZ, F, D = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float, None
+    sig = {
+        "ispa_decomp_attn": (I32, [ctypes.POINTER(AttnDesc)] + [P] * 12 + [SZ, P]),
+        "ispa_decomp_attn_workspace_size": (SZ, [ctypes.POINTER(AttnDesc)]),
+        "ispa_full_attn": (I32, [ctypes.POINTER(AttnDesc), P, P, P, P, P, P]),
+        "ispa_lse_merge": (I32, [I32, P, P, I64, I32, I32, I32, P, P, P]),
+        "ispa_gram_workspace_size": (SZ, [I64, I32, I32]),
+        "ispa_gram_accum": (I32, [I64, I32, I32, P, P, P, P, P, I32, P, SZ, P]),
+        "ispa_absorb_workspace_size": (SZ, [I32, I32, I32]),
+        "ispa_absorb_solve": (I32, [I32, I32, I32, P, P, P, F, P, P, P, P, SZ, P]),
+        "ispa_eps_workspace_size": (SZ, [I32, I32, I32]),
+        "ispa_layer_eps": (I32, [I32, I32, I32, P, P, P, P, P, F, P, P, P, SZ, P]),
+        "ispa_status_string": (ctypes.c_char_p, [I32]),
+        "ispa_last_error": (ctypes.c_char_p, []),
+        "ispa_version": (I32, []),
+        "ispa_device_check": (I32, [I32]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != ISPA_OK:
+        lib = load_library()
+        raise IspaError(status, f"{lib.ispa_status_string(status).decode()}: {lib.ispa_last_error().decode()}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise IspaError(ISPA_E_INVALID_ARG, "tensor is not on the GPU")
+    if not t.is_contiguous():
+        raise IspaError(ISPA_E_INVALID_ARG, "tensor is not contiguous")
+    return t.data_ptr() if t.numel() > 0 else None
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return ISPA_BF16
+    if t.dtype == torch.float32:
+        return ISPA_F32
+    raise IspaError(ISPA_E_INVALID_ARG, f"unsupported dtype {t.dtype}")
+
+
+def _expect(t: Optional[torch.Tensor], shape, dtype, name: str) -> None:
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise IspaError(ISPA_E_INVALID_ARG, f"{name}: expected {tuple(shape)} {dtype}, got {tuple(t.shape)} {t.dtype}")
+
+
+def make_desc(q: torch.Tensor, n_loc: int, n_hist: int, scale: Optional[float]) -> AttnDesc:
+    n_q, H, D = q.shape
+    return AttnDesc(H, D, n_q, n_loc, n_hist, float(scale if scale is not None else D ** -0.5), _dtype_code(q))
+
+
+def ispa_decomp_attn_workspace_size(q, n_loc: int, n_hist: int, scale=None) -> int:
+    desc = make_desc(q, n_loc, n_hist, scale)
+    return int(load_library().ispa_decomp_attn_workspace_size(ctypes.byref(desc)))
+
+
+def ispa_decomp_attn(q, k_loc, v_loc, k_hist=None, v_hist=None, *, scale=None, o_loc=None, lse_loc=None,
+                     o_hist=None, lse_hist=None, o_full=None, lse_full=None, workspace=None, stream=None) -> None:
+    """Dual-stream attention of one chunk; writes whichever outputs are given.
+
+    `workspace` (bytes >= ispa_decomp_attn_workspace_size) is needed for o_full with history keys;
+    when omitted here, one is allocated through torch for this call."""
+    n_q, H, D = q.shape
+    n_loc = k_loc.shape[0]
+    n_hist = 0 if k_hist is None else k_hist.shape[0]
+    for t, n in ((k_loc, "k_loc"), (v_loc, "v_loc")):
+        _expect(t, (n_loc, H, D), q.dtype, n)
+    if n_hist:
+        _expect(k_hist, (n_hist, H, D), q.dtype, "k_hist")
+        _expect(v_hist, (n_hist, H, D), q.dtype, "v_hist")
+    for t, n in ((o_loc, "o_loc"), (o_hist, "o_hist"), (o_full, "o_full")):
+        _expect(t, (n_q, H, D), q.dtype, n)
+    for t, n in ((lse_loc, "lse_loc"), (lse_hist, "lse_hist"), (lse_full, "lse_full")):
+        _expect(t, (H, n_q), torch.float32, n)
+    desc = make_desc(q, n_loc, n_hist, scale)
+    lib = load_library()
+    if workspace is None and o_full is not None:
+        workspace = _workspace(int(lib.ispa_decomp_attn_workspace_size(ctypes.byref(desc))), q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.ispa_decomp_attn(ctypes.byref(desc), _ptr(q), _ptr(k_loc), _ptr(v_loc),
+                                _ptr(k_hist) if n_hist else None, _ptr(v_hist) if n_hist else None,
+                                _ptr(o_loc), _ptr(lse_loc), _ptr(o_hist), _ptr(lse_hist), _ptr(o_full),
+                                _ptr(lse_full), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def ispa_full_attn(q, k, v, *, scale=None, o=None, lse=None, stream=None) -> None:
+    """One online-softmax pass over all keys of k/v."""
+    n_q, H, D = q.shape
+    n = k.shape[0]
+    _expect(k, (n, H, D), q.dtype, "k")
+    _expect(v, (n, H, D), q.dtype, "v")
+    _expect(o, (n_q, H, D), q.dtype, "o")
+    _expect(lse, (H, n_q), torch.float32, "lse")
+    desc = make_desc(q, n, 0, scale)
+    lib = load_library()
+    _check(lib.ispa_full_attn(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _stream(stream)))
+
+
+def ispa_lse_merge(o_parts: Sequence[torch.Tensor], lse_parts: Sequence[torch.Tensor], o_out, lse_out=None,
+                   stream=None) -> None:
+    """Merge partial (O, LSE) results over disjoint key sets."""
+    n = len(o_parts)
+    n_q, H, D = o_parts[0].shape
+    for o, l in zip(o_parts, lse_parts):
+        _expect(o, (n_q, H, D), o_parts[0].dtype, "o_part")
+        _expect(l, (H, n_q), torch.float32, "lse_part")
+    _expect(o_out, (n_q, H, D), o_parts[0].dtype, "o_out")
+    _expect(lse_out, (H, n_q), torch.float32, "lse_out")
+    optrs = (ctypes.c_void_p * n)(*[_ptr(o) for o in o_parts])
+    lptrs = (ctypes.c_void_p * n)(*[_ptr(l) for l in lse_parts])
+    lib = load_library()
+    _check(lib.ispa_lse_merge(n, optrs, lptrs, n_q, H, D, _dtype_code(o_parts[0]), _ptr(o_out), _ptr(lse_out),
+                              _stream(stream)))
+
+
+def ispa_gram_workspace_size(n_rows: int, d: int, dtype: torch.dtype) -> int:
+    code = ISPA_BF16 if dtype == torch.bfloat16 else ISPA_F32
+    return int(load_library().ispa_gram_workspace_size(n_rows, d, code))
+
+
+def ispa_gram_accum(a_loc, a_full, G, C, Q_ff=None, *, accumulate: bool, workspace=None, stream=None) -> None:
+    """G (+)= A_loc^T A_loc ; C (+)= A_loc^T A_full - A_loc^T A_loc ; Q_ff (+)= A_full^T A_full."""
+    n = a_loc.shape[0]
+    d = 1
+    for s_ in a_loc.shape[1:]:
+        d *= int(s_)
+    a_loc2 = a_loc.reshape(n, d)
+    a_full2 = a_full.reshape(a_full.shape[0], d)
+    _expect(a_full2, (n, d), a_loc.dtype, "a_full")
+    for t, nm in ((G, "G"), (C, "C"), (Q_ff, "Q_ff")):
+        _expect(t, (d, d), torch.float32, nm)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    lib = load_library()
+    _check(lib.ispa_gram_accum(n, d, _dtype_code(a_loc), _ptr(a_loc2), _ptr(a_full2), _ptr(G), _ptr(C), _ptr(Q_ff),
+                               1 if accumulate else 0, _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def ispa_absorb_workspace_size(d: int, d_out: int, batch: int) -> int:
+    return int(load_library().ispa_absorb_workspace_size(d, d_out, batch))
+
+
+def ispa_absorb_solve(G, C, W, lam: float, dW, info, *, W_new=None, workspace=None, stream=None) -> None:
+    """dW = (G + lam I)^-1 C W per batch entry; G, C [b,d,d] or [d,d]; W, dW [b,d,d_out] or [d,d_out]."""
+    G3 = G if G.dim() == 3 else G[None]
+    W3 = W if W.dim() == 3 else W[None]
+    b, d, _ = G3.shape
+    d_out = W3.shape[2]
+    _expect(G3, (b, d, d), torch.float32, "G")
+    _expect(C if C.dim() == 3 else C[None], (b, d, d), torch.float32, "C")
+    _expect(W3, (b, d, d_out), torch.float32, "W")
+    _expect(dW if dW.dim() == 3 else dW[None], (b, d, d_out), torch.float32, "dW")
+    if W_new is not None:
+        _expect(W_new if W_new.dim() == 3 else W_new[None], (b, d, d_out), torch.float32, "W_new")
+    _expect(info.reshape(-1), (b,), torch.int32, "info")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    lib = load_library()
+    _check(lib.ispa_absorb_solve(d, d_out, b, _ptr(G), _ptr(C), _ptr(W), float(lam), _ptr(dW), _ptr(W_new),
+                                 _ptr(info), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def ispa_eps_workspace_size(d: int, d_out: int, batch: int) -> int:
+    return int(load_library().ispa_eps_workspace_size(d, d_out, batch))
+
+
+def ispa_layer_eps(G, C, Q_ff, W, dW, lam: float, eps_abs, eps_rel, *, workspace=None, stream=None) -> None:
+    """Reconstruction error of each layer from its Gram statistics (float64 outputs [batch])."""
+    G3 = G if G.dim() == 3 else G[None]
+    W3 = W if W.dim() == 3 else W[None]
+    b, d, _ = G3.shape
+    d_out = W3.shape[2]
+    for t, nm in ((G, "G"), (C, "C"), (Q_ff, "Q_ff")):
+        _expect(t if t.dim() == 3 else t[None], (b, d, d), torch.float32, nm)
+    for t, nm in ((W, "W"), (dW, "dW")):
+        _expect(t if t.dim() == 3 else t[None], (b, d, d_out), torch.float32, nm)
+    _expect(eps_abs.reshape(-1), (b,), torch.float64, "eps_abs")
+    _expect(eps_rel.reshape(-1), (b,), torch.float64, "eps_rel")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    lib = load_library()
+    _check(lib.ispa_layer_eps(d, d_out, b, _ptr(G), _ptr(C), _ptr(Q_ff), _ptr(W), _ptr(dW), float(lam),
+                              _ptr(eps_abs), _ptr(eps_rel), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def ispa_version() -> int:
+    return int(load_library().ispa_version())
+
+
+def ispa_device_check(device: int = 0) -> None:
+    _check(load_library().ispa_device_check(device))
+
+
+def workspace(nbytes: int, device=None) -> Optional[torch.Tensor]:
+    """A caller-owned device workspace of at least nbytes (None when 0)."""
+    return _workspace(nbytes, device)
+
+
+def _workspace(nbytes: int, device=None) -> Optional[torch.Tensor]:
+    if nbytes <= 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device or "cuda")

@@ -1,0 +1,77 @@
+"""The C-ABI library loads and exports every entry point include/ispa.h declares (CPU only: no compute)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from kv_cache_absorption_ispa_amd import ispa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "ispa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ispa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_lists_the_entry_points():
+    names = header_functions()
+    for n in ("ispa_decomp_attn", "ispa_gram_accum", "ispa_absorb_solve", "ispa_full_attn", "ispa_lse_merge",
+              "ispa_layer_eps"):
+        assert n in names
+    assert sorted(ispa.EXPORTS) == names
+
+
+@pytest.mark.skipif(not os.path.exists(ispa.LIB_PATH), reason="libispa.so not built")
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(ispa.LIB_PATH)
+    for n in header_functions():
+        assert hasattr(lib, n), n
+    lib2 = ispa.load_library()
+    assert lib2.ispa_version() >= 100
+    assert lib2.ispa_status_string(0) == b"ISPA_OK"
+    assert lib2.ispa_status_string(3) == b"ISPA_E_WORKSPACE"
+
+
+@pytest.mark.skipif(not os.path.exists(ispa.LIB_PATH), reason="libispa.so not built")
+def test_validation_errors_need_no_gpu():
+    """Argument validation returns before any HIP call, so it is testable on the host."""
+    lib = ispa.load_library()
+    desc = ispa.AttnDesc(2, 96, 8, 8, 0, 0.1, 1)  # head_dim 96 unsupported
+    st = lib.ispa_decomp_attn(ctypes.byref(desc), *([None] * 11), None, 0, None)
+    assert st == ispa.ISPA_E_INVALID_ARG
+    assert b"head_dim" in lib.ispa_last_error()
+    desc = ispa.AttnDesc(2, 64, 8, 0, 0, 0.1, 1)  # n_loc = 0
+    assert lib.ispa_decomp_attn(ctypes.byref(desc), *([None] * 11), None, 0, None) == ispa.ISPA_E_INVALID_ARG
+    desc = ispa.AttnDesc(2, 64, 8, 4, 0, 0.1, 1)  # null Q
+    assert lib.ispa_decomp_attn(ctypes.byref(desc), *([None] * 11), None, 0, None) == ispa.ISPA_E_INVALID_ARG
+    misaligned = ctypes.c_void_p(0x1004)
+    assert lib.ispa_decomp_attn(ctypes.byref(desc), misaligned, misaligned, misaligned,
+                                *([None] * 8), None, 0, None) == ispa.ISPA_E_INVALID_ARG
+    # a bf16 merge with history keys needs the float32 workspace
+    d2 = ispa.AttnDesc(2, 128, 100, 50, 70, 0.1, 1)
+    assert lib.ispa_decomp_attn_workspace_size(ctypes.byref(d2)) == 100 * 2 * 128 * 4
+    d3 = ispa.AttnDesc(2, 128, 100, 50, 0, 0.1, 1)
+    assert lib.ispa_decomp_attn_workspace_size(ctypes.byref(d3)) == 0
+    ok = ctypes.c_void_p(0x10000)
+    assert lib.ispa_decomp_attn(ctypes.byref(d2), ok, ok, ok, ok, ok, None, None, None, None, ok, None,
+                                None, 0, None) == ispa.ISPA_E_WORKSPACE
+    assert lib.ispa_absorb_solve(100, 64, 1, *([None] * 3), 0.01, *([None] * 4), 0, None) == ispa.ISPA_E_INVALID_ARG
+    assert lib.ispa_absorb_solve(128, 64, 1, *([None] * 3), -1.0, *([None] * 4), 0, None) == ispa.ISPA_E_INVALID_ARG
+    assert lib.ispa_gram_accum(10, 192, ispa.ISPA_BF16, *([None] * 5), 0, None, 0, None) == ispa.ISPA_E_INVALID_ARG
+    assert lib.ispa_gram_accum(10, 128, ispa.ISPA_BF16, *([None] * 5), 2, None, 0, None) == ispa.ISPA_E_INVALID_ARG
+    assert lib.ispa_lse_merge(0, None, None, 4, 2, 64, 1, None, None, None) == ispa.ISPA_E_INVALID_ARG
+    assert lib.ispa_lse_merge(17, None, None, 4, 2, 64, 1, None, None, None) == ispa.ISPA_E_INVALID_ARG
+
+
+@pytest.mark.skipif(not os.path.exists(ispa.LIB_PATH), reason="libispa.so not built")
+def test_workspace_queries():
+    lib = ispa.load_library()
+    # the absorb factor lives in the workspace: at least batch*d*d floats
+    assert lib.ispa_absorb_workspace_size(1536, 1536, 30) >= 30 * 1536 * 1536 * 4
+    assert lib.ispa_eps_workspace_size(1536, 1536, 2) == 3 * 2 * 1536 * 1536 * 4
+    assert lib.ispa_gram_workspace_size(4680, 5120, ispa.ISPA_BF16) == 0  # enough tiles: no split
+    assert lib.ispa_gram_workspace_size(4680, 1536, ispa.ISPA_BF16) > 0  # few tiles: split rows
+    assert lib.ispa_gram_workspace_size(256, 128, ispa.ISPA_F32) == 0

@@ -1,0 +1,190 @@
+"""GPU parity of the decomposable attention (ispa_decomp_attn / ispa_full_attn / ispa_lse_merge)
+against the float64 oracle on the same seeded inputs, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from kv_cache_absorption_ispa_amd import inputs
+from kv_cache_absorption_ispa_amd import ispa
+from tests.gpu_util import (TOL_BF16_LSE, TOL_BF16_O, TOL_F32, dev, host64, maxabs, poisoned, relfro, say)
+
+pytestmark = pytest.mark.gpu
+
+
+def run_decomp(x: inputs.ChunkInputs, scale):
+    q = dev(x.q)
+    n_q, H, D = q.shape
+    dt = q.dtype
+    kl, vl = dev(x.k_loc), dev(x.v_loc)
+    nh = x.k_hist.shape[0]
+    kh = dev(x.k_hist) if nh else None
+    vh = dev(x.v_hist) if nh else None
+    out = dict(O_loc=poisoned((n_q, H, D), dt), LSE_loc=poisoned((H, n_q), torch.float32),
+               O_hist=poisoned((n_q, H, D), dt), LSE_hist=poisoned((H, n_q), torch.float32),
+               O_full=poisoned((n_q, H, D), dt), LSE_full=poisoned((H, n_q), torch.float32))
+    ispa.ispa_decomp_attn(q, kl, vl, kh, vh, scale=scale, o_loc=out["O_loc"], lse_loc=out["LSE_loc"],
+                          o_hist=out["O_hist"], lse_hist=out["LSE_hist"], o_full=out["O_full"],
+                          lse_full=out["LSE_full"])
+    torch.cuda.synchronize()
+    return out
+
+
+def check_against_oracle(x, out, scale, tol_o, tol_lse, rows=None):
+    qh = x.q.f64 if rows is None else x.q.f64[rows]
+    ref = oracle.branch_outputs(qh, x.k_loc.f64, x.v_loc.f64, x.k_hist.f64, x.v_hist.f64, scale)
+    report = {}
+    for name in ("O_loc", "O_hist", "O_full"):
+        got = host64(out[name])
+        got = got if rows is None else got[rows]
+        e = maxabs(got, ref[name])
+        report[name] = (e, relfro(got, ref[name]) if np.linalg.norm(ref[name]) > 0 else 0.0)
+        assert e <= tol_o, (name, e)
+    for name in ("LSE_loc", "LSE_hist", "LSE_full"):
+        got = out[name].cpu().numpy().astype(np.float64)
+        got = got if rows is None else got[:, rows]
+        if x.k_hist.shape[0] == 0 and name == "LSE_hist":
+            assert np.all(np.isneginf(got))
+            continue
+        e = maxabs(got, ref[name])
+        report[name] = e
+        assert e <= tol_lse, (name, e)
+    return report
+
+
+@pytest.mark.parametrize("case", [
+    # (seed, n_q, n_loc, n_hist, H, D): ragged tails everywhere, several tiles per branch
+    (1, 300, 200, 333, 2, 128),
+    (2, 129, 65, 64, 3, 128),
+    (3, 1, 1, 1, 1, 128),
+    (4, 257, 130, 0, 2, 128),
+    (5, 200, 97, 250, 2, 64),
+    (6, 64, 64, 64, 1, 64),
+])
+def test_bf16_parity_small(case):
+    seed, n_q, n_loc, n_hist, H, D = case
+    say("case", case)
+    x = inputs.custom_inputs(seed, n_q, n_loc, n_hist, H, D, "bf16", boost_rows=min(8, n_loc))
+    scale = D ** -0.5
+    out = run_decomp(x, scale)
+    rep = check_against_oracle(x, out, scale, TOL_BF16_O, TOL_BF16_LSE)
+    say("report", rep)
+
+
+@pytest.mark.parametrize("case", [(11, 256, 320, 1024, 2, 64), (12, 77, 33, 45, 2, 128), (13, 130, 64, 0, 2, 64)])
+def test_f32_parity_small(case):
+    seed, n_q, n_loc, n_hist, H, D = case
+    say("case", case)
+    x = inputs.custom_inputs(seed, n_q, n_loc, n_hist, H, D, "f32")
+    out = run_decomp(x, D ** -0.5)
+    say("report", check_against_oracle(x, out, D ** -0.5, TOL_F32, TOL_F32))
+
+
+def test_tiny_fp32_config_all_chunks():
+    """The float32 configuration at its full size: every output element of every warmup chunk."""
+    cfg = inputs.CONFIGS[0]
+    for c in range(cfg.n_chunks):
+        say("chunk", c)
+        x = inputs.chunk_inputs(cfg, 0, c)
+        out = run_decomp(x, cfg.scale)
+        check_against_oracle(x, out, cfg.scale, TOL_F32, TOL_F32)
+
+
+@pytest.mark.parametrize("cfg_id", [1, 2, 3])
+def test_bf16_full_size_sampled_rows(cfg_id):
+    """Full-size layers in the benchmark's launch configuration; the oracle checks sampled query rows
+    (first and last tiles, the ragged tail, and random rows) over every head and output."""
+    cfg = inputs.CONFIGS[cfg_id]
+    say("config", cfg.name)
+    x = inputs.chunk_inputs(cfg, 0, 0)
+    out = run_decomp(x, cfg.scale)
+    for name, t in out.items():
+        assert not torch.isnan(t).any().item(), f"{name} has unwritten (NaN) elements"
+    g = np.random.default_rng(cfg_id)
+    rows = np.unique(np.concatenate([np.arange(0, 8), np.arange(cfg.n_q - 80, cfg.n_q),
+                                     g.choice(cfg.n_q, 24, replace=False)]))
+    say("report", check_against_oracle(x, out, cfg.scale, TOL_BF16_O, TOL_BF16_LSE, rows=rows))
+
+
+def test_local_only_mode_is_bitwise_local():
+    """n_hist = 0 (an absorbed L-layer): O_full is bitwise O_loc, LSE_hist = -inf, O_hist = 0."""
+    x = inputs.custom_inputs(21, 200, 150, 0, 2, 128, "bf16")
+    out = run_decomp(x, 128 ** -0.5)
+    assert torch.equal(out["O_full"].view(torch.int16), out["O_loc"].view(torch.int16))
+    assert torch.equal(out["LSE_full"], out["LSE_loc"])
+    assert torch.all(out["O_hist"] == 0).item()
+    assert torch.all(torch.isneginf(out["LSE_hist"])).item()
+
+
+def test_decomp_matches_single_pass():
+    """The merged dual-stream output equals one pass over the concatenated keys (ispa_full_attn)."""
+    x = inputs.custom_inputs(22, 333, 250, 400, 3, 128, "bf16")
+    out = run_decomp(x, 128 ** -0.5)
+    q = dev(x.q)
+    k = torch.cat([dev(x.k_loc), dev(x.k_hist)])
+    v = torch.cat([dev(x.v_loc), dev(x.v_hist)])
+    o = poisoned(q.shape, q.dtype)
+    lse = poisoned((3, 333), torch.float32)
+    ispa.ispa_full_attn(q, k, v, o=o, lse=lse)
+    torch.cuda.synchronize()
+    assert maxabs(host64(o), host64(out["O_full"])) <= 4e-3
+    assert maxabs(lse.cpu().numpy(), out["LSE_full"].cpu().numpy()) <= 1e-4
+    ref = oracle.attention(x.q.f64, np.concatenate([x.k_loc.f64, x.k_hist.f64]),
+                           np.concatenate([x.v_loc.f64, x.v_hist.f64]), 128 ** -0.5)
+    assert maxabs(host64(o), ref[0]) <= TOL_BF16_O
+    assert maxabs(lse.cpu().numpy(), ref[1]) <= TOL_BF16_LSE
+
+
+def test_null_outputs_are_skipped():
+    x = inputs.custom_inputs(23, 100, 70, 90, 2, 128, "bf16")
+    q = dev(x.q)
+    o_full = poisoned(q.shape, q.dtype)
+    ispa.ispa_decomp_attn(q, dev(x.k_loc), dev(x.v_loc), dev(x.k_hist), dev(x.v_hist), o_full=o_full)
+    torch.cuda.synchronize()
+    ref = oracle.branch_outputs(x.q.f64, x.k_loc.f64, x.v_loc.f64, x.k_hist.f64, x.v_hist.f64, 128 ** -0.5)
+    assert maxabs(host64(o_full), ref["O_full"]) <= TOL_BF16_O
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_lse_merge_three_parts(dtype):
+    """Standalone N-way merge of three key ranges equals attention over all of them."""
+    g = inputs.custom_inputs(24, 150, 100, 0, 2, 128, dtype)
+    q = dev(g.q)
+    k, v = g.k_loc.f64, g.v_loc.f64
+    kd, vd = dev(g.k_loc), dev(g.v_loc)
+    parts = [(0, 30), (30, 31), (31, 100)]
+    os_, ls_ = [], []
+    for a, b in parts:
+        o = poisoned(q.shape, q.dtype)
+        l = poisoned((2, 150), torch.float32)
+        ispa.ispa_full_attn(q, kd[a:b].contiguous(), vd[a:b].contiguous(), o=o, lse=l)
+        os_.append(o)
+        ls_.append(l)
+    o_out = poisoned(q.shape, q.dtype)
+    l_out = poisoned((2, 150), torch.float32)
+    ispa.ispa_lse_merge(os_, ls_, o_out, l_out)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.attention(g.q.f64, k, v, 128 ** -0.5)
+    tol_o, tol_l = (TOL_BF16_O, TOL_BF16_LSE) if dtype == "bf16" else (TOL_F32, TOL_F32)
+    assert maxabs(host64(o_out), ref_o) <= tol_o
+    assert maxabs(l_out.cpu().numpy(), ref_l) <= tol_l
+
+
+def test_nan_query_row_stays_in_its_row():
+    x = inputs.custom_inputs(25, 64, 64, 64, 1, 128, "bf16")
+    q = dev(x.q)
+    q[5, 0, 3] = float("nan")
+    o = poisoned(q.shape, q.dtype)
+    ispa.ispa_decomp_attn(q, dev(x.k_loc), dev(x.v_loc), dev(x.k_hist), dev(x.v_hist), o_full=o)
+    torch.cuda.synchronize()
+    bad = torch.isnan(o.float()).any(dim=(1, 2)).cpu().numpy()
+    assert bad[5] and bad.sum() == 1
+
+
+def test_invalid_arguments_raise():
+    x = inputs.custom_inputs(26, 8, 8, 8, 1, 128, "bf16")
+    q = dev(x.q)
+    with pytest.raises(ispa.IspaError):
+        ispa.ispa_decomp_attn(q, dev(x.k_loc)[:0], dev(x.v_loc)[:0])  # n_loc = 0
+    with pytest.raises(ispa.IspaError):
+        ispa.ispa_decomp_attn(q.float(), dev(x.k_loc), dev(x.v_loc))  # dtype mismatch
