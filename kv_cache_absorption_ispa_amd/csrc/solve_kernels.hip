@@ -12,20 +12,23 @@
 //   M = G + lambda I                                   (init kernel)
 //   R = C W, accumulated in float64                    (float64 GEMM)
 //   for each panel k:
-//     factor M_kk = L_kk L_kk^T in LDS, form L_kk^-1  (one workgroup per layer)
+//     factor M_kk = L_kk L_kk^T and invert L_kk       (one workgroup per layer)
 //     L_ik = M_ik L_kk^-T                             (GEMM, in place)
 //     M_ij -= L_ik L_jk^T  (lower tiles only)         (GEMM)
-//   forward:  Y_k = L_kk^-1 Y_k ; Y_i -= L_ik Y_k      (GEMMs)
-//   backward: X_k = L_kk^-T Y_k ; Y_i -= L_ki^T X_k    (GEMMs)
-//   one refinement step: r = R - G X - lambda X in float64, solve again with
-//   the same factor, dW = X + correction.
+//   explicit inverse of L, one block row at a time:
+//     (L^-1)_{i,<i} = -L_ii^-1 L_{i,<i} (L^-1)_{<i,<i} (two GEMMs per block row)
+//   X = L^-T (L^-1 R)                                  (two triangular GEMMs)
+//   one refinement step: r = R - G X - lambda X in float64,
+//   dW = X + L^-T (L^-1 r).
 // The float32 factorisation alone loses about kappa * 2^-24 (about 1e-3 at the
 // conditioning warmup statistics have, 1e5); the refinement step with a
-// float64 residual brings dW to the accuracy of its float32 inputs.
-// The factor and solve GEMMs run on v_mfma_f32_32x32x2_f32 with 64x64 tiles;
-// the float64-accumulated products run on the float64 VALU.  A layer whose
-// pivot fails records info = column + 1 and is skipped by later kernels; its
-// dW is set to NaN at the end and its W_new is left alone.
+// float64 residual brings dW to the accuracy of its float32 inputs.  Forming
+// L^-1 once turns each triangular solve into one GEMM launch instead of one per
+// panel.  The factor, inverse and solve GEMMs run on v_mfma_f32_32x32x2_f32
+// with 64x64 tiles (triangular operands skip their zero blocks); the
+// float64-accumulated products run on the float64 VALU.  A layer whose pivot
+// fails records info = column + 1 and is skipped by later kernels; its dW is
+// set to NaN at the end and its W_new is left alone.
 #include "ispa_internal.h"
 
 namespace ispa {
@@ -43,6 +46,7 @@ struct GemmParams {
   size_t sA, sB, sC, sD;  // batch strides (elements)
   float alpha, beta;
   int lower_only;         // skip 64x64 tiles strictly above the diagonal
+  int kmode;              // 0 all k; 1 op(A) lower: k < m0+64; 2 op(A) upper: k >= m0; 3 op(B) lower: k >= n0
   const int32_t* info;    // skip batch entries with info != 0 (nullable)
 };
 
@@ -64,7 +68,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
   const float* A = p.A + b * p.sA;
   const float* B = p.B + b * p.sB;
   f32x16 acc = f32x16{0};
-  for (int k0 = 0; k0 < p.K; k0 += 16) {
+  const int kb = p.kmode == 2 ? m0 : (p.kmode == 3 ? n0 : 0);
+  const int ke = p.kmode == 1 ? min(p.K, m0 + 64) : p.K;
+  for (int k0 = kb; k0 < ke; k0 += 16) {
     if (!TA) {
       const int m = tid >> 2, kq = tid & 3;
       const f32x4 v = *(const f32x4*)(A + (size_t)(m0 + m) * p.lda + k0 + 4 * kq);
@@ -185,64 +191,99 @@ __global__ __launch_bounds__(256) void init_shift_kernel(const float* __restrict
   *(f32x4*)(M + b * dd + i4) = v;
 }
 
-// Factor the 64x64 diagonal block at (k0, k0) of each layer's M in LDS and
-// form its inverse.  The lower triangle of M's block is overwritten by L_kk.
-__global__ __launch_bounds__(256) void potrf_diag_kernel(float* M, int d, int k0, float* Linv, int32_t* info) {
+// Factor the 64x64 diagonal block at (k0, k0) of each layer's working matrix:
+// M_kk = L L^T, written over M's lower triangle, and L^-1, written into the
+// inverse's diagonal block.  Thread (r = tid/4, cg = tid%4) keeps row r at
+// columns cg, cg+4, ..., cg+60 in registers; each step publishes one column
+// of the Schur complement through LDS (one barrier per column).  The update
+// uses the unscaled complement S: S_ic -= S_ij S_cj / S_jj, and L_ic =
+// S_ic / sqrt(S_cc) at the end (which also gives L_cc = sqrt(S_cc)).
+__global__ __launch_bounds__(256) void potrf_diag_kernel(float* M, int d, int k0, float* Linvf, int32_t* info) {
   const int b = blockIdx.x;
   if (info[b] != 0) return;
-  __shared__ float L[NB][NB + 1];
-  __shared__ float X[NB][NB + 1];
-  __shared__ int fail_col;
-  const int tid = threadIdx.x;
-  float* Mb = M + (size_t)b * d * d;
-  for (int e = tid; e < NB * NB; e += 256) {
-    const int i = e / NB, j = e % NB;
-    L[i][j] = j <= i ? Mb[(size_t)(k0 + i) * d + k0 + j] : 0.f;
+  __shared__ __attribute__((aligned(16))) float col[2][4][16];  // a column, element c stored at [c%4][c/4]
+  __shared__ float piv[NB];
+  __shared__ float Ls[NB][NB + 1];
+  const int tid = threadIdx.x, r = tid >> 2, cg = tid & 3;
+  float* Mb = M + (size_t)b * d * d + (size_t)k0 * d + k0;
+  float a[16];
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    const int c = cg + 4 * m;
+    a[m] = c <= r ? Mb[(size_t)r * d + c] : 0.f;
   }
-  if (tid == 0) fail_col = -1;
-  __syncthreads();
+  int fail = -1;
+#pragma unroll
   for (int j = 0; j < NB; ++j) {
-    if (tid == 0) {
-      const float dj = L[j][j];
-      if (!(dj > 0.f)) fail_col = j;
-      L[j][j] = sqrtf(dj);
+    const int buf = j & 1;
+    if (cg == (j & 3)) col[buf][r & 3][r >> 2] = a[j >> 2];
+    __syncthreads();
+    const float dj = col[buf][j & 3][j >> 2];
+    if (!(dj > 0.f)) {
+      fail = j;
+      break;
     }
-    __syncthreads();
-    if (fail_col >= 0) break;
-    const float piv = L[j][j];
-    for (int i = j + 1 + tid; i < NB; i += 256) L[i][j] /= piv;
-    __syncthreads();
-    const int w = NB - 1 - j;
-    for (int e = tid; e < w * w; e += 256) {
-      const int i = j + 1 + e / w, c = j + 1 + e % w;
-      if (c <= i) L[i][c] = fmaf(-L[i][j], L[c][j], L[i][c]);
+    if (tid == 0) piv[j] = dj;
+    if (r > j) {
+      const float f = col[buf][r & 3][r >> 2] / dj;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 v = *(const f32x4*)(&col[buf][cg][4 * q]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int c = cg + 4 * (4 * q + e);
+          if (c > j && c <= r) a[4 * q + e] = fmaf(-f, v[e], a[4 * q + e]);
+        }
+      }
     }
-    __syncthreads();
   }
-  if (fail_col >= 0) {
-    if (tid == 0) info[b] = k0 + fail_col + 1;
+  if (fail >= 0) {
+    if (tid == 0) info[b] = k0 + fail + 1;
     return;
   }
-  // inverse of the lower-triangular L by forward substitution, one column per thread
-  if (tid < NB) {
-    const int c = tid;
-    for (int i = 0; i < NB; ++i) {
-      if (i < c) {
-        X[i][c] = 0.f;
-        continue;
-      }
-      float s = (i == c) ? 1.f : 0.f;
-      for (int m = c; m < i; ++m) s = fmaf(-L[i][m], X[m][c], s);
-      X[i][c] = s / L[i][i];
-    }
+  __syncthreads();
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    const int c = cg + 4 * m;
+    const float l = c <= r ? a[m] * rsqrtf(piv[c]) : 0.f;
+    Ls[r][c] = l;
+    if (c <= r) Mb[(size_t)r * d + c] = l;
   }
   __syncthreads();
-  float* Lv = Linv + ((size_t)b * (d / NB) + k0 / NB) * NB * NB;
-  for (int e = tid; e < NB * NB; e += 256) {
-    const int i = e / NB, j = e % NB;
-    Lv[e] = X[i][j];
-    if (j <= i) Mb[(size_t)(k0 + i) * d + k0 + j] = L[i][j];
+  // X = L^-1 by forward substitution on the identity, one row of X per step
+  float x[16];
+#pragma unroll
+  for (int m = 0; m < 16; ++m) x[m] = (cg + 4 * m == r) ? 1.f : 0.f;
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int buf = i & 1;
+    if (r == i) {
+      const float inv = 1.f / Ls[i][i];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[4 * q + e] *= inv;
+          v[e] = x[4 * q + e];
+        }
+        *(f32x4*)(&col[buf][cg][4 * q]) = v;
+      }
+    }
+    __syncthreads();
+    if (r > i) {
+      const float lri = Ls[r][i];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 v = *(const f32x4*)(&col[buf][cg][4 * q]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[4 * q + e] = fmaf(-lri, v[e], x[4 * q + e]);
+      }
+    }
   }
+  float* Xb = Linvf + (size_t)b * d * d + (size_t)k0 * d + k0;
+#pragma unroll
+  for (int m = 0; m < 16; ++m) Xb[(size_t)r * d + cg + 4 * m] = x[m];
 }
 
 // dW = X + correction, or NaN for failed layers; W_new = W + dW for the others (W_new may be W).
@@ -294,7 +335,7 @@ __global__ __launch_bounds__(256) void eps_reduce_kernel(const float* W, const f
 template <bool TA, bool TB>
 ispa_status_t gemm(hipStream_t s, int batch, int M, int N, int K, const float* A, int lda, size_t sA, const float* B,
                    int ldb, size_t sB, const float* Cin, int ldc, size_t sC, float* D, int ldd, size_t sD, float alpha,
-                   float beta, bool lower_only, const int32_t* info) {
+                   float beta, bool lower_only, const int32_t* info, int kmode = 0) {
   if (M <= 0 || N <= 0 || K <= 0) return ISPA_OK;
   GemmParams p;
   p.A = A; p.B = B; p.Cin = Cin; p.D = D;
@@ -303,6 +344,7 @@ ispa_status_t gemm(hipStream_t s, int batch, int M, int N, int K, const float* A
   p.sA = sA; p.sB = sB; p.sC = sC; p.sD = sD;
   p.alpha = alpha; p.beta = beta;
   p.lower_only = lower_only ? 1 : 0;
+  p.kmode = kmode;
   p.info = info;
   const dim3 grid(N / 64, M / 64, batch), block(256);
   hipLaunchKernelGGL((gemm_f32_kernel<TA, TB>), grid, block, 0, s, p);
@@ -334,47 +376,25 @@ ispa_status_t gemm_d(hipStream_t s, int batch, int M, int N, int K, const float*
 
 size_t absorb_workspace_size(int32_t d, int32_t d_out, int32_t batch) {
   const size_t b = (size_t)batch;
-  return b * d * d * sizeof(float)               // factor
-         + b * d * NB * sizeof(float)            // inverses of the diagonal blocks
-         + b * d * d_out * sizeof(double)        // R = C W in float64
-         + b * d * d_out * sizeof(float);        // residual / correction
+  return b * d * d * sizeof(float)          // factor L (lower triangle of M)
+         + b * d * d * sizeof(float)        // L^-1
+         + b * NB * d * sizeof(float)       // one block row of intermediate products
+         + b * d * d_out * sizeof(double)   // R = C W in float64
+         + 2 * b * d * d_out * sizeof(float);  // residual / correction and an intermediate
 }
 
 namespace {
 
-// Y <- (L L^T)^-1 Y in place, with the blocked factor L (lower triangle of M) and
-// the inverses of its diagonal blocks.
-ispa_status_t chol_solve_inplace(hipStream_t s, int batch, int d, int d_out, const float* M, const float* Linv,
-                                 float* Y, const int32_t* info) {
+constexpr int KM_LOWER_A = 1, KM_UPPER_A = 2, KM_LOWER_B = 3;
+
+// Y_out <- L^-T (L^-1 Y_in) with the explicit inverse; Z is scratch (d x d_out).
+ispa_status_t chol_apply(hipStream_t s, int batch, int d, int d_out, const float* Linvf, const float* Yin, float* Z,
+                         float* Yout, const int32_t* info) {
   const size_t dd = (size_t)d * d, dn = (size_t)d * d_out;
-  const int nblk = d / NB;
-  const size_t sL = (size_t)nblk * NB * NB;
-  for (int k = 0; k < nblk; ++k) {  // forward: L Z = Y
-    const int k0 = k * NB;
-    float* Yk = Y + (size_t)k0 * d_out;
-    const float* Lkk_inv = Linv + (size_t)k * NB * NB;
-    ISPA_TRY((gemm<false, false>(s, batch, NB, d_out, NB, Lkk_inv, NB, sL, Yk, d_out, dn, nullptr, 0, 0, Yk, d_out,
-                                 dn, 1.f, 0.f, false, info)));
-    const int rest = d - k0 - NB;
-    if (rest > 0) {
-      const float* Lik = M + (size_t)(k0 + NB) * d + k0;
-      float* Yi = Y + (size_t)(k0 + NB) * d_out;
-      ISPA_TRY((gemm<false, false>(s, batch, rest, d_out, NB, Lik, d, dd, Yk, d_out, dn, Yi, d_out, dn, Yi, d_out, dn,
-                                   -1.f, 1.f, false, info)));
-    }
-  }
-  for (int k = nblk - 1; k >= 0; --k) {  // backward: L^T X = Z
-    const int k0 = k * NB;
-    float* Xk = Y + (size_t)k0 * d_out;
-    const float* Lkk_inv = Linv + (size_t)k * NB * NB;
-    ISPA_TRY((gemm<true, false>(s, batch, NB, d_out, NB, Lkk_inv, NB, sL, Xk, d_out, dn, nullptr, 0, 0, Xk, d_out, dn,
-                                1.f, 0.f, false, info)));
-    if (k0 > 0) {
-      const float* Lki = M + (size_t)k0 * d;  // rows k0..k0+63, cols 0..k0-1; used transposed
-      ISPA_TRY((gemm<true, false>(s, batch, k0, d_out, NB, Lki, d, dd, Xk, d_out, dn, Y, d_out, dn, Y, d_out, dn, -1.f,
-                                  1.f, false, info)));
-    }
-  }
+  ISPA_TRY((gemm<false, false>(s, batch, d, d_out, d, Linvf, d, dd, Yin, d_out, dn, nullptr, 0, 0, Z, d_out, dn, 1.f,
+                               0.f, false, info, KM_LOWER_A)));
+  ISPA_TRY((gemm<true, false>(s, batch, d, d_out, d, Linvf, d, dd, Z, d_out, dn, nullptr, 0, 0, Yout, d_out, dn, 1.f,
+                              0.f, false, info, KM_UPPER_A)));
   return ISPA_OK;
 }
 
@@ -390,40 +410,50 @@ ispa_status_t launch_absorb(int32_t d, int32_t d_out, int32_t batch, const float
   }
   const size_t dd = (size_t)d * d, dn = (size_t)d * d_out;
   float* M = (float*)ws;
-  float* Linv = M + (size_t)batch * dd;
-  double* R64 = (double*)(Linv + (size_t)batch * d * NB);
+  float* Linvf = M + (size_t)batch * dd;
+  float* Tb = Linvf + (size_t)batch * dd;
+  double* R64 = (double*)(Tb + (size_t)batch * NB * d);
   float* Rr = (float*)(R64 + (size_t)batch * dn);
+  float* Zb = Rr + (size_t)batch * dn;
   const int nblk = d / NB;
 
   hipLaunchKernelGGL(init_shift_kernel, dim3((unsigned)((dd / 4 + 255) / 256), batch), dim3(256), 0, s, G, M, d,
                      lambda, info);
   ISPA_TRY(hip_check(hipGetLastError(), "init_shift_kernel launch"));
-  // R = C W (float64 accumulation), kept in float64 and rounded into dW as the first right-hand side
-  ISPA_TRY(gemm_d(s, batch, d, d_out, d, C, d, dd, W, d_out, dn, nullptr, 0, 0, nullptr, 0, 0, R64, dW, d_out, dn,
+  // R = C W (float64 accumulation), kept in float64 and rounded into Rr as the first right-hand side
+  ISPA_TRY(gemm_d(s, batch, d, d_out, d, C, d, dd, W, d_out, dn, nullptr, 0, 0, nullptr, 0, 0, R64, Rr, d_out, dn,
                   1.0, 0.0, 0.0, nullptr));
-  // Cholesky
+  // Cholesky, right-looking by 64-column panels
   for (int k = 0; k < nblk; ++k) {
     const int k0 = k * NB;
-    hipLaunchKernelGGL(potrf_diag_kernel, dim3(batch), dim3(256), 0, s, M, d, k0, Linv, info);
+    hipLaunchKernelGGL(potrf_diag_kernel, dim3(batch), dim3(256), 0, s, M, d, k0, Linvf, info);
     ISPA_TRY(hip_check(hipGetLastError(), "potrf_diag_kernel launch"));
     const int rest = d - k0 - NB;
     if (rest <= 0) break;
     float* panel = M + (size_t)(k0 + NB) * d + k0;
-    const float* Lkk_inv = Linv + (size_t)k * NB * NB;
+    const float* Lkk_inv = Linvf + (size_t)k0 * d + k0;
     // L_ik = M_ik L_kk^-T (in place)
-    ISPA_TRY((gemm<false, true>(s, batch, rest, NB, NB, panel, d, dd, Lkk_inv, NB, (size_t)nblk * NB * NB, nullptr,
-                                0, 0, panel, d, dd, 1.f, 0.f, false, info)));
+    ISPA_TRY((gemm<false, true>(s, batch, rest, NB, NB, panel, d, dd, Lkk_inv, d, dd, nullptr, 0, 0, panel, d, dd,
+                                1.f, 0.f, false, info)));
     // trailing update, lower tiles
     float* trail = M + (size_t)(k0 + NB) * d + k0 + NB;
     ISPA_TRY((gemm<false, true>(s, batch, rest, rest, NB, panel, d, dd, panel, d, dd, trail, d, dd, trail, d, dd, -1.f,
                                 1.f, true, info)));
   }
+  // explicit L^-1, block row by block row: T = L_{i,<i} (L^-1)_{<i,<i}; (L^-1)_{i,<i} = -L_ii^-1 T
+  for (int i = 1; i < nblk; ++i) {
+    const int i0 = i * NB;
+    ISPA_TRY((gemm<false, false>(s, batch, NB, i0, i0, M + (size_t)i0 * d, d, dd, Linvf, d, dd, nullptr, 0, 0, Tb, d,
+                                 (size_t)NB * d, 1.f, 0.f, false, info, KM_LOWER_B)));
+    ISPA_TRY((gemm<false, false>(s, batch, NB, i0, NB, Linvf + (size_t)i0 * d + i0, d, dd, Tb, d, (size_t)NB * d,
+                                 nullptr, 0, 0, Linvf + (size_t)i0 * d, d, dd, -1.f, 0.f, false, info)));
+  }
   // X = (L L^T)^-1 R
-  ISPA_TRY(chol_solve_inplace(s, batch, d, d_out, M, Linv, dW, info));
+  ISPA_TRY(chol_apply(s, batch, d, d_out, Linvf, Rr, Zb, dW, info));
   // refinement: r = R - G X - lambda X (float64), correction = (L L^T)^-1 r
   ISPA_TRY(gemm_d(s, batch, d, d_out, d, G, d, dd, dW, d_out, dn, R64, d_out, dn, dW, d_out, dn, nullptr, Rr, d_out,
                   dn, -1.0, 1.0, -(double)lambda, info));
-  ISPA_TRY(chol_solve_inplace(s, batch, d, d_out, M, Linv, Rr, info));
+  ISPA_TRY(chol_apply(s, batch, d, d_out, Linvf, Rr, Zb, Rr, info));
   hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)((dn / 4 + 255) / 256), batch), dim3(256), 0, s, W, dW,
                      (const float*)Rr, W_new, dn, (const int32_t*)info);
   return hip_check(hipGetLastError(), "finalize_kernel launch");
