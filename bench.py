@@ -43,7 +43,9 @@ def parse():
     ap.add_argument("--config", type=int, default=1, help="layer shape (1: Wan-1.3B, 2: long history, 3: Wan-14B)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU seconds for the oracle sample")
-    ap.add_argument("--traffic", type=str, default=os.path.join(ROOT, "profiles", "traffic.json"),
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES bytes (calibrates HBM byte counters)")
+    ap.add_argument("--traffic", type=str, default=os.path.join(ROOT, "profiles", "attn_bf16_kernel_wan1.3b_hbm_traffic.json"),
                     help="measured HBM traffic of the attention kernel (from rocprofv3 counters), if present")
     return ap.parse_args()
 
@@ -62,6 +64,14 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.copy_probe:
+        src = torch.empty(args.copy_probe, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": args.copy_probe, "launches": 3}), flush=True)
+        return
     ispa.load_library()
     ispa.ispa_device_check(0)
     cfg = inputs.CONFIGS[args.config]
