@@ -28,6 +28,8 @@
 //    runs in registers from the float32 O_loc and O_full is rounded once.
 //  * Scores are scaled by scale*log2(e) and exponentiated with v_exp_f32
 //    (2^x); LSE is exported in natural log.
+#include <cstdlib>
+
 #include "ispa_internal.h"
 
 namespace ispa {
@@ -57,8 +59,29 @@ struct AttnKParams {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnKParams p) {
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int RSRC_DW3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
+
+// Buffer resource over `bytes` bytes: loads at offsets >= bytes return 0 (hardware range check),
+// which masks the ragged last tile of each branch without branches.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* ptr, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(ptr), (short)0, (int)bytes, RSRC_DW3);
+}
+
+// Value held by the lane 32 away (the other half of the wave), via v_permlane32_swap.
+__device__ __forceinline__ float other_half(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (threadIdx.x & 32) ? r[0] : r[1]);
+}
+
+__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
+
+// QB = 32-query blocks per wave (1: 32 queries, two waves per SIMD; 2: 64 queries, one wave per SIMD
+// with half the LDS traffic per FLOP).
+template <int D, int NW, int QB>
+__global__ __launch_bounds__(NW * 64, (QB == 1 && NW <= 4) ? 2 : 1) void attn_bf16_kernel(AttnKParams p) {
   constexpr int NT = NW * 64;
   constexpr int KS = D + 8;   // K tile row stride (elements): rows 16 B apart in bank space
   constexpr int VS = BN + 8;  // V^T tile row stride (elements)
@@ -69,6 +92,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnKParams p) {
   static_assert(KC >= 1 && KC * NT * 8 == BN * D, "K tile split");
   constexpr int VITEMS = (BN / 8) * (D / 4);  // (8 keys x 4 dims) V items per tile
   constexpr int VI = (VITEMS + NT - 1) / NT;
+  constexpr int BM = NW * 32 * QB;
+  // The running max used as the exponent reference is raised only when a new
+  // score exceeds it by more than 2^8: p then stays below 2^8, and the
+  // accumulator rescale (D multiplies per query) is skipped on most tiles.
+  constexpr float RESCALE_T = 8.0f;
 
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * KS];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * VS];
@@ -78,52 +106,68 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnKParams p) {
   const int l32 = lane & 31, hh = lane >> 5;
   const uint32_t unit = xcd_remap(blockIdx.x, p.nblocks);
   const int head = unit / p.n_qtiles, qt = unit % p.n_qtiles;
-  const size_t HD = (size_t)p.heads * D;
-  const int myq = qt * (NW * 32) + wave * 32 + l32;
-  const bool qvalid = myq < p.n_q;
-  const int Tl = (p.n_loc + BN - 1) / BN;
-  const int Th = (p.n_hist + BN - 1) / BN;
+  const int n_q = p.n_q, n_loc = p.n_loc, n_hist = p.n_hist;
+  const uint32_t HD = (uint32_t)p.heads * D;
+  const uint32_t row_bytes = HD * 2u;
+  const float c2 = p.c2;
+  const int Tl = (n_loc + BN - 1) / BN;
+  const int Th = (n_hist + BN - 1) / BN;
   const int T = Tl + Th;
+  const rsrc_t rKl = make_rsrc(p.Kl, (uint32_t)n_loc * row_bytes);
+  const rsrc_t rVl = make_rsrc(p.Vl, (uint32_t)n_loc * row_bytes);
+  const rsrc_t rKh = make_rsrc(p.Kh, (uint32_t)n_hist * row_bytes);
+  const rsrc_t rVh = make_rsrc(p.Vh, (uint32_t)n_hist * row_bytes);
+
+  int myq[QB];
+  bool qvalid[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    myq[qb] = qt * BM + wave * 32 * QB + qb * 32 + l32;
+    qvalid[qb] = myq[qb] < n_q;
+  }
 
   // Q^T fragments (B operand of S^T = K Q^T): lane holds q[myq][16kk + 8hh .. +7].
-  bf16x8 qf[KK];
-  {
-    const uint16_t* qp = p.Q + (size_t)(qvalid ? myq : 0) * HD + head * D + 8 * hh;
+  bf16x8 qf[QB][KK];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const uint16_t* qp = p.Q + (size_t)(qvalid[qb] ? myq[qb] : 0) * HD + head * D + 8 * hh;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      u32x4 v = qvalid ? *(const u32x4*)(qp + 16 * kk) : u32x4{0, 0, 0, 0};
-      qf[kk] = __builtin_bit_cast(bf16x8, v);
+      const u32x4 v = qvalid[qb] ? *(const u32x4*)(qp + 16 * kk) : u32x4{0, 0, 0, 0};
+      qf[qb][kk] = __builtin_bit_cast(bf16x8, v);
     }
+  }
+
+  // per-thread byte offsets of the tile loads (the tile's key0 * row_bytes is added per tile)
+  uint32_t kofs[KC];
+#pragma unroll
+  for (int i = 0; i < KC; ++i) {
+    const int c = tid + i * NT;
+    kofs[i] = (uint32_t)(c / (D / 8)) * row_bytes + (uint32_t)(head * D + (c % (D / 8)) * 8) * 2u;
+  }
+  uint32_t vofs[VI];
+#pragma unroll
+  for (int i = 0; i < VI; ++i) {
+    const int it = tid + i * NT;
+    vofs[i] = (uint32_t)((it % (BN / 8)) * 8) * row_bytes + (uint32_t)(head * D + (it / (BN / 8)) * 4) * 2u;
   }
 
   u32x4 kreg[KC];
   u32x2 vreg[VI][8];
 
   auto load_tile = [&](int t) {
-    const uint16_t* Kp;
-    const uint16_t* Vp;
-    int key0, nvalid;
-    if (t < Tl) {
-      Kp = p.Kl; Vp = p.Vl; key0 = t * BN; nvalid = p.n_loc;
-    } else {
-      Kp = p.Kh; Vp = p.Vh; key0 = (t - Tl) * BN; nvalid = p.n_hist;
-    }
+    const bool loc = t < Tl;
+    const uint32_t tb = (uint32_t)((loc ? t : t - Tl) * BN) * row_bytes;
+    const rsrc_t rk = loc ? rKl : rKh;
+    const rsrc_t rv = loc ? rVl : rVh;
 #pragma unroll
-    for (int i = 0; i < KC; ++i) {
-      const int c = tid + i * NT;
-      const int row = c / (D / 8), col8 = c % (D / 8);
-      const int key = key0 + row;
-      kreg[i] = key < nvalid ? *(const u32x4*)(Kp + (size_t)key * HD + head * D + col8 * 8) : u32x4{0, 0, 0, 0};
-    }
+    for (int i = 0; i < KC; ++i) kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, kofs[i] + tb, 0, 0);
 #pragma unroll
     for (int i = 0; i < VI; ++i) {
-      const int it = tid + i * NT;
-      const int kg = it % (BN / 8), dq = it / (BN / 8);
+      if (VITEMS % NT == 0 || tid + i * NT < VITEMS) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int key = key0 + kg * 8 + e;
-        vreg[i][e] = (it < VITEMS && key < nvalid) ? *(const u32x2*)(Vp + (size_t)key * HD + head * D + dq * 4)
-                                                    : u32x2{0, 0};
+        for (int e = 0; e < 8; ++e)
+          vreg[i][e] = __builtin_amdgcn_raw_buffer_load_b64(rv, vofs[i] + tb + (uint32_t)e * row_bytes, 0, 0);
       }
     }
   };
@@ -132,13 +176,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnKParams p) {
 #pragma unroll
     for (int i = 0; i < KC; ++i) {
       const int c = tid + i * NT;
-      const int row = c / (D / 8), col8 = c % (D / 8);
-      *(u32x4*)(&sK[buf][row * KS + col8 * 8]) = kreg[i];
+      *(u32x4*)(&sK[buf][(c / (D / 8)) * KS + (c % (D / 8)) * 8]) = kreg[i];
     }
 #pragma unroll
     for (int i = 0; i < VI; ++i) {
       const int it = tid + i * NT;
-      if (it < VITEMS) {
+      if (VITEMS % NT == 0 || it < VITEMS) {
         const int kg = it % (BN / 8), dq = it / (BN / 8);
         // Key 8kg+e of the tile goes to position sigma(8kg+e); sigma swaps bits
         // 2 and 3 inside each 16-key group, so keys e=0..3 land at pos0+0..3
@@ -151,7 +194,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnKParams p) {
           for (int x = 0; x < 4; ++x) {
             const uint32_t a = (dd < 2) ? vreg[i][2 * x].x : vreg[i][2 * x].y;
             const uint32_t b = (dd < 2) ? vreg[i][2 * x + 1].x : vreg[i][2 * x + 1].y;
-            w[x] = (dd & 1) ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
+            w[x] = (dd & 1) ? pack_hi(a, b) : pack_lo(a, b);
           }
           uint16_t* row = &sV[buf][(dq * 4 + dd) * VS];
           *(u32x2*)(row + pos0) = u32x2{w[0], w[1]};
@@ -161,26 +204,55 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnKParams p) {
     }
   };
 
-  // Online-softmax state of the current branch (log2 domain).
-  f32x16 acc[DB];
-  float m = -INFINITY, l = 0.f;
+  // Online-softmax state per query block (log2 domain): reference max m, sum l, accumulator.
+  f32x16 acc[QB][DB];
+  float m[QB], l[QB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) acc[db] = f32x16{0};
+  for (int qb = 0; qb < QB; ++qb) {
+    m[qb] = -INFINITY;
+    l[qb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[qb][db] = f32x16{0};
+  }
+
+  // LDS fragment reads run two ahead of the MFMAs that consume them
+  // (sched_barrier keeps the compiler from sinking them next to their use).
+  constexpr int NS = NKB * KK;      // K fragments per tile: (kb, kk), chains of the NKB accumulators interleaved
+  constexpr int NV = DB * NKB * 2;  // V fragments per tile: (db, kb, mm), DB accumulators interleaved
+  auto kfrag = [&](int buf, int i) {
+    const int kb = i % NKB, kk = i / NKB;
+    return __builtin_bit_cast(bf16x8, *(const u32x4*)(&sK[buf][(kb * 32 + l32) * KS + 8 * hh + 16 * kk]));
+  };
+  auto vfrag = [&](int buf, int i) {
+    const int db = i % DB, j = i / DB, kb = j / 2, mm = j % 2;
+    return __builtin_bit_cast(bf16x8, *(const u32x4*)(&sV[buf][(db * 32 + l32) * VS + 8 * hh + kb * 32 + 16 * mm]));
+  };
 
   auto compute_tile = [&](int buf, int t) {
     const int key0 = (t < Tl ? t : t - Tl) * BN;
-    const int nvalid = t < Tl ? p.n_loc : p.n_hist;
-    f32x16 s[NKB];
+    const int nvalid = t < Tl ? n_loc : n_hist;
+    f32x16 s[QB][NKB];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      s[kb] = f32x16{0};
-      const uint16_t* kr = &sK[buf][(kb * 32 + l32) * KS + 8 * hh];
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const bf16x8 kf = __builtin_bit_cast(bf16x8, *(const u32x4*)(kr + 16 * kk));
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s[kb], 0, 0, 0);
-      }
+      for (int kb = 0; kb < NKB; ++kb) s[qb][kb] = f32x16{0};
+    bf16x8 kf[3];
+    kf[0] = kfrag(buf, 0);
+    kf[1] = kfrag(buf, 1);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      if (i + 2 < NS) kf[(i + 2) % 3] = kfrag(buf, i + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      const int kb = i % NKB, kk = i / NKB;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % 3], qf[qb][kk], s[qb][kb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    // the first V fragments do not depend on P: start reading them before the softmax
+    bf16x8 vf[3];
+    vf[0] = vfrag(buf, 0);
+    vf[1] = vfrag(buf, 1);
     // Accumulator element v of lane (query, hh) in key block kb is key
     // kb*32 + 8*(v/4) + 4*hh + v%4.  Mask keys past the branch's end.
     if (key0 + BN > nvalid) {
@@ -189,75 +261,88 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnKParams p) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int key = key0 + kb * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
-          if (key >= nvalid) s[kb][v] = -INFINITY;
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            if (key >= nvalid) s[qb][kb][v] = -INFINITY;
         }
     }
-    float mx = -INFINITY;
+    u32x4 pk[QB][NKB][2];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int qb = 0; qb < QB; ++qb) {
+      // row max as a tree (the halves' partial maxima are exchanged once)
+      float mt[4];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mnew = fmaxf(m, mx * p.c2);
-    const float alpha = fast_exp2(m - mnew);
-    m = mnew;
-    float ls = 0.f;
-    u32x4 pk[NKB][2];
+      for (int r = 0; r < 4; ++r) mt[r] = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int mm = 0; mm < 2; ++mm) {
-        uint32_t w[4];
+        for (int v = 0; v < 16; ++v) mt[v & 3] = fmaxf(mt[v & 3], s[qb][kb][v]);
+      float mx = fmaxf(fmaxf(mt[0], mt[1]), fmaxf(mt[2], mt[3]));
+      mx = fmaxf(mx, other_half(mx)) * c2;
+      if (__builtin_amdgcn_ballot_w64(mx > m[qb] + RESCALE_T) != 0) {
+        const float mnew = fmaxf(m[qb], mx);
+        const float alpha = fast_exp2(m[qb] - mnew);
+        m[qb] = mnew;
+        l[qb] *= alpha;
 #pragma unroll
-        for (int j = 0; j < 8; j += 2) {
-          const float p0 = fast_exp2(fmaf(s[kb][8 * mm + j], p.c2, -mnew));
-          const float p1 = fast_exp2(fmaf(s[kb][8 * mm + j + 1], p.c2, -mnew));
-          ls += p0 + p1;
-          const bf16x2 b = {(__bf16)p0, (__bf16)p1};
-          w[j >> 1] = __builtin_bit_cast(uint32_t, b);
-        }
-        pk[kb][mm] = u32x4{w[0], w[1], w[2], w[3]};
+        for (int db = 0; db < DB; ++db) acc[qb][db] *= alpha;
       }
-    l = fmaf(l, alpha, ls);
-#pragma unroll
-    for (int db = 0; db < DB; ++db) acc[db] *= alpha;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const uint16_t* vr = &sV[buf][(db * 32 + l32) * VS + 8 * hh];
+      const float mref = m[qb];
+      float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm) {
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, *(const u32x4*)(vr + kb * 32 + 16 * mm));
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, __builtin_bit_cast(bf16x8, pk[kb][mm]), acc[db],
-                                                            0, 0, 0);
+          uint32_t w[4];
+#pragma unroll
+          for (int j = 0; j < 8; j += 2) {
+            const float p0 = fast_exp2(fmaf(s[qb][kb][8 * mm + j], c2, -mref));
+            const float p1 = fast_exp2(fmaf(s[qb][kb][8 * mm + j + 1], c2, -mref));
+            ls[j >> 1] += p0 + p1;
+            const bf16x2 b = {(__bf16)p0, (__bf16)p1};
+            w[j >> 1] = __builtin_bit_cast(uint32_t, b);
+          }
+          pk[qb][kb][mm] = u32x4{w[0], w[1], w[2], w[3]};
         }
+      l[qb] += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      if (i + 2 < NV) vf[(i + 2) % 3] = vfrag(buf, i + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      const int db = i % DB, j = i / DB, kb = j / 2, mm = j % 2;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % 3], __builtin_bit_cast(bf16x8, pk[qb][kb][mm]),
+                                                              acc[qb][db], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   // O^T accumulator element v of lane (query, hh) in block db is dim 32db + 8(v/4) + 4hh + v%4.
-  auto write_o = [&](uint16_t* O, const u32x2 (&vals)[DB][4]) {
-    if (O == nullptr || !qvalid) return;
-    uint16_t* op = O + (size_t)myq * HD + head * D + 4 * hh;
+  auto write_o = [&](uint16_t* O, int qb, const u32x2 (&vals)[DB][4]) {
+    if (O == nullptr || !qvalid[qb]) return;
+    uint16_t* op = O + (size_t)myq[qb] * HD + head * D + 4 * hh;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) *(u32x2*)(op + 32 * db + 8 * g) = vals[db][g];
   };
-  auto pack_acc = [&](u32x2 (&out)[DB][4], float scale_by) {
+  auto pack_acc = [&](u32x2 (&out)[DB][4], int qb, float scale_by) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const bf16x2 a = {(__bf16)(acc[db][4 * g] * scale_by), (__bf16)(acc[db][4 * g + 1] * scale_by)};
-        const bf16x2 b = {(__bf16)(acc[db][4 * g + 2] * scale_by), (__bf16)(acc[db][4 * g + 3] * scale_by)};
+        const bf16x2 a = {(__bf16)(acc[qb][db][4 * g] * scale_by), (__bf16)(acc[qb][db][4 * g + 1] * scale_by)};
+        const bf16x2 b = {(__bf16)(acc[qb][db][4 * g + 2] * scale_by), (__bf16)(acc[qb][db][4 * g + 3] * scale_by)};
         out[db][g] = u32x2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
       }
   };
+  auto lse_store = [&](float* L, int qb, float v2) {
+    if (L && hh == 0 && qvalid[qb]) L[(size_t)head * n_q + myq[qb]] = v2 * LN2;
+  };
 
-  float lse2_loc = -INFINITY;
-  float* const stash = p.stash + (size_t)(qvalid ? myq : 0) * HD + head * D + 4 * hh;
-
+  float lse2_loc[QB];
   load_tile(0);
   store_tile(0);
   __syncthreads();
@@ -266,75 +351,85 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnKParams p) {
     compute_tile(t & 1, t);
     if (t == Tl - 1) {
       // local branch done: normalise, write O_loc / LSE_loc, keep float32 O_loc for the merge
-      const float lt = l + __shfl_xor(l, 32);
-      const float inv = 1.0f / lt;
-      lse2_loc = m + __log2f(lt);
-      u32x2 oloc[DB][4];
-      pack_acc(oloc, inv);
-      write_o(p.O_loc, oloc);
-      if (p.LSE_loc && hh == 0 && qvalid) p.LSE_loc[(size_t)head * p.n_q + myq] = lse2_loc * LN2;
-      if (Th == 0) {
-        // local-attention mode: the full output is the local one, bit for bit
-        write_o(p.O_full, oloc);
-        if (p.LSE_full && hh == 0 && qvalid) p.LSE_full[(size_t)head * p.n_q + myq] = lse2_loc * LN2;
-      } else if (p.O_full && qvalid) {
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+      for (int qb = 0; qb < QB; ++qb) {
+        const float lt = l[qb] + other_half(l[qb]);
+        const float inv = 1.0f / lt;
+        lse2_loc[qb] = m[qb] + __log2f(lt);
+        u32x2 oloc[DB][4];
+        pack_acc(oloc, qb, inv);
+        write_o(p.O_loc, qb, oloc);
+        lse_store(p.LSE_loc, qb, lse2_loc[qb]);
+        if (Th == 0) {
+          // local-attention mode: the full output is the local one, bit for bit
+          write_o(p.O_full, qb, oloc);
+          lse_store(p.LSE_full, qb, lse2_loc[qb]);
+        } else if (p.O_full && qvalid[qb]) {
+          float* stash = p.stash + (size_t)myq[qb] * HD + head * D + 4 * hh;
 #pragma unroll
-          for (int g = 0; g < 4; ++g)
-            *(f32x4*)(stash + 32 * db + 8 * g) = f32x4{acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv,
-                                                      acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv};
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+              *(f32x4*)(stash + 32 * db + 8 * g) = f32x4{acc[qb][db][4 * g] * inv, acc[qb][db][4 * g + 1] * inv,
+                                                         acc[qb][db][4 * g + 2] * inv, acc[qb][db][4 * g + 3] * inv};
+        }
+        m[qb] = -INFINITY;
+        l[qb] = 0.f;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[qb][db] = f32x16{0};
       }
-      m = -INFINITY;
-      l = 0.f;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) acc[db] = f32x16{0};
     }
     if (t + 1 < T) store_tile((t + 1) & 1);
     __syncthreads();
   }
 
-  if (Th > 0) {
-    const float lt = l + __shfl_xor(l, 32);
-    const float inv = 1.0f / lt;
-    const float lse2_hist = m + __log2f(lt);
-    if (p.O_hist) {
-      u32x2 oh[DB][4];
-      pack_acc(oh, inv);
-      write_o(p.O_hist, oh);
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    if (Th > 0) {
+      const float lt = l[qb] + other_half(l[qb]);
+      const float inv = 1.0f / lt;
+      const float lse2_hist = m[qb] + __log2f(lt);
+      if (p.O_hist) {
+        u32x2 oh[DB][4];
+        pack_acc(oh, qb, inv);
+        write_o(p.O_hist, qb, oh);
+      }
+      lse_store(p.LSE_hist, qb, lse2_hist);
+      // merge: LSE = logaddexp(LSE_loc, LSE_hist); O = w_loc O_loc + w_hist O_hist
+      const float mx = fmaxf(lse2_loc[qb], lse2_hist);
+      const float lse2 = mx + __log2f(fast_exp2(lse2_loc[qb] - mx) + fast_exp2(lse2_hist - mx));
+      const float wl = fast_exp2(lse2_loc[qb] - lse2);
+      const float wh = fast_exp2(lse2_hist - lse2) * inv;
+      if (p.O_full && qvalid[qb]) {
+        const float* stash = p.stash + (size_t)myq[qb] * HD + head * D + 4 * hh;
+        u32x2 of[DB][4];
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 ol = *(const f32x4*)(stash + 32 * db + 8 * g);
+            float x[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = fmaf(wl, ol[e], wh * acc[qb][db][4 * g + e]);
+            const bf16x2 a = {(__bf16)x[0], (__bf16)x[1]};
+            const bf16x2 b = {(__bf16)x[2], (__bf16)x[3]};
+            of[db][g] = u32x2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
+          }
+        write_o(p.O_full, qb, of);
+      }
+      lse_store(p.LSE_full, qb, lse2);
+    } else {
+      if (p.O_hist) {
+        u32x2 z[DB][4];
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) z[db][g] = u32x2{0, 0};
+        write_o(p.O_hist, qb, z);
+      }
+      if (p.LSE_hist && hh == 0 && qvalid[qb]) p.LSE_hist[(size_t)head * n_q + myq[qb]] = -INFINITY;
     }
-    if (p.LSE_hist && hh == 0 && qvalid) p.LSE_hist[(size_t)head * p.n_q + myq] = lse2_hist * LN2;
-    // merge: LSE = logaddexp(LSE_loc, LSE_hist); O = w_loc O_loc + w_hist O_hist
-    const float mx = fmaxf(lse2_loc, lse2_hist);
-    const float lse2 = mx + __log2f(fast_exp2(lse2_loc - mx) + fast_exp2(lse2_hist - mx));
-    const float wl = fast_exp2(lse2_loc - lse2);
-    const float wh = fast_exp2(lse2_hist - lse2) * inv;
-    if (p.O_full && qvalid) {
-      u32x2 of[DB][4];
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 ol = *(const f32x4*)(stash + 32 * db + 8 * g);
-          float x[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) x[e] = fmaf(wl, ol[e], wh * acc[db][4 * g + e]);
-          const bf16x2 a = {(__bf16)x[0], (__bf16)x[1]};
-          const bf16x2 b = {(__bf16)x[2], (__bf16)x[3]};
-          of[db][g] = u32x2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
-        }
-      write_o(p.O_full, of);
-    }
-    if (p.LSE_full && hh == 0 && qvalid) p.LSE_full[(size_t)head * p.n_q + myq] = lse2 * LN2;
-  } else if (p.O_hist) {
-    u32x2 z[DB][4];
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) z[db][g] = u32x2{0, 0};
-    write_o(p.O_hist, z);
   }
-  if (Th == 0 && p.LSE_hist && hh == 0 && qvalid) p.LSE_hist[(size_t)head * p.n_q + myq] = -INFINITY;
 }
 
 // ----------------------------------------------------------------------------
@@ -518,7 +613,32 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(MergeParams p) {
 
 }  // namespace
 
-constexpr int ATTN_NW = 4;
+// Launch shape of the bf16 kernel: waves per workgroup x 32-query blocks per wave.
+// Default 8 waves x 32 queries (256 queries share each staged K/V tile; two
+// waves per SIMD).  ISPA_ATTN_SHAPE = "4x1", "8x1" or "4x2" overrides it (a
+// tuning knob read once per process).
+struct AttnShape {
+  int nw, qb;
+};
+AttnShape attn_shape() {
+  static const AttnShape v = [] {
+    const char* e = getenv("ISPA_ATTN_SHAPE");
+    if (e && e[0] == '4' && e[2] == '1') return AttnShape{4, 1};
+    if (e && e[0] == '4' && e[2] == '2') return AttnShape{4, 2};
+    return AttnShape{8, 1};
+  }();
+  return v;
+}
+
+template <int D>
+void launch_bf16(const AttnShape sh, dim3 grid, hipStream_t s, const AttnKParams& p) {
+  if (sh.nw == 8)
+    hipLaunchKernelGGL((attn_bf16_kernel<D, 8, 1>), grid, dim3(512), 0, s, p);
+  else if (sh.qb == 2)
+    hipLaunchKernelGGL((attn_bf16_kernel<D, 4, 2>), grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((attn_bf16_kernel<D, 4, 1>), grid, dim3(256), 0, s, p);
+}
 
 ispa_status_t launch_attention(const AttnArgs& a, hipStream_t s) {
   if (a.n_q == 0) return ISPA_OK;
@@ -546,14 +666,15 @@ ispa_status_t launch_attention(const AttnArgs& a, hipStream_t s) {
       set_error("ispa_decomp_attn: workspace too small for the merge (query ispa_decomp_attn_workspace_size)");
       return ISPA_E_WORKSPACE;
     }
-    const int bm = ATTN_NW * 32;
+    const AttnShape sh = attn_shape();
+    const int bm = sh.nw * 32 * sh.qb;
     p.n_qtiles = (int)((a.n_q + bm - 1) / bm);
     p.nblocks = p.n_qtiles * a.heads;
-    const dim3 grid(p.nblocks), block(ATTN_NW * 64);
+    const dim3 grid(p.nblocks);
     if (a.head_dim == 128)
-      hipLaunchKernelGGL((attn_bf16_kernel<128, ATTN_NW>), grid, block, 0, s, p);
+      launch_bf16<128>(sh, grid, s, p);
     else
-      hipLaunchKernelGGL((attn_bf16_kernel<64, ATTN_NW>), grid, block, 0, s, p);
+      launch_bf16<64>(sh, grid, s, p);
     return hip_check(hipGetLastError(), "attn_bf16_kernel launch");
   }
   AttnF32Params p;
