@@ -80,26 +80,62 @@ __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return __b
 
 // QB = 32-query blocks per wave (1: 32 queries, two waves per SIMD; 2: 64 queries, one wave per SIMD
 // with half the LDS traffic per FLOP).
+typedef short bf16x4_raw __attribute__((__vector_size__(4 * sizeof(short))));
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Transposing LDS read (ds_read_b64_tr_b16): in each group of 16 lanes, lane i
+// receives element (i % 4) of the 8-byte words addressed by lanes i/4, 4 + i/4,
+// 8 + i/4 and 12 + i/4 of its group.
+// (The gfx950-only builtins below are hidden from the host compilation pass,
+// which otherwise drops the kernel's launch stub.)
+__device__ __forceinline__ u32x2 lds_read_tr(const uint16_t* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const bf16x4_raw r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) bf16x4_raw*)(p));
+  return __builtin_bit_cast(u32x2, r);
+#else
+  return u32x2{0, 0};
+#endif
+}
+
+// One wave moves 64 x 16 bytes from the buffer (at per-lane byte offset `voffset`) to LDS,
+// lane i's 16 bytes landing at lds_base + 16 i.  Offsets past the buffer's size read 0.
+__device__ __forceinline__ void load_to_lds(rsrc_t r, uint16_t* lds_base, uint32_t voffset) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, voffset, 0, 0, 0);
+#endif
+}
+
+// QB = 32-query blocks per wave (1: 32 queries per wave; 2: 64 queries, one wave per SIMD).
+//
+// K and V tiles (BN keys x D) are kept row-major in LDS, each row's 16-byte
+// chunks XOR-swizzled by (row & 7) so that both the K operand reads (8 rows,
+// same chunk) and the transposing V reads (8 rows, 4 chunks) spread over all
+// banks.  They are filled straight from global memory by buffer loads into LDS
+// (a wave moves 1 KB per load), so tile staging costs no VGPRs and no LDS
+// store instructions; rows past the branch's end read as 0 (range-checked).
 template <int D, int NW, int QB>
 __global__ __launch_bounds__(NW * 64, (QB == 1 && NW <= 4) ? 2 : 1) void attn_bf16_kernel(AttnKParams p) {
-  constexpr int NT = NW * 64;
-  constexpr int KS = D + 8;   // K tile row stride (elements): rows 16 B apart in bank space
-  constexpr int VS = BN + 8;  // V^T tile row stride (elements)
   constexpr int KK = D / 16;  // MFMA k-steps of S^T
   constexpr int DB = D / 32;  // 32-row blocks of O^T
   constexpr int NKB = BN / 32;
-  constexpr int KC = BN * D / 8 / NT;  // 16-byte K chunks per thread per tile
-  static_assert(KC >= 1 && KC * NT * 8 == BN * D, "K tile split");
-  constexpr int VITEMS = (BN / 8) * (D / 4);  // (8 keys x 4 dims) V items per tile
-  constexpr int VI = (VITEMS + NT - 1) / NT;
+  constexpr int CPR = D / 8;         // 16-byte chunks per row
+  constexpr int RPW = 64 / CPR;      // rows per wave load (1 KB)
+  constexpr int WLT = BN / RPW;      // wave loads per matrix tile
+  constexpr int WLW = 2 * WLT / NW;  // wave loads per wave per tile (K and V)
+  static_assert(WLW * NW == 2 * WLT, "tile loads must split evenly over the waves");
   constexpr int BM = NW * 32 * QB;
   // The running max used as the exponent reference is raised only when a new
   // score exceeds it by more than 2^8: p then stays below 2^8, and the
   // accumulator rescale (D multiplies per query) is skipped on most tiles.
   constexpr float RESCALE_T = 8.0f;
 
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * VS];
+  // Two buffers as four distinct arrays, addressed only with compile-time
+  // buffer choices, so the compiler can tell the loads landing in one buffer
+  // from the reads of the other and does not wait for the prefetch early.
+  __shared__ __attribute__((aligned(1024))) uint16_t sK0[BN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sK1[BN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV0[BN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV1[BN * D];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -138,69 +174,29 @@ __global__ __launch_bounds__(NW * 64, (QB == 1 && NW <= 4) ? 2 : 1) void attn_bf
     }
   }
 
-  // per-thread byte offsets of the tile loads (the tile's key0 * row_bytes is added per tile)
-  uint32_t kofs[KC];
+  // This wave's tile loads: load j is wave load g = wave + j*NW of the tile (K loads first, then V).
+  // Lane i fills row r0 + i/CPR, slot i%CPR, with the row's chunk (slot ^ (row & 7)).
+  uint32_t gofs[WLW];
 #pragma unroll
-  for (int i = 0; i < KC; ++i) {
-    const int c = tid + i * NT;
-    kofs[i] = (uint32_t)(c / (D / 8)) * row_bytes + (uint32_t)(head * D + (c % (D / 8)) * 8) * 2u;
-  }
-  uint32_t vofs[VI];
-#pragma unroll
-  for (int i = 0; i < VI; ++i) {
-    const int it = tid + i * NT;
-    vofs[i] = (uint32_t)((it % (BN / 8)) * 8) * row_bytes + (uint32_t)(head * D + (it / (BN / 8)) * 4) * 2u;
+  for (int j = 0; j < WLW; ++j) {
+    const int g = wave + j * NW;
+    const int row = (g % WLT) * RPW + lane / CPR;
+    const int chunk = (lane % CPR) ^ (row & 7);
+    gofs[j] = (uint32_t)row * row_bytes + (uint32_t)(head * D + chunk * 8) * 2u;
   }
 
-  u32x4 kreg[KC];
-  u32x2 vreg[VI][8];
-
-  auto load_tile = [&](int t) {
+  auto load_tile = [&](int t, uint16_t* sKb, uint16_t* sVb) {
     const bool loc = t < Tl;
     const uint32_t tb = (uint32_t)((loc ? t : t - Tl) * BN) * row_bytes;
     const rsrc_t rk = loc ? rKl : rKh;
     const rsrc_t rv = loc ? rVl : rVh;
 #pragma unroll
-    for (int i = 0; i < KC; ++i) kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, kofs[i] + tb, 0, 0);
-#pragma unroll
-    for (int i = 0; i < VI; ++i) {
-      if (VITEMS % NT == 0 || tid + i * NT < VITEMS) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          vreg[i][e] = __builtin_amdgcn_raw_buffer_load_b64(rv, vofs[i] + tb + (uint32_t)e * row_bytes, 0, 0);
-      }
-    }
-  };
-
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < KC; ++i) {
-      const int c = tid + i * NT;
-      *(u32x4*)(&sK[buf][(c / (D / 8)) * KS + (c % (D / 8)) * 8]) = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VI; ++i) {
-      const int it = tid + i * NT;
-      if (VITEMS % NT == 0 || it < VITEMS) {
-        const int kg = it % (BN / 8), dq = it / (BN / 8);
-        // Key 8kg+e of the tile goes to position sigma(8kg+e); sigma swaps bits
-        // 2 and 3 inside each 16-key group, so keys e=0..3 land at pos0+0..3
-        // and keys e=4..7 at pos0+8..11.
-        const int pos0 = (kg >> 1) * 16 + (kg & 1) * 4;
-#pragma unroll
-        for (int dd = 0; dd < 4; ++dd) {
-          uint32_t w[4];
-#pragma unroll
-          for (int x = 0; x < 4; ++x) {
-            const uint32_t a = (dd < 2) ? vreg[i][2 * x].x : vreg[i][2 * x].y;
-            const uint32_t b = (dd < 2) ? vreg[i][2 * x + 1].x : vreg[i][2 * x + 1].y;
-            w[x] = (dd & 1) ? pack_hi(a, b) : pack_lo(a, b);
-          }
-          uint16_t* row = &sV[buf][(dq * 4 + dd) * VS];
-          *(u32x2*)(row + pos0) = u32x2{w[0], w[1]};
-          *(u32x2*)(row + pos0 + 8) = u32x2{w[2], w[3]};
-        }
-      }
+    for (int j = 0; j < WLW; ++j) {
+      const int g = wave + j * NW;
+      if (g < WLT)
+        load_to_lds(rk, sKb + (g % WLT) * RPW * D, gofs[j] + tb);
+      else
+        load_to_lds(rv, sVb + (g % WLT) * RPW * D, gofs[j] + tb);
     }
   };
 
@@ -219,16 +215,29 @@ __global__ __launch_bounds__(NW * 64, (QB == 1 && NW <= 4) ? 2 : 1) void attn_bf
   // (sched_barrier keeps the compiler from sinking them next to their use).
   constexpr int NS = NKB * KK;      // K fragments per tile: (kb, kk), chains of the NKB accumulators interleaved
   constexpr int NV = DB * NKB * 2;  // V fragments per tile: (db, kb, mm), DB accumulators interleaved
-  auto kfrag = [&](int buf, int i) {
+  // K operand: row kb*32 + l32, chunk 2kk + hh (swizzled by row & 7 == l32 & 7).
+  auto kfrag = [&](const uint16_t* sKb, int i) {
     const int kb = i % NKB, kk = i / NKB;
-    return __builtin_bit_cast(bf16x8, *(const u32x4*)(&sK[buf][(kb * 32 + l32) * KS + 8 * hh + 16 * kk]));
+    const int row = kb * 32 + l32;
+    return __builtin_bit_cast(bf16x8, *(const u32x4*)(&sKb[row * D + (((2 * kk + hh) ^ (l32 & 7)) << 3)]));
   };
-  auto vfrag = [&](int buf, int i) {
+  // V^T operand of O^T = V^T P^T for lane (dim 32db + lane%32, hh): keys 32kb + 16mm + 4hh + {0..3}
+  // and + 8 + {0..3} (the key order of the P accumulator), read with two transposing loads.
+  // As a source lane, lane i of its 16-lane group points at key (4hh + i/4) and dims dbase + 4*(i%4).
+  const int q16 = lane >> 4, i16 = lane & 15;
+  const int vdim = 16 * (q16 & 1) + 4 * (i16 & 3);  // dim offset within the 32-dim block
+  const int vkey = 4 * (q16 >> 1) + (i16 >> 2);     // key offset within the 16-key step
+  auto vfrag = [&](const uint16_t* sVb, int i) {
     const int db = i % DB, j = i / DB, kb = j / 2, mm = j % 2;
-    return __builtin_bit_cast(bf16x8, *(const u32x4*)(&sV[buf][(db * 32 + l32) * VS + 8 * hh + kb * 32 + 16 * mm]));
+    const int d0 = 32 * db + vdim;
+    const int key_a = 32 * kb + 16 * mm + vkey, key_b = key_a + 8;
+    const uint16_t* pa = &sVb[key_a * D + (((d0 >> 3) ^ (key_a & 7)) << 3) + (d0 & 7)];
+    const uint16_t* pb = &sVb[key_b * D + (((d0 >> 3) ^ (key_b & 7)) << 3) + (d0 & 7)];
+    const u32x2 a = lds_read_tr(pa), b = lds_read_tr(pb);
+    return __builtin_bit_cast(bf16x8, u32x4{a.x, a.y, b.x, b.y});
   };
 
-  auto compute_tile = [&](int buf, int t) {
+  auto compute_tile = [&](const uint16_t* sKb, const uint16_t* sVb, int t) {
     const int key0 = (t < Tl ? t : t - Tl) * BN;
     const int nvalid = t < Tl ? n_loc : n_hist;
     f32x16 s[QB][NKB];
@@ -237,11 +246,11 @@ __global__ __launch_bounds__(NW * 64, (QB == 1 && NW <= 4) ? 2 : 1) void attn_bf
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) s[qb][kb] = f32x16{0};
     bf16x8 kf[3];
-    kf[0] = kfrag(buf, 0);
-    kf[1] = kfrag(buf, 1);
+    kf[0] = kfrag(sKb, 0);
+    kf[1] = kfrag(sKb, 1);
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
-      if (i + 2 < NS) kf[(i + 2) % 3] = kfrag(buf, i + 2);
+      if (i + 2 < NS) kf[(i + 2) % 3] = kfrag(sKb, i + 2);
       __builtin_amdgcn_sched_barrier(0);
       const int kb = i % NKB, kk = i / NKB;
 #pragma unroll
@@ -251,8 +260,8 @@ __global__ __launch_bounds__(NW * 64, (QB == 1 && NW <= 4) ? 2 : 1) void attn_bf
     }
     // the first V fragments do not depend on P: start reading them before the softmax
     bf16x8 vf[3];
-    vf[0] = vfrag(buf, 0);
-    vf[1] = vfrag(buf, 1);
+    vf[0] = vfrag(sVb, 0);
+    vf[1] = vfrag(sVb, 1);
     // Accumulator element v of lane (query, hh) in key block kb is key
     // kb*32 + 8*(v/4) + 4*hh + v%4.  Mask keys past the branch's end.
     if (key0 + BN > nvalid) {
@@ -308,7 +317,7 @@ __global__ __launch_bounds__(NW * 64, (QB == 1 && NW <= 4) ? 2 : 1) void attn_bf
     }
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      if (i + 2 < NV) vf[(i + 2) % 3] = vfrag(buf, i + 2);
+      if (i + 2 < NV) vf[(i + 2) % 3] = vfrag(sVb, i + 2);
       __builtin_amdgcn_sched_barrier(0);
       const int db = i % DB, j = i / DB, kb = j / 2, mm = j % 2;
 #pragma unroll
@@ -343,43 +352,53 @@ __global__ __launch_bounds__(NW * 64, (QB == 1 && NW <= 4) ? 2 : 1) void attn_bf
   };
 
   float lse2_loc[QB];
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  for (int t = 0; t < T; ++t) {
-    if (t + 1 < T) load_tile(t + 1);
-    compute_tile(t & 1, t);
-    if (t == Tl - 1) {
-      // local branch done: normalise, write O_loc / LSE_loc, keep float32 O_loc for the merge
+  // local branch done: normalise, write O_loc / LSE_loc, keep float32 O_loc for the merge
+  auto end_of_local = [&]() {
+    // local branch done: normalise, write O_loc / LSE_loc, keep float32 O_loc for the merge
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const float lt = l[qb] + other_half(l[qb]);
-        const float inv = 1.0f / lt;
-        lse2_loc[qb] = m[qb] + __log2f(lt);
-        u32x2 oloc[DB][4];
-        pack_acc(oloc, qb, inv);
-        write_o(p.O_loc, qb, oloc);
-        lse_store(p.LSE_loc, qb, lse2_loc[qb]);
-        if (Th == 0) {
-          // local-attention mode: the full output is the local one, bit for bit
-          write_o(p.O_full, qb, oloc);
-          lse_store(p.LSE_full, qb, lse2_loc[qb]);
-        } else if (p.O_full && qvalid[qb]) {
-          float* stash = p.stash + (size_t)myq[qb] * HD + head * D + 4 * hh;
+    for (int qb = 0; qb < QB; ++qb) {
+      const float lt = l[qb] + other_half(l[qb]);
+      const float inv = 1.0f / lt;
+      lse2_loc[qb] = m[qb] + __log2f(lt);
+      u32x2 oloc[DB][4];
+      pack_acc(oloc, qb, inv);
+      write_o(p.O_loc, qb, oloc);
+      lse_store(p.LSE_loc, qb, lse2_loc[qb]);
+      if (Th == 0) {
+        // local-attention mode: the full output is the local one, bit for bit
+        write_o(p.O_full, qb, oloc);
+        lse_store(p.LSE_full, qb, lse2_loc[qb]);
+      } else if (p.O_full && qvalid[qb]) {
+        float* stash = p.stash + (size_t)myq[qb] * HD + head * D + 4 * hh;
 #pragma unroll
-          for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int g = 0; g < 4; ++g)
-              *(f32x4*)(stash + 32 * db + 8 * g) = f32x4{acc[qb][db][4 * g] * inv, acc[qb][db][4 * g + 1] * inv,
-                                                         acc[qb][db][4 * g + 2] * inv, acc[qb][db][4 * g + 3] * inv};
-        }
-        m[qb] = -INFINITY;
-        l[qb] = 0.f;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) acc[qb][db] = f32x16{0};
+          for (int g = 0; g < 4; ++g)
+            *(f32x4*)(stash + 32 * db + 8 * g) = f32x4{acc[qb][db][4 * g] * inv, acc[qb][db][4 * g + 1] * inv,
+                                                       acc[qb][db][4 * g + 2] * inv, acc[qb][db][4 * g + 3] * inv};
       }
+      m[qb] = -INFINITY;
+      l[qb] = 0.f;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc[qb][db] = f32x16{0};
     }
-    if (t + 1 < T) store_tile((t + 1) & 1);
+  };
+
+  load_tile(0, sK0, sV0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int t = 0; t < T; t += 2) {
+    // even tile in buffer 0, odd tile in buffer 1; the next tile's loads are in flight meanwhile
+    if (t + 1 < T) load_tile(t + 1, sK1, sV1);
+    compute_tile(sK0, sV0, t);
+    if (t == Tl - 1) end_of_local();
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile t+1 have landed in LDS
+    __syncthreads();
+    if (t + 1 >= T) break;
+    if (t + 2 < T) load_tile(t + 2, sK0, sV0);
+    compute_tile(sK1, sV1, t + 1);
+    if (t + 1 == Tl - 1) end_of_local();
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
