@@ -10,7 +10,7 @@
 //
 // Structure (nb = 64 column panels, right-looking):
 //   M = G + lambda I                                   (init kernel)
-//   R = C W, accumulated in float64                    (float64 GEMM)
+//   R = C W, accumulated in float64                    (MFMA f64 GEMM)
 //   for each panel k:
 //     factor M_kk = L_kk L_kk^T and invert L_kk       (one workgroup per layer)
 //     L_ik = M_ik L_kk^-T                             (GEMM, in place)
@@ -26,9 +26,12 @@
 // L^-1 once turns each triangular solve into one GEMM launch instead of one per
 // panel.  The factor, inverse and solve GEMMs run on v_mfma_f32_32x32x2_f32
 // with 64x64 tiles (triangular operands skip their zero blocks); the
-// float64-accumulated products run on the float64 VALU.  A layer whose pivot
+// float64-accumulated products run on v_mfma_f64_16x16x4_f64.  A layer whose pivot
 // fails records info = column + 1 and is skipped by later kernels; its dW is
 // set to NaN at the end and its W_new is left alone.
+#include <utility>
+#include <vector>
+
 #include "ispa_internal.h"
 
 namespace ispa {
@@ -46,65 +49,91 @@ struct GemmParams {
   size_t sA, sB, sC, sD;  // batch strides (elements)
   float alpha, beta;
   int lower_only;         // skip 64x64 tiles strictly above the diagonal
-  int kmode;              // 0 all k; 1 op(A) lower: k < m0+64; 2 op(A) upper: k >= m0; 3 op(B) lower: k >= n0
+  int kmode;              // 0 all k; 1 op(A) lower: k < m0+T; 2 op(A) upper: k >= m0; 3 op(B) lower: k >= n0
   const int32_t* info;    // skip batch entries with info != 0 (nullable)
+  int npairs;             // grid.z = batch * npairs; pair q adds q * pA, pB, pC, pD
+  size_t pA, pB, pC, pD;
 };
 
 // D = alpha * op(A) op(B) + beta * Cin; op(A) is MxK, op(B) is KxN.
 // TA: A stored KxM (op(A) = A^T); TB: B stored NxK (op(B) = B^T).
-// M, N multiples of 64; K multiple of 16.  Cin may equal D.
-template <bool TA, bool TB>
+// T x T output tile (T = 64 or 128), 4 waves in 2x2, each (T/2)x(T/2) as blocks of
+// v_mfma_f32_32x32x2_f32.  M, N multiples of T; K multiple of 16.  Cin may equal D.
+template <bool TA, bool TB, int T>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
-  const int b = blockIdx.z;
+  constexpr int WB = T / 64;  // 32x32 blocks per wave per dimension
+  const int b = blockIdx.z / p.npairs, q = blockIdx.z % p.npairs;
   if (p.info && p.info[b] != 0) return;
   const int tm = blockIdx.y, tn = blockIdx.x;
   if (p.lower_only && tm < tn) return;
-  const int m0 = tm * 64, n0 = tn * 64;
-  __shared__ float As[16][64 + 4];  // [k][m]
-  __shared__ float Bs[16][64 + 4];  // [k][n]
+  const int m0 = tm * T, n0 = tn * T;
+  __shared__ float As[16][T + 4];  // [k][m]
+  __shared__ float Bs[16][T + 4];  // [k][n]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
-  const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
-  const float* A = p.A + b * p.sA;
-  const float* B = p.B + b * p.sB;
-  f32x16 acc = f32x16{0};
+  const int wm = (wave >> 1) * (T / 2), wn = (wave & 1) * (T / 2);
+  const float* A = p.A + b * p.sA + q * p.pA;
+  const float* B = p.B + b * p.sB + q * p.pB;
+  f32x16 acc[WB][WB];
+#pragma unroll
+  for (int i = 0; i < WB; ++i)
+#pragma unroll
+    for (int j = 0; j < WB; ++j) acc[i][j] = f32x16{0};
   const int kb = p.kmode == 2 ? m0 : (p.kmode == 3 ? n0 : 0);
-  const int ke = p.kmode == 1 ? min(p.K, m0 + 64) : p.K;
+  const int ke = p.kmode == 1 ? min(p.K, m0 + T) : p.K;
   for (int k0 = kb; k0 < ke; k0 += 16) {
-    if (!TA) {
-      const int m = tid >> 2, kq = tid & 3;
-      const f32x4 v = *(const f32x4*)(A + (size_t)(m0 + m) * p.lda + k0 + 4 * kq);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) As[4 * kq + e][m] = v[e];
-    } else {
-      const int k = tid >> 4, mq = tid & 15;
-      *(f32x4*)(&As[k][4 * mq]) = *(const f32x4*)(A + (size_t)(k0 + k) * p.lda + m0 + 4 * mq);
-    }
-    if (TB) {
-      const int n = tid >> 2, kq = tid & 3;
-      const f32x4 v = *(const f32x4*)(B + (size_t)(n0 + n) * p.ldb + k0 + 4 * kq);
+    for (int r = 0; r < T / 64; ++r) {
+      const int t = tid + 256 * r;
+      if (!TA) {
+        const int m = t >> 2, kq = t & 3;
+        const f32x4 v = *(const f32x4*)(A + (size_t)(m0 + m) * p.lda + k0 + 4 * kq);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) Bs[4 * kq + e][n] = v[e];
-    } else {
-      const int k = tid >> 4, nq = tid & 15;
-      *(f32x4*)(&Bs[k][4 * nq]) = *(const f32x4*)(B + (size_t)(k0 + k) * p.ldb + n0 + 4 * nq);
+        for (int e = 0; e < 4; ++e) As[4 * kq + e][m] = v[e];
+      } else {
+        const int k = t / (T / 4), mq = t % (T / 4);
+        *(f32x4*)(&As[k][4 * mq]) = *(const f32x4*)(A + (size_t)(k0 + k) * p.lda + m0 + 4 * mq);
+      }
+      if (TB) {
+        const int n = t >> 2, kq = t & 3;
+        const f32x4 v = *(const f32x4*)(B + (size_t)(n0 + n) * p.ldb + k0 + 4 * kq);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Bs[4 * kq + e][n] = v[e];
+      } else {
+        const int k = t / (T / 4), nq = t % (T / 4);
+        *(f32x4*)(&Bs[k][4 * nq]) = *(const f32x4*)(B + (size_t)(k0 + k) * p.ldb + n0 + 4 * nq);
+      }
     }
     __syncthreads();
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(As[2 * kk + hh][wm + l32], Bs[2 * kk + hh][wn + l32], acc, 0, 0, 0);
+    for (int kk = 0; kk < 8; ++kk) {
+      float a[WB], bv[WB];
+#pragma unroll
+      for (int i = 0; i < WB; ++i) {
+        a[i] = As[2 * kk + hh][wm + 32 * i + l32];
+        bv[i] = Bs[2 * kk + hh][wn + 32 * i + l32];
+      }
+#pragma unroll
+      for (int i = 0; i < WB; ++i)
+#pragma unroll
+        for (int j = 0; j < WB; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], bv[j], acc[i][j], 0, 0, 0);
+    }
     __syncthreads();
   }
-  const float* Cin = p.Cin ? p.Cin + b * p.sC : nullptr;
-  float* D = p.D + b * p.sD;
+  const float* Cin = p.Cin ? p.Cin + b * p.sC + q * p.pC : nullptr;
+  float* D = p.D + b * p.sD + q * p.pD;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int i = m0 + wm + 8 * (v >> 2) + 4 * hh + (v & 3);
-    const int j = n0 + wn + l32;
-    float r = p.alpha * acc[v];
-    if (Cin && p.beta != 0.f) r = fmaf(p.beta, Cin[(size_t)i * p.ldc + j], r);
-    D[(size_t)i * p.ldd + j] = r;
-  }
+  for (int i = 0; i < WB; ++i)
+#pragma unroll
+    for (int j = 0; j < WB; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = m0 + wm + 32 * i + 8 * (v >> 2) + 4 * hh + (v & 3);
+        const int c = n0 + wn + 32 * j + l32;
+        float x = p.alpha * acc[i][j][v];
+        if (Cin && p.beta != 0.f) x = fmaf(p.beta, Cin[(size_t)r * p.ldc + c], x);
+        D[(size_t)r * p.ldd + c] = x;
+      }
 }
 
 struct GemmDParams {
@@ -121,25 +150,29 @@ struct GemmDParams {
   const int32_t* info;
 };
 
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
 // D = alpha * A B + beta * Cin + gamma * X with float64 accumulation of the
-// (exact) products of float32 operands, on the float64 VALU (full rate on this
-// GPU): each thread owns a 4x4 block of the 64x64 tile.  M, N multiples of 64,
-// K of 16.
+// (exact) products of float32 operands, on v_mfma_f64_16x16x4_f64.  64x64 tile,
+// 4 waves of 32x32 (2x2 blocks of 16x16).  Operand layout of the f64 MFMA:
+// lane l holds A[l%16][l/16] and B[l/16][l%16]; output element v of lane l is
+// row 4v + l/16, column l%16 of its block.  M, N multiples of 64, K of 16.
 __global__ __launch_bounds__(256) void gemm_f64acc_kernel(GemmDParams p) {
   const int b = blockIdx.z;
   if (p.info && p.info[b] != 0) return;
   const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
-  __shared__ __attribute__((aligned(16))) float As[16][64 + 4];
-  __shared__ __attribute__((aligned(16))) float Bs[16][64 + 4];
-  const int tid = threadIdx.x;
-  const int ty = tid >> 4, tx = tid & 15;
+  __shared__ float As[16][64 + 4];  // [k][m]
+  __shared__ float Bs[16][64 + 4];  // [k][n]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
   const float* A = p.A + b * p.sA;
   const float* B = p.B + b * p.sB;
-  double acc[4][4];
+  f64x4 acc[2][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+    for (int j = 0; j < 2; ++j) acc[i][j] = f64x4{0, 0, 0, 0};
   for (int k0 = 0; k0 < p.K; k0 += 16) {
     {
       const int m = tid >> 2, kq = tid & 3;
@@ -150,29 +183,35 @@ __global__ __launch_bounds__(256) void gemm_f64acc_kernel(GemmDParams p) {
       *(f32x4*)(&Bs[k][4 * nq]) = *(const f32x4*)(B + (size_t)(k0 + k) * p.ldb + n0 + 4 * nq);
     }
     __syncthreads();
-#pragma unroll 4
-    for (int k = 0; k < 16; ++k) {
-      const f32x4 a = *(const f32x4*)(&As[k][4 * ty]);
-      const f32x4 bb = *(const f32x4*)(&Bs[k][4 * tx]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+    for (int kk = 0; kk < 4; ++kk) {
+      double a[2], bb[2];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fma((double)a[i], (double)bb[j], acc[i][j]);
+      for (int i = 0; i < 2; ++i) {
+        a[i] = (double)As[4 * kk + g][wm + 16 * i + l16];
+        bb[i] = (double)Bs[4 * kk + g][wn + 16 * i + l16];
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], bb[j], acc[i][j], 0, 0, 0);
     }
     __syncthreads();
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = m0 + 4 * ty + i;
-      const int c = n0 + 4 * tx + j;
-      double x = p.alpha * acc[i][j];
-      if (p.Cin) x += p.beta * p.Cin[b * p.sC + (size_t)r * p.ldc + c];
-      if (p.X) x += p.gamma * (double)p.X[b * p.sX + (size_t)r * p.ldx + c];
-      if (p.D64) p.D64[b * p.sD + (size_t)r * p.ldd + c] = x;
-      if (p.D32) p.D32[b * p.sD + (size_t)r * p.ldd + c] = (float)x;
-    }
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = m0 + wm + 16 * i + 4 * v + g;
+        const int c = n0 + wn + 16 * j + l16;
+        double x = p.alpha * acc[i][j][v];
+        if (p.Cin) x += p.beta * p.Cin[b * p.sC + (size_t)r * p.ldc + c];
+        if (p.X) x += p.gamma * (double)p.X[b * p.sX + (size_t)r * p.ldx + c];
+        if (p.D64) p.D64[b * p.sD + (size_t)r * p.ldd + c] = x;
+        if (p.D32) p.D32[b * p.sD + (size_t)r * p.ldd + c] = (float)x;
+      }
 }
 
 // M = G + lambda I (full matrix); info = 0.
@@ -335,7 +374,8 @@ __global__ __launch_bounds__(256) void eps_reduce_kernel(const float* W, const f
 template <bool TA, bool TB>
 ispa_status_t gemm(hipStream_t s, int batch, int M, int N, int K, const float* A, int lda, size_t sA, const float* B,
                    int ldb, size_t sB, const float* Cin, int ldc, size_t sC, float* D, int ldd, size_t sD, float alpha,
-                   float beta, bool lower_only, const int32_t* info, int kmode = 0) {
+                   float beta, bool lower_only, const int32_t* info, int kmode = 0, int npairs = 1,
+                   size_t pA = 0, size_t pB = 0, size_t pC = 0, size_t pD = 0) {
   if (M <= 0 || N <= 0 || K <= 0) return ISPA_OK;
   GemmParams p;
   p.A = A; p.B = B; p.Cin = Cin; p.D = D;
@@ -346,8 +386,15 @@ ispa_status_t gemm(hipStream_t s, int batch, int M, int N, int K, const float* A
   p.lower_only = lower_only ? 1 : 0;
   p.kmode = kmode;
   p.info = info;
-  const dim3 grid(N / 64, M / 64, batch), block(256);
-  hipLaunchKernelGGL((gemm_f32_kernel<TA, TB>), grid, block, 0, s, p);
+  p.npairs = npairs;
+  p.pA = pA; p.pB = pB; p.pC = pC; p.pD = pD;
+  // large products use 128x128 tiles (half the operand traffic per FLOP) when they still fill the GPU
+  const int z = batch * npairs;
+  const bool big = M % 128 == 0 && N % 128 == 0 && (size_t)(M / 128) * (N / 128) * z >= 192;
+  if (big)
+    hipLaunchKernelGGL((gemm_f32_kernel<TA, TB, 128>), dim3(N / 128, M / 128, z), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((gemm_f32_kernel<TA, TB, 64>), dim3(N / 64, M / 64, z), dim3(256), 0, s, p);
   return hip_check(hipGetLastError(), "gemm_f32_kernel launch");
 }
 
@@ -378,7 +425,7 @@ size_t absorb_workspace_size(int32_t d, int32_t d_out, int32_t batch) {
   const size_t b = (size_t)batch;
   return b * d * d * sizeof(float)          // factor L (lower triangle of M)
          + b * d * d * sizeof(float)        // L^-1
-         + b * NB * d * sizeof(float)       // one block row of intermediate products
+         + b * d * d * sizeof(float)        // intermediate products of the inverse
          + b * d * d_out * sizeof(double)   // R = C W in float64
          + 2 * b * d * d_out * sizeof(float);  // residual / correction and an intermediate
 }
@@ -400,6 +447,44 @@ ispa_status_t chol_apply(hipStream_t s, int batch, int d, int d_out, const float
 
 }  // namespace
 
+// Fill the blocks of L^-1 below its 64x64 diagonal inverses (already in Linvf) by recursive
+// doubling.  Ranges are [start, start+len) in 64-row blocks; each level merges adjacent ranges.
+ispa_status_t invert_lower(hipStream_t s, int batch, int d, const float* L, float* Linvf, float* Tb,
+                           const int32_t* info) {
+  const size_t dd = (size_t)d * d;
+  std::vector<std::pair<int, int>> rng;
+  for (int k = 0; k < d / NB; ++k) rng.push_back({k, 1});
+  while (rng.size() > 1) {
+    std::vector<std::pair<int, int>> next;
+    size_t i = 0;
+    while (i + 1 < rng.size()) {
+      const int sa = rng[i].second, sc = rng[i + 1].second;
+      int np = 0;
+      size_t j = i;
+      while (j + 1 < rng.size() && rng[j].second == sa && rng[j + 1].second == sc) {
+        ++np;
+        j += 2;
+      }
+      const int nA = sa * NB, nC = sc * NB;
+      const size_t a0 = (size_t)rng[i].first * NB;
+      const size_t pstep = (size_t)(nA + nC) * (d + 1);  // from one pair's corner to the next
+      // T = B A^-1, with B = L[a0+nA : a0+nA+nC, a0 : a0+nA] and A^-1 lower triangular
+      ISPA_TRY((gemm<false, false>(s, batch, nC, nA, nA, L + (a0 + nA) * d + a0, d, dd, Linvf + a0 * d + a0, d, dd,
+                                   nullptr, 0, 0, Tb, nA, dd, 1.f, 0.f, false, info, KM_LOWER_B, np, pstep, pstep, 0,
+                                   (size_t)nC * nA)));
+      // off-diagonal block of the inverse: -C^-1 T, with C^-1 lower triangular
+      ISPA_TRY((gemm<false, false>(s, batch, nC, nA, nC, Linvf + (a0 + nA) * (d + 1), d, dd, Tb, nA, dd, nullptr, 0,
+                                   0, Linvf + (a0 + nA) * d + a0, d, dd, -1.f, 0.f, false, info, KM_LOWER_A, np, pstep,
+                                   (size_t)nC * nA, 0, pstep)));
+      for (int k = 0; k < np; ++k) next.push_back({rng[i + 2 * k].first, sa + sc});
+      i = j;
+    }
+    if (i < rng.size()) next.push_back(rng[i]);
+    rng.swap(next);
+  }
+  return ISPA_OK;
+}
+
 ispa_status_t launch_absorb(int32_t d, int32_t d_out, int32_t batch, const float* G, const float* C, const float* W,
                             float lambda, float* dW, float* W_new, int32_t* info, void* ws, size_t ws_bytes,
                             hipStream_t s) {
@@ -412,7 +497,7 @@ ispa_status_t launch_absorb(int32_t d, int32_t d_out, int32_t batch, const float
   float* M = (float*)ws;
   float* Linvf = M + (size_t)batch * dd;
   float* Tb = Linvf + (size_t)batch * dd;
-  double* R64 = (double*)(Tb + (size_t)batch * NB * d);
+  double* R64 = (double*)(Tb + (size_t)batch * dd);
   float* Rr = (float*)(R64 + (size_t)batch * dn);
   float* Zb = Rr + (size_t)batch * dn;
   const int nblk = d / NB;
@@ -440,14 +525,9 @@ ispa_status_t launch_absorb(int32_t d, int32_t d_out, int32_t batch, const float
     ISPA_TRY((gemm<false, true>(s, batch, rest, rest, NB, panel, d, dd, panel, d, dd, trail, d, dd, trail, d, dd, -1.f,
                                 1.f, true, info)));
   }
-  // explicit L^-1, block row by block row: T = L_{i,<i} (L^-1)_{<i,<i}; (L^-1)_{i,<i} = -L_ii^-1 T
-  for (int i = 1; i < nblk; ++i) {
-    const int i0 = i * NB;
-    ISPA_TRY((gemm<false, false>(s, batch, NB, i0, i0, M + (size_t)i0 * d, d, dd, Linvf, d, dd, nullptr, 0, 0, Tb, d,
-                                 (size_t)NB * d, 1.f, 0.f, false, info, KM_LOWER_B)));
-    ISPA_TRY((gemm<false, false>(s, batch, NB, i0, NB, Linvf + (size_t)i0 * d + i0, d, dd, Tb, d, (size_t)NB * d,
-                                 nullptr, 0, 0, Linvf + (size_t)i0 * d, d, dd, -1.f, 0.f, false, info)));
-  }
+  // explicit L^-1 by recursive doubling over block ranges: for adjacent ranges A (first) and C,
+  // inv([A 0; B C]) has off-diagonal block -C^-1 (B A^-1); pairs of equal sizes run as one launch.
+  ISPA_TRY(invert_lower(s, batch, d, M, Linvf, Tb, info));
   // X = (L L^T)^-1 R
   ISPA_TRY(chol_apply(s, batch, d, d_out, Linvf, Rr, Zb, dW, info));
   // refinement: r = R - G X - lambda X (float64), correction = (L L^T)^-1 r
