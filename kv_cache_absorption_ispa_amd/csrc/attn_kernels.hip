@@ -59,15 +59,6 @@ struct AttnKParams {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-constexpr int RSRC_DW3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
-
-// Buffer resource over `bytes` bytes: loads at offsets >= bytes return 0 (hardware range check),
-// which masks the ragged last tile of each branch without branches.
-__device__ __forceinline__ rsrc_t make_rsrc(const void* ptr, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(ptr), (short)0, (int)bytes, RSRC_DW3);
-}
-
 // Value held by the lane 32 away (the other half of the wave), via v_permlane32_swap.
 __device__ __forceinline__ float other_half(float x) {
   const uint32_t u = __builtin_bit_cast(uint32_t, x);
@@ -77,33 +68,6 @@ __device__ __forceinline__ float other_half(float x) {
 
 __device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
 __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
-
-// QB = 32-query blocks per wave (1: 32 queries, two waves per SIMD; 2: 64 queries, one wave per SIMD
-// with half the LDS traffic per FLOP).
-typedef short bf16x4_raw __attribute__((__vector_size__(4 * sizeof(short))));
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Transposing LDS read (ds_read_b64_tr_b16): in each group of 16 lanes, lane i
-// receives element (i % 4) of the 8-byte words addressed by lanes i/4, 4 + i/4,
-// 8 + i/4 and 12 + i/4 of its group.
-// (The gfx950-only builtins below are hidden from the host compilation pass,
-// which otherwise drops the kernel's launch stub.)
-__device__ __forceinline__ u32x2 lds_read_tr(const uint16_t* p) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  const bf16x4_raw r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) bf16x4_raw*)(p));
-  return __builtin_bit_cast(u32x2, r);
-#else
-  return u32x2{0, 0};
-#endif
-}
-
-// One wave moves 64 x 16 bytes from the buffer (at per-lane byte offset `voffset`) to LDS,
-// lane i's 16 bytes landing at lds_base + 16 i.  Offsets past the buffer's size read 0.
-__device__ __forceinline__ void load_to_lds(rsrc_t r, uint16_t* lds_base, uint32_t voffset) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, voffset, 0, 0, 0);
-#endif
-}
 
 // QB = 32-query blocks per wave (1: 32 queries per wave; 2: 64 queries, one wave per SIMD).
 //
