@@ -40,7 +40,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--config", type=int, default=1, help="layer shape (1: Wan-1.3B, 2: long history, 3: Wan-14B)")
+    ap.add_argument("--config", type=int, default=1,
+                    help="1: Wan-1.3B layer, 2: long history, 3: Wan-14B layer, 4: 30-layer 1.3B stack")
+    ap.add_argument("--gen-workers", type=int, default=min(16, os.cpu_count() or 1),
+                    help="processes drawing the 30-layer stack's inputs (config 4)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU seconds for the oracle sample")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -58,6 +61,9 @@ def main():
                                    "see the design notes for how it would shard"}), flush=True)
         sys.exit(2)
 
+    if args.config == 4:
+        # the stack's inputs are drawn by worker processes before this process touches the GPU
+        stack_inputs = generate_stack_inputs(args.gen_workers)
     import torch
 
     from kv_cache_absorption_ispa_amd import inputs, ispa
@@ -74,6 +80,8 @@ def main():
         return
     ispa.load_library()
     ispa.ispa_device_check(0)
+    if args.config == 4:
+        return bench_stack(args, stack_inputs)
     cfg = inputs.CONFIGS[args.config]
     H, D, d = cfg.heads, cfg.head_dim, cfg.d
 
@@ -224,6 +232,171 @@ def main():
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+# --------------------------------------------------------------------------- #
+# 30-layer stack (config 4): warmup of every layer, transition, post-absorb chunk
+# --------------------------------------------------------------------------- #
+def _draw_chunk(job):
+    from kv_cache_absorption_ispa_amd import inputs
+
+    layer, chunk = job
+    x = inputs.chunk_inputs(inputs.CONFIGS[4], layer, chunk)
+    return layer, chunk, [t.raw for t in (x.q, x.k_loc, x.v_loc, x.k_hist, x.v_hist)]
+
+
+def generate_stack_inputs(workers: int):
+    """Host draws of every (layer, chunk) of the stack: 4 warmup chunks and the post-absorb chunk."""
+    import multiprocessing as mp
+
+    from kv_cache_absorption_ispa_amd import inputs
+
+    cfg = inputs.CONFIGS[4]
+    jobs = [(l, c) for c in range(cfg.n_chunks + 1) for l in range(cfg.n_layers)]
+    log(f"[bench] drawing {len(jobs)} chunk inputs of {cfg.name} with {workers} processes")
+    t0 = time.perf_counter()
+    out = {}
+    with mp.get_context("spawn").Pool(workers) as pool:
+        for i, (l, c, raws) in enumerate(pool.imap(_draw_chunk, jobs, chunksize=1)):
+            out[(l, c)] = raws
+            if (i + 1) % 30 == 0:
+                log(f"[bench]   {i + 1}/{len(jobs)} drawn ({time.perf_counter() - t0:.0f} s)")
+    return out
+
+
+def bench_stack(args, host_inputs):
+    """Config 4: 30 Wan-1.3B-shaped layers x 4 warmup chunks (decomposable attention + Gram), the
+    transition (batched absorb of all 30, eps, ranking, W += dW on the 15 lowest) and one post-absorb
+    chunk where those 15 attend locally.  One step = all of it; inputs resident in HBM."""
+    import torch
+
+    from kv_cache_absorption_ispa_amd import inputs, ispa
+    from kv_cache_absorption_ispa_amd.stack import LayerStack
+
+    cfg = inputs.CONFIGS[4]
+    L, H, D, d, nq = cfg.n_layers, cfg.heads, cfg.head_dim, cfg.d, cfg.n_q
+
+    def dev(raw):
+        return torch.from_numpy(raw.view(np.int16)).view(torch.bfloat16).cuda()
+
+    log("[bench] uploading stack inputs")
+    X = {}
+    for key in sorted(host_inputs):
+        X[key] = [dev(r) for r in host_inputs.pop(key)]
+    W0 = torch.from_numpy(np.stack([inputs.weight(cfg, l) for l in range(L)])).cuda()
+    W = W0.clone()
+    st = LayerStack(W, H, D, nq, cfg.lam, cfg.n_absorb)
+    o_loc = torch.empty(nq, H, D, dtype=torch.bfloat16, device="cuda")
+    o_full = torch.empty_like(o_loc)
+    torch.cuda.synchronize()
+
+    def run(ev=None):
+        """One pass of the stack; ev: dict of event lists for per-phase timing."""
+        W.copy_(W0)  # fresh weights (restored before the phase markers)
+        st.reset()
+        def mark(k):
+            if ev is not None:
+                e = torch.cuda.Event(enable_timing=True)
+                e.record()
+                ev[k].append(e)
+
+        mark("t0")
+        for c in range(cfg.n_chunks):
+            for l in range(L):
+                q, kl, vl, kh, vh = X[(l, c)]
+                st.warmup_chunk(l, q, kl, vl, kh, vh, o_loc, o_full)
+        mark("t1")
+        st.solve_and_rank()
+        mark("t2")
+        conv = st.convert()
+        mark("t3")
+        for l in range(L):
+            q, kl, vl, kh, vh = X[(l, cfg.n_chunks)]
+            st.post_chunk(l, q, kl, vl, kh, vh, o_full)
+        mark("t4")
+        return conv
+
+    log("[bench] stack warmup pass")
+    for _ in range(args.warmup):
+        conv = run()
+    torch.cuda.synchronize()
+    if st.info.cpu().tolist() != [0] * L:
+        raise RuntimeError(f"absorb failed: info = {st.info.cpu().tolist()}")
+
+    log(f"[bench] timing {args.steps} stack passes")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        conv = run()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    # per-phase times (separate pass, same work)
+    ev = {k: [] for k in ("t0", "t1", "t2", "t3", "t4")}
+    for _ in range(args.steps):
+        run(ev)
+        torch.cuda.synchronize()
+    ph = lambda a, b: float(np.median([x.elapsed_time(y) for x, y in zip(ev[a], ev[b])]))
+    warm_ms, solve_ms, conv_ms, post_ms = ph("t0", "t1"), ph("t1", "t2"), ph("t2", "t3"), ph("t3", "t4")
+
+    # the same post-absorb chunk with no layer converted (every layer keeps its history)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ws = ispa.workspace(ispa.ispa_decomp_attn_workspace_size(X[(0, 0)][0], cfg.n_loc, cfg.n_hist))
+    full_post = []
+    for _ in range(max(args.steps, 2)):
+        e0.record()
+        for l in range(L):
+            q, kl, vl, kh, vh = X[(l, cfg.n_chunks)]
+            ispa.ispa_decomp_attn(q, kl, vl, kh, vh, o_full=o_full, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        full_post.append(e0.elapsed_time(e1))
+    full_post_ms = float(np.median(full_post))
+
+    n_conv = len(conv)
+    f_full, f_loc = cfg.attn_flops(), cfg.attn_flops(n_hist=0)
+    warm_flops = L * cfg.n_chunks * f_full
+    post_flops = (L - n_conv) * f_full + n_conv * f_loc
+    value = (warm_flops + post_flops) / (ms_per_step * 1e-3) / 1e12
+    warm_tf = warm_flops / (warm_ms * 1e-3) / 1e12
+    kv_total = L * 2 * (cfg.n_loc + cfg.n_hist) * d * 2
+    evicted = st.evicted_kv_bytes(cfg.n_hist)
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q/K/V per layer and chunk, 8 sink keys at 4x norm; random-init W)",
+        "config": {
+            "workload": f"{cfg.name}: {L} layers of {H} heads x {D}, {nq} queries/chunk, {cfg.n_sink} sink + "
+                        f"{cfg.n_chunk} chunk local keys, {cfg.n_hist} history keys, {cfg.n_chunks} warmup chunks, "
+                        f"batched absorb of all {L} (d={d}), {cfg.n_absorb} converted, 1 post-absorb chunk",
+            "global_batch": L * (cfg.n_chunks + 1) * nq,
+            "seq_len": cfg.n_loc + cfg.n_hist,
+            "parallelism": "single GPU",
+        },
+        "warmup_ms": round(warm_ms, 3),
+        "warmup_attn_gram_tflops": round(warm_tf, 2),
+        "transition_ms": round(solve_ms + conv_ms, 3),
+        "absorb_ms_per_layer": round(solve_ms / L, 4),
+        "post_chunk_ms": round(post_ms, 3),
+        "post_chunk_ms_no_eviction": round(full_post_ms, 3),
+        "post_chunk_speedup": round(full_post_ms / post_ms, 3),
+        "converted_layers": sorted(conv),
+        "kv_bytes_total": kv_total,
+        "kv_bytes_evicted": evicted,
+        "kv_evicted_frac_of_history": round(evicted / (L * 2 * cfg.n_hist * d * 2), 4),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(inputs.CONFIGS[1], args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 

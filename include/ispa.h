@@ -12,6 +12,8 @@
  *   ispa_gram_accum    G = A_loc^T A_loc and C = A_loc^T (A_full - A_loc),
  *   ispa_absorb_solve  dW = (G + lambda I)^-1 C W  (Cholesky + triangular solves),
  *   ispa_layer_eps     the post-fit reconstruction error used to rank layers,
+ *   ispa_select_layers the k lowest-error layers (those converted),
+ *   ispa_absorb_apply  W += dW for the converted layers,
  *   ispa_full_attn     one softmax pass over all keys (the comparison pass),
  *   ispa_lse_merge     standalone N-way merge of (O, LSE) partial results.
  *
@@ -198,6 +200,36 @@ ispa_status_t ispa_layer_eps(int32_t d, int32_t d_out, int32_t batch, const floa
                              const float* Q_ff, const float* W, const float* dW, float lambda,
                              double* eps_abs, double* eps_rel, void* workspace, size_t workspace_bytes,
                              void* stream);
+
+/*
+ * ispa_select_layers — choose the k layers to convert to local attention.
+ *
+ * Source: ISPA technical summary, section 2 "Dynamic Layer Selection" (all
+ * layers ranked by reconstruction error after warmup; the lowest-error ones
+ * are converted).  Reading: rank by eps ascending (pass eps_rel of
+ * ispa_layer_eps), NaN (a failed solve) ranks last, equal values go to the
+ * lower layer index; this is a strict total order, so the result is unique.
+ *   eps [n_layers] float64 DEVICE; 1 <= n_layers <= 4096; 0 <= k <= n_layers.
+ *   selected [k] int32 DEVICE: the chosen layer ids, lowest eps first
+ *   (may be NULL when k = 0).
+ *   rank [n_layers] int32 DEVICE, may be NULL: each layer's rank (0 = lowest).
+ */
+ispa_status_t ispa_select_layers(int32_t n_layers, const double* eps, int32_t k, int32_t* selected,
+                                 int32_t* rank, void* stream);
+
+/*
+ * ispa_absorb_apply — W_l += dW_l for the selected layers.
+ *
+ * Source: ISPA technical summary, section 2, step 3 "Memory-Efficient
+ * Inference" (the converted layers use W_new = W + dW from then on).
+ *   W, dW [n_layers, d, d_out] float32 DEVICE, stacked as in
+ *   ispa_absorb_solve; selected [k] int32 DEVICE layer ids (as written by
+ *   ispa_select_layers), which must be distinct; an id outside
+ *   [0, n_layers) is skipped.  Unselected layers are untouched.  Each sum is
+ *   one float32 addition, the same value ispa_absorb_solve writes to W_new.
+ */
+ispa_status_t ispa_absorb_apply(int32_t d, int32_t d_out, int32_t n_layers, const int32_t* selected,
+                                int32_t k, const float* dW, float* W, void* stream);
 
 /* Human-readable name of a status code (static string). */
 const char* ispa_status_string(ispa_status_t status);

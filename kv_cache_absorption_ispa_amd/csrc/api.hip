@@ -236,6 +236,30 @@ ispa_status_t ispa_layer_eps(int32_t d, int32_t d_out, int32_t batch, const floa
                     (hipStream_t)stream);
 }
 
+ispa_status_t ispa_select_layers(int32_t n_layers, const double* eps, int32_t k, int32_t* selected, int32_t* rank,
+                                 void* stream) {
+  if (n_layers < 1 || n_layers > MAX_STACK_LAYERS) return invalid("n_layers must be in [1, 4096]");
+  if (k < 0 || k > n_layers) return invalid("k must be in [0, n_layers]");
+  if (!req(eps) || (k > 0 && !req(selected)) || !opt(selected) || !opt(rank))
+    return invalid("eps (and selected when k > 0) must be non-NULL and 16-byte aligned");
+  ispa_status_t st = check_current_device();
+  if (st != ISPA_OK) return st;
+  return launch_select_layers(n_layers, eps, k, selected, rank, (hipStream_t)stream);
+}
+
+ispa_status_t ispa_absorb_apply(int32_t d, int32_t d_out, int32_t n_layers, const int32_t* selected, int32_t k,
+                                const float* dW, float* W, void* stream) {
+  if (d <= 0 || d_out <= 0 || ((int64_t)d * d_out) % 4 != 0) return invalid("d * d_out must be a positive multiple of 4");
+  if (n_layers < 1 || n_layers > 65535) return invalid("n_layers must be in [1, 65535]");
+  if (k < 0 || k > n_layers) return invalid("k must be in [0, n_layers]");
+  if (k > 0 && (!req(selected) || !req(dW) || !req(W)))
+    return invalid("selected, dW, W must be non-NULL and 16-byte aligned");
+  if (k == 0) return ISPA_OK;
+  ispa_status_t st = check_current_device();
+  if (st != ISPA_OK) return st;
+  return launch_absorb_apply(d, d_out, n_layers, selected, k, dW, W, (hipStream_t)stream);
+}
+
 const char* ispa_status_string(ispa_status_t s) {
   switch (s) {
     case ISPA_OK: return "ISPA_OK";

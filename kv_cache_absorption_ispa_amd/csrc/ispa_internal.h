@@ -65,6 +65,12 @@ ispa_status_t launch_eps(int32_t d, int32_t d_out, int32_t batch, const float* G
                          const float* Qff, const float* W, const float* dW, float lambda, double* eps_abs,
                          double* eps_rel, void* ws, size_t ws_bytes, hipStream_t s);
 
+constexpr int MAX_STACK_LAYERS = 4096;
+ispa_status_t launch_select_layers(int32_t n_layers, const double* eps, int32_t k, int32_t* selected,
+                                   int32_t* rank, hipStream_t s);
+ispa_status_t launch_absorb_apply(int32_t d, int32_t d_out, int32_t n_layers, const int32_t* selected, int32_t k,
+                                  const float* dW, float* W, hipStream_t s);
+
 // ---------------------------------------------------------------- device helpers
 // Map a linear workgroup id so that ids dispatched to the same XCD (the
 // hardware deals workgroups round-robin over the 8 XCDs) get consecutive

@@ -23,7 +23,7 @@ ISPA_F32, ISPA_BF16 = 0, 1
 EXPORTS = [
     "ispa_decomp_attn", "ispa_decomp_attn_workspace_size", "ispa_full_attn", "ispa_lse_merge", "ispa_gram_workspace_size", "ispa_gram_accum",
     "ispa_absorb_workspace_size", "ispa_absorb_solve", "ispa_eps_workspace_size", "ispa_layer_eps",
-    "ispa_status_string", "ispa_last_error", "ispa_version", "ispa_device_check",
+    "ispa_select_layers", "ispa_absorb_apply", "ispa_status_string", "ispa_last_error", "ispa_version", "ispa_device_check",
 ]
 
 
@@ -68,6 +68,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "ispa_absorb_solve": (I32, [I32, I32, I32, P, P, P, F, P, P, P, P, SZ, P]),
         "ispa_eps_workspace_size": (SZ, [I32, I32, I32]),
         "ispa_layer_eps": (I32, [I32, I32, I32, P, P, P, P, P, F, P, P, P, SZ, P]),
+        "ispa_select_layers": (I32, [I32, P, I32, P, P, P]),
+        "ispa_absorb_apply": (I32, [I32, I32, I32, P, I32, P, P, P]),
         "ispa_status_string": (ctypes.c_char_p, [I32]),
         "ispa_last_error": (ctypes.c_char_p, []),
         "ispa_version": (I32, []),
@@ -254,6 +256,28 @@ def ispa_layer_eps(G, C, Q_ff, W, dW, lam: float, eps_abs, eps_rel, *, workspace
     lib = load_library()
     _check(lib.ispa_layer_eps(d, d_out, b, _ptr(G), _ptr(C), _ptr(Q_ff), _ptr(W), _ptr(dW), float(lam),
                               _ptr(eps_abs), _ptr(eps_rel), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def ispa_select_layers(eps, k: int, selected, rank=None, *, stream=None) -> None:
+    """selected[:k] = ids of the k layers with the lowest eps (ties to the lower id, NaN last)."""
+    n = eps.numel()
+    _expect(eps.reshape(-1), (n,), torch.float64, "eps")
+    _expect(selected.reshape(-1), (k,), torch.int32, "selected")
+    if rank is not None:
+        _expect(rank.reshape(-1), (n,), torch.int32, "rank")
+    lib = load_library()
+    _check(lib.ispa_select_layers(n, _ptr(eps), int(k), _ptr(selected), _ptr(rank), _stream(stream)))
+
+
+def ispa_absorb_apply(selected, dW, W, *, stream=None) -> None:
+    """W[l] += dW[l] for every layer id l in `selected`; W, dW [n_layers, d, d_out] float32."""
+    n, d, d_out = W.shape
+    _expect(dW, (n, d, d_out), torch.float32, "dW")
+    _expect(W, (n, d, d_out), torch.float32, "W")
+    k = selected.numel()
+    _expect(selected.reshape(-1), (k,), torch.int32, "selected")
+    lib = load_library()
+    _check(lib.ispa_absorb_apply(d, d_out, n, _ptr(selected), k, _ptr(dW), _ptr(W), _stream(stream)))
 
 
 def ispa_version() -> int:

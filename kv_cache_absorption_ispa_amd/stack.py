@@ -1,0 +1,147 @@
+"""A stack of attention layers through warmup, transition and post-absorb chunks.
+
+Source: "Technical Summary: Instance-Specific Parametric Absorption (ISPA) for
+Memory-Efficient Video Generation", section 2 "Methodology": step 1 (every
+layer runs the dual-stream warmup and collects A_loc / A_full), step 2 (closed
+form absorb), step 3 (the converted layers use W + dW, drop their history KV
+and attend locally from then on) and "Dynamic Layer Selection" (all layers are
+ranked by reconstruction error; the lowest-error ones are converted).
+
+This module is host orchestration only: it owns the per-layer device state
+(stacked G, C, Q_ff, W, dW) and issues the library's calls; every arithmetic
+step runs in the HIP kernels behind the C ABI.  Reading used for the ranking:
+every layer is solved (batched), its post-fit error eps_rel comes from the Gram
+statistics, and the k lowest (ties to the lower layer index) are converted.
+"""
+from __future__ import annotations
+
+from typing import List, Optional
+
+import torch
+
+from . import ispa
+
+
+class LayerStack:
+    """Per-layer state of an n_layers stack of attention layers with the same shape.
+
+    ``W`` is the stacked output-projection weight [n_layers, d, d_out] (float32,
+    device); it is updated in place for the converted layers at the transition.
+    """
+
+    def __init__(self, W: torch.Tensor, heads: int, head_dim: int, n_q: int, lam: float, n_convert: int,
+                 dtype: torch.dtype = torch.bfloat16, stream=None):
+        if W.dim() != 3 or W.dtype != torch.float32 or not W.is_cuda:
+            raise ispa.IspaError(ispa.ISPA_E_INVALID_ARG, "W must be a [n_layers, d, d_out] float32 device tensor")
+        self.n_layers, self.d, self.d_out = (int(s) for s in W.shape)
+        if self.d != heads * head_dim:
+            raise ispa.IspaError(ispa.ISPA_E_INVALID_ARG, "W's d must equal heads * head_dim")
+        if not 0 <= n_convert <= self.n_layers:
+            raise ispa.IspaError(ispa.ISPA_E_INVALID_ARG, "n_convert must be in [0, n_layers]")
+        self.heads, self.head_dim, self.n_q = heads, head_dim, n_q
+        self.lam = float(lam)
+        self.n_convert = n_convert
+        self.dtype = dtype
+        self.stream = stream
+        dev = W.device
+        L, d, do = self.n_layers, self.d, self.d_out
+        self.W = W
+        f32 = dict(dtype=torch.float32, device=dev)
+        self.G = torch.zeros(L, d, d, **f32)
+        self.C = torch.zeros(L, d, d, **f32)
+        self.Q_ff = torch.zeros(L, d, d, **f32)
+        self.dW = torch.zeros(L, d, do, **f32)
+        self.info = torch.zeros(L, dtype=torch.int32, device=dev)
+        self.eps_abs = torch.zeros(L, dtype=torch.float64, device=dev)
+        self.eps_rel = torch.zeros(L, dtype=torch.float64, device=dev)
+        self.selected = torch.zeros(max(n_convert, 1), dtype=torch.int32, device=dev)[:n_convert]
+        self.rank = torch.zeros(L, dtype=torch.int32, device=dev)
+        self.chunks_seen = [0] * L
+        self.converted: Optional[List[int]] = None  # host copy after the transition
+        # workspaces, sized once
+        self._gram_ws = None
+        self._attn_ws = None
+        self._absorb_ws = ispa.workspace(ispa.ispa_absorb_workspace_size(d, do, L), dev)
+        self._eps_ws = ispa.workspace(ispa.ispa_eps_workspace_size(d, do, L), dev)
+
+    def reset(self) -> None:
+        """Start a new warmup with the same buffers (W is the caller's; restore it first if needed)."""
+        self.chunks_seen = [0] * self.n_layers
+        self.converted = None
+
+    # ------------------------------------------------------------------ warmup
+    def warmup_chunk(self, layer: int, q, k_loc, v_loc, k_hist, v_hist, o_loc, o_full,
+                     lse_loc=None, lse_full=None) -> None:
+        """Dual-stream attention of one chunk of `layer`, then its rows into the layer's G, C, Q_ff.
+
+        ``o_loc`` / ``o_full`` [n_q, H, D] receive A_loc / A_full of this chunk."""
+        if self.converted is not None:
+            raise ispa.IspaError(ispa.ISPA_E_INVALID_ARG, "warmup is over (transition already ran)")
+        n_hist = 0 if k_hist is None else int(k_hist.shape[0])
+        need = ispa.ispa_decomp_attn_workspace_size(q, int(k_loc.shape[0]), n_hist)
+        if need and (self._attn_ws is None or self._attn_ws.numel() < need):
+            self._attn_ws = ispa.workspace(need, q.device)
+        ispa.ispa_decomp_attn(q, k_loc, v_loc, k_hist, v_hist, o_loc=o_loc, lse_loc=lse_loc, o_full=o_full,
+                              lse_full=lse_full, workspace=self._attn_ws, stream=self.stream)
+        n_rows = int(q.shape[0])
+        need = ispa.ispa_gram_workspace_size(n_rows, self.d, q.dtype)
+        if need and (self._gram_ws is None or self._gram_ws.numel() < need):
+            self._gram_ws = ispa.workspace(need, q.device)
+        ispa.ispa_gram_accum(o_loc, o_full, self.G[layer], self.C[layer], self.Q_ff[layer],
+                             accumulate=self.chunks_seen[layer] > 0, workspace=self._gram_ws, stream=self.stream)
+        self.chunks_seen[layer] += 1
+
+    # -------------------------------------------------------------- transition
+    def transition(self) -> List[int]:
+        """Solve every layer (batched), rank by eps_rel, convert the n_convert lowest: W += dW there.
+
+        Returns the converted layer ids (lowest error first); this is the one host sync of the
+        transition (the host needs the set to launch the post-absorb chunks)."""
+        if self.converted is not None:
+            raise ispa.IspaError(ispa.ISPA_E_INVALID_ARG, "transition already ran")
+        if min(self.chunks_seen) == 0:
+            raise ispa.IspaError(ispa.ISPA_E_INVALID_ARG, "every layer needs at least one warmup chunk")
+        self.solve_and_rank()
+        return self.convert()
+
+    def solve_and_rank(self) -> None:
+        """The transition's device work before the weights change: batched solve, eps, ranking."""
+        ispa.ispa_absorb_solve(self.G, self.C, self.W, self.lam, self.dW, self.info, workspace=self._absorb_ws,
+                               stream=self.stream)
+        ispa.ispa_layer_eps(self.G, self.C, self.Q_ff, self.W, self.dW, self.lam, self.eps_abs, self.eps_rel,
+                            workspace=self._eps_ws, stream=self.stream)
+        ispa.ispa_select_layers(self.eps_rel, self.n_convert, self.selected, self.rank, stream=self.stream)
+
+    def convert(self) -> List[int]:
+        """W += dW on the selected layers; returns their ids (a host sync)."""
+        if self.converted is not None:
+            raise ispa.IspaError(ispa.ISPA_E_INVALID_ARG, "layers already converted")
+        ispa.ispa_absorb_apply(self.selected, self.dW, self.W, stream=self.stream)
+        self.converted = [int(x) for x in self.selected.cpu().tolist()]
+        return self.converted
+
+    # ------------------------------------------------------------- post-absorb
+    def is_converted(self, layer: int) -> bool:
+        if self.converted is None:
+            raise ispa.IspaError(ispa.ISPA_E_INVALID_ARG, "transition has not run")
+        return layer in self.converted
+
+    def post_chunk(self, layer: int, q, k_loc, v_loc, k_hist, v_hist, o_full, lse_full=None) -> None:
+        """Attention of one post-absorb chunk: local keys only for a converted layer (its history is
+        evicted; ``k_hist`` / ``v_hist`` are ignored and may be None), all keys otherwise.
+        ``o_full`` receives the layer's attention output."""
+        if self.is_converted(layer):
+            ispa.ispa_decomp_attn(q, k_loc, v_loc, None, None, o_full=o_full, lse_full=lse_full, stream=self.stream)
+            return
+        need = ispa.ispa_decomp_attn_workspace_size(q, int(k_loc.shape[0]), int(k_hist.shape[0]))
+        if need and (self._attn_ws is None or self._attn_ws.numel() < need):
+            self._attn_ws = ispa.workspace(need, q.device)
+        ispa.ispa_decomp_attn(q, k_loc, v_loc, k_hist, v_hist, o_full=o_full, lse_full=lse_full,
+                              workspace=self._attn_ws, stream=self.stream)
+
+    def evicted_kv_bytes(self, n_hist: int) -> int:
+        """History K and V bytes the converted layers no longer hold (n_hist keys per layer)."""
+        if self.converted is None:
+            return 0
+        elt = 2 if self.dtype == torch.bfloat16 else 4
+        return len(self.converted) * 2 * n_hist * self.heads * self.head_dim * elt

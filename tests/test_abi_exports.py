@@ -19,7 +19,7 @@ def header_functions():
 def test_header_lists_the_entry_points():
     names = header_functions()
     for n in ("ispa_decomp_attn", "ispa_gram_accum", "ispa_absorb_solve", "ispa_full_attn", "ispa_lse_merge",
-              "ispa_layer_eps"):
+              "ispa_layer_eps", "ispa_select_layers", "ispa_absorb_apply"):
         assert n in names
     assert sorted(ispa.EXPORTS) == names
 
@@ -66,6 +66,17 @@ def test_validation_errors_need_no_gpu():
     assert lib.ispa_gram_accum(10, 128, ispa.ISPA_BF16, *([None] * 5), 2, None, 0, None) == ispa.ISPA_E_INVALID_ARG
     assert lib.ispa_lse_merge(0, None, None, 4, 2, 64, 1, None, None, None) == ispa.ISPA_E_INVALID_ARG
     assert lib.ispa_lse_merge(17, None, None, 4, 2, 64, 1, None, None, None) == ispa.ISPA_E_INVALID_ARG
+    # layer selection: k within [0, n_layers], at most 4096 layers, eps required
+    assert lib.ispa_select_layers(30, ok, 31, ok, None, None) == ispa.ISPA_E_INVALID_ARG
+    assert lib.ispa_select_layers(30, ok, -1, ok, None, None) == ispa.ISPA_E_INVALID_ARG
+    assert lib.ispa_select_layers(4097, ok, 1, ok, None, None) == ispa.ISPA_E_INVALID_ARG
+    assert lib.ispa_select_layers(30, None, 15, ok, None, None) == ispa.ISPA_E_INVALID_ARG
+    assert lib.ispa_select_layers(30, ok, 15, None, None, None) == ispa.ISPA_E_INVALID_ARG
+    assert lib.ispa_absorb_apply(128, 128, 30, ok, 31, ok, ok, None) == ispa.ISPA_E_INVALID_ARG
+    assert lib.ispa_absorb_apply(128, 128, 30, None, 15, ok, ok, None) == ispa.ISPA_E_INVALID_ARG
+    assert lib.ispa_absorb_apply(3, 5, 30, ok, 15, ok, ok, None) == ispa.ISPA_E_INVALID_ARG
+    # nothing to apply: succeeds without touching the device
+    assert lib.ispa_absorb_apply(128, 128, 30, None, 0, None, None, None) == ispa.ISPA_OK
 
 
 @pytest.mark.skipif(not os.path.exists(ispa.LIB_PATH), reason="libispa.so not built")
