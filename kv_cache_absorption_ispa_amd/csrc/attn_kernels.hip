@@ -14,12 +14,13 @@
 //    lane%32) for 16 keys: the softmax row max and row sum are in-lane, plus
 //    one exchange between the two 32-lane halves.
 //  * O^T = V^T P^T accumulates on the same MFMA; P goes from the score
-//    accumulator straight into the B operand (no LDS round trip).  V is
-//    stored transposed in LDS with the keys of each 16-key group permuted
-//    (bits 2 and 3 of the key index swapped) so that the 8 keys a lane's P
-//    register holds are 8 contiguous LDS elements: one ds_read_b128.
-//  * K and V^T tiles of 64 keys are double-buffered in LDS; the next tile's
-//    global loads are issued before the current tile's MFMAs.
+//    accumulator straight into the B operand (no LDS round trip).  The V^T
+//    operand comes from the row-major V tile through transposing LDS reads
+//    (ds_read_b64_tr_b16).
+//  * K and V tiles of 64 keys are double-buffered in LDS and filled straight
+//    from global memory by buffer loads into LDS, issued before the current
+//    tile's MFMAs; 16-byte chunks are permuted per row so that the K reads and
+//    the transposing V reads are free of bank conflicts.
 //  * Local tiles then history tiles form one tile sequence (the pipeline does
 //    not drain at the branch switch).  At the switch the local branch is
 //    normalised and written (O_loc, LSE_loc); its float32 values go to the
@@ -69,12 +70,26 @@ __device__ __forceinline__ float other_half(float x) {
 __device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
 __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
 
+// Slot of 16-byte chunk c of tile row r in LDS: c ^ kv_swizzle<D>(r).  The LDS has
+// 64 four-byte banks (256 bytes per cycle).  The K operand reads take one
+// chunk from each of 16 consecutive rows per 16-lane pass, and the
+// transposing V reads take 4 consecutive chunks from each of 4 consecutive
+// rows per 32-lane pass; a plain XOR with (r & 7) would leave both 2-way and
+// 4-way bank conflicts.  XOR-ing with a bit rotation of the row's low bits
+// puts the 16 rows of a K pass on 16 different slots, and the 4 rows of a V
+// pass on 4 different groups of 4 slots, so both read patterns are
+// conflict-free.  (D = 64: rows are 128 bytes, two rows per bank cycle.)
+template <int D>
+__device__ __forceinline__ int kv_swizzle(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
 // QB = 32-query blocks per wave (1: 32 queries per wave; 2: 64 queries, one wave per SIMD).
 //
 // K and V tiles (BN keys x D) are kept row-major in LDS, each row's 16-byte
-// chunks XOR-swizzled by (row & 7) so that both the K operand reads (8 rows,
-// same chunk) and the transposing V reads (8 rows, 4 chunks) spread over all
-// banks.  They are filled straight from global memory by buffer loads into LDS
+// chunks permuted by kv_swizzle so that both the K operand reads and the
+// transposing V reads are free of bank conflicts.  They are filled straight from global memory by buffer loads into LDS
 // (a wave moves 1 KB per load), so tile staging costs no VGPRs and no LDS
 // store instructions; rows past the branch's end read as 0 (range-checked).
 template <int D, int NW, int QB>
@@ -102,7 +117,8 @@ __global__ __launch_bounds__(NW * 64, (QB == 1 && NW <= 4) ? 2 : 1) void attn_bf
   __shared__ __attribute__((aligned(1024))) uint16_t sV1[BN * D];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: load targets stay scalar
   const int l32 = lane & 31, hh = lane >> 5;
   const uint32_t unit = xcd_remap(blockIdx.x, p.nblocks);
   const int head = unit / p.n_qtiles, qt = unit % p.n_qtiles;
@@ -139,13 +155,13 @@ __global__ __launch_bounds__(NW * 64, (QB == 1 && NW <= 4) ? 2 : 1) void attn_bf
   }
 
   // This wave's tile loads: load j is wave load g = wave + j*NW of the tile (K loads first, then V).
-  // Lane i fills row r0 + i/CPR, slot i%CPR, with the row's chunk (slot ^ (row & 7)).
+  // Lane i fills row r0 + i/CPR, slot i%CPR, with the row's chunk slot ^ kv_swizzle(row).
   uint32_t gofs[WLW];
 #pragma unroll
   for (int j = 0; j < WLW; ++j) {
     const int g = wave + j * NW;
     const int row = (g % WLT) * RPW + lane / CPR;
-    const int chunk = (lane % CPR) ^ (row & 7);
+    const int chunk = (lane % CPR) ^ kv_swizzle<D>(row);
     gofs[j] = (uint32_t)row * row_bytes + (uint32_t)(head * D + chunk * 8) * 2u;
   }
 
@@ -179,11 +195,12 @@ __global__ __launch_bounds__(NW * 64, (QB == 1 && NW <= 4) ? 2 : 1) void attn_bf
   // (sched_barrier keeps the compiler from sinking them next to their use).
   constexpr int NS = NKB * KK;      // K fragments per tile: (kb, kk), chains of the NKB accumulators interleaved
   constexpr int NV = DB * NKB * 2;  // V fragments per tile: (db, kb, mm), DB accumulators interleaved
-  // K operand: row kb*32 + l32, chunk 2kk + hh (swizzled by row & 7 == l32 & 7).
+  // K operand: row kb*32 + l32, chunk 2kk + hh (the swizzle depends on row & 15 == l32 & 15).
+  const int ksw = kv_swizzle<D>(l32);
   auto kfrag = [&](const uint16_t* sKb, int i) {
     const int kb = i % NKB, kk = i / NKB;
     const int row = kb * 32 + l32;
-    return __builtin_bit_cast(bf16x8, *(const u32x4*)(&sKb[row * D + (((2 * kk + hh) ^ (l32 & 7)) << 3)]));
+    return __builtin_bit_cast(bf16x8, *(const u32x4*)(&sKb[row * D + (((2 * kk + hh) ^ ksw) << 3)]));
   };
   // V^T operand of O^T = V^T P^T for lane (dim 32db + lane%32, hh): keys 32kb + 16mm + 4hh + {0..3}
   // and + 8 + {0..3} (the key order of the P accumulator), read with two transposing loads.
@@ -191,12 +208,13 @@ __global__ __launch_bounds__(NW * 64, (QB == 1 && NW <= 4) ? 2 : 1) void attn_bf
   const int q16 = lane >> 4, i16 = lane & 15;
   const int vdim = 16 * (q16 & 1) + 4 * (i16 & 3);  // dim offset within the 32-dim block
   const int vkey = 4 * (q16 >> 1) + (i16 >> 2);     // key offset within the 16-key step
+  const int vsw_a = kv_swizzle<D>(vkey), vsw_b = kv_swizzle<D>(vkey + 8);  // keys are vkey (+8) mod 16
   auto vfrag = [&](const uint16_t* sVb, int i) {
     const int db = i % DB, j = i / DB, kb = j / 2, mm = j % 2;
     const int d0 = 32 * db + vdim;
     const int key_a = 32 * kb + 16 * mm + vkey, key_b = key_a + 8;
-    const uint16_t* pa = &sVb[key_a * D + (((d0 >> 3) ^ (key_a & 7)) << 3) + (d0 & 7)];
-    const uint16_t* pb = &sVb[key_b * D + (((d0 >> 3) ^ (key_b & 7)) << 3) + (d0 & 7)];
+    const uint16_t* pa = &sVb[key_a * D + (((d0 >> 3) ^ vsw_a) << 3) + (d0 & 7)];
+    const uint16_t* pb = &sVb[key_b * D + (((d0 >> 3) ^ vsw_b) << 3) + (d0 & 7)];
     const u32x2 a = lds_read_tr(pa), b = lds_read_tr(pb);
     return __builtin_bit_cast(bf16x8, u32x4{a.x, a.y, b.x, b.y});
   };

@@ -26,6 +26,12 @@ namespace {
 constexpr int GT = 128;      // output tile edge
 constexpr int GBK = 32;      // rows per stage
 
+// Slot of 16-byte chunk c of staged row r: c ^ gram_swizzle(r).  Each 32-lane
+// pass of a transposing operand read takes 4 consecutive chunks from each of 4
+// consecutive rows; giving those rows different groups of 4 slots keeps the
+// read free of bank conflicts (64 four-byte banks, 256-byte rows).
+__device__ __forceinline__ int gram_swizzle(int r) { return (r & 3) << 2; }
+
 struct GramParams {
   const uint16_t* Al;
   const uint16_t* Af;
@@ -78,7 +84,7 @@ __global__ __launch_bounds__(256, 2) void gram_bf16_kernel(GramParams p) {
   for (int j = 0; j < WLW; ++j) {
     const int g = wave + 4 * j, mtx = g / WLM;
     const int rr = (g % WLM) * RPW + lane / CPR;
-    const int chunk = (lane % CPR) ^ (rr & 7);
+    const int chunk = (lane % CPR) ^ gram_swizzle(rr);
     const int col0 = (mtx == 0 || mtx == 3) ? I0 : J0;
     gofs[j] = (uint32_t)rr * row_bytes + (uint32_t)(col0 + chunk * 8) * 2u;
   }
@@ -97,14 +103,14 @@ __global__ __launch_bounds__(256, 2) void gram_bf16_kernel(GramParams p) {
   const int q16 = lane >> 4, i16 = lane & 15;
   const int trow = 4 * (q16 >> 1) + (i16 >> 2);  // row within each 8-row half of a 16-row step
   const int tcol = 16 * (q16 & 1) + 4 * (i16 & 3);
-  // The swizzle depends on (row & 7) == trow, a lane constant, so each operand block has one
+  // The swizzle depends on row & 3 == trow & 3, a lane constant, so each operand block has one
   // per-lane base offset; the row step is a compile-time offset.
   int offI[2], offJ[2];
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
     const int ci = wi + 32 * x + tcol, cj = wj + 32 * x + tcol;
-    offI[x] = trow * GT + (((ci >> 3) ^ trow) << 3) + (ci & 7);
-    offJ[x] = trow * GT + (((cj >> 3) ^ trow) << 3) + (cj & 7);
+    offI[x] = trow * GT + (((ci >> 3) ^ gram_swizzle(trow)) << 3) + (ci & 7);
+    offJ[x] = trow * GT + (((cj >> 3) ^ gram_swizzle(trow)) << 3) + (cj & 7);
   }
   auto frag = [&](const uint16_t* t, int off, int ks) {
     const uint16_t* q = t + off + 16 * ks * GT;
