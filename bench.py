@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--gen-workers", type=int, default=min(16, os.cpu_count() or 1),
                     help="processes drawing the 30-layer stack's inputs (config 4)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prewarm", type=float, default=1.0, metavar="SECONDS",
+                    help="untimed steps for this long before the warmup steps (GPU clocks settle)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU seconds for the oracle sample")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes (calibrates HBM byte counters)")
@@ -129,29 +131,28 @@ def main():
         if events is not None:
             events[-1][1].record()
 
-    log(f"[bench] warmup {args.warmup} steps")
+    prewarm_steps = prewarm(step, args.prewarm)
+    log(f"[bench] prewarm {prewarm_steps} steps, warmup {args.warmup} steps")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     if info.item() != 0:
         raise RuntimeError(f"absorb failed, info = {info.item()}")
 
-    # ---- timed region: exactly K steps, whole-job wall clock
+    # ---- timed region: exactly K steps, whole-job wall clock; per-kernel durations from HIP events
+    # recorded on the launch stream around each call of the same steps
     log(f"[bench] timing {args.steps} steps")
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
+           for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    for k in range(args.steps):
+        step(evs[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
-
-    # ---- per-kernel durations with events on the launch stream (separate pass, same work)
     attn_ms, gram_ms, solve_ms = [], [], []
-    for _ in range(args.steps):
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
-        step(ev)
-        torch.cuda.synchronize()
+    for ev in evs:
         for c in range(cfg.n_chunks):
             attn_ms.append(ev[2 * c][0].elapsed_time(ev[2 * c][1]))
             gram_ms.append(ev[2 * c + 1][0].elapsed_time(ev[2 * c + 1][1]))
@@ -199,6 +200,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "prewarm_steps": prewarm_steps,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -220,7 +222,7 @@ def main():
         "absorb_ms_per_layer": round(float(np.mean(solve_ms)), 4),
         "roofline": {
             "bound": "mfma",
-            "kernel": "attn_bf16_kernel (ispa_decomp_attn)",
+            "kernel": "attn_bf16_kernel<128, 8, 1> (ispa_decomp_attn)",
             "achieved": round(achieved, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
@@ -317,7 +319,8 @@ def bench_stack(args, host_inputs):
         mark("t4")
         return conv
 
-    log("[bench] stack warmup pass")
+    pw = prewarm(run, args.prewarm)
+    log(f"[bench] stack prewarm {pw} passes, warmup {args.warmup} passes")
     for _ in range(args.warmup):
         conv = run()
     torch.cuda.synchronize()
@@ -400,6 +403,21 @@ def bench_stack(args, host_inputs):
     print(json.dumps(result), flush=True)
 
 
+def prewarm(step, seconds: float) -> int:
+    """Untimed steps for `seconds` so the GPU clocks settle before the warmup steps."""
+    import torch
+
+    n = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        step()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n
+
+
 def kernel_source_sha() -> str:
     import hashlib
 
@@ -409,8 +427,9 @@ def kernel_source_sha() -> str:
 
 
 def cpu_baseline(cfg, target_s: float):
-    """The oracle (float64 numpy, as it stands) on a bounded sample of the same workload:
-    decomposable attention of a subset of one chunk's queries over all local and history keys."""
+    """The oracle (float64 numpy, as it stands) on a bounded sample of the same workload: decomposable
+    attention (both branches and the merge) of whole warmup chunks, the last one possibly cut to a query
+    prefix, over all local and history keys, stopping after about target_s seconds."""
     import oracle
     from kv_cache_absorption_ispa_amd import inputs
 
@@ -420,34 +439,44 @@ def cpu_baseline(cfg, target_s: float):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = os.cpu_count() or 1
-    x = inputs.chunk_inputs(cfg, 0, 0)
-    q, kl, vl, kh, vh = x.q.f64, x.k_loc.f64, x.v_loc.f64, x.k_hist.f64, x.v_hist.f64
-    def decomposed(qs):
+    def decomposed(x, qs):
+        kl, vl, kh, vh = x.k_loc.f64, x.v_loc.f64, x.k_hist.f64, x.v_hist.f64
         o_l, l_l = oracle.attention(qs, kl, vl, cfg.scale)
         o_h, l_h = oracle.attention(qs, kh, vh, cfg.scale)
         return oracle.merge(o_l, l_l, o_h, l_h)
 
+    # grow the query sample of chunk 0 until one run takes a measurable time
+    x0 = inputs.chunk_inputs(cfg, 0, 0)
+    q0 = x0.q.f64
     n = 32
-    t = 0.0
-    while True:  # grow the sample until one run takes a measurable time
+    while True:
         t0 = time.perf_counter()
-        decomposed(q[:n])
+        decomposed(x0, q0[:n])
         t = time.perf_counter() - t0
         if t > 0.5 or n >= cfg.n_q:
             break
         n = min(cfg.n_q, n * 4)
-    n_final = int(min(cfg.n_q, max(n, n * target_s / max(t, 1e-3))))
-    t0 = time.perf_counter()
-    decomposed(q[:n_final])
-    t = time.perf_counter() - t0
-    flops = 4.0 * n_final * (cfg.n_loc + cfg.n_hist) * cfg.head_dim * cfg.heads
+    # then whole warmup chunks (or a query prefix of one) up to about target_s of CPU time
+    per_q = t / n
+    done_q, elapsed, chunks = 0, 0.0, 0
+    for c in range(cfg.n_chunks):
+        want = int(min(cfg.n_q, max(32, (target_s - elapsed) / per_q)))
+        x = x0 if c == 0 else inputs.chunk_inputs(cfg, 0, c)
+        t0 = time.perf_counter()
+        decomposed(x, x.q.f64[:want])
+        elapsed += time.perf_counter() - t0
+        done_q += want
+        chunks += 1
+        if want < cfg.n_q or elapsed >= target_s:
+            break
+    flops = 4.0 * done_q * (cfg.n_loc + cfg.n_hist) * cfg.head_dim * cfg.heads
     return {
-        "value": round(flops / t / 1e12, 5),
+        "value": round(flops / elapsed / 1e12, 5),
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"{n_final} of {cfg.n_q} queries of one chunk, all {cfg.heads} heads, "
-                  f"{cfg.n_loc}+{cfg.n_hist} keys; {t:.1f} s",
+        "sample": f"{done_q} queries ({chunks} of {cfg.n_chunks} warmup chunks, {cfg.n_q} queries each), all "
+                  f"{cfg.heads} heads, {cfg.n_loc}+{cfg.n_hist} keys, decomposed attention and merge; {elapsed:.1f} s",
     }
 
 
