@@ -230,99 +230,166 @@ __global__ __launch_bounds__(256) void init_shift_kernel(const float* __restrict
   *(f32x4*)(M + b * dd + i4) = v;
 }
 
-// Factor the 64x64 diagonal block at (k0, k0) of each layer's working matrix:
-// M_kk = L L^T, written over M's lower triangle, and L^-1, written into the
-// inverse's diagonal block.  Thread (r = tid/4, cg = tid%4) keeps row r at
-// columns cg, cg+4, ..., cg+60 in registers; each step publishes one column
-// of the Schur complement through LDS (one barrier per column).  The update
-// uses the unscaled complement S: S_ic -= S_ij S_cj / S_jj, and L_ic =
-// S_ic / sqrt(S_cc) at the end (which also gives L_cc = sqrt(S_cc)).
+// Cholesky of the NB x NB diagonal block at (k0, k0) of each layer (lower L written in place, the
+// strict upper part of the block left as it is) and its inverse L^-1 into the same block of Linvf
+// (zeros above the diagonal).  info[b] = k0 + j + 1 if the leading minor of order k0 + j + 1 of
+// G + lambda I is not positive definite (LAPACK potrf convention); then nothing is written.
+//
+// One workgroup of 4 waves; wave w holds block column w (16 columns) with lane i = row i.  The
+// 16 pivot steps of a block column run inside its wave (cross-lane reads, no barrier); the wave
+// publishes the finished columns in LDS, the later block columns subtract their rank-16 update
+// in parallel, and meanwhile the wave inverts its 16 x 16 diagonal block.  The off-diagonal blocks
+// of L^-1 follow by two doubling levels, inv([A 0; B C]) = [A^-1 0; -C^-1 B A^-1  C^-1].
+constexpr int SB = NB / 4;     // block column width
+constexpr int LSTR = NB + 4;   // LDS row stride (floats): rows stay 16-byte aligned for vector reads
+static_assert(NB == 64 && SB == 16, "the diagonal kernel maps 64 rows onto the 64 lanes of a wave");
+
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+
 __global__ __launch_bounds__(256) void potrf_diag_kernel(float* M, int d, int k0, float* Linvf, int32_t* info) {
   const int b = blockIdx.x;
   if (info[b] != 0) return;
-  __shared__ __attribute__((aligned(16))) float col[2][4][16];  // a column, element c stored at [c%4][c/4]
-  __shared__ float piv[NB];
-  __shared__ float Ls[NB][NB + 1];
-  const int tid = threadIdx.x, r = tid >> 2, cg = tid & 3;
+  __shared__ __attribute__((aligned(16))) float Ls[NB][LSTR];  // L (zeros above the diagonal)
+  __shared__ __attribute__((aligned(16))) float Xs[NB][LSTR];  // L^-1
+  __shared__ __attribute__((aligned(16))) float Ts[32][36];    // product scratch of the doubling steps
+  __shared__ int fail_s;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   float* Mb = M + (size_t)b * d * d + (size_t)k0 * d + k0;
-  float a[16];
+
+  float a[SB];  // row `lane`, columns SB*wave .. SB*wave+15
+  {
+    const float* src = Mb + (size_t)lane * d + SB * wave;
 #pragma unroll
-  for (int m = 0; m < 16; ++m) {
-    const int c = cg + 4 * m;
-    a[m] = c <= r ? Mb[(size_t)r * d + c] : 0.f;
-  }
-  int fail = -1;
+    for (int q = 0; q < SB / 4; ++q) {
+      const f32x4 v = *(const f32x4*)(src + 4 * q);
 #pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    const int buf = j & 1;
-    if (cg == (j & 3)) col[buf][r & 3][r >> 2] = a[j >> 2];
-    __syncthreads();
-    const float dj = col[buf][j & 3][j >> 2];
-    if (!(dj > 0.f)) {
-      fail = j;
-      break;
+      for (int e = 0; e < 4; ++e) a[4 * q + e] = v[e];
     }
-    if (tid == 0) piv[j] = dj;
-    if (r > j) {
-      const float f = col[buf][r & 3][r >> 2] / dj;
+  }
+  // zero X outside the diagonal 16-blocks (the lower blocks are filled by the doubling steps)
+  for (int e = tid; e < NB * NB; e += 256) {
+    const int rr = e / NB, cc = e % NB;
+    if (rr / SB != cc / SB) Xs[rr][cc] = 0.f;
+  }
+  if (tid == 0) fail_s = 0;
+  __syncthreads();
+
+  for (int kb = 0; kb < NB / SB; ++kb) {
+    const int c0 = SB * kb;
+    if (wave == kb) {
+      // right-looking steps inside the block column; rows above c0 + j carry values that are
+      // never used (only lanes >= c0 + j feed pivots and multipliers) and are masked on publication.
+      // A failed pivot is recorded and the steps run on; nothing is published then.
+      int failed = 0;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4 v = *(const f32x4*)(&col[buf][cg][4 * q]);
+      for (int j = 0; j < SB; ++j) {
+        const float piv = readlane_f(a[j], c0 + j);
+        if (!(piv > 0.f) && failed == 0) failed = c0 + j + 1;
+        const float lij = a[j] * __builtin_amdgcn_rsqf(piv);  // v_rsq_f32 (pivots are normal positives)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int c = cg + 4 * (4 * q + e);
-          if (c > j && c <= r) a[4 * q + e] = fmaf(-f, v[e], a[4 * q + e]);
-        }
+        for (int k = j + 1; k < SB; ++k) a[k] = fmaf(-lij, readlane_f(lij, c0 + k), a[k]);
+        a[j] = lij;
       }
-    }
-  }
-  if (fail >= 0) {
-    if (tid == 0) info[b] = k0 + fail + 1;
-    return;
-  }
-  __syncthreads();
+      if (failed) {
+        if (lane == 0) fail_s = k0 + failed;
+      } else {
 #pragma unroll
-  for (int m = 0; m < 16; ++m) {
-    const int c = cg + 4 * m;
-    const float l = c <= r ? a[m] * rsqrtf(piv[c]) : 0.f;
-    Ls[r][c] = l;
-    if (c <= r) Mb[(size_t)r * d + c] = l;
-  }
-  __syncthreads();
-  // X = L^-1 by forward substitution on the identity, one row of X per step
-  float x[16];
-#pragma unroll
-  for (int m = 0; m < 16; ++m) x[m] = (cg + 4 * m == r) ? 1.f : 0.f;
-#pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    const int buf = i & 1;
-    if (r == i) {
-      const float inv = 1.f / Ls[i][i];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        f32x4 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          x[4 * q + e] *= inv;
-          v[e] = x[4 * q + e];
-        }
-        *(f32x4*)(&col[buf][cg][4 * q]) = v;
+        for (int m = 0; m < SB; m += 4)
+          *(f32x4*)(&Ls[lane][c0 + m]) = f32x4{lane >= c0 + m ? a[m] : 0.f, lane >= c0 + m + 1 ? a[m + 1] : 0.f,
+                                              lane >= c0 + m + 2 ? a[m + 2] : 0.f, lane >= c0 + m + 3 ? a[m + 3] : 0.f};
       }
     }
     __syncthreads();
-    if (r > i) {
-      const float lri = Ls[r][i];
+    if (fail_s != 0) {
+      if (tid == 0) info[b] = fail_s;
+      return;
+    }
+    if (wave > kb) {
+      // a[:, m] -= L[:, block kb] L[SB*wave + m, block kb]^T
+      // (16 independent accumulation chains: the FMAs are not latency-bound)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4 v = *(const f32x4*)(&col[buf][cg][4 * q]);
+      for (int q = 0; q < SB / 4; ++q) {
+        const f32x4 li = *(const f32x4*)(&Ls[lane][c0 + 4 * q]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[4 * q + e] = fmaf(-lri, v[e], x[4 * q + e]);
+        for (int m = 0; m < SB; ++m) {
+          const f32x4 lc = *(const f32x4*)(&Ls[SB * wave + m][c0 + 4 * q]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) a[m] = fmaf(-li[e], lc[e], a[m]);
+        }
+      }
+    } else if (wave == kb) {
+      // inverse of the diagonal block (rows c0 .. c0+15 = lanes): lane c0+i keeps row i of
+      // X = L_kk^-1 unnormalised, x = e_i - sum_{p<i} L[i][p] X[p]; row k is final once divided
+      // by L[k][k].  Lanes outside the block compute values that are never stored.
+      float x[SB];
+#pragma unroll
+      for (int c = 0; c < SB; ++c) x[c] = (lane == c0 + c) ? 1.f : 0.f;
+#pragma unroll
+      for (int k = 0; k < SB - 1; ++k) {
+        const float inv_kk = __builtin_amdgcn_rcpf(readlane_f(a[k], c0 + k));
+        const float t = lane > c0 + k ? a[k] * inv_kk : 0.f;  // L[i][k] / L[k][k] for the rows below k
+#pragma unroll
+        for (int c = 0; c <= k; ++c) x[c] = fmaf(-t, readlane_f(x[c], c0 + k), x[c]);
+      }
+      // lane c0+i: X[i] = x / L[i][i]; a[i] of lane c0+i is L[i][i]: read it from LDS
+      const float inv_ii = lane >= c0 && lane < c0 + SB ? __builtin_amdgcn_rcpf(Ls[lane][lane]) : 0.f;
+      if (lane >= c0 && lane < c0 + SB) {
+#pragma unroll
+        for (int c = 0; c < SB; c += 4)
+          *(f32x4*)(&Xs[lane][c0 + c]) = f32x4{x[c] * inv_ii, x[c + 1] * inv_ii, x[c + 2] * inv_ii, x[c + 3] * inv_ii};
       }
     }
   }
+  __syncthreads();
+
+  // ---- level 1: X[hi][lo] = -X[hi][hi] L[hi][lo] X[lo][lo] for 16-block pairs (0,1) and (2,3),
+  // waves 1 and 3 (lane (i, g): row i, columns 4g .. 4g+3 of the 16 x 16 result)
+  if (wave & 1) {
+    const int lo = SB * (wave - 1), hi = SB * wave;
+    const int i = lane & 15, g = lane >> 4;
+    const int tr = (wave >> 1) * SB;
+    // (four partial sums per product keep the FMA chains short)
+    f32x4 t[4] = {};  // (L[hi][lo] X[lo][lo])[i][4g .. 4g+3]
+#pragma unroll
+    for (int p = 0; p < SB; ++p) t[p & 3] += Ls[hi + i][lo + p] * *(const f32x4*)(&Xs[lo + p][lo + 4 * g]);
+    *(f32x4*)(&Ts[tr + i][4 * g]) = (t[0] + t[1]) + (t[2] + t[3]);
+    __builtin_amdgcn_wave_barrier();  // the same wave reads Ts back (LDS is in order within a wave)
+    f32x4 o[4] = {};
+#pragma unroll
+    for (int p = 0; p < SB; ++p) o[p & 3] += Xs[hi + i][hi + p] * *(const f32x4*)(&Ts[tr + p][4 * g]);
+    *(f32x4*)(&Xs[hi + i][lo + 4 * g]) = -((o[0] + o[1]) + (o[2] + o[3]));
+  }
+  __syncthreads();
+
+  // ---- level 2: X[32:64][0:32] = -X[32:64][32:64] L[32:64][0:32] X[0:32][0:32]; thread: row tid / 8,
+  // columns 4 (tid % 8) .. +3 of the 32 x 32 result
+  {
+    const int i = tid >> 3, c = 4 * (tid & 7);
+    f32x4 t[4] = {};
+#pragma unroll
+    for (int p = 0; p < 32; ++p) t[p & 3] += Ls[32 + i][p] * *(const f32x4*)(&Xs[p][c]);
+    *(f32x4*)(&Ts[i][c]) = (t[0] + t[1]) + (t[2] + t[3]);
+    __syncthreads();
+    f32x4 o[4] = {};
+#pragma unroll
+    for (int p = 0; p < 32; ++p) o[p & 3] += Xs[32 + i][32 + p] * *(const f32x4*)(&Ts[p][c]);
+    *(f32x4*)(&Xs[32 + i][c]) = -((o[0] + o[1]) + (o[2] + o[3]));
+  }
+  __syncthreads();
+
   float* Xb = Linvf + (size_t)b * d * d + (size_t)k0 * d + k0;
-#pragma unroll
-  for (int m = 0; m < 16; ++m) Xb[(size_t)r * d + cg + 4 * m] = x[m];
+  for (int e = tid; e < NB * NB / 4; e += 256) {
+    const int rr = e / (NB / 4), cc = 4 * (e % (NB / 4));
+    *(f32x4*)(Xb + (size_t)rr * d + cc) = *(const f32x4*)(&Xs[rr][cc]);
+    if (cc + 3 <= rr) {
+      *(f32x4*)(Mb + (size_t)rr * d + cc) = *(const f32x4*)(&Ls[rr][cc]);
+    } else if (cc <= rr) {
+      for (int q = 0; q <= rr - cc; ++q) Mb[(size_t)rr * d + cc + q] = Ls[rr][cc + q];
+    }
+  }
 }
 
 // dW = X + correction, or NaN for failed layers; W_new = W + dW for the others (W_new may be W).
