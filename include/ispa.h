@@ -165,7 +165,8 @@ size_t ispa_absorb_workspace_size(int32_t d, int32_t d_out, int32_t batch);
  * objective and its closed-form minimiser, non-iterative) and step 3
  * "Memory-Efficient Inference" (W_new = W + dW).  Computes, per batch entry,
  * M = G + lambda I, M = L L^T (blocked Cholesky, float32), R = C W,
- * L Y = R, L^T dW = Y.
+ * L Y = R, L^T dW = Y (through the explicit L^-1), then one refinement
+ * step: r = R - (G + lambda I) dW accumulated in float64, dW += M^-1 r.
  *
  *   G, C [batch, d, d]; W [batch, d, d_out]; dW [batch, d, d_out]; all float32.
  *   W_new [batch, d, d_out] may be NULL or equal to W (in-place absorb).

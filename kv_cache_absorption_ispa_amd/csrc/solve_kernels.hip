@@ -139,7 +139,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
 struct GemmDParams {
   const float* A;      // M x K, row-major (lda)
   const float* B;      // K x N, row-major (ldb)
-  const double* Cin;   // M x N float64 (ldc), nullable
+  const float* Cin;    // M x N float32 (ldc), nullable; widened to float64 in the epilogue
   const float* X;      // M x N float32 (ldx), nullable
   double* D64;         // nullable
   float* D32;          // nullable
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(256) void gemm_f64acc_kernel(GemmDParams p) {
         const int r = m0 + wm + 16 * i + 4 * v + g;
         const int c = n0 + wn + 16 * j + l16;
         double x = p.alpha * acc[i][j][v];
-        if (p.Cin) x += p.beta * p.Cin[b * p.sC + (size_t)r * p.ldc + c];
+        if (p.Cin) x += p.beta * (double)p.Cin[b * p.sC + (size_t)r * p.ldc + c];
         if (p.X) x += p.gamma * (double)p.X[b * p.sX + (size_t)r * p.ldx + c];
         if (p.D64) p.D64[b * p.sD + (size_t)r * p.ldd + c] = x;
         if (p.D32) p.D32[b * p.sD + (size_t)r * p.ldd + c] = (float)x;
@@ -466,7 +466,7 @@ ispa_status_t gemm(hipStream_t s, int batch, int M, int N, int K, const float* A
 }
 
 ispa_status_t gemm_d(hipStream_t s, int batch, int M, int N, int K, const float* A, int lda, size_t sA,
-                     const float* B, int ldb, size_t sB, const double* Cin, int ldc, size_t sC, const float* X,
+                     const float* B, int ldb, size_t sB, const float* Cin, int ldc, size_t sC, const float* X,
                      int ldx, size_t sX, double* D64, float* D32, int ldd, size_t sD, double alpha, double beta,
                      double gamma, const int32_t* info) {
   GemmDParams p;
@@ -493,8 +493,7 @@ size_t absorb_workspace_size(int32_t d, int32_t d_out, int32_t batch) {
   return b * d * d * sizeof(float)          // factor L (lower triangle of M)
          + b * d * d * sizeof(float)        // L^-1
          + b * d * d * sizeof(float)        // intermediate products of the inverse
-         + b * d * d_out * sizeof(double)   // R = C W in float64
-         + 2 * b * d * d_out * sizeof(float);  // residual / correction and an intermediate
+         + 3 * b * d * d_out * sizeof(float);  // R = C W, the residual / correction, an intermediate
 }
 
 namespace {
@@ -564,17 +563,17 @@ ispa_status_t launch_absorb(int32_t d, int32_t d_out, int32_t batch, const float
   float* M = (float*)ws;
   float* Linvf = M + (size_t)batch * dd;
   float* Tb = Linvf + (size_t)batch * dd;
-  double* R64 = (double*)(Tb + (size_t)batch * dd);
-  float* Rr = (float*)(R64 + (size_t)batch * dn);
+  float* Rb = Tb + (size_t)batch * dd;
+  float* Rr = Rb + (size_t)batch * dn;
   float* Zb = Rr + (size_t)batch * dn;
   const int nblk = d / NB;
 
   hipLaunchKernelGGL(init_shift_kernel, dim3((unsigned)((dd / 4 + 255) / 256), batch), dim3(256), 0, s, G, M, d,
                      lambda, info);
   ISPA_TRY(hip_check(hipGetLastError(), "init_shift_kernel launch"));
-  // R = C W (float64 accumulation), kept in float64 and rounded into Rr as the first right-hand side
-  ISPA_TRY(gemm_d(s, batch, d, d_out, d, C, d, dd, W, d_out, dn, nullptr, 0, 0, nullptr, 0, 0, R64, Rr, d_out, dn,
-                  1.0, 0.0, 0.0, nullptr));
+  // R = C W (float32; R's rounding perturbs the solution like the float32 statistics themselves do)
+  ISPA_TRY((gemm<false, false>(s, batch, d, d_out, d, C, d, dd, W, d_out, dn, nullptr, 0, 0, Rb, d_out, dn, 1.f, 0.f,
+                               false, nullptr)));
   // Cholesky, right-looking by 64-column panels
   for (int k = 0; k < nblk; ++k) {
     const int k0 = k * NB;
@@ -596,9 +595,10 @@ ispa_status_t launch_absorb(int32_t d, int32_t d_out, int32_t batch, const float
   // inv([A 0; B C]) has off-diagonal block -C^-1 (B A^-1); pairs of equal sizes run as one launch.
   ISPA_TRY(invert_lower(s, batch, d, M, Linvf, Tb, info));
   // X = (L L^T)^-1 R
-  ISPA_TRY(chol_apply(s, batch, d, d_out, Linvf, Rr, Zb, dW, info));
-  // refinement: r = R - G X - lambda X (float64), correction = (L L^T)^-1 r
-  ISPA_TRY(gemm_d(s, batch, d, d_out, d, G, d, dd, dW, d_out, dn, R64, d_out, dn, dW, d_out, dn, nullptr, Rr, d_out,
+  ISPA_TRY(chol_apply(s, batch, d, d_out, Linvf, Rb, Zb, dW, info));
+  // refinement: r = R - G X - lambda X accumulated in float64 (the cancellation needs it),
+  // correction = (L L^T)^-1 r
+  ISPA_TRY(gemm_d(s, batch, d, d_out, d, G, d, dd, dW, d_out, dn, Rb, d_out, dn, dW, d_out, dn, nullptr, Rr, d_out,
                   dn, -1.0, 1.0, -(double)lambda, info));
   ISPA_TRY(chol_apply(s, batch, d, d_out, Linvf, Rr, Zb, Rr, info));
   hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)((dn / 4 + 255) / 256), batch), dim3(256), 0, s, W, dW,

@@ -83,11 +83,17 @@ class LayerStack:
             self._attn_ws = ispa.workspace(need, q.device)
         ispa.ispa_decomp_attn(q, k_loc, v_loc, k_hist, v_hist, o_loc=o_loc, lse_loc=lse_loc, o_full=o_full,
                               lse_full=lse_full, workspace=self._attn_ws, stream=self.stream)
-        n_rows = int(q.shape[0])
-        need = ispa.ispa_gram_workspace_size(n_rows, self.d, q.dtype)
+        self.accumulate_rows(layer, o_loc, o_full)
+
+    def accumulate_rows(self, layer: int, a_loc, a_full) -> None:
+        """Add warmup rows computed elsewhere ([n, d] or [n, H, D]) to the layer's G, C, Q_ff."""
+        if self.converted is not None:
+            raise ispa.IspaError(ispa.ISPA_E_INVALID_ARG, "warmup is over (transition already ran)")
+        n_rows = int(a_loc.shape[0])
+        need = ispa.ispa_gram_workspace_size(n_rows, self.d, a_loc.dtype)
         if need and (self._gram_ws is None or self._gram_ws.numel() < need):
-            self._gram_ws = ispa.workspace(need, q.device)
-        ispa.ispa_gram_accum(o_loc, o_full, self.G[layer], self.C[layer], self.Q_ff[layer],
+            self._gram_ws = ispa.workspace(need, a_loc.device)
+        ispa.ispa_gram_accum(a_loc, a_full, self.G[layer], self.C[layer], self.Q_ff[layer],
                              accumulate=self.chunks_seen[layer] > 0, workspace=self._gram_ws, stream=self.stream)
         self.chunks_seen[layer] += 1
 
