@@ -166,19 +166,22 @@ def main():
     lse_single = torch.empty(H, nq, device="cuda")
     # back-to-back launches, like the attention calls inside the steps (an isolated launch after a
     # synchronisation would also time the GPU's wake-up)
-    for _ in range(3):
-        ispa.ispa_full_attn(ch["q"], kcat, vcat, o=o_single, lse=lse_single)
-    full_ms = []
-    n_single = 10
-    for _ in range(3):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(n_single):
-            ispa.ispa_full_attn(ch["q"], kcat, vcat, o=o_single, lse=lse_single)
-        e1.record()
-        torch.cuda.synchronize()
-        full_ms.append(e0.elapsed_time(e1) / n_single)
+    full_ms = back_to_back_ms(lambda: ispa.ispa_full_attn(ch["q"], kcat, vcat, o=o_single, lse=lse_single))
     del kcat, vcat
+
+    # ---- the same chunk with its keys as a streaming cache holds them: sink and chunk in their own
+    # buffers, the history as the two runs of a wrapped ring (two chunks, then one), attended in place
+    ns, nc = cfg.n_sink, cfg.n_chunk
+    loc_segs = [(ch["kl"][:ns].clone(), ch["vl"][:ns].clone()), (ch["kl"][ns:].clone(), ch["vl"][ns:].clone())]
+    cut = (cfg.n_hist // nc - 1) * nc if cfg.n_hist % nc == 0 and cfg.n_hist > nc else cfg.n_hist // 2
+    hist_segs = [(ch["kh"][:cut].clone(), ch["vh"][:cut].clone()), (ch["kh"][cut:].clone(), ch["vh"][cut:].clone())]
+    seg_ms = back_to_back_ms(lambda: ispa.ispa_decomp_attn_segments(
+        ch["q"], loc_segs, hist_segs, o_loc=o_loc, lse_loc=lse[0], o_hist=o_hist, lse_hist=lse[1], o_full=o_full,
+        lse_full=lse[2], workspace=atws))
+    two_ms = back_to_back_ms(lambda: ispa.ispa_decomp_attn(
+        ch["q"], ch["kl"], ch["vl"], ch["kh"], ch["vh"], o_loc=o_loc, lse_loc=lse[0], o_hist=o_hist,
+        lse_hist=lse[1], o_full=o_full, lse_full=lse[2], workspace=atws))
+    del loc_segs, hist_segs
     gemm_ref = reference_gemm_tflops()
 
     attn_flops = cfg.attn_flops()
@@ -224,6 +227,13 @@ def main():
         "single_pass_ms": round(float(np.median(full_ms)), 4),
         "ratio_decomp_vs_single_pass": round(attn_avg / float(np.median(full_ms)), 4),
         "reference_bf16_gemm_tflops": gemm_ref,
+        "segments": {
+            "layout": f"local [{ns} sink | {nc} chunk], history [{cut} | {cfg.n_hist - cut}] (wrapped ring)",
+            "ms": round(float(np.median(seg_ms)), 4),
+            "two_buffer_ms": round(float(np.median(two_ms)), 4),
+            "ratio_vs_two_buffer": round(float(np.median(seg_ms)) / float(np.median(two_ms)), 4),
+            "tflops": round(attn_flops / (float(np.median(seg_ms)) * 1e-3) / 1e12, 2),
+        },
         "gram_ms_per_chunk": round(float(np.mean(gram_ms)), 4),
         "absorb_ms_per_layer": round(float(np.mean(solve_ms)), 4),
         "roofline": {
@@ -426,6 +436,23 @@ def reference_gemm_tflops(n: int = 8192, reps: int = 20) -> float:
     e1.record()
     torch.cuda.synchronize()
     return round(2.0 * n ** 3 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
+
+
+def back_to_back_ms(fn, n: int = 10, rounds: int = 3, warm: int = 3):
+    """Per-launch ms of `fn`, launched n times back to back, for each of `rounds` rounds."""
+    import torch
+    for _ in range(warm):
+        fn()
+    out = []
+    for _ in range(rounds):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) / n)
+    return out
 
 
 def prewarm(step, seconds: float) -> int:

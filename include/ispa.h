@@ -9,6 +9,8 @@
  *
  *   ispa_decomp_attn   local and historical attention branches plus their
  *                      log-sum-exp merge (A_loc and A_full rows),
+ *   ispa_decomp_attn_segments  the same over a list of K/V segments
+ *                      (sink, chunk, history pages) attended in place,
  *   ispa_gram_accum    G = A_loc^T A_loc and C = A_loc^T (A_full - A_loc),
  *   ispa_absorb_solve  dW = (G + lambda I)^-1 C W  (Cholesky + triangular solves),
  *   ispa_layer_eps     the post-fit reconstruction error used to rank layers,
@@ -103,6 +105,45 @@ ispa_status_t ispa_decomp_attn(const ispa_attn_desc_t* desc, const void* Q, cons
                                const void* V_loc, const void* K_hist, const void* V_hist, void* O_loc,
                                float* LSE_loc, void* O_hist, float* LSE_hist, void* O_full,
                                float* LSE_full, void* workspace, size_t workspace_bytes, void* stream);
+
+/* At most this many K/V segments per ispa_decomp_attn_segments call. */
+#define ISPA_MAX_KV_SEGMENTS 16
+
+/* One contiguous run of cached keys and values: K, V [n_rows, H, D] (dtype). */
+typedef struct {
+  const void* K;
+  const void* V;
+  int64_t n_rows; /* >= 1 */
+} ispa_kv_segment_t;
+
+/*
+ * ispa_decomp_attn_segments — ispa_decomp_attn over keys given as a list of
+ * segments instead of one K_loc and one K_hist buffer (one launch).
+ *
+ * Source: ISPA technical summary, section 2 "Methodology": step 1 (the local
+ * stream sees the sink tokens plus the current chunk, the full stream the
+ * whole context) and step 3 (a converted layer drops its history K/V while
+ * the sink stays); the streaming generation appends every finished chunk's
+ * keys to the history.  A cache kept as separate buffers (a sink buffer, the
+ * current chunk, history pages or a wrapped ring buffer) is attended in place,
+ * with no concatenation copy.
+ *
+ * segs[0 .. n_loc_segs-1] are the local branch's keys, segs[n_loc_segs ..
+ * n_segs-1] the history branch's, in order; `segs` is a HOST array read
+ * during the call.  1 <= n_loc_segs <= n_segs <= ISPA_MAX_KV_SEGMENTS; every
+ * segment has n_rows >= 1 and 16-byte aligned K, V; the local rows must add
+ * up to desc->n_loc and the history rows to desc->n_hist (ISPA_E_INVALID_ARG
+ * otherwise).  Within a branch the softmax is over the union of its segments,
+ * so results depend on the keys, not on how they are split; the order of
+ * floating-point accumulation follows the segments, so a different split of
+ * the same keys may round differently.  Outputs, workspace and errors are
+ * those of ispa_decomp_attn (same workspace size for the same desc).
+ */
+ispa_status_t ispa_decomp_attn_segments(const ispa_attn_desc_t* desc, const void* Q,
+                                        const ispa_kv_segment_t* segs, int32_t n_segs, int32_t n_loc_segs,
+                                        void* O_loc, float* LSE_loc, void* O_hist, float* LSE_hist,
+                                        void* O_full, float* LSE_full, void* workspace,
+                                        size_t workspace_bytes, void* stream);
 
 /* Workspace bytes ispa_decomp_attn needs for this shape: n_q*H*D*4 for bf16
  * with history keys (the float32 O_loc the merge reads), else 0.  Needed only

@@ -80,6 +80,66 @@ ispa_status_t check_attn_desc(const ispa_attn_desc_t* d, bool allow_hist) {
   return ISPA_OK;
 }
 
+// One local segment and, with history keys, one history segment.
+KvSegments two_segments(const ispa_attn_desc_t* d, const void* Kl, const void* Vl, const void* Kh, const void* Vh) {
+  KvSegments kv = {};
+  kv.K[0] = Kl;
+  kv.V[0] = Vl;
+  kv.n[0] = d->n_loc;
+  kv.n_loc_seg = 1;
+  kv.n_seg = 1;
+  if (d->n_hist > 0) {
+    kv.K[1] = Kh;
+    kv.V[1] = Vh;
+    kv.n[1] = d->n_hist;
+    kv.n_seg = 2;
+  }
+  return kv;
+}
+
+ispa_status_t check_decomp_outputs(const ispa_attn_desc_t* desc, void* O_loc, float* LSE_loc, void* O_hist,
+                                   float* LSE_hist, void* O_full, float* LSE_full, void* workspace,
+                                   size_t workspace_bytes) {
+  if (!opt(O_loc) || !opt(LSE_loc) || !opt(O_hist) || !opt(LSE_hist) || !opt(O_full) || !opt(LSE_full) ||
+      !opt(workspace))
+    return invalid("output and workspace pointers must be 16-byte aligned");
+  const size_t ws_need = desc->n_q < 0 || desc->n_hist < 0
+                             ? 0
+                             : attention_workspace_size(desc->n_q, desc->heads, desc->head_dim, desc->n_hist,
+                                                        desc->dtype);
+  if (O_full != nullptr && ws_need > 0 && (workspace == nullptr || workspace_bytes < ws_need)) {
+    set_error("workspace smaller than ispa_decomp_attn_workspace_size()");
+    return ISPA_E_WORKSPACE;
+  }
+  return ISPA_OK;
+}
+
+ispa_status_t run_decomp(const ispa_attn_desc_t* desc, const void* Q, const KvSegments& kv, void* O_loc,
+                         float* LSE_loc, void* O_hist, float* LSE_hist, void* O_full, float* LSE_full,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  const ispa_status_t st = check_current_device();
+  if (st != ISPA_OK) return st;
+  AttnArgs a;
+  a.Q = Q;
+  a.kv = kv;
+  a.O_loc = O_loc;
+  a.LSE_loc = LSE_loc;
+  a.O_hist = O_hist;
+  a.LSE_hist = LSE_hist;
+  a.O_full = O_full;
+  a.LSE_full = LSE_full;
+  a.n_q = desc->n_q;
+  a.n_loc = desc->n_loc;
+  a.n_hist = desc->n_hist;
+  a.heads = desc->heads;
+  a.head_dim = desc->head_dim;
+  a.scale = desc->scale;
+  a.dtype = desc->dtype;
+  a.ws = workspace;
+  a.ws_bytes = workspace_bytes;
+  return launch_attention(a, (hipStream_t)stream);
+}
+
 }  // namespace
 }  // namespace ispa
 
@@ -102,38 +162,40 @@ ispa_status_t ispa_decomp_attn(const ispa_attn_desc_t* desc, const void* Q, cons
     return invalid("Q, K_loc, V_loc must be non-NULL and 16-byte aligned");
   if (desc->n_hist > 0 && (!req(K_hist) || !req(V_hist)))
     return invalid("K_hist, V_hist must be non-NULL and 16-byte aligned when n_hist > 0");
-  if (!opt(O_loc) || !opt(LSE_loc) || !opt(O_hist) || !opt(LSE_hist) || !opt(O_full) || !opt(LSE_full) ||
-      !opt(workspace))
-    return invalid("output and workspace pointers must be 16-byte aligned");
-  const size_t ws_need = ispa_decomp_attn_workspace_size(desc);
-  if (O_full != nullptr && ws_need > 0 && (workspace == nullptr || workspace_bytes < ws_need)) {
-    set_error("ispa_decomp_attn: workspace smaller than ispa_decomp_attn_workspace_size()");
-    return ISPA_E_WORKSPACE;
-  }
-  st = check_current_device();
+  st = check_decomp_outputs(desc, O_loc, LSE_loc, O_hist, LSE_hist, O_full, LSE_full, workspace, workspace_bytes);
   if (st != ISPA_OK) return st;
-  AttnArgs a;
-  a.Q = Q;
-  a.Kl = K_loc;
-  a.Vl = V_loc;
-  a.Kh = desc->n_hist > 0 ? K_hist : nullptr;
-  a.Vh = desc->n_hist > 0 ? V_hist : nullptr;
-  a.O_loc = O_loc;
-  a.LSE_loc = LSE_loc;
-  a.O_hist = O_hist;
-  a.LSE_hist = LSE_hist;
-  a.O_full = O_full;
-  a.LSE_full = LSE_full;
-  a.n_q = desc->n_q;
-  a.n_loc = desc->n_loc;
-  a.n_hist = desc->n_hist;
-  a.heads = desc->heads;
-  a.head_dim = desc->head_dim;
-  a.scale = desc->scale;
-  a.dtype = desc->dtype;
-  a.ws = workspace;
-  a.ws_bytes = workspace_bytes;
-  return launch_attention(a, (hipStream_t)stream);
+  return run_decomp(desc, Q, two_segments(desc, K_loc, V_loc, K_hist, V_hist), O_loc, LSE_loc, O_hist, LSE_hist,
+                    O_full, LSE_full, workspace, workspace_bytes, stream);
+}
+
+ispa_status_t ispa_decomp_attn_segments(const ispa_attn_desc_t* desc, const void* Q, const ispa_kv_segment_t* segs,
+                                        int32_t n_segs, int32_t n_loc_segs, void* O_loc, float* LSE_loc,
+                                        void* O_hist, float* LSE_hist, void* O_full, float* LSE_full,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+  ispa_status_t st = check_attn_desc(desc, true);
+  if (st != ISPA_OK) return st;
+  if (segs == nullptr) return invalid("segs is NULL");
+  if (n_segs < 1 || n_segs > ISPA_MAX_KV_SEGMENTS) return invalid("n_segs must be in [1, ISPA_MAX_KV_SEGMENTS]");
+  if (n_loc_segs < 1 || n_loc_segs > n_segs) return invalid("n_loc_segs must be in [1, n_segs]");
+  if (desc->n_q > 0 && !req(Q)) return invalid("Q must be non-NULL and 16-byte aligned");
+  int64_t sum_loc = 0, sum_hist = 0;
+  KvSegments kv = {};
+  for (int i = 0; i < n_segs; ++i) {
+    if (segs[i].n_rows < 1) return invalid("every segment needs n_rows >= 1");
+    if (!req(segs[i].K) || !req(segs[i].V)) return invalid("segment K, V must be non-NULL and 16-byte aligned");
+    (i < n_loc_segs ? sum_loc : sum_hist) += segs[i].n_rows;
+    kv.K[i] = segs[i].K;
+    kv.V[i] = segs[i].V;
+    kv.n[i] = segs[i].n_rows;
+  }
+  if (sum_loc != desc->n_loc || sum_hist != desc->n_hist)
+    return invalid("segment rows must add up to desc->n_loc (local) and desc->n_hist (history)");
+  kv.n_seg = n_segs;
+  kv.n_loc_seg = n_loc_segs;
+  st = check_decomp_outputs(desc, O_loc, LSE_loc, O_hist, LSE_hist, O_full, LSE_full, workspace, workspace_bytes);
+  if (st != ISPA_OK) return st;
+  return run_decomp(desc, Q, kv, O_loc, LSE_loc, O_hist, LSE_hist, O_full, LSE_full, workspace, workspace_bytes,
+                    stream);
 }
 
 ispa_status_t ispa_full_attn(const ispa_attn_desc_t* desc, const void* Q, const void* K, const void* V, void* O,
@@ -146,8 +208,11 @@ ispa_status_t ispa_full_attn(const ispa_attn_desc_t* desc, const void* Q, const 
   if (st != ISPA_OK) return st;
   AttnArgs a = {};
   a.Q = Q;
-  a.Kl = K;
-  a.Vl = V;
+  a.kv.K[0] = K;
+  a.kv.V[0] = V;
+  a.kv.n[0] = desc->n_loc + desc->n_hist;
+  a.kv.n_seg = 1;
+  a.kv.n_loc_seg = 1;
   a.O_loc = O;
   a.LSE_loc = LSE;
   a.n_q = desc->n_q;

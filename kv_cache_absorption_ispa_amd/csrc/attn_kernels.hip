@@ -42,10 +42,13 @@ constexpr float LN2 = 0.6931471805599453f;
 
 struct AttnKParams {
   const uint16_t* Q;
-  const uint16_t* Kl;
-  const uint16_t* Vl;
-  const uint16_t* Kh;
-  const uint16_t* Vh;
+  // key segments: tiles st0[s] .. st0[s+1]-1 of the tile sequence come from segment s (n[s] rows);
+  // segments [0, n_loc_seg) are the local branch
+  const uint16_t* Ks[MAX_KV_SEGS];
+  const uint16_t* Vs[MAX_KV_SEGS];
+  int sn[MAX_KV_SEGS];
+  int st0[MAX_KV_SEGS + 1];
+  int n_seg, n_loc_seg;
   uint16_t* O_loc;
   float* LSE_loc;
   uint16_t* O_hist;
@@ -53,7 +56,7 @@ struct AttnKParams {
   uint16_t* O_full;
   float* LSE_full;
   float* stash;  // float32 O_loc kept for the merge ([n_q, H, D]); used when O_full and history exist
-  int n_q, n_loc, n_hist, heads;
+  int n_q, heads;
   float c2;  // scale * log2(e)
   int n_qtiles, nblocks;
 };
@@ -122,17 +125,20 @@ __global__ __launch_bounds__(NW * 64, (QB == 1 && NW <= 4) ? 2 : 1) void attn_bf
   const int l32 = lane & 31, hh = lane >> 5;
   const uint32_t unit = xcd_remap(blockIdx.x, p.nblocks);
   const int head = unit / p.n_qtiles, qt = unit % p.n_qtiles;
-  const int n_q = p.n_q, n_loc = p.n_loc, n_hist = p.n_hist;
+  const int n_q = p.n_q;
   const uint32_t HD = (uint32_t)p.heads * D;
   const uint32_t row_bytes = HD * 2u;
   const float c2 = p.c2;
-  const int Tl = (n_loc + BN - 1) / BN;
-  const int Th = (n_hist + BN - 1) / BN;
-  const int T = Tl + Th;
-  const rsrc_t rKl = make_rsrc(p.Kl, (uint32_t)n_loc * row_bytes);
-  const rsrc_t rVl = make_rsrc(p.Vl, (uint32_t)n_loc * row_bytes);
-  const rsrc_t rKh = make_rsrc(p.Kh, (uint32_t)n_hist * row_bytes);
-  const rsrc_t rVh = make_rsrc(p.Vh, (uint32_t)n_hist * row_bytes);
+  const int Tl = p.st0[p.n_loc_seg];  // local tiles, then history tiles
+  const int T = p.st0[p.n_seg];
+  const int Th = T - Tl;
+  // segment of tile t (wave-uniform; a handful of scalar compares)
+  auto seg_of = [&](int t) {
+    int s = 0;
+#pragma unroll
+    for (int i = 1; i < MAX_KV_SEGS; ++i) s += (i < p.n_seg && t >= p.st0[i]) ? 1 : 0;
+    return s;
+  };
 
   int myq[QB];
   bool qvalid[QB];
@@ -166,10 +172,10 @@ __global__ __launch_bounds__(NW * 64, (QB == 1 && NW <= 4) ? 2 : 1) void attn_bf
   }
 
   auto load_tile = [&](int t, uint16_t* sKb, uint16_t* sVb) {
-    const bool loc = t < Tl;
-    const uint32_t tb = (uint32_t)((loc ? t : t - Tl) * BN) * row_bytes;
-    const rsrc_t rk = loc ? rKl : rKh;
-    const rsrc_t rv = loc ? rVl : rVh;
+    const int sg = seg_of(t);
+    const uint32_t tb = (uint32_t)((t - p.st0[sg]) * BN) * row_bytes;
+    const rsrc_t rk = make_rsrc(p.Ks[sg], (uint32_t)p.sn[sg] * row_bytes);
+    const rsrc_t rv = make_rsrc(p.Vs[sg], (uint32_t)p.sn[sg] * row_bytes);
 #pragma unroll
     for (int j = 0; j < WLW; ++j) {
       const int g = wave + j * NW;
@@ -220,8 +226,9 @@ __global__ __launch_bounds__(NW * 64, (QB == 1 && NW <= 4) ? 2 : 1) void attn_bf
   };
 
   auto compute_tile = [&](const uint16_t* sKb, const uint16_t* sVb, int t) {
-    const int key0 = (t < Tl ? t : t - Tl) * BN;
-    const int nvalid = t < Tl ? n_loc : n_hist;
+    const int sg = seg_of(t);
+    const int key0 = (t - p.st0[sg]) * BN;
+    const int nvalid = p.sn[sg];
     f32x16 s[QB][NKB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
@@ -439,17 +446,17 @@ __global__ __launch_bounds__(NW * 64, (QB == 1 && NW <= 4) ? 2 : 1) void attn_bf
 // ----------------------------------------------------------------------------
 struct AttnF32Params {
   const float* Q;
-  const float* Kl;
-  const float* Vl;
-  const float* Kh;
-  const float* Vh;
+  const float* Ks[MAX_KV_SEGS];  // key segments; [0, n_loc_seg) local, the rest history
+  const float* Vs[MAX_KV_SEGS];
+  int sn[MAX_KV_SEGS];
+  int n_seg, n_loc_seg;
   float* O_loc;
   float* LSE_loc;
   float* O_hist;
   float* LSE_hist;
   float* O_full;
   float* LSE_full;
-  int n_q, n_loc, n_hist, heads;
+  int n_q, n_hist, heads;
   float c2;
   int n_qtiles;
 };
@@ -473,21 +480,25 @@ __global__ __launch_bounds__(F32_NT) void attn_f32_kernel(AttnF32Params p) {
   float lse2_loc = -INFINITY, lse2_hist = -INFINITY, inv_hist = 0.f;
   float acc[D];
   for (int br = 0; br < 2; ++br) {
-    const float* Kp = br == 0 ? p.Kl : p.Kh;
-    const float* Vp = br == 0 ? p.Vl : p.Vh;
-    const int n = br == 0 ? p.n_loc : p.n_hist;
     float m = -INFINITY, l = 0.f;
     for (int e = 0; e < D; ++e) acc[e] = 0.f;
-    for (int k0 = 0; k0 < n; k0 += F32_BN) {
+    const int s_end = br == 0 ? p.n_loc_seg : p.n_seg;
+    int n = 0;  // keys of this branch
+    for (int sg = br == 0 ? 0 : p.n_loc_seg; sg < s_end; ++sg) {
+    const float* Kp = p.Ks[sg];
+    const float* Vp = p.Vs[sg];
+    const int ns = p.sn[sg];
+    n += ns;
+    for (int k0 = 0; k0 < ns; k0 += F32_BN) {
       __syncthreads();
       for (int i = tid; i < F32_BN * D; i += F32_NT) {
         const int r = i / D, c = i % D;
         const int key = k0 + r;
-        sK[r][c] = key < n ? Kp[(size_t)key * HD + head * D + c] : 0.f;
-        sV[r][c] = key < n ? Vp[(size_t)key * HD + head * D + c] : 0.f;
+        sK[r][c] = key < ns ? Kp[(size_t)key * HD + head * D + c] : 0.f;
+        sV[r][c] = key < ns ? Vp[(size_t)key * HD + head * D + c] : 0.f;
       }
       __syncthreads();
-      const int nk = min(F32_BN, n - k0);
+      const int nk = min(F32_BN, ns - k0);
       float s[F32_BN];
       float mx = -INFINITY;
       for (int j = 0; j < F32_BN; ++j) {
@@ -506,6 +517,7 @@ __global__ __launch_bounds__(F32_NT) void attn_f32_kernel(AttnF32Params p) {
         l += pj;
         for (int e = 0; e < D; ++e) acc[e] = fmaf(pj, sV[j][e], acc[e]);
       }
+    }
     }
     if (br == 0) {
       const float inv = 1.0f / l;
@@ -648,10 +660,6 @@ ispa_status_t launch_attention(const AttnArgs& a, hipStream_t s) {
   if (a.dtype == ISPA_BF16) {
     AttnKParams p;
     p.Q = (const uint16_t*)a.Q;
-    p.Kl = (const uint16_t*)a.Kl;
-    p.Vl = (const uint16_t*)a.Vl;
-    p.Kh = (const uint16_t*)a.Kh;
-    p.Vh = (const uint16_t*)a.Vh;
     p.O_loc = (uint16_t*)a.O_loc;
     p.LSE_loc = a.LSE_loc;
     p.O_hist = (uint16_t*)a.O_hist;
@@ -660,8 +668,6 @@ ispa_status_t launch_attention(const AttnArgs& a, hipStream_t s) {
     p.LSE_full = a.LSE_full;
     p.stash = (float*)a.ws;
     p.n_q = (int)a.n_q;
-    p.n_loc = (int)a.n_loc;
-    p.n_hist = (int)a.n_hist;
     p.heads = a.heads;
     p.c2 = a.scale * LOG2E;
     const size_t ws_need = attention_workspace_size(a.n_q, a.heads, a.head_dim, a.n_hist, a.dtype);
@@ -670,6 +676,16 @@ ispa_status_t launch_attention(const AttnArgs& a, hipStream_t s) {
       return ISPA_E_WORKSPACE;
     }
     const AttnShape sh = attn_shape();
+    p.n_seg = a.kv.n_seg;
+    p.n_loc_seg = a.kv.n_loc_seg;
+    p.st0[0] = 0;
+    for (int i = 0; i < MAX_KV_SEGS; ++i) {
+      const bool used = i < a.kv.n_seg;
+      p.Ks[i] = used ? (const uint16_t*)a.kv.K[i] : nullptr;
+      p.Vs[i] = used ? (const uint16_t*)a.kv.V[i] : nullptr;
+      p.sn[i] = used ? (int)a.kv.n[i] : 0;
+      p.st0[i + 1] = p.st0[i] + (int)((p.sn[i] + sh.bn - 1) / sh.bn);
+    }
     const int bm = sh.nw * 32;
     p.n_qtiles = (int)((a.n_q + bm - 1) / bm);
     p.nblocks = p.n_qtiles * a.heads;
@@ -682,10 +698,14 @@ ispa_status_t launch_attention(const AttnArgs& a, hipStream_t s) {
   }
   AttnF32Params p;
   p.Q = (const float*)a.Q;
-  p.Kl = (const float*)a.Kl;
-  p.Vl = (const float*)a.Vl;
-  p.Kh = (const float*)a.Kh;
-  p.Vh = (const float*)a.Vh;
+  p.n_seg = a.kv.n_seg;
+  p.n_loc_seg = a.kv.n_loc_seg;
+  for (int i = 0; i < MAX_KV_SEGS; ++i) {
+    const bool used = i < a.kv.n_seg;
+    p.Ks[i] = used ? (const float*)a.kv.K[i] : nullptr;
+    p.Vs[i] = used ? (const float*)a.kv.V[i] : nullptr;
+    p.sn[i] = used ? (int)a.kv.n[i] : 0;
+  }
   p.O_loc = (float*)a.O_loc;
   p.LSE_loc = a.LSE_loc;
   p.O_hist = (float*)a.O_hist;
@@ -693,7 +713,6 @@ ispa_status_t launch_attention(const AttnArgs& a, hipStream_t s) {
   p.O_full = (float*)a.O_full;
   p.LSE_full = a.LSE_full;
   p.n_q = (int)a.n_q;
-  p.n_loc = (int)a.n_loc;
   p.n_hist = (int)a.n_hist;
   p.heads = a.heads;
   p.c2 = a.scale * LOG2E;

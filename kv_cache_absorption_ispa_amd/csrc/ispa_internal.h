@@ -24,12 +24,19 @@ void set_error(const std::string& msg);
 ispa_status_t hip_check(hipError_t e, const char* what);
 
 // ---------------------------------------------------------------- launchers
+// Keys of one attention call as segments: segments [0, n_loc_seg) form the local branch, the rest
+// the history branch; each segment is a [n, H, D] K buffer and V buffer.
+constexpr int MAX_KV_SEGS = ISPA_MAX_KV_SEGMENTS;
+struct KvSegments {
+  const void* K[MAX_KV_SEGS];
+  const void* V[MAX_KV_SEGS];
+  int64_t n[MAX_KV_SEGS];
+  int32_t n_seg, n_loc_seg;
+};
+
 struct AttnArgs {
   const void* Q;
-  const void* Kl;
-  const void* Vl;
-  const void* Kh;
-  const void* Vh;
+  KvSegments kv;
   void* O_loc;
   float* LSE_loc;
   void* O_hist;

@@ -218,6 +218,35 @@ def custom_inputs(seed: int, n_q: int, n_loc: int, n_hist: int, heads: int, head
                        _encode(kh, dtype), _encode(vh, dtype))
 
 
+@dataclass
+class StreamChunk:
+    q: Tensor  # [n_q, H, D]
+    k: Tensor  # [n_chunk, H, D]: this chunk's own keys (history of the later chunks)
+    v: Tensor
+
+
+def stream_sink(seed: int, n_sink: int, heads: int, head_dim: int, dtype: str):
+    """Sink K and V of a streaming sequence (first 8 keys boosted x4 in bf16, as in the configs)."""
+    shp = (n_sink, heads, head_dim)
+    ks = normal(300 + seed, 0, LAYER_CHUNK, T_KS, shp)
+    vs = normal(300 + seed, 0, LAYER_CHUNK, T_VS, shp)
+    if dtype == "bf16":
+        ks[:8] *= np.float32(4.0)
+    return _encode(ks, dtype), _encode(vs, dtype)
+
+
+def stream_chunk(seed: int, chunk: int, n_q: int, n_chunk: int, heads: int, head_dim: int,
+                 dtype: str) -> StreamChunk:
+    """Queries and own K/V of chunk ``chunk`` of a streaming sequence.  The history
+    a chunk attends to is the K/V of the chunks before it, so these draws are
+    all a streaming test needs."""
+    H, D = heads, head_dim
+    q = normal(300 + seed, 0, chunk, T_Q, (n_q, H, D))
+    k = normal(300 + seed, 0, chunk, T_KC, (n_chunk, H, D))
+    v = normal(300 + seed, 0, chunk, T_VC, (n_chunk, H, D))
+    return StreamChunk(_encode(q, dtype), _encode(k, dtype), _encode(v, dtype))
+
+
 def weight(cfg: LayerConfig, layer: int = 0, d_out: int | None = None, cfg_id: int | None = None) -> np.ndarray:
     """Output-projection weight W [d, d_out], N(0, 1/d), float32 (row-vector convention y = a W)."""
     cid = cfg.cfg_id if cfg_id is None else cfg_id

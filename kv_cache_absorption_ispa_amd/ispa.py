@@ -21,7 +21,7 @@ ISPA_OK, ISPA_E_INVALID_ARG, ISPA_E_UNSUPPORTED, ISPA_E_WORKSPACE, ISPA_E_HIP = 
 ISPA_F32, ISPA_BF16 = 0, 1
 
 EXPORTS = [
-    "ispa_decomp_attn", "ispa_decomp_attn_workspace_size", "ispa_full_attn", "ispa_lse_merge", "ispa_gram_workspace_size", "ispa_gram_accum",
+    "ispa_decomp_attn", "ispa_decomp_attn_segments", "ispa_decomp_attn_workspace_size", "ispa_full_attn", "ispa_lse_merge", "ispa_gram_workspace_size", "ispa_gram_accum",
     "ispa_absorb_workspace_size", "ispa_absorb_solve", "ispa_eps_workspace_size", "ispa_layer_eps",
     "ispa_select_layers", "ispa_absorb_apply", "ispa_status_string", "ispa_last_error", "ispa_version", "ispa_device_check",
 ]
@@ -45,6 +45,12 @@ class AttnDesc(ctypes.Structure):
     ]
 
 
+class KvSegment(ctypes.Structure):
+    _fields_ = [("K", ctypes.c_void_p), ("V", ctypes.c_void_p), ("n_rows", ctypes.c_int64)]
+
+
+ISPA_MAX_KV_SEGMENTS = 16
+
 _lib = None
 
 
@@ -59,6 +65,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     P, I32, I64, SZ, F, D = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float, None
     sig = {
         "ispa_decomp_attn": (I32, [ctypes.POINTER(AttnDesc)] + [P] * 12 + [SZ, P]),
+        "ispa_decomp_attn_segments": (I32, [ctypes.POINTER(AttnDesc), P, ctypes.POINTER(KvSegment), I32, I32]
+                                      + [P] * 7 + [SZ, P]),
         "ispa_decomp_attn_workspace_size": (SZ, [ctypes.POINTER(AttnDesc)]),
         "ispa_full_attn": (I32, [ctypes.POINTER(AttnDesc), P, P, P, P, P, P]),
         "ispa_lse_merge": (I32, [I32, P, P, I64, I32, I32, I32, P, P, P]),
@@ -159,6 +167,38 @@ def ispa_decomp_attn(q, k_loc, v_loc, k_hist=None, v_hist=None, *, scale=None, o
                                 _ptr(k_hist) if n_hist else None, _ptr(v_hist) if n_hist else None,
                                 _ptr(o_loc), _ptr(lse_loc), _ptr(o_hist), _ptr(lse_hist), _ptr(o_full),
                                 _ptr(lse_full), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def ispa_decomp_attn_segments(q, loc_segs: Sequence, hist_segs: Sequence = (), *, scale=None, o_loc=None,
+                              lse_loc=None, o_hist=None, lse_hist=None, o_full=None, lse_full=None, workspace=None,
+                              stream=None) -> None:
+    """ispa_decomp_attn over K/V segments: ``loc_segs`` / ``hist_segs`` are sequences of (k, v) pairs,
+    each [n_i, H, D] contiguous, attended in place (no concatenation)."""
+    n_q, H, D = q.shape
+    segs = list(loc_segs) + list(hist_segs)
+    arr = (KvSegment * max(len(segs), 1))()
+    n_loc = n_hist = 0
+    for i, (k, v) in enumerate(segs):
+        n = int(k.shape[0])
+        _expect(k, (n, H, D), q.dtype, f"segment {i} k")
+        _expect(v, (n, H, D), q.dtype, f"segment {i} v")
+        arr[i] = KvSegment(_ptr(k), _ptr(v), n)
+        if i < len(loc_segs):
+            n_loc += n
+        else:
+            n_hist += n
+    for t, n in ((o_loc, "o_loc"), (o_hist, "o_hist"), (o_full, "o_full")):
+        _expect(t, (n_q, H, D), q.dtype, n)
+    for t, n in ((lse_loc, "lse_loc"), (lse_hist, "lse_hist"), (lse_full, "lse_full")):
+        _expect(t, (H, n_q), torch.float32, n)
+    desc = make_desc(q, n_loc, n_hist, scale)
+    lib = load_library()
+    if workspace is None and o_full is not None:
+        workspace = _workspace(int(lib.ispa_decomp_attn_workspace_size(ctypes.byref(desc))), q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.ispa_decomp_attn_segments(ctypes.byref(desc), _ptr(q), arr, len(segs), len(loc_segs),
+                                         _ptr(o_loc), _ptr(lse_loc), _ptr(o_hist), _ptr(lse_hist), _ptr(o_full),
+                                         _ptr(lse_full), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def ispa_full_attn(q, k, v, *, scale=None, o=None, lse=None, stream=None) -> None:

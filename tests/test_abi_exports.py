@@ -88,3 +88,36 @@ def test_workspace_queries():
     assert lib.ispa_gram_workspace_size(4680, 5120, ispa.ISPA_BF16) == 0  # enough tiles: no split
     assert lib.ispa_gram_workspace_size(4680, 1536, ispa.ISPA_BF16) > 0  # few tiles: split rows
     assert lib.ispa_gram_workspace_size(256, 128, ispa.ISPA_F32) == 0
+
+
+@pytest.mark.skipif(not os.path.exists(ispa.LIB_PATH), reason="libispa.so not built")
+def test_segment_validation_needs_no_gpu():
+    """ispa_decomp_attn_segments rejects bad segment lists before any HIP call."""
+    lib = ispa.load_library()
+    ok = 0x10000
+
+    def call(desc, segs, n_loc_segs, n_segs=None, o_full=None, ws=None, ws_bytes=0):
+        arr = (ispa.KvSegment * max(len(segs), 1))(*[ispa.KvSegment(k, v, n) for k, v, n in segs])
+        n_segs = len(segs) if n_segs is None else n_segs
+        return lib.ispa_decomp_attn_segments(ctypes.byref(desc), ok, arr, n_segs, n_loc_segs, None, None, None,
+                                             None, o_full, None, ws, ws_bytes, None)
+
+    d = ispa.AttnDesc(2, 128, 100, 50, 70, 0.1, 1)
+    good = [(ok, ok, 20), (ok, ok, 30), (ok, ok, 70)]
+    bad = ispa.ISPA_E_INVALID_ARG
+    assert call(d, good, 0) == bad                      # no local segment
+    assert call(d, good, 4) == bad                      # more local segments than segments
+    assert call(d, good, 1) == bad                      # local rows 20 != n_loc 50
+    assert call(d, good, 3) == bad                      # history rows 0 != n_hist 70
+    assert call(d, good, 2, n_segs=0) == bad
+    assert call(d, good * 6, 2, n_segs=17) == bad       # above ISPA_MAX_KV_SEGMENTS
+    assert call(d, [(ok, ok, 50), (ok, ok, 0), (ok, ok, 70)], 1) == bad  # empty segment
+    assert call(d, [(ok, ok, 50), (ok + 8, ok, 70)], 1) == bad           # misaligned K
+    assert call(d, [(ok, ok, 50), (ok, None, 70)], 1) == bad             # null V
+    assert b"n_loc" in (call(d, good, 1) and lib.ispa_last_error())
+    # the merge's float32 workspace is still required with history keys
+    assert call(d, good, 2, o_full=ok) == ispa.ISPA_E_WORKSPACE
+    assert call(d, good, 2, o_full=ok, ws=ok, ws_bytes=100 * 2 * 128 * 4 - 1) == ispa.ISPA_E_WORKSPACE
+    assert ispa.ISPA_MAX_KV_SEGMENTS == 16
+    hdr = open(os.path.join(ROOT, "include", "ispa.h")).read()
+    assert "#define ISPA_MAX_KV_SEGMENTS 16" in hdr
