@@ -132,13 +132,29 @@ __global__ __launch_bounds__(NW * 64, (QB == 1 && NW <= 4) ? 2 : 1) void attn_bf
   const int Tl = p.st0[p.n_loc_seg];  // local tiles, then history tiles
   const int T = p.st0[p.n_seg];
   const int Th = T - Tl;
-  // segment of tile t (wave-uniform; a handful of scalar compares)
-  auto seg_of = [&](int t) {
-    int s = 0;
-#pragma unroll
-    for (int i = 1; i < MAX_KV_SEGS; ++i) s += (i < p.n_seg && t >= p.st0[i]) ? 1 : 0;
-    return s;
+  // Tiles are visited in order, so the loads and the compute each keep a cursor
+  // (segment, tile within it) in scalar registers; the segment table is read
+  // only when a cursor crosses into the next segment (a scalar-memory read
+  // per tile would make every tile wait on it together with its LDS reads).
+  struct Cur {
+    int sg, tt, nt, n;
+    const uint16_t* kb;
+    const uint16_t* vb;
   };
+  auto cur_at = [&](int sg) {
+    Cur c;
+    c.sg = sg;
+    c.tt = 0;
+    c.n = p.sn[sg];
+    c.nt = (c.n + BN - 1) / BN;
+    c.kb = p.Ks[sg];
+    c.vb = p.Vs[sg];
+    return c;
+  };
+  auto cur_next = [&](Cur& c) {
+    if (++c.tt == c.nt && c.sg + 1 < p.n_seg) c = cur_at(c.sg + 1);
+  };
+  Cur lcur = cur_at(0), ccur = lcur;
 
   int myq[QB];
   bool qvalid[QB];
@@ -171,11 +187,11 @@ __global__ __launch_bounds__(NW * 64, (QB == 1 && NW <= 4) ? 2 : 1) void attn_bf
     gofs[j] = (uint32_t)row * row_bytes + (uint32_t)(head * D + chunk * 8) * 2u;
   }
 
-  auto load_tile = [&](int t, uint16_t* sKb, uint16_t* sVb) {
-    const int sg = seg_of(t);
-    const uint32_t tb = (uint32_t)((t - p.st0[sg]) * BN) * row_bytes;
-    const rsrc_t rk = make_rsrc(p.Ks[sg], (uint32_t)p.sn[sg] * row_bytes);
-    const rsrc_t rv = make_rsrc(p.Vs[sg], (uint32_t)p.sn[sg] * row_bytes);
+  auto load_tile = [&](uint16_t* sKb, uint16_t* sVb) {
+    const uint32_t tb = (uint32_t)(lcur.tt * BN) * row_bytes;
+    const rsrc_t rk = make_rsrc(lcur.kb, (uint32_t)lcur.n * row_bytes);
+    const rsrc_t rv = make_rsrc(lcur.vb, (uint32_t)lcur.n * row_bytes);
+    cur_next(lcur);
 #pragma unroll
     for (int j = 0; j < WLW; ++j) {
       const int g = wave + j * NW;
@@ -225,10 +241,10 @@ __global__ __launch_bounds__(NW * 64, (QB == 1 && NW <= 4) ? 2 : 1) void attn_bf
     return __builtin_bit_cast(bf16x8, u32x4{a.x, a.y, b.x, b.y});
   };
 
-  auto compute_tile = [&](const uint16_t* sKb, const uint16_t* sVb, int t) {
-    const int sg = seg_of(t);
-    const int key0 = (t - p.st0[sg]) * BN;
-    const int nvalid = p.sn[sg];
+  auto compute_tile = [&](const uint16_t* sKb, const uint16_t* sVb) {
+    const int key0 = ccur.tt * BN;
+    const int nvalid = ccur.n;
+    cur_next(ccur);
     f32x16 s[QB][NKB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
@@ -373,19 +389,19 @@ __global__ __launch_bounds__(NW * 64, (QB == 1 && NW <= 4) ? 2 : 1) void attn_bf
     }
   };
 
-  load_tile(0, sK0, sV0);
+  load_tile(sK0, sV0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int t = 0; t < T; t += 2) {
     // even tile in buffer 0, odd tile in buffer 1; the next tile's loads are in flight meanwhile
-    if (t + 1 < T) load_tile(t + 1, sK1, sV1);
-    compute_tile(sK0, sV0, t);
+    if (t + 1 < T) load_tile(sK1, sV1);
+    compute_tile(sK0, sV0);
     if (t == Tl - 1) end_of_local();
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile t+1 have landed in LDS
     __syncthreads();
     if (t + 1 >= T) break;
-    if (t + 2 < T) load_tile(t + 2, sK0, sV0);
-    compute_tile(sK1, sV1, t + 1);
+    if (t + 2 < T) load_tile(sK0, sV0);
+    compute_tile(sK1, sV1);
     if (t + 1 == Tl - 1) end_of_local();
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
