@@ -19,6 +19,9 @@ benchmark names, the distributions are stated here):
   Q, the chunk K/V and the history K/V are fresh per chunk.  The local key set
   handed to the attention call is the sink rows followed by the chunk rows.
 * W ~ N(0, 1/d), float32, kept float32.
+* Streaming sequences (:func:`stream_sink`, :func:`stream_chunk`) use
+  cfg id 300 + seed: a sink drawn once, then per chunk Q and the chunk's own
+  K/V; a chunk's history is the K/V of the chunks before it.
 * bf16 values are made from the float32 draws by round-to-nearest-even on the
   host (:func:`f32_to_bf16_bits`); the GPU receives the 16-bit patterns and the
   oracle receives the exact same values widened to float64.
