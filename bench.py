@@ -182,6 +182,26 @@ def main():
         ch["q"], ch["kl"], ch["vl"], ch["kh"], ch["vh"], o_loc=o_loc, lse_loc=lse[0], o_hist=o_hist,
         lse_hist=lse[1], o_full=o_full, lse_full=lse[2], workspace=atws))
     del loc_segs, hist_segs
+
+    # ---- split-KV form (ispa_decomp_attn_splitkv, one workgroup per CU): at the full chunk every XCD
+    # already has more units than spare workgroups (P = 1, the unsplit launch); a short query chunk of
+    # 512 queries (24 units for 256 CUs) is where the key split pays
+    skws = ispa.workspace(ispa.ispa_decomp_attn_splitkv_workspace_size(ch["q"], cfg.n_loc, cfg.n_hist, 0))
+    sk_ms = back_to_back_ms(lambda: ispa.ispa_decomp_attn_splitkv(
+        ch["q"], [(ch["kl"], ch["vl"])], [(ch["kh"], ch["vh"])], o_loc=o_loc, lse_loc=lse[0], o_hist=o_hist,
+        lse_hist=lse[1], o_full=o_full, lse_full=lse[2], workspace=skws))
+    nq_s = 512
+    q_s = ch["q"][:nq_s].contiguous()
+    o_s = [torch.empty(nq_s, H, D, dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+    l_s = [torch.empty(H, nq_s, device="cuda") for _ in range(3)]
+    short_unsplit = back_to_back_ms(lambda: ispa.ispa_decomp_attn(
+        q_s, ch["kl"], ch["vl"], ch["kh"], ch["vh"], o_loc=o_s[0], lse_loc=l_s[0], o_hist=o_s[1], lse_hist=l_s[1],
+        o_full=o_s[2], lse_full=l_s[2], workspace=skws))
+    short_split = back_to_back_ms(lambda: ispa.ispa_decomp_attn_splitkv(
+        q_s, [(ch["kl"], ch["vl"])], [(ch["kh"], ch["vh"])], o_loc=o_s[0], lse_loc=l_s[0], o_hist=o_s[1],
+        lse_hist=l_s[1], o_full=o_s[2], lse_full=l_s[2], workspace=skws))
+    short_flops = cfg.attn_flops() * nq_s / nq
+    del skws, q_s, o_s, l_s
     gemm_ref = reference_gemm_tflops()
 
     attn_flops = cfg.attn_flops()
@@ -227,6 +247,16 @@ def main():
         "single_pass_ms": round(float(np.median(full_ms)), 4),
         "ratio_decomp_vs_single_pass": round(attn_avg / float(np.median(full_ms)), 4),
         "reference_bf16_gemm_tflops": gemm_ref,
+        "splitkv": {
+            "workers": "one per compute unit",
+            "ms": round(float(np.median(sk_ms)), 4),
+            "ratio_vs_two_buffer": round(float(np.median(sk_ms)) / float(np.median(two_ms)), 4),
+            "short_chunk_queries": nq_s,
+            "short_chunk_unsplit_ms": round(float(np.median(short_unsplit)), 4),
+            "short_chunk_split_ms": round(float(np.median(short_split)), 4),
+            "short_chunk_speedup": round(float(np.median(short_unsplit)) / float(np.median(short_split)), 3),
+            "short_chunk_split_tflops": round(short_flops / (float(np.median(short_split)) * 1e-3) / 1e12, 2),
+        },
         "segments": {
             "layout": f"local [{ns} sink | {nc} chunk], history [{cut} | {cfg.n_hist - cut}] (wrapped ring)",
             "ms": round(float(np.median(seg_ms)), 4),

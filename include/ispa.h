@@ -11,6 +11,8 @@
  *                      log-sum-exp merge (A_loc and A_full rows),
  *   ispa_decomp_attn_segments  the same over a list of K/V segments
  *                      (sink, chunk, history pages) attended in place,
+ *   ispa_decomp_attn_splitkv   the same with the keys split across
+ *                      workgroups (even load) and merged through LSE,
  *   ispa_gram_accum    G = A_loc^T A_loc and C = A_loc^T (A_full - A_loc),
  *   ispa_absorb_solve  dW = (G + lambda I)^-1 C W  (Cholesky + triangular solves),
  *   ispa_layer_eps     the post-fit reconstruction error used to rank layers,
@@ -144,6 +146,48 @@ ispa_status_t ispa_decomp_attn_segments(const ispa_attn_desc_t* desc, const void
                                         void* O_loc, float* LSE_loc, void* O_hist, float* LSE_hist,
                                         void* O_full, float* LSE_full, void* workspace,
                                         size_t workspace_bytes, void* stream);
+
+/* At most this many workgroups per ispa_decomp_attn_splitkv call. */
+#define ISPA_MAX_SPLITKV_WORKERS 65535
+
+/*
+ * ispa_decomp_attn_splitkv — ispa_decomp_attn_segments with the keys of every
+ * (head, query tile) split into P equal pieces on P workgroups (split-KV),
+ * for shapes whose (head, query tile) units would leave most of the GPU idle
+ * (few heads, short query chunks, long histories); two launches: attention,
+ * then a merge of the pieces.
+ *
+ * Source: ISPA technical summary, section 2 "Methodology", step 1 (branches
+ * are independent online-softmax passes whose log-sum-exp states combine
+ * exactly afterwards) and section 3 (online softmax).  The same identity
+ * that fuses the local and history branches fuses any partition of a branch's
+ * keys: a piece of a branch leaves (O_p, LSE_p), and O = sum_p
+ * e^(LSE_p - LSE) O_p with LSE = log sum_p e^(LSE_p).
+ *
+ * `n_workers` workgroups (0 = one per compute unit of the current device,
+ * <= ISPA_MAX_SPLITKV_WORKERS).  The units (256 queries of one head) are dealt
+ * to the 8 XCDs in contiguous blocks; P is the number of workgroups every XCD
+ * can give each of its units (at most the number of 128-key tiles).  With
+ * P = 1 the call is ispa_decomp_attn_segments exactly (bitwise).  Otherwise
+ * every piece leaves float32 partial states in the workspace and the second
+ * launch merges them (float32, outputs rounded once); results equal the
+ * unsplit call's up to rounding (tested against the float64 reference).
+ * BF16 only (ISPA_E_INVALID_ARG for F32).  Arguments, outputs and errors are
+ * those of ispa_decomp_attn_segments; `workspace` (device, >=
+ * ispa_decomp_attn_splitkv_workspace_size(desc, n_workers) bytes) is always
+ * required (ISPA_E_WORKSPACE otherwise).
+ */
+ispa_status_t ispa_decomp_attn_splitkv(const ispa_attn_desc_t* desc, const void* Q,
+                                       const ispa_kv_segment_t* segs, int32_t n_segs, int32_t n_loc_segs,
+                                       int32_t n_workers, void* O_loc, float* LSE_loc, void* O_hist,
+                                       float* LSE_hist, void* O_full, float* LSE_full, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of ispa_decomp_attn_splitkv: the merge's float32 O_loc
+ * (with history keys, rounded up to 256 bytes) plus one partial slot of
+ * 2*BM*(D+1) float32 per workgroup (BM = 256 queries; 264 KB at D = 128).
+ * n_workers = 0 sizes for the current device (0 if there is none). */
+size_t ispa_decomp_attn_splitkv_workspace_size(const ispa_attn_desc_t* desc, int32_t n_workers);
 
 /* Workspace bytes ispa_decomp_attn needs for this shape: n_q*H*D*4 for bf16
  * with history keys (the float32 O_loc the merge reads), else 0.  Needed only

@@ -114,12 +114,43 @@ ispa_status_t check_decomp_outputs(const ispa_attn_desc_t* desc, void* O_loc, fl
   return ISPA_OK;
 }
 
+// Compute units of the current device (0 if there is none).
+int32_t current_cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return n;
+}
+
+// Validate a segment list against desc; fill kv.
+ispa_status_t check_segments(const ispa_attn_desc_t* desc, const ispa_kv_segment_t* segs, int32_t n_segs,
+                             int32_t n_loc_segs, KvSegments& kv) {
+  if (segs == nullptr) return invalid("segs is NULL");
+  if (n_segs < 1 || n_segs > ISPA_MAX_KV_SEGMENTS) return invalid("n_segs must be in [1, ISPA_MAX_KV_SEGMENTS]");
+  if (n_loc_segs < 1 || n_loc_segs > n_segs) return invalid("n_loc_segs must be in [1, n_segs]");
+  int64_t sum_loc = 0, sum_hist = 0;
+  kv = KvSegments{};
+  for (int i = 0; i < n_segs; ++i) {
+    if (segs[i].n_rows < 1) return invalid("every segment needs n_rows >= 1");
+    if (!req(segs[i].K) || !req(segs[i].V)) return invalid("segment K, V must be non-NULL and 16-byte aligned");
+    (i < n_loc_segs ? sum_loc : sum_hist) += segs[i].n_rows;
+    kv.K[i] = segs[i].K;
+    kv.V[i] = segs[i].V;
+    kv.n[i] = segs[i].n_rows;
+  }
+  if (sum_loc != desc->n_loc || sum_hist != desc->n_hist)
+    return invalid("segment rows must add up to desc->n_loc (local) and desc->n_hist (history)");
+  kv.n_seg = n_segs;
+  kv.n_loc_seg = n_loc_segs;
+  return ISPA_OK;
+}
+
 ispa_status_t run_decomp(const ispa_attn_desc_t* desc, const void* Q, const KvSegments& kv, void* O_loc,
                          float* LSE_loc, void* O_hist, float* LSE_hist, void* O_full, float* LSE_full,
-                         void* workspace, size_t workspace_bytes, void* stream) {
+                         void* workspace, size_t workspace_bytes, void* stream, int32_t sk_workers = 0) {
   const ispa_status_t st = check_current_device();
   if (st != ISPA_OK) return st;
-  AttnArgs a;
+  AttnArgs a = {};
   a.Q = Q;
   a.kv = kv;
   a.O_loc = O_loc;
@@ -137,6 +168,7 @@ ispa_status_t run_decomp(const ispa_attn_desc_t* desc, const void* Q, const KvSe
   a.dtype = desc->dtype;
   a.ws = workspace;
   a.ws_bytes = workspace_bytes;
+  a.sk_workers = sk_workers;
   return launch_attention(a, (hipStream_t)stream);
 }
 
@@ -174,28 +206,51 @@ ispa_status_t ispa_decomp_attn_segments(const ispa_attn_desc_t* desc, const void
                                         void* workspace, size_t workspace_bytes, void* stream) {
   ispa_status_t st = check_attn_desc(desc, true);
   if (st != ISPA_OK) return st;
-  if (segs == nullptr) return invalid("segs is NULL");
-  if (n_segs < 1 || n_segs > ISPA_MAX_KV_SEGMENTS) return invalid("n_segs must be in [1, ISPA_MAX_KV_SEGMENTS]");
-  if (n_loc_segs < 1 || n_loc_segs > n_segs) return invalid("n_loc_segs must be in [1, n_segs]");
+  KvSegments kv;
+  st = check_segments(desc, segs, n_segs, n_loc_segs, kv);
+  if (st != ISPA_OK) return st;
   if (desc->n_q > 0 && !req(Q)) return invalid("Q must be non-NULL and 16-byte aligned");
-  int64_t sum_loc = 0, sum_hist = 0;
-  KvSegments kv = {};
-  for (int i = 0; i < n_segs; ++i) {
-    if (segs[i].n_rows < 1) return invalid("every segment needs n_rows >= 1");
-    if (!req(segs[i].K) || !req(segs[i].V)) return invalid("segment K, V must be non-NULL and 16-byte aligned");
-    (i < n_loc_segs ? sum_loc : sum_hist) += segs[i].n_rows;
-    kv.K[i] = segs[i].K;
-    kv.V[i] = segs[i].V;
-    kv.n[i] = segs[i].n_rows;
-  }
-  if (sum_loc != desc->n_loc || sum_hist != desc->n_hist)
-    return invalid("segment rows must add up to desc->n_loc (local) and desc->n_hist (history)");
-  kv.n_seg = n_segs;
-  kv.n_loc_seg = n_loc_segs;
   st = check_decomp_outputs(desc, O_loc, LSE_loc, O_hist, LSE_hist, O_full, LSE_full, workspace, workspace_bytes);
   if (st != ISPA_OK) return st;
   return run_decomp(desc, Q, kv, O_loc, LSE_loc, O_hist, LSE_hist, O_full, LSE_full, workspace, workspace_bytes,
                     stream);
+}
+
+size_t ispa_decomp_attn_splitkv_workspace_size(const ispa_attn_desc_t* desc, int32_t n_workers) {
+  if (desc == nullptr || desc->n_q < 0 || desc->heads < 1 || desc->n_hist < 0 || n_workers < 0 ||
+      n_workers > ISPA_MAX_SPLITKV_WORKERS || (desc->head_dim != 64 && desc->head_dim != 128))
+    return 0;
+  const int32_t w = n_workers > 0 ? n_workers : current_cu_count();
+  return splitkv_workspace_size(desc->n_q, desc->heads, desc->head_dim, desc->n_hist, w);
+}
+
+ispa_status_t ispa_decomp_attn_splitkv(const ispa_attn_desc_t* desc, const void* Q, const ispa_kv_segment_t* segs,
+                                       int32_t n_segs, int32_t n_loc_segs, int32_t n_workers, void* O_loc,
+                                       float* LSE_loc, void* O_hist, float* LSE_hist, void* O_full,
+                                       float* LSE_full, void* workspace, size_t workspace_bytes, void* stream) {
+  ispa_status_t st = check_attn_desc(desc, true);
+  if (st != ISPA_OK) return st;
+  if (desc->dtype != ISPA_BF16) return invalid("split-KV attention is bf16 only");
+  if (n_workers < 0 || n_workers > ISPA_MAX_SPLITKV_WORKERS)
+    return invalid("n_workers must be in [0, ISPA_MAX_SPLITKV_WORKERS]");
+  KvSegments kv;
+  st = check_segments(desc, segs, n_segs, n_loc_segs, kv);
+  if (st != ISPA_OK) return st;
+  if (desc->n_q > 0 && !req(Q)) return invalid("Q must be non-NULL and 16-byte aligned");
+  if (!opt(O_loc) || !opt(LSE_loc) || !opt(O_hist) || !opt(LSE_hist) || !opt(O_full) || !opt(LSE_full) ||
+      !opt(workspace))
+    return invalid("output and workspace pointers must be 16-byte aligned");
+  st = check_current_device();
+  if (st != ISPA_OK) return st;
+  const int32_t w = n_workers > 0 ? n_workers : current_cu_count();
+  if (w < 1) return invalid("no compute units on the current device");
+  const size_t need = splitkv_workspace_size(desc->n_q, desc->heads, desc->head_dim, desc->n_hist, w);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) {
+    set_error("workspace smaller than ispa_decomp_attn_splitkv_workspace_size()");
+    return ISPA_E_WORKSPACE;
+  }
+  return run_decomp(desc, Q, kv, O_loc, LSE_loc, O_hist, LSE_hist, O_full, LSE_full, workspace, workspace_bytes,
+                    stream, w);
 }
 
 ispa_status_t ispa_full_attn(const ispa_attn_desc_t* desc, const void* Q, const void* K, const void* V, void* O,

@@ -59,7 +59,41 @@ struct AttnKParams {
   int n_q, heads;
   float c2;  // scale * log2(e)
   int n_qtiles, nblocks;
+  // split mode: unit u's key tiles are cut into sk_p equal pieces, piece i on its own workgroup,
+  // which leaves its branch states in partial slot u * sk_p + i
+  int sk_p;
+  float* part;
 };
+
+// Split-mode schedule.  Workgroup b runs on XCD b % 8 (round-robin dispatch).  The units are
+// dealt to the XCDs in contiguous blocks; on an XCD with n units, workgroup slot j takes piece
+// j / n of unit j % n, so the workgroups reading the same key range of a head sit on one XCD and
+// march through it together (shared L2), as the unsplit launch does.  Pure function of (b,
+// number of workgroups, units, pieces), shared with the host.
+__host__ __device__ inline void sk_xcd_counts(int x, int n_wg, int n_units, int& wx, int& nx, int& bx) {
+  wx = n_wg / 8 + (x < n_wg % 8 ? 1 : 0);
+  nx = n_units / 8 + (x < n_units % 8 ? 1 : 0);
+  bx = x * (n_units / 8) + (x < n_units % 8 ? x : n_units % 8);
+}
+// Pieces per unit: the most every XCD can give each of its units (1 = no split), at most T.
+__host__ __device__ inline int sk_pieces(int n_wg, int n_units, int T) {
+  int pc = T;
+  for (int x = 0; x < 8; ++x) {
+    int wx, nx, bx;
+    sk_xcd_counts(x, n_wg, n_units, wx, nx, bx);
+    if (nx > 0) pc = wx / nx < pc ? wx / nx : pc;
+  }
+  return pc < 1 ? 1 : pc;
+}
+// Key tiles [t0, t1) of piece i of P.
+__host__ __device__ inline void sk_piece_range(int i, int P, int T, int& t0, int& t1) {
+  t0 = (int)((int64_t)i * T / P);
+  t1 = (int)((int64_t)(i + 1) * T / P);
+}
+
+// Partial slot: float32 O for the local and the history branch ([2][BM][D]), then their
+// log2-domain LSEs ([2][BM]).
+__host__ __device__ constexpr size_t part_slot_floats(int bm, int d) { return (size_t)2 * bm * d + 2 * bm; }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -95,7 +129,11 @@ __device__ __forceinline__ int kv_swizzle(int r) {
 // transposing V reads are free of bank conflicts.  They are filled straight from global memory by buffer loads into LDS
 // (a wave moves 1 KB per load), so tile staging costs no VGPRs and no LDS
 // store instructions; rows past the branch's end read as 0 (range-checked).
-template <int D, int NW, int QB, int BN>
+//
+// SK = split mode: the grid is a fixed set of workgroups (one per CU) that
+// share the units' tiles evenly, so no CU idles when the units do not fill the
+// last round; pieces of split units are merged afterwards (sk_fixup_kernel).
+template <int D, int NW, int QB, int BN, bool SK>
 __global__ __launch_bounds__(NW * 64, (QB == 1 && NW <= 4) ? 2 : 1) void attn_bf16_kernel(AttnKParams p) {
   constexpr int KK = D / 16;  // MFMA k-steps of S^T
   constexpr int DB = D / 32;  // 32-row blocks of O^T
@@ -123,8 +161,6 @@ __global__ __launch_bounds__(NW * 64, (QB == 1 && NW <= 4) ? 2 : 1) void attn_bf
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: load targets stay scalar
   const int l32 = lane & 31, hh = lane >> 5;
-  const uint32_t unit = xcd_remap(blockIdx.x, p.nblocks);
-  const int head = unit / p.n_qtiles, qt = unit % p.n_qtiles;
   const int n_q = p.n_q;
   const uint32_t HD = (uint32_t)p.heads * D;
   const uint32_t row_bytes = HD * 2u;
@@ -132,6 +168,11 @@ __global__ __launch_bounds__(NW * 64, (QB == 1 && NW <= 4) ? 2 : 1) void attn_bf
   const int Tl = p.st0[p.n_loc_seg];  // local tiles, then history tiles
   const int T = p.st0[p.n_seg];
   const int Th = T - Tl;
+
+  // One piece: tiles [t0, t1) of unit `unit` (all of them outside split mode).
+  auto piece = [&](const int unit, const int t0, const int t1, float* slot) {
+  const bool whole = !SK || (t0 == 0 && t1 == T);
+  const int head = unit / p.n_qtiles, qt = unit % p.n_qtiles;
   // Tiles are visited in order, so the loads and the compute each keep a cursor
   // (segment, tile within it) in scalar registers; the segment table is read
   // only when a cursor crosses into the next segment (a scalar-memory read
@@ -154,7 +195,12 @@ __global__ __launch_bounds__(NW * 64, (QB == 1 && NW <= 4) ? 2 : 1) void attn_bf
   auto cur_next = [&](Cur& c) {
     if (++c.tt == c.nt && c.sg + 1 < p.n_seg) c = cur_at(c.sg + 1);
   };
-  Cur lcur = cur_at(0), ccur = lcur;
+  int sg0 = 0;
+  if (t0 > 0)
+    while (sg0 + 1 < p.n_seg && p.st0[sg0 + 1] <= t0) ++sg0;
+  Cur lcur = cur_at(sg0);
+  lcur.tt = t0 - p.st0[sg0];
+  Cur ccur = lcur;
 
   int myq[QB];
   bool qvalid[QB];
@@ -356,15 +402,35 @@ __global__ __launch_bounds__(NW * 64, (QB == 1 && NW <= 4) ? 2 : 1) void attn_bf
     if (L && hh == 0 && qvalid[qb]) L[(size_t)head * n_q + myq[qb]] = v2 * LN2;
   };
 
+  // a branch's part of a split unit: normalised float32 O and log2 LSE into the partial slot
+  auto write_part = [&](int br, int qb, float inv, float lse2) {
+    const int row = wave * 32 * QB + qb * 32 + l32;
+    float* op = slot + ((size_t)br * BM + row) * D + 4 * hh;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *(f32x4*)(op + 32 * db + 8 * g) = f32x4{acc[qb][db][4 * g] * inv, acc[qb][db][4 * g + 1] * inv,
+                                                 acc[qb][db][4 * g + 2] * inv, acc[qb][db][4 * g + 3] * inv};
+    if (hh == 0) slot[(size_t)2 * BM * D + br * BM + row] = lse2;
+  };
+
   float lse2_loc[QB];
   // local branch done: normalise, write O_loc / LSE_loc, keep float32 O_loc for the merge
   auto end_of_local = [&]() {
-    // local branch done: normalise, write O_loc / LSE_loc, keep float32 O_loc for the merge
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const float lt = l[qb] + other_half(l[qb]);
       const float inv = 1.0f / lt;
       lse2_loc[qb] = m[qb] + __log2f(lt);
+      if (!whole) {
+        write_part(0, qb, inv, lse2_loc[qb]);
+        m[qb] = -INFINITY;
+        l[qb] = 0.f;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[qb][db] = f32x16{0};
+        continue;
+      }
       u32x2 oloc[DB][4];
       pack_acc(oloc, qb, inv);
       write_o(p.O_loc, qb, oloc);
@@ -392,19 +458,32 @@ __global__ __launch_bounds__(NW * 64, (QB == 1 && NW <= 4) ? 2 : 1) void attn_bf
   load_tile(sK0, sV0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int t = 0; t < T; t += 2) {
+  for (int t = t0; t < t1; t += 2) {
     // even tile in buffer 0, odd tile in buffer 1; the next tile's loads are in flight meanwhile
-    if (t + 1 < T) load_tile(sK1, sV1);
+    if (t + 1 < t1) load_tile(sK1, sV1);
     compute_tile(sK0, sV0);
     if (t == Tl - 1) end_of_local();
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile t+1 have landed in LDS
     __syncthreads();
-    if (t + 1 >= T) break;
-    if (t + 2 < T) load_tile(sK0, sV0);
+    if (t + 1 >= t1) break;
+    if (t + 2 < t1) load_tile(sK0, sV0);
     compute_tile(sK1, sV1);
     if (t + 1 == Tl - 1) end_of_local();
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+  }
+
+  if (!whole) {
+    // the branch this piece of a split unit ends in: the history, or the local branch when the
+    // piece stops before the local tiles end (t1 == Tl: end_of_local already wrote it)
+    if (t1 != Tl) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float lt = l[qb] + other_half(l[qb]);
+        write_part(t1 > Tl ? 1 : 0, qb, 1.0f / lt, m[qb] + __log2f(lt));
+      }
+    }
+    return;
   }
 
 #pragma unroll
@@ -454,6 +533,106 @@ __global__ __launch_bounds__(NW * 64, (QB == 1 && NW <= 4) ? 2 : 1) void attn_bf
       if (p.LSE_hist && hh == 0 && qvalid[qb]) p.LSE_hist[(size_t)head * n_q + myq[qb]] = -INFINITY;
     }
   }
+  };  // piece
+
+  if constexpr (SK) {
+    int wx, nx, bx;
+    sk_xcd_counts(blockIdx.x % 8, gridDim.x, p.nblocks, wx, nx, bx);
+    const int j = blockIdx.x / 8;
+    if (nx > 0 && j < nx * p.sk_p) {
+      const int unit = bx + j % nx, i = j / nx;
+      int t0, t1;
+      sk_piece_range(i, p.sk_p, T, t0, t1);
+      piece(unit, t0, t1, p.part + (size_t)(unit * p.sk_p + i) * part_slot_floats(BM, D));
+    }
+  } else {
+    piece((int)xcd_remap(blockIdx.x, p.nblocks), 0, T, nullptr);
+  }
+}
+
+// Merge of the pieces of split units (split mode): per (query, head) the
+// pieces' local states merge into O_loc / LSE_loc, their history states into
+// O_hist / LSE_hist, and the two into O_full / LSE_full (log-sum-exp weights;
+// float32 inputs, outputs rounded once).  Thread: one query row, 4 dims.
+struct FixupParams {
+  const float* part;
+  uint16_t* O_loc;
+  float* LSE_loc;
+  uint16_t* O_hist;
+  float* LSE_hist;
+  uint16_t* O_full;
+  float* LSE_full;
+  int n_q, heads, n_qtiles, bm, T, Tl, sk_p;
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void sk_fixup_kernel(FixupParams p) {
+  constexpr int TPR = D / 4;      // threads per query row (4 dims each)
+  constexpr int RPB = 256 / TPR;  // rows per workgroup
+  const int unit = blockIdx.x;
+  const int r = blockIdx.y * RPB + threadIdx.x / TPR;
+  const int head = unit / p.n_qtiles, qt = unit % p.n_qtiles;
+  const int q = qt * p.bm + r;
+  if (r >= p.bm || q >= p.n_q) return;
+  const int T = p.T, Tl = p.Tl, P = p.sk_p;
+  const size_t slot_f = part_slot_floats(p.bm, D);
+  const float* base = p.part + (size_t)unit * P * slot_f;
+  const int c4 = (threadIdx.x % TPR) * 4;
+  float ml = -INFINITY, mh = -INFINITY;
+  for (int i = 0; i < P; ++i) {
+    int t0, t1;
+    sk_piece_range(i, P, T, t0, t1);
+    const float* sl = base + i * slot_f + (size_t)2 * p.bm * D;
+    if (t0 < Tl) ml = fmaxf(ml, sl[r]);
+    if (t1 > Tl) mh = fmaxf(mh, sl[p.bm + r]);
+  }
+  float sl_sum = 0.f, sh_sum = 0.f;
+  f32x4 ol = {0.f, 0.f, 0.f, 0.f}, oh = {0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < P; ++i) {
+    int t0, t1;
+    sk_piece_range(i, P, T, t0, t1);
+    const float* sb = base + i * slot_f;
+    const float* sl = sb + (size_t)2 * p.bm * D;
+    if (t0 < Tl) {
+      const float e = exp2f(sl[r] - ml);
+      sl_sum += e;
+      ol += e * *(const f32x4*)(sb + (size_t)r * D + c4);
+    }
+    if (t1 > Tl) {
+      const float e = exp2f(sl[p.bm + r] - mh);
+      sh_sum += e;
+      oh += e * *(const f32x4*)(sb + ((size_t)p.bm + r) * D + c4);
+    }
+  }
+  const float lse_l = ml + log2f(sl_sum);
+  ol *= 1.0f / sl_sum;
+  const size_t o = (size_t)q * p.heads * D + head * D + c4;
+  auto store_bf16 = [&](uint16_t* O, f32x4 v) {
+    if (O == nullptr) return;
+    const bf16x2 a = {(__bf16)v[0], (__bf16)v[1]};
+    const bf16x2 b = {(__bf16)v[2], (__bf16)v[3]};
+    *(u32x2*)(O + o) = u32x2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
+  };
+  const bool lead = threadIdx.x % TPR == 0;
+  const size_t li = (size_t)head * p.n_q + q;
+  store_bf16(p.O_loc, ol);
+  if (lead && p.LSE_loc) p.LSE_loc[li] = lse_l * LN2;
+  if (T == Tl) {
+    store_bf16(p.O_hist, f32x4{0.f, 0.f, 0.f, 0.f});
+    if (lead && p.LSE_hist) p.LSE_hist[li] = -INFINITY;
+    store_bf16(p.O_full, ol);
+    if (lead && p.LSE_full) p.LSE_full[li] = lse_l * LN2;
+    return;
+  }
+  const float lse_h = mh + log2f(sh_sum);
+  oh *= 1.0f / sh_sum;
+  store_bf16(p.O_hist, oh);
+  if (lead && p.LSE_hist) p.LSE_hist[li] = lse_h * LN2;
+  const float mx = fmaxf(lse_l, lse_h);
+  const float lse = mx + log2f(exp2f(lse_l - mx) + exp2f(lse_h - mx));
+  const float wl = exp2f(lse_l - lse), wh = exp2f(lse_h - lse);
+  store_bf16(p.O_full, wl * ol + wh * oh);
+  if (lead && p.LSE_full) p.LSE_full[li] = lse * LN2;
 }
 
 // ----------------------------------------------------------------------------
@@ -661,14 +840,18 @@ AttnShape attn_shape() {
   return v;
 }
 
-template <int D>
+template <int D, bool SK>
 void launch_bf16(const AttnShape sh, dim3 grid, hipStream_t s, const AttnKParams& p) {
   if (sh.nw == 4)
-    hipLaunchKernelGGL((attn_bf16_kernel<D, 4, 1, 64>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((attn_bf16_kernel<D, 4, 1, 64, SK>), grid, dim3(256), 0, s, p);
   else if (sh.bn == 128)
-    hipLaunchKernelGGL((attn_bf16_kernel<D, 8, 1, 128>), grid, dim3(512), 0, s, p);
+    hipLaunchKernelGGL((attn_bf16_kernel<D, 8, 1, 128, SK>), grid, dim3(512), 0, s, p);
   else
-    hipLaunchKernelGGL((attn_bf16_kernel<D, 8, 1, 64>), grid, dim3(512), 0, s, p);
+    hipLaunchKernelGGL((attn_bf16_kernel<D, 8, 1, 64, SK>), grid, dim3(512), 0, s, p);
+}
+
+size_t stash_bytes(int64_t n_q, int32_t heads, int32_t head_dim, int64_t n_hist) {
+  return n_hist == 0 ? 0 : ((size_t)n_q * heads * head_dim * sizeof(float) + 255) & ~(size_t)255;
 }
 
 ispa_status_t launch_attention(const AttnArgs& a, hipStream_t s) {
@@ -705,12 +888,62 @@ ispa_status_t launch_attention(const AttnArgs& a, hipStream_t s) {
     const int bm = sh.nw * 32;
     p.n_qtiles = (int)((a.n_q + bm - 1) / bm);
     p.nblocks = p.n_qtiles * a.heads;
-    const dim3 grid(p.nblocks);
+    p.sk_p = 1;
+    p.part = nullptr;
+    if (a.sk_workers <= 0) {
+      const dim3 grid(p.nblocks);
+      if (a.head_dim == 128)
+        launch_bf16<128, false>(sh, grid, s, p);
+      else
+        launch_bf16<64, false>(sh, grid, s, p);
+      return hip_check(hipGetLastError(), "attn_bf16_kernel launch");
+    }
+    // split mode: each unit's key tiles cut into P pieces on P workgroups of its XCD
+    const int T = p.st0[p.n_seg];
+    const size_t need = splitkv_workspace_size(a.n_q, a.heads, a.head_dim, a.n_hist, a.sk_workers);
+    if (a.ws == nullptr || a.ws_bytes < need) {
+      set_error("split-KV attention: workspace smaller than ispa_decomp_attn_splitkv_workspace_size()");
+      return ISPA_E_WORKSPACE;
+    }
+    p.sk_p = sk_pieces(a.sk_workers, p.nblocks, T);
+    p.part = (float*)((char*)a.ws + stash_bytes(a.n_q, a.heads, a.head_dim, a.n_hist));
+    if (p.sk_p <= 1) {  // nothing to split: the unsplit launch
+      const dim3 grid(p.nblocks);
+      if (a.head_dim == 128)
+        launch_bf16<128, false>(sh, grid, s, p);
+      else
+        launch_bf16<64, false>(sh, grid, s, p);
+      return hip_check(hipGetLastError(), "attn_bf16_kernel launch");
+    }
+    const dim3 grid(a.sk_workers);
     if (a.head_dim == 128)
-      launch_bf16<128>(sh, grid, s, p);
+      launch_bf16<128, true>(sh, grid, s, p);
     else
-      launch_bf16<64>(sh, grid, s, p);
-    return hip_check(hipGetLastError(), "attn_bf16_kernel launch");
+      launch_bf16<64, true>(sh, grid, s, p);
+    ispa_status_t st = hip_check(hipGetLastError(), "attn_bf16_kernel (split) launch");
+    if (st != ISPA_OK) return st;
+    FixupParams f;
+    f.part = p.part;
+    f.O_loc = p.O_loc;
+    f.LSE_loc = p.LSE_loc;
+    f.O_hist = p.O_hist;
+    f.LSE_hist = p.LSE_hist;
+    f.O_full = p.O_full;
+    f.LSE_full = p.LSE_full;
+    f.n_q = p.n_q;
+    f.heads = p.heads;
+    f.n_qtiles = p.n_qtiles;
+    f.bm = bm;
+    f.T = T;
+    f.Tl = p.st0[p.n_loc_seg];
+    f.sk_p = p.sk_p;
+    const int rpb = 256 / (a.head_dim / 4);
+    const dim3 fgrid(p.nblocks, (bm + rpb - 1) / rpb);
+    if (a.head_dim == 128)
+      hipLaunchKernelGGL(sk_fixup_kernel<128>, fgrid, dim3(256), 0, s, f);
+    else
+      hipLaunchKernelGGL(sk_fixup_kernel<64>, fgrid, dim3(256), 0, s, f);
+    return hip_check(hipGetLastError(), "sk_fixup_kernel launch");
   }
   AttnF32Params p;
   p.Q = (const float*)a.Q;
@@ -744,6 +977,12 @@ ispa_status_t launch_attention(const AttnArgs& a, hipStream_t s) {
 size_t attention_workspace_size(int64_t n_q, int32_t heads, int32_t head_dim, int64_t n_hist, int32_t dtype) {
   if (dtype != ISPA_BF16 || n_hist == 0) return 0;
   return (size_t)n_q * heads * head_dim * sizeof(float);
+}
+
+size_t splitkv_workspace_size(int64_t n_q, int32_t heads, int32_t head_dim, int64_t n_hist, int32_t n_workers) {
+  if (n_q <= 0 || n_workers <= 0) return 0;
+  const int bm = attn_shape().nw * 32;
+  return stash_bytes(n_q, heads, head_dim, n_hist) + (size_t)n_workers * part_slot_floats(bm, head_dim) * 4;
 }
 
 ispa_status_t launch_lse_merge(int32_t n_parts, const void* const* O, const float* const* LSE, int64_t n_q,

@@ -49,8 +49,11 @@ struct AttnArgs {
   int32_t dtype;
   void* ws;
   size_t ws_bytes;
+  int32_t sk_workers;  // > 0: split mode with this many workgroups (bf16 only); 0: one workgroup per unit
 };
 size_t attention_workspace_size(int64_t n_q, int32_t heads, int32_t head_dim, int64_t n_hist, int32_t dtype);
+// Workspace of split mode: the merge's float32 O_loc (as above) and one partial slot per workgroup.
+size_t splitkv_workspace_size(int64_t n_q, int32_t heads, int32_t head_dim, int64_t n_hist, int32_t n_workers);
 ispa_status_t launch_attention(const AttnArgs& a, hipStream_t s);
 
 ispa_status_t launch_lse_merge(int32_t n_parts, const void* const* O, const float* const* LSE, int64_t n_q,

@@ -21,7 +21,8 @@ ISPA_OK, ISPA_E_INVALID_ARG, ISPA_E_UNSUPPORTED, ISPA_E_WORKSPACE, ISPA_E_HIP = 
 ISPA_F32, ISPA_BF16 = 0, 1
 
 EXPORTS = [
-    "ispa_decomp_attn", "ispa_decomp_attn_segments", "ispa_decomp_attn_workspace_size", "ispa_full_attn", "ispa_lse_merge", "ispa_gram_workspace_size", "ispa_gram_accum",
+    "ispa_decomp_attn", "ispa_decomp_attn_segments", "ispa_decomp_attn_splitkv",
+    "ispa_decomp_attn_splitkv_workspace_size", "ispa_decomp_attn_workspace_size", "ispa_full_attn", "ispa_lse_merge", "ispa_gram_workspace_size", "ispa_gram_accum",
     "ispa_absorb_workspace_size", "ispa_absorb_solve", "ispa_eps_workspace_size", "ispa_layer_eps",
     "ispa_select_layers", "ispa_absorb_apply", "ispa_status_string", "ispa_last_error", "ispa_version", "ispa_device_check",
 ]
@@ -50,6 +51,7 @@ class KvSegment(ctypes.Structure):
 
 
 ISPA_MAX_KV_SEGMENTS = 16
+ISPA_MAX_SPLITKV_WORKERS = 65535
 
 _lib = None
 
@@ -67,6 +69,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "ispa_decomp_attn": (I32, [ctypes.POINTER(AttnDesc)] + [P] * 12 + [SZ, P]),
         "ispa_decomp_attn_segments": (I32, [ctypes.POINTER(AttnDesc), P, ctypes.POINTER(KvSegment), I32, I32]
                                       + [P] * 7 + [SZ, P]),
+        "ispa_decomp_attn_splitkv": (I32, [ctypes.POINTER(AttnDesc), P, ctypes.POINTER(KvSegment), I32, I32, I32]
+                                     + [P] * 7 + [SZ, P]),
+        "ispa_decomp_attn_splitkv_workspace_size": (SZ, [ctypes.POINTER(AttnDesc), I32]),
         "ispa_decomp_attn_workspace_size": (SZ, [ctypes.POINTER(AttnDesc)]),
         "ispa_full_attn": (I32, [ctypes.POINTER(AttnDesc), P, P, P, P, P, P]),
         "ispa_lse_merge": (I32, [I32, P, P, I64, I32, I32, I32, P, P, P]),
@@ -169,11 +174,8 @@ def ispa_decomp_attn(q, k_loc, v_loc, k_hist=None, v_hist=None, *, scale=None, o
                                 _ptr(lse_full), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
-def ispa_decomp_attn_segments(q, loc_segs: Sequence, hist_segs: Sequence = (), *, scale=None, o_loc=None,
-                              lse_loc=None, o_hist=None, lse_hist=None, o_full=None, lse_full=None, workspace=None,
-                              stream=None) -> None:
-    """ispa_decomp_attn over K/V segments: ``loc_segs`` / ``hist_segs`` are sequences of (k, v) pairs,
-    each [n_i, H, D] contiguous, attended in place (no concatenation)."""
+def _segments(q, loc_segs, hist_segs, o_loc, o_hist, o_full, lse_loc, lse_hist, lse_full):
+    """Check shapes; marshal the (k, v) pairs into a KvSegment array."""
     n_q, H, D = q.shape
     segs = list(loc_segs) + list(hist_segs)
     arr = (KvSegment * max(len(segs), 1))()
@@ -191,12 +193,47 @@ def ispa_decomp_attn_segments(q, loc_segs: Sequence, hist_segs: Sequence = (), *
         _expect(t, (n_q, H, D), q.dtype, n)
     for t, n in ((lse_loc, "lse_loc"), (lse_hist, "lse_hist"), (lse_full, "lse_full")):
         _expect(t, (H, n_q), torch.float32, n)
+    return arr, len(segs), n_loc, n_hist
+
+
+def ispa_decomp_attn_splitkv_workspace_size(q, n_loc: int, n_hist: int, n_workers: int = 0, scale=None) -> int:
+    desc = make_desc(q, n_loc, n_hist, scale)
+    return int(load_library().ispa_decomp_attn_splitkv_workspace_size(ctypes.byref(desc), n_workers))
+
+
+def ispa_decomp_attn_splitkv(q, loc_segs: Sequence, hist_segs: Sequence = (), *, n_workers: int = 0, scale=None,
+                             o_loc=None, lse_loc=None, o_hist=None, lse_hist=None, o_full=None, lse_full=None,
+                             workspace=None, stream=None) -> None:
+    """Split-KV form of ispa_decomp_attn_segments: the (head, query tile, key tile) steps are shared
+    evenly by ``n_workers`` workgroups (0 = one per compute unit) and split units are merged through
+    their LSE states.  ``workspace`` (bytes >= ispa_decomp_attn_splitkv_workspace_size) is allocated
+    through torch for this call when omitted."""
+    arr, n_segs, n_loc, n_hist = _segments(q, loc_segs, hist_segs, o_loc, o_hist, o_full, lse_loc, lse_hist,
+                                           lse_full)
+    desc = make_desc(q, n_loc, n_hist, scale)
+    lib = load_library()
+    if workspace is None:
+        workspace = _workspace(int(lib.ispa_decomp_attn_splitkv_workspace_size(ctypes.byref(desc), n_workers)),
+                               q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.ispa_decomp_attn_splitkv(ctypes.byref(desc), _ptr(q), arr, n_segs, len(loc_segs), n_workers,
+                                        _ptr(o_loc), _ptr(lse_loc), _ptr(o_hist), _ptr(lse_hist), _ptr(o_full),
+                                        _ptr(lse_full), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def ispa_decomp_attn_segments(q, loc_segs: Sequence, hist_segs: Sequence = (), *, scale=None, o_loc=None,
+                              lse_loc=None, o_hist=None, lse_hist=None, o_full=None, lse_full=None, workspace=None,
+                              stream=None) -> None:
+    """ispa_decomp_attn over K/V segments: ``loc_segs`` / ``hist_segs`` are sequences of (k, v) pairs,
+    each [n_i, H, D] contiguous, attended in place (no concatenation)."""
+    arr, n_segs, n_loc, n_hist = _segments(q, loc_segs, hist_segs, o_loc, o_hist, o_full, lse_loc, lse_hist,
+                                           lse_full)
     desc = make_desc(q, n_loc, n_hist, scale)
     lib = load_library()
     if workspace is None and o_full is not None:
         workspace = _workspace(int(lib.ispa_decomp_attn_workspace_size(ctypes.byref(desc))), q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib.ispa_decomp_attn_segments(ctypes.byref(desc), _ptr(q), arr, len(segs), len(loc_segs),
+    _check(lib.ispa_decomp_attn_segments(ctypes.byref(desc), _ptr(q), arr, n_segs, len(loc_segs),
                                          _ptr(o_loc), _ptr(lse_loc), _ptr(o_hist), _ptr(lse_hist), _ptr(o_full),
                                          _ptr(lse_full), _ptr(workspace), ws_bytes, _stream(stream)))
 

@@ -121,3 +121,29 @@ def test_segment_validation_needs_no_gpu():
     assert ispa.ISPA_MAX_KV_SEGMENTS == 16
     hdr = open(os.path.join(ROOT, "include", "ispa.h")).read()
     assert "#define ISPA_MAX_KV_SEGMENTS 16" in hdr
+
+
+@pytest.mark.skipif(not os.path.exists(ispa.LIB_PATH), reason="libispa.so not built")
+def test_splitkv_validation_needs_no_gpu():
+    lib = ispa.load_library()
+    ok = 0x10000
+    seg = (ispa.KvSegment * 2)(ispa.KvSegment(ok, ok, 50), ispa.KvSegment(ok, ok, 70))
+
+    def call(desc, workers, n_loc_segs=1):
+        return lib.ispa_decomp_attn_splitkv(ctypes.byref(desc), ok, seg, 2, n_loc_segs, workers, *([None] * 6),
+                                            None, 0, None)
+
+    bad = ispa.ISPA_E_INVALID_ARG
+    d = ispa.AttnDesc(2, 128, 100, 50, 70, 0.1, 1)
+    assert call(ispa.AttnDesc(2, 128, 100, 50, 70, 0.1, 0), 4) == bad  # float32: bf16 only
+    assert b"bf16" in lib.ispa_last_error()
+    assert call(d, -1) == bad
+    assert call(d, 65536) == bad
+    assert call(d, 4, n_loc_segs=2) == bad  # local rows 120 != 50
+    # workspace: the merge's float32 O_loc (rounded up to 256 bytes) + 1 slot of 2*256*(128+1) floats per worker
+    stash = (100 * 2 * 128 * 4 + 255) // 256 * 256
+    slot = (2 * 256 * 128 + 2 * 256) * 4
+    assert lib.ispa_decomp_attn_splitkv_workspace_size(ctypes.byref(d), 7) == stash + 7 * slot
+    d0 = ispa.AttnDesc(2, 128, 100, 50, 0, 0.1, 1)
+    assert lib.ispa_decomp_attn_splitkv_workspace_size(ctypes.byref(d0), 7) == 7 * slot
+    assert lib.ispa_decomp_attn_splitkv_workspace_size(ctypes.byref(d), -3) == 0
