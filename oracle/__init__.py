@@ -22,7 +22,8 @@ these exact results, up to rounding order), in float64, with numpy/LAPACK
 primitives and no blocking or reordering beyond the definition.
 """
 from .softmax_attention import attention, branch_outputs, merge
-from .ridge_absorb import gram, gram_from_chunks, ridge_solve, objective, reconstruction_error, select_layers
+from .ridge_absorb import (gram, gram_from_chunks, ridge_solve, objective, reconstruction_error, select_layers,
+                           select_below, trace_scaled_lambda)
 
 __all__ = [
     "attention",
@@ -34,4 +35,6 @@ __all__ = [
     "objective",
     "reconstruction_error",
     "select_layers",
+    "select_below",
+    "trace_scaled_lambda",
 ]

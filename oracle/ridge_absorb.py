@@ -12,6 +12,13 @@ Memory-Efficient Video Generation", section 2 "Methodology":
 * "Dynamic Layer Selection": layers are ranked by their reconstruction error
   and the lowest-error ones are converted.
 
+The pages leave the error measure, lambda and the number of converted layers
+open; besides the reading used by default (below) the variants are: ranking by
+the error before the fit (``reconstruction_error`` with dW = 0), by the error on
+held-out rows (``reconstruction_error`` on rows the fit did not see), lambda
+proportional to the mean eigenvalue of G (:func:`trace_scaled_lambda`), and
+converting every layer whose error is under a threshold (:func:`select_below`).
+
 Readings (listed in the design notes): the norm is Frobenius and the objective
 is a sum (not a mean) over all warmup rows, every row weighted equally; lambda
 is absolute; W is the attention output projection in the row-vector convention
@@ -75,3 +82,16 @@ def select_layers(eps_rel, k):
     eps_rel = np.asarray(eps_rel, dtype=np.float64)
     order = np.argsort(eps_rel, kind="stable")
     return [int(i) for i in order[:k]]
+
+
+def trace_scaled_lambda(G, lam_scale):
+    """lambda = lam_scale * tr(G) / d: the ridge weight as a fraction of G's mean eigenvalue."""
+    G = np.asarray(G, dtype=np.float64)
+    return float(lam_scale) * float(np.trace(G)) / G.shape[0]
+
+
+def select_below(eps_rel, tau, k_max):
+    """Layers with eps_rel <= tau, lowest first (ties to the lower index), at most k_max; NaN never."""
+    eps_rel = np.asarray(eps_rel, dtype=np.float64)
+    order = [int(i) for i in np.argsort(eps_rel, kind="stable")]
+    return [i for i in order if eps_rel[i] <= tau][:k_max]

@@ -144,3 +144,61 @@ def test_standin_rows_conditioning():
     G, _ = oracle.gram(a_loc.f64, a_full.f64)
     ev = np.linalg.eigvalsh(G + 1e-2 * np.eye(256))
     assert 1e3 < ev[-1] / ev[0] < 1e7
+
+
+# ---------------------------------------------------------------- selection and lambda variants
+def test_trace_scaled_lambda_value_and_scale_invariance():
+    """lambda = scale * tr(G) / d: on G = diag(1, 2, 3, 6) the mean eigenvalue is 3.  With it the
+    update is unchanged when both streams are scaled by c (G, C scale by c^2, so does lambda); with
+    an absolute lambda it is not."""
+    assert oracle.trace_scaled_lambda(np.diag([1.0, 2.0, 3.0, 6.0]), 0.5) == pytest.approx(1.5, rel=1e-15)
+    # eigenvalues, not the diagonal, set the trace: a rotated G gives the same lambda
+    Qm, _ = np.linalg.qr(np.random.default_rng(3).standard_normal((4, 4)))
+    assert oracle.trace_scaled_lambda(Qm @ np.diag([1.0, 2.0, 3.0, 6.0]) @ Qm.T, 0.5) == pytest.approx(1.5, rel=1e-13)
+    a_loc, a_full = _rows(21, 300, 12)
+    W = np.random.default_rng(22).standard_normal((12, 8)) / 3
+    c = 7.0
+    G1, C1 = oracle.gram(a_loc, a_full)
+    G2, C2 = oracle.gram(c * a_loc, c * a_full)
+    d1 = oracle.ridge_solve(G1, C1, W, oracle.trace_scaled_lambda(G1, 1e-2))
+    d2 = oracle.ridge_solve(G2, C2, W, oracle.trace_scaled_lambda(G2, 1e-2))
+    assert np.max(np.abs(d1 - d2)) <= 1e-12 * np.max(np.abs(d1))
+    a1 = oracle.ridge_solve(G1, C1, W, 1.0)
+    a2 = oracle.ridge_solve(G2, C2, W, 1.0)
+    assert np.max(np.abs(a1 - a2)) > 1e-6
+
+
+def test_select_below_brute_force():
+    rng = np.random.default_rng(5)
+    for trial in range(200):
+        n = int(rng.integers(1, 12))
+        eps = rng.choice([0.1, 0.2, 0.3, 0.5, np.nan], size=n)
+        tau = float(rng.choice([0.0, 0.15, 0.3, 1.0]))
+        k_max = int(rng.integers(0, n + 1))
+        got = oracle.select_below(eps, tau, k_max)
+        # brute force: all (eps, index) pairs under the threshold in lexicographic order
+        want = [i for _, i in sorted((float(eps[i]), i) for i in range(n) if eps[i] <= tau)][:k_max]
+        assert got == want, (eps, tau, k_max)
+    assert oracle.select_below([0.5, 0.1, 0.3, 0.1, np.nan], 0.3, 10) == [1, 3, 2]
+    assert oracle.select_below([0.5, 0.1, 0.3, 0.1], 0.3, 2) == [1, 3]
+    assert oracle.select_below([0.5, 0.4], 0.3, 2) == []
+
+
+def test_prefit_and_heldout_errors_are_the_residual_definition():
+    """The variants reuse reconstruction_error: at dW = 0 it is ||(A_full - A_loc) W||^2, and on
+    held-out rows it is that residual with the update fitted elsewhere, which the fitted rows'
+    closed form (using the normal equation) does not give."""
+    a_loc, a_full = _rows(31, 500, 16)
+    W = np.random.default_rng(32).standard_normal((16, 16)) / 4
+    eps0, rel0 = oracle.reconstruction_error(a_loc, a_full, W, np.zeros((16, 16)))
+    diff = (a_full - a_loc) @ W
+    assert eps0 == pytest.approx(float(np.einsum("ij,ij->", diff, diff)), rel=1e-13)
+    G, C = oracle.gram(a_loc[:400], a_full[:400])
+    dW = oracle.ridge_solve(G, C, W, 1e-2)
+    Gh, Ch = oracle.gram(a_loc[400:], a_full[400:])
+    Qh = a_full[400:].T @ a_full[400:]
+    eh, _ = oracle.reconstruction_error(a_loc[400:], a_full[400:], W, dW)
+    general = (np.sum((Qh - Ch - Ch.T - Gh) * (W @ W.T)) + np.sum(dW * (Gh @ dW)) - 2 * np.sum(dW * (Ch @ W)))
+    assert eh == pytest.approx(general, rel=1e-10)
+    fitted_form = np.sum((Qh - Ch - Ch.T - Gh) * (W @ W.T)) - np.sum(dW * (Ch @ W)) - 1e-2 * np.sum(dW * dW)
+    assert abs(eh - fitted_form) > 1e-6 * abs(eh)

@@ -18,6 +18,8 @@ _merge = oatt.merge
 _gram = oabs.gram
 _solve = oabs.ridge_solve
 _eps = oabs.reconstruction_error
+_tlam = oabs.trace_scaled_lambda
+_below = oabs.select_below
 
 
 def _attn_pins():
@@ -43,6 +45,13 @@ def _absorb_pins():
         PA.test_large_lambda_limit,
         PA.test_solution_minimises_objective,
         PA.test_reconstruction_error_closed_form,
+    ]
+
+
+def _variant_pins():
+    return [
+        PA.test_trace_scaled_lambda_value_and_scale_invariance,
+        PA.test_select_below_brute_force,
     ]
 
 
@@ -101,6 +110,35 @@ EPS_MUTANTS = {
 }
 
 
+TLAM_MUTANTS = {
+    "trace without 1/d": lambda G, s: s * float(np.trace(np.asarray(G, float))),
+    "mean diagonal of G^2": lambda G, s: s * float(np.trace(np.asarray(G, float) @ np.asarray(G, float))) / len(G),
+    "largest diagonal entry": lambda G, s: s * float(np.max(np.diag(np.asarray(G, float)))),
+    "constant (absolute) lambda": lambda G, s: float(s),
+}
+
+BELOW_MUTANTS = {
+    "strict threshold": lambda e, t, k: [i for i in _below(e, t, k + 1) if np.asarray(e, float)[i] < t][:k],
+    "NaN admitted": lambda e, t, k: [int(i) for i in np.argsort(np.nan_to_num(np.asarray(e, float), nan=-1.0),
+                                                               kind="stable") if not np.asarray(e, float)[i] > t][:k],
+    "cap ignored": lambda e, t, k: _below(e, t, len(e)),
+    "ties to the higher index": lambda e, t, k: [-j for _, j in sorted(
+        (float(np.asarray(e, float)[i]), -i) for i in range(len(e)) if np.asarray(e, float)[i] <= t)][:k],
+}
+
+
+@pytest.mark.parametrize("name", TLAM_MUTANTS)
+def test_trace_lambda_mutant_caught(name, monkeypatch):
+    monkeypatch.setattr(oracle, "trace_scaled_lambda", TLAM_MUTANTS[name])
+    assert _some_pin_fails(_variant_pins()), name
+
+
+@pytest.mark.parametrize("name", BELOW_MUTANTS)
+def test_select_below_mutant_caught(name, monkeypatch):
+    monkeypatch.setattr(oracle, "select_below", BELOW_MUTANTS[name])
+    assert _some_pin_fails(_variant_pins()), name
+
+
 @pytest.mark.parametrize("name", ATTN_MUTANTS)
 def test_attention_mutant_caught(name, monkeypatch):
     monkeypatch.setattr(oracle, "attention", ATTN_MUTANTS[name])
@@ -134,3 +172,4 @@ def test_eps_mutant_caught(name, monkeypatch):
 def test_unmutated_oracle_passes_every_pin():
     assert not _some_pin_fails(_attn_pins())
     assert not _some_pin_fails(_absorb_pins())
+    assert not _some_pin_fails(_variant_pins())
