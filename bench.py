@@ -403,6 +403,30 @@ def bench_stack(args, host_inputs):
         full_post.append(e0.elapsed_time(e1))
     full_post_ms = float(np.median(full_post))
 
+    # the transition under the other selection / lambda policies, on the same warmup statistics
+    policies = {}
+    for name, kw in (("prefit", dict(selection="prefit")), ("heldout", dict(selection="heldout")),
+                     ("trace_lambda", dict(lam_policy="trace")), ("threshold", dict(threshold=0.5))):
+        times, n_c = [], 0
+        for _ in range(max(args.steps, 2)):
+            st2 = LayerStack(W0.clone(), H, D, nq, cfg.lam if "lam_policy" not in kw else 1e-4, cfg.n_absorb, **kw)
+            st2.G.copy_(st.G)
+            st2.C.copy_(st.C)
+            st2.Q_ff.copy_(st.Q_ff)
+            st2.chunks_seen = [cfg.n_chunks] * L
+            if kw.get("selection") == "heldout":  # timing stand-in: the fitted rows as held-out rows
+                st2.G_h.copy_(st.G)
+                st2.C_h.copy_(st.C)
+                st2.Q_h.copy_(st.Q_ff)
+                st2.heldout_seen = [1] * L
+            torch.cuda.synchronize()
+            t_a = time.perf_counter()
+            n_c = len(st2.transition())
+            torch.cuda.synchronize()
+            times.append((time.perf_counter() - t_a) * 1e3)
+            del st2
+        policies[name] = {"transition_ms": round(float(np.median(times)), 3), "converted": n_c}
+
     n_conv = len(conv)
     f_full, f_loc = cfg.attn_flops(), cfg.attn_flops(n_hist=0)
     warm_flops = L * cfg.n_chunks * f_full
@@ -435,6 +459,7 @@ def bench_stack(args, host_inputs):
         "warmup_ms": round(warm_ms, 3),
         "warmup_attn_gram_tflops": round(warm_tf, 2),
         "transition_ms": round(solve_ms + conv_ms, 3),
+        "transition_policies": policies,
         "absorb_ms_per_layer": round(solve_ms / L, 4),
         "post_chunk_ms": round(post_ms, 3),
         "post_chunk_ms_no_eviction": round(full_post_ms, 3),

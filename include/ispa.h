@@ -18,6 +18,10 @@
  *   ispa_layer_eps     the post-fit reconstruction error used to rank layers,
  *   ispa_select_layers the k lowest-error layers (those converted),
  *   ispa_absorb_apply  W += dW for the converted layers,
+ *   ispa_fit_error, ispa_lambda_from_trace, ispa_absorb_solve_lambdas,
+ *   ispa_select_layers_below, ispa_gather_layers, ispa_absorb_apply_compact
+ *                      selection and lambda variants (error before the fit or
+ *                      on held-out rows, lambda from tr(G), threshold K),
  *   ispa_full_attn     one softmax pass over all keys (the comparison pass),
  *   ispa_lse_merge     standalone N-way merge of (O, LSE) partial results.
  *
@@ -316,6 +320,83 @@ ispa_status_t ispa_select_layers(int32_t n_layers, const double* eps, int32_t k,
  */
 ispa_status_t ispa_absorb_apply(int32_t d, int32_t d_out, int32_t n_layers, const int32_t* selected,
                                 int32_t k, const float* dW, float* W, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Selection and lambda variants.  The pages leave the error measure, the ridge
+ * weight and the number of converted layers open; these calls give the other
+ * plain readings (ISPA technical summary, section 2, "Layer Absorb" and
+ * "Dynamic Layer Selection").
+ * ------------------------------------------------------------------------- */
+
+/* Workspace bytes ispa_fit_error needs: 4 * batch * d * d_out float32. */
+size_t ispa_fit_error_workspace_size(int32_t d, int32_t d_out, int32_t batch);
+
+/*
+ * ispa_fit_error — eps = ||A_loc (W + dW) - A_full W||_F^2 over the rows
+ * whose statistics are G, C, Q_ff (as ispa_gram_accum writes them), for ANY
+ * dW: rows the fit did not see (held-out error), or dW = NULL (dW = 0: the
+ * discrepancy before the fit, ||(A_full - A_loc) W||^2, which needs no
+ * solve).  From the statistics:
+ *   eps = <Q_ff W, W> - 2 <C W, W> - <G W, W> + <G dW, dW> - 2 <dW, C W>,
+ *   eps_rel = eps / <Q_ff W, W>.
+ * ispa_layer_eps is the special case where dW solves the ridge problem on the
+ * same rows.  Products in float32, inner products reduced in float64.
+ *   G, C, Q_ff [batch, d, d]; W, dW [batch, d, d_out] float32 (dW nullable);
+ *   eps_abs, eps_rel [batch] float64 DEVICE.  d, d_out multiples of 64.
+ */
+ispa_status_t ispa_fit_error(int32_t d, int32_t d_out, int32_t batch, const float* G, const float* C,
+                             const float* Q_ff, const float* W, const float* dW, double* eps_abs,
+                             double* eps_rel, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ispa_lambda_from_trace — lambdas[b] = lam_scale * tr(G_b) / d (G's mean
+ * eigenvalue; the trace summed in float64): a ridge weight that scales with
+ * the layer's activations, so dW does not change when both streams are
+ * scaled.  G [batch, d, d] float32, lambdas [batch] float32 DEVICE;
+ * lam_scale finite, >= 0.
+ */
+ispa_status_t ispa_lambda_from_trace(int32_t d, int32_t batch, const float* G, float lam_scale, float* lambdas,
+                                     void* stream);
+
+/*
+ * ispa_absorb_solve_lambdas — ispa_absorb_solve with lambda read per layer
+ * from the DEVICE array lambdas [batch] float32 (as ispa_lambda_from_trace
+ * writes it).  Same arguments, workspace and errors otherwise; a lambda that
+ * leaves G + lambda I indefinite shows up in info, not as an error.
+ */
+ispa_status_t ispa_absorb_solve_lambdas(int32_t d, int32_t d_out, int32_t batch, const float* G, const float* C,
+                                        const float* W, const float* lambdas, float* dW, float* W_new,
+                                        int32_t* info, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ispa_select_layers_below — convert every layer whose error is at most tau,
+ * lowest first, at most k_max of them (the number converted then follows from
+ * the errors instead of being fixed).  Same total order as
+ * ispa_select_layers (eps ascending, ties to the lower id, NaN never chosen).
+ *   eps [n_layers] float64 DEVICE; 1 <= n_layers <= 4096; 0 <= k_max <= n_layers;
+ *   tau not NaN.  selected [k_max] int32 DEVICE (the first *count entries are
+ *   written); count [1] int32 DEVICE; rank [n_layers] int32 DEVICE or NULL.
+ */
+ispa_status_t ispa_select_layers_below(int32_t n_layers, const double* eps, double tau, int32_t k_max,
+                                       int32_t* selected, int32_t* count, int32_t* rank, void* stream);
+
+/*
+ * ispa_gather_layers — dst[s] = src[selected[s]] for s < k, each layer
+ * per_layer float32 values (to solve only the chosen layers, e.g. after
+ * ranking by ispa_fit_error with dW = NULL).  src [n_layers, per_layer],
+ * dst [k, per_layer] DEVICE; an id outside [0, n_layers) gives a NaN layer.
+ */
+ispa_status_t ispa_gather_layers(int32_t n_layers, int64_t per_layer, const float* src, const int32_t* selected,
+                                 int32_t k, float* dst, void* stream);
+
+/*
+ * ispa_absorb_apply_compact — W[selected[s]] += dW[s] for s < k, where dW
+ * [k, d, d_out] holds only the chosen layers in selection order (the output
+ * of a solve on gathered layers).  W [n_layers, d, d_out] float32 DEVICE; ids
+ * distinct; an id outside [0, n_layers) is skipped.
+ */
+ispa_status_t ispa_absorb_apply_compact(int32_t d, int32_t d_out, int32_t n_layers, const int32_t* selected,
+                                        int32_t k, const float* dW, float* W, void* stream);
 
 /* Human-readable name of a status code (static string). */
 const char* ispa_status_string(ispa_status_t status);

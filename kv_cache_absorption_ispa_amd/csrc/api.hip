@@ -333,8 +333,49 @@ ispa_status_t ispa_absorb_solve(int32_t d, int32_t d_out, int32_t batch, const f
     return invalid("G, C, W, dW, info must be non-NULL and 16-byte aligned");
   ispa_status_t st = check_current_device();
   if (st != ISPA_OK) return st;
-  return launch_absorb(d, d_out, batch, G, C, W, lambda, dW, W_new, info, workspace, workspace_bytes,
+  return launch_absorb(d, d_out, batch, G, C, W, lambda, nullptr, dW, W_new, info, workspace, workspace_bytes,
                        (hipStream_t)stream);
+}
+
+ispa_status_t ispa_absorb_solve_lambdas(int32_t d, int32_t d_out, int32_t batch, const float* G, const float* C,
+                                        const float* W, const float* lambdas, float* dW, float* W_new,
+                                        int32_t* info, void* workspace, size_t workspace_bytes, void* stream) {
+  if (d <= 0 || d % 64 != 0 || d_out <= 0 || d_out % 64 != 0) return invalid("d and d_out must be multiples of 64");
+  if (batch < 1 || batch > 65535) return invalid("batch must be in [1, 65535]");
+  if (!req(G) || !req(C) || !req(W) || !req(lambdas) || !req(dW) || !req(info) || !opt(W_new))
+    return invalid("G, C, W, lambdas, dW, info must be non-NULL and 16-byte aligned");
+  ispa_status_t st = check_current_device();
+  if (st != ISPA_OK) return st;
+  return launch_absorb(d, d_out, batch, G, C, W, 0.f, lambdas, dW, W_new, info, workspace, workspace_bytes,
+                       (hipStream_t)stream);
+}
+
+ispa_status_t ispa_lambda_from_trace(int32_t d, int32_t batch, const float* G, float lam_scale, float* lambdas,
+                                     void* stream) {
+  if (d <= 0 || batch < 1 || batch > 65535) return invalid("need d > 0 and batch in [1, 65535]");
+  if (!(lam_scale >= 0.f) || lam_scale == INFINITY) return invalid("lam_scale must be finite and >= 0");
+  if (!req(G) || !req(lambdas)) return invalid("G, lambdas must be non-NULL and 16-byte aligned");
+  ispa_status_t st = check_current_device();
+  if (st != ISPA_OK) return st;
+  return launch_trace_lambda(d, batch, G, lam_scale, lambdas, (hipStream_t)stream);
+}
+
+size_t ispa_fit_error_workspace_size(int32_t d, int32_t d_out, int32_t batch) {
+  if (d <= 0 || d_out <= 0 || batch <= 0) return 0;
+  return fit_error_workspace_size(d, d_out, batch);
+}
+
+ispa_status_t ispa_fit_error(int32_t d, int32_t d_out, int32_t batch, const float* G, const float* C,
+                             const float* Q_ff, const float* W, const float* dW, double* eps_abs, double* eps_rel,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  if (d <= 0 || d % 64 != 0 || d_out <= 0 || d_out % 64 != 0) return invalid("d and d_out must be multiples of 64");
+  if (batch < 1 || batch > 65535) return invalid("batch must be in [1, 65535]");
+  if (!req(G) || !req(C) || !req(Q_ff) || !req(W) || !opt(dW) || !req(eps_abs) || !req(eps_rel))
+    return invalid("G, C, Q_ff, W, eps_abs, eps_rel must be non-NULL (dW may be NULL) and 16-byte aligned");
+  ispa_status_t st = check_current_device();
+  if (st != ISPA_OK) return st;
+  return launch_fit_error(d, d_out, batch, G, C, Q_ff, W, dW, eps_abs, eps_rel, workspace, workspace_bytes,
+                          (hipStream_t)stream);
 }
 
 size_t ispa_eps_workspace_size(int32_t d, int32_t d_out, int32_t batch) {
@@ -365,6 +406,41 @@ ispa_status_t ispa_select_layers(int32_t n_layers, const double* eps, int32_t k,
   ispa_status_t st = check_current_device();
   if (st != ISPA_OK) return st;
   return launch_select_layers(n_layers, eps, k, selected, rank, (hipStream_t)stream);
+}
+
+ispa_status_t ispa_select_layers_below(int32_t n_layers, const double* eps, double tau, int32_t k_max,
+                                       int32_t* selected, int32_t* count, int32_t* rank, void* stream) {
+  if (n_layers < 1 || n_layers > MAX_STACK_LAYERS) return invalid("n_layers must be in [1, 4096]");
+  if (k_max < 0 || k_max > n_layers) return invalid("k_max must be in [0, n_layers]");
+  if (tau != tau) return invalid("tau is NaN");
+  if (!req(eps) || !req(count) || (k_max > 0 && !req(selected)) || !opt(selected) || !opt(rank))
+    return invalid("eps, count (and selected when k_max > 0) must be non-NULL and 16-byte aligned");
+  ispa_status_t st = check_current_device();
+  if (st != ISPA_OK) return st;
+  return launch_select_below(n_layers, eps, tau, k_max, selected, count, rank, (hipStream_t)stream);
+}
+
+ispa_status_t ispa_gather_layers(int32_t n_layers, int64_t per_layer, const float* src, const int32_t* selected,
+                                 int32_t k, float* dst, void* stream) {
+  if (n_layers < 1 || n_layers > 65535 || per_layer < 1) return invalid("need n_layers in [1, 65535], per_layer >= 1");
+  if (k < 0 || k > 65535) return invalid("k must be in [0, 65535]");
+  if (k == 0) return ISPA_OK;
+  if (!req(src) || !req(selected) || !req(dst)) return invalid("src, selected, dst must be non-NULL and 16-byte aligned");
+  ispa_status_t st = check_current_device();
+  if (st != ISPA_OK) return st;
+  return launch_gather_layers(k, (size_t)per_layer, src, selected, n_layers, dst, (hipStream_t)stream);
+}
+
+ispa_status_t ispa_absorb_apply_compact(int32_t d, int32_t d_out, int32_t n_layers, const int32_t* selected,
+                                        int32_t k, const float* dW, float* W, void* stream) {
+  if (d <= 0 || d_out <= 0 || ((int64_t)d * d_out) % 4 != 0) return invalid("d * d_out must be a positive multiple of 4");
+  if (n_layers < 1 || n_layers > 65535) return invalid("n_layers must be in [1, 65535]");
+  if (k < 0 || k > n_layers) return invalid("k must be in [0, n_layers]");
+  if (k == 0) return ISPA_OK;
+  if (!req(selected) || !req(dW) || !req(W)) return invalid("selected, dW, W must be non-NULL and 16-byte aligned");
+  ispa_status_t st = check_current_device();
+  if (st != ISPA_OK) return st;
+  return launch_absorb_apply_compact(d, d_out, n_layers, selected, k, dW, W, (hipStream_t)stream);
 }
 
 ispa_status_t ispa_absorb_apply(int32_t d, int32_t d_out, int32_t n_layers, const int32_t* selected, int32_t k,

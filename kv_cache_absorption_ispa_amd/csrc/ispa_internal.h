@@ -67,8 +67,19 @@ ispa_status_t launch_gram(int64_t n_rows, int32_t d, int32_t dtype, const void* 
 
 size_t absorb_workspace_size(int32_t d, int32_t d_out, int32_t batch);
 ispa_status_t launch_absorb(int32_t d, int32_t d_out, int32_t batch, const float* G, const float* C,
-                            const float* W, float lambda, float* dW, float* W_new, int32_t* info, void* ws,
-                            size_t ws_bytes, hipStream_t s);
+                            const float* W, float lambda, const float* lam_b, float* dW, float* W_new,
+                            int32_t* info, void* ws, size_t ws_bytes, hipStream_t s);
+size_t fit_error_workspace_size(int32_t d, int32_t d_out, int32_t batch);
+ispa_status_t launch_fit_error(int32_t d, int32_t d_out, int32_t batch, const float* G, const float* C,
+                               const float* Qff, const float* W, const float* dW, double* eps_abs, double* eps_rel,
+                               void* ws, size_t ws_bytes, hipStream_t s);
+ispa_status_t launch_trace_lambda(int32_t d, int32_t batch, const float* G, float scale, float* lam, hipStream_t s);
+ispa_status_t launch_select_below(int32_t n_layers, const double* eps, double tau, int32_t k_max, int32_t* selected,
+                                  int32_t* count, int32_t* rank, hipStream_t s);
+ispa_status_t launch_gather_layers(int32_t k, size_t per_layer, const float* src, const int32_t* selected,
+                                   int32_t n_layers, float* dst, hipStream_t s);
+ispa_status_t launch_absorb_apply_compact(int32_t d, int32_t d_out, int32_t n_layers, const int32_t* selected,
+                                          int32_t k, const float* dW, float* W, hipStream_t s);
 
 size_t eps_workspace_size(int32_t d, int32_t d_out, int32_t batch);
 ispa_status_t launch_eps(int32_t d, int32_t d_out, int32_t batch, const float* G, const float* C,

@@ -147,6 +147,7 @@ struct GemmDParams {
   int lda, ldb, ldc, ldx, ldd;
   size_t sA, sB, sC, sX, sD;
   double alpha, beta, gamma;
+  const float* gamma_b;  // nullable: gamma * gamma_b[b] for batch entry b (per-layer lambda)
   const int32_t* info;
 };
 
@@ -168,6 +169,7 @@ __global__ __launch_bounds__(256) void gemm_f64acc_kernel(GemmDParams p) {
   const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
   const float* A = p.A + b * p.sA;
   const float* B = p.B + b * p.sB;
+  const double gb = p.gamma_b ? p.gamma * (double)p.gamma_b[b] : p.gamma;
   f64x4 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -208,7 +210,7 @@ __global__ __launch_bounds__(256) void gemm_f64acc_kernel(GemmDParams p) {
         const int c = n0 + wn + 16 * j + l16;
         double x = p.alpha * acc[i][j][v];
         if (p.Cin) x += p.beta * (double)p.Cin[b * p.sC + (size_t)r * p.ldc + c];
-        if (p.X) x += p.gamma * (double)p.X[b * p.sX + (size_t)r * p.ldx + c];
+        if (p.X) x += gb * (double)p.X[b * p.sX + (size_t)r * p.ldx + c];
         if (p.D64) p.D64[b * p.sD + (size_t)r * p.ldd + c] = x;
         if (p.D32) p.D32[b * p.sD + (size_t)r * p.ldd + c] = (float)x;
       }
@@ -216,8 +218,9 @@ __global__ __launch_bounds__(256) void gemm_f64acc_kernel(GemmDParams p) {
 
 // M = G + lambda I (full matrix); info = 0.
 __global__ __launch_bounds__(256) void init_shift_kernel(const float* __restrict__ G, float* M, int d, float lambda,
-                                                         int32_t* info) {
+                                                         const float* __restrict__ lam_b, int32_t* info) {
   const int b = blockIdx.y;
+  if (lam_b) lambda = lam_b[b];
   const size_t dd = (size_t)d * d;
   const size_t i4 = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (blockIdx.x == 0 && threadIdx.x == 0) info[b] = 0;
@@ -438,6 +441,56 @@ __global__ __launch_bounds__(256) void eps_reduce_kernel(const float* W, const f
   }
 }
 
+// Reconstruction error for any dW (held-out rows, or dW = 0 before the fit), from the statistics:
+// eps = <Q_ff W, W> - 2 <C W, W> - <G W, W> + <G dW, dW> - 2 <dW, C W>; float64 reductions.
+__global__ __launch_bounds__(256) void fit_error_reduce_kernel(const float* W, const float* dW, const float* QW,
+                                                               const float* CW, const float* GW, const float* GdW,
+                                                               size_t n, double* eps_abs, double* eps_rel) {
+  const int b = blockIdx.x;
+  const size_t off = (size_t)b * n;
+  double s[5] = {0, 0, 0, 0, 0};
+  for (size_t i = threadIdx.x; i < n; i += 256) {
+    const double w = W[off + i], cw = CW[off + i];
+    s[0] += (double)QW[off + i] * w;
+    s[1] += cw * w;
+    s[2] += (double)GW[off + i] * w;
+    if (dW) {
+      const double dw = dW[off + i];
+      s[3] += (double)GdW[off + i] * dw;
+      s[4] += dw * cw;
+    }
+  }
+  __shared__ double red[5][256];
+  for (int k = 0; k < 5; ++k) red[k][threadIdx.x] = s[k];
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w)
+      for (int k = 0; k < 5; ++k) red[k][threadIdx.x] += red[k][threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const double e = red[0][0] - 2.0 * red[1][0] - red[2][0] + red[3][0] - 2.0 * red[4][0];
+    eps_abs[b] = e;
+    eps_rel[b] = e / red[0][0];
+  }
+}
+
+// lambda_b = scale * tr(G_b) / d (trace summed in float64, fixed order).
+__global__ __launch_bounds__(256) void trace_lambda_kernel(int d, const float* G, float scale, float* lam) {
+  const int b = blockIdx.x;
+  const float* g = G + (size_t)b * d * d;
+  double t = 0;
+  for (int i = threadIdx.x; i < d; i += 256) t += g[(size_t)i * d + i];
+  __shared__ double red[256];
+  red[threadIdx.x] = t;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) lam[b] = (float)((double)scale * red[0] / d);
+}
+
 template <bool TA, bool TB>
 ispa_status_t gemm(hipStream_t s, int batch, int M, int N, int K, const float* A, int lda, size_t sA, const float* B,
                    int ldb, size_t sB, const float* Cin, int ldc, size_t sC, float* D, int ldd, size_t sD, float alpha,
@@ -468,13 +521,14 @@ ispa_status_t gemm(hipStream_t s, int batch, int M, int N, int K, const float* A
 ispa_status_t gemm_d(hipStream_t s, int batch, int M, int N, int K, const float* A, int lda, size_t sA,
                      const float* B, int ldb, size_t sB, const float* Cin, int ldc, size_t sC, const float* X,
                      int ldx, size_t sX, double* D64, float* D32, int ldd, size_t sD, double alpha, double beta,
-                     double gamma, const int32_t* info) {
+                     double gamma, const int32_t* info, const float* gamma_b = nullptr) {
   GemmDParams p;
   p.A = A; p.B = B; p.Cin = Cin; p.X = X; p.D64 = D64; p.D32 = D32;
   p.M = M; p.N = N; p.K = K;
   p.lda = lda; p.ldb = ldb; p.ldc = ldc; p.ldx = ldx; p.ldd = ldd;
   p.sA = sA; p.sB = sB; p.sC = sC; p.sX = sX; p.sD = sD;
   p.alpha = alpha; p.beta = beta; p.gamma = gamma;
+  p.gamma_b = gamma_b;
   p.info = info;
   hipLaunchKernelGGL(gemm_f64acc_kernel, dim3(N / 64, M / 64, batch), dim3(256), 0, s, p);
   return hip_check(hipGetLastError(), "gemm_f64acc_kernel launch");
@@ -552,8 +606,8 @@ ispa_status_t invert_lower(hipStream_t s, int batch, int d, const float* L, floa
 }
 
 ispa_status_t launch_absorb(int32_t d, int32_t d_out, int32_t batch, const float* G, const float* C, const float* W,
-                            float lambda, float* dW, float* W_new, int32_t* info, void* ws, size_t ws_bytes,
-                            hipStream_t s) {
+                            float lambda, const float* lam_b, float* dW, float* W_new, int32_t* info, void* ws,
+                            size_t ws_bytes, hipStream_t s) {
   const size_t need = absorb_workspace_size(d, d_out, batch);
   if (ws == nullptr || ws_bytes < need) {
     set_error("ispa_absorb_solve: workspace too small");
@@ -569,7 +623,7 @@ ispa_status_t launch_absorb(int32_t d, int32_t d_out, int32_t batch, const float
   const int nblk = d / NB;
 
   hipLaunchKernelGGL(init_shift_kernel, dim3((unsigned)((dd / 4 + 255) / 256), batch), dim3(256), 0, s, G, M, d,
-                     lambda, info);
+                     lambda, lam_b, info);
   ISPA_TRY(hip_check(hipGetLastError(), "init_shift_kernel launch"));
   // R = C W (float32; R's rounding perturbs the solution like the float32 statistics themselves do)
   ISPA_TRY((gemm<false, false>(s, batch, d, d_out, d, C, d, dd, W, d_out, dn, nullptr, 0, 0, Rb, d_out, dn, 1.f, 0.f,
@@ -599,11 +653,46 @@ ispa_status_t launch_absorb(int32_t d, int32_t d_out, int32_t batch, const float
   // refinement: r = R - G X - lambda X accumulated in float64 (the cancellation needs it),
   // correction = (L L^T)^-1 r
   ISPA_TRY(gemm_d(s, batch, d, d_out, d, G, d, dd, dW, d_out, dn, Rb, d_out, dn, dW, d_out, dn, nullptr, Rr, d_out,
-                  dn, -1.0, 1.0, -(double)lambda, info));
+                  dn, -1.0, 1.0, lam_b ? -1.0 : -(double)lambda, info, lam_b));
   ISPA_TRY(chol_apply(s, batch, d, d_out, Linvf, Rr, Zb, Rr, info));
   hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)((dn / 4 + 255) / 256), batch), dim3(256), 0, s, W, dW,
                      (const float*)Rr, W_new, dn, (const int32_t*)info);
   return hip_check(hipGetLastError(), "finalize_kernel launch");
+}
+
+size_t fit_error_workspace_size(int32_t d, int32_t d_out, int32_t batch) {
+  return 4 * (size_t)batch * d * d_out * sizeof(float);
+}
+
+ispa_status_t launch_fit_error(int32_t d, int32_t d_out, int32_t batch, const float* G, const float* C,
+                               const float* Qff, const float* W, const float* dW, double* eps_abs, double* eps_rel,
+                               void* ws, size_t ws_bytes, hipStream_t s) {
+  if (ws == nullptr || ws_bytes < fit_error_workspace_size(d, d_out, batch)) {
+    set_error("ispa_fit_error: workspace too small");
+    return ISPA_E_WORKSPACE;
+  }
+  const size_t dd = (size_t)d * d, dn = (size_t)d * d_out;
+  float* QW = (float*)ws;
+  float* CW = QW + (size_t)batch * dn;
+  float* GW = CW + (size_t)batch * dn;
+  float* GdW = GW + (size_t)batch * dn;
+  ISPA_TRY((gemm<false, false>(s, batch, d, d_out, d, Qff, d, dd, W, d_out, dn, nullptr, 0, 0, QW, d_out, dn, 1.f, 0.f,
+                               false, nullptr)));
+  ISPA_TRY((gemm<false, false>(s, batch, d, d_out, d, C, d, dd, W, d_out, dn, nullptr, 0, 0, CW, d_out, dn, 1.f, 0.f,
+                               false, nullptr)));
+  ISPA_TRY((gemm<false, false>(s, batch, d, d_out, d, G, d, dd, W, d_out, dn, nullptr, 0, 0, GW, d_out, dn, 1.f, 0.f,
+                               false, nullptr)));
+  if (dW)
+    ISPA_TRY((gemm<false, false>(s, batch, d, d_out, d, G, d, dd, dW, d_out, dn, nullptr, 0, 0, GdW, d_out, dn, 1.f,
+                                 0.f, false, nullptr)));
+  hipLaunchKernelGGL(fit_error_reduce_kernel, dim3(batch), dim3(256), 0, s, W, dW, QW, CW, GW, GdW, dn, eps_abs,
+                     eps_rel);
+  return hip_check(hipGetLastError(), "fit_error_reduce_kernel launch");
+}
+
+ispa_status_t launch_trace_lambda(int32_t d, int32_t batch, const float* G, float scale, float* lam, hipStream_t s) {
+  hipLaunchKernelGGL(trace_lambda_kernel, dim3(batch), dim3(256), 0, s, d, G, scale, lam);
+  return hip_check(hipGetLastError(), "trace_lambda_kernel launch");
 }
 
 size_t eps_workspace_size(int32_t d, int32_t d_out, int32_t batch) {

@@ -24,7 +24,9 @@ EXPORTS = [
     "ispa_decomp_attn", "ispa_decomp_attn_segments", "ispa_decomp_attn_splitkv",
     "ispa_decomp_attn_splitkv_workspace_size", "ispa_decomp_attn_workspace_size", "ispa_full_attn", "ispa_lse_merge", "ispa_gram_workspace_size", "ispa_gram_accum",
     "ispa_absorb_workspace_size", "ispa_absorb_solve", "ispa_eps_workspace_size", "ispa_layer_eps",
-    "ispa_select_layers", "ispa_absorb_apply", "ispa_status_string", "ispa_last_error", "ispa_version", "ispa_device_check",
+    "ispa_select_layers", "ispa_absorb_apply", "ispa_fit_error", "ispa_fit_error_workspace_size",
+    "ispa_lambda_from_trace", "ispa_absorb_solve_lambdas", "ispa_select_layers_below", "ispa_gather_layers",
+    "ispa_absorb_apply_compact", "ispa_status_string", "ispa_last_error", "ispa_version", "ispa_device_check",
 ]
 
 
@@ -83,6 +85,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "ispa_layer_eps": (I32, [I32, I32, I32, P, P, P, P, P, F, P, P, P, SZ, P]),
         "ispa_select_layers": (I32, [I32, P, I32, P, P, P]),
         "ispa_absorb_apply": (I32, [I32, I32, I32, P, I32, P, P, P]),
+        "ispa_fit_error_workspace_size": (SZ, [I32, I32, I32]),
+        "ispa_fit_error": (I32, [I32, I32, I32, P, P, P, P, P, P, P, P, SZ, P]),
+        "ispa_lambda_from_trace": (I32, [I32, I32, P, F, P, P]),
+        "ispa_absorb_solve_lambdas": (I32, [I32, I32, I32, P, P, P, P, P, P, P, P, SZ, P]),
+        "ispa_select_layers_below": (I32, [I32, P, ctypes.c_double, I32, P, P, P, P]),
+        "ispa_gather_layers": (I32, [I32, I64, P, P, I32, P, P]),
+        "ispa_absorb_apply_compact": (I32, [I32, I32, I32, P, I32, P, P, P]),
         "ispa_status_string": (ctypes.c_char_p, [I32]),
         "ispa_last_error": (ctypes.c_char_p, []),
         "ispa_version": (I32, []),
@@ -355,6 +364,93 @@ def ispa_absorb_apply(selected, dW, W, *, stream=None) -> None:
     _expect(selected.reshape(-1), (k,), torch.int32, "selected")
     lib = load_library()
     _check(lib.ispa_absorb_apply(d, d_out, n, _ptr(selected), k, _ptr(dW), _ptr(W), _stream(stream)))
+
+
+def _as3(t):
+    return t if t.dim() == 3 else t[None]
+
+
+def ispa_fit_error_workspace_size(d: int, d_out: int, batch: int) -> int:
+    return int(load_library().ispa_fit_error_workspace_size(d, d_out, batch))
+
+
+def ispa_fit_error(G, C, Q_ff, W, dW, eps_abs, eps_rel, *, workspace=None, stream=None) -> None:
+    """||A_loc (W + dW) - A_full W||^2 over the rows summarised by (G, C, Q_ff), any dW (None: dW = 0)."""
+    G3, W3 = _as3(G), _as3(W)
+    b, d, _ = G3.shape
+    d_out = W3.shape[2]
+    for t, nm in ((G, "G"), (C, "C"), (Q_ff, "Q_ff")):
+        _expect(_as3(t), (b, d, d), torch.float32, nm)
+    _expect(W3, (b, d, d_out), torch.float32, "W")
+    if dW is not None:
+        _expect(_as3(dW), (b, d, d_out), torch.float32, "dW")
+    _expect(eps_abs.reshape(-1), (b,), torch.float64, "eps_abs")
+    _expect(eps_rel.reshape(-1), (b,), torch.float64, "eps_rel")
+    lib = load_library()
+    if workspace is None:
+        workspace = _workspace(int(lib.ispa_fit_error_workspace_size(d, d_out, b)), G.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.ispa_fit_error(d, d_out, b, _ptr(G), _ptr(C), _ptr(Q_ff), _ptr(W), _ptr(dW), _ptr(eps_abs),
+                              _ptr(eps_rel), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def ispa_lambda_from_trace(G, lam_scale: float, lambdas, *, stream=None) -> None:
+    """lambdas[b] = lam_scale * tr(G_b) / d (float32 [batch])."""
+    G3 = _as3(G)
+    b, d, _ = G3.shape
+    _expect(G3, (b, d, d), torch.float32, "G")
+    _expect(lambdas.reshape(-1), (b,), torch.float32, "lambdas")
+    _check(load_library().ispa_lambda_from_trace(d, b, _ptr(G), float(lam_scale), _ptr(lambdas), _stream(stream)))
+
+
+def ispa_absorb_solve_lambdas(G, C, W, lambdas, dW, info, *, W_new=None, workspace=None, stream=None) -> None:
+    """ispa_absorb_solve with a per-layer lambda (device float32 [batch])."""
+    G3, W3 = _as3(G), _as3(W)
+    b, d, _ = G3.shape
+    d_out = W3.shape[2]
+    _expect(G3, (b, d, d), torch.float32, "G")
+    _expect(_as3(C), (b, d, d), torch.float32, "C")
+    _expect(W3, (b, d, d_out), torch.float32, "W")
+    _expect(_as3(dW), (b, d, d_out), torch.float32, "dW")
+    if W_new is not None:
+        _expect(_as3(W_new), (b, d, d_out), torch.float32, "W_new")
+    _expect(lambdas.reshape(-1), (b,), torch.float32, "lambdas")
+    _expect(info.reshape(-1), (b,), torch.int32, "info")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().ispa_absorb_solve_lambdas(d, d_out, b, _ptr(G), _ptr(C), _ptr(W), _ptr(lambdas), _ptr(dW),
+                                                    _ptr(W_new), _ptr(info), _ptr(workspace), ws_bytes,
+                                                    _stream(stream)))
+
+
+def ispa_select_layers_below(eps, tau: float, k_max: int, selected, count, rank=None, *, stream=None) -> None:
+    """The layers with eps <= tau, lowest first, at most k_max; count[0] = how many."""
+    n = eps.numel()
+    _expect(eps.reshape(-1), (n,), torch.float64, "eps")
+    _expect(selected.reshape(-1), (k_max,), torch.int32, "selected")
+    _expect(count.reshape(-1), (1,), torch.int32, "count")
+    if rank is not None:
+        _expect(rank.reshape(-1), (n,), torch.int32, "rank")
+    _check(load_library().ispa_select_layers_below(n, _ptr(eps), float(tau), int(k_max), _ptr(selected), _ptr(count),
+                                                   _ptr(rank), _stream(stream)))
+
+
+def ispa_gather_layers(src, selected, dst, *, stream=None) -> None:
+    """dst[s] = src[selected[s]]; src [n_layers, ...], dst [k, ...] float32."""
+    n = src.shape[0]
+    k = selected.numel()
+    per = src[0].numel() if n else 0
+    _expect(src.reshape(n, -1), (n, per), torch.float32, "src")
+    _expect(dst.reshape(k, -1) if k else dst, (k, per) if k else tuple(dst.shape), torch.float32, "dst")
+    _check(load_library().ispa_gather_layers(n, per, _ptr(src), _ptr(selected), k, _ptr(dst), _stream(stream)))
+
+
+def ispa_absorb_apply_compact(selected, dW, W, *, stream=None) -> None:
+    """W[selected[s]] += dW[s]; W [n_layers, d, d_out], dW [k, d, d_out] float32."""
+    n, d, d_out = W.shape
+    k = selected.numel()
+    _expect(dW, (k, d, d_out), torch.float32, "dW")
+    _check(load_library().ispa_absorb_apply_compact(d, d_out, n, _ptr(selected), k, _ptr(dW), _ptr(W),
+                                                    _stream(stream)))
 
 
 def ispa_version() -> int:

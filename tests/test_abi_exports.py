@@ -147,3 +147,23 @@ def test_splitkv_validation_needs_no_gpu():
     d0 = ispa.AttnDesc(2, 128, 100, 50, 0, 0.1, 1)
     assert lib.ispa_decomp_attn_splitkv_workspace_size(ctypes.byref(d0), 7) == 7 * slot
     assert lib.ispa_decomp_attn_splitkv_workspace_size(ctypes.byref(d), -3) == 0
+
+
+@pytest.mark.skipif(not os.path.exists(ispa.LIB_PATH), reason="libispa.so not built")
+def test_variant_validation_needs_no_gpu():
+    lib = ispa.load_library()
+    ok = 0x10000
+    bad = ispa.ISPA_E_INVALID_ARG
+    assert lib.ispa_fit_error(100, 64, 1, ok, ok, ok, ok, None, ok, ok, None, 0, None) == bad  # d % 64
+    assert lib.ispa_fit_error(128, 64, 1, ok, ok, None, ok, None, ok, ok, None, 0, None) == bad  # Q_ff required
+    assert lib.ispa_fit_error_workspace_size(128, 64, 3) == 4 * 3 * 128 * 64 * 4
+    assert lib.ispa_lambda_from_trace(128, 2, ok, -1.0, ok, None) == bad
+    assert lib.ispa_lambda_from_trace(128, 0, ok, 1.0, ok, None) == bad
+    assert lib.ispa_absorb_solve_lambdas(128, 64, 1, ok, ok, ok, None, ok, None, ok, None, 0, None) == bad
+    assert lib.ispa_select_layers_below(30, ok, 0.5, 31, ok, ok, None, None) == bad  # k_max > n_layers
+    assert lib.ispa_select_layers_below(30, ok, float("nan"), 3, ok, ok, None, None) == bad
+    assert lib.ispa_select_layers_below(30, ok, 0.5, 3, ok, None, None, None) == bad  # count required
+    assert lib.ispa_gather_layers(4, 0, ok, ok, 2, ok, None) == bad
+    assert lib.ispa_gather_layers(4, 16, ok, ok, 0, None, None) == ispa.ISPA_OK  # nothing to gather
+    assert lib.ispa_absorb_apply_compact(128, 64, 4, ok, 5, ok, ok, None) == bad
+    assert lib.ispa_absorb_apply_compact(128, 64, 4, None, 0, None, None, None) == ispa.ISPA_OK
