@@ -21,11 +21,13 @@ Every function computes the plain definition of its quantity (the method reaches
 these exact results, up to rounding order), in float64, with numpy/LAPACK
 primitives and no blocking or reordering beyond the definition.
 """
+from . import fp8
 from .softmax_attention import attention, branch_outputs, merge
 from .ridge_absorb import (gram, gram_from_chunks, ridge_solve, objective, reconstruction_error, select_layers,
                            select_below, trace_scaled_lambda)
 
 __all__ = [
+    "fp8",
     "attention",
     "branch_outputs",
     "merge",

@@ -10,7 +10,9 @@ import pytest
 import oracle
 import oracle.ridge_absorb as oabs
 import oracle.softmax_attention as oatt
+import oracle.fp8 as ofp8
 from tests import test_oracle_absorb as PA
+from tests import test_oracle_fp8 as PF
 from tests import test_oracle_attention as PT
 
 _attn = oatt.attention
@@ -18,6 +20,8 @@ _merge = oatt.merge
 _gram = oabs.gram
 _solve = oabs.ridge_solve
 _eps = oabs.reconstruction_error
+_enc = ofp8.e4m3_encode
+_scale = ofp8.absmax_scale
 _tlam = oabs.trace_scaled_lambda
 _below = oabs.select_below
 
@@ -127,6 +131,43 @@ BELOW_MUTANTS = {
 }
 
 
+def _fp8_pins():
+    return [PF.test_hand_values, PF.test_matches_torch_cast, PF.test_every_finite_code_round_trips,
+            PF.test_nearest_and_ties_to_even, PF.test_per_head_scale_maps_amax_to_448,
+            PF.test_w8a8_matmul_exact_and_bounded]
+
+
+ENC_MUTANTS = {
+    "ties away from zero": lambda x: np.where(
+        np.abs(ofp8.e4m3_decode(_enc(x)) - np.asarray(x, np.float64)) > 0,
+        _enc(np.nextafter(np.asarray(x, np.float32), np.float32(np.inf) * np.sign(np.asarray(x, np.float32)))),
+        _enc(x)).astype(np.uint8),
+    "subnormals flushed": lambda x: np.where(np.abs(np.asarray(x, np.float32)) < 2.0 ** -6,
+                                             (np.signbit(np.asarray(x, np.float32)) * 0x80).astype(np.uint8),
+                                             _enc(x)).astype(np.uint8),
+    "truncation": lambda x: _enc(np.asarray(x, np.float32) * np.float32(1 - 2.0 ** -5)),
+}
+
+SCALE_MUTANTS = {
+    "amax / 256": lambda x, axis=None: (_scale(x, axis) * np.float32(448.0 / 256.0)).astype(np.float32),
+    "amax / 448 in float64": lambda x, axis=None: np.where(
+        np.max(np.abs(np.asarray(x, np.float64)), axis=axis) > 0,
+        np.max(np.abs(np.asarray(x, np.float64)), axis=axis) / 448.0 * (1 + 1e-7), 1.0),
+}
+
+
+@pytest.mark.parametrize("name", ENC_MUTANTS)
+def test_fp8_encode_mutant_caught(name, monkeypatch):
+    monkeypatch.setattr(ofp8, "e4m3_encode", ENC_MUTANTS[name])
+    assert _some_pin_fails(_fp8_pins()), name
+
+
+@pytest.mark.parametrize("name", SCALE_MUTANTS)
+def test_fp8_scale_mutant_caught(name, monkeypatch):
+    monkeypatch.setattr(ofp8, "absmax_scale", SCALE_MUTANTS[name])
+    assert _some_pin_fails(_fp8_pins()), name
+
+
 @pytest.mark.parametrize("name", TLAM_MUTANTS)
 def test_trace_lambda_mutant_caught(name, monkeypatch):
     monkeypatch.setattr(oracle, "trace_scaled_lambda", TLAM_MUTANTS[name])
@@ -173,3 +214,4 @@ def test_unmutated_oracle_passes_every_pin():
     assert not _some_pin_fails(_attn_pins())
     assert not _some_pin_fails(_absorb_pins())
     assert not _some_pin_fails(_variant_pins())
+    assert not _some_pin_fails(_fp8_pins())
