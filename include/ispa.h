@@ -18,6 +18,8 @@
  *   ispa_layer_eps     the post-fit reconstruction error used to rank layers,
  *   ispa_select_layers the k lowest-error layers (those converted),
  *   ispa_absorb_apply  W += dW for the converted layers,
+ *   ispa_decomp_attn_fp8k, ispa_quantize_fp8_*, ispa_w8a8_gemm
+ *                      fp8 keys / queries and the W8A8 projection,
  *   ispa_fit_error, ispa_lambda_from_trace, ispa_absorb_solve_lambdas,
  *   ispa_select_layers_below, ispa_gather_layers, ispa_absorb_apply_compact
  *                      selection and lambda variants (error before the fit or
@@ -320,6 +322,80 @@ ispa_status_t ispa_select_layers(int32_t n_layers, const double* eps, int32_t k,
  */
 ispa_status_t ispa_absorb_apply(int32_t d, int32_t d_out, int32_t n_layers, const int32_t* selected,
                                 int32_t k, const float* dW, float* W, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * fp8 (E4M3) variants.  Source: ISPA technical summary, section 4 "Results"
+ * (ISPA combined with W8A8 post-training quantisation).  The pages fix no
+ * format or scaling.  Reading: E4M3 with the OCP "FN" encoding (bias 7, max
+ * 448, no infinities); one absmax scale per block, scale = amax / 448 in
+ * float32 (1 when amax = 0); code = x / scale (float32 division) clamped to
+ * +-448 and rounded to nearest, ties to even.  Codes are uint8.
+ * ------------------------------------------------------------------------- */
+
+/* Workspace bytes of ispa_quantize_fp8_heads: ceil(n_rows / 256) * heads floats. */
+size_t ispa_quantize_fp8_heads_workspace_size(int64_t n_rows, int32_t heads);
+
+/*
+ * ispa_quantize_fp8_heads — X [n_rows, heads, head_dim] (dtype BF16 or F32)
+ * to codes X8 (same layout, uint8) with one scale per head over all its rows
+ * and dims: scale [heads] float32 DEVICE.  For Q and K of
+ * ispa_decomp_attn_fp8k.  head_dim 64 or 128; workspace required.
+ */
+ispa_status_t ispa_quantize_fp8_heads(int64_t n_rows, int32_t heads, int32_t head_dim, int32_t dtype, const void* X,
+                                      uint8_t* X8, float* scale, void* workspace, size_t workspace_bytes,
+                                      void* stream);
+
+/*
+ * ispa_quantize_fp8_rows — X [n_rows, d] (BF16 or F32) to codes X8 [n_rows, d]
+ * with one scale per row (token): scale [n_rows] float32 DEVICE.  The
+ * activation side of ispa_w8a8_gemm.  d a positive multiple of 4.
+ */
+ispa_status_t ispa_quantize_fp8_rows(int64_t n_rows, int32_t d, int32_t dtype, const void* X, uint8_t* X8,
+                                     float* scale, void* stream);
+
+/*
+ * ispa_quantize_fp8_cols — W [d, d_out] float32 to codes with one scale per
+ * output column: scale [d_out] float32, codes written TRANSPOSED as
+ * W8T [d_out, d] (each column's d codes contiguous, the operand layout of
+ * ispa_w8a8_gemm).  d a positive multiple of 4.
+ */
+ispa_status_t ispa_quantize_fp8_cols(int32_t d, int32_t d_out, const float* W, uint8_t* W8T, float* scale,
+                                     void* stream);
+
+/*
+ * ispa_w8a8_gemm — Y = (A8 W8) * a_scale[row] * w_scale[col] as bf16 [n, d_out]:
+ * the W8A8 output projection of an absorbed layer (A = its attention output,
+ * W = its W_new).  A8 [n, d] codes per row (ispa_quantize_fp8_rows), W8T
+ * [d_out, d] codes per column (ispa_quantize_fp8_cols); products of codes
+ * accumulate in float32 on gfx950 fp8 matrix cores.  d a multiple of 64,
+ * d_out a multiple of 128, operands below 2^32 bytes.
+ */
+ispa_status_t ispa_w8a8_gemm(int64_t n, int32_t d, int32_t d_out, const uint8_t* A8, const float* a_scale,
+                             const uint8_t* W8T, const float* w_scale, void* Y, void* stream);
+
+/* One run of fp8 keys and their values: K8 [n_rows, H, D] codes with scale
+ * k_scale [H] (DEVICE, as ispa_quantize_fp8_heads writes it), V [n_rows, H, D]
+ * bf16. */
+typedef struct {
+  const void* K8;
+  const float* k_scale;
+  const void* V;
+  int64_t n_rows; /* >= 1 */
+} ispa_kv_segment_fp8k_t;
+
+/*
+ * ispa_decomp_attn_fp8k — ispa_decomp_attn_segments with fp8 queries and
+ * keys: scores scale * (q_scale[h] q8) . (k_scale[h] k8) from codes Q8
+ * [n_q, H, D] (scale q_scale [H] DEVICE) and per-segment K8; S = K Q^T runs
+ * on the fp8 matrix cores (twice the bf16 rate), the softmax, P V and the
+ * merge as in the bf16 path, V and the outputs bf16.  A K cache held as codes
+ * takes half the K bytes.  desc->dtype must be ISPA_BF16; everything else as
+ * ispa_decomp_attn_segments (same workspace).
+ */
+ispa_status_t ispa_decomp_attn_fp8k(const ispa_attn_desc_t* desc, const void* Q8, const float* q_scale,
+                                    const ispa_kv_segment_fp8k_t* segs, int32_t n_segs, int32_t n_loc_segs,
+                                    void* O_loc, float* LSE_loc, void* O_hist, float* LSE_hist, void* O_full,
+                                    float* LSE_full, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Selection and lambda variants.  The pages leave the error measure, the ridge

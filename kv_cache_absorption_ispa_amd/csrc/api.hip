@@ -216,6 +216,117 @@ ispa_status_t ispa_decomp_attn_segments(const ispa_attn_desc_t* desc, const void
                     stream);
 }
 
+ispa_status_t ispa_decomp_attn_fp8k(const ispa_attn_desc_t* desc, const void* Q8, const float* q_scale,
+                                    const ispa_kv_segment_fp8k_t* segs, int32_t n_segs, int32_t n_loc_segs,
+                                    void* O_loc, float* LSE_loc, void* O_hist, float* LSE_hist, void* O_full,
+                                    float* LSE_full, void* workspace, size_t workspace_bytes, void* stream) {
+  ispa_status_t st = check_attn_desc(desc, true);
+  if (st != ISPA_OK) return st;
+  if (desc->dtype != ISPA_BF16) return invalid("fp8-key attention: desc->dtype (V and outputs) must be ISPA_BF16");
+  if (segs == nullptr) return invalid("segs is NULL");
+  if (n_segs < 1 || n_segs > ISPA_MAX_KV_SEGMENTS) return invalid("n_segs must be in [1, ISPA_MAX_KV_SEGMENTS]");
+  if (n_loc_segs < 1 || n_loc_segs > n_segs) return invalid("n_loc_segs must be in [1, n_segs]");
+  if ((desc->n_q > 0 && !req(Q8)) || !req(q_scale)) return invalid("Q8, q_scale must be non-NULL and 16-byte aligned");
+  KvSegments kv = {};
+  const float* ks[MAX_KV_SEGS] = {};
+  int64_t sum_loc = 0, sum_hist = 0;
+  for (int i = 0; i < n_segs; ++i) {
+    if (segs[i].n_rows < 1) return invalid("every segment needs n_rows >= 1");
+    if (!req(segs[i].K8) || !req(segs[i].V) || !req(segs[i].k_scale))
+      return invalid("segment K8, V, k_scale must be non-NULL and 16-byte aligned");
+    (i < n_loc_segs ? sum_loc : sum_hist) += segs[i].n_rows;
+    kv.K[i] = segs[i].K8;
+    kv.V[i] = segs[i].V;
+    kv.n[i] = segs[i].n_rows;
+    ks[i] = segs[i].k_scale;
+  }
+  if (sum_loc != desc->n_loc || sum_hist != desc->n_hist)
+    return invalid("segment rows must add up to desc->n_loc (local) and desc->n_hist (history)");
+  kv.n_seg = n_segs;
+  kv.n_loc_seg = n_loc_segs;
+  st = check_decomp_outputs(desc, O_loc, LSE_loc, O_hist, LSE_hist, O_full, LSE_full, workspace, workspace_bytes);
+  if (st != ISPA_OK) return st;
+  st = check_current_device();
+  if (st != ISPA_OK) return st;
+  AttnArgs a = {};
+  a.Q = Q8;
+  a.kv = kv;
+  a.O_loc = O_loc;
+  a.LSE_loc = LSE_loc;
+  a.O_hist = O_hist;
+  a.LSE_hist = LSE_hist;
+  a.O_full = O_full;
+  a.LSE_full = LSE_full;
+  a.n_q = desc->n_q;
+  a.n_loc = desc->n_loc;
+  a.n_hist = desc->n_hist;
+  a.heads = desc->heads;
+  a.head_dim = desc->head_dim;
+  a.scale = desc->scale;
+  a.dtype = ISPA_BF16;
+  a.ws = workspace;
+  a.ws_bytes = workspace_bytes;
+  a.k_fp8 = 1;
+  a.q_scale = q_scale;
+  for (int i = 0; i < n_segs; ++i) a.k_scale[i] = ks[i];
+  return launch_attention(a, (hipStream_t)stream);
+}
+
+size_t ispa_quantize_fp8_heads_workspace_size(int64_t n_rows, int32_t heads) {
+  if (n_rows < 0 || heads < 1) return 0;
+  return quant_head_workspace_size(n_rows, heads);
+}
+
+ispa_status_t ispa_quantize_fp8_heads(int64_t n_rows, int32_t heads, int32_t head_dim, int32_t dtype, const void* X,
+                                      uint8_t* X8, float* scale, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  if (n_rows < 0 || heads < 1 || heads > 65535 || (head_dim != 64 && head_dim != 128))
+    return invalid("need n_rows >= 0, heads in [1, 65535], head_dim 64 or 128");
+  if (dtype != ISPA_F32 && dtype != ISPA_BF16) return invalid("dtype must be ISPA_F32 or ISPA_BF16");
+  if ((n_rows > 0 && (!req(X) || !req(X8))) || !req(scale)) return invalid("X, X8, scale must be non-NULL and 16-byte aligned");
+  if (!req(workspace) || workspace_bytes < quant_head_workspace_size(n_rows, heads)) {
+    set_error("ispa_quantize_fp8_heads: workspace smaller than ispa_quantize_fp8_heads_workspace_size()");
+    return ISPA_E_WORKSPACE;
+  }
+  ispa_status_t st = check_current_device();
+  if (st != ISPA_OK) return st;
+  return launch_quant_head(n_rows, heads, head_dim, dtype, X, X8, scale, workspace, (hipStream_t)stream);
+}
+
+ispa_status_t ispa_quantize_fp8_rows(int64_t n_rows, int32_t d, int32_t dtype, const void* X, uint8_t* X8, float* scale,
+                                     void* stream) {
+  if (n_rows < 0 || d < 4 || d % 4 != 0) return invalid("need n_rows >= 0 and d a positive multiple of 4");
+  if (dtype != ISPA_F32 && dtype != ISPA_BF16) return invalid("dtype must be ISPA_F32 or ISPA_BF16");
+  if (n_rows > 0 && (!req(X) || !req(X8) || !req(scale))) return invalid("X, X8, scale must be non-NULL and 16-byte aligned");
+  if (n_rows == 0) return ISPA_OK;
+  ispa_status_t st = check_current_device();
+  if (st != ISPA_OK) return st;
+  return launch_quant_rows(n_rows, d, dtype, X, X8, scale, (hipStream_t)stream);
+}
+
+ispa_status_t ispa_quantize_fp8_cols(int32_t d, int32_t d_out, const float* W, uint8_t* W8T, float* scale,
+                                     void* stream) {
+  if (d < 4 || d % 4 != 0 || d_out < 1) return invalid("need d a positive multiple of 4 and d_out >= 1");
+  if (!req(W) || !req(W8T) || !req(scale)) return invalid("W, W8T, scale must be non-NULL and 16-byte aligned");
+  ispa_status_t st = check_current_device();
+  if (st != ISPA_OK) return st;
+  return launch_quant_cols(d, d_out, W, W8T, scale, (hipStream_t)stream);
+}
+
+ispa_status_t ispa_w8a8_gemm(int64_t n, int32_t d, int32_t d_out, const uint8_t* A8, const float* a_scale,
+                             const uint8_t* W8T, const float* w_scale, void* Y, void* stream) {
+  if (n < 0 || d < 64 || d % 64 != 0 || d_out < 128 || d_out % 128 != 0)
+    return invalid("need n >= 0, d a multiple of 64, d_out a multiple of 128");
+  if (n * (int64_t)d >= ((int64_t)1 << 32) || (int64_t)d_out * d >= ((int64_t)1 << 32) || n >= ((int64_t)1 << 31))
+    return invalid("operands too large (2^32 bytes each)");
+  if (n > 0 && (!req(A8) || !req(a_scale) || !req(W8T) || !req(w_scale) || !req(Y)))
+    return invalid("A8, a_scale, W8T, w_scale, Y must be non-NULL and 16-byte aligned");
+  if (n == 0) return ISPA_OK;
+  ispa_status_t st = check_current_device();
+  if (st != ISPA_OK) return st;
+  return launch_w8a8_gemm(n, d_out, d, A8, a_scale, W8T, w_scale, (uint16_t*)Y, (hipStream_t)stream);
+}
+
 size_t ispa_decomp_attn_splitkv_workspace_size(const ispa_attn_desc_t* desc, int32_t n_workers) {
   if (desc == nullptr || desc->n_q < 0 || desc->heads < 1 || desc->n_hist < 0 || n_workers < 0 ||
       n_workers > ISPA_MAX_SPLITKV_WORKERS || (desc->head_dim != 64 && desc->head_dim != 128))

@@ -63,6 +63,10 @@ struct AttnKParams {
   // which leaves its branch states in partial slot u * sk_p + i
   int sk_p;
   float* part;
+  // fp8 keys (KF8 kernels): Q and the K segments hold E4M3 codes, score scale per head and segment
+  // c2 * q_scale[head] * k_scale[segment][head]
+  const float* q_scale;
+  const float* k_scale[MAX_KV_SEGS];
 };
 
 // Split-mode schedule.  Workgroup b runs on XCD b % 8 (round-robin dispatch).  The units are
@@ -116,6 +120,14 @@ __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return __b
 // puts the 16 rows of a K pass on 16 different slots, and the 4 rows of a V
 // pass on 4 different groups of 4 slots, so both read patterns are
 // conflict-free.  (D = 64: rows are 128 bytes, two rows per bank cycle.)
+// fp8 K rows (D bytes): slot of 16-byte chunk c of row r is c ^ kf8_swizzle<D>(r); the 16 rows of a
+// read pass (one chunk each) then cover all 64 banks.
+template <int D>
+__device__ __forceinline__ int kf8_swizzle(int r) {
+  if constexpr (D == 128) return (r >> 1) & 7;
+  else return (r >> 2) & 3;
+}
+
 template <int D>
 __device__ __forceinline__ int kv_swizzle(int r) {
   if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
@@ -133,16 +145,25 @@ __device__ __forceinline__ int kv_swizzle(int r) {
 // SK = split mode: the grid is a fixed set of workgroups (one per CU) that
 // share the units' tiles evenly, so no CU idles when the units do not fill the
 // last round; pieces of split units are merged afterwards (sk_fixup_kernel).
-template <int D, int NW, int QB, int BN, bool SK>
+//
+// KF8 = fp8 keys: Q and K are E4M3 codes and S^T = K Q^T runs on
+// v_mfma_f32_32x32x64_f8f6f4 (twice the bf16 rate, half the K bytes); the
+// softmax, P and V stay as in the bf16 kernel.
+template <int D, int NW, int QB, int BN, bool SK, bool KF8 = false>
 __global__ __launch_bounds__(NW * 64, (QB == 1 && NW <= 4) ? 2 : 1) void attn_bf16_kernel(AttnKParams p) {
-  constexpr int KK = D / 16;  // MFMA k-steps of S^T
-  constexpr int DB = D / 32;  // 32-row blocks of O^T
+  constexpr int KK = KF8 ? D / 64 : D / 16;  // MFMA k-steps of S^T
+  constexpr int DB = D / 32;                  // 32-row blocks of O^T
   constexpr int NKB = BN / 32;
-  constexpr int CPR = D / 8;         // 16-byte chunks per row
-  constexpr int RPW = 64 / CPR;      // rows per wave load (1 KB)
-  constexpr int WLT = BN / RPW;      // wave loads per matrix tile
-  constexpr int WLW = 2 * WLT / NW;  // wave loads per wave per tile (K and V)
-  static_assert(WLW * NW == 2 * WLT, "tile loads must split evenly over the waves");
+  constexpr int CPR = D / 8;                  // 16-byte chunks per V row
+  constexpr int RPW = 64 / CPR;               // V rows per wave load (1 KB)
+  constexpr int WLT = BN / RPW;               // wave loads per V tile
+  constexpr int KRB = KF8 ? D : 2 * D;        // bytes per K row in LDS
+  constexpr int CPRK = KRB / 16;              // 16-byte chunks per K row
+  constexpr int RPWK = 64 / CPRK;             // K rows per wave load
+  constexpr int WLTK = BN / RPWK;             // wave loads per K tile
+  constexpr int WLW = (WLTK + WLT) / NW;      // wave loads per wave per tile (K and V)
+  static_assert(WLW * NW == WLTK + WLT, "tile loads must split evenly over the waves");
+  using QFrag = typename std::conditional<KF8, v8i_t, bf16x8>::type;
   constexpr int BM = NW * 32 * QB;
   // The running max used as the exponent reference is raised only when a new
   // score exceeds it by more than 2^8: p then stays below 2^8, and the
@@ -163,8 +184,8 @@ __global__ __launch_bounds__(NW * 64, (QB == 1 && NW <= 4) ? 2 : 1) void attn_bf
   const int l32 = lane & 31, hh = lane >> 5;
   const int n_q = p.n_q;
   const uint32_t HD = (uint32_t)p.heads * D;
-  const uint32_t row_bytes = HD * 2u;
-  const float c2 = p.c2;
+  const uint32_t row_bytes = HD * 2u;            // V (and bf16 K) row in memory
+  const uint32_t krow_bytes = KF8 ? HD : HD * 2u;  // K row in memory
   const int Tl = p.st0[p.n_loc_seg];  // local tiles, then history tiles
   const int T = p.st0[p.n_seg];
   const int Th = T - Tl;
@@ -181,7 +202,9 @@ __global__ __launch_bounds__(NW * 64, (QB == 1 && NW <= 4) ? 2 : 1) void attn_bf
     int sg, tt, nt, n;
     const uint16_t* kb;
     const uint16_t* vb;
+    float c2;  // score scale of the segment (log2 domain)
   };
+  const float c2h = KF8 ? p.c2 * p.q_scale[head] : p.c2;
   auto cur_at = [&](int sg) {
     Cur c;
     c.sg = sg;
@@ -190,6 +213,7 @@ __global__ __launch_bounds__(NW * 64, (QB == 1 && NW <= 4) ? 2 : 1) void attn_bf
     c.nt = (c.n + BN - 1) / BN;
     c.kb = p.Ks[sg];
     c.vb = p.Vs[sg];
+    c.c2 = KF8 ? c2h * p.k_scale[sg][head] : c2h;
     return c;
   };
   auto cur_next = [&](Cur& c) {
@@ -210,41 +234,59 @@ __global__ __launch_bounds__(NW * 64, (QB == 1 && NW <= 4) ? 2 : 1) void attn_bf
     qvalid[qb] = myq[qb] < n_q;
   }
 
-  // Q^T fragments (B operand of S^T = K Q^T): lane holds q[myq][16kk + 8hh .. +7].
-  bf16x8 qf[QB][KK];
+  // Q^T fragments (B operand of S^T = K Q^T).  bf16: lane holds q[myq][16kk + 8hh .. +7];
+  // fp8: codes q[myq][64kk + 32hh .. +31] (K fragments use the same dims, so the k order matches).
+  QFrag qf[QB][KK];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const uint16_t* qp = p.Q + (size_t)(qvalid[qb] ? myq[qb] : 0) * HD + head * D + 8 * hh;
+    if constexpr (KF8) {
+      const uint8_t* qp = (const uint8_t*)p.Q + (size_t)(qvalid[qb] ? myq[qb] : 0) * HD + head * D + 32 * hh;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const u32x4 v = qvalid[qb] ? *(const u32x4*)(qp + 16 * kk) : u32x4{0, 0, 0, 0};
-      qf[qb][kk] = __builtin_bit_cast(bf16x8, v);
+      for (int kk = 0; kk < KK; ++kk) {
+        const u32x4 a = qvalid[qb] ? *(const u32x4*)(qp + 64 * kk) : u32x4{0, 0, 0, 0};
+        const u32x4 b = qvalid[qb] ? *(const u32x4*)(qp + 64 * kk + 16) : u32x4{0, 0, 0, 0};
+        qf[qb][kk] = v8i_t{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+      }
+    } else {
+      const uint16_t* qp = p.Q + (size_t)(qvalid[qb] ? myq[qb] : 0) * HD + head * D + 8 * hh;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const u32x4 v = qvalid[qb] ? *(const u32x4*)(qp + 16 * kk) : u32x4{0, 0, 0, 0};
+        qf[qb][kk] = __builtin_bit_cast(bf16x8, v);
+      }
     }
   }
 
   // This wave's tile loads: load j is wave load g = wave + j*NW of the tile (K loads first, then V).
-  // Lane i fills row r0 + i/CPR, slot i%CPR, with the row's chunk slot ^ kv_swizzle(row).
+  // Lane i fills row r0 + i/CPR(K), slot i%CPR(K), with the row's chunk slot ^ swizzle(row).
   uint32_t gofs[WLW];
 #pragma unroll
   for (int j = 0; j < WLW; ++j) {
     const int g = wave + j * NW;
-    const int row = (g % WLT) * RPW + lane / CPR;
-    const int chunk = (lane % CPR) ^ kv_swizzle<D>(row);
-    gofs[j] = (uint32_t)row * row_bytes + (uint32_t)(head * D + chunk * 8) * 2u;
+    if (g < WLTK) {
+      const int row = g * RPWK + lane / CPRK;
+      const int chunk = (lane % CPRK) ^ (KF8 ? kf8_swizzle<D>(row) : kv_swizzle<D>(row));
+      gofs[j] = (uint32_t)row * krow_bytes + (uint32_t)(head * D) * (KF8 ? 1u : 2u) + chunk * 16u;
+    } else {
+      const int row = (g - WLTK) * RPW + lane / CPR;
+      const int chunk = (lane % CPR) ^ kv_swizzle<D>(row);
+      gofs[j] = (uint32_t)row * row_bytes + (uint32_t)(head * D + chunk * 8) * 2u;
+    }
   }
 
   auto load_tile = [&](uint16_t* sKb, uint16_t* sVb) {
+    const uint32_t tbk = (uint32_t)(lcur.tt * BN) * krow_bytes;
     const uint32_t tb = (uint32_t)(lcur.tt * BN) * row_bytes;
-    const rsrc_t rk = make_rsrc(lcur.kb, (uint32_t)lcur.n * row_bytes);
+    const rsrc_t rk = make_rsrc(lcur.kb, (uint32_t)lcur.n * krow_bytes);
     const rsrc_t rv = make_rsrc(lcur.vb, (uint32_t)lcur.n * row_bytes);
     cur_next(lcur);
 #pragma unroll
     for (int j = 0; j < WLW; ++j) {
       const int g = wave + j * NW;
-      if (g < WLT)
-        load_to_lds(rk, sKb + (g % WLT) * RPW * D, gofs[j] + tb);
+      if (g < WLTK)
+        load_to_lds(rk, (uint16_t*)((uint8_t*)sKb + g * RPWK * KRB), gofs[j] + tbk);
       else
-        load_to_lds(rv, sVb + (g % WLT) * RPW * D, gofs[j] + tb);
+        load_to_lds(rv, sVb + (g - WLTK) * RPW * D, gofs[j] + tb);
     }
   };
 
@@ -263,12 +305,20 @@ __global__ __launch_bounds__(NW * 64, (QB == 1 && NW <= 4) ? 2 : 1) void attn_bf
   // (sched_barrier keeps the compiler from sinking them next to their use).
   constexpr int NS = NKB * KK;      // K fragments per tile: (kb, kk), chains of the NKB accumulators interleaved
   constexpr int NV = DB * NKB * 2;  // V fragments per tile: (db, kb, mm), DB accumulators interleaved
-  // K operand: row kb*32 + l32, chunk 2kk + hh (the swizzle depends on row & 15 == l32 & 15).
-  const int ksw = kv_swizzle<D>(l32);
+  // K operand: row kb*32 + l32; bf16: chunk 2kk + hh; fp8: chunks 4kk + 2hh and 4kk + 2hh + 1
+  // (the swizzles depend on row & 15 == l32 & 15).
+  const int ksw = KF8 ? kf8_swizzle<D>(l32) : kv_swizzle<D>(l32);
   auto kfrag = [&](const uint16_t* sKb, int i) {
     const int kb = i % NKB, kk = i / NKB;
     const int row = kb * 32 + l32;
-    return __builtin_bit_cast(bf16x8, *(const u32x4*)(&sKb[row * D + (((2 * kk + hh) ^ ksw) << 3)]));
+    if constexpr (KF8) {
+      const uint8_t* rp = (const uint8_t*)sKb + row * KRB;
+      const u32x4 a = *(const u32x4*)(rp + (((4 * kk + 2 * hh) ^ ksw) << 4));
+      const u32x4 b = *(const u32x4*)(rp + (((4 * kk + 2 * hh + 1) ^ ksw) << 4));
+      return v8i_t{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+    } else {
+      return __builtin_bit_cast(bf16x8, *(const u32x4*)(&sKb[row * D + (((2 * kk + hh) ^ ksw) << 3)]));
+    }
   };
   // V^T operand of O^T = V^T P^T for lane (dim 32db + lane%32, hh): keys 32kb + 16mm + 4hh + {0..3}
   // and + 8 + {0..3} (the key order of the P accumulator), read with two transposing loads.
@@ -290,13 +340,14 @@ __global__ __launch_bounds__(NW * 64, (QB == 1 && NW <= 4) ? 2 : 1) void attn_bf
   auto compute_tile = [&](const uint16_t* sKb, const uint16_t* sVb) {
     const int key0 = ccur.tt * BN;
     const int nvalid = ccur.n;
+    const float c2 = ccur.c2;
     cur_next(ccur);
     f32x16 s[QB][NKB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) s[qb][kb] = f32x16{0};
-    bf16x8 kf[3];
+    QFrag kf[3];
     kf[0] = kfrag(sKb, 0);
     kf[1] = kfrag(sKb, 1);
 #pragma unroll
@@ -305,8 +356,13 @@ __global__ __launch_bounds__(NW * 64, (QB == 1 && NW <= 4) ? 2 : 1) void attn_bf
       __builtin_amdgcn_sched_barrier(0);
       const int kb = i % NKB, kk = i / NKB;
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-        s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % 3], qf[qb][kk], s[qb][kb], 0, 0, 0);
+      for (int qb = 0; qb < QB; ++qb) {
+        if constexpr (KF8)
+          s[qb][kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf[i % 3], qf[qb][kk], s[qb][kb], 0, 0, 0, 0,
+                                                                      0, 0);
+        else
+          s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % 3], qf[qb][kk], s[qb][kb], 0, 0, 0);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     // the first V fragments do not depend on P: start reading them before the softmax
@@ -874,7 +930,8 @@ ispa_status_t launch_attention(const AttnArgs& a, hipStream_t s) {
       set_error("ispa_decomp_attn: workspace too small for the merge (query ispa_decomp_attn_workspace_size)");
       return ISPA_E_WORKSPACE;
     }
-    const AttnShape sh = attn_shape();
+    const AttnShape sh = a.k_fp8 ? AttnShape{8, 128} : attn_shape();
+    p.q_scale = a.q_scale;
     p.n_seg = a.kv.n_seg;
     p.n_loc_seg = a.kv.n_loc_seg;
     p.st0[0] = 0;
@@ -883,6 +940,7 @@ ispa_status_t launch_attention(const AttnArgs& a, hipStream_t s) {
       p.Ks[i] = used ? (const uint16_t*)a.kv.K[i] : nullptr;
       p.Vs[i] = used ? (const uint16_t*)a.kv.V[i] : nullptr;
       p.sn[i] = used ? (int)a.kv.n[i] : 0;
+      p.k_scale[i] = used ? a.k_scale[i] : nullptr;
       p.st0[i + 1] = p.st0[i] + (int)((p.sn[i] + sh.bn - 1) / sh.bn);
     }
     const int bm = sh.nw * 32;
@@ -890,6 +948,14 @@ ispa_status_t launch_attention(const AttnArgs& a, hipStream_t s) {
     p.nblocks = p.n_qtiles * a.heads;
     p.sk_p = 1;
     p.part = nullptr;
+    if (a.k_fp8) {
+      const dim3 grid(p.nblocks);
+      if (a.head_dim == 128)
+        hipLaunchKernelGGL((attn_bf16_kernel<128, 8, 1, 128, false, true>), grid, dim3(512), 0, s, p);
+      else
+        hipLaunchKernelGGL((attn_bf16_kernel<64, 8, 1, 128, false, true>), grid, dim3(512), 0, s, p);
+      return hip_check(hipGetLastError(), "attn_bf16_kernel (fp8 keys) launch");
+    }
     if (a.sk_workers <= 0) {
       const dim3 grid(p.nblocks);
       if (a.head_dim == 128)

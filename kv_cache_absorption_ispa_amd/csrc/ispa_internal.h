@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <string>
+#include <type_traits>
 
 #include "../../include/ispa.h"
 
@@ -18,6 +19,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int v8i_t __attribute__((ext_vector_type(8)));  // 32 fp8 codes: an operand of the f8f6f4 MFMA
 
 // ---------------------------------------------------------------- error state
 void set_error(const std::string& msg);
@@ -50,6 +52,9 @@ struct AttnArgs {
   void* ws;
   size_t ws_bytes;
   int32_t sk_workers;  // > 0: split mode with this many workgroups (bf16 only); 0: one workgroup per unit
+  int32_t k_fp8;       // 1: Q and K are E4M3 codes with the scales below (V and outputs bf16)
+  const float* q_scale;                 // [heads] device
+  const float* k_scale[MAX_KV_SEGS];    // per segment: [heads] device
 };
 size_t attention_workspace_size(int64_t n_q, int32_t heads, int32_t head_dim, int64_t n_hist, int32_t dtype);
 // Workspace of split mode: the merge's float32 O_loc (as above) and one partial slot per workgroup.
@@ -59,6 +64,16 @@ ispa_status_t launch_attention(const AttnArgs& a, hipStream_t s);
 ispa_status_t launch_lse_merge(int32_t n_parts, const void* const* O, const float* const* LSE, int64_t n_q,
                                int32_t heads, int32_t head_dim, int32_t dtype, void* O_out, float* LSE_out,
                                hipStream_t s);
+
+size_t quant_head_workspace_size(int64_t n, int32_t heads);
+ispa_status_t launch_quant_head(int64_t n, int32_t H, int32_t D, int32_t dtype, const void* X, uint8_t* X8,
+                                float* scale, void* ws, hipStream_t s);
+ispa_status_t launch_quant_rows(int64_t n, int32_t d, int32_t dtype, const void* X, uint8_t* X8, float* scale,
+                                hipStream_t s);
+ispa_status_t launch_quant_cols(int32_t d, int32_t d_out, const float* W, uint8_t* W8T, float* scale,
+                                hipStream_t s);
+ispa_status_t launch_w8a8_gemm(int64_t n, int32_t N, int32_t K, const uint8_t* A8, const float* sa,
+                               const uint8_t* W8T, const float* sw, uint16_t* Y, hipStream_t s);
 
 size_t gram_workspace_size(int64_t n_rows, int32_t d, int32_t dtype);
 ispa_status_t launch_gram(int64_t n_rows, int32_t d, int32_t dtype, const void* A_loc, const void* A_full,

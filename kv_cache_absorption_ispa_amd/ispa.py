@@ -26,7 +26,8 @@ EXPORTS = [
     "ispa_absorb_workspace_size", "ispa_absorb_solve", "ispa_eps_workspace_size", "ispa_layer_eps",
     "ispa_select_layers", "ispa_absorb_apply", "ispa_fit_error", "ispa_fit_error_workspace_size",
     "ispa_lambda_from_trace", "ispa_absorb_solve_lambdas", "ispa_select_layers_below", "ispa_gather_layers",
-    "ispa_absorb_apply_compact", "ispa_status_string", "ispa_last_error", "ispa_version", "ispa_device_check",
+    "ispa_absorb_apply_compact", "ispa_decomp_attn_fp8k", "ispa_quantize_fp8_heads",
+    "ispa_quantize_fp8_heads_workspace_size", "ispa_quantize_fp8_rows", "ispa_quantize_fp8_cols", "ispa_w8a8_gemm", "ispa_status_string", "ispa_last_error", "ispa_version", "ispa_device_check",
 ]
 
 
@@ -50,6 +51,11 @@ class AttnDesc(ctypes.Structure):
 
 class KvSegment(ctypes.Structure):
     _fields_ = [("K", ctypes.c_void_p), ("V", ctypes.c_void_p), ("n_rows", ctypes.c_int64)]
+
+
+class KvSegmentFp8k(ctypes.Structure):
+    _fields_ = [("K8", ctypes.c_void_p), ("k_scale", ctypes.c_void_p), ("V", ctypes.c_void_p),
+                ("n_rows", ctypes.c_int64)]
 
 
 ISPA_MAX_KV_SEGMENTS = 16
@@ -92,6 +98,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "ispa_select_layers_below": (I32, [I32, P, ctypes.c_double, I32, P, P, P, P]),
         "ispa_gather_layers": (I32, [I32, I64, P, P, I32, P, P]),
         "ispa_absorb_apply_compact": (I32, [I32, I32, I32, P, I32, P, P, P]),
+        "ispa_decomp_attn_fp8k": (I32, [ctypes.POINTER(AttnDesc), P, P, ctypes.POINTER(KvSegmentFp8k), I32, I32]
+                                  + [P] * 7 + [SZ, P]),
+        "ispa_quantize_fp8_heads_workspace_size": (SZ, [I64, I32]),
+        "ispa_quantize_fp8_heads": (I32, [I64, I32, I32, I32, P, P, P, P, SZ, P]),
+        "ispa_quantize_fp8_rows": (I32, [I64, I32, I32, P, P, P, P]),
+        "ispa_quantize_fp8_cols": (I32, [I32, I32, P, P, P, P]),
+        "ispa_w8a8_gemm": (I32, [I64, I32, I32, P, P, P, P, P, P]),
         "ispa_status_string": (ctypes.c_char_p, [I32]),
         "ispa_last_error": (ctypes.c_char_p, []),
         "ispa_version": (I32, []),
@@ -451,6 +464,86 @@ def ispa_absorb_apply_compact(selected, dW, W, *, stream=None) -> None:
     _expect(dW, (k, d, d_out), torch.float32, "dW")
     _check(load_library().ispa_absorb_apply_compact(d, d_out, n, _ptr(selected), k, _ptr(dW), _ptr(W),
                                                     _stream(stream)))
+
+
+def ispa_quantize_fp8_heads(x, x8, scale, *, workspace=None, stream=None) -> None:
+    """x [n, H, D] (bf16 / float32) -> codes x8 (uint8, same shape) and scale [H] (one per head)."""
+    n, H, D = x.shape
+    _expect(x8, (n, H, D), torch.uint8, "x8")
+    _expect(scale.reshape(-1), (H,), torch.float32, "scale")
+    lib = load_library()
+    if workspace is None:
+        workspace = _workspace(int(lib.ispa_quantize_fp8_heads_workspace_size(n, H)), x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.ispa_quantize_fp8_heads(n, H, D, _dtype_code(x), _ptr(x), _ptr(x8), _ptr(scale), _ptr(workspace),
+                                       ws_bytes, _stream(stream)))
+
+
+def ispa_quantize_fp8_rows(x, x8, scale, *, stream=None) -> None:
+    """x [n, d] -> codes x8 [n, d] (uint8) with scale [n] (one per row)."""
+    n = x.shape[0]
+    d = x[0].numel() if n else int(x.shape[-1])
+    _expect(x8.reshape(n, -1) if n else x8, (n, d) if n else tuple(x8.shape), torch.uint8, "x8")
+    _expect(scale.reshape(-1), (n,), torch.float32, "scale")
+    _check(load_library().ispa_quantize_fp8_rows(n, d, _dtype_code(x), _ptr(x), _ptr(x8), _ptr(scale),
+                                                 _stream(stream)))
+
+
+def ispa_quantize_fp8_cols(W, w8t, scale, *, stream=None) -> None:
+    """W [d, d_out] float32 -> codes w8t [d_out, d] (uint8, transposed) with scale [d_out] (one per column)."""
+    d, d_out = W.shape
+    _expect(W, (d, d_out), torch.float32, "W")
+    _expect(w8t, (d_out, d), torch.uint8, "w8t")
+    _expect(scale.reshape(-1), (d_out,), torch.float32, "scale")
+    _check(load_library().ispa_quantize_fp8_cols(d, d_out, _ptr(W), _ptr(w8t), _ptr(scale), _stream(stream)))
+
+
+def ispa_w8a8_gemm(a8, a_scale, w8t, w_scale, y, *, stream=None) -> None:
+    """y [n, d_out] bf16 = (a8 [n, d] . w8t [d_out, d]^T) * a_scale[row] * w_scale[col]."""
+    n, d = a8.shape
+    d_out = w8t.shape[0]
+    _expect(a8, (n, d), torch.uint8, "a8")
+    _expect(w8t, (d_out, d), torch.uint8, "w8t")
+    _expect(a_scale.reshape(-1), (n,), torch.float32, "a_scale")
+    _expect(w_scale.reshape(-1), (d_out,), torch.float32, "w_scale")
+    _expect(y, (n, d_out), torch.bfloat16, "y")
+    _check(load_library().ispa_w8a8_gemm(n, d, d_out, _ptr(a8), _ptr(a_scale), _ptr(w8t), _ptr(w_scale), _ptr(y),
+                                         _stream(stream)))
+
+
+def ispa_decomp_attn_fp8k(q8, q_scale, loc_segs: Sequence, hist_segs: Sequence = (), *, scale=None, o_loc=None,
+                          lse_loc=None, o_hist=None, lse_hist=None, o_full=None, lse_full=None, workspace=None,
+                          stream=None) -> None:
+    """Decomposable attention with fp8 queries and keys: q8 [n_q, H, D] codes (scale q_scale [H]); segments
+    are (k8, k_scale, v) triples (k8 uint8 codes, k_scale [H] float32, v bf16).  Outputs bf16 / float32."""
+    n_q, H, D = q8.shape
+    _expect(q8, (n_q, H, D), torch.uint8, "q8")
+    _expect(q_scale.reshape(-1), (H,), torch.float32, "q_scale")
+    segs = list(loc_segs) + list(hist_segs)
+    arr = (KvSegmentFp8k * max(len(segs), 1))()
+    n_loc = n_hist = 0
+    for i, (k8, ks, v) in enumerate(segs):
+        n = int(k8.shape[0])
+        _expect(k8, (n, H, D), torch.uint8, f"segment {i} k8")
+        _expect(ks.reshape(-1), (H,), torch.float32, f"segment {i} k_scale")
+        _expect(v, (n, H, D), torch.bfloat16, f"segment {i} v")
+        arr[i] = KvSegmentFp8k(_ptr(k8), _ptr(ks), _ptr(v), n)
+        if i < len(loc_segs):
+            n_loc += n
+        else:
+            n_hist += n
+    for t, nm in ((o_loc, "o_loc"), (o_hist, "o_hist"), (o_full, "o_full")):
+        _expect(t, (n_q, H, D), torch.bfloat16, nm)
+    for t, nm in ((lse_loc, "lse_loc"), (lse_hist, "lse_hist"), (lse_full, "lse_full")):
+        _expect(t, (H, n_q), torch.float32, nm)
+    desc = AttnDesc(H, D, n_q, n_loc, n_hist, float(scale if scale is not None else D ** -0.5), ISPA_BF16)
+    lib = load_library()
+    if workspace is None and o_full is not None:
+        workspace = _workspace(int(lib.ispa_decomp_attn_workspace_size(ctypes.byref(desc))), q8.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.ispa_decomp_attn_fp8k(ctypes.byref(desc), _ptr(q8), _ptr(q_scale), arr, len(segs), len(loc_segs),
+                                     _ptr(o_loc), _ptr(lse_loc), _ptr(o_hist), _ptr(lse_hist), _ptr(o_full),
+                                     _ptr(lse_full), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def ispa_version() -> int:
