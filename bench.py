@@ -28,6 +28,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decomposable-attn TFLOP/s (% bf16 MFMA peak) + absorb ms/layer, 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA
+# fp8-key attention: half its FLOPs (S = K Q^T) at the fp8 rate, half (P V) at the bf16 rate
+PEAK_FP8K_TFLOPS = round(1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS), 1)
 PEAK_HBM_GBS = 8000.0
 
 
@@ -202,6 +205,34 @@ def main():
         lse_hist=l_s[1], o_full=o_s[2], lse_full=l_s[2], workspace=skws))
     short_flops = cfg.attn_flops() * nq_s / nq
     del skws, q_s, o_s, l_s
+
+    # ---- fp8 keys (ispa_decomp_attn_fp8k): Q and K as E4M3 codes with per-head scales (quantised on the
+    # GPU, timed apart), S = K Q^T on the fp8 matrix cores; and the W8A8 projection of the chunk's rows
+    q8 = torch.empty(nq, H, D, dtype=torch.uint8, device="cuda")
+    kl8 = torch.empty(cfg.n_loc, H, D, dtype=torch.uint8, device="cuda")
+    kh8 = torch.empty(cfg.n_hist, H, D, dtype=torch.uint8, device="cuda")
+    qsc, klsc, khsc = (torch.empty(H, device="cuda") for _ in range(3))
+    qws = ispa.workspace(ispa.ispa_quantize_fp8_heads_workspace_size(max(nq, cfg.n_hist, cfg.n_loc), H))
+
+    def quant_qk():
+        ispa.ispa_quantize_fp8_heads(ch["q"], q8, qsc, workspace=qws)
+        ispa.ispa_quantize_fp8_heads(ch["kl"], kl8, klsc, workspace=qws)
+        ispa.ispa_quantize_fp8_heads(ch["kh"], kh8, khsc, workspace=qws)
+
+    quant_ms = back_to_back_ms(quant_qk)
+    f8_ms = back_to_back_ms(lambda: ispa.ispa_decomp_attn_fp8k(
+        q8, qsc, [(kl8, klsc, ch["vl"])], [(kh8, khsc, ch["vh"])], o_loc=o_loc, lse_loc=lse[0], o_hist=o_hist,
+        lse_hist=lse[1], o_full=o_full, lse_full=lse[2], workspace=atws))
+    a8 = torch.empty(nq, d, dtype=torch.uint8, device="cuda")
+    asc = torch.empty(nq, device="cuda")
+    w8t = torch.empty(d, d, dtype=torch.uint8, device="cuda")
+    wsc = torch.empty(d, device="cuda")
+    a_rows = o_loc.reshape(nq, d)
+    ispa.ispa_quantize_fp8_cols(W, w8t, wsc)
+    y8 = torch.empty(nq, d, dtype=torch.bfloat16, device="cuda")
+    rowq_ms = back_to_back_ms(lambda: ispa.ispa_quantize_fp8_rows(a_rows, a8, asc))
+    w8a8_ms = back_to_back_ms(lambda: ispa.ispa_w8a8_gemm(a8, asc, w8t, wsc, y8))
+    del q8, kl8, kh8, qws, a8, w8t, y8
     gemm_ref = reference_gemm_tflops()
 
     attn_flops = cfg.attn_flops()
@@ -256,6 +287,19 @@ def main():
             "short_chunk_split_ms": round(float(np.median(short_split)), 4),
             "short_chunk_speedup": round(float(np.median(short_unsplit)) / float(np.median(short_split)), 3),
             "short_chunk_split_tflops": round(short_flops / (float(np.median(short_split)) * 1e-3) / 1e12, 2),
+        },
+        "fp8": {
+            "attn_ms": round(float(np.median(f8_ms)), 4),
+            "attn_tflops": round(attn_flops / (float(np.median(f8_ms)) * 1e-3) / 1e12, 2),
+            "attn_speedup_vs_bf16": round(float(np.median(two_ms)) / float(np.median(f8_ms)), 3),
+            "attn_peak_tflops": PEAK_FP8K_TFLOPS,
+            "quantize_q_k_ms": round(float(np.median(quant_ms)), 4),
+            "w8a8_rows": nq, "w8a8_d": d,
+            "quantize_rows_ms": round(float(np.median(rowq_ms)), 4),
+            "w8a8_gemm_ms": round(float(np.median(w8a8_ms)), 4),
+            "w8a8_tflops": round(2.0 * nq * d * d / (float(np.median(w8a8_ms)) * 1e-3) / 1e12, 2),
+            "w8a8_frac_of_fp8_peak": round(2.0 * nq * d * d / (float(np.median(w8a8_ms)) * 1e-3) / 1e12
+                                           / PEAK_FP8_TFLOPS, 4),
         },
         "segments": {
             "layout": f"local [{ns} sink | {nc} chunk], history [{cut} | {cfg.n_hist - cut}] (wrapped ring)",

@@ -332,14 +332,15 @@ ispa_status_t ispa_absorb_apply(int32_t d, int32_t d_out, int32_t n_layers, cons
  * +-448 and rounded to nearest, ties to even.  Codes are uint8.
  * ------------------------------------------------------------------------- */
 
-/* Workspace bytes of ispa_quantize_fp8_heads: ceil(n_rows / 256) * heads floats. */
+/* Workspace bytes of ispa_quantize_fp8_heads: ceil(n_rows / 16) * heads floats. */
 size_t ispa_quantize_fp8_heads_workspace_size(int64_t n_rows, int32_t heads);
 
 /*
  * ispa_quantize_fp8_heads — X [n_rows, heads, head_dim] (dtype BF16 or F32)
  * to codes X8 (same layout, uint8) with one scale per head over all its rows
  * and dims: scale [heads] float32 DEVICE.  For Q and K of
- * ispa_decomp_attn_fp8k.  head_dim 64 or 128; workspace required.
+ * ispa_decomp_attn_fp8k.  head_dim 64 or 128, heads * head_dim <= 16384;
+ * workspace required.
  */
 ispa_status_t ispa_quantize_fp8_heads(int64_t n_rows, int32_t heads, int32_t head_dim, int32_t dtype, const void* X,
                                       uint8_t* X8, float* scale, void* workspace, size_t workspace_bytes,

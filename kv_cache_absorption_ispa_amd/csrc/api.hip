@@ -280,8 +280,8 @@ size_t ispa_quantize_fp8_heads_workspace_size(int64_t n_rows, int32_t heads) {
 ispa_status_t ispa_quantize_fp8_heads(int64_t n_rows, int32_t heads, int32_t head_dim, int32_t dtype, const void* X,
                                       uint8_t* X8, float* scale, void* workspace, size_t workspace_bytes,
                                       void* stream) {
-  if (n_rows < 0 || heads < 1 || heads > 65535 || (head_dim != 64 && head_dim != 128))
-    return invalid("need n_rows >= 0, heads in [1, 65535], head_dim 64 or 128");
+  if (n_rows < 0 || heads < 1 || (head_dim != 64 && head_dim != 128) || heads * head_dim > quant_head_max_width())
+    return invalid("need n_rows >= 0, head_dim 64 or 128, heads * head_dim <= 16384");
   if (dtype != ISPA_F32 && dtype != ISPA_BF16) return invalid("dtype must be ISPA_F32 or ISPA_BF16");
   if ((n_rows > 0 && (!req(X) || !req(X8))) || !req(scale)) return invalid("X, X8, scale must be non-NULL and 16-byte aligned");
   if (!req(workspace) || workspace_bytes < quant_head_workspace_size(n_rows, heads)) {

@@ -22,6 +22,25 @@ __device__ __forceinline__ float load_elem(const void* X, size_t i, int dtype) {
   return dtype == ISPA_BF16 ? bf16_to_f32(((const uint16_t*)X)[i]) : ((const float*)X)[i];
 }
 
+// Eight consecutive elements (16 bytes of bf16 or 32 of float32; i a multiple of 8) as float32.
+__device__ __forceinline__ void load8(const void* X, size_t i, int dtype, float (&v)[8]) {
+  if (dtype == ISPA_BF16) {
+    const u32x4 w = *(const u32x4*)((const uint16_t*)X + i);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] = __builtin_bit_cast(float, w[e] << 16);
+      v[2 * e + 1] = __builtin_bit_cast(float, w[e] & 0xFFFF0000u);
+    }
+  } else {
+    const f32x4 a = *(const f32x4*)((const float*)X + i), b = *(const f32x4*)((const float*)X + i + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] = a[e];
+      v[4 + e] = b[e];
+    }
+  }
+}
+
 // Four codes of x[0..3] / scale, packed little-endian (x[0] in the low byte).
 __device__ __forceinline__ uint32_t quant4(float a, float b, float c, float d, float scale) {
   const float qa = fminf(fmaxf(a / scale, -E4M3_MAX), E4M3_MAX);
@@ -47,40 +66,60 @@ __device__ __forceinline__ float block_max256(float v, float* red) {
   return r;
 }
 
-constexpr int QH_ROWS = 256;  // rows per workgroup of the per-head quantiser
+constexpr int QH_ROWS = 16;          // rows per workgroup of the per-head quantiser
+constexpr int QH_MAX_CHUNKS = 2048;  // 8-element chunks per row it supports (H * D <= 16384)
 
-// Pass 1: partial |x| maxima of head h over rows [b * QH_ROWS, ...): part[h * nblk + b].
+// Pass 1: partial |x| maxima per head over rows [b * QH_ROWS, ...): part[h * nblk + b].  Thread t
+// owns the 8-element chunks t, t + 256, ... of every row (one head each), so rows are read whole
+// and contiguously.
 __global__ __launch_bounds__(256) void head_amax_kernel(const void* X, int dtype, int64_t n, int H, int D,
                                                         float* part) {
-  __shared__ float red[256];
-  const int b = blockIdx.x, h = blockIdx.y;
-  const int tpr = D / 4, rpp = 256 / tpr;
-  const int c4 = (threadIdx.x % tpr) * 4;
-  float m = 0.f;
-  for (int64_t r = (int64_t)b * QH_ROWS + threadIdx.x / tpr; r < min((int64_t)(b + 1) * QH_ROWS, n); r += rpp) {
-    const size_t i = ((size_t)r * H + h) * D + c4;
-    for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf(load_elem(X, i + e, dtype)));
+  __shared__ float cmax[QH_MAX_CHUNKS];
+  const int b = blockIdx.x;
+  const int cpr = H * D / 8;
+  const int64_t r0 = (int64_t)b * QH_ROWS, r1 = min(r0 + QH_ROWS, n);
+  for (int c = threadIdx.x; c < cpr; c += 256) {
+    float m = 0.f;
+    for (int64_t r = r0; r < r1; ++r) {
+      float v[8];
+      load8(X, (size_t)r * H * D + (size_t)c * 8, dtype, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[e]));
+    }
+    cmax[c] = m;
   }
-  m = block_max256(m, red);
-  if (threadIdx.x == 0) part[(size_t)h * gridDim.x + b] = m;
+  __syncthreads();
+  const int cph = D / 8;  // chunks per head
+  for (int h = threadIdx.x; h < H; h += 256) {
+    float m = 0.f;
+    for (int c = 0; c < cph; ++c) m = fmaxf(m, cmax[h * cph + c]);
+    part[(size_t)h * gridDim.x + b] = m;
+  }
 }
 
-// Pass 2: scale of head h from the partials, then the codes of its rows in this block.
-__global__ __launch_bounds__(256) void head_quant_kernel(const void* X, int dtype, int64_t n, int H, int D,
-                                                         const float* part, uint8_t* X8, float* scale) {
+// Pass 2: one workgroup per head reduces its partials to scale[h].
+__global__ __launch_bounds__(256) void head_scale_kernel(const float* part, int nblk, float* scale) {
   __shared__ float red[256];
-  const int b = blockIdx.x, h = blockIdx.y, nb = gridDim.x;
+  const int h = blockIdx.x;
   float m = 0.f;
-  for (int i = threadIdx.x; i < nb; i += 256) m = fmaxf(m, part[(size_t)h * nb + i]);
-  const float s = scale_of(block_max256(m, red));
-  if (b == 0 && threadIdx.x == 0) scale[h] = s;
-  const int tpr = D / 4, rpp = 256 / tpr;
-  const int c4 = (threadIdx.x % tpr) * 4;
-  for (int64_t r = (int64_t)b * QH_ROWS + threadIdx.x / tpr; r < min((int64_t)(b + 1) * QH_ROWS, n); r += rpp) {
-    const size_t i = ((size_t)r * H + h) * D + c4;
-    *(uint32_t*)(X8 + i) = quant4(load_elem(X, i, dtype), load_elem(X, i + 1, dtype), load_elem(X, i + 2, dtype),
-                                  load_elem(X, i + 3, dtype), s);
-  }
+  for (int i = threadIdx.x; i < nblk; i += 256) m = fmaxf(m, part[(size_t)h * nblk + i]);
+  m = block_max256(m, red);
+  if (threadIdx.x == 0) scale[h] = scale_of(m);
+}
+
+// Pass 3: the codes, 8 elements per thread per step, rows read whole.
+__global__ __launch_bounds__(256) void head_quant_kernel(const void* X, int dtype, int64_t n, int H, int D,
+                                                         const float* scale, uint8_t* X8) {
+  const int cpr = H * D / 8, cph = D / 8;
+  const int64_t r0 = (int64_t)blockIdx.x * QH_ROWS, r1 = min(r0 + QH_ROWS, n);
+  for (int64_t r = r0; r < r1; ++r)
+    for (int c = threadIdx.x; c < cpr; c += 256) {
+      const float s = scale[c / cph];
+      const size_t i = (size_t)r * H * D + (size_t)c * 8;
+      float v[8];
+      load8(X, i, dtype, v);
+      *(u32x2*)(X8 + i) = u32x2{quant4(v[0], v[1], v[2], v[3], s), quant4(v[4], v[5], v[6], v[7], s)};
+    }
 }
 
 // One wave per row of X [n, d]: scale[r] = amax(row) / 448 and the row's codes.
@@ -218,14 +257,18 @@ size_t quant_head_workspace_size(int64_t n, int32_t heads) {
   return (size_t)(nb > 0 ? nb : 1) * heads * sizeof(float);
 }
 
+int32_t quant_head_max_width() { return QH_MAX_CHUNKS * 8; }
+
 ispa_status_t launch_quant_head(int64_t n, int32_t H, int32_t D, int32_t dtype, const void* X, uint8_t* X8,
                                 float* scale, void* ws, hipStream_t s) {
   const unsigned nb = (unsigned)std::max<int64_t>((n + QH_ROWS - 1) / QH_ROWS, 1);
-  hipLaunchKernelGGL(head_amax_kernel, dim3(nb, H), dim3(256), 0, s, X, dtype, n, H, D, (float*)ws);
+  hipLaunchKernelGGL(head_amax_kernel, dim3(nb), dim3(256), 0, s, X, dtype, n, H, D, (float*)ws);
   ispa_status_t st = hip_check(hipGetLastError(), "head_amax_kernel launch");
   if (st != ISPA_OK) return st;
-  hipLaunchKernelGGL(head_quant_kernel, dim3(nb, H), dim3(256), 0, s, X, dtype, n, H, D, (const float*)ws, X8,
-                     scale);
+  hipLaunchKernelGGL(head_scale_kernel, dim3(H), dim3(256), 0, s, (const float*)ws, (int)nb, scale);
+  st = hip_check(hipGetLastError(), "head_scale_kernel launch");
+  if (st != ISPA_OK || n == 0) return st;
+  hipLaunchKernelGGL(head_quant_kernel, dim3(nb), dim3(256), 0, s, X, dtype, n, H, D, (const float*)scale, X8);
   return hip_check(hipGetLastError(), "head_quant_kernel launch");
 }
 

@@ -66,6 +66,7 @@ ispa_status_t launch_lse_merge(int32_t n_parts, const void* const* O, const floa
                                hipStream_t s);
 
 size_t quant_head_workspace_size(int64_t n, int32_t heads);
+int32_t quant_head_max_width();  // largest heads * head_dim the per-head quantiser takes
 ispa_status_t launch_quant_head(int64_t n, int32_t H, int32_t D, int32_t dtype, const void* X, uint8_t* X8,
                                 float* scale, void* ws, hipStream_t s);
 ispa_status_t launch_quant_rows(int64_t n, int32_t d, int32_t dtype, const void* X, uint8_t* X8, float* scale,

@@ -466,6 +466,10 @@ def ispa_absorb_apply_compact(selected, dW, W, *, stream=None) -> None:
                                                     _stream(stream)))
 
 
+def ispa_quantize_fp8_heads_workspace_size(n_rows: int, heads: int) -> int:
+    return int(load_library().ispa_quantize_fp8_heads_workspace_size(n_rows, heads))
+
+
 def ispa_quantize_fp8_heads(x, x8, scale, *, workspace=None, stream=None) -> None:
     """x [n, H, D] (bf16 / float32) -> codes x8 (uint8, same shape) and scale [H] (one per head)."""
     n, H, D = x.shape

@@ -167,3 +167,9 @@ def test_variant_validation_needs_no_gpu():
     assert lib.ispa_gather_layers(4, 16, ok, ok, 0, None, None) == ispa.ISPA_OK  # nothing to gather
     assert lib.ispa_absorb_apply_compact(128, 64, 4, ok, 5, ok, ok, None) == bad
     assert lib.ispa_absorb_apply_compact(128, 64, 4, None, 0, None, None, None) == ispa.ISPA_OK
+
+
+def test_every_entry_point_has_a_python_wrapper():
+    skip = {"ispa_status_string", "ispa_last_error"}
+    missing = [n for n in ispa.EXPORTS if n not in skip and not callable(getattr(ispa, n, None))]
+    assert missing == []
