@@ -9,14 +9,13 @@
 // Selection" (rank layers by reconstruction error).
 //
 // Structure (nb = 64 column panels, right-looking):
-//   M = G + lambda I                                   (init kernel)
-//   R = C W, accumulated in float64                    (MFMA f64 GEMM)
+//   M = G + lambda I (lambda scalar or per layer)      (init kernel)
+//   R = C W in float32                                 (GEMM, on a second stream beside the factorisation)
 //   for each panel k:
 //     factor M_kk = L_kk L_kk^T and invert L_kk       (one workgroup per layer)
 //     L_ik = M_ik L_kk^-T                             (GEMM, in place)
 //     M_ij -= L_ik L_jk^T  (lower tiles only)         (GEMM)
-//   explicit inverse of L, one block row at a time:
-//     (L^-1)_{i,<i} = -L_ii^-1 L_{i,<i} (L^-1)_{<i,<i} (two GEMMs per block row)
+//   explicit inverse of L by recursive doubling over block ranges
 //   X = L^-T (L^-1 R)                                  (two triangular GEMMs)
 //   one refinement step: r = R - G X - lambda X in float64,
 //   dW = X + L^-T (L^-1 r).
@@ -31,6 +30,8 @@
 // set to NaN at the end and its W_new is left alone.
 #include <utility>
 #include <vector>
+
+#include <mutex>
 
 #include "ispa_internal.h"
 
@@ -605,6 +606,34 @@ ispa_status_t invert_lower(hipStream_t s, int batch, int d, const float* L, floa
   return ISPA_OK;
 }
 
+// A second stream per device for R = C W beside the latency-bound factorisation, with its fork and
+// join events (created once, kept until the process ends; default priority).  The enqueue of one solve holds the mutex, so the
+// events' record/wait pairs of two host threads never interleave.
+struct AuxStream {
+  hipStream_t s2 = nullptr;
+  std::vector<hipEvent_t> ev;
+};
+std::mutex g_aux_mu;
+AuxStream g_aux[64];
+
+ispa_status_t aux_stream(int n_events, AuxStream*& out) {
+  int dev = 0;
+  ISPA_TRY(hip_check(hipGetDevice(&dev), "hipGetDevice"));
+  if (dev < 0 || dev >= 64) {
+    set_error("device index above 63");
+    return ISPA_E_UNSUPPORTED;
+  }
+  AuxStream& a = g_aux[dev];
+  if (a.s2 == nullptr) ISPA_TRY(hip_check(hipStreamCreateWithFlags(&a.s2, hipStreamNonBlocking), "hipStreamCreate"));
+  while ((int)a.ev.size() < n_events) {
+    hipEvent_t e;
+    ISPA_TRY(hip_check(hipEventCreateWithFlags(&e, hipEventDisableTiming), "hipEventCreate"));
+    a.ev.push_back(e);
+  }
+  out = &a;
+  return ISPA_OK;
+}
+
 ispa_status_t launch_absorb(int32_t d, int32_t d_out, int32_t batch, const float* G, const float* C, const float* W,
                             float lambda, const float* lam_b, float* dW, float* W_new, int32_t* info, void* ws,
                             size_t ws_bytes, hipStream_t s) {
@@ -622,13 +651,23 @@ ispa_status_t launch_absorb(int32_t d, int32_t d_out, int32_t batch, const float
   float* Zb = Rr + (size_t)batch * dn;
   const int nblk = d / NB;
 
+  std::lock_guard<std::mutex> lock(g_aux_mu);
+  AuxStream* aux = nullptr;
+  ISPA_TRY(aux_stream(2, aux));
+  hipStream_t s2 = aux->s2;
+  hipEvent_t* ev = aux->ev.data();  // [0] fork, [1] join
+
   hipLaunchKernelGGL(init_shift_kernel, dim3((unsigned)((dd / 4 + 255) / 256), batch), dim3(256), 0, s, G, M, d,
                      lambda, lam_b, info);
   ISPA_TRY(hip_check(hipGetLastError(), "init_shift_kernel launch"));
-  // R = C W (float32; R's rounding perturbs the solution like the float32 statistics themselves do)
-  ISPA_TRY((gemm<false, false>(s, batch, d, d_out, d, C, d, dd, W, d_out, dn, nullptr, 0, 0, Rb, d_out, dn, 1.f, 0.f,
-                               false, nullptr)));
-  // Cholesky, right-looking by 64-column panels
+  ISPA_TRY(hip_check(hipEventRecord(ev[0], s), "hipEventRecord"));
+  ISPA_TRY(hip_check(hipStreamWaitEvent(s2, ev[0], 0), "hipStreamWaitEvent"));
+  // R = C W on the second stream, beside the factorisation (float32; R's rounding perturbs the
+  // solution like the float32 statistics themselves do)
+  ISPA_TRY((gemm<false, false>(s2, batch, d, d_out, d, C, d, dd, W, d_out, dn, nullptr, 0, 0, Rb, d_out, dn, 1.f,
+                               0.f, false, nullptr)));
+  // Cholesky, right-looking by 64-column panels (one stream: a wait on an event recorded on another
+  // stream costs ~15 us of latency here, more than a look-ahead split of the trailing update saves)
   for (int k = 0; k < nblk; ++k) {
     const int k0 = k * NB;
     hipLaunchKernelGGL(potrf_diag_kernel, dim3(batch), dim3(256), 0, s, M, d, k0, Linvf, info);
@@ -645,6 +684,9 @@ ispa_status_t launch_absorb(int32_t d, int32_t d_out, int32_t batch, const float
     ISPA_TRY((gemm<false, true>(s, batch, rest, rest, NB, panel, d, dd, panel, d, dd, trail, d, dd, trail, d, dd, -1.f,
                                 1.f, true, info)));
   }
+  // join: R = C W is done before the solve reads it
+  ISPA_TRY(hip_check(hipEventRecord(ev[1], s2), "hipEventRecord"));
+  ISPA_TRY(hip_check(hipStreamWaitEvent(s, ev[1], 0), "hipStreamWaitEvent"));
   // explicit L^-1 by recursive doubling over block ranges: for adjacent ranges A (first) and C,
   // inv([A 0; B C]) has off-diagonal block -C^-1 (B A^-1); pairs of equal sizes run as one launch.
   ISPA_TRY(invert_lower(s, batch, d, M, Linvf, Tb, info));
