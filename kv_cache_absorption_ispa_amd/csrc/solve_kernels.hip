@@ -59,17 +59,23 @@ struct GemmParams {
 // D = alpha * op(A) op(B) + beta * Cin; op(A) is MxK, op(B) is KxN.
 // TA: A stored KxM (op(A) = A^T); TB: B stored NxK (op(B) = B^T).
 // T x T output tile (T = 64 or 128), 4 waves in 2x2, each (T/2)x(T/2) as blocks of
-// v_mfma_f32_32x32x2_f32.  M, N multiples of T; K multiple of 16.  Cin may equal D.
+// v_mfma_f32_32x32x2_f32.  K advances in slabs of GKS: the next slab's operands are loaded into
+// registers while the current one is multiplied from LDS (two LDS buffers, one barrier per slab),
+// so few resident workgroups still hide the load latency.  M, N multiples of T; K multiple of GKS.
+// Cin may equal D.
+constexpr int GKS = 32;
+
 template <bool TA, bool TB, int T>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
-  constexpr int WB = T / 64;  // 32x32 blocks per wave per dimension
+  constexpr int WB = T / 64;               // 32x32 blocks per wave per dimension
+  constexpr int NLD = T * GKS / 1024;      // float4 loads per thread per operand per slab
   const int b = blockIdx.z / p.npairs, q = blockIdx.z % p.npairs;
   if (p.info && p.info[b] != 0) return;
   const int tm = blockIdx.y, tn = blockIdx.x;
   if (p.lower_only && tm < tn) return;
   const int m0 = tm * T, n0 = tn * T;
-  __shared__ float As[16][T + 4];  // [k][m]
-  __shared__ float Bs[16][T + 4];  // [k][n]
+  __shared__ float As[2][GKS][T + 4];  // [buffer][k][m]
+  __shared__ float Bs[2][GKS][T + 4];  // [buffer][k][n]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
   const int wm = (wave >> 1) * (T / 2), wn = (wave & 1) * (T / 2);
@@ -82,44 +88,74 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
     for (int j = 0; j < WB; ++j) acc[i][j] = f32x16{0};
   const int kb = p.kmode == 2 ? m0 : (p.kmode == 3 ? n0 : 0);
   const int ke = p.kmode == 1 ? min(p.K, m0 + T) : p.K;
-  for (int k0 = kb; k0 < ke; k0 += 16) {
+  f32x4 ra[NLD], rb[NLD];
+  auto load = [&](int k0) {
 #pragma unroll
-    for (int r = 0; r < T / 64; ++r) {
+    for (int r = 0; r < NLD; ++r) {
       const int t = tid + 256 * r;
       if (!TA) {
-        const int m = t >> 2, kq = t & 3;
-        const f32x4 v = *(const f32x4*)(A + (size_t)(m0 + m) * p.lda + k0 + 4 * kq);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) As[4 * kq + e][m] = v[e];
+        const int m = t / (GKS / 4), kq = t % (GKS / 4);
+        ra[r] = *(const f32x4*)(A + (size_t)(m0 + m) * p.lda + k0 + 4 * kq);
       } else {
         const int k = t / (T / 4), mq = t % (T / 4);
-        *(f32x4*)(&As[k][4 * mq]) = *(const f32x4*)(A + (size_t)(k0 + k) * p.lda + m0 + 4 * mq);
+        ra[r] = *(const f32x4*)(A + (size_t)(k0 + k) * p.lda + m0 + 4 * mq);
       }
       if (TB) {
-        const int n = t >> 2, kq = t & 3;
-        const f32x4 v = *(const f32x4*)(B + (size_t)(n0 + n) * p.ldb + k0 + 4 * kq);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) Bs[4 * kq + e][n] = v[e];
+        const int n = t / (GKS / 4), kq = t % (GKS / 4);
+        rb[r] = *(const f32x4*)(B + (size_t)(n0 + n) * p.ldb + k0 + 4 * kq);
       } else {
         const int k = t / (T / 4), nq = t % (T / 4);
-        *(f32x4*)(&Bs[k][4 * nq]) = *(const f32x4*)(B + (size_t)(k0 + k) * p.ldb + n0 + 4 * nq);
+        rb[r] = *(const f32x4*)(B + (size_t)(k0 + k) * p.ldb + n0 + 4 * nq);
       }
     }
-    __syncthreads();
+  };
+  auto store = [&](int buf) {
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
+    for (int r = 0; r < NLD; ++r) {
+      const int t = tid + 256 * r;
+      if (!TA) {
+        const int m = t / (GKS / 4), kq = t % (GKS / 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) As[buf][4 * kq + e][m] = ra[r][e];
+      } else {
+        const int k = t / (T / 4), mq = t % (T / 4);
+        *(f32x4*)(&As[buf][k][4 * mq]) = ra[r];
+      }
+      if (TB) {
+        const int n = t / (GKS / 4), kq = t % (GKS / 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Bs[buf][4 * kq + e][n] = rb[r][e];
+      } else {
+        const int k = t / (T / 4), nq = t % (T / 4);
+        *(f32x4*)(&Bs[buf][k][4 * nq]) = rb[r];
+      }
+    }
+  };
+  if (kb < ke) {
+    load(kb);
+    store(0);
+    __syncthreads();
+  }
+  int buf = 0;
+  for (int k0 = kb; k0 < ke; k0 += GKS) {
+    const bool more = k0 + GKS < ke;
+    if (more) load(k0 + GKS);  // in flight during the multiplies below
+#pragma unroll
+    for (int kk = 0; kk < GKS / 2; ++kk) {
       float a[WB], bv[WB];
 #pragma unroll
       for (int i = 0; i < WB; ++i) {
-        a[i] = As[2 * kk + hh][wm + 32 * i + l32];
-        bv[i] = Bs[2 * kk + hh][wn + 32 * i + l32];
+        a[i] = As[buf][2 * kk + hh][wm + 32 * i + l32];
+        bv[i] = Bs[buf][2 * kk + hh][wn + 32 * i + l32];
       }
 #pragma unroll
       for (int i = 0; i < WB; ++i)
 #pragma unroll
         for (int j = 0; j < WB; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], bv[j], acc[i][j], 0, 0, 0);
     }
+    if (more) store(buf ^ 1);  // the other buffer: its last readers finished before the previous barrier
     __syncthreads();
+    buf ^= 1;
   }
   const float* Cin = p.Cin ? p.Cin + b * p.sC + q * p.pC : nullptr;
   float* D = p.D + b * p.sD + q * p.pD;
@@ -498,6 +534,10 @@ ispa_status_t gemm(hipStream_t s, int batch, int M, int N, int K, const float* A
                    float beta, bool lower_only, const int32_t* info, int kmode = 0, int npairs = 1,
                    size_t pA = 0, size_t pB = 0, size_t pC = 0, size_t pD = 0) {
   if (M <= 0 || N <= 0 || K <= 0) return ISPA_OK;
+  if (K % GKS != 0) {
+    set_error("internal: GEMM depth not a multiple of 32");
+    return ISPA_E_INVALID_ARG;
+  }
   GemmParams p;
   p.A = A; p.B = B; p.Cin = Cin; p.D = D;
   p.M = M; p.N = N; p.K = K;
