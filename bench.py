@@ -312,7 +312,7 @@ def main():
         "absorb_ms_per_layer": round(float(np.mean(solve_ms)), 4),
         "roofline": {
             "bound": "mfma",
-            "kernel": "attn_bf16_kernel<128, 8, 1, 128> (ispa_decomp_attn)",
+            "kernel": "attn_bf16_kernel<128, 8, 1, 128, false, false> (ispa_decomp_attn)",
             "achieved": round(achieved, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
