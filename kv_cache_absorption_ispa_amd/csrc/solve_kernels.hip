@@ -649,14 +649,16 @@ ispa_status_t invert_lower(hipStream_t s, int batch, int d, const float* L, floa
 // A second stream per device for R = C W beside the latency-bound factorisation, with its fork and
 // join events (created once, kept until the process ends; default priority).  The enqueue of one solve holds the mutex, so the
 // events' record/wait pairs of two host threads never interleave.
+namespace {
 struct AuxStream {
   hipStream_t s2 = nullptr;
   std::vector<hipEvent_t> ev;
 };
 std::mutex g_aux_mu;
 AuxStream g_aux[64];
+}  // namespace
 
-ispa_status_t aux_stream(int n_events, AuxStream*& out) {
+static ispa_status_t aux_stream(int n_events, AuxStream*& out) {
   int dev = 0;
   ISPA_TRY(hip_check(hipGetDevice(&dev), "hipGetDevice"));
   if (dev < 0 || dev >= 64) {

@@ -234,6 +234,48 @@ class LayerStack:
         ispa.ispa_decomp_attn(q, k_loc, v_loc, k_hist, v_hist, o_full=o_full, lse_full=lse_full,
                               workspace=self._attn_ws, stream=self.stream)
 
+    # ------------------------------------------------------- streaming K/V cache
+    def _attn_ws_for(self, q, n_loc: int, n_hist: int):
+        need = ispa.ispa_decomp_attn_workspace_size(q, n_loc, n_hist)
+        if need and (self._attn_ws is None or self._attn_ws.numel() < need):
+            self._attn_ws = ispa.workspace(need, q.device)
+        return self._attn_ws
+
+    def warmup_chunk_cached(self, layer: int, q, cache, o_loc, o_full, heldout: bool = False) -> None:
+        """warmup_chunk with the keys taken from a StreamingKVCache: the layer's sink and current slot
+        (local) and its history runs, attended in place.  The caller writes the chunk's K/V into
+        ``cache.current(layer)`` before and calls ``cache.commit(layer)`` after."""
+        if self.converted is not None:
+            raise ispa.IspaError(ispa.ISPA_E_INVALID_ARG, "warmup is over (transition already ran)")
+        loc, hist = cache.segments(layer)
+        n_loc = sum(int(k.shape[0]) for k, _ in loc)
+        n_hist = sum(int(k.shape[0]) for k, _ in hist)
+        ispa.ispa_decomp_attn_segments(q, loc, hist, o_loc=o_loc, o_full=o_full,
+                                       workspace=self._attn_ws_for(q, n_loc, n_hist), stream=self.stream)
+        self.accumulate_rows(layer, o_loc, o_full, heldout=heldout)
+
+    def post_chunk_cached(self, layer: int, q, cache, o_full, lse_full=None) -> None:
+        """Attention of a post-absorb chunk from the cache (a converted layer's cache holds no history
+        once evict_converted ran, so it attends locally)."""
+        if self.converted is None:
+            raise ispa.IspaError(ispa.ISPA_E_INVALID_ARG, "transition has not run")
+        loc, hist = cache.segments(layer)
+        if self.is_converted(layer) and hist:
+            raise ispa.IspaError(ispa.ISPA_E_INVALID_ARG, "converted layer still holds history (evict_converted)")
+        n_loc = sum(int(k.shape[0]) for k, _ in loc)
+        n_hist = sum(int(k.shape[0]) for k, _ in hist)
+        ispa.ispa_decomp_attn_segments(q, loc, hist, o_full=o_full, lse_full=lse_full,
+                                       workspace=self._attn_ws_for(q, n_loc, n_hist), stream=self.stream)
+
+    def evict_converted(self, cache) -> int:
+        """Drop the converted layers' history K/V from the cache; returns the bytes released."""
+        if self.converted is None:
+            raise ispa.IspaError(ispa.ISPA_E_INVALID_ARG, "transition has not run")
+        before = cache.resident_bytes()
+        for layer in self.converted:
+            cache.evict(layer)
+        return before - cache.resident_bytes()
+
     def evicted_kv_bytes(self, n_hist: int) -> int:
         """History K and V bytes the converted layers no longer hold (n_hist keys per layer)."""
         if self.converted is None:

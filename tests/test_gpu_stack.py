@@ -212,3 +212,60 @@ def test_absorb_apply_touches_only_selected():
     Wn = W.cpu().numpy()
     for l in range(L):
         assert np.array_equal(Wn[l], W0[l] + dW0[l] if l in (1, 4) else W0[l]), l
+
+
+def test_streaming_loop_through_the_cache():
+    """The pages' streaming loop on a small stack: chunks enter a StreamingKVCache; warmup chunks run
+    the dual-stream attention on the cached segments and feed the Gram statistics; the transition
+    converts the lowest-error layers and evicts their history from the cache; later chunks attend to
+    sink + chunk (converted) or to the whole cached context (the rest).  Every chunk's attention is
+    checked against the oracle on the keys the loop must see; the transition by its properties."""
+    from kv_cache_absorption_ispa_amd.kv_cache import StreamingKVCache
+    H, D, n_sink, ct, L, K, n_warm, n_post = 1, 128, 64, 256, 4, 2, 3, 2
+    d = H * D
+    W0 = np.stack([inputs.normal(90, l, inputs.LAYER_CHUNK, inputs.T_W, (d, d)) * np.float32(d ** -0.5)
+                   for l in range(L)])
+    st = LayerStack(torch.from_numpy(W0.copy()).cuda(), H, D, ct, 1e-2, K)
+    cache = StreamingKVCache(L, H, D, n_sink, ct, max_hist_chunks=8, dtype=torch.bfloat16, device="cuda")
+    sinks = [inputs.stream_sink(90 + l, n_sink, H, D, "bf16") for l in range(L)]
+    for l in range(L):
+        cache.sink(l)[0].copy_(dev(sinks[l][0]))
+        cache.sink(l)[1].copy_(dev(sinks[l][1]))
+    host = {l: ([], []) for l in range(L)}
+    o_loc = torch.empty(ct, H, D, dtype=torch.bfloat16, device="cuda")
+    o_full = torch.empty_like(o_loc)
+    worst = 0.0
+    for c in range(n_warm + n_post):
+        if c == n_warm:
+            conv = st.transition()
+            torch.cuda.synchronize()
+            assert st.info.cpu().tolist() == [0] * L and len(conv) == K
+            released = st.evict_converted(cache)
+            assert released == K * 2 * 8 * ct * H * D * 2  # 8 history slots of K and V per converted layer
+        for l in range(L):
+            ch = inputs.stream_chunk(90 + l, c, ct, ct, H, D, "bf16")
+            host[l][0].append(ch.k.f64)
+            host[l][1].append(ch.v.f64)
+            cache.write_current(l, dev(ch.k), dev(ch.v))
+            q = dev(ch.q)
+            if c < n_warm:
+                st.warmup_chunk_cached(l, q, cache, o_loc, o_full)
+            else:
+                st.post_chunk_cached(l, q, cache, o_full)
+            torch.cuda.synchronize()
+            converted = c >= n_warm and l in st.converted
+            kl = np.concatenate([sinks[l][0].f64, host[l][0][c]])
+            vl = np.concatenate([sinks[l][1].f64, host[l][1][c]])
+            kh = np.concatenate(host[l][0][:c]) if c and not converted else np.zeros((0, H, D))
+            vh = np.concatenate(host[l][1][:c]) if c and not converted else np.zeros((0, H, D))
+            ref = oracle.branch_outputs(ch.q.f64, kl, vl, kh, vh, 128 ** -0.5)
+            worst = max(worst, maxabs(host64(o_full), ref["O_full"]))
+            if c < n_warm:
+                worst = max(worst, maxabs(host64(o_loc), ref["O_loc"]))
+            cache.commit(l)
+    say("streaming loop worst max-abs", worst)
+    assert worst <= TOL_BF16_O
+    # converted layers hold sink + one slot; the others the whole window
+    for l in range(L):
+        rows = cache.sink_k[l].shape[0] + cache.ring_k[l].shape[0]
+        assert rows == (n_sink + ct if l in st.converted else n_sink + 9 * ct)
