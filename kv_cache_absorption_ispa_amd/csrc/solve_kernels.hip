@@ -140,18 +140,31 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
   for (int k0 = kb; k0 < ke; k0 += GKS) {
     const bool more = k0 + GKS < ke;
     if (more) load(k0 + GKS);  // in flight during the multiplies below
+    // operands of step kk + 1 are read from LDS before the multiplies of step kk are issued, so the
+    // LDS latency hides behind them (sched_barrier keeps the compiler from sinking the reads)
+    float a[2][WB], bv[2][WB];
+#pragma unroll
+    for (int i = 0; i < WB; ++i) {
+      a[0][i] = As[buf][hh][wm + 32 * i + l32];
+      bv[0][i] = Bs[buf][hh][wn + 32 * i + l32];
+    }
 #pragma unroll
     for (int kk = 0; kk < GKS / 2; ++kk) {
-      float a[WB], bv[WB];
+      const int c = kk & 1;
+      if (kk + 1 < GKS / 2) {
 #pragma unroll
-      for (int i = 0; i < WB; ++i) {
-        a[i] = As[buf][2 * kk + hh][wm + 32 * i + l32];
-        bv[i] = Bs[buf][2 * kk + hh][wn + 32 * i + l32];
+        for (int i = 0; i < WB; ++i) {
+          a[c ^ 1][i] = As[buf][2 * (kk + 1) + hh][wm + 32 * i + l32];
+          bv[c ^ 1][i] = Bs[buf][2 * (kk + 1) + hh][wn + 32 * i + l32];
+        }
       }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < WB; ++i)
 #pragma unroll
-        for (int j = 0; j < WB; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], bv[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < WB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[c][i], bv[c][j], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (more) store(buf ^ 1);  // the other buffer: its last readers finished before the previous barrier
     __syncthreads();
