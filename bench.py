@@ -204,6 +204,12 @@ def main():
         q_s, [(ch["kl"], ch["vl"])], [(ch["kh"], ch["vh"])], o_loc=o_s[0], lse_loc=l_s[0], o_hist=o_s[1],
         lse_hist=l_s[1], o_full=o_s[2], lse_full=l_s[2], workspace=skws))
     short_flops = cfg.attn_flops() * nq_s / nq
+
+    # ---- the absorb without its refinement step (ispa_absorb_solve_ex, ISPA_ABSORB_NO_REFINE)
+    dW2 = torch.empty_like(dW)
+    norefine_ms = back_to_back_ms(lambda: ispa.ispa_absorb_solve_ex(G, C, W, cfg.lam, dW2, info, refine=False,
+                                                                    workspace=aws), n=3)
+    del dW2
     del skws, q_s, o_s, l_s
 
     # ---- fp8 keys (ispa_decomp_attn_fp8k): Q and K as E4M3 codes with per-head scales (quantised on the
@@ -310,6 +316,7 @@ def main():
         },
         "gram_ms_per_chunk": round(float(np.mean(gram_ms)), 4),
         "absorb_ms_per_layer": round(float(np.mean(solve_ms)), 4),
+        "absorb_ms_per_layer_no_refine": round(float(np.median(norefine_ms)), 4),
         "roofline": {
             "bound": "mfma",
             "kernel": "attn_bf16_kernel<128, 8, 1, 128, false, false> (ispa_decomp_attn)",

@@ -20,7 +20,7 @@
  *   ispa_absorb_apply  W += dW for the converted layers,
  *   ispa_decomp_attn_fp8k, ispa_quantize_fp8_*, ispa_w8a8_gemm
  *                      fp8 keys / queries and the W8A8 projection,
- *   ispa_fit_error, ispa_lambda_from_trace, ispa_absorb_solve_lambdas,
+ *   ispa_fit_error, ispa_lambda_from_trace, ispa_absorb_solve_lambdas, ispa_absorb_solve_ex,
  *   ispa_select_layers_below, ispa_gather_layers, ispa_absorb_apply_compact
  *                      selection and lambda variants (error before the fit or
  *                      on held-out rows, lambda from tr(G), threshold K),
@@ -444,6 +444,23 @@ ispa_status_t ispa_lambda_from_trace(int32_t d, int32_t batch, const float* G, f
 ispa_status_t ispa_absorb_solve_lambdas(int32_t d, int32_t d_out, int32_t batch, const float* G, const float* C,
                                         const float* W, const float* lambdas, float* dW, float* W_new,
                                         int32_t* info, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Flag of ispa_absorb_solve_ex: skip the float64-residual refinement step. */
+#define ISPA_ABSORB_NO_REFINE 1
+
+/*
+ * ispa_absorb_solve_ex — ispa_absorb_solve with options: lambda from the
+ * DEVICE array lambdas [batch] when it is non-NULL (else the scalar lambda),
+ * and flags.  ISPA_ABSORB_NO_REFINE skips the refinement step (the float64
+ * residual and the second pair of triangular products, ~40 % of the solve at
+ * d = 5120): dW is then the float32 solve, whose error grows like
+ * cond(G + lambda I) * 2^-24 instead of reaching the float32 statistics'
+ * own accuracy.  Same workspace and errors as ispa_absorb_solve.
+ */
+ispa_status_t ispa_absorb_solve_ex(int32_t d, int32_t d_out, int32_t batch, const float* G, const float* C,
+                                   const float* W, float lambda, const float* lambdas, int32_t flags, float* dW,
+                                   float* W_new, int32_t* info, void* workspace, size_t workspace_bytes,
+                                   void* stream);
 
 /*
  * ispa_select_layers_below — convert every layer whose error is at most tau,

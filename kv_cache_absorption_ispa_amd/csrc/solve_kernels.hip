@@ -456,7 +456,7 @@ __global__ __launch_bounds__(256) void finalize_kernel(const float* W, float* dW
     *(f32x4*)dw = f32x4{NAN, NAN, NAN, NAN};
     return;
   }
-  const f32x4 x = *(const f32x4*)dw + *(const f32x4*)(corr + b * n + i4);
+  const f32x4 x = corr ? *(const f32x4*)dw + *(const f32x4*)(corr + b * n + i4) : *(const f32x4*)dw;
   *(f32x4*)dw = x;
   if (Wn) *(f32x4*)(Wn + b * n + i4) = *(const f32x4*)(W + b * n + i4) + x;
 }
@@ -691,7 +691,7 @@ static ispa_status_t aux_stream(int n_events, AuxStream*& out) {
 
 ispa_status_t launch_absorb(int32_t d, int32_t d_out, int32_t batch, const float* G, const float* C, const float* W,
                             float lambda, const float* lam_b, float* dW, float* W_new, int32_t* info, void* ws,
-                            size_t ws_bytes, hipStream_t s) {
+                            size_t ws_bytes, hipStream_t s, bool refine) {
   const size_t need = absorb_workspace_size(d, d_out, batch);
   if (ws == nullptr || ws_bytes < need) {
     set_error("ispa_absorb_solve: workspace too small");
@@ -747,6 +747,11 @@ ispa_status_t launch_absorb(int32_t d, int32_t d_out, int32_t batch, const float
   ISPA_TRY(invert_lower(s, batch, d, M, Linvf, Tb, info));
   // X = (L L^T)^-1 R
   ISPA_TRY(chol_apply(s, batch, d, d_out, Linvf, Rb, Zb, dW, info));
+  if (!refine) {
+    hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)((dn / 4 + 255) / 256), batch), dim3(256), 0, s, W, dW,
+                       (const float*)nullptr, W_new, dn, (const int32_t*)info);
+    return hip_check(hipGetLastError(), "finalize_kernel launch");
+  }
   // refinement: r = R - G X - lambda X accumulated in float64 (the cancellation needs it),
   // correction = (L L^T)^-1 r
   ISPA_TRY(gemm_d(s, batch, d, d_out, d, G, d, dd, dW, d_out, dn, Rb, d_out, dn, dW, d_out, dn, nullptr, Rr, d_out,

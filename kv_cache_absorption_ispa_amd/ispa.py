@@ -26,7 +26,7 @@ EXPORTS = [
     "ispa_absorb_workspace_size", "ispa_absorb_solve", "ispa_eps_workspace_size", "ispa_layer_eps",
     "ispa_select_layers", "ispa_absorb_apply", "ispa_fit_error", "ispa_fit_error_workspace_size",
     "ispa_lambda_from_trace", "ispa_absorb_solve_lambdas", "ispa_select_layers_below", "ispa_gather_layers",
-    "ispa_absorb_apply_compact", "ispa_decomp_attn_fp8k", "ispa_quantize_fp8_heads",
+    "ispa_absorb_apply_compact", "ispa_absorb_solve_ex", "ispa_decomp_attn_fp8k", "ispa_quantize_fp8_heads",
     "ispa_quantize_fp8_heads_workspace_size", "ispa_quantize_fp8_rows", "ispa_quantize_fp8_cols", "ispa_w8a8_gemm", "ispa_status_string", "ispa_last_error", "ispa_version", "ispa_device_check",
 ]
 
@@ -95,6 +95,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "ispa_fit_error": (I32, [I32, I32, I32, P, P, P, P, P, P, P, P, SZ, P]),
         "ispa_lambda_from_trace": (I32, [I32, I32, P, F, P, P]),
         "ispa_absorb_solve_lambdas": (I32, [I32, I32, I32, P, P, P, P, P, P, P, P, SZ, P]),
+        "ispa_absorb_solve_ex": (I32, [I32, I32, I32, P, P, P, F, P, I32, P, P, P, P, SZ, P]),
         "ispa_select_layers_below": (I32, [I32, P, ctypes.c_double, I32, P, P, P, P]),
         "ispa_gather_layers": (I32, [I32, I64, P, P, I32, P, P]),
         "ispa_absorb_apply_compact": (I32, [I32, I32, I32, P, I32, P, P, P]),
@@ -433,6 +434,30 @@ def ispa_absorb_solve_lambdas(G, C, W, lambdas, dW, info, *, W_new=None, workspa
     _check(load_library().ispa_absorb_solve_lambdas(d, d_out, b, _ptr(G), _ptr(C), _ptr(W), _ptr(lambdas), _ptr(dW),
                                                     _ptr(W_new), _ptr(info), _ptr(workspace), ws_bytes,
                                                     _stream(stream)))
+
+
+ISPA_ABSORB_NO_REFINE = 1
+
+
+def ispa_absorb_solve_ex(G, C, W, lam: float, dW, info, *, lambdas=None, refine: bool = True, W_new=None,
+                         workspace=None, stream=None) -> None:
+    """ispa_absorb_solve with a per-layer lambda (``lambdas``, device float32) and the refinement optional."""
+    G3, W3 = _as3(G), _as3(W)
+    b, d, _ = G3.shape
+    d_out = W3.shape[2]
+    _expect(G3, (b, d, d), torch.float32, "G")
+    _expect(_as3(C), (b, d, d), torch.float32, "C")
+    _expect(W3, (b, d, d_out), torch.float32, "W")
+    _expect(_as3(dW), (b, d, d_out), torch.float32, "dW")
+    if W_new is not None:
+        _expect(_as3(W_new), (b, d, d_out), torch.float32, "W_new")
+    if lambdas is not None:
+        _expect(lambdas.reshape(-1), (b,), torch.float32, "lambdas")
+    _expect(info.reshape(-1), (b,), torch.int32, "info")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().ispa_absorb_solve_ex(d, d_out, b, _ptr(G), _ptr(C), _ptr(W), float(lam), _ptr(lambdas),
+                                               0 if refine else ISPA_ABSORB_NO_REFINE, _ptr(dW), _ptr(W_new),
+                                               _ptr(info), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def ispa_select_layers_below(eps, tau: float, k_max: int, selected, count, rank=None, *, stream=None) -> None:

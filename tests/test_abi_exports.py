@@ -173,3 +173,13 @@ def test_every_entry_point_has_a_python_wrapper():
     skip = {"ispa_status_string", "ispa_last_error"}
     missing = [n for n in ispa.EXPORTS if n not in skip and not callable(getattr(ispa, n, None))]
     assert missing == []
+
+
+@pytest.mark.skipif(not os.path.exists(ispa.LIB_PATH), reason="libispa.so not built")
+def test_absorb_solve_ex_validation_needs_no_gpu():
+    lib = ispa.load_library()
+    ok = 0x10000
+    bad = ispa.ISPA_E_INVALID_ARG
+    assert lib.ispa_absorb_solve_ex(128, 64, 1, ok, ok, ok, 0.01, None, 2, ok, None, ok, None, 0, None) == bad
+    assert lib.ispa_absorb_solve_ex(128, 64, 1, ok, ok, ok, -1.0, None, 0, ok, None, ok, None, 0, None) == bad
+    assert lib.ispa_absorb_solve_ex(100, 64, 1, ok, ok, ok, 0.01, None, 1, ok, None, ok, None, 0, None) == bad

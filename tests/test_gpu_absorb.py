@@ -211,3 +211,33 @@ def test_tiny_fp32_chain_end_to_end():
     e = relfro(host64(dW), ref)
     say("chain dW relfro", e)
     assert e <= TOL_DW
+
+
+@pytest.mark.parametrize("d", [256, 1536])
+def test_absorb_solve_ex_refinement_optional(d):
+    """solve_ex with refinement is ispa_absorb_solve bit for bit; without it dW is the float32 solve,
+    still inside the dW gate against the oracle (its error reported beside the refined one)."""
+    al, af = inputs.absorb_rows(21, 0, 4 * d, d, "bf16")
+    G, C, _ = gpu_gram([(al, af)], d)
+    W = torch.from_numpy(inputs.normal(21, 0, inputs.LAYER_CHUNK, inputs.T_W, (d, d)) * np.float32(d ** -0.5)).cuda()
+    ws = ispa.workspace(ispa.ispa_absorb_workspace_size(d, d, 1))
+    dW_ref, info = gpu_solve(G, C, W, 1e-2)
+    dW1 = poisoned((d, d), torch.float32)
+    dW2 = poisoned((d, d), torch.float32)
+    ispa.ispa_absorb_solve_ex(G, C, W, 1e-2, dW1, info, refine=True, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(dW1, dW_ref)
+    ispa.ispa_absorb_solve_ex(G, C, W, 1e-2, dW2, info, refine=False, workspace=ws)
+    torch.cuda.synchronize()
+    assert info.item() == 0
+    Gr, Cr = oracle.gram(al.f64, af.f64)
+    ref = oracle.ridge_solve(Gr, Cr, W.cpu().numpy().astype(np.float64), 1e-2)
+    e1, e2 = relfro(host64(dW1), ref), relfro(host64(dW2), ref)
+    say("dW relfro refined / float32 only", e1, e2)
+    assert e2 <= TOL_DW
+    # a constant lambda array is the scalar lambda, bit for bit
+    lam = torch.full((1,), 1e-2, dtype=torch.float32, device="cuda")
+    dW3 = poisoned((d, d), torch.float32)
+    ispa.ispa_absorb_solve_ex(G, C, W, 0.0, dW3, info, lambdas=lam, refine=True, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(dW3, dW_ref)
