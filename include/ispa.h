@@ -41,6 +41,11 @@
  *   workspace whose size is queried first.
  * - Calls only enqueue work on `stream` (a hipStream_t; NULL = default
  *   stream) and return; results are valid once the stream is synchronised.
+ *   The absorb solves also run R = C W on a second stream the library owns
+ *   (one per device, default priority, created with its two events on the
+ *   first solve and kept until the process ends), forked from and joined back
+ *   to `stream` with events, so the call stays ordered on `stream` and can be
+ *   captured into a graph once that first solve has run outside capture.
  * - Inputs must not alias outputs (the one exception is W_new == W).
  * - Layouts: Q, K, V and O are [tokens, heads, head_dim] contiguous, so an O
  *   buffer is also the row-major [tokens, d] matrix A with d = heads*head_dim
