@@ -11,10 +11,11 @@
 // Structure (nb = 64 column panels, right-looking):
 //   M = G + lambda I (lambda scalar or per layer)      (init kernel)
 //   R = C W in float32                                 (GEMM, on a second stream beside the factorisation)
+//   factor M_00 = L_00 L_00^T and invert L_00        (one workgroup per layer)
 //   for each panel k:
-//     factor M_kk = L_kk L_kk^T and invert L_kk       (one workgroup per layer)
 //     L_ik = M_ik L_kk^-T                             (GEMM, in place)
-//     M_ij -= L_ik L_jk^T  (lower tiles only)         (GEMM)
+//     M_ij -= L_ik L_jk^T  (lower tiles only)         (GEMM; the workgroup of the next diagonal
+//                                                      block then factors and inverts it)
 //   explicit inverse of L by recursive doubling over block ranges
 //   X = L^-T (L^-1 R)                                  (two triangular GEMMs)
 //   one refinement step: r = R - G X - lambda X in float64,
@@ -40,249 +41,6 @@ namespace {
 
 constexpr int NB = 64;  // panel width
 
-struct GemmParams {
-  const float* A;
-  const float* B;
-  const float* Cin;
-  float* D;
-  int M, N, K;
-  int lda, ldb, ldc, ldd;
-  size_t sA, sB, sC, sD;  // batch strides (elements)
-  float alpha, beta;
-  int lower_only;         // skip 64x64 tiles strictly above the diagonal
-  int kmode;              // 0 all k; 1 op(A) lower: k < m0+T; 2 op(A) upper: k >= m0; 3 op(B) lower: k >= n0
-  const int32_t* info;    // skip batch entries with info != 0 (nullable)
-  int npairs;             // grid.z = batch * npairs; pair q adds q * pA, pB, pC, pD
-  size_t pA, pB, pC, pD;
-};
-
-// D = alpha * op(A) op(B) + beta * Cin; op(A) is MxK, op(B) is KxN.
-// TA: A stored KxM (op(A) = A^T); TB: B stored NxK (op(B) = B^T).
-// T x T output tile (T = 64 or 128), 4 waves in 2x2, each (T/2)x(T/2) as blocks of
-// v_mfma_f32_32x32x2_f32.  K advances in slabs of GKS: the next slab's operands are loaded into
-// registers while the current one is multiplied from LDS (two LDS buffers, one barrier per slab),
-// so few resident workgroups still hide the load latency.  M, N multiples of T; K multiple of GKS.
-// Cin may equal D.
-constexpr int GKS = 32;
-
-template <bool TA, bool TB, int T>
-__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
-  constexpr int WB = T / 64;               // 32x32 blocks per wave per dimension
-  constexpr int NLD = T * GKS / 1024;      // float4 loads per thread per operand per slab
-  const int b = blockIdx.z / p.npairs, q = blockIdx.z % p.npairs;
-  if (p.info && p.info[b] != 0) return;
-  const int tm = blockIdx.y, tn = blockIdx.x;
-  if (p.lower_only && tm < tn) return;
-  const int m0 = tm * T, n0 = tn * T;
-  __shared__ float As[2][GKS][T + 4];  // [buffer][k][m]
-  __shared__ float Bs[2][GKS][T + 4];  // [buffer][k][n]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l32 = lane & 31, hh = lane >> 5;
-  const int wm = (wave >> 1) * (T / 2), wn = (wave & 1) * (T / 2);
-  const float* A = p.A + b * p.sA + q * p.pA;
-  const float* B = p.B + b * p.sB + q * p.pB;
-  f32x16 acc[WB][WB];
-#pragma unroll
-  for (int i = 0; i < WB; ++i)
-#pragma unroll
-    for (int j = 0; j < WB; ++j) acc[i][j] = f32x16{0};
-  const int kb = p.kmode == 2 ? m0 : (p.kmode == 3 ? n0 : 0);
-  const int ke = p.kmode == 1 ? min(p.K, m0 + T) : p.K;
-  f32x4 ra[NLD], rb[NLD];
-  auto load = [&](int k0) {
-#pragma unroll
-    for (int r = 0; r < NLD; ++r) {
-      const int t = tid + 256 * r;
-      if (!TA) {
-        const int m = t / (GKS / 4), kq = t % (GKS / 4);
-        ra[r] = *(const f32x4*)(A + (size_t)(m0 + m) * p.lda + k0 + 4 * kq);
-      } else {
-        const int k = t / (T / 4), mq = t % (T / 4);
-        ra[r] = *(const f32x4*)(A + (size_t)(k0 + k) * p.lda + m0 + 4 * mq);
-      }
-      if (TB) {
-        const int n = t / (GKS / 4), kq = t % (GKS / 4);
-        rb[r] = *(const f32x4*)(B + (size_t)(n0 + n) * p.ldb + k0 + 4 * kq);
-      } else {
-        const int k = t / (T / 4), nq = t % (T / 4);
-        rb[r] = *(const f32x4*)(B + (size_t)(k0 + k) * p.ldb + n0 + 4 * nq);
-      }
-    }
-  };
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int r = 0; r < NLD; ++r) {
-      const int t = tid + 256 * r;
-      if (!TA) {
-        const int m = t / (GKS / 4), kq = t % (GKS / 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) As[buf][4 * kq + e][m] = ra[r][e];
-      } else {
-        const int k = t / (T / 4), mq = t % (T / 4);
-        *(f32x4*)(&As[buf][k][4 * mq]) = ra[r];
-      }
-      if (TB) {
-        const int n = t / (GKS / 4), kq = t % (GKS / 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) Bs[buf][4 * kq + e][n] = rb[r][e];
-      } else {
-        const int k = t / (T / 4), nq = t % (T / 4);
-        *(f32x4*)(&Bs[buf][k][4 * nq]) = rb[r];
-      }
-    }
-  };
-  if (kb < ke) {
-    load(kb);
-    store(0);
-    __syncthreads();
-  }
-  int buf = 0;
-  for (int k0 = kb; k0 < ke; k0 += GKS) {
-    const bool more = k0 + GKS < ke;
-    if (more) load(k0 + GKS);  // in flight during the multiplies below
-    // operands of step kk + 1 are read from LDS before the multiplies of step kk are issued, so the
-    // LDS latency hides behind them (sched_barrier keeps the compiler from sinking the reads)
-    float a[2][WB], bv[2][WB];
-#pragma unroll
-    for (int i = 0; i < WB; ++i) {
-      a[0][i] = As[buf][hh][wm + 32 * i + l32];
-      bv[0][i] = Bs[buf][hh][wn + 32 * i + l32];
-    }
-#pragma unroll
-    for (int kk = 0; kk < GKS / 2; ++kk) {
-      const int c = kk & 1;
-      if (kk + 1 < GKS / 2) {
-#pragma unroll
-        for (int i = 0; i < WB; ++i) {
-          a[c ^ 1][i] = As[buf][2 * (kk + 1) + hh][wm + 32 * i + l32];
-          bv[c ^ 1][i] = Bs[buf][2 * (kk + 1) + hh][wn + 32 * i + l32];
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < WB; ++i)
-#pragma unroll
-        for (int j = 0; j < WB; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[c][i], bv[c][j], acc[i][j], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (more) store(buf ^ 1);  // the other buffer: its last readers finished before the previous barrier
-    __syncthreads();
-    buf ^= 1;
-  }
-  const float* Cin = p.Cin ? p.Cin + b * p.sC + q * p.pC : nullptr;
-  float* D = p.D + b * p.sD + q * p.pD;
-#pragma unroll
-  for (int i = 0; i < WB; ++i)
-#pragma unroll
-    for (int j = 0; j < WB; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = m0 + wm + 32 * i + 8 * (v >> 2) + 4 * hh + (v & 3);
-        const int c = n0 + wn + 32 * j + l32;
-        float x = p.alpha * acc[i][j][v];
-        if (Cin && p.beta != 0.f) x = fmaf(p.beta, Cin[(size_t)r * p.ldc + c], x);
-        D[(size_t)r * p.ldd + c] = x;
-      }
-}
-
-struct GemmDParams {
-  const float* A;      // M x K, row-major (lda)
-  const float* B;      // K x N, row-major (ldb)
-  const float* Cin;    // M x N float32 (ldc), nullable; widened to float64 in the epilogue
-  const float* X;      // M x N float32 (ldx), nullable
-  double* D64;         // nullable
-  float* D32;          // nullable
-  int M, N, K;
-  int lda, ldb, ldc, ldx, ldd;
-  size_t sA, sB, sC, sX, sD;
-  double alpha, beta, gamma;
-  const float* gamma_b;  // nullable: gamma * gamma_b[b] for batch entry b (per-layer lambda)
-  const int32_t* info;
-};
-
-typedef double f64x4 __attribute__((ext_vector_type(4)));
-
-// D = alpha * A B + beta * Cin + gamma * X with float64 accumulation of the
-// (exact) products of float32 operands, on v_mfma_f64_16x16x4_f64.  64x64 tile,
-// 4 waves of 32x32 (2x2 blocks of 16x16).  Operand layout of the f64 MFMA:
-// lane l holds A[l%16][l/16] and B[l/16][l%16]; output element v of lane l is
-// row 4v + l/16, column l%16 of its block.  M, N multiples of 64, K of 16.
-__global__ __launch_bounds__(256) void gemm_f64acc_kernel(GemmDParams p) {
-  const int b = blockIdx.z;
-  if (p.info && p.info[b] != 0) return;
-  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
-  __shared__ float As[16][64 + 4];  // [k][m]
-  __shared__ float Bs[16][64 + 4];  // [k][n]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l16 = lane & 15, g = lane >> 4;
-  const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
-  const float* A = p.A + b * p.sA;
-  const float* B = p.B + b * p.sB;
-  const double gb = p.gamma_b ? p.gamma * (double)p.gamma_b[b] : p.gamma;
-  f64x4 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f64x4{0, 0, 0, 0};
-  for (int k0 = 0; k0 < p.K; k0 += 16) {
-    {
-      const int m = tid >> 2, kq = tid & 3;
-      const f32x4 v = *(const f32x4*)(A + (size_t)(m0 + m) * p.lda + k0 + 4 * kq);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) As[4 * kq + e][m] = v[e];
-      const int k = tid >> 4, nq = tid & 15;
-      *(f32x4*)(&Bs[k][4 * nq]) = *(const f32x4*)(B + (size_t)(k0 + k) * p.ldb + n0 + 4 * nq);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      double a[2], bb[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        a[i] = (double)As[4 * kk + g][wm + 16 * i + l16];
-        bb[i] = (double)Bs[4 * kk + g][wn + 16 * i + l16];
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], bb[j], acc[i][j], 0, 0, 0);
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int r = m0 + wm + 16 * i + 4 * v + g;
-        const int c = n0 + wn + 16 * j + l16;
-        double x = p.alpha * acc[i][j][v];
-        if (p.Cin) x += p.beta * (double)p.Cin[b * p.sC + (size_t)r * p.ldc + c];
-        if (p.X) x += gb * (double)p.X[b * p.sX + (size_t)r * p.ldx + c];
-        if (p.D64) p.D64[b * p.sD + (size_t)r * p.ldd + c] = x;
-        if (p.D32) p.D32[b * p.sD + (size_t)r * p.ldd + c] = (float)x;
-      }
-}
-
-// M = G + lambda I (full matrix); info = 0.
-__global__ __launch_bounds__(256) void init_shift_kernel(const float* __restrict__ G, float* M, int d, float lambda,
-                                                         const float* __restrict__ lam_b, int32_t* info) {
-  const int b = blockIdx.y;
-  if (lam_b) lambda = lam_b[b];
-  const size_t dd = (size_t)d * d;
-  const size_t i4 = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
-  if (blockIdx.x == 0 && threadIdx.x == 0) info[b] = 0;
-  if (i4 >= dd) return;
-  f32x4 v = *(const f32x4*)(G + b * dd + i4);
-  const int row = (int)(i4 / d), col = (int)(i4 % d);
-#pragma unroll
-  for (int e = 0; e < 4; ++e)
-    if (col + e == row) v[e] += lambda;
-  *(f32x4*)(M + b * dd + i4) = v;
-}
-
 // Cholesky of the NB x NB diagonal block at (k0, k0) of each layer (lower L written in place, the
 // strict upper part of the block left as it is) and its inverse L^-1 into the same block of Linvf
 // (zeros above the diagonal).  info[b] = k0 + j + 1 if the leading minor of order k0 + j + 1 of
@@ -301,13 +59,16 @@ __device__ __forceinline__ float readlane_f(float v, int l) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
 }
 
-__global__ __launch_bounds__(256) void potrf_diag_kernel(float* M, int d, int k0, float* Linvf, int32_t* info) {
-  const int b = blockIdx.x;
-  if (info[b] != 0) return;
-  __shared__ __attribute__((aligned(16))) float Ls[NB][LSTR];  // L (zeros above the diagonal)
-  __shared__ __attribute__((aligned(16))) float Xs[NB][LSTR];  // L^-1
-  __shared__ __attribute__((aligned(16))) float Ts[32][36];    // product scratch of the doubling steps
-  __shared__ int fail_s;
+// LDS of one diagonal-block factorisation: L (zeros above the diagonal), L^-1, and the product
+// scratch of the doubling steps with the failure flag after it.
+constexpr int DIAG_LS_FLOATS = NB * LSTR, DIAG_TS_FLOATS = 32 * 36 + 4;
+
+// Body of the factorisation for layer b; called by all 256 threads of a workgroup, which must not
+// be inside a branch that differs between its waves.  Ls and Xs hold NB * LSTR floats each, Ts
+// DIAG_TS_FLOATS, all 16-byte aligned.
+__device__ __forceinline__ void potrf_diag_block(float* M, int d, int k0, float* Linvf, int32_t* info, int b,
+                                                 float (*Ls)[LSTR], float (*Xs)[LSTR], float (*Ts)[36]) {
+  int& fail_s = *(int*)&Ts[32][0];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   float* Mb = M + (size_t)b * d * d + (size_t)k0 * d + k0;
@@ -445,6 +206,278 @@ __global__ __launch_bounds__(256) void potrf_diag_kernel(float* M, int d, int k0
   }
 }
 
+__global__ __launch_bounds__(256) void potrf_diag_kernel(float* M, int d, int k0, float* Linvf, int32_t* info) {
+  const int b = blockIdx.x;
+  if (info[b] != 0) return;
+  __shared__ __attribute__((aligned(16))) float Ls[NB][LSTR];
+  __shared__ __attribute__((aligned(16))) float Xs[NB][LSTR];
+  __shared__ __attribute__((aligned(16))) float Ts[DIAG_TS_FLOATS / 36 + 1][36];
+  potrf_diag_block(M, d, k0, Linvf, info, b, Ls, Xs, Ts);
+}
+
+struct GemmParams {
+  const float* A;
+  const float* B;
+  const float* Cin;
+  float* D;
+  int M, N, K;
+  int lda, ldb, ldc, ldd;
+  size_t sA, sB, sC, sD;  // batch strides (elements)
+  float alpha, beta;
+  int lower_only;         // skip 64x64 tiles strictly above the diagonal
+  int kmode;              // 0 all k; 1 op(A) lower: k < m0+T; 2 op(A) upper: k >= m0; 3 op(B) lower: k >= n0
+  const int32_t* info;    // skip batch entries with info != 0 (nullable)
+  int npairs;             // grid.z = batch * npairs; pair q adds q * pA, pB, pC, pD
+  size_t pA, pB, pC, pD;
+  // fused look-ahead (trailing update only): the workgroup of output tile (0, 0), the next
+  // diagonal block, factors it afterwards (potrf_diag_block on block diag_k0 of diag_M)
+  float* diag_M;
+  float* diag_Linv;
+  int32_t* diag_info;
+  int diag_d, diag_k0;
+};
+
+// D = alpha * op(A) op(B) + beta * Cin; op(A) is MxK, op(B) is KxN.
+// TA: A stored KxM (op(A) = A^T); TB: B stored NxK (op(B) = B^T).
+// T x T output tile (T = 64 or 128), 4 waves in 2x2, each (T/2)x(T/2) as blocks of
+// v_mfma_f32_32x32x2_f32.  K advances in slabs of GKS: the next slab's operands are loaded into
+// registers while the current one is multiplied from LDS (two LDS buffers, one barrier per slab),
+// so few resident workgroups still hide the load latency.  M, N multiples of T; K multiple of GKS.
+// Cin may equal D.
+constexpr int GKS = 32;
+
+template <bool TA, bool TB, int T, bool DIAG = false>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
+  constexpr int WB = T / 64;               // 32x32 blocks per wave per dimension
+  constexpr int NLD = T * GKS / 1024;      // float4 loads per thread per operand per slab
+  const int b = blockIdx.z / p.npairs, q = blockIdx.z % p.npairs;
+  if (p.info && p.info[b] != 0) return;
+  const int tm = blockIdx.y, tn = blockIdx.x;
+  if (p.lower_only && tm < tn) return;
+  const int m0 = tm * T, n0 = tn * T;
+  __shared__ __attribute__((aligned(16))) float As[2][GKS][T + 4];  // [buffer][k][m]
+  __shared__ __attribute__((aligned(16))) float Bs[2][GKS][T + 4];  // [buffer][k][n]
+  static_assert(2 * GKS * (T + 4) >= DIAG_LS_FLOATS, "the diagonal factorisation reuses As and Bs");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int wm = (wave >> 1) * (T / 2), wn = (wave & 1) * (T / 2);
+  const float* A = p.A + b * p.sA + q * p.pA;
+  const float* B = p.B + b * p.sB + q * p.pB;
+  f32x16 acc[WB][WB];
+#pragma unroll
+  for (int i = 0; i < WB; ++i)
+#pragma unroll
+    for (int j = 0; j < WB; ++j) acc[i][j] = f32x16{0};
+  const int kb = p.kmode == 2 ? m0 : (p.kmode == 3 ? n0 : 0);
+  const int ke = p.kmode == 1 ? min(p.K, m0 + T) : p.K;
+  f32x4 ra[NLD], rb[NLD];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int r = 0; r < NLD; ++r) {
+      const int t = tid + 256 * r;
+      if (!TA) {
+        const int m = t / (GKS / 4), kq = t % (GKS / 4);
+        ra[r] = *(const f32x4*)(A + (size_t)(m0 + m) * p.lda + k0 + 4 * kq);
+      } else {
+        const int k = t / (T / 4), mq = t % (T / 4);
+        ra[r] = *(const f32x4*)(A + (size_t)(k0 + k) * p.lda + m0 + 4 * mq);
+      }
+      if (TB) {
+        const int n = t / (GKS / 4), kq = t % (GKS / 4);
+        rb[r] = *(const f32x4*)(B + (size_t)(n0 + n) * p.ldb + k0 + 4 * kq);
+      } else {
+        const int k = t / (T / 4), nq = t % (T / 4);
+        rb[r] = *(const f32x4*)(B + (size_t)(k0 + k) * p.ldb + n0 + 4 * nq);
+      }
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < NLD; ++r) {
+      const int t = tid + 256 * r;
+      if (!TA) {
+        const int m = t / (GKS / 4), kq = t % (GKS / 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) As[buf][4 * kq + e][m] = ra[r][e];
+      } else {
+        const int k = t / (T / 4), mq = t % (T / 4);
+        *(f32x4*)(&As[buf][k][4 * mq]) = ra[r];
+      }
+      if (TB) {
+        const int n = t / (GKS / 4), kq = t % (GKS / 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Bs[buf][4 * kq + e][n] = rb[r][e];
+      } else {
+        const int k = t / (T / 4), nq = t % (T / 4);
+        *(f32x4*)(&Bs[buf][k][4 * nq]) = rb[r];
+      }
+    }
+  };
+  if (kb < ke) {
+    load(kb);
+    store(0);
+    __syncthreads();
+  }
+  int buf = 0;
+  for (int k0 = kb; k0 < ke; k0 += GKS) {
+    const bool more = k0 + GKS < ke;
+    if (more) load(k0 + GKS);  // in flight during the multiplies below
+    // operands of step kk + 1 are read from LDS before the multiplies of step kk are issued, so the
+    // LDS latency hides behind them (sched_barrier keeps the compiler from sinking the reads)
+    float a[2][WB], bv[2][WB];
+#pragma unroll
+    for (int i = 0; i < WB; ++i) {
+      a[0][i] = As[buf][hh][wm + 32 * i + l32];
+      bv[0][i] = Bs[buf][hh][wn + 32 * i + l32];
+    }
+#pragma unroll
+    for (int kk = 0; kk < GKS / 2; ++kk) {
+      const int c = kk & 1;
+      if (kk + 1 < GKS / 2) {
+#pragma unroll
+        for (int i = 0; i < WB; ++i) {
+          a[c ^ 1][i] = As[buf][2 * (kk + 1) + hh][wm + 32 * i + l32];
+          bv[c ^ 1][i] = Bs[buf][2 * (kk + 1) + hh][wn + 32 * i + l32];
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < WB; ++i)
+#pragma unroll
+        for (int j = 0; j < WB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[c][i], bv[c][j], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (more) store(buf ^ 1);  // the other buffer: its last readers finished before the previous barrier
+    __syncthreads();
+    buf ^= 1;
+  }
+  const float* Cin = p.Cin ? p.Cin + b * p.sC + q * p.pC : nullptr;
+  float* D = p.D + b * p.sD + q * p.pD;
+#pragma unroll
+  for (int i = 0; i < WB; ++i)
+#pragma unroll
+    for (int j = 0; j < WB; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = m0 + wm + 32 * i + 8 * (v >> 2) + 4 * hh + (v & 3);
+        const int c = n0 + wn + 32 * j + l32;
+        float x = p.alpha * acc[i][j][v];
+        if (Cin && p.beta != 0.f) x = fmaf(p.beta, Cin[(size_t)r * p.ldc + c], x);
+        D[(size_t)r * p.ldd + c] = x;
+      }
+  if constexpr (DIAG) {
+    if (tm == 0 && tn == 0 && q == 0) {
+      // the tile just written holds the next diagonal block: make the stores visible to this
+      // workgroup's loads (the fence also drops stale L1 lines of the tile), then factor it in the
+      // LDS the multiply no longer needs
+      __shared__ __attribute__((aligned(16))) float Tx[DIAG_TS_FLOATS / 36 + 1][36];
+      __threadfence();
+      __syncthreads();
+      potrf_diag_block(p.diag_M, p.diag_d, p.diag_k0, p.diag_Linv, p.diag_info, b, (float(*)[LSTR]) & As[0][0][0],
+                       (float(*)[LSTR]) & Bs[0][0][0], Tx);
+    }
+  }
+}
+
+struct GemmDParams {
+  const float* A;      // M x K, row-major (lda)
+  const float* B;      // K x N, row-major (ldb)
+  const float* Cin;    // M x N float32 (ldc), nullable; widened to float64 in the epilogue
+  const float* X;      // M x N float32 (ldx), nullable
+  double* D64;         // nullable
+  float* D32;          // nullable
+  int M, N, K;
+  int lda, ldb, ldc, ldx, ldd;
+  size_t sA, sB, sC, sX, sD;
+  double alpha, beta, gamma;
+  const float* gamma_b;  // nullable: gamma * gamma_b[b] for batch entry b (per-layer lambda)
+  const int32_t* info;
+};
+
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+// D = alpha * A B + beta * Cin + gamma * X with float64 accumulation of the
+// (exact) products of float32 operands, on v_mfma_f64_16x16x4_f64.  64x64 tile,
+// 4 waves of 32x32 (2x2 blocks of 16x16).  Operand layout of the f64 MFMA:
+// lane l holds A[l%16][l/16] and B[l/16][l%16]; output element v of lane l is
+// row 4v + l/16, column l%16 of its block.  M, N multiples of 64, K of 16.
+__global__ __launch_bounds__(256) void gemm_f64acc_kernel(GemmDParams p) {
+  const int b = blockIdx.z;
+  if (p.info && p.info[b] != 0) return;
+  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  __shared__ float As[16][64 + 4];  // [k][m]
+  __shared__ float Bs[16][64 + 4];  // [k][n]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
+  const float* A = p.A + b * p.sA;
+  const float* B = p.B + b * p.sB;
+  const double gb = p.gamma_b ? p.gamma * (double)p.gamma_b[b] : p.gamma;
+  f64x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f64x4{0, 0, 0, 0};
+  for (int k0 = 0; k0 < p.K; k0 += 16) {
+    {
+      const int m = tid >> 2, kq = tid & 3;
+      const f32x4 v = *(const f32x4*)(A + (size_t)(m0 + m) * p.lda + k0 + 4 * kq);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) As[4 * kq + e][m] = v[e];
+      const int k = tid >> 4, nq = tid & 15;
+      *(f32x4*)(&Bs[k][4 * nq]) = *(const f32x4*)(B + (size_t)(k0 + k) * p.ldb + n0 + 4 * nq);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      double a[2], bb[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        a[i] = (double)As[4 * kk + g][wm + 16 * i + l16];
+        bb[i] = (double)Bs[4 * kk + g][wn + 16 * i + l16];
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], bb[j], acc[i][j], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = m0 + wm + 16 * i + 4 * v + g;
+        const int c = n0 + wn + 16 * j + l16;
+        double x = p.alpha * acc[i][j][v];
+        if (p.Cin) x += p.beta * (double)p.Cin[b * p.sC + (size_t)r * p.ldc + c];
+        if (p.X) x += gb * (double)p.X[b * p.sX + (size_t)r * p.ldx + c];
+        if (p.D64) p.D64[b * p.sD + (size_t)r * p.ldd + c] = x;
+        if (p.D32) p.D32[b * p.sD + (size_t)r * p.ldd + c] = (float)x;
+      }
+}
+
+// M = G + lambda I (full matrix); info = 0.
+__global__ __launch_bounds__(256) void init_shift_kernel(const float* __restrict__ G, float* M, int d, float lambda,
+                                                         const float* __restrict__ lam_b, int32_t* info) {
+  const int b = blockIdx.y;
+  if (lam_b) lambda = lam_b[b];
+  const size_t dd = (size_t)d * d;
+  const size_t i4 = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (blockIdx.x == 0 && threadIdx.x == 0) info[b] = 0;
+  if (i4 >= dd) return;
+  f32x4 v = *(const f32x4*)(G + b * dd + i4);
+  const int row = (int)(i4 / d), col = (int)(i4 % d);
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (col + e == row) v[e] += lambda;
+  *(f32x4*)(M + b * dd + i4) = v;
+}
+
+
 // dW = X + correction, or NaN for failed layers; W_new = W + dW for the others (W_new may be W).
 __global__ __launch_bounds__(256) void finalize_kernel(const float* W, float* dW, const float* corr, float* Wn,
                                                        size_t n, const int32_t* info) {
@@ -545,7 +578,8 @@ template <bool TA, bool TB>
 ispa_status_t gemm(hipStream_t s, int batch, int M, int N, int K, const float* A, int lda, size_t sA, const float* B,
                    int ldb, size_t sB, const float* Cin, int ldc, size_t sC, float* D, int ldd, size_t sD, float alpha,
                    float beta, bool lower_only, const int32_t* info, int kmode = 0, int npairs = 1,
-                   size_t pA = 0, size_t pB = 0, size_t pC = 0, size_t pD = 0) {
+                   size_t pA = 0, size_t pB = 0, size_t pC = 0, size_t pD = 0, float* diag_M = nullptr,
+                   float* diag_Linv = nullptr, int32_t* diag_info = nullptr, int diag_d = 0, int diag_k0 = 0) {
   if (M <= 0 || N <= 0 || K <= 0) return ISPA_OK;
   if (K % GKS != 0) {
     set_error("internal: GEMM depth not a multiple of 32");
@@ -562,9 +596,24 @@ ispa_status_t gemm(hipStream_t s, int batch, int M, int N, int K, const float* A
   p.info = info;
   p.npairs = npairs;
   p.pA = pA; p.pB = pB; p.pC = pC; p.pD = pD;
+  p.diag_M = diag_M; p.diag_Linv = diag_Linv; p.diag_info = diag_info;
+  p.diag_d = diag_d; p.diag_k0 = diag_k0;
   // large products use 128x128 tiles (half the operand traffic per FLOP) when they still fill the GPU
   const int z = batch * npairs;
   const bool big = M % 128 == 0 && N % 128 == 0 && (size_t)(M / 128) * (N / 128) * z >= 192;
+  if constexpr (!TA && TB) {
+    if (diag_M) {
+      if (npairs != 1) {
+        set_error("internal: fused diagonal factorisation with paired products");
+        return ISPA_E_INVALID_ARG;
+      }
+      if (big)
+        hipLaunchKernelGGL((gemm_f32_kernel<TA, TB, 128, true>), dim3(N / 128, M / 128, z), dim3(256), 0, s, p);
+      else
+        hipLaunchKernelGGL((gemm_f32_kernel<TA, TB, 64, true>), dim3(N / 64, M / 64, z), dim3(256), 0, s, p);
+      return hip_check(hipGetLastError(), "gemm_f32_kernel launch");
+    }
+  }
   if (big)
     hipLaunchKernelGGL((gemm_f32_kernel<TA, TB, 128>), dim3(N / 128, M / 128, z), dim3(256), 0, s, p);
   else
@@ -721,23 +770,25 @@ ispa_status_t launch_absorb(int32_t d, int32_t d_out, int32_t batch, const float
   // solution like the float32 statistics themselves do)
   ISPA_TRY((gemm<false, false>(s2, batch, d, d_out, d, C, d, dd, W, d_out, dn, nullptr, 0, 0, Rb, d_out, dn, 1.f,
                                0.f, false, nullptr)));
-  // Cholesky, right-looking by 64-column panels (one stream: a wait on an event recorded on another
-  // stream costs ~15 us of latency here, more than a look-ahead split of the trailing update saves)
-  for (int k = 0; k < nblk; ++k) {
+  // Cholesky, right-looking by 64-column panels, with a one-panel look-ahead inside the trailing
+  // update: the workgroup that updates the next diagonal block factors it right away, while the
+  // other workgroups finish the update, so the factorisation (a latency-bound chain of 64 pivot
+  // steps) overlaps the update instead of following it.  (One stream: a wait on an event recorded
+  // on another stream costs ~15 us of latency here.)
+  hipLaunchKernelGGL(potrf_diag_kernel, dim3(batch), dim3(256), 0, s, M, d, 0, Linvf, info);
+  ISPA_TRY(hip_check(hipGetLastError(), "potrf_diag_kernel launch"));
+  for (int k = 0; k + 1 < nblk; ++k) {
     const int k0 = k * NB;
-    hipLaunchKernelGGL(potrf_diag_kernel, dim3(batch), dim3(256), 0, s, M, d, k0, Linvf, info);
-    ISPA_TRY(hip_check(hipGetLastError(), "potrf_diag_kernel launch"));
     const int rest = d - k0 - NB;
-    if (rest <= 0) break;
     float* panel = M + (size_t)(k0 + NB) * d + k0;
     const float* Lkk_inv = Linvf + (size_t)k0 * d + k0;
     // L_ik = M_ik L_kk^-T (in place)
     ISPA_TRY((gemm<false, true>(s, batch, rest, NB, NB, panel, d, dd, Lkk_inv, d, dd, nullptr, 0, 0, panel, d, dd,
                                 1.f, 0.f, false, info)));
-    // trailing update, lower tiles
+    // trailing update, lower tiles; tile (0, 0) is diagonal block k + 1, factored in the same launch
     float* trail = M + (size_t)(k0 + NB) * d + k0 + NB;
     ISPA_TRY((gemm<false, true>(s, batch, rest, rest, NB, panel, d, dd, panel, d, dd, trail, d, dd, trail, d, dd, -1.f,
-                                1.f, true, info)));
+                                1.f, true, info, 0, 1, 0, 0, 0, 0, M, Linvf, info, d, k0 + NB)));
   }
   // join: R = C W is done before the solve reads it
   ISPA_TRY(hip_check(hipEventRecord(ev[1], s2), "hipEventRecord"));
