@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decomposable-attn TFLOP/s (% bf16 MFMA peak) + absorb ms/layer, 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3   # MI355X fp32 (vector and MFMA)
 PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA
 # fp8-key attention: half its FLOPs (S = K Q^T) at the fp8 rate, half (P V) at the bf16 rate
 PEAK_FP8K_TFLOPS = round(1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS), 1)
@@ -243,6 +244,9 @@ def main():
 
     attn_flops = cfg.attn_flops()
     step_attn_flops = attn_flops * cfg.n_chunks
+    gram_flops = 3.0 * nq * d * d
+    solve_flops = 13.0 / 3.0 * float(d) ** 3
+    solve_bytes = 16.0 * d * d
     attn_avg = float(np.mean(attn_ms))
     achieved = attn_flops / (attn_avg * 1e-3) / 1e12
     value = step_attn_flops / (ms_per_step * 1e-3) / 1e12
@@ -315,8 +319,18 @@ def main():
             "tflops": round(attn_flops / (float(np.median(seg_ms)) * 1e-3) / 1e12, 2),
         },
         "gram_ms_per_chunk": round(float(np.mean(gram_ms)), 4),
+        # algorithmic Gram work: 2 d^2 per row for C plus d^2 per row for the symmetric G
+        "gram_tflops": round(gram_flops / (float(np.mean(gram_ms)) * 1e-3) / 1e12, 2),
+        "gram_pct_bf16_peak": round(100 * gram_flops / (float(np.mean(gram_ms)) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                                    2),
         "absorb_ms_per_layer": round(float(np.mean(solve_ms)), 4),
         "absorb_ms_per_layer_no_refine": round(float(np.median(norefine_ms)), 4),
+        # algorithmic solve work 13/3 d^3 (factor d^3/3, R = C W 2 d^3, two triangular solves 2 d^3) and its
+        # compulsory bytes (read G, C, W, write dW: 16 d^2), against the measured absorb time
+        "absorb_tflops": round(solve_flops / (float(np.mean(solve_ms)) * 1e-3) / 1e12, 3),
+        "absorb_pct_fp32_peak": round(100 * solve_flops / (float(np.mean(solve_ms)) * 1e-3) / 1e12
+                                      / PEAK_FP32_TFLOPS, 2),
+        "absorb_gbps": round(solve_bytes / (float(np.mean(solve_ms)) * 1e-3) / 1e9, 1),
         "roofline": {
             "bound": "mfma",
             "kernel": "attn_bf16_kernel<128, 8, 1, 128, false, false> (ispa_decomp_attn)",

@@ -157,6 +157,42 @@ def test_not_positive_definite_reports_info():
     assert torch.equal(Wn, W)  # untouched
 
 
+@pytest.mark.parametrize("d,bad_col", [(64, 40), (256, 200), (384, 70)])
+def test_batched_solve_with_a_failing_layer(d, bad_col):
+    """Three layers, the middle one singular at column bad_col (lambda = 0 and an all-zero column of
+    its A_loc): info names that column for it alone, its dW is NaN and W_new untouched, and the other
+    two layers match the oracle.  The failing pivot lies in the first diagonal block (d = 64, where
+    the factorisation is one block) or in a later block, which is factored inside the launch that
+    applies the previous panel's trailing update."""
+    Gs, Cs, Ws, refs = [], [], [], []
+    for layer in range(3):
+        al, af = inputs.absorb_rows(12, layer, max(4 * d, 600), d, "f32")
+        raw = al.raw.copy()
+        if layer == 1:
+            raw[:, bad_col] = 0
+        Gr, Cr = oracle.gram(raw.astype(np.float64), af.f64)
+        W = inputs.normal(12, layer, inputs.LAYER_CHUNK, inputs.T_W, (d, d)) * np.float32(d ** -0.5)
+        Gs.append(Gr.astype(np.float32))
+        Cs.append(Cr.astype(np.float32))
+        Ws.append(W)
+        refs.append(None if layer == 1 else
+                    oracle.ridge_solve(Gs[-1].astype(np.float64), Cs[-1].astype(np.float64), W.astype(np.float64),
+                                       0.0))
+    G = torch.from_numpy(np.stack(Gs)).cuda()
+    C = torch.from_numpy(np.stack(Cs)).cuda()
+    W = torch.from_numpy(np.stack(Ws)).cuda()
+    Wn = W.clone()
+    dW, info = gpu_solve(G, C, W, 0.0, W_new=Wn)
+    assert info.cpu().tolist() == [0, bad_col + 1, 0]
+    assert torch.all(torch.isnan(dW[1])).item()
+    assert torch.equal(Wn[1], W[1])
+    for i in (0, 2):
+        e = relfro(host64(dW[i]), refs[i])
+        say("layer", i, "dW relfro", e)
+        assert e <= TOL_DW
+        assert torch.equal(Wn[i], W[i] + dW[i])
+
+
 def test_reconstruction_error_parity():
     d, b = 256, 3
     Gs, Cs, Qs, Ws, eps_ref = [], [], [], [], []
