@@ -8,8 +8,9 @@
 // exact stored operands (same value; no rounding of A_full - A_loc).
 //
 // bf16 design: a workgroup owns a 128x128 output tile (I, J) and a range of
-// rows.  Per 32-row stage it stages A_loc[:, I], A_loc[:, J], A_full[:, J]
-// (and A_full[:, I] when Q_ff is wanted) row-major in LDS, straight from
+// rows.  Per 32-row stage (three stages in flight) it stages A_loc[:, I],
+// A_loc[:, J], A_full[:, J] (and A_full[:, I] when Q_ff is wanted) row-major
+// in LDS, straight from
 // global memory (buffer loads into LDS, 16-byte chunks XOR-swizzled by row);
 // MFMA operands need 8 consecutive rows at one column and come from two
 // transposing LDS reads (ds_read_b64_tr_b16).  The A_loc[:, I] operand feeds
@@ -23,7 +24,7 @@
 namespace ispa {
 namespace {
 
-constexpr int GT = 128;      // output tile edge
+constexpr int GT = 128;      // output tile J extent (and the I extent of the small tile)
 constexpr int GBK = 32;      // rows per stage
 
 // Slot of 16-byte chunk c of staged row r: c ^ gram_swizzle(r).  Each 32-lane
@@ -40,33 +41,47 @@ struct GramParams {
   float* Q;
   int64_t n_rows;
   int d;
-  int tiles_per_dim;
+  int tiles_j;  // output tiles along J (d / 128); tile t is (t / tiles_j, t % tiles_j)
   int64_t rows_per_split;
   int accumulate;
   int direct;
   size_t slab;  // elements per partial matrix (d*d) when !direct
 };
 
-template <bool QFF>
-__global__ __launch_bounds__(256, 2) void gram_bf16_kernel(GramParams p) {
+// Staged matrix m of a stage: 0 A_loc[:, I] and 3 A_full[:, I] (TI columns), 1 A_loc[:, J] and
+// 2 A_full[:, J] (GT columns); each GBK rows, row-major, stored one after the other.
+template <int TI>
+__host__ __device__ constexpr int gram_width(int m) { return (m == 0 || m == 3) ? TI : GT; }
+template <int TI>
+__host__ __device__ constexpr int gram_moff(int m) {  // element offset of matrix m in a stage
+  return m == 0 ? 0 : gram_moff<TI>(m - 1) + GBK * gram_width<TI>(m - 1);
+}
+template <int TI>
+__host__ __device__ constexpr int gram_mloads(int m) { return GBK * gram_width<TI>(m) / 512; }  // 1 KB loads
+
+// TI = I extent of the output tile (128: 4 waves, two workgroups per CU; 256: 8 waves, one per CU,
+// a third less operand traffic per product).  Waves sit in a (TI / 64) x 2 grid of 64 x 64 tiles.
+template <bool QFF, int TI>
+__global__ __launch_bounds__(TI * 2, (TI == 128 && !QFF) ? 2 : 1) void gram_bf16_kernel(GramParams p) {
+  constexpr int NWV = TI / 32;      // waves
   constexpr int NM = QFF ? 4 : 3;   // staged matrices: A_loc[:,I], A_loc[:,J], A_full[:,J], [A_full[:,I]]
-  constexpr int CPR = GT / 8;       // 16-byte chunks per staged row
-  constexpr int RPW = 64 / CPR;     // rows per wave load (1 KB)
-  constexpr int WLM = GBK / RPW;    // wave loads per matrix per stage
-  constexpr int WLW = NM * WLM / 4; // wave loads per wave per stage
-  static_assert(WLW * 4 == NM * WLM, "stage loads must split over 4 waves");
-  // two stage buffers as distinct arrays (see the attention kernel: lets the
-  // compiler overlap the next stage's loads with this stage's reads)
-  __shared__ __attribute__((aligned(1024))) uint16_t s0[NM][GBK * GT];
-  __shared__ __attribute__((aligned(1024))) uint16_t s1[NM][GBK * GT];
+  constexpr int SS = gram_moff<TI>(NM);  // elements per stage
+  constexpr int NLD = gram_moff<TI>(NM) / 512;  // 1 KB wave loads per stage
+  constexpr int WLW = NLD / NWV;    // wave loads per wave per stage
+  static_assert(WLW * NWV == NLD, "stage loads must split over the waves");
+  // three stage buffers as distinct arrays (see the attention kernel: lets the
+  // compiler overlap the next stages' loads with this stage's reads)
+  __shared__ __attribute__((aligned(1024))) uint16_t s0[SS];
+  __shared__ __attribute__((aligned(1024))) uint16_t s1[SS];
+  __shared__ __attribute__((aligned(1024))) uint16_t s2[SS];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: buffer choice stays scalar
   const int l32 = lane & 31, hh = lane >> 5;
   const int tile = blockIdx.x;
   const int split = blockIdx.y;
-  const int ti = tile / p.tiles_per_dim, tj = tile % p.tiles_per_dim;
-  const int I0 = ti * GT, J0 = tj * GT;
+  const int ti = tile / p.tiles_j, tj = tile % p.tiles_j;
+  const int I0 = ti * TI, J0 = tj * GT;
   const int64_t r_begin = (int64_t)split * p.rows_per_split;
   const int64_t r_end = min(p.n_rows, r_begin + p.rows_per_split);
   const int nst = r_end > r_begin ? (int)((r_end - r_begin + GBK - 1) / GBK) : 0;
@@ -78,23 +93,30 @@ __global__ __launch_bounds__(256, 2) void gram_bf16_kernel(GramParams p) {
   const rsrc_t rl = make_rsrc(p.Al + r_begin * p.d, span);
   const rsrc_t rf = make_rsrc(p.Af + r_begin * p.d, span);
 
-  // this wave's stage loads: wave load g = wave + 4j covers matrix g / WLM, rows (g % WLM) * RPW ..
+  // this wave's stage loads: wave load g = wave + NWV*j covers load (g - first load of its matrix)
+  // of matrix m: 512 / width rows of it
   uint32_t gofs[WLW];
+  int lmat[WLW], ldst[WLW];
 #pragma unroll
   for (int j = 0; j < WLW; ++j) {
-    const int g = wave + 4 * j, mtx = g / WLM;
-    const int rr = (g % WLM) * RPW + lane / CPR;
-    const int chunk = (lane % CPR) ^ gram_swizzle(rr);
+    const int g = wave + NWV * j;
+    int mtx = 0;
+#pragma unroll
+    for (int m = 1; m < NM; ++m)
+      if (g >= gram_moff<TI>(m) / 512) mtx = m;
+    const int w = gram_width<TI>(mtx), cpr = w / 8, rpw = 64 / cpr;
+    const int li = g - gram_moff<TI>(mtx) / 512;
+    const int rr = li * rpw + lane / cpr;
+    const int chunk = (lane % cpr) ^ gram_swizzle(rr);
     const int col0 = (mtx == 0 || mtx == 3) ? I0 : J0;
     gofs[j] = (uint32_t)rr * row_bytes + (uint32_t)(col0 + chunk * 8) * 2u;
+    lmat[j] = mtx;
+    ldst[j] = gram_moff<TI>(mtx) + li * 512;
   }
-  auto load_stage = [&](int st, uint16_t (*buf)[GBK * GT]) {
+  auto load_stage = [&](int st, uint16_t* buf) {
     const uint32_t sb = (uint32_t)(st * GBK) * row_bytes;
 #pragma unroll
-    for (int j = 0; j < WLW; ++j) {
-      const int g = wave + 4 * j, mtx = g / WLM;
-      load_to_lds(mtx <= 1 ? rl : rf, buf[mtx] + (g % WLM) * RPW * GT, gofs[j] + sb);
-    }
+    for (int j = 0; j < WLW; ++j) load_to_lds(lmat[j] <= 1 ? rl : rf, buf + ldst[j], gofs[j] + sb);
   };
 
   // Operand for columns xb .. xb+31 of a staged [32 rows][128 cols] tile and rows 16ks .. 16ks+15:
@@ -109,12 +131,13 @@ __global__ __launch_bounds__(256, 2) void gram_bf16_kernel(GramParams p) {
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
     const int ci = wi + 32 * x + tcol, cj = wj + 32 * x + tcol;
-    offI[x] = trow * GT + (((ci >> 3) ^ gram_swizzle(trow)) << 3) + (ci & 7);
+    offI[x] = trow * TI + (((ci >> 3) ^ gram_swizzle(trow)) << 3) + (ci & 7);
     offJ[x] = trow * GT + (((cj >> 3) ^ gram_swizzle(trow)) << 3) + (cj & 7);
   }
-  auto frag = [&](const uint16_t* t, int off, int ks) {
-    const uint16_t* q = t + off + 16 * ks * GT;
-    const u32x2 a = lds_read_tr(q), b = lds_read_tr(q + 8 * GT);
+  // rows 16ks + 8*(j/4) + 4hh + j%4 of the matrix at t, w columns wide
+  auto frag = [&](const uint16_t* t, int off, int ks, int w) {
+    const uint16_t* q = t + off + 16 * ks * w;
+    const u32x2 a = lds_read_tr(q), b = lds_read_tr(q + 8 * w);
     return __builtin_bit_cast(bf16x8, u32x4{a.x, a.y, b.x, b.y});
   };
 
@@ -128,16 +151,16 @@ __global__ __launch_bounds__(256, 2) void gram_bf16_kernel(GramParams p) {
       accQ[a][b] = f32x16{0};
     }
 
-  auto compute = [&](uint16_t (*buf)[GBK * GT]) {
+  auto compute = [&](const uint16_t* buf) {
 #pragma unroll
     for (int ks = 0; ks < GBK / 16; ++ks) {
       bf16x8 aI[2], bJ[2], fJ[2], fI[2];
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
-        aI[b] = frag(buf[0], offI[b], ks);
-        bJ[b] = frag(buf[1], offJ[b], ks);
-        fJ[b] = frag(buf[2], offJ[b], ks);
-        if (QFF) fI[b] = frag(buf[NM - 1], offI[b], ks);
+        aI[b] = frag(buf + gram_moff<TI>(0), offI[b], ks, TI);
+        bJ[b] = frag(buf + gram_moff<TI>(1), offJ[b], ks, GT);
+        fJ[b] = frag(buf + gram_moff<TI>(2), offJ[b], ks, GT);
+        if (QFF) fI[b] = frag(buf + gram_moff<TI>(3), offI[b], ks, TI);
       }
 #pragma unroll
       for (int a = 0; a < 2; ++a)
@@ -150,20 +173,33 @@ __global__ __launch_bounds__(256, 2) void gram_bf16_kernel(GramParams p) {
     }
   };
 
-  // Stages past r_end read as zeros, so the stage count is rounded up to even and the loop
-  // body (two stages, one per buffer) has no early exit.
-  const int nst2 = (nst + 1) & ~1;
-  if (nst2 > 0) load_stage(0, s0);
-  __builtin_amdgcn_s_waitcnt(0);
+  // Stages past r_end read as zeros, so the stage count is rounded up to a multiple of three and
+  // the loop body (three stages, one per buffer) has no early exit.  Stage st + 2 is in flight
+  // while stage st is multiplied; each wait leaves the newest stage's loads outstanding (vmcnt
+  // counts this wave's loads, which complete in order).
+  constexpr int WAIT_OLDER = 0xF70 | (WLW & 15) | ((WLW >> 4) << 14);  // vmcnt(WLW); expcnt, lgkmcnt free
+  const int nst3 = (nst + 2) / 3 * 3;
+  if (nst3 > 0) {
+    load_stage(0, s0);
+    load_stage(1, s1);
+  }
+  __builtin_amdgcn_s_waitcnt(WAIT_OLDER);
   __syncthreads();
-  for (int st = 0; st < nst2; st += 2) {
-    load_stage(st + 1, s1);
+  for (int st = 0; st < nst3; st += 3) {
+    load_stage(st + 2, s2);
     compute(s0);
-    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_waitcnt(WAIT_OLDER);
     __syncthreads();
-    if (st + 2 < nst2) load_stage(st + 2, s0);
+    const bool more = st + 3 < nst3;
+    if (more) load_stage(st + 3, s0);
     compute(s1);
-    __builtin_amdgcn_s_waitcnt(0);
+    if (more) __builtin_amdgcn_s_waitcnt(WAIT_OLDER);
+    else __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (more) load_stage(st + 4, s1);
+    compute(s2);
+    if (more) __builtin_amdgcn_s_waitcnt(WAIT_OLDER);
+    else __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
@@ -294,10 +330,17 @@ int64_t gram_block_rows(int d) {
   return (r / GBK) * GBK;
 }
 
+// I extent of the output tile: 256 where d allows it and its tiles fit one round of the 256 CUs
+// (with split rows); for larger d the 4-wave 128 tiles pack the rounds better (measured at d = 5120:
+// 0.47 ms against 0.49)
+int gram_ti(int d) { return (d % 256 == 0 && (d / 256) * (d / GT) <= 256) ? 256 : 128; }
+
 int gram_splits(int64_t n_rows, int d) {
-  const int tiles = (d / GT) * (d / GT);
-  // aim for about two resident workgroups per CU (256 CUs), at least 256 rows per split
-  int s = (512 + tiles - 1) / tiles;
+  const int ti = gram_ti(d);
+  const int tiles = (d / ti) * (d / GT);
+  // 4-wave tiles: about two resident workgroups per CU (256 CUs); 8-wave tiles (one per CU): the
+  // most splits that still fit one round.  At least 256 rows per split.
+  int s = ti == 128 ? (512 + tiles - 1) / tiles : (tiles >= 256 ? 1 : 256 / tiles);
   const int64_t max_s = std::max<int64_t>(1, n_rows / 256);
   if (s > max_s) s = (int)max_s;
   if (s > 8) s = 8;
@@ -344,7 +387,8 @@ ispa_status_t launch_gram(int64_t n_rows, int32_t d, int32_t dtype, const void* 
     p.Af = (const uint16_t*)A_full + r0 * d;
     p.n_rows = nr;
     p.d = d;
-    p.tiles_per_dim = d / GT;
+    const int ti = gram_ti(d);
+    p.tiles_j = d / GT;
     p.accumulate = acc;
     p.slab = (size_t)d * d;
     const int64_t per = (nr + splits - 1) / splits;
@@ -360,11 +404,18 @@ ispa_status_t launch_gram(int64_t n_rows, int32_t d, int32_t dtype, const void* 
       p.C = nullptr;
       p.Q = nullptr;
     }
-    const dim3 grid(p.tiles_per_dim * p.tiles_per_dim, splits), block(256);
-    if (Qff)
-      hipLaunchKernelGGL((gram_bf16_kernel<true>), grid, block, 0, s, p);
-    else
-      hipLaunchKernelGGL((gram_bf16_kernel<false>), grid, block, 0, s, p);
+    const dim3 grid((d / ti) * p.tiles_j, splits), block(2 * ti);
+    if (ti == 256) {
+      if (Qff)
+        hipLaunchKernelGGL((gram_bf16_kernel<true, 256>), grid, block, 0, s, p);
+      else
+        hipLaunchKernelGGL((gram_bf16_kernel<false, 256>), grid, block, 0, s, p);
+    } else {
+      if (Qff)
+        hipLaunchKernelGGL((gram_bf16_kernel<true, 128>), grid, block, 0, s, p);
+      else
+        hipLaunchKernelGGL((gram_bf16_kernel<false, 128>), grid, block, 0, s, p);
+    }
     ispa_status_t st = hip_check(hipGetLastError(), "gram_bf16_kernel launch");
     if (st != ISPA_OK) return st;
     if (!p.direct) {
