@@ -460,9 +460,10 @@ __global__ __launch_bounds__(256) void gemm_f64acc_kernel(GemmDParams p) {
       }
 }
 
-// M = G + lambda I (full matrix); info = 0.
-__global__ __launch_bounds__(256) void init_shift_kernel(const float* __restrict__ G, float* M, int d, float lambda,
-                                                         const float* __restrict__ lam_b, int32_t* info) {
+// M = G + lambda I (full matrix); L^-1 = 0; info = 0.
+__global__ __launch_bounds__(256) void init_shift_kernel(const float* __restrict__ G, float* M, float* Linvf, int d,
+                                                         float lambda, const float* __restrict__ lam_b,
+                                                         int32_t* info) {
   const int b = blockIdx.y;
   if (lam_b) lambda = lam_b[b];
   const size_t dd = (size_t)d * d;
@@ -475,6 +476,9 @@ __global__ __launch_bounds__(256) void init_shift_kernel(const float* __restrict
   for (int e = 0; e < 4; ++e)
     if (col + e == row) v[e] += lambda;
   *(f32x4*)(M + b * dd + i4) = v;
+  // L^-1 is only ever written on and below its diagonal blocks, while the triangular products read
+  // whole 128 x 128 tiles of it: the part above must be zero, whatever the workspace held before
+  *(f32x4*)(Linvf + b * dd + i4) = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
 
@@ -761,8 +765,8 @@ ispa_status_t launch_absorb(int32_t d, int32_t d_out, int32_t batch, const float
   hipStream_t s2 = aux->s2;
   hipEvent_t* ev = aux->ev.data();  // [0] fork, [1] join
 
-  hipLaunchKernelGGL(init_shift_kernel, dim3((unsigned)((dd / 4 + 255) / 256), batch), dim3(256), 0, s, G, M, d,
-                     lambda, lam_b, info);
+  hipLaunchKernelGGL(init_shift_kernel, dim3((unsigned)((dd / 4 + 255) / 256), batch), dim3(256), 0, s, G, M, Linvf,
+                     d, lambda, lam_b, info);
   ISPA_TRY(hip_check(hipGetLastError(), "init_shift_kernel launch"));
   ISPA_TRY(hip_check(hipEventRecord(ev[0], s), "hipEventRecord"));
   ISPA_TRY(hip_check(hipStreamWaitEvent(s2, ev[0], 0), "hipStreamWaitEvent"));

@@ -23,6 +23,16 @@ def poisoned(shape, dtype) -> torch.Tensor:
     return torch.full(shape, float("nan"), dtype=dtype, device="cuda")
 
 
+def nan_workspace(nbytes: int):
+    """A caller workspace whose previous contents are NaN (None when nbytes is 0): a kernel that reads
+    any part of it before writing that part shows in the results."""
+    from kv_cache_absorption_ispa_amd import ispa
+    ws = ispa.workspace(nbytes)
+    if ws is not None:
+        ws[: nbytes // 4 * 4].view(torch.float32).fill_(float("nan"))
+    return ws
+
+
 def maxabs(a, b) -> float:
     d = np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64))
     return float(np.nanmax(d)) if not np.isnan(d).any() else float("inf")

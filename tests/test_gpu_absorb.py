@@ -11,7 +11,7 @@ import torch
 import oracle
 from kv_cache_absorption_ispa_amd import inputs
 from kv_cache_absorption_ispa_amd import ispa
-from tests.gpu_util import TOL_DW, dev, host64, poisoned, relfro, say
+from tests.gpu_util import TOL_DW, dev, host64, nan_workspace, poisoned, relfro, say
 
 pytestmark = pytest.mark.gpu
 
@@ -26,7 +26,7 @@ def gpu_gram(chunks, d, qff=False):
     Q = poisoned((d, d), torch.float32) if qff else None
     for i, (al, af) in enumerate(chunks):
         a_loc, a_full = dev(al), dev(af)
-        ws = ispa.workspace(ispa.ispa_gram_workspace_size(a_loc.shape[0], d, a_loc.dtype))
+        ws = nan_workspace(ispa.ispa_gram_workspace_size(a_loc.shape[0], d, a_loc.dtype))
         ispa.ispa_gram_accum(a_loc, a_full, G, C, Q, accumulate=i > 0, workspace=ws)
     torch.cuda.synchronize()
     return G, C, Q
@@ -44,7 +44,7 @@ def gpu_solve(G, C, W, lam, W_new=None):
     d_out = W.shape[-1]
     dW = poisoned(W.shape, torch.float32)
     info = torch.full((b,), -7, dtype=torch.int32, device="cuda")
-    ws = ispa.workspace(ispa.ispa_absorb_workspace_size(d, d_out, b))
+    ws = nan_workspace(ispa.ispa_absorb_workspace_size(d, d_out, b))
     ispa.ispa_absorb_solve(G, C, W, lam, dW, info, W_new=W_new, workspace=ws)
     torch.cuda.synchronize()
     return dW, info
@@ -193,6 +193,44 @@ def test_batched_solve_with_a_failing_layer(d, bad_col):
         assert torch.equal(Wn[i], W[i] + dW[i])
 
 
+@pytest.mark.parametrize("d,batch", [(384, 1), (1536, 4)])
+def test_refinement_reaches_the_float64_solve(d, batch):
+    """W is a column permutation scaled by powers of two, so R = C W is exact in float32 and the only
+    float32 error left is the factorisation's.  At lambda = 0 (cond ~4e4 at d = 384, ~2e5 at d = 1536)
+    the float32 solve is off by ~1e-4; the refinement step (float64-accumulated residual) must bring
+    dW to the float64 solve of the same float32 statistics.  The batched d = 1536 case multiplies by
+    L^-1 on 128 x 128 tiles, which also read the part above its diagonal blocks (it must be zero
+    whatever the workspace held: the workspaces here start as NaN); the single d = 384 one on 64 x 64."""
+    Gs, Cs, Ws, refs = [], [], [], []
+    for layer in range(batch):
+        al, af = inputs.absorb_rows(12, layer, max(4 * d, 600), d, "f32")
+        Gr, Cr = oracle.gram(al.f64, af.f64)
+        perm = np.random.default_rng(layer).permutation(d)
+        W = np.zeros((d, d), np.float32)
+        W[perm, np.arange(d)] = np.float32(2.0) ** (np.arange(d) % 5 - 2)
+        Gs.append(Gr.astype(np.float32))
+        Cs.append(Cr.astype(np.float32))
+        Ws.append(W)
+        refs.append(oracle.ridge_solve(Gs[-1].astype(np.float64), Cs[-1].astype(np.float64), W.astype(np.float64),
+                                       0.0))
+    G = torch.from_numpy(np.stack(Gs)).cuda()
+    C = torch.from_numpy(np.stack(Cs)).cuda()
+    W = torch.from_numpy(np.stack(Ws)).cuda()
+    ws = nan_workspace(ispa.ispa_absorb_workspace_size(d, d, batch))
+    info = torch.full((batch,), -7, dtype=torch.int32, device="cuda")
+    dW1 = poisoned((batch, d, d), torch.float32)
+    dW2 = poisoned((batch, d, d), torch.float32)
+    ispa.ispa_absorb_solve_ex(G, C, W, 0.0, dW1, info, refine=True, workspace=ws)
+    ispa.ispa_absorb_solve_ex(G, C, W, 0.0, dW2, info, refine=False, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.all(info == 0).item()
+    for i in range(batch):
+        e1, e2 = relfro(host64(dW1[i]), refs[i]), relfro(host64(dW2[i]), refs[i])
+        say("layer", i, "dW relfro refined / float32 only", e1, e2)
+        assert e2 >= 3e-5  # the float32 solve is measurably off at this conditioning
+        assert e1 <= 1e-5 and e1 <= e2 / 10
+
+
 def test_reconstruction_error_parity():
     d, b = 256, 3
     Gs, Cs, Qs, Ws, eps_ref = [], [], [], [], []
@@ -212,7 +250,7 @@ def test_reconstruction_error_parity():
     assert torch.all(info == 0).item()
     ea = torch.empty(b, dtype=torch.float64, device="cuda")
     er = torch.empty(b, dtype=torch.float64, device="cuda")
-    ws = ispa.workspace(ispa.ispa_eps_workspace_size(d, d, b))
+    ws = nan_workspace(ispa.ispa_eps_workspace_size(d, d, b))
     ispa.ispa_layer_eps(G, C, Q, W, dW, 1e-2, ea, er, workspace=ws)
     torch.cuda.synchronize()
     for i in range(b):
@@ -256,7 +294,7 @@ def test_absorb_solve_ex_refinement_optional(d):
     al, af = inputs.absorb_rows(21, 0, 4 * d, d, "bf16")
     G, C, _ = gpu_gram([(al, af)], d)
     W = torch.from_numpy(inputs.normal(21, 0, inputs.LAYER_CHUNK, inputs.T_W, (d, d)) * np.float32(d ** -0.5)).cuda()
-    ws = ispa.workspace(ispa.ispa_absorb_workspace_size(d, d, 1))
+    ws = nan_workspace(ispa.ispa_absorb_workspace_size(d, d, 1))
     dW_ref, info = gpu_solve(G, C, W, 1e-2)
     dW1 = poisoned((d, d), torch.float32)
     dW2 = poisoned((d, d), torch.float32)

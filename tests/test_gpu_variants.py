@@ -10,7 +10,7 @@ import torch
 import oracle
 from kv_cache_absorption_ispa_amd import inputs, ispa
 from kv_cache_absorption_ispa_amd.stack import LayerStack
-from tests.gpu_util import TOL_DW, dev, host64, poisoned, relfro, say
+from tests.gpu_util import TOL_DW, dev, host64, nan_workspace, poisoned, relfro, say
 from tests.test_gpu_absorb import gpu_gram, gpu_solve
 
 pytestmark = pytest.mark.gpu
@@ -64,7 +64,8 @@ def test_fit_error_before_the_fit_and_on_held_out_rows():
     ispa.ispa_fit_error(G, C, Q, W, dWg, ea, er)
     _, gen = _eps(ea, er)
     ea2, er2 = torch.empty_like(ea), torch.empty_like(er)
-    ispa.ispa_layer_eps(G, C, Q, W, dWg, 1e-2, ea2, er2, workspace=ispa.workspace(ispa.ispa_eps_workspace_size(D, D, b)))
+    ispa.ispa_layer_eps(G, C, Q, W, dWg, 1e-2, ea2, er2,
+                        workspace=nan_workspace(ispa.ispa_eps_workspace_size(D, D, b)))
     _, ne = _eps(ea2, er2)
     assert np.all(np.abs(gen - ne) <= 1e-3 * ne + 1e-6)
 
@@ -91,7 +92,7 @@ def test_trace_lambda_and_per_layer_solve():
     dW = poisoned(W.shape, torch.float32)
     info = torch.full((b,), -7, dtype=torch.int32, device="cuda")
     ispa.ispa_absorb_solve_lambdas(G, C, W, lam, dW, info,
-                                   workspace=ispa.workspace(ispa.ispa_absorb_workspace_size(D, D, b)))
+                                   workspace=nan_workspace(ispa.ispa_absorb_workspace_size(D, D, b)))
     torch.cuda.synchronize()
     assert info.cpu().tolist() == [0] * b
     for i in range(b):
@@ -102,7 +103,7 @@ def test_trace_lambda_and_per_layer_solve():
     const = torch.full((b,), 0.25, dtype=torch.float32, device="cuda")
     dW2 = poisoned(W.shape, torch.float32)
     ispa.ispa_absorb_solve_lambdas(G, C, W, const, dW2, info,
-                                   workspace=ispa.workspace(ispa.ispa_absorb_workspace_size(D, D, b)))
+                                   workspace=nan_workspace(ispa.ispa_absorb_workspace_size(D, D, b)))
     dW3, _ = gpu_solve(G, C, W, 0.25)
     torch.cuda.synchronize()
     assert torch.equal(dW2, dW3)
