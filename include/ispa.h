@@ -38,7 +38,9 @@
  * --------------------------
  * - Every buffer is DEVICE memory owned by the caller.  The library never
  *   allocates or frees in these calls; scratch space is a caller-provided
- *   workspace whose size is queried first.
+ *   workspace whose size is queried first.  Its contents on entry do not
+ *   matter (a call reads only workspace bytes it has written itself); calls
+ *   that share a workspace must not run concurrently.
  * - Calls only enqueue work on `stream` (a hipStream_t; NULL = default
  *   stream) and return; results are valid once the stream is synchronised.
  *   The absorb solves also run R = C W on a second stream the library owns
