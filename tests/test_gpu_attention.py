@@ -7,7 +7,8 @@ import torch
 import oracle
 from kv_cache_absorption_ispa_amd import inputs
 from kv_cache_absorption_ispa_amd import ispa
-from tests.gpu_util import (TOL_BF16_LSE, TOL_BF16_O, TOL_F32, dev, host64, maxabs, poisoned, relfro, say)
+from tests.gpu_util import (TOL_BF16_LSE, TOL_BF16_O, TOL_F32, dev, host64, maxabs, nan_workspace, poisoned,
+                            relfro, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -23,9 +24,10 @@ def run_decomp(x: inputs.ChunkInputs, scale):
     out = dict(O_loc=poisoned((n_q, H, D), dt), LSE_loc=poisoned((H, n_q), torch.float32),
                O_hist=poisoned((n_q, H, D), dt), LSE_hist=poisoned((H, n_q), torch.float32),
                O_full=poisoned((n_q, H, D), dt), LSE_full=poisoned((H, n_q), torch.float32))
+    ws = nan_workspace(ispa.ispa_decomp_attn_workspace_size(q, kl.shape[0], nh))
     ispa.ispa_decomp_attn(q, kl, vl, kh, vh, scale=scale, o_loc=out["O_loc"], lse_loc=out["LSE_loc"],
                           o_hist=out["O_hist"], lse_hist=out["LSE_hist"], o_full=out["O_full"],
-                          lse_full=out["LSE_full"])
+                          lse_full=out["LSE_full"], workspace=ws)
     torch.cuda.synchronize()
     return out
 
