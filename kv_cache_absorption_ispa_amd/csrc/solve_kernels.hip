@@ -768,12 +768,22 @@ ispa_status_t launch_absorb(int32_t d, int32_t d_out, int32_t batch, const float
   hipLaunchKernelGGL(init_shift_kernel, dim3((unsigned)((dd / 4 + 255) / 256), batch), dim3(256), 0, s, G, M, Linvf,
                      d, lambda, lam_b, info);
   ISPA_TRY(hip_check(hipGetLastError(), "init_shift_kernel launch"));
-  ISPA_TRY(hip_check(hipEventRecord(ev[0], s), "hipEventRecord"));
-  ISPA_TRY(hip_check(hipStreamWaitEvent(s2, ev[0], 0), "hipStreamWaitEvent"));
   // R = C W on the second stream, beside the factorisation (float32; R's rounding perturbs the
-  // solution like the float32 statistics themselves do)
-  ISPA_TRY((gemm<false, false>(s2, batch, d, d_out, d, C, d, dd, W, d_out, dn, nullptr, 0, 0, Rb, d_out, dn, 1.f,
-                               0.f, false, nullptr)));
+  // solution like the float32 statistics themselves do).  For small d it is forked after the first
+  // panel steps: sharing the GPU with it would slow the first diagonal factorisations, which sit on
+  // the latency-bound chain (d = 1536: 1.36 -> 1.33 ms per solve); at d = 5120 it goes first.
+  auto fork_cw = [&]() -> ispa_status_t {
+    ISPA_TRY(hip_check(hipEventRecord(ev[0], s), "hipEventRecord"));
+    ISPA_TRY(hip_check(hipStreamWaitEvent(s2, ev[0], 0), "hipStreamWaitEvent"));
+    return gemm<false, false>(s2, batch, d, d_out, d, C, d, dd, W, d_out, dn, nullptr, 0, 0, Rb, d_out, dn, 1.f, 0.f,
+                              false, nullptr);
+  };
+  const int fork_k = d <= 2048 ? 4 : -1;  // panel step before which it is forked (-1: right away)
+  bool forked = false;
+  if (fork_k < 0) {
+    ISPA_TRY(fork_cw());
+    forked = true;
+  }
   // Cholesky, right-looking by 64-column panels, with a one-panel look-ahead inside the trailing
   // update: the workgroup that updates the next diagonal block factors it right away, while the
   // other workgroups finish the update, so the factorisation (a latency-bound chain of 64 pivot
@@ -782,6 +792,10 @@ ispa_status_t launch_absorb(int32_t d, int32_t d_out, int32_t batch, const float
   hipLaunchKernelGGL(potrf_diag_kernel, dim3(batch), dim3(256), 0, s, M, d, 0, Linvf, info);
   ISPA_TRY(hip_check(hipGetLastError(), "potrf_diag_kernel launch"));
   for (int k = 0; k + 1 < nblk; ++k) {
+    if (k == fork_k) {
+      ISPA_TRY(fork_cw());
+      forked = true;
+    }
     const int k0 = k * NB;
     const int rest = d - k0 - NB;
     float* panel = M + (size_t)(k0 + NB) * d + k0;
@@ -794,6 +808,7 @@ ispa_status_t launch_absorb(int32_t d, int32_t d_out, int32_t batch, const float
     ISPA_TRY((gemm<false, true>(s, batch, rest, rest, NB, panel, d, dd, panel, d, dd, trail, d, dd, trail, d, dd, -1.f,
                                 1.f, true, info, 0, 1, 0, 0, 0, 0, M, Linvf, info, d, k0 + NB)));
   }
+  if (!forked) ISPA_TRY(fork_cw());
   // join: R = C W is done before the solve reads it
   ISPA_TRY(hip_check(hipEventRecord(ev[1], s2), "hipEventRecord"));
   ISPA_TRY(hip_check(hipStreamWaitEvent(s, ev[1], 0), "hipStreamWaitEvent"));
