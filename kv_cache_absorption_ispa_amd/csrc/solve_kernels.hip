@@ -106,6 +106,9 @@ __device__ __forceinline__ void potrf_diag_block(float* M, int d, int k0, float*
 #pragma unroll
         for (int k = j + 1; k < SB; ++k) a[k] = fmaf(-lij, readlane_f(lij, c0 + k), a[k]);
         a[j] = lij;
+        // one pivot step at a time: its cross-lane reads issue before the next pivot's (17.0 -> 16.0 us
+        // per 64 x 64 block)
+        __builtin_amdgcn_sched_barrier(0);
       }
       if (failed) {
         if (lane == 0) fail_s = k0 + failed;
