@@ -716,8 +716,8 @@ ispa_status_t invert_lower(hipStream_t s, int batch, int d, const float* L, floa
 }
 
 // A second stream per device for R = C W beside the latency-bound factorisation, with its fork and
-// join events (created once, kept until the process ends; default priority).  The enqueue of one solve holds the mutex, so the
-// events' record/wait pairs of two host threads never interleave.
+// join events (created once, kept until the process ends; default priority).  The enqueue of one
+// solve holds the mutex, so the events' record/wait pairs of two host threads never interleave.
 namespace {
 struct AuxStream {
   hipStream_t s2 = nullptr;
