@@ -355,7 +355,7 @@ def _draw_chunk(job):
     from kv_cache_absorption_ispa_amd import inputs
 
     layer, chunk = job
-    x = inputs.chunk_inputs(inputs.CONFIGS[4], layer, chunk)
+    x = inputs.chunk_inputs(inputs.WAN13B_STACK30, layer, chunk)
     return layer, chunk, [t.raw for t in (x.q, x.k_loc, x.v_loc, x.k_hist, x.v_hist)]
 
 
@@ -365,7 +365,7 @@ def generate_stack_inputs(workers: int):
 
     from kv_cache_absorption_ispa_amd import inputs
 
-    cfg = inputs.CONFIGS[4]
+    cfg = inputs.WAN13B_STACK30
     jobs = [(l, c) for c in range(cfg.n_chunks + 1) for l in range(cfg.n_layers)]
     log(f"[bench] drawing {len(jobs)} chunk inputs of {cfg.name} with {workers} processes")
     t0 = time.perf_counter()
@@ -387,7 +387,7 @@ def bench_stack(args, host_inputs):
     from kv_cache_absorption_ispa_amd import inputs, ispa
     from kv_cache_absorption_ispa_amd.stack import LayerStack
 
-    cfg = inputs.CONFIGS[4]
+    cfg = inputs.WAN13B_STACK30
     L, H, D, d, nq = cfg.n_layers, cfg.heads, cfg.head_dim, cfg.d, cfg.n_q
 
     def dev(raw):
@@ -535,7 +535,7 @@ def bench_stack(args, host_inputs):
         "kv_evicted_frac_of_history": round(evicted / (L * 2 * cfg.n_hist * d * 2), 4),
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(inputs.CONFIGS[1], args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(inputs.WAN13B_LAYER, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 

@@ -101,6 +101,12 @@ CONFIGS = {
     4: LayerConfig(4, "wan1.3b-stack30", heads=12, head_dim=128, n_q=4680, n_sink=1560, n_chunk=4680,
                    n_hist=14040, dtype="bf16", n_layers=30, n_absorb=15),
 }
+BY_NAME = {c.name: c for c in CONFIGS.values()}
+TINY_F32 = BY_NAME["tiny-fp32"]
+WAN13B_LAYER = BY_NAME["wan1.3b-layer"]
+WAN13B_LONG_HISTORY = BY_NAME["wan1.3b-long-history"]
+WAN14B_LAYER = BY_NAME["wan14b-layer"]
+WAN13B_STACK30 = BY_NAME["wan1.3b-stack30"]
 
 
 # --------------------------------------------------------------------------- #

@@ -20,7 +20,7 @@ from kv_cache_absorption_ispa_amd import inputs  # noqa: E402
 
 
 def case():
-    cfg = inputs.CONFIGS[0]
+    cfg = inputs.TINY_F32
     x = inputs.chunk_inputs(cfg, 0, 0, n_q=4, n_hist=16)
     b = oracle.branch_outputs(x.q.f64, x.k_loc.f64, x.v_loc.f64, x.k_hist.f64, x.v_hist.f64, cfg.scale)
     a_loc, a_full = inputs.absorb_rows(0, 0, 64, 8, "f32")

@@ -27,7 +27,7 @@ def test_header_lists_the_entry_points():
 @pytest.mark.skipif(not os.path.exists(ispa.LIB_PATH), reason="libispa.so not built")
 def test_library_exports_every_declared_symbol():
     # RTLD_NOW: every symbol the library needs must resolve at load time (a kernel whose
-    # launch stub went missing shows up here, not only at its first launch on a GPU machine)
+    # launch stub went missing shows up here, not only at its first launch on a GPU)
     lib = ctypes.CDLL(ispa.LIB_PATH, mode=os.RTLD_NOW | os.RTLD_LOCAL)
     for n in header_functions():
         assert hasattr(lib, n), n

@@ -71,7 +71,7 @@ def test_gram_parity(case):
 
 def test_gram_full_size_and_deterministic():
     """Wan-1.3B layer: 4 chunks x 4680 rows, d = 1536, split over rows; bitwise repeatable."""
-    cfg = inputs.CONFIGS[1]
+    cfg = inputs.WAN13B_LAYER
     al, af = inputs.absorb_rows(1, 0, cfg.gram_rows, cfg.d, "bf16")
     chunks = list(zip(split_rows(al, 4), split_rows(af, 4)))
     G1, C1, _ = gpu_gram(chunks, cfg.d)
@@ -98,12 +98,12 @@ def test_solve_parity_on_oracle_statistics(d, d_out):
     assert e <= TOL_DW
 
 
-@pytest.mark.parametrize("cfg_id", [0, 1, 3])
-def test_gram_and_solve_boundary(cfg_id):
+@pytest.mark.parametrize("cfg_name", ["tiny-fp32", "wan1.3b-layer", "wan14b-layer"])
+def test_gram_and_solve_boundary(cfg_name):
     """The absorb at the gram+solve boundary on each layer shape's full warmup row count."""
-    cfg = inputs.CONFIGS[cfg_id]
+    cfg = inputs.BY_NAME[cfg_name]
     say("config", cfg.name, "rows", cfg.gram_rows, "d", cfg.d)
-    al, af = inputs.absorb_rows(cfg_id, 0, cfg.gram_rows, cfg.d, cfg.dtype)
+    al, af = inputs.absorb_rows(cfg.cfg_id, 0, cfg.gram_rows, cfg.d, cfg.dtype)
     chunks = list(zip(split_rows(al, cfg.n_chunks), split_rows(af, cfg.n_chunks)))
     G, C, _ = gpu_gram(chunks, cfg.d)
     W = inputs.weight(cfg, 0)
@@ -262,7 +262,7 @@ def test_reconstruction_error_parity():
 def test_tiny_fp32_chain_end_to_end():
     """Attention -> Gram -> absorb on the float32 configuration, every step on the GPU, against the
     oracle's own chain from the same seeded Q/K/V (gated: the float32 chain is well conditioned)."""
-    cfg = inputs.CONFIGS[0]
+    cfg = inputs.TINY_F32
     d = cfg.d
     G = poisoned((d, d), torch.float32)
     C = poisoned((d, d), torch.float32)

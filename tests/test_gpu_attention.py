@@ -84,7 +84,7 @@ def test_f32_parity_small(case):
 
 def test_tiny_fp32_config_all_chunks():
     """The float32 configuration at its full size: every output element of every warmup chunk."""
-    cfg = inputs.CONFIGS[0]
+    cfg = inputs.TINY_F32
     for c in range(cfg.n_chunks):
         say("chunk", c)
         x = inputs.chunk_inputs(cfg, 0, c)
@@ -92,17 +92,17 @@ def test_tiny_fp32_config_all_chunks():
         check_against_oracle(x, out, cfg.scale, TOL_F32, TOL_F32)
 
 
-@pytest.mark.parametrize("cfg_id", [1, 2, 3])
-def test_bf16_full_size_sampled_rows(cfg_id):
+@pytest.mark.parametrize("cfg_name", ["wan1.3b-layer", "wan1.3b-long-history", "wan14b-layer"])
+def test_bf16_full_size_sampled_rows(cfg_name):
     """Full-size layers in the benchmark's launch configuration; the oracle checks sampled query rows
     (first and last tiles, the ragged tail, and random rows) over every head and output."""
-    cfg = inputs.CONFIGS[cfg_id]
+    cfg = inputs.BY_NAME[cfg_name]
     say("config", cfg.name)
     x = inputs.chunk_inputs(cfg, 0, 0)
     out = run_decomp(x, cfg.scale)
     for name, t in out.items():
         assert not torch.isnan(t).any().item(), f"{name} has unwritten (NaN) elements"
-    g = np.random.default_rng(cfg_id)
+    g = np.random.default_rng(cfg.cfg_id)
     rows = np.unique(np.concatenate([np.arange(0, 8), np.arange(cfg.n_q - 80, cfg.n_q),
                                      g.choice(cfg.n_q, 24, replace=False)]))
     say("report", check_against_oracle(x, out, cfg.scale, TOL_BF16_O, TOL_BF16_LSE, rows=rows))

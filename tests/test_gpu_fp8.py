@@ -158,7 +158,7 @@ def test_fp8k_attention_parity(case):
 
 def test_fp8k_attention_full_size_sampled_rows():
     """The Wan-1.3B layer with fp8 Q and K (sink, chunk and a 3-chunk history as separate segments)."""
-    cfg = inputs.CONFIGS[1]
+    cfg = inputs.WAN13B_LAYER
     x = inputs.chunk_inputs(cfg, 0, 0)
     ls, hs = (cfg.n_sink, cfg.n_chunk), (cfg.n_chunk,) * (cfg.n_hist // cfg.n_chunk)
     q8, qs, segs, kd = _fp8k_inputs(x, ls, hs)

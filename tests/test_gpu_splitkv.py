@@ -73,18 +73,19 @@ def test_one_unit_per_workgroup_is_bitwise_decomp():
         assert torch.equal(out[n], ref[n]), n
 
 
-@pytest.mark.parametrize("cfg_id,n_q", [(1, 256), (1, 4680), (2, 512)])
-def test_splitkv_full_size_sampled_rows(cfg_id, n_q):
+@pytest.mark.parametrize("cfg_name,n_q", [("wan1.3b-layer", 256), ("wan1.3b-layer", 4680),
+                                          ("wan1.3b-long-history", 512)])
+def test_splitkv_full_size_sampled_rows(cfg_name, n_q):
     """Full-size keys with one workgroup per compute unit: a short query chunk (12 or 24 units, so
     10-16 pieces each) and the full chunk (228 units: P = 1).  Sampled rows against the oracle,
     every element against the unsplit call within the bf16 output bound."""
-    cfg = inputs.CONFIGS[cfg_id]
+    cfg = inputs.BY_NAME[cfg_name]
     say("config", cfg.name, "n_q", n_q)
     x = inputs.chunk_inputs(cfg, 0, 0, n_q=n_q)
     out = run_splitkv(x, cfg.scale, 0, (cfg.n_sink, cfg.n_chunk))
     for name, t in out.items():
         assert not torch.isnan(t).any().item(), f"{name} has unwritten (NaN) elements"
-    g = np.random.default_rng(cfg_id)
+    g = np.random.default_rng(cfg.cfg_id)
     rows = np.unique(np.concatenate([np.arange(0, 8), np.arange(n_q - 80, n_q), g.choice(n_q, 24, replace=False)]))
     say("report", check_against_oracle(x, out, cfg.scale, TOL_BF16_O, TOL_BF16_LSE, rows=rows))
     ref = run_decomp(x, cfg.scale)

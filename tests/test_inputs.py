@@ -24,7 +24,7 @@ def test_bf16_rne_matches_torch():
 
 
 def test_deterministic_and_distinct():
-    cfg = inputs.CONFIGS[0]
+    cfg = inputs.TINY_F32
     a = inputs.chunk_inputs(cfg, 0, 0)
     b = inputs.chunk_inputs(cfg, 0, 0)
     c = inputs.chunk_inputs(cfg, 0, 1)
@@ -36,7 +36,7 @@ def test_deterministic_and_distinct():
 
 
 def test_shapes_and_boost():
-    cfg = inputs.CONFIGS[1]
+    cfg = inputs.WAN13B_LAYER
     x = inputs.chunk_inputs(cfg, 0, 0, n_hist=64)
     assert x.q.shape == (4680, 12, 128) and x.q.raw.dtype == np.uint16
     assert x.k_loc.shape == (cfg.n_loc, 12, 128)
@@ -48,13 +48,13 @@ def test_shapes_and_boost():
 
 
 def test_weight_scale():
-    cfg = inputs.CONFIGS[1]
+    cfg = inputs.WAN13B_LAYER
     W = inputs.weight(cfg, 0)
     assert W.shape == (1536, 1536) and W.dtype == np.float32
     assert abs(W.std() * np.sqrt(1536) - 1) < 0.01
 
 
 def test_flop_counts():
-    cfg = inputs.CONFIGS[1]
+    cfg = inputs.WAN13B_LAYER
     assert abs(cfg.attn_flops() - 5.83e11) / 5.83e11 < 0.01
     assert cfg.gram_rows == 18720

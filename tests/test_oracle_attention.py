@@ -160,7 +160,7 @@ def test_merge_weights_and_empty_branch():
 
 def test_branch_outputs_on_seeded_tiny_layer():
     """The dual-stream quantities on the seeded fp32 layer: full = merge(local, history)."""
-    cfg = inputs.CONFIGS[0]
+    cfg = inputs.TINY_F32
     x = inputs.chunk_inputs(cfg, 0, 0, n_q=48, n_hist=200)
     b = oracle.branch_outputs(x.q.f64, x.k_loc.f64, x.v_loc.f64, x.k_hist.f64, x.v_hist.f64, cfg.scale)
     om, lm = oracle.merge(b["O_loc"], b["LSE_loc"], b["O_hist"], b["LSE_hist"])
