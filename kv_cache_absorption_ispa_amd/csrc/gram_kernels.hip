@@ -88,7 +88,8 @@ __global__ __launch_bounds__(TI * 2, (TI == 128 && !QFF) ? 2 : 1) void gram_bf16
   const int wi = (wave >> 1) * 64, wj = (wave & 1) * 64;  // wave sub-tile origin
   const uint32_t row_bytes = (uint32_t)p.d * 2u;
   // Buffers start at this split's first row; rows at or past r_end read as 0 (range-checked
-  // buffer loads).  The host keeps (rows per launch + 64) * row_bytes below 2^31.
+  // buffer loads).  The host keeps (rows per launch + 64) * row_bytes <= 2^31, so the byte offsets
+  // of the padding stages (at most 95 rows past the last row) stay far below 2^32.
   const uint32_t span = r_end > r_begin ? (uint32_t)(r_end - r_begin) * row_bytes : 0u;
   const rsrc_t rl = make_rsrc(p.Al + r_begin * p.d, span);
   const rsrc_t rf = make_rsrc(p.Af + r_begin * p.d, span);
@@ -324,7 +325,7 @@ __global__ __launch_bounds__(256) void gram_f32_kernel(const float* __restrict__
     }
 }
 
-// Rows per launch: (rows + 64) * 2d bytes stays below 2^31 (buffer offsets are 32-bit).
+// Rows per launch: (rows + 64) * 2d bytes stays within 2^31 (buffer offsets are 32-bit).
 int64_t gram_block_rows(int d) {
   const int64_t r = ((int64_t)1 << 31) / (2 * (int64_t)d) - 2 * GBK;
   return (r / GBK) * GBK;

@@ -83,6 +83,41 @@ def test_gram_full_size_and_deterministic():
     assert eg <= TOL_G and ec <= TOL_C
 
 
+def test_gram_rows_past_one_launch():
+    """More rows than one launch takes (row offsets are 32-bit: (rows + 64) * 2d bytes < 2^31, so
+    262080 rows at d = 4096): the call splits them over launches, the later ones accumulating.  It
+    must equal the same rows given as two calls bit for bit, and sampled entries of G and C must
+    match float64 dot products of the rows on the host.  Rows are seeded draws made on the device
+    (4.3 GB of input would take minutes to draw on the host)."""
+    d = 4096
+    block = ((1 << 31) // (2 * d) - 64) // 32 * 32
+    n = block + 1000
+    gen = torch.Generator(device="cuda").manual_seed(77)
+    al = torch.randn(n, d, device="cuda", generator=gen).to(torch.bfloat16)
+    af = (al.float() + 0.3 * torch.randn(n, d, device="cuda", generator=gen)).to(torch.bfloat16)
+    G1, C1 = poisoned((d, d), torch.float32), poisoned((d, d), torch.float32)
+    ispa.ispa_gram_accum(al, af, G1, C1, accumulate=False,
+                         workspace=nan_workspace(ispa.ispa_gram_workspace_size(n, d, torch.bfloat16)))
+    G2, C2 = poisoned((d, d), torch.float32), poisoned((d, d), torch.float32)
+    ispa.ispa_gram_accum(al[:block], af[:block], G2, C2, accumulate=False,
+                         workspace=nan_workspace(ispa.ispa_gram_workspace_size(block, d, torch.bfloat16)))
+    ispa.ispa_gram_accum(al[block:], af[block:], G2, C2, accumulate=True,
+                         workspace=nan_workspace(ispa.ispa_gram_workspace_size(n - block, d, torch.bfloat16)))
+    torch.cuda.synchronize()
+    assert torch.equal(G1, G2) and torch.equal(C1, C2)
+    g = np.random.default_rng(5)
+    pairs = [(0, 0), (d - 1, d - 1), (d - 1, 0), (0, d - 1)] + [tuple(g.integers(0, d, 2)) for _ in range(8)]
+    for i, j in pairs:
+        ai = al[:, i].double().cpu().numpy()
+        aj = al[:, j].double().cpu().numpy()
+        fj = af[:, j].double().cpu().numpy()
+        g_ref, c_ref = float(ai @ aj), float(ai @ (fj - aj))
+        g_abs, c_abs = float(np.abs(ai) @ np.abs(aj)), float(np.abs(ai) @ (np.abs(fj) + np.abs(aj)))
+        # float32 accumulation of n exact products: well inside n * 2^-24 of the absolute sums
+        assert abs(G1[i, j].item() - g_ref) <= 1e-4 * g_abs, (i, j)
+        assert abs(C1[i, j].item() - c_ref) <= 1e-4 * c_abs, (i, j)
+
+
 @pytest.mark.parametrize("d,d_out", [(128, 128), (256, 192), (1536, 1536)])
 def test_solve_parity_on_oracle_statistics(d, d_out):
     """ispa_absorb_solve alone: G, C are the oracle's (rounded to float32), dW vs the float64 solve."""
