@@ -259,11 +259,14 @@ __global__ __launch_bounds__(NW * 64, (QB == 1 && NW <= 4) ? 2 : 1) void attn_bf
 
   // This wave's tile loads: load j is wave load g = wave + j*NW of the tile (K loads first, then V).
   // Lane i fills row r0 + i/CPR(K), slot i%CPR(K), with the row's chunk slot ^ swizzle(row).
+  // When NW divides the K loads, load j is a K load exactly when j < WLTK/NW (wave < NW): a
+  // compile-time choice, so no per-load condition is kept in scalar registers.
+  auto is_kload = [&](int j) { return WLTK % NW == 0 ? j < WLTK / NW : wave + j * NW < WLTK; };
   uint32_t gofs[WLW];
 #pragma unroll
   for (int j = 0; j < WLW; ++j) {
     const int g = wave + j * NW;
-    if (g < WLTK) {
+    if (is_kload(j)) {
       const int row = g * RPWK + lane / CPRK;
       const int chunk = (lane % CPRK) ^ (KF8 ? kf8_swizzle<D>(row) : kv_swizzle<D>(row));
       gofs[j] = (uint32_t)row * krow_bytes + (uint32_t)(head * D) * (KF8 ? 1u : 2u) + chunk * 16u;
@@ -283,7 +286,7 @@ __global__ __launch_bounds__(NW * 64, (QB == 1 && NW <= 4) ? 2 : 1) void attn_bf
 #pragma unroll
     for (int j = 0; j < WLW; ++j) {
       const int g = wave + j * NW;
-      if (g < WLTK)
+      if (is_kload(j))
         load_to_lds(rk, (uint16_t*)((uint8_t*)sKb + g * RPWK * KRB), gofs[j] + tbk);
       else
         load_to_lds(rv, sVb + (g - WLTK) * RPW * D, gofs[j] + tb);
