@@ -63,8 +63,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build runs on one GPU only: the hot path is one layer on one device; "
-                                   "see the design notes for how it would shard"}), flush=True)
+        print(json.dumps({"error": "bench.py measures one GPU only: the hot path is one layer on one device, "
+                                   "with no sharding or collectives; --gpus must be 1"}), flush=True)
         sys.exit(2)
 
     if args.config == 4:

@@ -6,7 +6,7 @@ The fp8 variant pairs ISPA with 8-bit arithmetic, as the technical summary's
 results do when it combines ISPA with W8A8 post-training quantisation
 ("Technical Summary: Instance-Specific Parametric Absorption (ISPA) for
 Memory-Efficient Video Generation", section 4 "Results").  The pages give no
-format or scaling; the reading (listed in the design notes) is:
+format or scaling; the reading taken here is:
 
 * format: E4M3 with the OCP "FN" encoding: 1 sign bit, 4 exponent bits with
   bias 7, 3 mantissa bits, subnormals below 2^-6 (spacing 2^-9), largest

@@ -19,7 +19,7 @@ held-out rows (``reconstruction_error`` on rows the fit did not see), lambda
 proportional to the mean eigenvalue of G (:func:`trace_scaled_lambda`), and
 converting every layer whose error is under a threshold (:func:`select_below`).
 
-Readings (listed in the design notes): the norm is Frobenius and the objective
+Readings taken here: the norm is Frobenius and the objective
 is a sum (not a mean) over all warmup rows, every row weighted equally; lambda
 is absolute; W is the attention output projection in the row-vector convention
 y = a W with W of shape [d, d_out]; the reconstruction error is the post-fit

@@ -9,7 +9,7 @@ the current chunk plus the sink tokens, and the decomposable form computes a
 local and a historical branch and fuses them after the fact from their
 log-sum-exp (LSE) states.
 
-Readings of what the page leaves open (each is listed in the design notes):
+Readings of what the page leaves open:
 
 * scores are scale * <q, k> with scale = 1/sqrt(head_dim); no mask: every query
   sees every sink, chunk and history key;
