@@ -350,3 +350,21 @@ def test_absorb_solve_ex_refinement_optional(d):
     ispa.ispa_absorb_solve_ex(G, C, W, 0.0, dW3, info, lambdas=lam, refine=True, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(dW3, dW_ref)
+
+
+@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 256), (torch.float32, 192)])
+def test_gram_zero_rows(dtype, d):
+    """0 warmup rows: with accumulate = 0 the statistics are written as zeros (the sums over no rows);
+    with accumulate = 1 they are left exactly as they were."""
+    a = torch.empty(0, d, dtype=dtype, device="cuda")
+    G, C = poisoned((d, d), torch.float32), poisoned((d, d), torch.float32)
+    ws = nan_workspace(ispa.ispa_gram_workspace_size(0, d, dtype))
+    ispa.ispa_gram_accum(a, a, G, C, accumulate=False, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(G).item() == 0 and torch.count_nonzero(C).item() == 0
+    g = torch.Generator(device="cpu").manual_seed(5)
+    G0, C0 = torch.randn(d, d, generator=g).cuda(), torch.randn(d, d, generator=g).cuda()
+    G, C = G0.clone(), C0.clone()
+    ispa.ispa_gram_accum(a, a, G, C, accumulate=True, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(G, G0) and torch.equal(C, C0)

@@ -190,3 +190,22 @@ def test_invalid_arguments_raise():
         ispa.ispa_decomp_attn(q, dev(x.k_loc)[:0], dev(x.v_loc)[:0])  # n_loc = 0
     with pytest.raises(ispa.IspaError):
         ispa.ispa_decomp_attn(q.float(), dev(x.k_loc), dev(x.v_loc))  # dtype mismatch
+
+
+def test_empty_query_chunk_is_a_no_op():
+    """n_q = 0 is a valid chunk (the API takes n_q >= 0): the two-buffer, segment-list, split-KV and
+    single-pass calls all return without error and write nothing (a NaN sentinel beside the empty
+    outputs stays NaN)."""
+    H, D = 2, 128
+    x = inputs.custom_inputs(27, 1, 130, 70, H, D, "bf16")
+    kl, vl, kh, vh = dev(x.k_loc), dev(x.v_loc), dev(x.k_hist), dev(x.v_hist)
+    q = torch.empty(0, H, D, dtype=torch.bfloat16, device="cuda")
+    sentinel = poisoned((8, H, D), torch.bfloat16)
+    o = sentinel[:0]
+    lse = torch.empty(H, 0, device="cuda")
+    ispa.ispa_decomp_attn(q, kl, vl, kh, vh, o_loc=o, lse_loc=lse, o_hist=o, lse_hist=lse, o_full=o, lse_full=lse)
+    ispa.ispa_decomp_attn_segments(q, [(kl, vl)], [(kh, vh)], o_loc=o, o_full=o, lse_full=lse)
+    ispa.ispa_decomp_attn_splitkv(q, [(kl, vl)], [(kh, vh)], o_loc=o, o_full=o, lse_full=lse)
+    ispa.ispa_full_attn(q, kh, vh, o=o, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.isnan(sentinel.float()).all()
