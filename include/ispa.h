@@ -199,12 +199,14 @@ ispa_status_t ispa_decomp_attn_splitkv(const ispa_attn_desc_t* desc, const void*
 /* Workspace bytes of ispa_decomp_attn_splitkv: the merge's float32 O_loc
  * (with history keys, rounded up to 256 bytes) plus one partial slot of
  * 2*BM*(D+1) float32 per workgroup (BM = 256 queries; 264 KB at D = 128).
- * n_workers = 0 sizes for the current device (0 if there is none). */
+ * n_workers = 0 sizes for the current device (0 if there is none).
+ * Support call: no passage of the pages defines it. */
 size_t ispa_decomp_attn_splitkv_workspace_size(const ispa_attn_desc_t* desc, int32_t n_workers);
 
 /* Workspace bytes ispa_decomp_attn needs for this shape: n_q*H*D*4 for bf16
  * with history keys (the float32 O_loc the merge reads), else 0.  Needed only
- * when O_full is requested. */
+ * when O_full is requested.
+ * Support call: no passage of the pages defines it. */
 size_t ispa_decomp_attn_workspace_size(const ispa_attn_desc_t* desc);
 
 /*
@@ -212,6 +214,8 @@ size_t ispa_decomp_attn_workspace_size(const ispa_attn_desc_t* desc);
  * single concatenated K, V ([n_loc + n_hist, H, D]).  This is the
  * single-stream attention the decomposable pass is compared against (same
  * kernel family, one phase).  O / LSE may be NULL.
+ * Source: ISPA technical summary, section 2 "Methodology", step 1 (the full
+ * stream, here over the keys concatenated) and section 3 (online softmax).
  */
 ispa_status_t ispa_full_attn(const ispa_attn_desc_t* desc, const void* Q, const void* K, const void* V,
                              void* O, float* LSE, void* stream);
@@ -229,7 +233,8 @@ ispa_status_t ispa_lse_merge(int32_t n_parts, const void* const* O_parts, const 
                              int64_t n_q, int32_t heads, int32_t head_dim, int32_t dtype, void* O_out,
                              float* LSE_out, void* stream);
 
-/* Workspace bytes ispa_gram_accum needs for these sizes (0 is possible). */
+/* Workspace bytes ispa_gram_accum needs for these sizes (0 is possible).
+ * Support call: no passage of the pages defines it. */
 size_t ispa_gram_workspace_size(int64_t n_rows, int32_t d, int32_t dtype);
 
 /*
@@ -253,7 +258,8 @@ ispa_status_t ispa_gram_accum(int64_t n_rows, int32_t d, int32_t dtype, const vo
                               const void* A_full, float* G, float* C, float* Q_ff, int32_t accumulate,
                               void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes ispa_absorb_solve needs for these sizes. */
+/* Workspace bytes ispa_absorb_solve needs for these sizes.
+ * Support call: no passage of the pages defines it. */
 size_t ispa_absorb_workspace_size(int32_t d, int32_t d_out, int32_t batch);
 
 /*
@@ -278,7 +284,8 @@ ispa_status_t ispa_absorb_solve(int32_t d, int32_t d_out, int32_t batch, const f
                                 const float* W, float lambda, float* dW, float* W_new, int32_t* info,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes ispa_layer_eps needs. */
+/* Workspace bytes ispa_layer_eps needs.
+ * Support call: no passage of the pages defines it. */
 size_t ispa_eps_workspace_size(int32_t d, int32_t d_out, int32_t batch);
 
 /*
@@ -339,7 +346,8 @@ ispa_status_t ispa_absorb_apply(int32_t d, int32_t d_out, int32_t n_layers, cons
  * +-448 and rounded to nearest, ties to even.  Codes are uint8.
  * ------------------------------------------------------------------------- */
 
-/* Workspace bytes of ispa_quantize_fp8_heads: ceil(n_rows / 16) * heads floats. */
+/* Workspace bytes of ispa_quantize_fp8_heads: ceil(n_rows / 16) * heads floats.
+ * Support call: no passage of the pages defines it. */
 size_t ispa_quantize_fp8_heads_workspace_size(int64_t n_rows, int32_t heads);
 
 /*
@@ -348,6 +356,9 @@ size_t ispa_quantize_fp8_heads_workspace_size(int64_t n_rows, int32_t heads);
  * and dims: scale [heads] float32 DEVICE.  For Q and K of
  * ispa_decomp_attn_fp8k.  head_dim 64 or 128, heads * head_dim <= 16384;
  * workspace required.
+ * Source: ISPA technical summary, section 4 "Results" (ISPA combined with W8A8
+ * quantisation); the format and scaling are this library's reading (E4M3,
+ * absmax scales).
  */
 ispa_status_t ispa_quantize_fp8_heads(int64_t n_rows, int32_t heads, int32_t head_dim, int32_t dtype, const void* X,
                                       uint8_t* X8, float* scale, void* workspace, size_t workspace_bytes,
@@ -357,6 +368,9 @@ ispa_status_t ispa_quantize_fp8_heads(int64_t n_rows, int32_t heads, int32_t hea
  * ispa_quantize_fp8_rows — X [n_rows, d] (BF16 or F32) to codes X8 [n_rows, d]
  * with one scale per row (token): scale [n_rows] float32 DEVICE.  The
  * activation side of ispa_w8a8_gemm.  d a positive multiple of 4.
+ * Source: ISPA technical summary, section 4 "Results" (ISPA combined with W8A8
+ * quantisation); the format and scaling are this library's reading (E4M3,
+ * absmax scales).
  */
 ispa_status_t ispa_quantize_fp8_rows(int64_t n_rows, int32_t d, int32_t dtype, const void* X, uint8_t* X8,
                                      float* scale, void* stream);
@@ -366,6 +380,9 @@ ispa_status_t ispa_quantize_fp8_rows(int64_t n_rows, int32_t d, int32_t dtype, c
  * output column: scale [d_out] float32, codes written TRANSPOSED as
  * W8T [d_out, d] (each column's d codes contiguous, the operand layout of
  * ispa_w8a8_gemm).  d a positive multiple of 4.
+ * Source: ISPA technical summary, section 4 "Results" (ISPA combined with W8A8
+ * quantisation); the format and scaling are this library's reading (E4M3,
+ * absmax scales).
  */
 ispa_status_t ispa_quantize_fp8_cols(int32_t d, int32_t d_out, const float* W, uint8_t* W8T, float* scale,
                                      void* stream);
@@ -377,6 +394,9 @@ ispa_status_t ispa_quantize_fp8_cols(int32_t d, int32_t d_out, const float* W, u
  * [d_out, d] codes per column (ispa_quantize_fp8_cols); products of codes
  * accumulate in float32 on gfx950 fp8 matrix cores.  d a multiple of 64,
  * d_out a multiple of 128, operands below 2^32 bytes.
+ * Source: ISPA technical summary, section 4 "Results" (ISPA combined with W8A8
+ * quantisation); the format and scaling are this library's reading (E4M3,
+ * absmax scales).
  */
 ispa_status_t ispa_w8a8_gemm(int64_t n, int32_t d, int32_t d_out, const uint8_t* A8, const float* a_scale,
                              const uint8_t* W8T, const float* w_scale, void* Y, void* stream);
@@ -399,6 +419,9 @@ typedef struct {
  * merge as in the bf16 path, V and the outputs bf16.  A K cache held as codes
  * takes half the K bytes.  desc->dtype must be ISPA_BF16; everything else as
  * ispa_decomp_attn_segments (same workspace).
+ * Source: ISPA technical summary, section 4 "Results" (ISPA combined with W8A8
+ * quantisation); the format and scaling are this library's reading (E4M3,
+ * absmax scales).
  */
 ispa_status_t ispa_decomp_attn_fp8k(const ispa_attn_desc_t* desc, const void* Q8, const float* q_scale,
                                     const ispa_kv_segment_fp8k_t* segs, int32_t n_segs, int32_t n_loc_segs,
@@ -427,6 +450,8 @@ size_t ispa_fit_error_workspace_size(int32_t d, int32_t d_out, int32_t batch);
  * same rows.  Products in float32, inner products reduced in float64.
  *   G, C, Q_ff [batch, d, d]; W, dW [batch, d, d_out] float32 (dW nullable);
  *   eps_abs, eps_rel [batch] float64 DEVICE.  d, d_out multiples of 64.
+ * Source: ISPA technical summary, section 2 "Dynamic Layer Selection" (layers ranked
+ * by reconstruction error; the variants here are this library's readings of it).
  */
 ispa_status_t ispa_fit_error(int32_t d, int32_t d_out, int32_t batch, const float* G, const float* C,
                              const float* Q_ff, const float* W, const float* dW, double* eps_abs,
@@ -438,6 +463,8 @@ ispa_status_t ispa_fit_error(int32_t d, int32_t d_out, int32_t batch, const floa
  * the layer's activations, so dW does not change when both streams are
  * scaled.  G [batch, d, d] float32, lambdas [batch] float32 DEVICE;
  * lam_scale finite, >= 0.
+ * Source: ISPA technical summary, section 2, step 2 "Layer Absorb" (ridge objective
+ * and its closed-form solution).
  */
 ispa_status_t ispa_lambda_from_trace(int32_t d, int32_t batch, const float* G, float lam_scale, float* lambdas,
                                      void* stream);
@@ -447,6 +474,8 @@ ispa_status_t ispa_lambda_from_trace(int32_t d, int32_t batch, const float* G, f
  * from the DEVICE array lambdas [batch] float32 (as ispa_lambda_from_trace
  * writes it).  Same arguments, workspace and errors otherwise; a lambda that
  * leaves G + lambda I indefinite shows up in info, not as an error.
+ * Source: ISPA technical summary, section 2, step 2 "Layer Absorb" (ridge objective
+ * and its closed-form solution).
  */
 ispa_status_t ispa_absorb_solve_lambdas(int32_t d, int32_t d_out, int32_t batch, const float* G, const float* C,
                                         const float* W, const float* lambdas, float* dW, float* W_new,
@@ -463,6 +492,8 @@ ispa_status_t ispa_absorb_solve_lambdas(int32_t d, int32_t d_out, int32_t batch,
  * d = 5120): dW is then the float32 solve, whose error grows like
  * cond(G + lambda I) * 2^-24 instead of reaching the float32 statistics'
  * own accuracy.  Same workspace and errors as ispa_absorb_solve.
+ * Source: ISPA technical summary, section 2, step 2 "Layer Absorb" (ridge objective
+ * and its closed-form solution).
  */
 ispa_status_t ispa_absorb_solve_ex(int32_t d, int32_t d_out, int32_t batch, const float* G, const float* C,
                                    const float* W, float lambda, const float* lambdas, int32_t flags, float* dW,
@@ -477,6 +508,8 @@ ispa_status_t ispa_absorb_solve_ex(int32_t d, int32_t d_out, int32_t batch, cons
  *   eps [n_layers] float64 DEVICE; 1 <= n_layers <= 4096; 0 <= k_max <= n_layers;
  *   tau not NaN.  selected [k_max] int32 DEVICE (the first *count entries are
  *   written); count [1] int32 DEVICE; rank [n_layers] int32 DEVICE or NULL.
+ * Source: ISPA technical summary, section 2 "Dynamic Layer Selection" (layers ranked
+ * by reconstruction error; the variants here are this library's readings of it).
  */
 ispa_status_t ispa_select_layers_below(int32_t n_layers, const double* eps, double tau, int32_t k_max,
                                        int32_t* selected, int32_t* count, int32_t* rank, void* stream);
@@ -486,6 +519,8 @@ ispa_status_t ispa_select_layers_below(int32_t n_layers, const double* eps, doub
  * per_layer float32 values (to solve only the chosen layers, e.g. after
  * ranking by ispa_fit_error with dW = NULL).  src [n_layers, per_layer],
  * dst [k, per_layer] DEVICE; an id outside [0, n_layers) gives a NaN layer.
+ * Source: ISPA technical summary, section 2 "Dynamic Layer Selection" and step 2
+ * "Layer Absorb" (only the selected layers are solved and absorbed).
  */
 ispa_status_t ispa_gather_layers(int32_t n_layers, int64_t per_layer, const float* src, const int32_t* selected,
                                  int32_t k, float* dst, void* stream);
@@ -495,20 +530,25 @@ ispa_status_t ispa_gather_layers(int32_t n_layers, int64_t per_layer, const floa
  * [k, d, d_out] holds only the chosen layers in selection order (the output
  * of a solve on gathered layers).  W [n_layers, d, d_out] float32 DEVICE; ids
  * distinct; an id outside [0, n_layers) is skipped.
+ * Source: ISPA technical summary, section 2, step 3 "Memory-Efficient Inference"
+ * (the converted layers run with W + dW).
  */
 ispa_status_t ispa_absorb_apply_compact(int32_t d, int32_t d_out, int32_t n_layers, const int32_t* selected,
                                         int32_t k, const float* dW, float* W, void* stream);
 
-/* Human-readable name of a status code (static string). */
+/* Human-readable name of a status code (static string).
+ * Support call: no passage of the pages defines it. */
 const char* ispa_status_string(ispa_status_t status);
 
-/* Detail of the last error on the calling thread ("" if none). */
+/* Detail of the last error on the calling thread ("" if none).
+ * Support call: no passage of the pages defines it. */
 const char* ispa_last_error(void);
 
 /* Library version, major*10000 + minor*100 + patch. */
 int32_t ispa_version(void);
 
-/* ISPA_OK if `device` is a gfx950 GPU, else ISPA_E_UNSUPPORTED (or ISPA_E_HIP). */
+/* ISPA_OK if `device` is a gfx950 GPU, else ISPA_E_UNSUPPORTED (or ISPA_E_HIP).
+ * Support call: no passage of the pages defines it. */
 ispa_status_t ispa_device_check(int32_t device);
 
 #ifdef __cplusplus
