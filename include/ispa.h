@@ -80,7 +80,9 @@ typedef enum {
 
 typedef enum { ISPA_F32 = 0, ISPA_BF16 = 1 } ispa_dtype_t;
 
-/* Shape of one attention call. */
+/* Shape of one attention call.  Q and each output ([n_q, H, D]), the keys
+ * and values ([n_loc + n_hist, H, D] in all) and each LSE ([H, n_q]) must hold
+ * fewer than 2^31 elements; a larger shape returns ISPA_E_INVALID_ARG. */
 typedef struct {
   int32_t heads;    /* H >= 1 */
   int32_t head_dim; /* D in {64, 128} */
@@ -251,8 +253,9 @@ size_t ispa_gram_workspace_size(int64_t n_rows, int32_t d, int32_t dtype);
  *   accumulate = 0 overwrites G, C (and Q_ff); 1 adds to them.
  *   Q_ff may be NULL; if given, Q_ff (+)= A_full^T A_full (for ispa_layer_eps).
  *   G and Q_ff are written in full (both triangles).  d must be a multiple of
- *   128 (bf16) or 64 (float32); n_rows >= 0 (0 rows with accumulate = 0 writes zeros).  The result is
- *   deterministic: no atomics, fixed reduction order.
+ *   128 (bf16) or 64 (float32); 0 <= n_rows with n_rows * d < 2^40 (0 rows
+ *   with accumulate = 0 writes zeros).  The result is deterministic: no
+ *   atomics, fixed reduction order.
  */
 ispa_status_t ispa_gram_accum(int64_t n_rows, int32_t d, int32_t dtype, const void* A_loc,
                               const void* A_full, float* G, float* C, float* Q_ff, int32_t accumulate,

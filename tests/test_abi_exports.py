@@ -183,3 +183,22 @@ def test_absorb_solve_ex_validation_needs_no_gpu():
     assert lib.ispa_absorb_solve_ex(128, 64, 1, ok, ok, ok, 0.01, None, 2, ok, None, ok, None, 0, None) == bad
     assert lib.ispa_absorb_solve_ex(128, 64, 1, ok, ok, ok, -1.0, None, 0, ok, None, ok, None, 0, None) == bad
     assert lib.ispa_absorb_solve_ex(100, 64, 1, ok, ok, ok, 0.01, None, 1, ok, None, ok, None, 0, None) == bad
+
+
+def test_size_limits_are_rejected_without_a_gpu():
+    """The documented size limits (fewer than 2^31 elements in each attention tensor, n_rows * d
+    below 2^40 for the Gram) are checked before any HIP call.  Only the rejected side is exercised
+    here: an accepted call would go on to the device.  (The LSE bound H * n_q < 2^31 follows from
+    the bound on Q, since D >= 64.)"""
+    lib = ispa.load_library()
+    ok = ctypes.c_void_p(0x10000)
+    args = [ok, ok, ok, ok, ok] + [None] * 6
+    for n_q, n_loc, n_hist in ((1 << 20, 8, 0),             # Q: 2^20 * 16 * 128 = 2^31 elements
+                               (8, (1 << 20) - 8, 8),       # keys: n_loc + n_hist = 2^20
+                               (8, 8, 1 << 20)):
+        desc = ispa.AttnDesc(16, 128, n_q, n_loc, n_hist, 0.1, ispa.ISPA_BF16)
+        assert lib.ispa_decomp_attn(ctypes.byref(desc), *args, None, 0, None) == ispa.ISPA_E_INVALID_ARG
+        assert b"too large" in lib.ispa_last_error()
+    assert lib.ispa_gram_accum(1 << 30, 1024, ispa.ISPA_BF16, ok, ok, ok, ok, None, 0, None, 0,
+                               None) == ispa.ISPA_E_INVALID_ARG
+    assert b"too many rows" in lib.ispa_last_error()
