@@ -43,11 +43,11 @@
  *   that share a workspace must not run concurrently.
  * - Calls only enqueue work on `stream` (a hipStream_t; NULL = default
  *   stream) and return; results are valid once the stream is synchronised.
- *   The absorb solves also run R = C W on a second stream the library owns
- *   (one per device, default priority, created with its two events on the
- *   first solve and kept until the process ends), forked from and joined back
- *   to `stream` with events, so the call stays ordered on `stream` and can be
- *   captured into a graph once that first solve has run outside capture.
+ *   The library creates no streams or events and keeps no state between
+ *   calls besides its loaded kernels.  ispa_absorb_solve_ex can also use a
+ *   second stream the CALLER owns (ispa_side_stream_t), forked from and joined
+ *   back to `stream` with the caller's events inside the call, so the call
+ *   stays ordered on `stream` and can be captured into a graph.
  * - Inputs must not alias outputs (the one exception is W_new == W).
  * - Layouts: Q, K, V and O are [tokens, heads, head_dim] contiguous, so an O
  *   buffer is also the row-major [tokens, d] matrix A with d = heads*head_dim
@@ -487,21 +487,41 @@ ispa_status_t ispa_absorb_solve_lambdas(int32_t d, int32_t d_out, int32_t batch,
 /* Flag of ispa_absorb_solve_ex: skip the float64-residual refinement step. */
 #define ISPA_ABSORB_NO_REFINE 1
 
+/* A second stream the caller owns, with two events the caller owns, for
+ * ispa_absorb_solve_ex: R = C W runs on `stream` beside the factorisation on
+ * the call's main stream.  `stream` (hipStream_t) must differ from the main
+ * stream and should have the default priority; `ev_fork`, `ev_join`
+ * (hipEvent_t, timing may be disabled) are recorded and waited on inside the
+ * call: the side stream waits for the main stream's earlier work before R =
+ * C W, and the main stream waits for R = C W before the solve reads it, on
+ * every return after the fork (error returns included).  Calls that share one
+ * side stream and its events must be enqueued from one host thread at a time
+ * (the event record / wait pairs must not interleave). */
+typedef struct {
+  void* stream;
+  void* ev_fork;
+  void* ev_join;
+} ispa_side_stream_t;
+
 /*
  * ispa_absorb_solve_ex — ispa_absorb_solve with options: lambda from the
  * DEVICE array lambdas [batch] when it is non-NULL (else the scalar lambda),
- * and flags.  ISPA_ABSORB_NO_REFINE skips the refinement step (the float64
+ * flags, and an optional caller-owned side stream (`side`, NULL = everything
+ * on `stream`; ispa_absorb_solve and ispa_absorb_solve_lambdas run everything
+ * on `stream`).  ISPA_ABSORB_NO_REFINE skips the refinement step (the float64
  * residual and the second pair of triangular products, ~40 % of the solve at
  * d = 5120): dW is then the float32 solve, whose error grows like
  * cond(G + lambda I) * 2^-24 instead of reaching the float32 statistics'
- * own accuracy.  Same workspace and errors as ispa_absorb_solve.
+ * own accuracy.  Same workspace and errors as ispa_absorb_solve; a `side`
+ * with a NULL member, or a side stream equal to `stream`, is
+ * ISPA_E_INVALID_ARG.
  * Source: ISPA technical summary, section 2, step 2 "Layer Absorb" (ridge objective
  * and its closed-form solution).
  */
 ispa_status_t ispa_absorb_solve_ex(int32_t d, int32_t d_out, int32_t batch, const float* G, const float* C,
                                    const float* W, float lambda, const float* lambdas, int32_t flags, float* dW,
                                    float* W_new, int32_t* info, void* workspace, size_t workspace_bytes,
-                                   void* stream);
+                                   const ispa_side_stream_t* side, void* stream);
 
 /*
  * ispa_select_layers_below — convert every layer whose error is at most tau,
@@ -547,7 +567,8 @@ const char* ispa_status_string(ispa_status_t status);
  * Support call: no passage of the pages defines it. */
 const char* ispa_last_error(void);
 
-/* Library version, major*10000 + minor*100 + patch. */
+/* Library version, major*10000 + minor*100 + patch.
+ * Support call: no passage of the pages defines it. */
 int32_t ispa_version(void);
 
 /* ISPA_OK if `device` is a gfx950 GPU, else ISPA_E_UNSUPPORTED (or ISPA_E_HIP).

@@ -464,17 +464,26 @@ ispa_status_t ispa_absorb_solve_lambdas(int32_t d, int32_t d_out, int32_t batch,
 ispa_status_t ispa_absorb_solve_ex(int32_t d, int32_t d_out, int32_t batch, const float* G, const float* C,
                                    const float* W, float lambda, const float* lambdas, int32_t flags, float* dW,
                                    float* W_new, int32_t* info, void* workspace, size_t workspace_bytes,
-                                   void* stream) {
+                                   const ispa_side_stream_t* side, void* stream) {
   if (d <= 0 || d % 64 != 0 || d_out <= 0 || d_out % 64 != 0) return invalid("d and d_out must be multiples of 64");
   if (batch < 1 || batch > 65535) return invalid("batch must be in [1, 65535]");
   if ((flags & ~ISPA_ABSORB_NO_REFINE) != 0) return invalid("unknown flags");
   if (lambdas == nullptr && (!(lambda >= 0.f) || lambda == INFINITY)) return invalid("lambda must be finite and >= 0");
   if (!req(G) || !req(C) || !req(W) || !opt(lambdas) || !req(dW) || !req(info) || !opt(W_new))
     return invalid("G, C, W, dW, info must be non-NULL and 16-byte aligned");
+  SideStream ss = {};
+  if (side != nullptr) {
+    if (side->stream == nullptr || side->ev_fork == nullptr || side->ev_join == nullptr)
+      return invalid("side stream: stream, ev_fork and ev_join must all be given");
+    if (side->stream == stream) return invalid("side stream must differ from the main stream");
+    ss.stream = (hipStream_t)side->stream;
+    ss.ev_fork = (hipEvent_t)side->ev_fork;
+    ss.ev_join = (hipEvent_t)side->ev_join;
+  }
   ispa_status_t st = check_current_device();
   if (st != ISPA_OK) return st;
   return launch_absorb(d, d_out, batch, G, C, W, lambda, lambdas, dW, W_new, info, workspace, workspace_bytes,
-                       (hipStream_t)stream, (flags & ISPA_ABSORB_NO_REFINE) == 0);
+                       (hipStream_t)stream, (flags & ISPA_ABSORB_NO_REFINE) == 0, side ? &ss : nullptr);
 }
 
 ispa_status_t ispa_lambda_from_trace(int32_t d, int32_t batch, const float* G, float lam_scale, float* lambdas,

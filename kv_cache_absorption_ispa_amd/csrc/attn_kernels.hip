@@ -29,9 +29,6 @@
 //    runs in registers from the float32 O_loc and O_full is rounded once.
 //  * Scores are scaled by scale*log2(e) and exponentiated with v_exp_f32
 //    (2^x); LSE is exported in natural log.
-#include <cstdlib>
-#include <string>
-
 #include "ispa_internal.h"
 
 namespace ispa {
@@ -880,33 +877,14 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(MergeParams p) {
 
 }  // namespace
 
-// Default 8 waves x 32 queries with 128-key tiles (256 queries share each
-// staged tile; two waves per SIMD; 128 KB of LDS for the double-buffered K and
-// V tiles; 2 % faster than 64-key tiles, which halve the per-tile barrier,
-// load issue and row-max finishing).  ISPA_ATTN_SHAPE overrides it (a tuning
-// knob read once per process): "8x1x64" = 64-key tiles, "4x1" = 4 waves x 32
-// queries with 64-key tiles (two workgroups per CU).
-struct AttnShape {
-  int nw, bn;
-};
-AttnShape attn_shape() {
-  static const AttnShape v = [] {
-    const char* e = getenv("ISPA_ATTN_SHAPE");
-    if (e && std::string(e) == "4x1") return AttnShape{4, 64};
-    if (e && std::string(e) == "8x1x64") return AttnShape{8, 64};
-    return AttnShape{8, 128};
-  }();
-  return v;
-}
+// One shape: 8 waves x 32 queries with 128-key tiles (256 queries share each staged tile; two waves
+// per SIMD; 128 KB of LDS for the double-buffered K and V tiles).  Measured against 64-key tiles
+// (2 % slower: twice the per-tile barrier, load issue and row-max finishing) and 4 waves x 32 queries.
+constexpr int ATTN_NW = 8, ATTN_BN = 128, ATTN_BM = ATTN_NW * 32;
 
 template <int D, bool SK>
-void launch_bf16(const AttnShape sh, dim3 grid, hipStream_t s, const AttnKParams& p) {
-  if (sh.nw == 4)
-    hipLaunchKernelGGL((attn_bf16_kernel<D, 4, 1, 64, SK>), grid, dim3(256), 0, s, p);
-  else if (sh.bn == 128)
-    hipLaunchKernelGGL((attn_bf16_kernel<D, 8, 1, 128, SK>), grid, dim3(512), 0, s, p);
-  else
-    hipLaunchKernelGGL((attn_bf16_kernel<D, 8, 1, 64, SK>), grid, dim3(512), 0, s, p);
+void launch_bf16(dim3 grid, hipStream_t s, const AttnKParams& p) {
+  hipLaunchKernelGGL((attn_bf16_kernel<D, ATTN_NW, 1, ATTN_BN, SK>), grid, dim3(ATTN_NW * 64), 0, s, p);
 }
 
 size_t stash_bytes(int64_t n_q, int32_t heads, int32_t head_dim, int64_t n_hist) {
@@ -933,7 +911,6 @@ ispa_status_t launch_attention(const AttnArgs& a, hipStream_t s) {
       set_error("ispa_decomp_attn: workspace too small for the merge (query ispa_decomp_attn_workspace_size)");
       return ISPA_E_WORKSPACE;
     }
-    const AttnShape sh = a.k_fp8 ? AttnShape{8, 128} : attn_shape();
     p.q_scale = a.q_scale;
     p.n_seg = a.kv.n_seg;
     p.n_loc_seg = a.kv.n_loc_seg;
@@ -944,9 +921,9 @@ ispa_status_t launch_attention(const AttnArgs& a, hipStream_t s) {
       p.Vs[i] = used ? (const uint16_t*)a.kv.V[i] : nullptr;
       p.sn[i] = used ? (int)a.kv.n[i] : 0;
       p.k_scale[i] = used ? a.k_scale[i] : nullptr;
-      p.st0[i + 1] = p.st0[i] + (int)((p.sn[i] + sh.bn - 1) / sh.bn);
+      p.st0[i + 1] = p.st0[i] + (int)((p.sn[i] + ATTN_BN - 1) / ATTN_BN);
     }
-    const int bm = sh.nw * 32;
+    const int bm = ATTN_BM;
     p.n_qtiles = (int)((a.n_q + bm - 1) / bm);
     p.nblocks = p.n_qtiles * a.heads;
     p.sk_p = 1;
@@ -954,17 +931,17 @@ ispa_status_t launch_attention(const AttnArgs& a, hipStream_t s) {
     if (a.k_fp8) {
       const dim3 grid(p.nblocks);
       if (a.head_dim == 128)
-        hipLaunchKernelGGL((attn_bf16_kernel<128, 8, 1, 128, false, true>), grid, dim3(512), 0, s, p);
+        hipLaunchKernelGGL((attn_bf16_kernel<128, ATTN_NW, 1, ATTN_BN, false, true>), grid, dim3(ATTN_NW * 64), 0, s, p);
       else
-        hipLaunchKernelGGL((attn_bf16_kernel<64, 8, 1, 128, false, true>), grid, dim3(512), 0, s, p);
+        hipLaunchKernelGGL((attn_bf16_kernel<64, ATTN_NW, 1, ATTN_BN, false, true>), grid, dim3(ATTN_NW * 64), 0, s, p);
       return hip_check(hipGetLastError(), "attn_bf16_kernel (fp8 keys) launch");
     }
     if (a.sk_workers <= 0) {
       const dim3 grid(p.nblocks);
       if (a.head_dim == 128)
-        launch_bf16<128, false>(sh, grid, s, p);
+        launch_bf16<128, false>(grid, s, p);
       else
-        launch_bf16<64, false>(sh, grid, s, p);
+        launch_bf16<64, false>(grid, s, p);
       return hip_check(hipGetLastError(), "attn_bf16_kernel launch");
     }
     // split mode: each unit's key tiles cut into P pieces on P workgroups of its XCD
@@ -979,16 +956,16 @@ ispa_status_t launch_attention(const AttnArgs& a, hipStream_t s) {
     if (p.sk_p <= 1) {  // nothing to split: the unsplit launch
       const dim3 grid(p.nblocks);
       if (a.head_dim == 128)
-        launch_bf16<128, false>(sh, grid, s, p);
+        launch_bf16<128, false>(grid, s, p);
       else
-        launch_bf16<64, false>(sh, grid, s, p);
+        launch_bf16<64, false>(grid, s, p);
       return hip_check(hipGetLastError(), "attn_bf16_kernel launch");
     }
     const dim3 grid(a.sk_workers);
     if (a.head_dim == 128)
-      launch_bf16<128, true>(sh, grid, s, p);
+      launch_bf16<128, true>(grid, s, p);
     else
-      launch_bf16<64, true>(sh, grid, s, p);
+      launch_bf16<64, true>(grid, s, p);
     ispa_status_t st = hip_check(hipGetLastError(), "attn_bf16_kernel (split) launch");
     if (st != ISPA_OK) return st;
     FixupParams f;
@@ -1050,7 +1027,7 @@ size_t attention_workspace_size(int64_t n_q, int32_t heads, int32_t head_dim, in
 
 size_t splitkv_workspace_size(int64_t n_q, int32_t heads, int32_t head_dim, int64_t n_hist, int32_t n_workers) {
   if (n_q <= 0 || n_workers <= 0) return 0;
-  const int bm = attn_shape().nw * 32;
+  const int bm = ATTN_BM;
   return stash_bytes(n_q, heads, head_dim, n_hist) + (size_t)n_workers * part_slot_floats(bm, head_dim) * 4;
 }
 

@@ -82,9 +82,15 @@ ispa_status_t launch_gram(int64_t n_rows, int32_t d, int32_t dtype, const void* 
                           hipStream_t s);
 
 size_t absorb_workspace_size(int32_t d, int32_t d_out, int32_t batch);
+// A caller-owned second stream and its fork / join events (see ispa_side_stream_t).
+struct SideStream {
+  hipStream_t stream;
+  hipEvent_t ev_fork, ev_join;
+};
 ispa_status_t launch_absorb(int32_t d, int32_t d_out, int32_t batch, const float* G, const float* C,
                             const float* W, float lambda, const float* lam_b, float* dW, float* W_new,
-                            int32_t* info, void* ws, size_t ws_bytes, hipStream_t s, bool refine = true);
+                            int32_t* info, void* ws, size_t ws_bytes, hipStream_t s, bool refine = true,
+                            const SideStream* side = nullptr);
 size_t fit_error_workspace_size(int32_t d, int32_t d_out, int32_t batch);
 ispa_status_t launch_fit_error(int32_t d, int32_t d_out, int32_t batch, const float* G, const float* C,
                                const float* Qff, const float* W, const float* dW, double* eps_abs, double* eps_rel,

@@ -10,7 +10,8 @@
 //
 // Structure (nb = 64 column panels, right-looking):
 //   M = G + lambda I (lambda scalar or per layer)      (init kernel)
-//   R = C W in float32                                 (GEMM, on a second stream beside the factorisation)
+//   R = C W in float32                                 (GEMM; on the caller's side stream, if given, beside
+//                                                       the factorisation)
 //   factor M_00 = L_00 L_00^T and invert L_00        (one workgroup per layer)
 //   for each panel k:
 //     L_ik = M_ik L_kk^-T                             (GEMM, in place)
@@ -31,8 +32,6 @@
 // set to NaN at the end and its W_new is left alone.
 #include <utility>
 #include <vector>
-
-#include <mutex>
 
 #include "ispa_internal.h"
 
@@ -715,39 +714,28 @@ ispa_status_t invert_lower(hipStream_t s, int batch, int d, const float* L, floa
   return ISPA_OK;
 }
 
-// A second stream per device for R = C W beside the latency-bound factorisation, with its fork and
-// join events (created once, kept until the process ends; default priority).  The enqueue of one
-// solve holds the mutex, so the events' record/wait pairs of two host threads never interleave.
 namespace {
-struct AuxStream {
-  hipStream_t s2 = nullptr;
-  std::vector<hipEvent_t> ev;
+// After R = C W has been forked onto the caller's side stream, every return joins the side stream
+// back to the main one, error returns included: the call then leaves nothing unordered against the
+// caller's stream and never breaks a graph capture in progress.
+struct SideJoin {
+  hipStream_t s = nullptr, s2 = nullptr;
+  hipEvent_t ev = nullptr;
+  bool armed = false;
+  ispa_status_t join() {
+    if (!armed) return ISPA_OK;
+    armed = false;
+    ispa_status_t st = hip_check(hipEventRecord(ev, s2), "hipEventRecord (join)");
+    const ispa_status_t st2 = hip_check(hipStreamWaitEvent(s, ev, 0), "hipStreamWaitEvent (join)");
+    return st != ISPA_OK ? st : st2;
+  }
+  ~SideJoin() { join(); }
 };
-std::mutex g_aux_mu;
-AuxStream g_aux[64];
 }  // namespace
-
-static ispa_status_t aux_stream(int n_events, AuxStream*& out) {
-  int dev = 0;
-  ISPA_TRY(hip_check(hipGetDevice(&dev), "hipGetDevice"));
-  if (dev < 0 || dev >= 64) {
-    set_error("device index above 63");
-    return ISPA_E_UNSUPPORTED;
-  }
-  AuxStream& a = g_aux[dev];
-  if (a.s2 == nullptr) ISPA_TRY(hip_check(hipStreamCreateWithFlags(&a.s2, hipStreamNonBlocking), "hipStreamCreate"));
-  while ((int)a.ev.size() < n_events) {
-    hipEvent_t e;
-    ISPA_TRY(hip_check(hipEventCreateWithFlags(&e, hipEventDisableTiming), "hipEventCreate"));
-    a.ev.push_back(e);
-  }
-  out = &a;
-  return ISPA_OK;
-}
 
 ispa_status_t launch_absorb(int32_t d, int32_t d_out, int32_t batch, const float* G, const float* C, const float* W,
                             float lambda, const float* lam_b, float* dW, float* W_new, int32_t* info, void* ws,
-                            size_t ws_bytes, hipStream_t s, bool refine) {
+                            size_t ws_bytes, hipStream_t s, bool refine, const SideStream* side) {
   const size_t need = absorb_workspace_size(d, d_out, batch);
   if (ws == nullptr || ws_bytes < need) {
     set_error("ispa_absorb_solve: workspace too small");
@@ -762,26 +750,29 @@ ispa_status_t launch_absorb(int32_t d, int32_t d_out, int32_t batch, const float
   float* Zb = Rr + (size_t)batch * dn;
   const int nblk = d / NB;
 
-  std::lock_guard<std::mutex> lock(g_aux_mu);
-  AuxStream* aux = nullptr;
-  ISPA_TRY(aux_stream(2, aux));
-  hipStream_t s2 = aux->s2;
-  hipEvent_t* ev = aux->ev.data();  // [0] fork, [1] join
-
   hipLaunchKernelGGL(init_shift_kernel, dim3((unsigned)((dd / 4 + 255) / 256), batch), dim3(256), 0, s, G, M, Linvf,
                      d, lambda, lam_b, info);
   ISPA_TRY(hip_check(hipGetLastError(), "init_shift_kernel launch"));
-  // R = C W on the second stream, beside the factorisation (float32; R's rounding perturbs the
-  // solution like the float32 statistics themselves do).  For small d it is forked after the first
-  // panel steps: sharing the GPU with it would slow the first diagonal factorisations, which sit on
-  // the latency-bound chain (d = 1536: 1.36 -> 1.33 ms per solve); at d = 5120 it goes first.
+  // R = C W (float32; R's rounding perturbs the solution like the float32 statistics themselves do).
+  // With a caller-owned side stream it runs there, beside the latency-bound factorisation; for small
+  // d it is forked after the first panel steps, since sharing the GPU with it would slow the first
+  // diagonal factorisations, which sit on the chain (d = 1536: 1.36 -> 1.33 ms per solve); at
+  // d = 5120 it goes first.  Without a side stream it runs on `s` before the factorisation.
+  SideJoin joiner;
   auto fork_cw = [&]() -> ispa_status_t {
-    ISPA_TRY(hip_check(hipEventRecord(ev[0], s), "hipEventRecord"));
-    ISPA_TRY(hip_check(hipStreamWaitEvent(s2, ev[0], 0), "hipStreamWaitEvent"));
-    return gemm<false, false>(s2, batch, d, d_out, d, C, d, dd, W, d_out, dn, nullptr, 0, 0, Rb, d_out, dn, 1.f, 0.f,
-                              false, nullptr);
+    if (side == nullptr)
+      return gemm<false, false>(s, batch, d, d_out, d, C, d, dd, W, d_out, dn, nullptr, 0, 0, Rb, d_out, dn, 1.f,
+                                0.f, false, nullptr);
+    ISPA_TRY(hip_check(hipEventRecord(side->ev_fork, s), "hipEventRecord (fork)"));
+    ISPA_TRY(hip_check(hipStreamWaitEvent(side->stream, side->ev_fork, 0), "hipStreamWaitEvent (fork)"));
+    joiner.s = s;
+    joiner.s2 = side->stream;
+    joiner.ev = side->ev_join;
+    joiner.armed = true;
+    return gemm<false, false>(side->stream, batch, d, d_out, d, C, d, dd, W, d_out, dn, nullptr, 0, 0, Rb, d_out, dn,
+                              1.f, 0.f, false, nullptr);
   };
-  const int fork_k = d <= 2048 ? 4 : -1;  // panel step before which it is forked (-1: right away)
+  const int fork_k = (side != nullptr && d <= 2048) ? 4 : -1;  // panel step before which it is forked (-1: first)
   bool forked = false;
   if (fork_k < 0) {
     ISPA_TRY(fork_cw());
@@ -813,8 +804,7 @@ ispa_status_t launch_absorb(int32_t d, int32_t d_out, int32_t batch, const float
   }
   if (!forked) ISPA_TRY(fork_cw());
   // join: R = C W is done before the solve reads it
-  ISPA_TRY(hip_check(hipEventRecord(ev[1], s2), "hipEventRecord"));
-  ISPA_TRY(hip_check(hipStreamWaitEvent(s, ev[1], 0), "hipStreamWaitEvent"));
+  ISPA_TRY(joiner.join());
   // explicit L^-1 by recursive doubling over block ranges: for adjacent ranges A (first) and C,
   // inv([A 0; B C]) has off-diagonal block -C^-1 (B A^-1); pairs of equal sizes run as one launch.
   ISPA_TRY(invert_lower(s, batch, d, M, Linvf, Tb, info));

@@ -227,6 +227,24 @@ def custom_inputs(seed: int, n_q: int, n_loc: int, n_hist: int, heads: int, head
                        _encode(kh, dtype), _encode(vh, dtype))
 
 
+def planted_inputs(seed: int, n_q: int, n_loc: int, n_hist: int, heads: int, head_dim: int, dtype: str,
+                   loc_rows=(), hist_rows=(), factor: float = 24.0, boost_rows: int = 8) -> ChunkInputs:
+    """custom_inputs with some keys made dominant late in a branch: the K rows listed in ``loc_rows``
+    (local) and ``hist_rows`` (history), all heads, are multiplied by ``factor`` before rounding.
+    Their scores spread over ``factor`` times the usual range, so for many queries such a key beats
+    every earlier key of its branch by a wide margin (the online softmax then has to move its
+    reference maximum in the middle of the branch)."""
+    x = custom_inputs(seed, n_q, n_loc, n_hist, heads, head_dim, "f32", boost_rows=boost_rows)
+    kl = x.k_loc.raw.copy()
+    kh = x.k_hist.raw.copy()
+    for r in loc_rows:
+        kl[r] *= np.float32(factor)
+    for r in hist_rows:
+        kh[r] *= np.float32(factor)
+    return ChunkInputs(_encode(x.q.raw, dtype), _encode(kl, dtype), _encode(x.v_loc.raw, dtype),
+                       _encode(kh, dtype), _encode(x.v_hist.raw, dtype))
+
+
 @dataclass
 class StreamChunk:
     q: Tensor  # [n_q, H, D]
@@ -266,7 +284,8 @@ def weight(cfg: LayerConfig, layer: int = 0, d_out: int | None = None, cfg_id: i
 # --------------------------------------------------------------------------- #
 # Stand-in attention rows for the Gram / solve step
 # --------------------------------------------------------------------------- #
-def absorb_rows(cfg_id: int, layer: int, n_rows: int, d: int, dtype: str, mismatch: float = 1.0):
+def absorb_rows(cfg_id: int, layer: int, n_rows: int, d: int, dtype: str, mismatch: float = 1.0,
+                diff_scale: float = 1.0):
     """Stand-in rows (A_loc, A_full), each [n_rows, d], for testing the Gram and solve step.
 
     The Gram/solve step consumes attention outputs; a test of it may not take its
@@ -278,7 +297,9 @@ def absorb_rows(cfg_id: int, layer: int, n_rows: int, d: int, dtype: str, mismat
     component give, at that size, condition number 1.9e5, eigenvalues
     0.16..3.1e4 and rms 0.20.  A_full is A_loc plus a per-column modulation and
     independent noise (so the ridge solution is non-trivial).  ``mismatch`` scales the noise part, giving
-    layers of a stack different reconstruction errors.
+    layers of a stack different reconstruction errors.  ``diff_scale`` scales the whole difference
+    A_full - A_loc (modulation and noise): small values give layers whose full and local rows nearly
+    agree (the layers a stack converts first).
     """
     g = rng_for(cfg_id, layer, LAYER_CHUNK, T_AROW_BASE)
     perm = g.permutation(d).astype(np.float32)
@@ -289,5 +310,8 @@ def absorb_rows(cfg_id: int, layer: int, n_rows: int, d: int, dtype: str, mismat
     u = normal(cfg_id, layer, LAYER_CHUNK, T_AROW_BASE + 2, (n_rows, 1))
     e = normal(cfg_id, layer, LAYER_CHUNK, T_AROW_BASE + 3, (n_rows, d))
     a_loc = z * s + u * b
-    a_full = a_loc * (np.float32(1.0) + m) + np.float32(0.3 * mismatch) * e * s
+    if diff_scale == 1.0:
+        a_full = a_loc * (np.float32(1.0) + m) + np.float32(0.3 * mismatch) * e * s
+    else:
+        a_full = a_loc + np.float32(diff_scale) * (a_loc * m + np.float32(0.3 * mismatch) * e * s)
     return _encode(a_loc.astype(np.float32), dtype), _encode(a_full.astype(np.float32), dtype)

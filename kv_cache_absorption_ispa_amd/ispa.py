@@ -58,6 +58,10 @@ class KvSegmentFp8k(ctypes.Structure):
                 ("n_rows", ctypes.c_int64)]
 
 
+class SideStreamDesc(ctypes.Structure):
+    _fields_ = [("stream", ctypes.c_void_p), ("ev_fork", ctypes.c_void_p), ("ev_join", ctypes.c_void_p)]
+
+
 ISPA_MAX_KV_SEGMENTS = 16
 ISPA_MAX_SPLITKV_WORKERS = 65535
 
@@ -95,7 +99,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "ispa_fit_error": (I32, [I32, I32, I32, P, P, P, P, P, P, P, P, SZ, P]),
         "ispa_lambda_from_trace": (I32, [I32, I32, P, F, P, P]),
         "ispa_absorb_solve_lambdas": (I32, [I32, I32, I32, P, P, P, P, P, P, P, P, SZ, P]),
-        "ispa_absorb_solve_ex": (I32, [I32, I32, I32, P, P, P, F, P, I32, P, P, P, P, SZ, P]),
+        "ispa_absorb_solve_ex": (I32, [I32, I32, I32, P, P, P, F, P, I32, P, P, P, P, SZ,
+                                       ctypes.POINTER(SideStreamDesc), P]),
         "ispa_select_layers_below": (I32, [I32, P, ctypes.c_double, I32, P, P, P, P]),
         "ispa_gather_layers": (I32, [I32, I64, P, P, I32, P, P]),
         "ispa_absorb_apply_compact": (I32, [I32, I32, I32, P, I32, P, P, P]),
@@ -439,9 +444,24 @@ def ispa_absorb_solve_lambdas(G, C, W, lambdas, dW, info, *, W_new=None, workspa
 ISPA_ABSORB_NO_REFINE = 1
 
 
+class SideStream:
+    """A caller-owned second stream and its fork / join events for ispa_absorb_solve_ex (created here,
+    outside any hot-path call, and kept alive by this object)."""
+
+    def __init__(self, device=None):
+        self.stream = torch.cuda.Stream(device=device)
+        self.ev_fork = torch.cuda.Event()
+        self.ev_join = torch.cuda.Event()
+        # torch creates an event's handle on its first record
+        self.ev_fork.record(self.stream)
+        self.ev_join.record(self.stream)
+        self.desc = SideStreamDesc(self.stream.cuda_stream, self.ev_fork.cuda_event, self.ev_join.cuda_event)
+
+
 def ispa_absorb_solve_ex(G, C, W, lam: float, dW, info, *, lambdas=None, refine: bool = True, W_new=None,
-                         workspace=None, stream=None) -> None:
-    """ispa_absorb_solve with a per-layer lambda (``lambdas``, device float32) and the refinement optional."""
+                         workspace=None, side: Optional[SideStream] = None, stream=None) -> None:
+    """ispa_absorb_solve with a per-layer lambda (``lambdas``, device float32), the refinement optional and
+    R = C W on a caller-owned side stream (``side``) beside the factorisation."""
     G3, W3 = _as3(G), _as3(W)
     b, d, _ = G3.shape
     d_out = W3.shape[2]
@@ -457,7 +477,8 @@ def ispa_absorb_solve_ex(G, C, W, lam: float, dW, info, *, lambdas=None, refine:
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load_library().ispa_absorb_solve_ex(d, d_out, b, _ptr(G), _ptr(C), _ptr(W), float(lam), _ptr(lambdas),
                                                0 if refine else ISPA_ABSORB_NO_REFINE, _ptr(dW), _ptr(W_new),
-                                               _ptr(info), _ptr(workspace), ws_bytes, _stream(stream)))
+                                               _ptr(info), _ptr(workspace), ws_bytes,
+                                               None if side is None else ctypes.byref(side.desc), _stream(stream)))
 
 
 def ispa_select_layers_below(eps, tau: float, k_max: int, selected, count, rank=None, *, stream=None) -> None:

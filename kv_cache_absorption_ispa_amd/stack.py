@@ -24,11 +24,26 @@ converted.  The pages leave the error, lambda and k open; the other readings:
 """
 from __future__ import annotations
 
+import contextlib
+import functools
 from typing import List, Optional
 
 import torch
 
 from . import ispa
+
+
+def _on_stack_stream(method):
+    """Run a LayerStack method with its stream as torch's current stream: the library calls are then
+    enqueued on it, temporaries come from that stream's pool (freed only behind its work), and host
+    reads of device values (the converted set) wait for it."""
+
+    @functools.wraps(method)
+    def wrapper(self, *args, **kwargs):
+        with self._stream_ctx():
+            return method(self, *args, **kwargs)
+
+    return wrapper
 
 
 class LayerStack:
@@ -88,9 +103,16 @@ class LayerStack:
         # workspaces, sized once
         self._gram_ws = None
         self._attn_ws = None
-        self._absorb_ws = ispa.workspace(ispa.ispa_absorb_workspace_size(d, do, L), dev)
-        self._eps_ws = ispa.workspace(max(ispa.ispa_fit_error_workspace_size(d, do, L),
-                                          ispa.ispa_eps_workspace_size(d, do, L)), dev)
+        with self._stream_ctx():
+            self._absorb_ws = ispa.workspace(ispa.ispa_absorb_workspace_size(d, do, L), dev)
+            self._eps_ws = ispa.workspace(max(ispa.ispa_fit_error_workspace_size(d, do, L),
+                                              ispa.ispa_eps_workspace_size(d, do, L)), dev)
+        # R = C W of the absorb solves runs on this second stream beside the factorisation (owned here,
+        # created once, outside the hot path)
+        self.side = ispa.SideStream(dev)
+
+    def _stream_ctx(self):
+        return torch.cuda.stream(self.stream) if self.stream is not None else contextlib.nullcontext()
 
     def reset(self) -> None:
         """Start a new warmup with the same buffers (W is the caller's; restore it first if needed)."""
@@ -101,6 +123,7 @@ class LayerStack:
         self.dW_compact = self.info_compact = None
 
     # ------------------------------------------------------------------ warmup
+    @_on_stack_stream
     def warmup_chunk(self, layer: int, q, k_loc, v_loc, k_hist, v_hist, o_loc, o_full,
                      lse_loc=None, lse_full=None, heldout: bool = False) -> None:
         """Dual-stream attention of one chunk of `layer`, then its rows into the layer's G, C, Q_ff.
@@ -113,9 +136,10 @@ class LayerStack:
         if need and (self._attn_ws is None or self._attn_ws.numel() < need):
             self._attn_ws = ispa.workspace(need, q.device)
         ispa.ispa_decomp_attn(q, k_loc, v_loc, k_hist, v_hist, o_loc=o_loc, lse_loc=lse_loc, o_full=o_full,
-                              lse_full=lse_full, workspace=self._attn_ws, stream=self.stream)
+                              lse_full=lse_full, workspace=self._attn_ws)
         self.accumulate_rows(layer, o_loc, o_full, heldout=heldout)
 
+    @_on_stack_stream
     def accumulate_rows(self, layer: int, a_loc, a_full, heldout: bool = False) -> None:
         """Add warmup rows computed elsewhere ([n, d] or [n, H, D]) to the layer's G, C, Q_ff (or, with
         ``heldout`` under selection="heldout", to the held-out statistics the ranking is measured on)."""
@@ -129,15 +153,15 @@ class LayerStack:
             self._gram_ws = ispa.workspace(need, a_loc.device)
         if heldout:
             ispa.ispa_gram_accum(a_loc, a_full, self.G_h[layer], self.C_h[layer], self.Q_h[layer],
-                                 accumulate=self.heldout_seen[layer] > 0, workspace=self._gram_ws,
-                                 stream=self.stream)
+                                 accumulate=self.heldout_seen[layer] > 0, workspace=self._gram_ws)
             self.heldout_seen[layer] += 1
             return
         ispa.ispa_gram_accum(a_loc, a_full, self.G[layer], self.C[layer], self.Q_ff[layer],
-                             accumulate=self.chunks_seen[layer] > 0, workspace=self._gram_ws, stream=self.stream)
+                             accumulate=self.chunks_seen[layer] > 0, workspace=self._gram_ws)
         self.chunks_seen[layer] += 1
 
     # -------------------------------------------------------------- transition
+    @_on_stack_stream
     def transition(self) -> List[int]:
         """Solve every layer (batched), rank by eps_rel, convert the n_convert lowest: W += dW there.
 
@@ -154,39 +178,41 @@ class LayerStack:
 
     def _select(self) -> None:
         if self.threshold is None:
-            ispa.ispa_select_layers(self.eps_rel, self.n_convert, self.selected, self.rank, stream=self.stream)
+            ispa.ispa_select_layers(self.eps_rel, self.n_convert, self.selected, self.rank)
         else:
             ispa.ispa_select_layers_below(self.eps_rel, self.threshold, self.n_convert, self.selected, self.count,
-                                          self.rank, stream=self.stream)
+                                          self.rank)
 
     def _solve(self, G, C, W, dW, info, lambdas, workspace) -> None:
         if self.lam_policy == "trace":
-            ispa.ispa_lambda_from_trace(G, self.lam, lambdas, stream=self.stream)
-            ispa.ispa_absorb_solve_lambdas(G, C, W, lambdas, dW, info, workspace=workspace, stream=self.stream)
+            ispa.ispa_lambda_from_trace(G, self.lam, lambdas)
+            ispa.ispa_absorb_solve_ex(G, C, W, 0.0, dW, info, lambdas=lambdas, workspace=workspace, side=self.side)
         else:
-            ispa.ispa_absorb_solve(G, C, W, self.lam, dW, info, workspace=workspace, stream=self.stream)
+            ispa.ispa_absorb_solve_ex(G, C, W, self.lam, dW, info, workspace=workspace, side=self.side)
 
+    @_on_stack_stream
     def solve_and_rank(self) -> None:
         """The transition's device work before the weights change: solves, errors, ranking.
 
         prefit: errors at dW = 0 and ranking first; the chosen layers are solved in convert()."""
         if self.selection == "prefit":
             ispa.ispa_fit_error(self.G, self.C, self.Q_ff, self.W, None, self.eps_abs, self.eps_rel,
-                                workspace=self._eps_ws, stream=self.stream)
+                                workspace=self._eps_ws)
             self._select()
             return
         self._solve(self.G, self.C, self.W, self.dW, self.info, self.lambdas, self._absorb_ws)
         if self.selection == "heldout":
             ispa.ispa_fit_error(self.G_h, self.C_h, self.Q_h, self.W, self.dW, self.eps_abs, self.eps_rel,
-                                workspace=self._eps_ws, stream=self.stream)
+                                workspace=self._eps_ws)
         elif self.lam_policy == "trace":  # per-layer lambda: the general form (no normal-equation shortcut)
             ispa.ispa_fit_error(self.G, self.C, self.Q_ff, self.W, self.dW, self.eps_abs, self.eps_rel,
-                                workspace=self._eps_ws, stream=self.stream)
+                                workspace=self._eps_ws)
         else:
             ispa.ispa_layer_eps(self.G, self.C, self.Q_ff, self.W, self.dW, self.lam, self.eps_abs, self.eps_rel,
-                                workspace=self._eps_ws, stream=self.stream)
+                                workspace=self._eps_ws)
         self._select()
 
+    @_on_stack_stream
     def convert(self) -> List[int]:
         """W += dW on the selected layers; returns their ids (a host sync)."""
         if self.converted is not None:
@@ -201,17 +227,17 @@ class LayerStack:
             if k:
                 Gs, Cs = torch.empty(k, d, d, **f32), torch.empty(k, d, d, **f32)
                 Ws, dWs = torch.empty(k, d, do, **f32), torch.empty(k, d, do, **f32)
-                ispa.ispa_gather_layers(self.G, sel, Gs, stream=self.stream)
-                ispa.ispa_gather_layers(self.C, sel, Cs, stream=self.stream)
-                ispa.ispa_gather_layers(self.W, sel, Ws, stream=self.stream)
+                ispa.ispa_gather_layers(self.G, sel, Gs)
+                ispa.ispa_gather_layers(self.C, sel, Cs)
+                ispa.ispa_gather_layers(self.W, sel, Ws)
                 info = torch.empty(k, dtype=torch.int32, device=dev)
                 lambdas = torch.empty(k, **f32)
                 ws = ispa.workspace(ispa.ispa_absorb_workspace_size(d, do, k), dev)
                 self._solve(Gs, Cs, Ws, dWs, info, lambdas, ws)
-                ispa.ispa_absorb_apply_compact(sel, dWs, self.W, stream=self.stream)
+                ispa.ispa_absorb_apply_compact(sel, dWs, self.W)
                 self.dW_compact, self.info_compact = dWs, info
         else:
-            ispa.ispa_absorb_apply(sel, self.dW, self.W, stream=self.stream)
+            ispa.ispa_absorb_apply(sel, self.dW, self.W)
         self.converted = [int(x) for x in sel.cpu().tolist()]
         return self.converted
 
@@ -221,18 +247,19 @@ class LayerStack:
             raise ispa.IspaError(ispa.ISPA_E_INVALID_ARG, "transition has not run")
         return layer in self.converted
 
+    @_on_stack_stream
     def post_chunk(self, layer: int, q, k_loc, v_loc, k_hist, v_hist, o_full, lse_full=None) -> None:
         """Attention of one post-absorb chunk: local keys only for a converted layer (its history is
         evicted; ``k_hist`` / ``v_hist`` are ignored and may be None), all keys otherwise.
         ``o_full`` receives the layer's attention output."""
         if self.is_converted(layer):
-            ispa.ispa_decomp_attn(q, k_loc, v_loc, None, None, o_full=o_full, lse_full=lse_full, stream=self.stream)
+            ispa.ispa_decomp_attn(q, k_loc, v_loc, None, None, o_full=o_full, lse_full=lse_full)
             return
         need = ispa.ispa_decomp_attn_workspace_size(q, int(k_loc.shape[0]), int(k_hist.shape[0]))
         if need and (self._attn_ws is None or self._attn_ws.numel() < need):
             self._attn_ws = ispa.workspace(need, q.device)
         ispa.ispa_decomp_attn(q, k_loc, v_loc, k_hist, v_hist, o_full=o_full, lse_full=lse_full,
-                              workspace=self._attn_ws, stream=self.stream)
+                              workspace=self._attn_ws)
 
     # ------------------------------------------------------- streaming K/V cache
     def _attn_ws_for(self, q, n_loc: int, n_hist: int):
@@ -241,6 +268,7 @@ class LayerStack:
             self._attn_ws = ispa.workspace(need, q.device)
         return self._attn_ws
 
+    @_on_stack_stream
     def warmup_chunk_cached(self, layer: int, q, cache, o_loc, o_full, heldout: bool = False) -> None:
         """warmup_chunk with the keys taken from a StreamingKVCache: the layer's sink and current slot
         (local) and its history runs, attended in place.  The caller writes the chunk's K/V into
@@ -251,9 +279,10 @@ class LayerStack:
         n_loc = sum(int(k.shape[0]) for k, _ in loc)
         n_hist = sum(int(k.shape[0]) for k, _ in hist)
         ispa.ispa_decomp_attn_segments(q, loc, hist, o_loc=o_loc, o_full=o_full,
-                                       workspace=self._attn_ws_for(q, n_loc, n_hist), stream=self.stream)
+                                       workspace=self._attn_ws_for(q, n_loc, n_hist))
         self.accumulate_rows(layer, o_loc, o_full, heldout=heldout)
 
+    @_on_stack_stream
     def post_chunk_cached(self, layer: int, q, cache, o_full, lse_full=None) -> None:
         """Attention of a post-absorb chunk from the cache (a converted layer's cache holds no history
         once evict_converted ran, so it attends locally)."""
@@ -265,7 +294,7 @@ class LayerStack:
         n_loc = sum(int(k.shape[0]) for k, _ in loc)
         n_hist = sum(int(k.shape[0]) for k, _ in hist)
         ispa.ispa_decomp_attn_segments(q, loc, hist, o_full=o_full, lse_full=lse_full,
-                                       workspace=self._attn_ws_for(q, n_loc, n_hist), stream=self.stream)
+                                       workspace=self._attn_ws_for(q, n_loc, n_hist))
 
     def evict_converted(self, cache) -> int:
         """Drop the converted layers' history K/V from the cache; returns the bytes released."""

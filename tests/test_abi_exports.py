@@ -180,9 +180,18 @@ def test_absorb_solve_ex_validation_needs_no_gpu():
     lib = ispa.load_library()
     ok = 0x10000
     bad = ispa.ISPA_E_INVALID_ARG
-    assert lib.ispa_absorb_solve_ex(128, 64, 1, ok, ok, ok, 0.01, None, 2, ok, None, ok, None, 0, None) == bad
-    assert lib.ispa_absorb_solve_ex(128, 64, 1, ok, ok, ok, -1.0, None, 0, ok, None, ok, None, 0, None) == bad
-    assert lib.ispa_absorb_solve_ex(100, 64, 1, ok, ok, ok, 0.01, None, 1, ok, None, ok, None, 0, None) == bad
+    assert lib.ispa_absorb_solve_ex(128, 64, 1, ok, ok, ok, 0.01, None, 2, ok, None, ok, None, 0, None, None) == bad
+    assert lib.ispa_absorb_solve_ex(128, 64, 1, ok, ok, ok, -1.0, None, 0, ok, None, ok, None, 0, None, None) == bad
+    assert lib.ispa_absorb_solve_ex(100, 64, 1, ok, ok, ok, 0.01, None, 1, ok, None, ok, None, 0, None, None) == bad
+    # a side stream needs all three handles and must differ from the main stream
+    part = ispa.SideStreamDesc(0x20000, None, 0x30000)
+    assert lib.ispa_absorb_solve_ex(128, 64, 1, ok, ok, ok, 0.01, None, 0, ok, None, ok, None, 0,
+                                    ctypes.byref(part), None) == bad
+    assert b"side stream" in lib.ispa_last_error()
+    same = ispa.SideStreamDesc(0x20000, 0x30000, 0x40000)
+    assert lib.ispa_absorb_solve_ex(128, 64, 1, ok, ok, ok, 0.01, None, 0, ok, None, ok, None, 0,
+                                    ctypes.byref(same), 0x20000) == bad
+    assert b"differ" in lib.ispa_last_error()
 
 
 def test_size_limits_are_rejected_without_a_gpu():
