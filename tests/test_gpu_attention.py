@@ -32,7 +32,13 @@ def run_decomp(x: inputs.ChunkInputs, scale):
     return out
 
 
-def check_against_oracle(x, out, scale, tol_o, tol_lse, rows=None):
+# relative-Frobenius bound on the bf16 outputs of full-size chunks: the output rounding alone gives
+# ~2^-9 / sqrt(3) = 1.1e-3 and the bf16 P of the PV product about as much again (observed ~1.7e-3);
+# a systematic bias of a few tenths of a percent, invisible to the 2e-2 max-abs gate, fails it
+TOL_BF16_O_REL = 3e-3
+
+
+def check_against_oracle(x, out, scale, tol_o, tol_lse, rows=None, tol_rel=None):
     qh = x.q.f64 if rows is None else x.q.f64[rows]
     ref = oracle.branch_outputs(qh, x.k_loc.f64, x.v_loc.f64, x.k_hist.f64, x.v_hist.f64, scale)
     report = {}
@@ -42,6 +48,8 @@ def check_against_oracle(x, out, scale, tol_o, tol_lse, rows=None):
         e = maxabs(got, ref[name])
         report[name] = (e, relfro(got, ref[name]) if np.linalg.norm(ref[name]) > 0 else 0.0)
         assert e <= tol_o, (name, e)
+        if tol_rel is not None:
+            assert report[name][1] <= tol_rel, (name, report[name])
     for name in ("LSE_loc", "LSE_hist", "LSE_full"):
         got = out[name].cpu().numpy().astype(np.float64)
         got = got if rows is None else got[:, rows]
@@ -92,20 +100,44 @@ def test_tiny_fp32_config_all_chunks():
         check_against_oracle(x, out, cfg.scale, TOL_F32, TOL_F32)
 
 
-@pytest.mark.parametrize("cfg_name", ["wan1.3b-layer", "wan1.3b-long-history", "wan14b-layer"])
-def test_bf16_full_size_sampled_rows(cfg_name):
-    """Full-size layers in the benchmark's launch configuration; the oracle checks sampled query rows
-    (first and last tiles, the ragged tail, and random rows) over every head and output."""
+def _all_written(out):
+    for name, t in out.items():
+        assert not torch.isnan(t).any().item(), f"{name} has unwritten (NaN) elements"
+
+
+def test_bf16_full_chunk_every_row():
+    """The Wan-1.3B layer in the benchmark's launch configuration: every output element of a whole
+    warmup chunk (4680 queries x 12 heads, all three outputs and LSEs) against the oracle, with the
+    relative-Frobenius bound; and sampled rows of a later chunk."""
+    cfg = inputs.WAN13B_LAYER
+    say("config", cfg.name, "chunk 0, every row")
+    x = inputs.chunk_inputs(cfg, 0, 0)
+    out = run_decomp(x, cfg.scale)
+    _all_written(out)
+    say("report", check_against_oracle(x, out, cfg.scale, TOL_BF16_O, TOL_BF16_LSE, tol_rel=TOL_BF16_O_REL))
+    say("config", cfg.name, "chunk 2, sampled rows")
+    x = inputs.chunk_inputs(cfg, 0, 2)
+    out = run_decomp(x, cfg.scale)
+    _all_written(out)
+    g = np.random.default_rng(22)
+    rows = np.unique(np.concatenate([np.arange(250, 262), g.choice(cfg.n_q, 200, replace=False)]))
+    say("report", check_against_oracle(x, out, cfg.scale, TOL_BF16_O, TOL_BF16_LSE, rows=rows,
+                                       tol_rel=TOL_BF16_O_REL))
+
+
+@pytest.mark.parametrize("cfg_name", ["wan1.3b-long-history", "wan14b-layer"])
+def test_bf16_full_size_whole_tiles(cfg_name):
+    """Full-size layers in the benchmark's launch configuration: whole 256-query tiles (the first, a
+    middle one and the ragged tail of 72 queries) over every head and output."""
     cfg = inputs.BY_NAME[cfg_name]
     say("config", cfg.name)
     x = inputs.chunk_inputs(cfg, 0, 0)
     out = run_decomp(x, cfg.scale)
-    for name, t in out.items():
-        assert not torch.isnan(t).any().item(), f"{name} has unwritten (NaN) elements"
-    g = np.random.default_rng(cfg.cfg_id)
-    rows = np.unique(np.concatenate([np.arange(0, 8), np.arange(cfg.n_q - 80, cfg.n_q),
-                                     g.choice(cfg.n_q, 24, replace=False)]))
-    say("report", check_against_oracle(x, out, cfg.scale, TOL_BF16_O, TOL_BF16_LSE, rows=rows))
+    _all_written(out)
+    tail0 = (cfg.n_q // 256) * 256
+    rows = np.concatenate([np.arange(0, 256), np.arange(2304, 2560), np.arange(tail0, cfg.n_q)])
+    say("report", check_against_oracle(x, out, cfg.scale, TOL_BF16_O, TOL_BF16_LSE, rows=rows,
+                                       tol_rel=TOL_BF16_O_REL))
 
 
 def test_local_only_mode_is_bitwise_local():

@@ -90,9 +90,10 @@ def test_rescale_inside_a_later_split_kv_piece(workers):
     P = _sk_pieces(workers, H * -(-n_q // 256), T)
     cuts = [i * T // P for i in range(P + 1)]
     assert P >= 2, P
-    for tile in (Tl - 1, T - 1):  # the tiles holding the dominant keys
-        i = max(j for j in range(P) if cuts[j] <= tile)
-        assert i > 0 and cuts[i] < tile, (P, cuts, tile)  # a later piece, not at its first tile
+    piece_of = lambda tile: max(j for j in range(P) if cuts[j] <= tile)
+    for tile in (Tl - 1, T - 1):  # the tiles holding the dominant keys: never a piece's first tile
+        assert cuts[piece_of(tile)] < tile, (P, cuts, tile)
+    assert piece_of(T - 1) > 0, (P, cuts)  # the history plant lies in a later piece
     # within its piece the history plant follows earlier history tiles of the same piece
     p_last = max(j for j in range(P) if cuts[j] <= T - 1)
     first_hist_tile_of_piece = max(cuts[p_last], Tl)
