@@ -9,6 +9,8 @@
  *
  *   ispa_decomp_attn   local and historical attention branches plus their
  *                      log-sum-exp merge (A_loc and A_full rows),
+ *   ispa_decomp_attn_noalloc   the same with its scratch in a static device
+ *                      array (no workspace argument, nothing allocated),
  *   ispa_decomp_attn_segments  the same over a list of K/V segments
  *                      (sink, chunk, history pages) attended in place,
  *   ispa_decomp_attn_splitkv   the same with the keys split across
@@ -122,6 +124,31 @@ ispa_status_t ispa_decomp_attn(const ispa_attn_desc_t* desc, const void* Q, cons
                                const void* V_loc, const void* K_hist, const void* V_hist, void* O_loc,
                                float* LSE_loc, void* O_hist, float* LSE_hist, void* O_full,
                                float* LSE_full, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Scratch bytes ispa_decomp_attn_noalloc keeps in device memory (per GPU). */
+#define ISPA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+/*
+ * ispa_decomp_attn_noalloc — ispa_decomp_attn without a workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation).
+ *
+ * The only scratch the call needs, the float32 O_loc the merge reads back
+ * (n_q * heads * head_dim * 4 bytes when O_full is requested in bf16 with
+ * history keys), lives in a static device array of ISPA_NOALLOC_SCRATCH_BYTES
+ * (128 MiB) that each GPU the library runs on holds until the process ends;
+ * the call allocates nothing.  A shape that needs more returns
+ * ISPA_E_INVALID_ARG before anything is enqueued (128 MiB covers n_q = 4680
+ * queries at 40 heads x 128).  The scratch needs no clearing (each value is
+ * read back only by the lane that wrote it in the same launch).  Calls that
+ * overlap on one GPU (two streams, or two host threads) share the array and
+ * race: serialise them.  Arguments, outputs and the other errors are those of
+ * ispa_decomp_attn; results are bitwise equal to it.
+ */
+ispa_status_t ispa_decomp_attn_noalloc(const ispa_attn_desc_t* desc, const void* Q, const void* K_loc,
+                                       const void* V_loc, const void* K_hist, const void* V_hist, void* O_loc,
+                                       float* LSE_loc, void* O_hist, float* LSE_hist, void* O_full,
+                                       float* LSE_full, void* stream);
 
 /* At most this many K/V segments per ispa_decomp_attn_segments call. */
 #define ISPA_MAX_KV_SEGMENTS 16

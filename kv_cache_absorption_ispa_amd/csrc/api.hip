@@ -200,6 +200,75 @@ ispa_status_t ispa_decomp_attn(const ispa_attn_desc_t* desc, const void* Q, cons
                     O_full, LSE_full, workspace, workspace_bytes, stream);
 }
 
+}  // extern "C"
+
+// ---------------------------------------------------------------------------------------------
+// ispa_decomp_attn_noalloc: the merge's float32 O_loc (the only scratch the decomposable attention
+// needs) lives in this file-scope device array instead of a caller workspace.  Every GPU the library
+// runs on holds its own copy until the process ends.  Host code never passes the array's name to a
+// kernel (on the host it is only a stand-in): the device address is looked up once per device with
+// hipGetSymbolAddress, on the first call with that device current, and only that address is used.
+namespace ispa {
+namespace {
+static __device__ __align__(256) unsigned char scratch[ISPA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+std::once_flag g_scratch_once[kMaxScratchDevices];
+void* g_scratch_ptr[kMaxScratchDevices];
+hipError_t g_scratch_err[kMaxScratchDevices];
+
+// Device address of `scratch` on the current device (looked up once per device).
+ispa_status_t scratch_address(void** out) {
+  int dev = 0;
+  ispa_status_t st = hip_check(hipGetDevice(&dev), "hipGetDevice");
+  if (st != ISPA_OK) return st;
+  if (dev < 0 || dev >= kMaxScratchDevices) {
+    set_error("device index above 63");
+    return ISPA_E_UNSUPPORTED;
+  }
+  std::call_once(g_scratch_once[dev], [dev]() {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+  });
+  st = hip_check(g_scratch_err[dev], "hipGetSymbolAddress(scratch)");
+  if (st != ISPA_OK) return st;
+  *out = g_scratch_ptr[dev];
+  return ISPA_OK;
+}
+}  // namespace
+}  // namespace ispa
+
+extern "C" {
+
+ispa_status_t ispa_decomp_attn_noalloc(const ispa_attn_desc_t* desc, const void* Q, const void* K_loc,
+                                       const void* V_loc, const void* K_hist, const void* V_hist, void* O_loc,
+                                       float* LSE_loc, void* O_hist, float* LSE_hist, void* O_full,
+                                       float* LSE_full, void* stream) {
+  ispa_status_t st = check_attn_desc(desc, true);
+  if (st != ISPA_OK) return st;
+  if ((desc->n_q > 0 && !req(Q)) || !req(K_loc) || !req(V_loc))
+    return invalid("Q, K_loc, V_loc must be non-NULL and 16-byte aligned");
+  if (desc->n_hist > 0 && (!req(K_hist) || !req(V_hist)))
+    return invalid("K_hist, V_hist must be non-NULL and 16-byte aligned when n_hist > 0");
+  if (!opt(O_loc) || !opt(LSE_loc) || !opt(O_hist) || !opt(LSE_hist) || !opt(O_full) || !opt(LSE_full))
+    return invalid("output pointers must be 16-byte aligned");
+  const size_t need = attention_workspace_size(desc->n_q, desc->heads, desc->head_dim, desc->n_hist, desc->dtype);
+  if (need > ISPA_NOALLOC_SCRATCH_BYTES)
+    return invalid("ispa_decomp_attn_noalloc: the merge needs " + std::to_string(need) +
+                   " bytes of scratch (n_q * heads * head_dim * 4), above ISPA_NOALLOC_SCRATCH_BYTES = " +
+                   std::to_string((size_t)ISPA_NOALLOC_SCRATCH_BYTES) + "; use ispa_decomp_attn with a workspace");
+  st = check_current_device();
+  if (st != ISPA_OK) return st;
+  void* ws = nullptr;
+  if (need > 0) {
+    st = scratch_address(&ws);
+    if (st != ISPA_OK) return st;
+  }
+  return run_decomp(desc, Q, two_segments(desc, K_loc, V_loc, K_hist, V_hist), O_loc, LSE_loc, O_hist, LSE_hist,
+                    O_full, LSE_full, ws, need, stream);
+}
+
 ispa_status_t ispa_decomp_attn_segments(const ispa_attn_desc_t* desc, const void* Q, const ispa_kv_segment_t* segs,
                                         int32_t n_segs, int32_t n_loc_segs, void* O_loc, float* LSE_loc,
                                         void* O_hist, float* LSE_hist, void* O_full, float* LSE_full,

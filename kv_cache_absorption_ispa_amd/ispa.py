@@ -21,7 +21,7 @@ ISPA_OK, ISPA_E_INVALID_ARG, ISPA_E_UNSUPPORTED, ISPA_E_WORKSPACE, ISPA_E_HIP = 
 ISPA_F32, ISPA_BF16 = 0, 1
 
 EXPORTS = [
-    "ispa_decomp_attn", "ispa_decomp_attn_segments", "ispa_decomp_attn_splitkv",
+    "ispa_decomp_attn", "ispa_decomp_attn_noalloc", "ispa_decomp_attn_segments", "ispa_decomp_attn_splitkv",
     "ispa_decomp_attn_splitkv_workspace_size", "ispa_decomp_attn_workspace_size", "ispa_full_attn", "ispa_lse_merge", "ispa_gram_workspace_size", "ispa_gram_accum",
     "ispa_absorb_workspace_size", "ispa_absorb_solve", "ispa_eps_workspace_size", "ispa_layer_eps",
     "ispa_select_layers", "ispa_absorb_apply", "ispa_fit_error", "ispa_fit_error_workspace_size",
@@ -79,6 +79,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     P, I32, I64, SZ, F, D = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float, None
     sig = {
         "ispa_decomp_attn": (I32, [ctypes.POINTER(AttnDesc)] + [P] * 12 + [SZ, P]),
+        "ispa_decomp_attn_noalloc": (I32, [ctypes.POINTER(AttnDesc)] + [P] * 11 + [P]),
         "ispa_decomp_attn_segments": (I32, [ctypes.POINTER(AttnDesc), P, ctypes.POINTER(KvSegment), I32, I32]
                                       + [P] * 7 + [SZ, P]),
         "ispa_decomp_attn_splitkv": (I32, [ctypes.POINTER(AttnDesc), P, ctypes.POINTER(KvSegment), I32, I32, I32]
@@ -200,6 +201,32 @@ def ispa_decomp_attn(q, k_loc, v_loc, k_hist=None, v_hist=None, *, scale=None, o
                                 _ptr(k_hist) if n_hist else None, _ptr(v_hist) if n_hist else None,
                                 _ptr(o_loc), _ptr(lse_loc), _ptr(o_hist), _ptr(lse_hist), _ptr(o_full),
                                 _ptr(lse_full), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+ISPA_NOALLOC_SCRATCH_BYTES = 128 << 20
+
+
+def ispa_decomp_attn_noalloc(q, k_loc, v_loc, k_hist=None, v_hist=None, *, scale=None, o_loc=None, lse_loc=None,
+                             o_hist=None, lse_hist=None, o_full=None, lse_full=None, stream=None) -> None:
+    """ispa_decomp_attn with its scratch in the library's static device array: no workspace, nothing
+    allocated (n_q * H * D * 4 <= ISPA_NOALLOC_SCRATCH_BYTES; calls overlapping on one GPU race)."""
+    n_q, H, D = q.shape
+    n_loc = k_loc.shape[0]
+    n_hist = 0 if k_hist is None else k_hist.shape[0]
+    for t, n in ((k_loc, "k_loc"), (v_loc, "v_loc")):
+        _expect(t, (n_loc, H, D), q.dtype, n)
+    if n_hist:
+        _expect(k_hist, (n_hist, H, D), q.dtype, "k_hist")
+        _expect(v_hist, (n_hist, H, D), q.dtype, "v_hist")
+    for t, n in ((o_loc, "o_loc"), (o_hist, "o_hist"), (o_full, "o_full")):
+        _expect(t, (n_q, H, D), q.dtype, n)
+    for t, n in ((lse_loc, "lse_loc"), (lse_hist, "lse_hist"), (lse_full, "lse_full")):
+        _expect(t, (H, n_q), torch.float32, n)
+    desc = make_desc(q, n_loc, n_hist, scale)
+    _check(load_library().ispa_decomp_attn_noalloc(
+        ctypes.byref(desc), _ptr(q), _ptr(k_loc), _ptr(v_loc), _ptr(k_hist) if n_hist else None,
+        _ptr(v_hist) if n_hist else None, _ptr(o_loc), _ptr(lse_loc), _ptr(o_hist), _ptr(lse_hist), _ptr(o_full),
+        _ptr(lse_full), _stream(stream)))
 
 
 def _segments(q, loc_segs, hist_segs, o_loc, o_hist, o_full, lse_loc, lse_hist, lse_full):
