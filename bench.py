@@ -478,12 +478,12 @@ def bench_stack(args, host_inputs):
             st2 = LayerStack(W0.clone(), H, D, nq, cfg.lam if "lam_policy" not in kw else 1e-4, cfg.n_absorb, **kw)
             st2.G.copy_(st.G)
             st2.C.copy_(st.C)
-            st2.Q_ff.copy_(st.Q_ff)
+            st2.E.copy_(st.E)
             st2.chunks_seen = [cfg.n_chunks] * L
             if kw.get("selection") == "heldout":  # timing stand-in: the fitted rows as held-out rows
                 st2.G_h.copy_(st.G)
                 st2.C_h.copy_(st.C)
-                st2.Q_h.copy_(st.Q_ff)
+                st2.E_h.copy_(st.E)
                 st2.heldout_seen = [1] * L
             torch.cuda.synchronize()
             t_a = time.perf_counter()

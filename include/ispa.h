@@ -15,7 +15,8 @@
  *                      (sink, chunk, history pages) attended in place,
  *   ispa_decomp_attn_splitkv   the same with the keys split across
  *                      workgroups (even load) and merged through LSE,
- *   ispa_gram_accum    G = A_loc^T A_loc and C = A_loc^T (A_full - A_loc),
+ *   ispa_gram_accum    G = A_loc^T A_loc, C = A_loc^T (A_full - A_loc) and
+ *                      E = (A_full - A_loc)^T (A_full - A_loc),
  *   ispa_absorb_solve  dW = (G + lambda I)^-1 C W  (Cholesky + triangular solves),
  *   ispa_layer_eps     the post-fit reconstruction error used to rank layers,
  *   ispa_select_layers the k lowest-error layers (those converted),
@@ -54,7 +55,7 @@
  * - Layouts: Q, K, V and O are [tokens, heads, head_dim] contiguous, so an O
  *   buffer is also the row-major [tokens, d] matrix A with d = heads*head_dim
  *   and column h*head_dim + e.  LSE is [heads, tokens] float32, natural log,
- *   scale included.  G, C, Q_ff, W, dW, W_new are row-major float32.
+ *   scale included.  G, C, E, W, dW, W_new are row-major float32.
  * - bf16 tensors are passed as 16-bit patterns (uint16 storage).
  * - Return value: ISPA_OK, or an error status with detail in
  *   ispa_last_error() (thread-local).  Nothing throws, aborts or exits.
@@ -262,7 +263,9 @@ ispa_status_t ispa_lse_merge(int32_t n_parts, const void* const* O_parts, const 
                              int64_t n_q, int32_t heads, int32_t head_dim, int32_t dtype, void* O_out,
                              float* LSE_out, void* stream);
 
-/* Workspace bytes ispa_gram_accum needs for these sizes (0 is possible).
+/* Workspace bytes ispa_gram_accum needs for these sizes (0 for float32 or no
+ * rows): the bf16 split of D for one block of up to 32768 rows, a counter per
+ * output tile, and the split partials when rows are split over workgroups.
  * Support call: no passage of the pages defines it. */
 size_t ispa_gram_workspace_size(int64_t n_rows, int32_t d, int32_t dtype);
 
@@ -271,21 +274,26 @@ size_t ispa_gram_workspace_size(int64_t n_rows, int32_t d, int32_t dtype);
  *
  * Source: ISPA technical summary, section 2, step 2 "Layer Absorb": the
  * closed form needs only A_loc^T A_loc and A_loc^T (A_full - A_loc) over the
- * warmup rows.  Computed as G += A_loc^T A_loc, C += A_loc^T A_full -
- * A_loc^T A_loc from the exact stored operands (mathematically identical to
- * the page's form; it avoids rounding A_full - A_loc to bf16).
+ * warmup rows; "Dynamic Layer Selection" ranks layers by the fit's error,
+ * which also needs (A_full - A_loc)^T (A_full - A_loc).  With D = A_full -
+ * A_loc (exact in float32 for bf16 rows):
+ *   G (+)= A_loc^T A_loc,  C (+)= A_loc^T D,  E (+)= D^T D  (E optional).
+ * C and E are formed from D itself, not as differences of products, so they
+ * keep their accuracy when the two streams nearly agree (bf16: D enters the
+ * matrix cores as two bf16 terms, D_hi + D_lo, within 2^-17 of D).
  *
  *   A_loc, A_full [n_rows, d] (dtype), row-major (an O buffer of
- *   ispa_decomp_attn is such a matrix).  G, C, Q_ff [d, d] float32.
- *   accumulate = 0 overwrites G, C (and Q_ff); 1 adds to them.
- *   Q_ff may be NULL; if given, Q_ff (+)= A_full^T A_full (for ispa_layer_eps).
- *   G and Q_ff are written in full (both triangles).  d must be a multiple of
- *   128 (bf16) or 64 (float32); 0 <= n_rows with n_rows * d < 2^40 (0 rows
- *   with accumulate = 0 writes zeros).  The result is deterministic: no
- *   atomics, fixed reduction order.
+ *   ispa_decomp_attn is such a matrix).  G, C, E [d, d] float32.
+ *   accumulate = 0 overwrites G, C (and E); 1 adds to them.
+ *   E may be NULL (not formed).  G and E are written in full (both triangles
+ *   hold the same bits).  d must be a multiple of 128 (bf16) or 64 (float32);
+ *   0 <= n_rows with n_rows * d < 2^40 (0 rows with accumulate = 0 writes
+ *   zeros).  bf16 needs `workspace` (>= ispa_gram_workspace_size bytes;
+ *   ISPA_E_WORKSPACE otherwise).  The result is deterministic: no
+ *   floating-point atomics, fixed reduction order.
  */
 ispa_status_t ispa_gram_accum(int64_t n_rows, int32_t d, int32_t dtype, const void* A_loc,
-                              const void* A_full, float* G, float* C, float* Q_ff, int32_t accumulate,
+                              const void* A_full, float* G, float* C, float* E, int32_t accumulate,
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace bytes ispa_absorb_solve needs for these sizes.
@@ -324,16 +332,16 @@ size_t ispa_eps_workspace_size(int32_t d, int32_t d_out, int32_t batch);
  * Source: ISPA technical summary, section 2 "Dynamic Layer Selection" (layers
  * ranked by reconstruction error after warmup, lowest converted).  Reading:
  * eps = ||A_loc (W + dW) - A_full W||_F^2 over the warmup rows (the lambda
- * term excluded), evaluated from the Gram statistics with D = A_full - A_loc:
- *   eps = <Q_ff - C - C^T - G, W W^T> - <dW, C W> - lambda ||dW||^2
- *       = <Q_ff W, W> - 2 <C W, W> - <G W, W> - <dW, C W> - lambda ||dW||^2,
- * eps_rel = eps / <Q_ff W, W>  (= eps / ||A_full W||_F^2).
+ * term excluded), evaluated from the statistics of ispa_gram_accum (D =
+ * A_full - A_loc; G, C, E) and the normal equation (G + lambda I) dW = C W:
+ *   eps = <E W, W> - <dW, C W> - lambda ||dW||^2,
+ *   eps_rel = eps / <(G + C + C^T + E) W, W>  (= eps / ||A_full W||_F^2).
  * Products in float32, the inner products reduced in float64.
- *   G, C, Q_ff [batch, d, d]; W, dW [batch, d, d_out]; eps_abs, eps_rel
+ *   G, C, E [batch, d, d]; W, dW [batch, d, d_out]; eps_abs, eps_rel
  *   [batch] float64 DEVICE.
  */
 ispa_status_t ispa_layer_eps(int32_t d, int32_t d_out, int32_t batch, const float* G, const float* C,
-                             const float* Q_ff, const float* W, const float* dW, float lambda,
+                             const float* E, const float* W, const float* dW, float lambda,
                              double* eps_abs, double* eps_rel, void* workspace, size_t workspace_bytes,
                              void* stream);
 
@@ -470,21 +478,21 @@ size_t ispa_fit_error_workspace_size(int32_t d, int32_t d_out, int32_t batch);
 
 /*
  * ispa_fit_error — eps = ||A_loc (W + dW) - A_full W||_F^2 over the rows
- * whose statistics are G, C, Q_ff (as ispa_gram_accum writes them), for ANY
+ * whose statistics are G, C, E (as ispa_gram_accum writes them), for ANY
  * dW: rows the fit did not see (held-out error), or dW = NULL (dW = 0: the
- * discrepancy before the fit, ||(A_full - A_loc) W||^2, which needs no
- * solve).  From the statistics:
- *   eps = <Q_ff W, W> - 2 <C W, W> - <G W, W> + <G dW, dW> - 2 <dW, C W>,
- *   eps_rel = eps / <Q_ff W, W>.
+ * discrepancy before the fit, ||(A_full - A_loc) W||^2 = <E W, W>, which
+ * needs no solve).  From the statistics:
+ *   eps = <E W, W> + <G dW, dW> - 2 <dW, C W>,
+ *   eps_rel = eps / <(G + C + C^T + E) W, W>.
  * ispa_layer_eps is the special case where dW solves the ridge problem on the
  * same rows.  Products in float32, inner products reduced in float64.
- *   G, C, Q_ff [batch, d, d]; W, dW [batch, d, d_out] float32 (dW nullable);
+ *   G, C, E [batch, d, d]; W, dW [batch, d, d_out] float32 (dW nullable);
  *   eps_abs, eps_rel [batch] float64 DEVICE.  d, d_out multiples of 64.
  * Source: ISPA technical summary, section 2 "Dynamic Layer Selection" (layers ranked
  * by reconstruction error; the variants here are this library's readings of it).
  */
 ispa_status_t ispa_fit_error(int32_t d, int32_t d_out, int32_t batch, const float* G, const float* C,
-                             const float* Q_ff, const float* W, const float* dW, double* eps_abs,
+                             const float* E, const float* W, const float* dW, double* eps_abs,
                              double* eps_rel, void* workspace, size_t workspace_bytes, void* stream);
 
 /*

@@ -482,19 +482,19 @@ size_t ispa_gram_workspace_size(int64_t n_rows, int32_t d, int32_t dtype) {
 }
 
 ispa_status_t ispa_gram_accum(int64_t n_rows, int32_t d, int32_t dtype, const void* A_loc, const void* A_full, float* G,
-                              float* C, float* Q_ff, int32_t accumulate, void* workspace, size_t workspace_bytes,
+                              float* C, float* E, int32_t accumulate, void* workspace, size_t workspace_bytes,
                               void* stream) {
   if (n_rows < 0) return invalid("n_rows must be >= 0");
   if (dtype != ISPA_F32 && dtype != ISPA_BF16) return invalid("bad dtype");
   if (d <= 0 || (dtype == ISPA_BF16 && d % 128 != 0) || (dtype == ISPA_F32 && d % 64 != 0))
     return invalid("d must be a multiple of 128 (bf16) or 64 (f32)");
   if (accumulate != 0 && accumulate != 1) return invalid("accumulate must be 0 or 1");
-  if ((n_rows > 0 && (!req(A_loc) || !req(A_full))) || !req(G) || !req(C) || !opt(Q_ff))
+  if ((n_rows > 0 && (!req(A_loc) || !req(A_full))) || !req(G) || !req(C) || !opt(E))
     return invalid("A_loc, A_full, G, C must be non-NULL and 16-byte aligned");
   if (n_rows * (int64_t)d >= ((int64_t)1 << 40)) return invalid("too many rows");
   ispa_status_t st = check_current_device();
   if (st != ISPA_OK) return st;
-  return launch_gram(n_rows, d, dtype, A_loc, A_full, G, C, Q_ff, accumulate, workspace, workspace_bytes,
+  return launch_gram(n_rows, d, dtype, A_loc, A_full, G, C, E, accumulate, workspace, workspace_bytes,
                      (hipStream_t)stream);
 }
 
@@ -571,15 +571,15 @@ size_t ispa_fit_error_workspace_size(int32_t d, int32_t d_out, int32_t batch) {
 }
 
 ispa_status_t ispa_fit_error(int32_t d, int32_t d_out, int32_t batch, const float* G, const float* C,
-                             const float* Q_ff, const float* W, const float* dW, double* eps_abs, double* eps_rel,
+                             const float* E, const float* W, const float* dW, double* eps_abs, double* eps_rel,
                              void* workspace, size_t workspace_bytes, void* stream) {
   if (d <= 0 || d % 64 != 0 || d_out <= 0 || d_out % 64 != 0) return invalid("d and d_out must be multiples of 64");
   if (batch < 1 || batch > 65535) return invalid("batch must be in [1, 65535]");
-  if (!req(G) || !req(C) || !req(Q_ff) || !req(W) || !opt(dW) || !req(eps_abs) || !req(eps_rel))
-    return invalid("G, C, Q_ff, W, eps_abs, eps_rel must be non-NULL (dW may be NULL) and 16-byte aligned");
+  if (!req(G) || !req(C) || !req(E) || !req(W) || !opt(dW) || !req(eps_abs) || !req(eps_rel))
+    return invalid("G, C, E, W, eps_abs, eps_rel must be non-NULL (dW may be NULL) and 16-byte aligned");
   ispa_status_t st = check_current_device();
   if (st != ISPA_OK) return st;
-  return launch_fit_error(d, d_out, batch, G, C, Q_ff, W, dW, eps_abs, eps_rel, workspace, workspace_bytes,
+  return launch_fit_error(d, d_out, batch, G, C, E, W, dW, eps_abs, eps_rel, workspace, workspace_bytes,
                           (hipStream_t)stream);
 }
 
@@ -588,17 +588,17 @@ size_t ispa_eps_workspace_size(int32_t d, int32_t d_out, int32_t batch) {
   return eps_workspace_size(d, d_out, batch);
 }
 
-ispa_status_t ispa_layer_eps(int32_t d, int32_t d_out, int32_t batch, const float* G, const float* C, const float* Q_ff,
+ispa_status_t ispa_layer_eps(int32_t d, int32_t d_out, int32_t batch, const float* G, const float* C, const float* E,
                              const float* W, const float* dW, float lambda, double* eps_abs, double* eps_rel,
                              void* workspace, size_t workspace_bytes, void* stream) {
   if (d <= 0 || d % 64 != 0 || d_out <= 0 || d_out % 64 != 0) return invalid("d and d_out must be multiples of 64");
   if (batch < 1 || batch > 65535) return invalid("batch must be in [1, 65535]");
   if (!(lambda >= 0.f) || lambda == INFINITY) return invalid("lambda must be finite and >= 0");
-  if (!req(G) || !req(C) || !req(Q_ff) || !req(W) || !req(dW) || !req(eps_abs) || !req(eps_rel))
+  if (!req(G) || !req(C) || !req(E) || !req(W) || !req(dW) || !req(eps_abs) || !req(eps_rel))
     return invalid("all pointers must be non-NULL and 16-byte aligned");
   ispa_status_t st = check_current_device();
   if (st != ISPA_OK) return st;
-  return launch_eps(d, d_out, batch, G, C, Q_ff, W, dW, lambda, eps_abs, eps_rel, workspace, workspace_bytes,
+  return launch_eps(d, d_out, batch, G, C, E, W, dW, lambda, eps_abs, eps_rel, workspace, workspace_bytes,
                     (hipStream_t)stream);
 }
 

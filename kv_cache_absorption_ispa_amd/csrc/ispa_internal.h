@@ -78,7 +78,7 @@ ispa_status_t launch_w8a8_gemm(int64_t n, int32_t N, int32_t K, const uint8_t* A
 
 size_t gram_workspace_size(int64_t n_rows, int32_t d, int32_t dtype);
 ispa_status_t launch_gram(int64_t n_rows, int32_t d, int32_t dtype, const void* A_loc, const void* A_full,
-                          float* G, float* C, float* Qff, int32_t accumulate, void* ws, size_t ws_bytes,
+                          float* G, float* C, float* E, int32_t accumulate, void* ws, size_t ws_bytes,
                           hipStream_t s);
 
 size_t absorb_workspace_size(int32_t d, int32_t d_out, int32_t batch);
@@ -93,7 +93,7 @@ ispa_status_t launch_absorb(int32_t d, int32_t d_out, int32_t batch, const float
                             const SideStream* side = nullptr);
 size_t fit_error_workspace_size(int32_t d, int32_t d_out, int32_t batch);
 ispa_status_t launch_fit_error(int32_t d, int32_t d_out, int32_t batch, const float* G, const float* C,
-                               const float* Qff, const float* W, const float* dW, double* eps_abs, double* eps_rel,
+                               const float* E, const float* W, const float* dW, double* eps_abs, double* eps_rel,
                                void* ws, size_t ws_bytes, hipStream_t s);
 ispa_status_t launch_trace_lambda(int32_t d, int32_t batch, const float* G, float scale, float* lam, hipStream_t s);
 ispa_status_t launch_select_below(int32_t n_layers, const double* eps, double tau, int32_t k_max, int32_t* selected,
@@ -105,7 +105,7 @@ ispa_status_t launch_absorb_apply_compact(int32_t d, int32_t d_out, int32_t n_la
 
 size_t eps_workspace_size(int32_t d, int32_t d_out, int32_t batch);
 ispa_status_t launch_eps(int32_t d, int32_t d_out, int32_t batch, const float* G, const float* C,
-                         const float* Qff, const float* W, const float* dW, float lambda, double* eps_abs,
+                         const float* E, const float* W, const float* dW, float lambda, double* eps_abs,
                          double* eps_rel, void* ws, size_t ws_bytes, hipStream_t s);
 
 constexpr int MAX_STACK_LAYERS = 4096;

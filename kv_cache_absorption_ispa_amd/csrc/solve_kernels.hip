@@ -500,8 +500,13 @@ __global__ __launch_bounds__(256) void finalize_kernel(const float* W, float* dW
   if (Wn) *(f32x4*)(Wn + b * n + i4) = *(const f32x4*)(W + b * n + i4) + x;
 }
 
-// Inner products for the reconstruction error, reduced in float64 in a fixed order.
-__global__ __launch_bounds__(256) void eps_reduce_kernel(const float* W, const float* dW, const float* QW,
+// Inner products for the reconstruction error of the fitted dW, reduced in float64 in a fixed
+// order.  With D = A_full - A_loc and the statistics G = A_loc^T A_loc, C = A_loc^T D, E = D^T D:
+//   eps = ||D W - A_loc dW||^2 = <E W, W> - 2 <C W, dW> + <G dW, dW>, and the normal equation
+//   (G + lambda I) dW = C W turns the last two terms into -<dW, C W> - lambda ||dW||^2;
+//   ||A_full W||^2 = <(G + C + C^T + E) W, W> = <E W, W> + 2 <C W, W> + <G W, W>.
+// Forming E from D (not from A_full^T A_full) keeps eps accurate when D is small.
+__global__ __launch_bounds__(256) void eps_reduce_kernel(const float* W, const float* dW, const float* EW,
                                                          const float* CW, const float* GW, size_t n, float lambda,
                                                          double* eps_abs, double* eps_rel) {
   const int b = blockIdx.x;
@@ -509,7 +514,7 @@ __global__ __launch_bounds__(256) void eps_reduce_kernel(const float* W, const f
   double s[5] = {0, 0, 0, 0, 0};
   for (size_t i = threadIdx.x; i < n; i += 256) {
     const double w = W[off + i], dw = dW[off + i], cw = CW[off + i];
-    s[0] += (double)QW[off + i] * w;
+    s[0] += (double)EW[off + i] * w;
     s[1] += cw * w;
     s[2] += (double)GW[off + i] * w;
     s[3] += dw * cw;
@@ -524,15 +529,15 @@ __global__ __launch_bounds__(256) void eps_reduce_kernel(const float* W, const f
     __syncthreads();
   }
   if (threadIdx.x == 0) {
-    const double e = red[0][0] - 2.0 * red[1][0] - red[2][0] - red[3][0] - (double)lambda * red[4][0];
+    const double e = red[0][0] - red[3][0] - (double)lambda * red[4][0];
     eps_abs[b] = e;
-    eps_rel[b] = e / red[0][0];
+    eps_rel[b] = e / (red[0][0] + 2.0 * red[1][0] + red[2][0]);
   }
 }
 
 // Reconstruction error for any dW (held-out rows, or dW = 0 before the fit), from the statistics:
-// eps = <Q_ff W, W> - 2 <C W, W> - <G W, W> + <G dW, dW> - 2 <dW, C W>; float64 reductions.
-__global__ __launch_bounds__(256) void fit_error_reduce_kernel(const float* W, const float* dW, const float* QW,
+// eps = <E W, W> + <G dW, dW> - 2 <dW, C W>; float64 reductions.
+__global__ __launch_bounds__(256) void fit_error_reduce_kernel(const float* W, const float* dW, const float* EW,
                                                                const float* CW, const float* GW, const float* GdW,
                                                                size_t n, double* eps_abs, double* eps_rel) {
   const int b = blockIdx.x;
@@ -540,7 +545,7 @@ __global__ __launch_bounds__(256) void fit_error_reduce_kernel(const float* W, c
   double s[5] = {0, 0, 0, 0, 0};
   for (size_t i = threadIdx.x; i < n; i += 256) {
     const double w = W[off + i], cw = CW[off + i];
-    s[0] += (double)QW[off + i] * w;
+    s[0] += (double)EW[off + i] * w;
     s[1] += cw * w;
     s[2] += (double)GW[off + i] * w;
     if (dW) {
@@ -558,9 +563,9 @@ __global__ __launch_bounds__(256) void fit_error_reduce_kernel(const float* W, c
     __syncthreads();
   }
   if (threadIdx.x == 0) {
-    const double e = red[0][0] - 2.0 * red[1][0] - red[2][0] + red[3][0] - 2.0 * red[4][0];
+    const double e = red[0][0] + red[3][0] - 2.0 * red[4][0];
     eps_abs[b] = e;
-    eps_rel[b] = e / red[0][0];
+    eps_rel[b] = e / (red[0][0] + 2.0 * red[1][0] + red[2][0]);
   }
 }
 
@@ -830,18 +835,18 @@ size_t fit_error_workspace_size(int32_t d, int32_t d_out, int32_t batch) {
 }
 
 ispa_status_t launch_fit_error(int32_t d, int32_t d_out, int32_t batch, const float* G, const float* C,
-                               const float* Qff, const float* W, const float* dW, double* eps_abs, double* eps_rel,
+                               const float* E, const float* W, const float* dW, double* eps_abs, double* eps_rel,
                                void* ws, size_t ws_bytes, hipStream_t s) {
   if (ws == nullptr || ws_bytes < fit_error_workspace_size(d, d_out, batch)) {
     set_error("ispa_fit_error: workspace too small");
     return ISPA_E_WORKSPACE;
   }
   const size_t dd = (size_t)d * d, dn = (size_t)d * d_out;
-  float* QW = (float*)ws;
-  float* CW = QW + (size_t)batch * dn;
+  float* EW = (float*)ws;
+  float* CW = EW + (size_t)batch * dn;
   float* GW = CW + (size_t)batch * dn;
   float* GdW = GW + (size_t)batch * dn;
-  ISPA_TRY((gemm<false, false>(s, batch, d, d_out, d, Qff, d, dd, W, d_out, dn, nullptr, 0, 0, QW, d_out, dn, 1.f, 0.f,
+  ISPA_TRY((gemm<false, false>(s, batch, d, d_out, d, E, d, dd, W, d_out, dn, nullptr, 0, 0, EW, d_out, dn, 1.f, 0.f,
                                false, nullptr)));
   ISPA_TRY((gemm<false, false>(s, batch, d, d_out, d, C, d, dd, W, d_out, dn, nullptr, 0, 0, CW, d_out, dn, 1.f, 0.f,
                                false, nullptr)));
@@ -850,7 +855,7 @@ ispa_status_t launch_fit_error(int32_t d, int32_t d_out, int32_t batch, const fl
   if (dW)
     ISPA_TRY((gemm<false, false>(s, batch, d, d_out, d, G, d, dd, dW, d_out, dn, nullptr, 0, 0, GdW, d_out, dn, 1.f,
                                  0.f, false, nullptr)));
-  hipLaunchKernelGGL(fit_error_reduce_kernel, dim3(batch), dim3(256), 0, s, W, dW, QW, CW, GW, GdW, dn, eps_abs,
+  hipLaunchKernelGGL(fit_error_reduce_kernel, dim3(batch), dim3(256), 0, s, W, dW, EW, CW, GW, GdW, dn, eps_abs,
                      eps_rel);
   return hip_check(hipGetLastError(), "fit_error_reduce_kernel launch");
 }
@@ -864,7 +869,7 @@ size_t eps_workspace_size(int32_t d, int32_t d_out, int32_t batch) {
   return 3 * (size_t)batch * d * d_out * sizeof(float);
 }
 
-ispa_status_t launch_eps(int32_t d, int32_t d_out, int32_t batch, const float* G, const float* C, const float* Qff,
+ispa_status_t launch_eps(int32_t d, int32_t d_out, int32_t batch, const float* G, const float* C, const float* E,
                          const float* W, const float* dW, float lambda, double* eps_abs, double* eps_rel, void* ws,
                          size_t ws_bytes, hipStream_t s) {
   if (ws == nullptr || ws_bytes < eps_workspace_size(d, d_out, batch)) {
@@ -872,16 +877,16 @@ ispa_status_t launch_eps(int32_t d, int32_t d_out, int32_t batch, const float* G
     return ISPA_E_WORKSPACE;
   }
   const size_t dd = (size_t)d * d, dn = (size_t)d * d_out;
-  float* QW = (float*)ws;
-  float* CW = QW + (size_t)batch * dn;
+  float* EW = (float*)ws;
+  float* CW = EW + (size_t)batch * dn;
   float* GW = CW + (size_t)batch * dn;
-  ISPA_TRY((gemm<false, false>(s, batch, d, d_out, d, Qff, d, dd, W, d_out, dn, nullptr, 0, 0, QW, d_out, dn, 1.f, 0.f,
+  ISPA_TRY((gemm<false, false>(s, batch, d, d_out, d, E, d, dd, W, d_out, dn, nullptr, 0, 0, EW, d_out, dn, 1.f, 0.f,
                                false, nullptr)));
   ISPA_TRY((gemm<false, false>(s, batch, d, d_out, d, C, d, dd, W, d_out, dn, nullptr, 0, 0, CW, d_out, dn, 1.f, 0.f,
                                false, nullptr)));
   ISPA_TRY((gemm<false, false>(s, batch, d, d_out, d, G, d, dd, W, d_out, dn, nullptr, 0, 0, GW, d_out, dn, 1.f, 0.f,
                                false, nullptr)));
-  hipLaunchKernelGGL(eps_reduce_kernel, dim3(batch), dim3(256), 0, s, W, dW, QW, CW, GW, dn, lambda, eps_abs, eps_rel);
+  hipLaunchKernelGGL(eps_reduce_kernel, dim3(batch), dim3(256), 0, s, W, dW, EW, CW, GW, dn, lambda, eps_abs, eps_rel);
   return hip_check(hipGetLastError(), "eps_reduce_kernel launch");
 }
 

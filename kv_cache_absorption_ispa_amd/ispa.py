@@ -328,8 +328,11 @@ def ispa_gram_workspace_size(n_rows: int, d: int, dtype: torch.dtype) -> int:
     return int(load_library().ispa_gram_workspace_size(n_rows, d, code))
 
 
-def ispa_gram_accum(a_loc, a_full, G, C, Q_ff=None, *, accumulate: bool, workspace=None, stream=None) -> None:
-    """G (+)= A_loc^T A_loc ; C (+)= A_loc^T A_full - A_loc^T A_loc ; Q_ff (+)= A_full^T A_full."""
+def ispa_gram_accum(a_loc, a_full, G, C, E=None, *, accumulate: bool, workspace=None, stream=None) -> None:
+    """With D = A_full - A_loc: G (+)= A_loc^T A_loc ; C (+)= A_loc^T D ; E (+)= D^T D (E optional).
+
+    bf16 rows need ``workspace`` (bytes >= ispa_gram_workspace_size); when omitted here, one is allocated
+    through torch for this call."""
     n = a_loc.shape[0]
     d = 1
     for s_ in a_loc.shape[1:]:
@@ -337,11 +340,13 @@ def ispa_gram_accum(a_loc, a_full, G, C, Q_ff=None, *, accumulate: bool, workspa
     a_loc2 = a_loc.reshape(n, d)
     a_full2 = a_full.reshape(a_full.shape[0], d)
     _expect(a_full2, (n, d), a_loc.dtype, "a_full")
-    for t, nm in ((G, "G"), (C, "C"), (Q_ff, "Q_ff")):
+    for t, nm in ((G, "G"), (C, "C"), (E, "E")):
         _expect(t, (d, d), torch.float32, nm)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     lib = load_library()
-    _check(lib.ispa_gram_accum(n, d, _dtype_code(a_loc), _ptr(a_loc2), _ptr(a_full2), _ptr(G), _ptr(C), _ptr(Q_ff),
+    if workspace is None:
+        workspace = _workspace(int(lib.ispa_gram_workspace_size(n, d, _dtype_code(a_loc))), a_loc.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.ispa_gram_accum(n, d, _dtype_code(a_loc), _ptr(a_loc2), _ptr(a_full2), _ptr(G), _ptr(C), _ptr(E),
                                1 if accumulate else 0, _ptr(workspace), ws_bytes, _stream(stream)))
 
 
@@ -372,13 +377,13 @@ def ispa_eps_workspace_size(d: int, d_out: int, batch: int) -> int:
     return int(load_library().ispa_eps_workspace_size(d, d_out, batch))
 
 
-def ispa_layer_eps(G, C, Q_ff, W, dW, lam: float, eps_abs, eps_rel, *, workspace=None, stream=None) -> None:
+def ispa_layer_eps(G, C, E, W, dW, lam: float, eps_abs, eps_rel, *, workspace=None, stream=None) -> None:
     """Reconstruction error of each layer from its Gram statistics (float64 outputs [batch])."""
     G3 = G if G.dim() == 3 else G[None]
     W3 = W if W.dim() == 3 else W[None]
     b, d, _ = G3.shape
     d_out = W3.shape[2]
-    for t, nm in ((G, "G"), (C, "C"), (Q_ff, "Q_ff")):
+    for t, nm in ((G, "G"), (C, "C"), (E, "E")):
         _expect(t if t.dim() == 3 else t[None], (b, d, d), torch.float32, nm)
     for t, nm in ((W, "W"), (dW, "dW")):
         _expect(t if t.dim() == 3 else t[None], (b, d, d_out), torch.float32, nm)
@@ -386,7 +391,7 @@ def ispa_layer_eps(G, C, Q_ff, W, dW, lam: float, eps_abs, eps_rel, *, workspace
     _expect(eps_rel.reshape(-1), (b,), torch.float64, "eps_rel")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     lib = load_library()
-    _check(lib.ispa_layer_eps(d, d_out, b, _ptr(G), _ptr(C), _ptr(Q_ff), _ptr(W), _ptr(dW), float(lam),
+    _check(lib.ispa_layer_eps(d, d_out, b, _ptr(G), _ptr(C), _ptr(E), _ptr(W), _ptr(dW), float(lam),
                               _ptr(eps_abs), _ptr(eps_rel), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
@@ -420,12 +425,12 @@ def ispa_fit_error_workspace_size(d: int, d_out: int, batch: int) -> int:
     return int(load_library().ispa_fit_error_workspace_size(d, d_out, batch))
 
 
-def ispa_fit_error(G, C, Q_ff, W, dW, eps_abs, eps_rel, *, workspace=None, stream=None) -> None:
-    """||A_loc (W + dW) - A_full W||^2 over the rows summarised by (G, C, Q_ff), any dW (None: dW = 0)."""
+def ispa_fit_error(G, C, E, W, dW, eps_abs, eps_rel, *, workspace=None, stream=None) -> None:
+    """||A_loc (W + dW) - A_full W||^2 over the rows summarised by (G, C, E), any dW (None: dW = 0)."""
     G3, W3 = _as3(G), _as3(W)
     b, d, _ = G3.shape
     d_out = W3.shape[2]
-    for t, nm in ((G, "G"), (C, "C"), (Q_ff, "Q_ff")):
+    for t, nm in ((G, "G"), (C, "C"), (E, "E")):
         _expect(_as3(t), (b, d, d), torch.float32, nm)
     _expect(W3, (b, d, d_out), torch.float32, "W")
     if dW is not None:
@@ -436,7 +441,7 @@ def ispa_fit_error(G, C, Q_ff, W, dW, eps_abs, eps_rel, *, workspace=None, strea
     if workspace is None:
         workspace = _workspace(int(lib.ispa_fit_error_workspace_size(d, d_out, b)), G.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib.ispa_fit_error(d, d_out, b, _ptr(G), _ptr(C), _ptr(Q_ff), _ptr(W), _ptr(dW), _ptr(eps_abs),
+    _check(lib.ispa_fit_error(d, d_out, b, _ptr(G), _ptr(C), _ptr(E), _ptr(W), _ptr(dW), _ptr(eps_abs),
                               _ptr(eps_rel), _ptr(workspace), ws_bytes, _stream(stream)))
 
 

@@ -8,7 +8,7 @@ and attend locally from then on) and "Dynamic Layer Selection" (all layers are
 ranked by reconstruction error; the lowest-error ones are converted).
 
 This module is host orchestration only: it owns the per-layer device state
-(stacked G, C, Q_ff, W, dW) and issues the library's calls; every arithmetic
+(stacked G, C, E, W, dW) and issues the library's calls; every arithmetic
 step runs in the HIP kernels behind the C ABI.  Reading used for the ranking by
 default: every layer is solved (batched), its post-fit error eps_rel comes from
 the Gram statistics, and the k lowest (ties to the lower layer index) are
@@ -82,7 +82,7 @@ class LayerStack:
         f32 = dict(dtype=torch.float32, device=dev)
         self.G = torch.zeros(L, d, d, **f32)
         self.C = torch.zeros(L, d, d, **f32)
-        self.Q_ff = torch.zeros(L, d, d, **f32)
+        self.E = torch.zeros(L, d, d, **f32)
         self.dW = torch.zeros(L, d, do, **f32)
         self.info = torch.zeros(L, dtype=torch.int32, device=dev)
         self.eps_abs = torch.zeros(L, dtype=torch.float64, device=dev)
@@ -94,7 +94,7 @@ class LayerStack:
         if selection == "heldout":
             self.G_h = torch.zeros(L, d, d, **f32)
             self.C_h = torch.zeros(L, d, d, **f32)
-            self.Q_h = torch.zeros(L, d, d, **f32)
+            self.E_h = torch.zeros(L, d, d, **f32)
             self.heldout_seen = [0] * L
         self.dW_compact: Optional[torch.Tensor] = None  # prefit: dW of the chosen layers, selection order
         self.info_compact: Optional[torch.Tensor] = None
@@ -126,7 +126,7 @@ class LayerStack:
     @_on_stack_stream
     def warmup_chunk(self, layer: int, q, k_loc, v_loc, k_hist, v_hist, o_loc, o_full,
                      lse_loc=None, lse_full=None, heldout: bool = False) -> None:
-        """Dual-stream attention of one chunk of `layer`, then its rows into the layer's G, C, Q_ff.
+        """Dual-stream attention of one chunk of `layer`, then its rows into the layer's G, C, E.
 
         ``o_loc`` / ``o_full`` [n_q, H, D] receive A_loc / A_full of this chunk."""
         if self.converted is not None:
@@ -141,7 +141,7 @@ class LayerStack:
 
     @_on_stack_stream
     def accumulate_rows(self, layer: int, a_loc, a_full, heldout: bool = False) -> None:
-        """Add warmup rows computed elsewhere ([n, d] or [n, H, D]) to the layer's G, C, Q_ff (or, with
+        """Add warmup rows computed elsewhere ([n, d] or [n, H, D]) to the layer's G, C, E (or, with
         ``heldout`` under selection="heldout", to the held-out statistics the ranking is measured on)."""
         if self.converted is not None:
             raise ispa.IspaError(ispa.ISPA_E_INVALID_ARG, "warmup is over (transition already ran)")
@@ -152,11 +152,11 @@ class LayerStack:
         if need and (self._gram_ws is None or self._gram_ws.numel() < need):
             self._gram_ws = ispa.workspace(need, a_loc.device)
         if heldout:
-            ispa.ispa_gram_accum(a_loc, a_full, self.G_h[layer], self.C_h[layer], self.Q_h[layer],
+            ispa.ispa_gram_accum(a_loc, a_full, self.G_h[layer], self.C_h[layer], self.E_h[layer],
                                  accumulate=self.heldout_seen[layer] > 0, workspace=self._gram_ws)
             self.heldout_seen[layer] += 1
             return
-        ispa.ispa_gram_accum(a_loc, a_full, self.G[layer], self.C[layer], self.Q_ff[layer],
+        ispa.ispa_gram_accum(a_loc, a_full, self.G[layer], self.C[layer], self.E[layer],
                              accumulate=self.chunks_seen[layer] > 0, workspace=self._gram_ws)
         self.chunks_seen[layer] += 1
 
@@ -196,19 +196,19 @@ class LayerStack:
 
         prefit: errors at dW = 0 and ranking first; the chosen layers are solved in convert()."""
         if self.selection == "prefit":
-            ispa.ispa_fit_error(self.G, self.C, self.Q_ff, self.W, None, self.eps_abs, self.eps_rel,
+            ispa.ispa_fit_error(self.G, self.C, self.E, self.W, None, self.eps_abs, self.eps_rel,
                                 workspace=self._eps_ws)
             self._select()
             return
         self._solve(self.G, self.C, self.W, self.dW, self.info, self.lambdas, self._absorb_ws)
         if self.selection == "heldout":
-            ispa.ispa_fit_error(self.G_h, self.C_h, self.Q_h, self.W, self.dW, self.eps_abs, self.eps_rel,
+            ispa.ispa_fit_error(self.G_h, self.C_h, self.E_h, self.W, self.dW, self.eps_abs, self.eps_rel,
                                 workspace=self._eps_ws)
         elif self.lam_policy == "trace":  # per-layer lambda: the general form (no normal-equation shortcut)
-            ispa.ispa_fit_error(self.G, self.C, self.Q_ff, self.W, self.dW, self.eps_abs, self.eps_rel,
+            ispa.ispa_fit_error(self.G, self.C, self.E, self.W, self.dW, self.eps_abs, self.eps_rel,
                                 workspace=self._eps_ws)
         else:
-            ispa.ispa_layer_eps(self.G, self.C, self.Q_ff, self.W, self.dW, self.lam, self.eps_abs, self.eps_rel,
+            ispa.ispa_layer_eps(self.G, self.C, self.E, self.W, self.dW, self.lam, self.eps_abs, self.eps_rel,
                                 workspace=self._eps_ws)
         self._select()
 

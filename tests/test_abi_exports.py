@@ -85,8 +85,16 @@ def test_workspace_queries():
     # the absorb factor lives in the workspace: at least batch*d*d floats
     assert lib.ispa_absorb_workspace_size(1536, 1536, 30) >= 30 * 1536 * 1536 * 4
     assert lib.ispa_eps_workspace_size(1536, 1536, 2) == 3 * 2 * 1536 * 1536 * 4
-    assert lib.ispa_gram_workspace_size(4680, 5120, ispa.ISPA_BF16) == 0  # enough tiles: no split
-    assert lib.ispa_gram_workspace_size(4680, 1536, ispa.ISPA_BF16) > 0  # few tiles: split rows
+    # bf16: the split D_hi, D_lo of the rows (2 x 2 bytes per element), a counter per output tile, and
+    # partial sums only when the tiles alone cannot fill the GPU
+    dsplit = 2 * 4680 * 5120 * 2
+    assert dsplit <= lib.ispa_gram_workspace_size(4680, 5120, ispa.ISPA_BF16) < dsplit + (1 << 20)  # no split
+    dsplit = 2 * 4680 * 1536 * 2
+    assert lib.ispa_gram_workspace_size(4680, 1536, ispa.ISPA_BF16) >= dsplit + 2 * 3 * 1536 * 1536 * 4  # split rows
+    # more rows than one block: the split is formed 32768 rows at a time
+    assert lib.ispa_gram_workspace_size(10 ** 6, 1536, ispa.ISPA_BF16) == lib.ispa_gram_workspace_size(32768, 1536,
+                                                                                                     ispa.ISPA_BF16)
+    assert lib.ispa_gram_workspace_size(0, 1536, ispa.ISPA_BF16) == 0
     assert lib.ispa_gram_workspace_size(256, 128, ispa.ISPA_F32) == 0
 
 
@@ -155,7 +163,7 @@ def test_variant_validation_needs_no_gpu():
     ok = 0x10000
     bad = ispa.ISPA_E_INVALID_ARG
     assert lib.ispa_fit_error(100, 64, 1, ok, ok, ok, ok, None, ok, ok, None, 0, None) == bad  # d % 64
-    assert lib.ispa_fit_error(128, 64, 1, ok, ok, None, ok, None, ok, ok, None, 0, None) == bad  # Q_ff required
+    assert lib.ispa_fit_error(128, 64, 1, ok, ok, None, ok, None, ok, ok, None, 0, None) == bad  # E required
     assert lib.ispa_fit_error_workspace_size(128, 64, 3) == 4 * 3 * 128 * 64 * 4
     assert lib.ispa_lambda_from_trace(128, 2, ok, -1.0, ok, None) == bad
     assert lib.ispa_lambda_from_trace(128, 0, ok, 1.0, ok, None) == bad

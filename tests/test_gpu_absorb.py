@@ -16,7 +16,8 @@ from tests.gpu_util import TOL_DW, dev, host64, nan_workspace, poisoned, relfro,
 pytestmark = pytest.mark.gpu
 
 TOL_G = 1e-5  # relative Frobenius, float32 accumulation over <= 2e4 rows (derived: ~sqrt(n) * 2^-24)
-TOL_C = 1e-4  # C = X - G loses up to |X|/|C| (about 10 here) of that
+TOL_C = 1e-5  # C = A_loc^T (D_hi + D_lo): D carried to within 2^-17, then the same accumulation as G
+TOL_E = 2e-5  # E = D_hi^T D_hi + D_hi^T D_lo + D_lo^T D_hi: the dropped D_lo^T D_lo term is below 2^-17
 
 
 def gpu_gram(chunks, d, qff=False):
@@ -59,14 +60,14 @@ def test_gram_parity(case):
     chunks = list(zip(split_rows(al, 3), split_rows(af, 3))) if n else [(al, af)]
     G, C, Q = gpu_gram(chunks, d, qff=True)
     Gr, Cr = oracle.gram(al.f64, af.f64)
-    Qr = af.f64.T @ af.f64
+    Er = (af.f64 - al.f64).T @ (af.f64 - al.f64)
     if n == 0:
         assert torch.all(G == 0).item() and torch.all(C == 0).item() and torch.all(Q == 0).item()
         return
-    eg, ec, eq = relfro(host64(G), Gr), relfro(host64(C), Cr), relfro(host64(Q), Qr)
-    say("relfro G, C, Q_ff", eg, ec, eq)
-    assert eg <= TOL_G and ec <= TOL_C and eq <= TOL_G
-    assert torch.equal(G, G.T)  # both triangles written, exactly symmetric
+    eg, ec, eq = relfro(host64(G), Gr), relfro(host64(C), Cr), relfro(host64(Q), Er)
+    say("relfro G, C, E", eg, ec, eq)
+    assert eg <= TOL_G and ec <= TOL_C and eq <= TOL_E
+    assert torch.equal(G, G.T) and torch.equal(Q, Q.T)  # both triangles written, exactly symmetric
 
 
 def test_gram_full_size_and_deterministic():
@@ -84,38 +85,63 @@ def test_gram_full_size_and_deterministic():
 
 
 def test_gram_rows_past_one_launch():
-    """More rows than one launch takes (row offsets are 32-bit: (rows + 64) * 2d bytes < 2^31, so
-    262080 rows at d = 4096): the call splits them over launches, the later ones accumulating.  It
-    must equal the same rows given as two calls bit for bit, and sampled entries of G and C must
-    match float64 dot products of the rows on the host.  Rows are seeded draws made on the device
-    (4.3 GB of input would take minutes to draw on the host)."""
+    """More rows than one launch block takes (the bf16 split of D = A_full - A_loc is formed for at
+    most 32768 rows at a time): the call splits them over blocks, the later ones accumulating.  It
+    must equal the same rows given as two calls at a block boundary bit for bit, and sampled entries
+    of G, C and E must match float64 dot products of the rows on the host.  Rows are seeded draws
+    made on the device (0.5 GB of input would take long to draw on the host)."""
     d = 4096
-    block = ((1 << 31) // (2 * d) - 64) // 32 * 32
-    n = block + 1000
+    block = min(((1 << 31) // (2 * d) - 64) // 32 * 32, 32768)
+    n = 2 * block + 1000
     gen = torch.Generator(device="cuda").manual_seed(77)
     al = torch.randn(n, d, device="cuda", generator=gen).to(torch.bfloat16)
     af = (al.float() + 0.3 * torch.randn(n, d, device="cuda", generator=gen)).to(torch.bfloat16)
-    G1, C1 = poisoned((d, d), torch.float32), poisoned((d, d), torch.float32)
-    ispa.ispa_gram_accum(al, af, G1, C1, accumulate=False,
+    G1, C1, E1 = (poisoned((d, d), torch.float32) for _ in range(3))
+    ispa.ispa_gram_accum(al, af, G1, C1, E1, accumulate=False,
                          workspace=nan_workspace(ispa.ispa_gram_workspace_size(n, d, torch.bfloat16)))
-    G2, C2 = poisoned((d, d), torch.float32), poisoned((d, d), torch.float32)
-    ispa.ispa_gram_accum(al[:block], af[:block], G2, C2, accumulate=False,
-                         workspace=nan_workspace(ispa.ispa_gram_workspace_size(block, d, torch.bfloat16)))
-    ispa.ispa_gram_accum(al[block:], af[block:], G2, C2, accumulate=True,
-                         workspace=nan_workspace(ispa.ispa_gram_workspace_size(n - block, d, torch.bfloat16)))
+    G2, C2, E2 = (poisoned((d, d), torch.float32) for _ in range(3))
+    ispa.ispa_gram_accum(al[:2 * block], af[:2 * block], G2, C2, E2, accumulate=False,
+                         workspace=nan_workspace(ispa.ispa_gram_workspace_size(2 * block, d, torch.bfloat16)))
+    ispa.ispa_gram_accum(al[2 * block:], af[2 * block:], G2, C2, E2, accumulate=True,
+                         workspace=nan_workspace(ispa.ispa_gram_workspace_size(n - 2 * block, d, torch.bfloat16)))
     torch.cuda.synchronize()
-    assert torch.equal(G1, G2) and torch.equal(C1, C2)
+    assert torch.equal(G1, G2) and torch.equal(C1, C2) and torch.equal(E1, E2)
     g = np.random.default_rng(5)
     pairs = [(0, 0), (d - 1, d - 1), (d - 1, 0), (0, d - 1)] + [tuple(g.integers(0, d, 2)) for _ in range(8)]
     for i, j in pairs:
         ai = al[:, i].double().cpu().numpy()
         aj = al[:, j].double().cpu().numpy()
-        fj = af[:, j].double().cpu().numpy()
-        g_ref, c_ref = float(ai @ aj), float(ai @ (fj - aj))
-        g_abs, c_abs = float(np.abs(ai) @ np.abs(aj)), float(np.abs(ai) @ (np.abs(fj) + np.abs(aj)))
-        # float32 accumulation of n exact products: well inside n * 2^-24 of the absolute sums
-        assert abs(G1[i, j].item() - g_ref) <= 1e-4 * g_abs, (i, j)
-        assert abs(C1[i, j].item() - c_ref) <= 1e-4 * c_abs, (i, j)
+        di = af[:, i].double().cpu().numpy() - ai
+        dj = af[:, j].double().cpu().numpy() - aj
+        # float32 accumulation of n products (D carried to within 2^-17): well inside n * 2^-24 of the
+        # absolute sums
+        for got, ref, absum in ((G1[i, j], ai @ aj, np.abs(ai) @ np.abs(aj)), (C1[i, j], ai @ dj, np.abs(ai) @ np.abs(dj)),
+                                (E1[i, j], di @ dj, np.abs(di) @ np.abs(dj))):
+            assert abs(got.item() - float(ref)) <= 1e-4 * float(absum), (i, j)
+
+
+@pytest.mark.parametrize("d,n,scale", [(256, 18720, 1.0), (256, 18720, 0.1), (256, 18720, 0.01),
+                                       (1536, 18720, 0.1), (1536, 18720, 0.01)])
+def test_gram_and_solve_when_the_streams_nearly_agree(d, n, scale):
+    """A_full - A_loc scaled down to 10 % and 1 % (the layers the selection converts first): C and E
+    are formed from the difference itself, so their relative accuracy, and dW's, does not degrade as
+    the difference shrinks (forming C as A_loc^T A_full - A_loc^T A_loc would lose a factor 1 / scale).
+    Gated on dW (relative Frobenius 1e-3) and on C, E against the oracle's float64 statistics."""
+    al, af = inputs.absorb_rows(31, 0, n, d, "bf16", diff_scale=scale)
+    chunks = list(zip(split_rows(al, 4), split_rows(af, 4)))
+    G, C, E = gpu_gram(chunks, d, qff=True)
+    Gr, Cr = oracle.gram(al.f64, af.f64)
+    D = af.f64 - al.f64
+    Er = D.T @ D
+    eg, ec, ee = relfro(host64(G), Gr), relfro(host64(C), Cr), relfro(host64(E), Er)
+    W = inputs.normal(31, 0, inputs.LAYER_CHUNK, inputs.T_W, (d, d)) * np.float32(d ** -0.5)
+    dW, info = gpu_solve(G, C, torch.from_numpy(W).cuda(), 1e-2)
+    assert info.item() == 0
+    ref = oracle.ridge_solve(Gr, Cr, W.astype(np.float64), 1e-2)
+    e = relfro(host64(dW), ref)
+    say("scale", scale, "relfro G, C, E", eg, ec, ee, "dW", e)
+    assert eg <= TOL_G and ec <= TOL_C and ee <= TOL_E
+    assert e <= TOL_DW
 
 
 @pytest.mark.parametrize("d,d_out", [(128, 128), (256, 192), (1536, 1536)])

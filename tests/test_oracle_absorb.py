@@ -117,17 +117,20 @@ def test_solution_minimises_objective():
 
 
 def test_reconstruction_error_closed_form():
-    """eps from the rows equals the Gram-statistics form
-    <Q_ff - C - C^T - G, W W^T> - <dW, C W> - lambda ||dW||^2 (with Q_ff = A_full^T A_full)."""
+    """eps from the rows equals the Gram-statistics form the GPU evaluates, with D = A_full - A_loc,
+    E = D^T D and the normal equation: <E, W W^T> - <dW, C W> - lambda ||dW||^2; and the denominator
+    ||A_full W||^2 = <G + C + C^T + E, W W^T>."""
     a_loc, a_full = _rows(15, 400, 16)
     W = np.random.default_rng(16).standard_normal((16, 16)) / 4
     lam = 1e-2
     G, C = oracle.gram(a_loc, a_full)
     dW = oracle.ridge_solve(G, C, W, lam)
     eps, eps_rel = oracle.reconstruction_error(a_loc, a_full, W, dW)
-    Qff = a_full.T @ a_full
-    cf = np.sum((Qff - C - C.T - G) * (W @ W.T)) - np.sum(dW * (C @ W)) - lam * np.sum(dW * dW)
+    E = (a_full - a_loc).T @ (a_full - a_loc)
+    cf = np.sum(E * (W @ W.T)) - np.sum(dW * (C @ W)) - lam * np.sum(dW * dW)
     assert abs(eps - cf) <= 1e-11 * abs(eps)
+    denom = np.sum((G + C + C.T + E) * (W @ W.T))
+    assert abs(denom - np.sum((a_full @ W) ** 2)) <= 1e-12 * denom
     assert abs(eps_rel - eps / np.sum((a_full @ W) ** 2)) <= 1e-15
     # the post-fit error is below the pre-fit discrepancy ||(A_full - A_loc) W||^2
     assert eps < np.sum(((a_full - a_loc) @ W) ** 2)
@@ -196,9 +199,10 @@ def test_prefit_and_heldout_errors_are_the_residual_definition():
     G, C = oracle.gram(a_loc[:400], a_full[:400])
     dW = oracle.ridge_solve(G, C, W, 1e-2)
     Gh, Ch = oracle.gram(a_loc[400:], a_full[400:])
-    Qh = a_full[400:].T @ a_full[400:]
+    Dh = a_full[400:] - a_loc[400:]
+    Eh = Dh.T @ Dh
     eh, _ = oracle.reconstruction_error(a_loc[400:], a_full[400:], W, dW)
-    general = (np.sum((Qh - Ch - Ch.T - Gh) * (W @ W.T)) + np.sum(dW * (Gh @ dW)) - 2 * np.sum(dW * (Ch @ W)))
+    general = np.sum(Eh * (W @ W.T)) + np.sum(dW * (Gh @ dW)) - 2 * np.sum(dW * (Ch @ W))
     assert eh == pytest.approx(general, rel=1e-10)
-    fitted_form = np.sum((Qh - Ch - Ch.T - Gh) * (W @ W.T)) - np.sum(dW * (Ch @ W)) - 1e-2 * np.sum(dW * dW)
+    fitted_form = np.sum(Eh * (W @ W.T)) - np.sum(dW * (Ch @ W)) - 1e-2 * np.sum(dW * dW)
     assert abs(eh - fitted_form) > 1e-6 * abs(eh)
