@@ -1,17 +1,18 @@
 """Benchmark of the ISPA hot path on one MI355X.
 
-One step = the whole warmup-and-absorb path of one Wan-1.3B-shaped attention
-layer: for each of the 4 warmup chunks, ispa_decomp_attn (local branch,
+One step = the whole warmup-and-absorb path of one attention layer (by
+default the Wan-14B-shaped layer, the largest single layer; --config picks
+another): for each of the 4 warmup chunks, ispa_decomp_attn (local branch,
 history branch, fused LSE merge) then ispa_gram_accum on (A_loc, A_full);
-then ispa_absorb_solve (dW for the layer).  Inputs are seeded synthetic data
-already resident in HBM when timing starts.
+then ispa_absorb_solve_ex (dW for the layer).  Inputs are seeded synthetic
+data already resident in HBM when timing starts.
 
 Prints ONE JSON line.  `value` is decomposable-attention TFLOP/s over the
 whole step (attention matmul FLOPs of the 4 chunks / step time); the per-kernel
 numbers, the absorb ms/layer, the roofline of the dominant kernel and the
 oracle's CPU rate are reported beside it.
 
-    python bench.py [--steps K] [--warmup W] [--config 1] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--config 3] [--also 1] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -44,8 +45,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--config", type=int, default=1,
-                    help="1: Wan-1.3B layer, 2: long history, 3: Wan-14B layer, 4: 30-layer 1.3B stack")
+    ap.add_argument("--config", type=int, default=3,
+                    help="1: Wan-1.3B layer, 2: long history, 3: Wan-14B layer (the largest single layer, default), "
+                         "4: 30-layer 1.3B stack")
+    ap.add_argument("--also", type=lambda v: [int(x) for x in v.split(",") if x], default=[1],
+                    help="other single-layer configurations whose core figures are reported beside (comma list)")
     ap.add_argument("--gen-workers", type=int, default=min(16, os.cpu_count() or 1),
                     help="processes drawing the 30-layer stack's inputs (config 4)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -54,8 +58,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU seconds for the oracle sample")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes (calibrates HBM byte counters)")
-    ap.add_argument("--traffic", type=str, default=os.path.join(ROOT, "profiles", "attn_bf16_kernel_wan1.3b_hbm_traffic.json"),
-                    help="measured HBM traffic of the attention kernel (from rocprofv3 counters), if present")
+    ap.add_argument("--traffic", type=str, default=None,
+                    help="measured HBM traffic of the attention kernel (from rocprofv3 counters); default "
+                         "profiles/attn_bf16_kernel_<workload>_hbm_traffic.json")
     return ap.parse_args()
 
 
@@ -89,89 +94,236 @@ def main():
     if args.config == 4:
         return bench_stack(args, stack_inputs)
     cfg = inputs.CONFIGS[args.config]
+    main_run = time_layer_step(cfg, args.steps, args.warmup, args.prewarm)
+    result = layer_result(args, cfg, main_run)
+    # the comparison, streaming, split-KV, fp8 and no-refinement figures on the headline layer's chunk 0
+    result.update(layer_extras(cfg, main_run))
+    main_run.release()
+    # the other single-layer shapes' core figures, timed the same way (fewer steps)
+    also = {}
+    for other in args.also:
+        if other == args.config or other not in (1, 2, 3):
+            continue
+        ocfg = inputs.CONFIGS[other]
+        run = time_layer_step(ocfg, max(3, args.steps // 2), 1, min(args.prewarm, 0.5))
+        also[ocfg.name] = core_figures(ocfg, run)
+        run.release()
+    if also:
+        result["also"] = also
+    result["reference_bf16_gemm_tflops"] = reference_gemm_tflops()
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+class LayerRun:
+    """Device inputs and buffers of one layer shape, with the timed steps' measurements."""
+
+    def release(self):
+        import torch
+
+        self.__dict__.clear()
+        torch.cuda.empty_cache()
+
+
+def time_layer_step(cfg, steps: int, warmup: int, prewarm_s: float) -> LayerRun:
+    """One step = for each warmup chunk: ispa_decomp_attn (both branches and the fused merge) then
+    ispa_gram_accum on its rows; then ispa_absorb_solve_ex (R = C W on a caller-owned side stream).
+    Inputs resident in HBM; `steps` timed steps after `warmup` untimed ones, per-kernel durations from
+    HIP events recorded on the launch stream inside the timed steps."""
+    import torch
+
+    from kv_cache_absorption_ispa_amd import inputs, ispa
+
     H, D, d = cfg.heads, cfg.head_dim, cfg.d
+    r = LayerRun()
 
     def dev(t):
         return torch.from_numpy(t.raw.view(np.int16)).view(torch.bfloat16).cuda()
 
-    # ---- inputs resident in HBM: 4 warmup chunks (different Q / chunk K,V / history K,V each)
     log(f"[bench] generating inputs for {cfg.name}")
-    chunks = []
+    r.chunks = []
     for c in range(cfg.n_chunks):
         x = inputs.chunk_inputs(cfg, 0, c)
-        chunks.append(dict(q=dev(x.q), kl=dev(x.k_loc), vl=dev(x.v_loc), kh=dev(x.k_hist), vh=dev(x.v_hist)))
-    W = torch.from_numpy(inputs.weight(cfg, 0)).cuda()
+        r.chunks.append(dict(q=dev(x.q), kl=dev(x.k_loc), vl=dev(x.v_loc), kh=dev(x.k_hist), vh=dev(x.v_hist)))
+    r.W = torch.from_numpy(inputs.weight(cfg, 0)).cuda()
     nq = cfg.n_q
-    o_loc = torch.empty(nq, H, D, dtype=torch.bfloat16, device="cuda")
-    o_hist = torch.empty_like(o_loc)
-    o_full = torch.empty_like(o_loc)
-    lse = [torch.empty(H, nq, device="cuda") for _ in range(3)]
-    G = torch.empty(d, d, device="cuda")
-    C = torch.empty(d, d, device="cuda")
-    dW = torch.empty(d, d, device="cuda")
-    info = torch.empty(1, dtype=torch.int32, device="cuda")
-    gws = ispa.workspace(ispa.ispa_gram_workspace_size(nq, d, torch.bfloat16))
-    atws = ispa.workspace(ispa.ispa_decomp_attn_workspace_size(chunks[0]["q"], cfg.n_loc, cfg.n_hist))
-    aws = ispa.workspace(ispa.ispa_absorb_workspace_size(d, d, 1))
-    side = ispa.SideStream()  # caller-owned stream for R = C W beside the factorisation
+    r.o_loc = torch.empty(nq, H, D, dtype=torch.bfloat16, device="cuda")
+    r.o_hist = torch.empty_like(r.o_loc)
+    r.o_full = torch.empty_like(r.o_loc)
+    r.lse = [torch.empty(H, nq, device="cuda") for _ in range(3)]
+    r.G = torch.empty(d, d, device="cuda")
+    r.C = torch.empty(d, d, device="cuda")
+    r.dW = torch.empty(d, d, device="cuda")
+    r.info = torch.empty(1, dtype=torch.int32, device="cuda")
+    r.gws = ispa.workspace(ispa.ispa_gram_workspace_size(nq, d, torch.bfloat16))
+    r.atws = ispa.workspace(ispa.ispa_decomp_attn_workspace_size(r.chunks[0]["q"], cfg.n_loc, cfg.n_hist))
+    r.aws = ispa.workspace(ispa.ispa_absorb_workspace_size(d, d, 1))
+    r.side = ispa.SideStream()  # caller-owned stream for R = C W beside the factorisation
     torch.cuda.synchronize()
-
     n_ev = 2 * cfg.n_chunks + 1
 
     def step(events=None):
-        for c, ch in enumerate(chunks):
+        for c, ch in enumerate(r.chunks):
             if events is not None:
                 events[2 * c][0].record()
-            ispa.ispa_decomp_attn(ch["q"], ch["kl"], ch["vl"], ch["kh"], ch["vh"], o_loc=o_loc, lse_loc=lse[0],
-                                  o_hist=o_hist, lse_hist=lse[1], o_full=o_full, lse_full=lse[2], workspace=atws)
+            ispa.ispa_decomp_attn(ch["q"], ch["kl"], ch["vl"], ch["kh"], ch["vh"], o_loc=r.o_loc, lse_loc=r.lse[0],
+                                  o_hist=r.o_hist, lse_hist=r.lse[1], o_full=r.o_full, lse_full=r.lse[2],
+                                  workspace=r.atws)
             if events is not None:
                 events[2 * c][1].record()
                 events[2 * c + 1][0].record()
-            ispa.ispa_gram_accum(o_loc, o_full, G, C, accumulate=c > 0, workspace=gws)
+            ispa.ispa_gram_accum(r.o_loc, r.o_full, r.G, r.C, accumulate=c > 0, workspace=r.gws)
             if events is not None:
                 events[2 * c + 1][1].record()
         if events is not None:
             events[-1][0].record()
-        ispa.ispa_absorb_solve_ex(G, C, W, cfg.lam, dW, info, workspace=aws, side=side)
+        ispa.ispa_absorb_solve_ex(r.G, r.C, r.W, cfg.lam, r.dW, r.info, workspace=r.aws, side=r.side)
         if events is not None:
             events[-1][1].record()
 
-    prewarm_steps = prewarm(step, args.prewarm)
-    log(f"[bench] prewarm {prewarm_steps} steps, warmup {args.warmup} steps")
-    for _ in range(args.warmup):
+    r.prewarm_steps = prewarm(step, prewarm_s)
+    log(f"[bench] {cfg.name}: prewarm {r.prewarm_steps} steps, warmup {warmup} steps")
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    if info.item() != 0:
-        raise RuntimeError(f"absorb failed, info = {info.item()}")
-
-    # ---- timed region: exactly K steps, whole-job wall clock; per-kernel durations from HIP events
-    # recorded on the launch stream around each call of the same steps
-    log(f"[bench] timing {args.steps} steps")
+    if r.info.item() != 0:
+        raise RuntimeError(f"absorb failed, info = {r.info.item()}")
+    log(f"[bench] {cfg.name}: timing {steps} steps")
     evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
-           for _ in range(args.steps)]
+           for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for k in range(args.steps):
+    for k in range(steps):
         step(evs[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-    attn_ms, gram_ms, solve_ms = [], [], []
+    r.steps = steps
+    r.ms_per_step = wall * 1e3 / steps
+    r.attn_ms, r.gram_ms, r.solve_ms = [], [], []
     for ev in evs:
         for c in range(cfg.n_chunks):
-            attn_ms.append(ev[2 * c][0].elapsed_time(ev[2 * c][1]))
-            gram_ms.append(ev[2 * c + 1][0].elapsed_time(ev[2 * c + 1][1]))
-        solve_ms.append(ev[-1][0].elapsed_time(ev[-1][1]))
+            r.attn_ms.append(ev[2 * c][0].elapsed_time(ev[2 * c][1]))
+            r.gram_ms.append(ev[2 * c + 1][0].elapsed_time(ev[2 * c + 1][1]))
+        r.solve_ms.append(ev[-1][0].elapsed_time(ev[-1][1]))
+    return r
 
-    # ---- single-pass attention over the concatenated keys (the comparison pass)
-    ch = chunks[0]
+
+def core_figures(cfg, r: LayerRun) -> dict:
+    """Whole-step and per-kernel figures of a timed layer run."""
+    d, nq = cfg.d, cfg.n_q
+    attn_flops = cfg.attn_flops()
+    attn_avg = float(np.mean(r.attn_ms))
+    achieved = attn_flops / (attn_avg * 1e-3) / 1e12
+    gram_flops = 3.0 * nq * d * d
+    solve_flops = 13.0 / 3.0 * float(d) ** 3
+    solve_bytes = 16.0 * d * d
+    solve_ms = float(np.mean(r.solve_ms))
+    gram_ms = float(np.mean(r.gram_ms))
+    return {
+        "workload": workload_name(cfg),
+        "ms_per_step": round(r.ms_per_step, 4),
+        "value_tflops": round(attn_flops * cfg.n_chunks / (r.ms_per_step * 1e-3) / 1e12, 2),
+        "attn_tflops_kernel": round(achieved, 2),
+        "attn_pct_bf16_peak": round(100 * achieved / PEAK_BF16_TFLOPS, 2),
+        "attn_ms_per_chunk": round(attn_avg, 4),
+        "gram_ms_per_chunk": round(gram_ms, 4),
+        # algorithmic Gram work: 2 d^2 per row for C plus d^2 per row for the symmetric G
+        "gram_tflops": round(gram_flops / (gram_ms * 1e-3) / 1e12, 2),
+        "gram_pct_bf16_peak": round(100 * gram_flops / (gram_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "absorb_ms_per_layer": round(solve_ms, 4),
+        # algorithmic solve work 13/3 d^3 (factor d^3/3, R = C W 2 d^3, two triangular solves 2 d^3) and its
+        # compulsory bytes (read G, C, W, write dW: 16 d^2), against the measured absorb time
+        "absorb_tflops": round(solve_flops / (solve_ms * 1e-3) / 1e12, 3),
+        "absorb_pct_fp32_peak": round(100 * solve_flops / (solve_ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 2),
+        "absorb_gbps": round(solve_bytes / (solve_ms * 1e-3) / 1e9, 1),
+    }
+
+
+def workload_name(cfg) -> str:
+    return (f"{cfg.name}: {cfg.heads} heads x {cfg.head_dim}, {cfg.n_q} queries/chunk, {cfg.n_sink} sink + "
+            f"{cfg.n_chunk} chunk local keys, {cfg.n_hist} history keys, {cfg.n_chunks} warmup chunks, "
+            f"absorb d={cfg.d}")
+
+
+def layer_result(args, cfg, r: LayerRun) -> dict:
+    """The JSON line's fixed keys, the roofline of the dominant kernel and the core figures."""
+    core = core_figures(cfg, r)
+    attn_flops = cfg.attn_flops()
+    achieved = core["attn_tflops_kernel"]
+    traffic = None
+    tpath = args.traffic or os.path.join(ROOT, "profiles", f"attn_bf16_kernel_{cfg.name}_hbm_traffic.json")
+    if os.path.exists(tpath):
+        try:
+            with open(tpath) as f:
+                t = json.load(f)
+            if t.get("kernel_source_sha") == kernel_source_sha():
+                traffic = t.get("bytes_per_launch")
+        except Exception:
+            traffic = None
+    out = {
+        "metric": METRIC,
+        "value": core["value_tflops"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": core["ms_per_step"],
+        "prewarm_steps": r.prewarm_steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q/K/V, 8 sink keys at 4x norm; random-init W)",
+        "config": {
+            "workload": core["workload"],
+            "global_batch": cfg.n_chunks * cfg.n_q,
+            "seq_len": cfg.n_loc + cfg.n_hist,
+            "parallelism": "single GPU",
+        },
+    }
+    out.update({k: v for k, v in core.items() if k not in ("workload", "ms_per_step", "value_tflops")})
+    out["roofline"] = {
+        "bound": "mfma",
+        "kernel": "attn_bf16_kernel<128, 8, 1, 128, false, false> (ispa_decomp_attn)",
+        "achieved": achieved,
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "traffic": traffic,
+        "algorithmic_flops_per_launch": attn_flops,
+    }
+    return out
+
+
+def layer_extras(cfg, r: LayerRun) -> dict:
+    """Comparison and variant figures on chunk 0 of the timed layer (each timed back to back)."""
+    import torch
+
+    from kv_cache_absorption_ispa_amd import ispa
+
+    H, D, d, nq = cfg.heads, cfg.head_dim, cfg.d, cfg.n_q
+    attn_flops = cfg.attn_flops()
+    ch = r.chunks[0]
+    o_loc, o_hist, o_full, lse = r.o_loc, r.o_hist, r.o_full, r.lse
+    tf = lambda ms, fl=attn_flops: round(fl / (ms * 1e-3) / 1e12, 2)
+
+    # ---- the ratio to one softmax pass over the concatenated keys: the decomposable call on its two
+    # buffers, the single pass, and the decomposable call on two views of the single pass's buffer, timed
+    # with the same protocol on the same chunk (rounds interleaved, so clock drift hits all three alike)
     kcat = torch.cat([ch["kl"], ch["kh"]])
     vcat = torch.cat([ch["vl"], ch["vh"]])
     o_single = torch.empty_like(o_loc)
     lse_single = torch.empty(H, nq, device="cuda")
-    # back-to-back launches, like the attention calls inside the steps (an isolated launch after a
-    # synchronisation would also time the GPU's wake-up)
-    full_ms = back_to_back_ms(lambda: ispa.ispa_full_attn(ch["q"], kcat, vcat, o=o_single, lse=lse_single))
+    nl = cfg.n_loc
+    two = lambda: ispa.ispa_decomp_attn(ch["q"], ch["kl"], ch["vl"], ch["kh"], ch["vh"], o_loc=o_loc, lse_loc=lse[0],
+                                        o_hist=o_hist, lse_hist=lse[1], o_full=o_full, lse_full=lse[2],
+                                        workspace=r.atws)
+    single = lambda: ispa.ispa_full_attn(ch["q"], kcat, vcat, o=o_single, lse=lse_single)
+    views = lambda: ispa.ispa_decomp_attn(ch["q"], kcat[:nl], vcat[:nl], kcat[nl:], vcat[nl:], o_loc=o_loc,
+                                          lse_loc=lse[0], o_hist=o_hist, lse_hist=lse[1], o_full=o_full,
+                                          lse_full=lse[2], workspace=r.atws)
+    two_ms, single_ms, views_ms = interleaved_ms([two, single, views])
     del kcat, vcat
 
     # ---- the same chunk with its keys as a streaming cache holds them: sink and chunk in their own
@@ -182,15 +334,12 @@ def main():
     hist_segs = [(ch["kh"][:cut].clone(), ch["vh"][:cut].clone()), (ch["kh"][cut:].clone(), ch["vh"][cut:].clone())]
     seg_ms = back_to_back_ms(lambda: ispa.ispa_decomp_attn_segments(
         ch["q"], loc_segs, hist_segs, o_loc=o_loc, lse_loc=lse[0], o_hist=o_hist, lse_hist=lse[1], o_full=o_full,
-        lse_full=lse[2], workspace=atws))
-    two_ms = back_to_back_ms(lambda: ispa.ispa_decomp_attn(
-        ch["q"], ch["kl"], ch["vl"], ch["kh"], ch["vh"], o_loc=o_loc, lse_loc=lse[0], o_hist=o_hist,
-        lse_hist=lse[1], o_full=o_full, lse_full=lse[2], workspace=atws))
+        lse_full=lse[2], workspace=r.atws))
     del loc_segs, hist_segs
 
     # ---- split-KV form (ispa_decomp_attn_splitkv, one workgroup per CU): at the full chunk every XCD
     # already has more units than spare workgroups (P = 1, the unsplit launch); a short query chunk of
-    # 512 queries (24 units for 256 CUs) is where the key split pays
+    # 512 queries is where the key split pays
     skws = ispa.workspace(ispa.ispa_decomp_attn_splitkv_workspace_size(ch["q"], cfg.n_loc, cfg.n_hist, 0))
     sk_ms = back_to_back_ms(lambda: ispa.ispa_decomp_attn_splitkv(
         ch["q"], [(ch["kl"], ch["vl"])], [(ch["kh"], ch["vh"])], o_loc=o_loc, lse_loc=lse[0], o_hist=o_hist,
@@ -205,14 +354,14 @@ def main():
     short_split = back_to_back_ms(lambda: ispa.ispa_decomp_attn_splitkv(
         q_s, [(ch["kl"], ch["vl"])], [(ch["kh"], ch["vh"])], o_loc=o_s[0], lse_loc=l_s[0], o_hist=o_s[1],
         lse_hist=l_s[1], o_full=o_s[2], lse_full=l_s[2], workspace=skws))
-    short_flops = cfg.attn_flops() * nq_s / nq
+    short_flops = attn_flops * nq_s / nq
+    del skws, q_s, o_s, l_s
 
     # ---- the absorb without its refinement step (ispa_absorb_solve_ex, ISPA_ABSORB_NO_REFINE)
-    dW2 = torch.empty_like(dW)
-    norefine_ms = back_to_back_ms(lambda: ispa.ispa_absorb_solve_ex(G, C, W, cfg.lam, dW2, info, refine=False,
-                                                                    workspace=aws, side=side), n=3)
+    dW2 = torch.empty_like(r.dW)
+    norefine_ms = back_to_back_ms(lambda: ispa.ispa_absorb_solve_ex(r.G, r.C, r.W, cfg.lam, dW2, r.info, refine=False,
+                                                                    workspace=r.aws, side=r.side), n=3)
     del dW2
-    del skws, q_s, o_s, l_s
 
     # ---- fp8 keys (ispa_decomp_attn_fp8k): Q and K as E4M3 codes with per-head scales (quantised on the
     # GPU, timed apart), S = K Q^T on the fp8 matrix cores; and the W8A8 projection of the chunk's rows
@@ -230,123 +379,61 @@ def main():
     quant_ms = back_to_back_ms(quant_qk)
     f8_ms = back_to_back_ms(lambda: ispa.ispa_decomp_attn_fp8k(
         q8, qsc, [(kl8, klsc, ch["vl"])], [(kh8, khsc, ch["vh"])], o_loc=o_loc, lse_loc=lse[0], o_hist=o_hist,
-        lse_hist=lse[1], o_full=o_full, lse_full=lse[2], workspace=atws))
+        lse_hist=lse[1], o_full=o_full, lse_full=lse[2], workspace=r.atws))
     a8 = torch.empty(nq, d, dtype=torch.uint8, device="cuda")
     asc = torch.empty(nq, device="cuda")
     w8t = torch.empty(d, d, dtype=torch.uint8, device="cuda")
     wsc = torch.empty(d, device="cuda")
     a_rows = o_loc.reshape(nq, d)
-    ispa.ispa_quantize_fp8_cols(W, w8t, wsc)
+    ispa.ispa_quantize_fp8_cols(r.W, w8t, wsc)
     y8 = torch.empty(nq, d, dtype=torch.bfloat16, device="cuda")
     rowq_ms = back_to_back_ms(lambda: ispa.ispa_quantize_fp8_rows(a_rows, a8, asc))
     w8a8_ms = back_to_back_ms(lambda: ispa.ispa_w8a8_gemm(a8, asc, w8t, wsc, y8))
     del q8, kl8, kh8, qws, a8, w8t, y8
-    gemm_ref = reference_gemm_tflops()
 
-    attn_flops = cfg.attn_flops()
-    step_attn_flops = attn_flops * cfg.n_chunks
-    gram_flops = 3.0 * nq * d * d
-    solve_flops = 13.0 / 3.0 * float(d) ** 3
-    solve_bytes = 16.0 * d * d
-    attn_avg = float(np.mean(attn_ms))
-    achieved = attn_flops / (attn_avg * 1e-3) / 1e12
-    value = step_attn_flops / (ms_per_step * 1e-3) / 1e12
-
-    traffic = None
-    if os.path.exists(args.traffic):
-        try:
-            with open(args.traffic) as f:
-                t = json.load(f)
-            if t.get("kernel_source_sha") == kernel_source_sha():
-                traffic = t.get("bytes_per_launch")
-        except Exception:
-            traffic = None
-
-    result = {
-        "metric": METRIC,
-        "value": round(value, 2),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
-        "prewarm_steps": prewarm_steps,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) Q/K/V, 8 sink keys at 4x norm; random-init W)",
-        "config": {
-            "workload": f"{cfg.name}: {H} heads x {D}, {nq} queries/chunk, {cfg.n_sink} sink + {cfg.n_chunk} chunk "
-                        f"local keys, {cfg.n_hist} history keys, {cfg.n_chunks} warmup chunks, absorb d={d}",
-            "global_batch": cfg.n_chunks * nq,
-            "seq_len": cfg.n_loc + cfg.n_hist,
-            "parallelism": "single GPU",
+    med = lambda v: float(np.median(v))
+    return {
+        "ratio": {
+            "protocol": "back to back, 10 launches per round, 5 rounds interleaved, median, chunk 0",
+            "decomp_two_buffers_ms": round(med(two_ms), 4),
+            "single_pass_ms": round(med(single_ms), 4),
+            "single_pass_tflops": tf(med(single_ms)),
+            "single_pass_pct_bf16_peak": round(100 * attn_flops / (med(single_ms) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+            "decomp_on_single_pass_buffer_ms": round(med(views_ms), 4),
+            "decomp_vs_single_pass": round(med(two_ms) / med(single_ms), 4),
         },
-        "attn_tflops_kernel": round(achieved, 2),
-        "attn_pct_bf16_peak": round(100 * achieved / PEAK_BF16_TFLOPS, 2),
-        "attn_ms_per_chunk": round(attn_avg, 4),
-        "single_pass_ms": round(float(np.median(full_ms)), 4),
-        "ratio_decomp_vs_single_pass": round(attn_avg / float(np.median(full_ms)), 4),
-        "reference_bf16_gemm_tflops": gemm_ref,
+        "ratio_decomp_vs_single_pass": round(med(two_ms) / med(single_ms), 4),
         "splitkv": {
             "workers": "one per compute unit",
-            "ms": round(float(np.median(sk_ms)), 4),
-            "ratio_vs_two_buffer": round(float(np.median(sk_ms)) / float(np.median(two_ms)), 4),
+            "ms": round(med(sk_ms), 4),
+            "ratio_vs_two_buffer": round(med(sk_ms) / med(two_ms), 4),
             "short_chunk_queries": nq_s,
-            "short_chunk_unsplit_ms": round(float(np.median(short_unsplit)), 4),
-            "short_chunk_split_ms": round(float(np.median(short_split)), 4),
-            "short_chunk_speedup": round(float(np.median(short_unsplit)) / float(np.median(short_split)), 3),
-            "short_chunk_split_tflops": round(short_flops / (float(np.median(short_split)) * 1e-3) / 1e12, 2),
+            "short_chunk_unsplit_ms": round(med(short_unsplit), 4),
+            "short_chunk_split_ms": round(med(short_split), 4),
+            "short_chunk_speedup": round(med(short_unsplit) / med(short_split), 3),
+            "short_chunk_split_tflops": tf(med(short_split), short_flops),
         },
         "fp8": {
-            "attn_ms": round(float(np.median(f8_ms)), 4),
-            "attn_tflops": round(attn_flops / (float(np.median(f8_ms)) * 1e-3) / 1e12, 2),
-            "attn_speedup_vs_bf16": round(float(np.median(two_ms)) / float(np.median(f8_ms)), 3),
+            "attn_ms": round(med(f8_ms), 4),
+            "attn_tflops": tf(med(f8_ms)),
+            "attn_speedup_vs_bf16": round(med(two_ms) / med(f8_ms), 3),
             "attn_peak_tflops": PEAK_FP8K_TFLOPS,
-            "quantize_q_k_ms": round(float(np.median(quant_ms)), 4),
+            "quantize_q_k_ms": round(med(quant_ms), 4),
             "w8a8_rows": nq, "w8a8_d": d,
-            "quantize_rows_ms": round(float(np.median(rowq_ms)), 4),
-            "w8a8_gemm_ms": round(float(np.median(w8a8_ms)), 4),
-            "w8a8_tflops": round(2.0 * nq * d * d / (float(np.median(w8a8_ms)) * 1e-3) / 1e12, 2),
-            "w8a8_frac_of_fp8_peak": round(2.0 * nq * d * d / (float(np.median(w8a8_ms)) * 1e-3) / 1e12
-                                           / PEAK_FP8_TFLOPS, 4),
+            "quantize_rows_ms": round(med(rowq_ms), 4),
+            "w8a8_gemm_ms": round(med(w8a8_ms), 4),
+            "w8a8_tflops": tf(med(w8a8_ms), 2.0 * nq * d * d),
+            "w8a8_frac_of_fp8_peak": round(2.0 * nq * d * d / (med(w8a8_ms) * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
         },
         "segments": {
             "layout": f"local [{ns} sink | {nc} chunk], history [{cut} | {cfg.n_hist - cut}] (wrapped ring)",
-            "ms": round(float(np.median(seg_ms)), 4),
-            "two_buffer_ms": round(float(np.median(two_ms)), 4),
-            "ratio_vs_two_buffer": round(float(np.median(seg_ms)) / float(np.median(two_ms)), 4),
-            "tflops": round(attn_flops / (float(np.median(seg_ms)) * 1e-3) / 1e12, 2),
+            "ms": round(med(seg_ms), 4),
+            "two_buffer_ms": round(med(two_ms), 4),
+            "ratio_vs_two_buffer": round(med(seg_ms) / med(two_ms), 4),
+            "tflops": tf(med(seg_ms)),
         },
-        "gram_ms_per_chunk": round(float(np.mean(gram_ms)), 4),
-        # algorithmic Gram work: 2 d^2 per row for C plus d^2 per row for the symmetric G
-        "gram_tflops": round(gram_flops / (float(np.mean(gram_ms)) * 1e-3) / 1e12, 2),
-        "gram_pct_bf16_peak": round(100 * gram_flops / (float(np.mean(gram_ms)) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-                                    2),
-        "absorb_ms_per_layer": round(float(np.mean(solve_ms)), 4),
-        "absorb_ms_per_layer_no_refine": round(float(np.median(norefine_ms)), 4),
-        # algorithmic solve work 13/3 d^3 (factor d^3/3, R = C W 2 d^3, two triangular solves 2 d^3) and its
-        # compulsory bytes (read G, C, W, write dW: 16 d^2), against the measured absorb time
-        "absorb_tflops": round(solve_flops / (float(np.mean(solve_ms)) * 1e-3) / 1e12, 3),
-        "absorb_pct_fp32_peak": round(100 * solve_flops / (float(np.mean(solve_ms)) * 1e-3) / 1e12
-                                      / PEAK_FP32_TFLOPS, 2),
-        "absorb_gbps": round(solve_bytes / (float(np.mean(solve_ms)) * 1e-3) / 1e9, 1),
-        "roofline": {
-            "bound": "mfma",
-            "kernel": "attn_bf16_kernel<128, 8, 1, 128, false, false> (ispa_decomp_attn)",
-            "achieved": round(achieved, 2),
-            "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": traffic,
-            "algorithmic_flops_per_launch": attn_flops,
-        },
+        "absorb_ms_per_layer_no_refine": round(med(norefine_ms), 4),
     }
-
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
-    print(json.dumps(result), flush=True)
 
 
 # --------------------------------------------------------------------------- #
@@ -557,6 +644,26 @@ def reference_gemm_tflops(n: int = 8192, reps: int = 20) -> float:
     e1.record()
     torch.cuda.synchronize()
     return round(2.0 * n ** 3 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
+
+
+def interleaved_ms(fns, n: int = 10, rounds: int = 5, warm: int = 3):
+    """Per-launch ms of each of `fns`, launched n times back to back per round, the functions taking turns
+    round by round."""
+    import torch
+    for fn in fns:
+        for _ in range(warm):
+            fn()
+    out = [[] for _ in fns]
+    for _ in range(rounds):
+        for i, fn in enumerate(fns):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(n):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            out[i].append(e0.elapsed_time(e1) / n)
+    return out
 
 
 def back_to_back_ms(fn, n: int = 10, rounds: int = 3, warm: int = 3):
