@@ -91,6 +91,14 @@ ispa_status_t launch_absorb(int32_t d, int32_t d_out, int32_t batch, const float
                             const float* W, float lambda, const float* lam_b, float* dW, float* W_new,
                             int32_t* info, void* ws, size_t ws_bytes, hipStream_t s, bool refine = true,
                             const SideStream* side = nullptr);
+// bf16x3 triangular applies (hi*hi + hi*lo + lo*hi): Lsplit / LTsplit hold split(L^-1) and
+// split(L^-T) (2 * batch * d * d bf16 each), YTsplit and ZTsplit 2 * batch * d * d_out bf16 each.
+bool apply3_supported(int32_t d, int32_t d_out);
+ispa_status_t launch_split_lower(int32_t d, int32_t batch, const float* Linv, void* Lsplit, void* LTsplit,
+                                 const int32_t* info, hipStream_t s);
+ispa_status_t launch_chol_apply3(int32_t d, int32_t d_out, int32_t batch, const void* Lsplit, const void* LTsplit,
+                                 const float* Y, void* YTsplit, void* ZTsplit, float* X, const int32_t* info,
+                                 hipStream_t s);
 size_t fit_error_workspace_size(int32_t d, int32_t d_out, int32_t batch);
 ispa_status_t launch_fit_error(int32_t d, int32_t d_out, int32_t batch, const float* G, const float* C,
                                const float* E, const float* W, const float* dW, double* eps_abs, double* eps_rel,

@@ -30,6 +30,7 @@
 // float64-accumulated products run on v_mfma_f64_16x16x4_f64.  A layer whose pivot
 // fails records info = column + 1 and is skipped by later kernels; its dW is
 // set to NaN at the end and its W_new is left alone.
+#include <algorithm>
 #include <utility>
 #include <vector>
 
@@ -50,6 +51,17 @@ constexpr int NB = 64;  // panel width
 // publishes the finished columns in LDS, the later block columns subtract their rank-16 update
 // in parallel, and meanwhile the wave inverts its 16 x 16 diagonal block.  The off-diagonal blocks
 // of L^-1 follow by two doubling levels, inv([A 0; B C]) = [A^-1 0; -C^-1 B A^-1  C^-1].
+// Workgroups (over the batch) that R = C W may hold while it runs beside the factorisation: one
+// per compute unit, so every unit keeps room for the factorisation's launches.
+#ifndef ISPA_CW_WORKGROUPS
+#define ISPA_CW_WORKGROUPS 256
+#endif
+// Columns per panel of the blocked trailing update (a multiple of NB).
+#ifndef ISPA_CHOL_PANEL
+#define ISPA_CHOL_PANEL 512
+#endif
+constexpr int CP = ISPA_CHOL_PANEL;
+static_assert(CP % 64 == 0, "panel of whole blocks");
 constexpr int SB = NB / 4;     // block column width
 constexpr int LSTR = NB + 4;   // LDS row stride (floats): rows stay 16-byte aligned for vector reads
 static_assert(NB == 64 && SB == 16, "the diagonal kernel maps 64 rows onto the 64 lanes of a wave");
@@ -248,15 +260,15 @@ struct GemmParams {
 // Cin may equal D.
 constexpr int GKS = 32;
 
-template <bool TA, bool TB, int T, bool DIAG = false>
+// PERSIST: grid.x workgroups per batch entry loop over the output tiles (row-major, each XCD's
+// workgroups on consecutive tiles), so a long product holds at most grid.x slots of the GPU while
+// a latency-bound chain of small launches runs beside it on another stream.
+template <bool TA, bool TB, int T, bool DIAG = false, bool PERSIST = false>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
   constexpr int WB = T / 64;               // 32x32 blocks per wave per dimension
   constexpr int NLD = T * GKS / 1024;      // float4 loads per thread per operand per slab
   const int b = blockIdx.z / p.npairs, q = blockIdx.z % p.npairs;
   if (p.info && p.info[b] != 0) return;
-  const int tm = blockIdx.y, tn = blockIdx.x;
-  if (p.lower_only && tm < tn) return;
-  const int m0 = tm * T, n0 = tn * T;
   __shared__ __attribute__((aligned(16))) float As[2][GKS][T + 4];  // [buffer][k][m]
   __shared__ __attribute__((aligned(16))) float Bs[2][GKS][T + 4];  // [buffer][k][n]
   static_assert(2 * GKS * (T + 4) >= DIAG_LS_FLOATS, "the diagonal factorisation reuses As and Bs");
@@ -265,6 +277,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
   const int wm = (wave >> 1) * (T / 2), wn = (wave & 1) * (T / 2);
   const float* A = p.A + b * p.sA + q * p.pA;
   const float* B = p.B + b * p.sB + q * p.pB;
+  auto run_tile = [&](const int tm, const int tn) {
+  const int m0 = tm * T, n0 = tn * T;
   f32x16 acc[WB][WB];
 #pragma unroll
   for (int i = 0; i < WB; ++i)
@@ -368,6 +382,16 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
         if (Cin && p.beta != 0.f) x = fmaf(p.beta, Cin[(size_t)r * p.ldc + c], x);
         D[(size_t)r * p.ldd + c] = x;
       }
+  };
+  if constexpr (PERSIST) {
+    // (every slab ends with a barrier, so the LDS is free when the next tile starts)
+    const int tiles_n = p.N / T, tiles = (p.M / T) * tiles_n;
+    for (int t = (int)xcd_remap(blockIdx.x, gridDim.x); t < tiles; t += gridDim.x) run_tile(t / tiles_n, t % tiles_n);
+    return;
+  }
+  const int tm = blockIdx.y, tn = blockIdx.x;
+  if (p.lower_only && tm < tn) return;
+  run_tile(tm, tn);
   if constexpr (DIAG) {
     if (tm == 0 && tn == 0 && q == 0) {
       // the tile just written holds the next diagonal block: make the stores visible to this
@@ -461,6 +485,7 @@ __global__ __launch_bounds__(256) void gemm_f64acc_kernel(GemmDParams p) {
         if (p.D32) p.D32[b * p.sD + (size_t)r * p.ldd + c] = (float)x;
       }
 }
+
 
 // M = G + lambda I (full matrix); L^-1 = 0; info = 0.
 __global__ __launch_bounds__(256) void init_shift_kernel(const float* __restrict__ G, float* M, float* Linvf, int d,
@@ -590,7 +615,8 @@ ispa_status_t gemm(hipStream_t s, int batch, int M, int N, int K, const float* A
                    int ldb, size_t sB, const float* Cin, int ldc, size_t sC, float* D, int ldd, size_t sD, float alpha,
                    float beta, bool lower_only, const int32_t* info, int kmode = 0, int npairs = 1,
                    size_t pA = 0, size_t pB = 0, size_t pC = 0, size_t pD = 0, float* diag_M = nullptr,
-                   float* diag_Linv = nullptr, int32_t* diag_info = nullptr, int diag_d = 0, int diag_k0 = 0) {
+                   float* diag_Linv = nullptr, int32_t* diag_info = nullptr, int diag_d = 0, int diag_k0 = 0,
+                   int max_wg = 0) {
   if (M <= 0 || N <= 0 || K <= 0) return ISPA_OK;
   if (K % GKS != 0) {
     set_error("internal: GEMM depth not a multiple of 32");
@@ -624,6 +650,10 @@ ispa_status_t gemm(hipStream_t s, int batch, int M, int N, int K, const float* A
         hipLaunchKernelGGL((gemm_f32_kernel<TA, TB, 64, true>), dim3(N / 64, M / 64, z), dim3(256), 0, s, p);
       return hip_check(hipGetLastError(), "gemm_f32_kernel launch");
     }
+  }
+  if (big && max_wg > 0 && !lower_only && (M / 128) * (N / 128) > max_wg) {
+    hipLaunchKernelGGL((gemm_f32_kernel<TA, TB, 128, false, true>), dim3(max_wg, 1, z), dim3(256), 0, s, p);
+    return hip_check(hipGetLastError(), "gemm_f32_kernel launch");
   }
   if (big)
     hipLaunchKernelGGL((gemm_f32_kernel<TA, TB, 128>), dim3(N / 128, M / 128, z), dim3(256), 0, s, p);
@@ -775,7 +805,8 @@ ispa_status_t launch_absorb(int32_t d, int32_t d_out, int32_t batch, const float
     joiner.ev = side->ev_join;
     joiner.armed = true;
     return gemm<false, false>(side->stream, batch, d, d_out, d, C, d, dd, W, d_out, dn, nullptr, 0, 0, Rb, d_out, dn,
-                              1.f, 0.f, false, nullptr);
+                              1.f, 0.f, false, nullptr, 0, 1, 0, 0, 0, 0, nullptr, nullptr, nullptr, 0, 0,
+                              d > 2048 ? ISPA_CW_WORKGROUPS / batch : 0);
   };
   const int fork_k = (side != nullptr && d <= 2048) ? 4 : -1;  // panel step before which it is forked (-1: first)
   bool forked = false;
@@ -802,10 +833,21 @@ ispa_status_t launch_absorb(int32_t d, int32_t d_out, int32_t batch, const float
     // L_ik = M_ik L_kk^-T (in place)
     ISPA_TRY((gemm<false, true>(s, batch, rest, NB, NB, panel, d, dd, Lkk_inv, d, dd, nullptr, 0, 0, panel, d, dd,
                                 1.f, 0.f, false, info)));
-    // trailing update, lower tiles; tile (0, 0) is diagonal block k + 1, factored in the same launch
+    // trailing update, lower tiles; tile (0, 0) is diagonal block k + 1, factored in the same launch.
+    // Blocks are grouped in panels of CP columns: inside a panel a step updates only the panel's
+    // remaining columns (a narrow launch on the chain); the panel's last step updates everything to
+    // its right with all CP columns at once (K = CP), so the trailing matrix is read and written once
+    // per panel instead of once per block.
     float* trail = M + (size_t)(k0 + NB) * d + k0 + NB;
-    ISPA_TRY((gemm<false, true>(s, batch, rest, rest, NB, panel, d, dd, panel, d, dd, trail, d, dd, trail, d, dd, -1.f,
-                                1.f, true, info, 0, 1, 0, 0, 0, 0, M, Linvf, info, d, k0 + NB)));
+    const int p0 = k0 / CP * CP, pe = std::min(d, p0 + CP);
+    if (k0 + NB < pe) {
+      ISPA_TRY((gemm<false, true>(s, batch, rest, pe - k0 - NB, NB, panel, d, dd, panel, d, dd, trail, d, dd, trail, d,
+                                  dd, -1.f, 1.f, true, info, 0, 1, 0, 0, 0, 0, M, Linvf, info, d, k0 + NB)));
+    } else {
+      const float* pan = M + (size_t)pe * d + p0;  // rows pe.., columns p0 .. pe of L
+      ISPA_TRY((gemm<false, true>(s, batch, rest, rest, pe - p0, pan, d, dd, pan, d, dd, trail, d, dd, trail, d, dd,
+                                  -1.f, 1.f, true, info, 0, 1, 0, 0, 0, 0, M, Linvf, info, d, k0 + NB)));
+    }
   }
   if (!forked) ISPA_TRY(fork_cw());
   // join: R = C W is done before the solve reads it
@@ -813,8 +855,18 @@ ispa_status_t launch_absorb(int32_t d, int32_t d_out, int32_t batch, const float
   // explicit L^-1 by recursive doubling over block ranges: for adjacent ranges A (first) and C,
   // inv([A 0; B C]) has off-diagonal block -C^-1 (B A^-1); pairs of equal sizes run as one launch.
   ISPA_TRY(invert_lower(s, batch, d, M, Linvf, Tb, info));
-  // X = (L L^T)^-1 R
-  ISPA_TRY(chol_apply(s, batch, d, d_out, Linvf, Rb, Zb, dW, info));
+  // X = (L L^T)^-1 R.  With the refinement, both solves run on the bf16 matrix cores as three-term
+  // products (about 2^-16 relative per product); the float64-accumulated residual then corrects
+  // the first solve's error and the correction's error is that much smaller again.  L (M) and the
+  // doubling scratch (Tb) are free once L^-1 is built and take its splits; Rr (not yet written)
+  // takes the split R, Zb the split intermediate.
+  const bool use3 = refine && apply3_supported(d, d_out);
+  if (use3) {
+    ISPA_TRY(launch_split_lower(d, batch, Linvf, Tb, M, info, s));
+    ISPA_TRY(launch_chol_apply3(d, d_out, batch, Tb, M, Rb, Rr, Zb, dW, info, s));
+  } else {
+    ISPA_TRY(chol_apply(s, batch, d, d_out, Linvf, Rb, Zb, dW, info));
+  }
   if (!refine) {
     hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)((dn / 4 + 255) / 256), batch), dim3(256), 0, s, W, dW,
                        (const float*)nullptr, W_new, dn, (const int32_t*)info);
@@ -824,7 +876,10 @@ ispa_status_t launch_absorb(int32_t d, int32_t d_out, int32_t batch, const float
   // correction = (L L^T)^-1 r
   ISPA_TRY(gemm_d(s, batch, d, d_out, d, G, d, dd, dW, d_out, dn, Rb, d_out, dn, dW, d_out, dn, nullptr, Rr, d_out,
                   dn, -1.0, 1.0, lam_b ? -1.0 : -(double)lambda, info, lam_b));
-  ISPA_TRY(chol_apply(s, batch, d, d_out, Linvf, Rr, Zb, Rr, info));
+  if (use3)  // R is no longer needed: its buffer takes the split residual
+    ISPA_TRY(launch_chol_apply3(d, d_out, batch, Tb, M, Rr, Rb, Zb, Rr, info, s));
+  else
+    ISPA_TRY(chol_apply(s, batch, d, d_out, Linvf, Rr, Zb, Rr, info));
   hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)((dn / 4 + 255) / 256), batch), dim3(256), 0, s, W, dW,
                      (const float*)Rr, W_new, dn, (const int32_t*)info);
   return hip_check(hipGetLastError(), "finalize_kernel launch");

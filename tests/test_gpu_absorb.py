@@ -144,7 +144,7 @@ def test_gram_and_solve_when_the_streams_nearly_agree(d, n, scale):
     assert e <= TOL_DW
 
 
-@pytest.mark.parametrize("d,d_out", [(128, 128), (256, 192), (1536, 1536)])
+@pytest.mark.parametrize("d,d_out", [(128, 128), (256, 192), (1536, 1536), (2048, 1024), (2560, 640)])
 def test_solve_parity_on_oracle_statistics(d, d_out):
     """ispa_absorb_solve alone: G, C are the oracle's (rounded to float32), dW vs the float64 solve."""
     al, af = inputs.absorb_rows(7, 0, max(4 * d, 512), d, "f32")
@@ -218,13 +218,15 @@ def test_not_positive_definite_reports_info():
     assert torch.equal(Wn, W)  # untouched
 
 
-@pytest.mark.parametrize("d,bad_col", [(64, 40), (256, 200), (384, 70)])
+@pytest.mark.parametrize("d,bad_col", [(64, 40), (256, 200), (384, 70), (2048, 100), (2048, 1030), (2048, 1100)])
 def test_batched_solve_with_a_failing_layer(d, bad_col):
     """Three layers, the middle one singular at column bad_col (lambda = 0 and an all-zero column of
     its A_loc): info names that column for it alone, its dW is NaN and W_new untouched, and the other
     two layers match the oracle.  The failing pivot lies in the first diagonal block (d = 64, where
     the factorisation is one block) or in a later block, which is factored inside the launch that
-    applies the previous panel's trailing update."""
+    applies the previous panel's trailing update.  At d = 2048 that launch runs on 128 x 128 tiles
+    when the trailing size is a multiple of 128 and large (1030: block 16, trailing size 1024) and on
+    64 x 64 tiles otherwise (100: block 1; 1100: block 17)."""
     Gs, Cs, Ws, refs = [], [], [], []
     for layer in range(3):
         al, af = inputs.absorb_rows(12, layer, max(4 * d, 600), d, "f32")
@@ -254,7 +256,7 @@ def test_batched_solve_with_a_failing_layer(d, bad_col):
         assert torch.equal(Wn[i], W[i] + dW[i])
 
 
-@pytest.mark.parametrize("d,batch", [(384, 1), (1536, 4)])
+@pytest.mark.parametrize("d,batch", [(384, 1), (1536, 4), (2048, 2)])
 def test_refinement_reaches_the_float64_solve(d, batch):
     """W is a column permutation scaled by powers of two, so R = C W is exact in float32 and the only
     float32 error left is the factorisation's.  At lambda = 0 (cond ~4e4 at d = 384, ~2e5 at d = 1536)
