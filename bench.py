@@ -357,6 +357,12 @@ def layer_extras(cfg, r: LayerRun) -> dict:
     short_flops = attn_flops * nq_s / nq
     del skws, q_s, o_s, l_s
 
+    # ---- the standalone N-way merge (ispa_lse_merge) of the chunk's two branch results into O_full and
+    # LSE_full: reads both (O, LSE) pairs once and writes one, so HBM-bound
+    two()
+    merge_ms = back_to_back_ms(lambda: ispa.ispa_lse_merge([o_loc, o_hist], [lse[0], lse[1]], o_full, lse[2]))
+    merge_bytes = 3 * (o_loc.numel() * o_loc.element_size() + lse[0].numel() * 4)
+
     # ---- the absorb without its refinement step (ispa_absorb_solve_ex, ISPA_ABSORB_NO_REFINE)
     dW2 = torch.empty_like(r.dW)
     norefine_ms = back_to_back_ms(lambda: ispa.ispa_absorb_solve_ex(r.G, r.C, r.W, cfg.lam, dW2, r.info, refine=False,
@@ -433,6 +439,13 @@ def layer_extras(cfg, r: LayerRun) -> dict:
             "tflops": tf(med(seg_ms)),
         },
         "absorb_ms_per_layer_no_refine": round(med(norefine_ms), 4),
+        "lse_merge": {
+            "parts": 2,
+            "ms": round(med(merge_ms), 4),
+            "algorithmic_bytes": merge_bytes,
+            "gbps": round(merge_bytes / (med(merge_ms) * 1e-3) / 1e9, 1),
+            "frac_hbm_peak": round(merge_bytes / (med(merge_ms) * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        },
     }
 
 
