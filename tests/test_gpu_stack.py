@@ -170,6 +170,40 @@ def test_stack_gpu_chain_properties():
         relfro(dWn[0], oracle.ridge_solve(G, C, W0[0].astype(np.float64), cfg.lam)))
 
 
+def _run_chain(cfg, W0, stream, delay):
+    """Warmup + transition of the small stack, optionally on a caller stream held back by a bounded
+    spin kernel first (so anything read without waiting for that stream would be stale)."""
+    L, K, H, D, nq = cfg.n_layers, cfg.n_absorb, cfg.heads, cfg.head_dim, cfg.n_q
+    st = LayerStack(torch.from_numpy(W0.copy()).cuda(), H, D, nq, cfg.lam, K, stream=stream)
+    o_loc = torch.empty(nq, H, D, dtype=torch.bfloat16, device="cuda")
+    o_full = torch.empty_like(o_loc)
+    inp = {(l, c): _chunk(cfg, l, c)[1] for c in range(cfg.n_chunks) for l in range(L)}
+    torch.cuda.synchronize()
+    if delay and stream is not None:
+        with torch.cuda.stream(stream):
+            torch.cuda._sleep(delay)
+    for c in range(cfg.n_chunks):
+        for l in range(L):
+            st.warmup_chunk(l, *inp[(l, c)], o_loc, o_full)
+    conv = st.transition()  # host reads of the selection: must wait for the stack's stream
+    return st, conv
+
+
+def test_stack_on_a_caller_stream_matches_the_default_stream():
+    """LayerStack(stream=s): every call runs on s and the host reads wait for it.  A spin kernel
+    queued on s first delays all of its work; the chain's results (selection, eps, dW, W) must still
+    equal, bit for bit, those of the same chain on the default stream."""
+    cfg = SMALL_STACK
+    W0 = _weights(cfg)
+    ref, conv_ref = _run_chain(cfg, W0, None, 0)
+    side = torch.cuda.Stream()
+    st, conv = _run_chain(cfg, W0, side, 200_000_000)
+    torch.cuda.synchronize()
+    assert conv == conv_ref
+    for name in ("eps_rel", "dW", "W", "selected", "info"):
+        assert torch.equal(getattr(st, name), getattr(ref, name)), name
+
+
 def test_select_layers_orders_ties_and_nan():
     """Ranking kernel on planted values: ties go to the lower id, NaN ranks last."""
     e = torch.tensor([3.0, 1.0, float("nan"), 1.0, 0.5, 2.0, float("nan"), 1.0], dtype=torch.float64,
