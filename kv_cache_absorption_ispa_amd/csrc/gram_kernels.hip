@@ -19,21 +19,20 @@
 //
 // bf16 design (three launches per block of rows):
 //  * split pass (HBM-bound): D_hi, D_lo [rows, d] into the workspace;
-//  * Gram kernel: a workgroup owns an output tile (I, J) of TI x 128 and a
-//    range of rows.  Per 32-row stage (two or three in flight) it stages
-//    A_loc[:, I], D_hi[:, J], D_lo[:, J] and, for tiles that reach the upper
-//    triangle, A_loc[:, J] (and D_hi[:, I], D_lo[:, I] for E) row-major in LDS
-//    straight from global memory (buffer loads into LDS, 16-byte chunks
-//    XOR-swizzled by row); MFMA operands need 8 consecutive rows at one column
-//    and come from two transposing LDS reads (ds_read_b64_tr_b16).  Waves own
-//    (TI / (waves / 2)) x 64 sub-tiles (blocks of v_mfma_f32_32x32x16_bf16).  C
-//    is formed on every tile; the symmetric G and E only on tiles that reach
-//    the upper triangle, and only their elements on or above the diagonal are
-//    kept.  Rows are split over workgroups when the tiles alone cannot fill the
-//    GPU; every split then stores its partial tile in the workspace;
-//  * finish kernel: adds the partials in split order (bitwise deterministic,
-//    no atomics) and mirrors G and E into the lower triangle through LDS
-//    transposes, so both triangles hold the same bits.
+//  * Gram kernel, two passes over the rows.  The C pass owns output tiles of TI x 128 (TI = 256
+//    where d allows) and forms C from A_loc[:, I], D_hi[:, J], D_lo[:, J]; the G pass owns the
+//    TI x 128 tiles that reach the upper triangle and forms G (and, in a launch of its own, E) from
+//    A_loc[:, I], A_loc[:, J] (and D_hi, D_lo of both).  Without E both passes run in one launch.
+//    Per 32-row stage (two in flight) the staged matrices go row-major into LDS straight from
+//    global memory (buffer loads into LDS, 16-byte chunks XOR-swizzled by row); MFMA operands need
+//    8 consecutive rows at one column and come from two transposing LDS reads (ds_read_b64_tr_b16).
+//    Four waves own (TI / 2) x 64 sub-tiles (blocks of v_mfma_f32_32x32x16_bf16): each operand
+//    fragment read from LDS feeds TI / 32 or 4 MFMAs, and one accumulator set per pass keeps two
+//    waves per SIMD.  Rows are split over workgroups when the tiles alone cannot fill the GPU;
+//    every split then stores its partial tile in the workspace;
+//  * finish kernel: adds the partials in split order (bitwise deterministic, no atomics) and
+//    mirrors G and E into the lower triangle through LDS transposes, so both triangles hold the
+//    same bits.
 #include "ispa_internal.h"
 
 namespace ispa {
@@ -58,80 +57,113 @@ struct GramParams {
   float* part;         // split partials: [split][matrix (C, G, E)][d][d] (splits > 1), else NULL
   int64_t n_rows;
   int d;
-  int tiles_j;  // output tiles along J (d / 128); tile t is (t / tiles_j, t % tiles_j)
+  int tiles_j;  // output tiles along J (d / 128); C pass tile t is (t / tiles_j, t % tiles_j)
+  int tiles_c, tiles_ge;  // tiles of the C pass and of the G (and E) pass
   int64_t rows_per_split;
-  int splits;
+  int splits;  // row splits (the same for both passes)
   int accumulate;
 };
 
+// The kernel runs as two passes over the same rows.
+//  * PASS_C: C = A_loc^T D_hi + A_loc^T D_lo on every output tile.  Tiles are TI (256 where d allows,
+//    else 128) x 128; a wave owns (TI / 2) x 64, so each operand fragment read from LDS feeds
+//    TI / 32 (A side) or 4 (D side) MFMAs, and one accumulator set keeps two waves per SIMD.
+//  * PASS_GE: G = A_loc^T A_loc, and E = D_hi^T D_hi + D_hi^T D_lo + D_lo^T D_hi when EV, on the
+//    128 x 128 tiles on or above the diagonal only (listed compactly, row by row); the finish
+//    kernel mirrors them.
 // Staged matrices of a stage, one after the other, each GBK rows, row-major:
-//   0 A_loc[:, I] (TI wide)  1 D_hi[:, J]  2 D_lo[:, J]  3 A_loc[:, J]  4 D_hi[:, I] (TI)  5 D_lo[:, I] (TI)
-// 3 is staged on tiles that reach the upper triangle (for G), 4 and 5 there too when E is formed.
-template <int TI>
-__host__ __device__ constexpr int gram_width(int m) { return (m == 0 || m >= 4) ? TI : GT; }
-template <int TI>
-__host__ __device__ constexpr int gram_moff(int m) {  // element offset of matrix m in a stage
-  return m == 0 ? 0 : gram_moff<TI>(m - 1) + GBK * gram_width<TI>(m - 1);
+//   PASS_C:  0 A_loc[:, I] (TI)   1 D_hi[:, J]   2 D_lo[:, J]
+//   PASS_GE: 0 A_loc[:, I]   1 A_loc[:, J]   (EV: 2 D_hi[:, I]   3 D_lo[:, I]   4 D_hi[:, J]   5 D_lo[:, J])
+constexpr int PASS_C = 0, PASS_GE = 1;
+
+template <int PASS, bool EV, int TI_>
+struct GramShape {
+  static constexpr int TI = TI_;
+  static constexpr int TJ = GT;
+  static constexpr int NM = PASS == PASS_C ? 3 : (EV ? 6 : 2);
+  static constexpr int WBI = TI / 64;  // 32-row blocks per wave along I (2 x 2 waves)
+  static constexpr int WBJ = TJ / 64;
+  __host__ __device__ static constexpr int side(int m) {  // 0: columns I, 1: columns J
+    return PASS == PASS_C ? (m == 0 ? 0 : 1) : ((m == 0 || m == 2 || m == 3) ? 0 : 1);
+  }
+  __host__ __device__ static constexpr int src(int m) {  // 0: A_loc, 1: D_hi, 2: D_lo
+    return PASS == PASS_C ? m : (m < 2 ? 0 : ((m == 2 || m == 4) ? 1 : 2));
+  }
+  __host__ __device__ static constexpr int width(int m) { return side(m) == 0 ? TI : TJ; }
+  __host__ __device__ static constexpr int moff(int m) { return m == 0 ? 0 : moff(m - 1) + GBK * width(m - 1); }
+  static constexpr int SS = moff(NM);  // elements per stage
+};
+
+// Tile (ti, tj) of PASS_GE's compact list of TI x 128 tiles that reach the upper triangle: u runs
+// row by row; row ti holds the n - r*ti tiles tj >= r*ti (n = d / 128, r = TI / 128).
+__device__ __forceinline__ void upper_tile(int u, int n, int r, int& ti, int& tj) {
+  int t = 0;
+  while (u >= n - r * t) {
+    u -= n - r * t;
+    ++t;
+  }
+  ti = t;
+  tj = r * t + u;
 }
 
-// Body of the Gram kernel for one tile kind: UP = the tile reaches the upper triangle (G, and E
-// when EV, are formed there).  NM matrices are staged (3 without G, 4 with G, 6 with G and E).
-template <bool EV, int TI, int NWV, int NSTG, bool UP>
-__device__ __forceinline__ void gram_tile(const GramParams& p, uint16_t* s0, uint16_t* s1, uint16_t* s2) {
-  constexpr int WGI = NWV / 2;                       // waves along I (a WGI x 2 grid of (TI / WGI) x 64 sub-tiles)
-  constexpr int WBI = TI / WGI / 32;                 // 32-row blocks per wave along I
-  constexpr int NM = !UP ? 3 : (EV ? 6 : 4);         // staged matrices
-  constexpr int NLD = gram_moff<TI>(NM) / 512;       // 1 KB wave loads per stage
-  constexpr int WLW = NLD / NWV;                     // wave loads per wave per stage
+// All 256 threads of a workgroup; NSTG stage buffers (2 or 3) in LDS.
+template <int PASS, bool EV, int TI_, int NSTG>
+__device__ __forceinline__ void gram_pass(const GramParams& p, const int tile, const int split, uint16_t* s0,
+                                          uint16_t* s1, uint16_t* s2) {
+  using S = GramShape<PASS, EV, TI_>;
+  constexpr int TI = S::TI, TJ = S::TJ, NM = S::NM, WBI = S::WBI, WBJ = S::WBJ;
+  constexpr int NWV = 4;
+  constexpr int NLD = S::SS / 512;  // 1 KB wave loads per stage
+  constexpr int WLW = NLD / NWV;    // wave loads per wave per stage
   static_assert(WLW * NWV == NLD, "stage loads must split over the waves");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: buffer choice stays scalar
   const int l32 = lane & 31, hh = lane >> 5;
-  const int tile = blockIdx.x;
-  const int split = blockIdx.y;
-  const int ti = tile / p.tiles_j, tj = tile % p.tiles_j;
-  const int I0 = ti * TI, J0 = tj * GT;
+  int ti, tj;
+  if (PASS == PASS_C) {
+    ti = tile / p.tiles_j;
+    tj = tile % p.tiles_j;
+  } else {
+    upper_tile(tile, p.d / GT, TI / GT, ti, tj);
+  }
+  const int I0 = ti * TI, J0 = tj * TJ;
   const int64_t r_begin = (int64_t)split * p.rows_per_split;
   const int64_t r_end = min(p.n_rows, r_begin + p.rows_per_split);
   const int nst = r_end > r_begin ? (int)((r_end - r_begin + GBK - 1) / GBK) : 0;
-  const int wi = (wave >> 1) * (TI / WGI), wj = (wave & 1) * 64;  // wave sub-tile origin
+  const int wi = (wave >> 1) * (TI / 2), wj = (wave & 1) * (TJ / 2);  // wave sub-tile origin
   const uint32_t row_bytes = (uint32_t)p.d * 2u;
   // Buffers start at this split's first row; rows at or past r_end read as 0 (range-checked
   // buffer loads).  The host keeps (rows per launch + 64) * row_bytes <= 2^31, so the byte offsets
   // of the padding stages (at most 95 rows past the last row) stay far below 2^32.
   const uint32_t span = r_end > r_begin ? (uint32_t)(r_end - r_begin) * row_bytes : 0u;
-  const rsrc_t rA = make_rsrc(p.A + r_begin * p.d, span);
-  const rsrc_t rH = make_rsrc(p.Dh + r_begin * p.d, span);
-  const rsrc_t rL = make_rsrc(p.Dl + r_begin * p.d, span);
+  const rsrc_t rsc[3] = {make_rsrc(p.A + r_begin * p.d, span), make_rsrc(p.Dh + r_begin * p.d, span),
+                         make_rsrc(p.Dl + r_begin * p.d, span)};
 
-  // this wave's stage loads: wave load g = wave + NWV*j covers load (g - first load of its matrix)
-  // of matrix m: 512 / width rows of it
+  // this wave's stage loads: wave load g = wave + NWV*j is load (g - first load of its matrix) of
+  // matrix m: 512 / width rows of it
   uint32_t gofs[WLW];
-  int lmat[WLW], ldst[WLW];
+  int lsrc[WLW], ldst[WLW];
 #pragma unroll
   for (int j = 0; j < WLW; ++j) {
     const int g = wave + NWV * j;
     int mtx = 0;
 #pragma unroll
     for (int m = 1; m < NM; ++m)
-      if (g >= gram_moff<TI>(m) / 512) mtx = m;
-    const int w = gram_width<TI>(mtx), cpr = w / 8, rpw = 64 / cpr;
-    const int li = g - gram_moff<TI>(mtx) / 512;
+      if (g >= S::moff(m) / 512) mtx = m;
+    const int w = S::width(mtx), cpr = w / 8, rpw = 64 / cpr;
+    const int li = g - S::moff(mtx) / 512;
     const int rr = li * rpw + lane / cpr;
     const int chunk = (lane % cpr) ^ gram_swizzle(rr);
-    const int col0 = (mtx == 0 || mtx >= 4) ? I0 : J0;
+    const int col0 = S::side(mtx) == 0 ? I0 : J0;
     gofs[j] = (uint32_t)rr * row_bytes + (uint32_t)(col0 + chunk * 8) * 2u;
-    lmat[j] = mtx;
-    ldst[j] = gram_moff<TI>(mtx) + li * 512;
+    lsrc[j] = S::src(mtx);
+    ldst[j] = S::moff(mtx) + li * 512;
   }
   auto load_stage = [&](int st, uint16_t* buf) {
     const uint32_t sb = (uint32_t)(st * GBK) * row_bytes;
 #pragma unroll
-    for (int j = 0; j < WLW; ++j) {
-      const int m = lmat[j];
-      load_to_lds((m == 0 || m == 3) ? rA : ((m == 1 || m == 4) ? rH : rL), buf + ldst[j], gofs[j] + sb);
-    }
+    for (int j = 0; j < WLW; ++j) load_to_lds(rsc[lsrc[j]], buf + ldst[j], gofs[j] + sb);
   };
 
   // Operand for columns xb .. xb+31 of a staged [32 rows][w cols] matrix and rows 16ks .. 16ks+15:
@@ -142,16 +174,16 @@ __device__ __forceinline__ void gram_tile(const GramParams& p, uint16_t* s0, uin
   const int tcol = 16 * (q16 & 1) + 4 * (i16 & 3);
   // The swizzle depends on row & 3 == trow & 3, a lane constant, so each operand block has one
   // per-lane base offset; the row step is a compile-time offset.
-  int offI[WBI], offJ[2];
+  int offI[WBI], offJ[WBJ];
 #pragma unroll
   for (int x = 0; x < WBI; ++x) {
     const int ci = wi + 32 * x + tcol;
     offI[x] = trow * TI + (((ci >> 3) ^ gram_swizzle(trow)) << 3) + (ci & 7);
   }
 #pragma unroll
-  for (int x = 0; x < 2; ++x) {
+  for (int x = 0; x < WBJ; ++x) {
     const int cj = wj + 32 * x + tcol;
-    offJ[x] = trow * GT + (((cj >> 3) ^ gram_swizzle(trow)) << 3) + (cj & 7);
+    offJ[x] = trow * TJ + (((cj >> 3) ^ gram_swizzle(trow)) << 3) + (cj & 7);
   }
   auto frag = [&](const uint16_t* t, int off, int ks, int w) {
     const uint16_t* q = t + off + 16 * ks * w;
@@ -159,47 +191,68 @@ __device__ __forceinline__ void gram_tile(const GramParams& p, uint16_t* s0, uin
     return __builtin_bit_cast(bf16x8, u32x4{a.x, a.y, b.x, b.y});
   };
 
-  f32x16 accC[WBI][2], accG[WBI][2], accE[WBI][2];
+  // PASS_C: acc0 = C; PASS_GE: acc0 = G, acc1 = E
+  f32x16 acc0[WBI][WBJ], acc1[WBI][WBJ];
 #pragma unroll
   for (int a = 0; a < WBI; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      accC[a][b] = f32x16{0};
-      accG[a][b] = f32x16{0};
-      accE[a][b] = f32x16{0};
+    for (int b = 0; b < WBJ; ++b) {
+      acc0[a][b] = f32x16{0};
+      acc1[a][b] = f32x16{0};
     }
 
   auto compute = [&](const uint16_t* buf) {
 #pragma unroll
     for (int ks = 0; ks < GBK / 16; ++ks) {
-      bf16x8 aI[WBI], hJ[2], lJ[2], aJ[2], hI[WBI], lI[WBI];
+      if constexpr (PASS == PASS_C) {
+        bf16x8 aI[WBI], hJ[WBJ], lJ[WBJ];
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        hJ[b] = frag(buf + gram_moff<TI>(1), offJ[b], ks, GT);
-        lJ[b] = frag(buf + gram_moff<TI>(2), offJ[b], ks, GT);
-        if (UP) aJ[b] = frag(buf + gram_moff<TI>(3), offJ[b], ks, GT);
-      }
-#pragma unroll
-      for (int a = 0; a < WBI; ++a) {
-        aI[a] = frag(buf + gram_moff<TI>(0), offI[a], ks, TI);
-        if (UP && EV) {
-          hI[a] = frag(buf + gram_moff<TI>(4), offI[a], ks, TI);
-          lI[a] = frag(buf + gram_moff<TI>(5), offI[a], ks, TI);
+        for (int b = 0; b < WBJ; ++b) {
+          hJ[b] = frag(buf + S::moff(1), offJ[b], ks, TJ);
+          lJ[b] = frag(buf + S::moff(2), offJ[b], ks, TJ);
         }
-      }
 #pragma unroll
-      for (int a = 0; a < WBI; ++a)
+        for (int a = 0; a < WBI; ++a) aI[a] = frag(buf + S::moff(0), offI[a], ks, TI);
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          accC[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aI[a], hJ[b], accC[a][b], 0, 0, 0);
-          accC[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aI[a], lJ[b], accC[a][b], 0, 0, 0);
-          if (UP) accG[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aI[a], aJ[b], accG[a][b], 0, 0, 0);
-          if (UP && EV) {
-            accE[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hI[a], hJ[b], accE[a][b], 0, 0, 0);
-            accE[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hI[a], lJ[b], accE[a][b], 0, 0, 0);
-            accE[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lI[a], hJ[b], accE[a][b], 0, 0, 0);
+        for (int a = 0; a < WBI; ++a)
+#pragma unroll
+          for (int b = 0; b < WBJ; ++b) {
+            acc0[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aI[a], hJ[b], acc0[a][b], 0, 0, 0);
+            acc0[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aI[a], lJ[b], acc0[a][b], 0, 0, 0);
           }
+      } else {
+        bf16x8 aI[WBI], aJ[WBJ];
+#pragma unroll
+        for (int b = 0; b < WBJ; ++b) aJ[b] = frag(buf + S::moff(1), offJ[b], ks, TJ);
+#pragma unroll
+        for (int a = 0; a < WBI; ++a) aI[a] = frag(buf + S::moff(0), offI[a], ks, TI);
+#pragma unroll
+        for (int a = 0; a < WBI; ++a)
+#pragma unroll
+          for (int b = 0; b < WBJ; ++b)
+            acc0[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aI[a], aJ[b], acc0[a][b], 0, 0, 0);
+        if constexpr (EV) {
+          bf16x8 hI[WBI], lI[WBI], hJ[WBJ], lJ[WBJ];
+#pragma unroll
+          for (int b = 0; b < WBJ; ++b) {
+            hJ[b] = frag(buf + S::moff(4), offJ[b], ks, TJ);
+            lJ[b] = frag(buf + S::moff(5), offJ[b], ks, TJ);
+          }
+#pragma unroll
+          for (int a = 0; a < WBI; ++a) {
+            hI[a] = frag(buf + S::moff(2), offI[a], ks, TI);
+            lI[a] = frag(buf + S::moff(3), offI[a], ks, TI);
+          }
+#pragma unroll
+          for (int a = 0; a < WBI; ++a)
+#pragma unroll
+            for (int b = 0; b < WBJ; ++b) {
+              acc1[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hI[a], hJ[b], acc1[a][b], 0, 0, 0);
+              acc1[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hI[a], lJ[b], acc1[a][b], 0, 0, 0);
+              acc1[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lI[a], hJ[b], acc1[a][b], 0, 0, 0);
+            }
         }
+      }
     }
   };
 
@@ -254,26 +307,25 @@ __device__ __forceinline__ void gram_tile(const GramParams& p, uint16_t* s0, uin
   // ---- epilogue, straight from the accumulators: element v of lane (col, hh) is row
   // 8(v/4) + 4hh + v%4 of its 32 x 32 block, so for each v the 32 lanes of a half-wave cover 32
   // consecutive columns of one row (128-byte stores).  With split rows every split stores its
-  // partial tile (C everywhere; G and E over the whole tile when it reaches the upper triangle);
-  // otherwise C is stored everywhere and G, E at and above the diagonal.  gram_finish_kernel then
-  // adds the partials in split order and mirrors G and E into the lower triangle.  Offsets within
-  // a d x d matrix fit in 32 bits (d <= 2^15).
+  // partial tile; otherwise C is stored everywhere and G, E at and above the diagonal.
+  // gram_finish_kernel then adds the partials in split order and mirrors G and E into the lower
+  // triangle.  Offsets within a d x d matrix fit in 32 bits (d <= 2^15).
   const uint32_t d = (uint32_t)p.d;
-  constexpr int NMAT = EV ? 3 : 2;  // C, G, E
+  constexpr int NOUT = PASS == PASS_C ? 1 : (EV ? 2 : 1);
 #pragma unroll
-  for (int m = 0; m < NMAT; ++m) {
-    if (m > 0 && !UP) continue;
+  for (int o = 0; o < NOUT; ++o) {
+    const int m = PASS == PASS_C ? 0 : 1 + o;  // matrix: 0 C, 1 G, 2 E
     float* X;
     if (p.part != nullptr)
-      X = p.part + ((size_t)split * NMAT + m) * (size_t)d * d;
+      X = p.part + ((size_t)split * 3 + m) * (size_t)d * d;
     else
       X = m == 0 ? p.C : (m == 1 ? p.G : p.E);
     const bool upper_only = p.part == nullptr && m > 0;
 #pragma unroll
     for (int a = 0; a < WBI; ++a)
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const f32x16& acc = m == 0 ? accC[a][b] : (m == 1 ? accG[a][b] : accE[a][b]);
+      for (int b = 0; b < WBJ; ++b) {
+        const f32x16& acc = o == 0 ? acc0[a][b] : acc1[a][b];
         const uint32_t c = (uint32_t)(J0 + wj + 32 * b + l32);
         const uint32_t r0 = (uint32_t)(I0 + wi + 32 * a + 4 * hh);
 #pragma unroll
@@ -290,23 +342,25 @@ __device__ __forceinline__ void gram_tile(const GramParams& p, uint16_t* s0, uin
   }
 }
 
-// Completes a Gram call, per 64 x 64 block (bi, bj) of the output: with split rows, C = the splits'
-// partials added in split order (plus the old C when accumulating), and for bi <= bj the same for
-// the elements of G and E at and above the diagonal; then G and E are mirrored: element (r, c) with
-// r < c is copied to (c, r) through an LDS transpose, so both triangles hold the same bits.
-__global__ __launch_bounds__(256) void gram_finish_kernel(const float* __restrict__ part, int splits, int nmat,
-                                                          float* C, float* G, float* E, int d, int accumulate) {
+// Completes a Gram call, per 64 x 64 block (bi, bj) of the output: with split rows, C = the C pass's
+// splits_c partials added in split order (plus the old C when accumulating), and for bi <= bj the
+// same for the elements of G and E at and above the diagonal (splits_ge partials); then G and E are
+// mirrored: element (r, c) with r < c is copied to (c, r) through an LDS transpose, so both
+// triangles hold the same bits.
+__global__ __launch_bounds__(256) void gram_finish_kernel(const float* __restrict__ part, int splits_c, int splits_ge,
+                                                          int nmat, float* C, float* G, float* E, int d,
+                                                          int accumulate) {
   __shared__ float T[64][65];
   const int bi = blockIdx.y, bj = blockIdx.x;
   const int tid = threadIdx.x;
   const size_t dd = (size_t)d * d;
   const int r_in = tid >> 4, c4 = (tid & 15) * 4;  // thread: rows r_in + 16 k, columns c4 .. c4 + 3
-  if (splits > 1) {
+  if (splits_c > 1) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const size_t o = (size_t)(bi * 64 + r_in + 16 * k) * d + bj * 64 + c4;
       f32x4 v = {0.f, 0.f, 0.f, 0.f};
-      for (int s = 0; s < splits; ++s) v += *(const f32x4*)(part + (size_t)s * nmat * dd + o);
+      for (int s = 0; s < splits_c; ++s) v += *(const f32x4*)(part + (size_t)s * 3 * dd + o);
       if (accumulate) v += *(const f32x4*)(C + o);
       *(f32x4*)(C + o) = v;
     }
@@ -320,9 +374,9 @@ __global__ __launch_bounds__(256) void gram_finish_kernel(const float* __restric
       const int r = bi * 64 + r_in + 16 * k, c = bj * 64 + c4;
       const size_t o = (size_t)r * d + c;
       f32x4 v;
-      if (splits > 1) {
+      if (splits_ge > 1) {
         v = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int s = 0; s < splits; ++s) v += *(const f32x4*)(part + ((size_t)s * nmat + m) * dd + o);
+        for (int s = 0; s < splits_ge; ++s) v += *(const f32x4*)(part + ((size_t)s * 3 + m) * dd + o);
         if (accumulate) v += *(const f32x4*)(X + o);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -353,21 +407,31 @@ __global__ __launch_bounds__(256) void gram_finish_kernel(const float* __restric
   }
 }
 
-// NWV waves (4: one per SIMD, accumulators in the AGPRs; 8: two per SIMD), NSTG stage buffers.
-template <bool EV, int TI, int NWV, int NSTG>
-__global__ __launch_bounds__(NWV * 64, (NWV == 4 && NSTG == 2 && !EV) ? 2 : 1) void gram_bf16_kernel(GramParams p) {
-  constexpr int NM = EV ? 6 : 4;
-  constexpr int SS = gram_moff<TI>(NM);  // elements per stage (largest tile kind)
+// One Gram pass per launch (grid: tiles x splits): 256 threads (4 waves, 2 x 2), NSTG stage buffers.
+template <int PASS, bool EV, int TI, int NSTG>
+__global__ __launch_bounds__(256, (PASS == PASS_GE && EV) ? 1 : 2) void gram_bf16_kernel(GramParams p) {
+  constexpr int SS = GramShape<PASS, EV, TI>::SS;
   // the stage buffers as distinct arrays (see the attention kernel: lets the compiler overlap the
   // next stages' loads with this stage's reads)
   __shared__ __attribute__((aligned(1024))) uint16_t s0[SS];
   __shared__ __attribute__((aligned(1024))) uint16_t s1[SS];
   __shared__ __attribute__((aligned(1024))) uint16_t s2[NSTG == 3 ? SS : 8];
-  const int ti = blockIdx.x / p.tiles_j, tj = blockIdx.x % p.tiles_j;
-  if (ti * TI < (tj + 1) * GT)  // some element of the tile is on or above the diagonal
-    gram_tile<EV, TI, NWV, NSTG, true>(p, s0, s1, s2);
+  gram_pass<PASS, EV, TI, NSTG>(p, blockIdx.x, blockIdx.y, s0, s1, s2);
+}
+
+// C and G in one launch (without E): workgroups [0, tiles_c * splits) run the C pass, the rest the G
+// pass, so the two fill the GPU together (the G tiles, shorter, come last).
+template <int TIC, int TIG>
+__global__ __launch_bounds__(256, 2) void gram_cg_kernel(GramParams p) {
+  constexpr int SC = GramShape<PASS_C, false, TIC>::SS, SG = GramShape<PASS_GE, false, TIG>::SS;
+  constexpr int SS = SC > SG ? SC : SG;
+  __shared__ __attribute__((aligned(1024))) uint16_t s0[SS];
+  __shared__ __attribute__((aligned(1024))) uint16_t s1[SS];
+  const int bid = blockIdx.x, nc = p.tiles_c * p.splits;
+  if (bid < nc)
+    gram_pass<PASS_C, false, TIC, 2>(p, bid % p.tiles_c, bid / p.tiles_c, s0, s1, nullptr);
   else
-    gram_tile<EV, TI, NWV, NSTG, false>(p, s0, s1, s2);
+    gram_pass<PASS_GE, false, TIG, 2>(p, (bid - nc) % p.tiles_ge, (bid - nc) / p.tiles_ge, s0, s1, nullptr);
 }
 
 // D = A_full - A_loc (exact in float32) as D_hi = bf16(D), D_lo = bf16(D - D_hi); 8 elements per
@@ -463,17 +527,23 @@ int64_t gram_block_rows(int d) {
   return (r / GBK) * GBK;
 }
 
-// I extent of the output tile: 256 where d allows it and its tiles fit one round of the
-// 256 CUs (with split rows); for larger d the 128 tiles pack the rounds better.  With E, six matrices are staged: 128 (three stages of 256-wide
-// tiles would not fit the 160 KB of LDS).
-int gram_ti(int d, bool ev) { return (!ev && d % 256 == 0 && (d / 256) * (d / GT) <= 256) ? 256 : 128; }
+// I extent of the C pass's output tile: 256 where d allows it (a wave then owns 128 x 64), else 128.
+int gram_ti(int d) { return d % 256 == 0 ? 256 : 128; }
 
-int gram_tiles(int d, int ti) { return (d / ti) * (d / GT); }
+int gram_tiles_c(int d) { return (d / gram_ti(d)) * (d / GT); }
+// TI x 128 tiles that reach the upper triangle (G and E pass): sum over I rows of n - r * ti
+int gram_tiles_ge(int d, int ti) {
+  const int n = d / GT, r = ti / GT;
+  int t = 0;
+  for (int i = 0; i < d / ti; ++i) t += n - r * i;
+  return t;
+}
+int gram_ti_ge(int d, bool ev) { return (!ev && d % 256 == 0) ? 256 : 128; }
 
 int gram_splits(int64_t n_rows, int tiles) {
-  // the most splits that still fit one round of 256 CUs (one workgroup per CU for the tiles that
-  // split at all), at least 256 rows per split, at most 8
-  int s = tiles >= 256 ? 1 : 256 / tiles;
+  // the most splits that still fit one round of two workgroups on each of the 256 CUs, at least 256
+  // rows per split, at most 8
+  int s = tiles >= 512 ? 1 : 512 / tiles;
   const int64_t max_s = std::max<int64_t>(1, n_rows / 256);
   if (s > max_s) s = (int)max_s;
   if (s > 8) s = 8;
@@ -485,18 +555,17 @@ struct GramWs {
   size_t dsplit, dbytes, parts, total;  // byte offsets / sizes
 };
 
-// Workspace: D_hi and D_lo of one block of rows and the split partials (C, G, E) of the larger of
-// the two tile shapes (with and without E).
+// Workspace: D_hi and D_lo of one block of rows and the split partials ([split][C, G, E][d][d]) of
+// the pass with the most splits.
 GramWs gram_ws_layout(int64_t n_rows, int d) {
   GramWs w;
   const int64_t rows = std::max<int64_t>(std::min(n_rows, gram_block_rows(d)), 0);
   w.dbytes = ((size_t)rows * d * 2 + 255) & ~(size_t)255;
   w.dsplit = 0;
-  size_t part_bytes = 0;
-  for (int ev = 0; ev < 2; ++ev) {
-    const int s = gram_splits(std::max<int64_t>(rows, 1), gram_tiles(d, gram_ti(d, ev != 0)));
-    if (s > 1) part_bytes = std::max(part_bytes, (size_t)s * 3 * (size_t)d * d * sizeof(float));
-  }
+  const int64_t r1 = std::max<int64_t>(rows, 1);
+  const int s = std::max(gram_splits(r1, gram_tiles_c(d) + gram_tiles_ge(d, gram_ti_ge(d, false))),
+                         gram_splits(r1, gram_tiles_c(d) + gram_tiles_ge(d, gram_ti_ge(d, true))));
+  const size_t part_bytes = s > 1 ? (size_t)s * 3 * (size_t)d * d * sizeof(float) : 0;
   w.parts = 2 * w.dbytes;
   w.total = w.parts + part_bytes;
   return w;
@@ -529,15 +598,17 @@ ispa_status_t launch_gram(int64_t n_rows, int32_t d, int32_t dtype, const void* 
     return ISPA_E_WORKSPACE;
   }
   const GramWs lay = gram_ws_layout(n_rows, d);
-  const int ti = gram_ti(d, E != nullptr);
-  const int tiles = gram_tiles(d, ti);
+  const int ti = gram_ti(d);
+  const int ti_ge = gram_ti_ge(d, E != nullptr);
+  const int tiles_c = gram_tiles_c(d), tiles_ge = gram_tiles_ge(d, ti_ge);
   // Rows go in blocks (the D_hi / D_lo workspace holds one); later blocks accumulate.
   const int64_t block_rows = gram_block_rows(d);
   int64_t r0 = 0;
   do {
     const int64_t nr = std::min(block_rows, n_rows - r0);
     const int acc = (r0 > 0) ? 1 : accumulate;
-    const int splits = gram_splits(std::max<int64_t>(nr, 1), tiles);
+    const int64_t nr1 = std::max<int64_t>(nr, 1);
+    const int splits = gram_splits(nr1, tiles_c + tiles_ge);
     GramParams p;
     p.A = (const uint16_t*)A_loc + r0 * d;
     p.Dh = (const uint16_t*)((char*)ws + lay.dsplit);
@@ -545,12 +616,14 @@ ispa_status_t launch_gram(int64_t n_rows, int32_t d, int32_t dtype, const void* 
     p.G = G;
     p.C = C;
     p.E = E;
-    p.part = splits > 1 ? (float*)((char*)ws + lay.parts) : nullptr;
     p.n_rows = nr;
     p.d = d;
     p.tiles_j = d / GT;
+    p.tiles_c = tiles_c;
+    p.tiles_ge = tiles_ge;
     p.accumulate = acc;
     p.splits = splits;
+    p.part = splits > 1 ? (float*)((char*)ws + lay.parts) : nullptr;
     const int64_t per = (nr + splits - 1) / splits;
     p.rows_per_split = std::max<int64_t>(((per + GBK - 1) / GBK) * GBK, GBK);
     const size_t n8 = (size_t)nr * d / 8;
@@ -561,20 +634,26 @@ ispa_status_t launch_gram(int64_t n_rows, int32_t d, int32_t dtype, const void* 
       ispa_status_t st = hip_check(hipGetLastError(), "gram_split_kernel launch");
       if (st != ISPA_OK) return st;
     }
-    const dim3 grid(tiles, splits);
-    // shapes measured at 4680 rows: d = 1536 (72 tiles of 256 x 128, split rows): 8 waves of 64 x 64
-    // (two per SIMD), three stages; d = 5120 (1600 tiles of 128 x 128): 4 waves, two stages, two
-    // workgroups per CU.  With E (six staged matrices): 4 waves, 128 x 128, three stages.
-    if (E)
-      hipLaunchKernelGGL((gram_bf16_kernel<true, 128, 4, 3>), grid, dim3(256), 0, s, p);
-    else if (ti == 256)
-      hipLaunchKernelGGL((gram_bf16_kernel<false, 256, 8, 3>), grid, dim3(512), 0, s, p);
-    else
-      hipLaunchKernelGGL((gram_bf16_kernel<false, 128, 4, 2>), grid, dim3(256), 0, s, p);
+    if (E) {
+      // E needs six staged matrices: its pass runs on its own (one workgroup per CU), after C's
+      if (ti == 256)
+        hipLaunchKernelGGL((gram_bf16_kernel<PASS_C, false, 256, 2>), dim3(tiles_c, splits), dim3(256), 0, s, p);
+      else
+        hipLaunchKernelGGL((gram_bf16_kernel<PASS_C, false, 128, 2>), dim3(tiles_c, splits), dim3(256), 0, s, p);
+      ispa_status_t st = hip_check(hipGetLastError(), "gram_bf16_kernel launch (C)");
+      if (st != ISPA_OK) return st;
+      hipLaunchKernelGGL((gram_bf16_kernel<PASS_GE, true, GT, 2>), dim3(tiles_ge, splits), dim3(256), 0, s, p);
+    } else {
+      const dim3 grid((unsigned)((tiles_c + tiles_ge) * splits));
+      if (ti == 256 && ti_ge == 256)
+        hipLaunchKernelGGL((gram_cg_kernel<256, 256>), grid, dim3(256), 0, s, p);
+      else
+        hipLaunchKernelGGL((gram_cg_kernel<128, 128>), grid, dim3(256), 0, s, p);
+    }
     ispa_status_t st = hip_check(hipGetLastError(), "gram_bf16_kernel launch");
     if (st != ISPA_OK) return st;
-    hipLaunchKernelGGL(gram_finish_kernel, dim3(d / 64, d / 64), dim3(256), 0, s, (const float*)p.part, splits,
-                       E ? 3 : 2, C, G, E, d, acc);
+    hipLaunchKernelGGL(gram_finish_kernel, dim3(d / 64, d / 64), dim3(256), 0, s,
+                       (const float*)((char*)ws + lay.parts), splits, splits, E ? 3 : 2, C, G, E, d, acc);
     st = hip_check(hipGetLastError(), "gram_finish_kernel launch");
     if (st != ISPA_OK) return st;
     r0 += nr;
