@@ -22,9 +22,13 @@ namespace ispa {
 namespace {
 
 constexpr int PT = 128;        // output tile (PT x PT), 4 waves of 64 x 64
-constexpr int PKS = 32;        // K slab
-constexpr int PLS = PKS + 8;   // LDS row stride (bf16): 80-byte rows, conflict-free 16-byte reads
 constexpr int SPB = 64;        // split / transpose block
+#ifndef APPLY3_RK
+#define APPLY3_RK 32    // K columns per stage of the bf16x3 products
+#endif
+#ifndef APPLY3_NSTG
+#define APPLY3_NSTG 3   // stages in the LDS ring
+#endif
 
 __device__ __forceinline__ void split2(float x, __bf16& h, __bf16& l) {
   h = (__bf16)x;
@@ -123,58 +127,89 @@ struct Apply3Params {
 };
 
 // D = A B^T with A triangular (LOWER: k < m0 + PT; else k >= m0), as hi*hi + hi*lo + lo*hi.
-// The next slab's operands are loaded into registers while the current one is multiplied from LDS
-// (two LDS buffers, one barrier per slab).  M, N multiples of PT, K of PKS.
-template <bool LOWER, bool OUT_T>
+// K advances in stages of RK columns held in a ring of NSTG LDS buffers, filled straight from global
+// memory by buffer loads into LDS (a wave moves 1 KB per load: 32 rows x 16 columns, or 16 rows x 32
+// columns); while stage st is multiplied, stages st + 1 .. st + NSTG - 1 are in flight.  A row's
+// 16-byte chunks are permuted by row (apply3_slot) so that the 16 rows of a fragment read pass cover
+// all 64 banks.  Measured at d = 5120 (refined solve): 32 columns x 3 stages 12.81 ms, x 2 stages
+// 13.06, 16 x 4 13.55, 16 x 3 13.83, and 12.96 for register-staged 32-column slabs in two LDS
+// buffers.  M, N multiples of PT, K of RK.
+template <int RK>
+__device__ __forceinline__ int apply3_slot(int row, int chunk) {
+  if constexpr (RK == 16) return chunk ^ ((row >> 3) & 1);
+  else return chunk ^ ((row >> 2) & 3);
+}
+
+template <bool LOWER, bool OUT_T, int RK, int NSTG>
 __global__ __launch_bounds__(256, 2) void apply3_kernel(Apply3Params p) {
   const int b = blockIdx.z;
   if (p.info[b] != 0) return;
   const int m0 = blockIdx.y * PT, n0 = blockIdx.x * PT;
-  __shared__ __attribute__((aligned(16))) __bf16 S[2][4][PT][PLS];  // [buffer][Ah, Al, Bh, Bl][row][k]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int CPR = RK / 8;              // 16-byte chunks per staged row
+  constexpr int RPL = 64 / CPR;            // rows per wave load
+  constexpr int OPS = PT * RK;             // elements of one operand per stage
+  constexpr int SS = 4 * OPS;              // elements per stage: Ah, Al, Bh, Bl
+  constexpr int NLD = SS / 512;            // wave loads per stage
+  constexpr int WLW = NLD / 4;             // per wave
+  static_assert(NLD % 4 == 0, "stage loads must split over the waves");
+  __shared__ __attribute__((aligned(1024))) __bf16 S0[SS];
+  __shared__ __attribute__((aligned(1024))) __bf16 S1[SS];
+  __shared__ __attribute__((aligned(1024))) __bf16 S2[NSTG >= 3 ? SS : 8];
+  __shared__ __attribute__((aligned(1024))) __bf16 S3[NSTG >= 4 ? SS : 8];
+  __bf16* const buf[4] = {S0, S1, S2, S3};
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
   const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
-  const size_t K = (size_t)p.K;
-  const __bf16* src[4] = {p.Ah + b * p.sA + (size_t)m0 * K, p.Al + b * p.sA + (size_t)m0 * K,
-                          p.Bh + b * p.sB + (size_t)n0 * K, p.Bl + b * p.sB + (size_t)n0 * K};
+  const uint32_t K = (uint32_t)p.K;
+  const uint32_t rows_bytes = (uint32_t)PT * K * 2u;
+  const rsrc_t rs[4] = {make_rsrc(p.Ah + b * p.sA + (size_t)m0 * K, rows_bytes),
+                        make_rsrc(p.Al + b * p.sA + (size_t)m0 * K, rows_bytes),
+                        make_rsrc(p.Bh + b * p.sB + (size_t)n0 * K, rows_bytes),
+                        make_rsrc(p.Bl + b * p.sB + (size_t)n0 * K, rows_bytes)};
   const int kb = LOWER ? 0 : m0;
   const int ke = LOWER ? min(p.K, m0 + PT) : p.K;
-  // thread t moves rows t / 4 and 64 + t / 4, 16-byte chunk t % 4, of each operand
-  const int lr = tid >> 2, lc = 8 * (tid & 3);
-  u32x4 reg[4][2];
-  auto load = [&](int k0) {
+  const int nst = (ke - kb) / RK;
+
+  // this wave's loads: wave load g = wave + 4 j is rows RPL * (g % (PT / RPL)) .. of operand g / (PT / RPL)
+  uint32_t gofs[WLW];
+  int lop[WLW], ldst[WLW];
 #pragma unroll
-    for (int o = 0; o < 4; ++o)
+  for (int j = 0; j < WLW; ++j) {
+    const int g = wave + 4 * j;
+    const int o = g / (PT / RPL), blk = g % (PT / RPL);
+    const int row = blk * RPL + lane / CPR;
+    const int chunk = apply3_slot<RK>(row, lane % CPR);  // the data chunk that lands in slot lane % CPR
+    gofs[j] = (uint32_t)row * K * 2u + (uint32_t)chunk * 16u;
+    lop[j] = o;
+    ldst[j] = o * OPS + blk * 512;
+  }
+  auto load_stage = [&](int st, __bf16* bb) {
+    const uint32_t kofs = (uint32_t)(kb + st * RK) * 2u;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) reg[o][h] = *(const u32x4*)(src[o] + (size_t)(lr + 64 * h) * K + k0 + lc);
+    for (int j = 0; j < WLW; ++j) load_to_lds(rs[lop[j]], (uint16_t*)(bb + ldst[j]), gofs[j] + kofs);
   };
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int o = 0; o < 4; ++o)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) *(u32x4*)(&S[buf][o][lr + 64 * h][lc]) = reg[o][h];
+  // fragment of rows r0 + l32, columns 16 ks + 8 hh .. + 7 of operand o in a stage
+  auto frag = [&](const __bf16* bb, int o, int r0, int ks) {
+    const int row = r0 + l32;
+    return *(const bf16x8*)(bb + o * OPS + row * RK + 8 * apply3_slot<RK>(row, 2 * ks + hh));
   };
+
   f32x16 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{0};
-  load(kb);
-  store(0);
-  __syncthreads();
-  int buf = 0;
-  for (int k0 = kb; k0 < ke; k0 += PKS) {
-    const bool more = k0 + PKS < ke;
-    if (more) load(k0 + PKS);
+  auto compute = [&](const __bf16* bb) {
 #pragma unroll
-    for (int ks = 0; ks < PKS / 16; ++ks) {
+    for (int ks = 0; ks < RK / 16; ++ks) {
       bf16x8 ah[2], al[2], bh[2], bl[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        ah[i] = *(const bf16x8*)(&S[buf][0][wm + 32 * i + l32][16 * ks + 8 * hh]);
-        al[i] = *(const bf16x8*)(&S[buf][1][wm + 32 * i + l32][16 * ks + 8 * hh]);
-        bh[i] = *(const bf16x8*)(&S[buf][2][wn + 32 * i + l32][16 * ks + 8 * hh]);
-        bl[i] = *(const bf16x8*)(&S[buf][3][wn + 32 * i + l32][16 * ks + 8 * hh]);
+        ah[i] = frag(bb, 0, wm + 32 * i, ks);
+        al[i] = frag(bb, 1, wm + 32 * i, ks);
+        bh[i] = frag(bb, 2, wn + 32 * i, ks);
+        bl[i] = frag(bb, 3, wn + 32 * i, ks);
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -185,9 +220,27 @@ __global__ __launch_bounds__(256, 2) void apply3_kernel(Apply3Params p) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bh[j], acc[i][j], 0, 0, 0);
         }
     }
-    if (more) store(buf ^ 1);  // the other buffer: its last readers finished before the previous barrier
-    __syncthreads();
-    buf ^= 1;
+  };
+  // ring: stage st in buffer st % NSTG (buffers chosen at compile time); before the barrier that ends
+  // stage st each wave waits until stage st + 1 has landed, leaving the NSTG - 2 newer stages in flight
+  constexpr int KEEP = (NSTG - 2) * WLW;
+  constexpr int WAIT_KEEP = 0xF70 | (KEEP & 15) | ((KEEP >> 4) << 14);  // vmcnt(KEEP)
+  const int nstR = (nst + NSTG - 1) / NSTG * NSTG;  // padding stages load past ke: zeros or unused columns
+#pragma unroll
+  for (int k = 0; k + 1 < NSTG; ++k)
+    if (k < nst) load_stage(k, buf[k]);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int st = 0; st < nstR; st += NSTG) {
+#pragma unroll
+    for (int k = 0; k < NSTG; ++k) {
+      const int cur = st + k, nxt = cur + NSTG - 1;
+      if (nxt < nst) load_stage(nxt, buf[(k + NSTG - 1) % NSTG]);
+      if (cur < nst) compute(buf[k]);
+      if (nxt < nst) __builtin_amdgcn_s_waitcnt(WAIT_KEEP);
+      else __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
   }
   // acc[i][j][v]: row m0 + wm + 32 i + 8 (v / 4) + 4 hh + v % 4, column n0 + wn + 32 j + l32
   if constexpr (OUT_T) {
@@ -264,7 +317,7 @@ ispa_status_t launch_chol_apply3(int32_t d, int32_t d_out, int32_t batch, const 
   p.M = d; p.N = d_out; p.K = d;
   p.sA = dd; p.sB = dn; p.sD = dn;
   p.info = info;
-  hipLaunchKernelGGL((apply3_kernel<true, true>), dim3(d_out / PT, d / PT, batch), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((apply3_kernel<true, true, APPLY3_RK, APPLY3_NSTG>), dim3(d_out / PT, d / PT, batch), dim3(256), 0, s, p);
   st = hip_check(hipGetLastError(), "apply3_kernel launch");
   if (st != ISPA_OK) return st;
   // X = L^-T Z
@@ -273,7 +326,7 @@ ispa_status_t launch_chol_apply3(int32_t d, int32_t d_out, int32_t batch, const 
   q.M = d; q.N = d_out; q.K = d;
   q.sA = dd; q.sB = dn; q.sD = dn;
   q.info = info;
-  hipLaunchKernelGGL((apply3_kernel<false, false>), dim3(d_out / PT, d / PT, batch), dim3(256), 0, s, q);
+  hipLaunchKernelGGL((apply3_kernel<false, false, APPLY3_RK, APPLY3_NSTG>), dim3(d_out / PT, d / PT, batch), dim3(256), 0, s, q);
   return hip_check(hipGetLastError(), "apply3_kernel launch");
 }
 
