@@ -141,7 +141,7 @@ __device__ __forceinline__ int apply3_slot(int row, int chunk) {
 }
 
 template <bool LOWER, bool OUT_T, int RK, int NSTG>
-__global__ __launch_bounds__(256, 2) void apply3_kernel(Apply3Params p) {
+__global__ __launch_bounds__(256, (NSTG * 4 * PT * RK * 2 <= 80 * 1024) ? 2 : 1) void apply3_kernel(Apply3Params p) {
   const int b = blockIdx.z;
   if (p.info[b] != 0) return;
   const int m0 = blockIdx.y * PT, n0 = blockIdx.x * PT;
