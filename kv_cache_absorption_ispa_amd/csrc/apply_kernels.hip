@@ -13,9 +13,9 @@
 //
 // Layout: both operands K-contiguous (A as M x K, B as N x K, row-major), so every 16-byte LDS read
 // is one lane's MFMA fragment (v_mfma_f32_32x32x16_bf16: lane l holds row l % 32, k = 8 (l / 32)
-// .. + 7).  The first product writes its result transposed and split (the second product's B), the
-// second one float32.  L^-1 is split once per solve, row-major (A of Z = L^-1 Y) and transposed
-// (A of X = L^-T Z).
+// .. + 7).  The first product forms Z^T = Y^T L^-T (A = split(Y^T), B = split(L^-1), lower in k)
+// and writes it split, row-major: the second product's B operand; the second, X = L^-T Z
+// (A = split(L^-T)), writes float32.  L^-1 is split once per solve, row-major and transposed.
 #include "ispa_internal.h"
 
 namespace ispa {
@@ -119,14 +119,15 @@ __global__ __launch_bounds__(256) void split_t_kernel(const float* __restrict__ 
 struct Apply3Params {
   const __bf16 *Ah, *Al;  // M x K (row stride K)
   const __bf16 *Bh, *Bl;  // N x K (row stride K)
-  __bf16 *Dh, *Dl;        // OUT_T: D^T split, N x M (row stride M)
+  __bf16 *Dh, *Dl;        // OUT_SPLIT: D split, M x N (row stride N)
   float* D;               // else: D float32, M x N (row stride N)
   int M, N, K;
   size_t sA, sB, sD;      // batch strides (elements)
   const int32_t* info;
 };
 
-// D = A B^T with A triangular (LOWER: k < m0 + PT; else k >= m0), as hi*hi + hi*lo + lo*hi.
+// D = A B^T with one operand triangular (KM_LA: A lower, k < m0 + PT; KM_UA: A upper, k >= m0;
+// KM_LB: B lower, k < n0 + PT), as hi*hi + hi*lo + lo*hi.
 // K advances in stages of RK columns held in a ring of NSTG LDS buffers, filled straight from global
 // memory by buffer loads into LDS (a wave moves 1 KB per load: 32 rows x 16 columns, or 16 rows x 32
 // columns); while stage st is multiplied, stages st + 1 .. st + NSTG - 1 are in flight.  A row's
@@ -140,11 +141,15 @@ __device__ __forceinline__ int apply3_slot(int row, int chunk) {
   else return chunk ^ ((row >> 2) & 3);
 }
 
-template <bool LOWER, bool OUT_T, int RK, int NSTG>
+constexpr int KM_LA = 0, KM_UA = 1, KM_LB = 2;
+template <int KM, bool OUT_SPLIT, int RK, int NSTG>
 __global__ __launch_bounds__(256, (NSTG * 4 * PT * RK * 2 <= 80 * 1024) ? 2 : 1) void apply3_kernel(Apply3Params p) {
   const int b = blockIdx.z;
   if (p.info[b] != 0) return;
-  const int m0 = blockIdx.y * PT, n0 = blockIdx.x * PT;
+  // tiles with the most K work first (the dispatch order): for a lower operand the last tiles of
+  // its triangle; KM_LB's grid is (M tiles, N tiles) so that its N tile is the slow index
+  const int m0 = (KM == KM_LB ? blockIdx.x : (KM == KM_LA ? gridDim.y - 1 - blockIdx.y : blockIdx.y)) * PT;
+  const int n0 = (KM == KM_LB ? gridDim.y - 1 - blockIdx.y : blockIdx.x) * PT;
   constexpr int CPR = RK / 8;              // 16-byte chunks per staged row
   constexpr int RPL = 64 / CPR;            // rows per wave load
   constexpr int OPS = PT * RK;             // elements of one operand per stage
@@ -167,8 +172,8 @@ __global__ __launch_bounds__(256, (NSTG * 4 * PT * RK * 2 <= 80 * 1024) ? 2 : 1)
                         make_rsrc(p.Al + b * p.sA + (size_t)m0 * K, rows_bytes),
                         make_rsrc(p.Bh + b * p.sB + (size_t)n0 * K, rows_bytes),
                         make_rsrc(p.Bl + b * p.sB + (size_t)n0 * K, rows_bytes)};
-  const int kb = LOWER ? 0 : m0;
-  const int ke = LOWER ? min(p.K, m0 + PT) : p.K;
+  const int kb = KM == KM_UA ? m0 : 0;
+  const int ke = KM == KM_LA ? min(p.K, m0 + PT) : (KM == KM_LB ? min(p.K, n0 + PT) : p.K);
   const int nst = (ke - kb) / RK;
 
   // this wave's loads: wave load g = wave + 4 j is rows RPL * (g % (PT / RPL)) .. of operand g / (PT / RPL)
@@ -243,28 +248,43 @@ __global__ __launch_bounds__(256, (NSTG * 4 * PT * RK * 2 <= 80 * 1024) ? 2 : 1)
     }
   }
   // acc[i][j][v]: row m0 + wm + 32 i + 8 (v / 4) + 4 hh + v % 4, column n0 + wn + 32 j + l32
-  if constexpr (OUT_T) {
-    const size_t M = (size_t)p.M;
+  if constexpr (OUT_SPLIT) {
+    // through LDS (the ring is free after the last barrier): each wave parks half of its 64 x 64
+    // float32 tile at a time (32 rows, 8.5 KB; waves 0-2 in the first buffer, wave 3 in the second),
+    // then every lane splits 8 consecutive elements of a row and stores 16 bytes of hi and of lo, 8
+    // lanes covering a 128-byte row segment
+    constexpr int TS = 64 + 4;  // row stride (floats) of a parked half tile
+    static_assert(3 * 32 * TS * 4 <= SS * 2 && 32 * TS * 4 <= SS * 2, "parked halves fit the buffers");
+    float* T = wave < 3 ? (float*)&S0[0] + wave * 32 * TS : (float*)&S1[0];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 2; ++i) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const size_t col = (size_t)(n0 + wn + 32 * j + l32);
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int row = m0 + wm + 32 * i + 8 * g + 4 * hh;
-          bf16x4 h, l;
+        for (int v = 0; v < 16; ++v) T[(8 * (v >> 2) + 4 * hh + (v & 3)) * TS + 32 * j + l32] = acc[i][j][v];
+      __builtin_amdgcn_wave_barrier();  // the same wave reads its half back (LDS is in order within a wave)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            __bf16 he, le;
-            split2(acc[i][j][4 * g + e], he, le);
-            h[e] = he;
-            l[e] = le;
-          }
-          *(bf16x4*)(p.Dh + b * p.sD + col * M + row) = h;
-          *(bf16x4*)(p.Dl + b * p.sD + col * M + row) = l;
+      for (int q = 0; q < 4; ++q) {
+        const int row = (lane >> 3) + 8 * q, c8 = 8 * (lane & 7);
+        const f32x4 x0 = *(const f32x4*)(T + row * TS + c8);
+        const f32x4 x1 = *(const f32x4*)(T + row * TS + c8 + 4);
+        bf16x8 h, l;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          __bf16 he, le;
+          split2(x0[e], he, le);
+          h[e] = he;
+          l[e] = le;
+          split2(x1[e], he, le);
+          h[4 + e] = he;
+          l[4 + e] = le;
         }
+        const size_t o = b * p.sD + (size_t)(m0 + wm + 32 * i + row) * p.N + n0 + wn + c8;
+        *(bf16x8*)(p.Dh + o) = h;
+        *(bf16x8*)(p.Dl + o) = l;
       }
+      __builtin_amdgcn_wave_barrier();  // all reads of this half are issued before the next overwrites it
+    }
   } else {
     float* D = p.D + b * p.sD;
 #pragma unroll
@@ -311,13 +331,15 @@ ispa_status_t launch_chol_apply3(int32_t d, int32_t d_out, int32_t batch, const 
                      info);
   ispa_status_t st = hip_check(hipGetLastError(), "split_t_kernel launch");
   if (st != ISPA_OK) return st;
-  // Z^T = (L^-1 Y)^T, split
+  // Z^T = Y^T L^-T (A = Y^T, d_out x d; B = L^-1 as rows of k, lower: k <= n), split, row-major:
+  // exactly the second product's B operand
   Apply3Params p{};
-  p.Ah = L; p.Al = L + bdd; p.Bh = YT; p.Bl = YT + bdn; p.Dh = ZT; p.Dl = ZT + bdn;
-  p.M = d; p.N = d_out; p.K = d;
-  p.sA = dd; p.sB = dn; p.sD = dn;
+  p.Ah = YT; p.Al = YT + bdn; p.Bh = L; p.Bl = L + bdd; p.Dh = ZT; p.Dl = ZT + bdn;
+  p.M = d_out; p.N = d; p.K = d;
+  p.sA = dn; p.sB = dd; p.sD = dn;
   p.info = info;
-  hipLaunchKernelGGL((apply3_kernel<true, true, APPLY3_RK, APPLY3_NSTG>), dim3(d_out / PT, d / PT, batch), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((apply3_kernel<KM_LB, true, APPLY3_RK, APPLY3_NSTG>), dim3(d_out / PT, d / PT, batch),
+                     dim3(256), 0, s, p);
   st = hip_check(hipGetLastError(), "apply3_kernel launch");
   if (st != ISPA_OK) return st;
   // X = L^-T Z
@@ -326,7 +348,8 @@ ispa_status_t launch_chol_apply3(int32_t d, int32_t d_out, int32_t batch, const 
   q.M = d; q.N = d_out; q.K = d;
   q.sA = dd; q.sB = dn; q.sD = dn;
   q.info = info;
-  hipLaunchKernelGGL((apply3_kernel<false, false, APPLY3_RK, APPLY3_NSTG>), dim3(d_out / PT, d / PT, batch), dim3(256), 0, s, q);
+  hipLaunchKernelGGL((apply3_kernel<KM_UA, false, APPLY3_RK, APPLY3_NSTG>), dim3(d_out / PT, d / PT, batch),
+                     dim3(256), 0, s, q);
   return hip_check(hipGetLastError(), "apply3_kernel launch");
 }
 

@@ -389,7 +389,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
     for (int t = (int)xcd_remap(blockIdx.x, gridDim.x); t < tiles; t += gridDim.x) run_tile(t / tiles_n, t % tiles_n);
     return;
   }
-  const int tm = blockIdx.y, tn = blockIdx.x;
+  // with op(A) lower the last row tiles carry the most K work: dispatch them first
+  const int tm = p.kmode == 1 ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y, tn = blockIdx.x;
   if (p.lower_only && tm < tn) return;
   run_tile(tm, tn);
   if constexpr (DIAG) {
@@ -469,6 +470,88 @@ __global__ __launch_bounds__(256) void gemm_f64acc_kernel(GemmDParams p) {
         for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], bb[j], acc[i][j], 0, 0, 0);
     }
     __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = m0 + wm + 16 * i + 4 * v + g;
+        const int c = n0 + wn + 16 * j + l16;
+        double x = p.alpha * acc[i][j][v];
+        if (p.Cin) x += p.beta * (double)p.Cin[b * p.sC + (size_t)r * p.ldc + c];
+        if (p.X) x += gb * (double)p.X[b * p.sX + (size_t)r * p.ldx + c];
+        if (p.D64) p.D64[b * p.sD + (size_t)r * p.ldd + c] = x;
+        if (p.D32) p.D32[b * p.sD + (size_t)r * p.ldd + c] = (float)x;
+      }
+}
+
+// The same product with 32-deep K slabs: the next slab's operands are loaded into registers while
+// the current one is multiplied from LDS (two LDS buffers, one barrier per slab).
+constexpr int DKS = 32;
+__global__ __launch_bounds__(256) void gemm_f64acc2_kernel(GemmDParams p) {
+  const int b = blockIdx.z;
+  if (p.info && p.info[b] != 0) return;
+  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  __shared__ float As[2][DKS][64 + 4];  // [buffer][k][m]
+  __shared__ float Bs[2][DKS][64 + 4];  // [buffer][k][n]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
+  const float* A = p.A + b * p.sA;
+  const float* B = p.B + b * p.sB;
+  const double gb = p.gamma_b ? p.gamma * (double)p.gamma_b[b] : p.gamma;
+  f32x4 ra[2], rb[2];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int t = tid + 256 * r;
+      const int m = t >> 3, kq = t & 7;  // A: 64 rows x 8 float4 along k
+      ra[r] = *(const f32x4*)(A + (size_t)(m0 + m) * p.lda + k0 + 4 * kq);
+      const int k = t >> 4, nq = t & 15;  // B: 32 rows (k) x 16 float4 along n
+      rb[r] = *(const f32x4*)(B + (size_t)(k0 + k) * p.ldb + n0 + 4 * nq);
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int t = tid + 256 * r;
+      const int m = t >> 3, kq = t & 7;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) As[buf][4 * kq + e][m] = ra[r][e];
+      const int k = t >> 4, nq = t & 15;
+      *(f32x4*)(&Bs[buf][k][4 * nq]) = rb[r];
+    }
+  };
+  f64x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f64x4{0, 0, 0, 0};
+  load(0);
+  store(0);
+  __syncthreads();
+  int buf = 0;
+  for (int k0 = 0; k0 < p.K; k0 += DKS) {
+    const bool more = k0 + DKS < p.K;
+    if (more) load(k0 + DKS);
+#pragma unroll
+    for (int kk = 0; kk < DKS / 4; ++kk) {
+      double a[2], bb[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        a[i] = (double)As[buf][4 * kk + g][wm + 16 * i + l16];
+        bb[i] = (double)Bs[buf][4 * kk + g][wn + 16 * i + l16];
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], bb[j], acc[i][j], 0, 0, 0);
+    }
+    if (more) store(buf ^ 1);  // the other buffer: its last readers finished before the previous barrier
+    __syncthreads();
+    buf ^= 1;
   }
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -674,6 +757,13 @@ ispa_status_t gemm_d(hipStream_t s, int batch, int M, int N, int K, const float*
   p.alpha = alpha; p.beta = beta; p.gamma = gamma;
   p.gamma_b = gamma_b;
   p.info = info;
+#ifndef ISPA_F64_V2
+#define ISPA_F64_V2 1
+#endif
+  if (ISPA_F64_V2 && K % DKS == 0) {
+    hipLaunchKernelGGL(gemm_f64acc2_kernel, dim3(N / 64, M / 64, batch), dim3(256), 0, s, p);
+    return hip_check(hipGetLastError(), "gemm_f64acc2_kernel launch");
+  }
   hipLaunchKernelGGL(gemm_f64acc_kernel, dim3(N / 64, M / 64, batch), dim3(256), 0, s, p);
   return hip_check(hipGetLastError(), "gemm_f64acc_kernel launch");
 }
