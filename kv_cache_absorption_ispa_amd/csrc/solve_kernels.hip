@@ -494,8 +494,10 @@ __global__ __launch_bounds__(256) void gemm_f64acc2_kernel(GemmDParams p) {
   const int b = blockIdx.z;
   if (p.info && p.info[b] != 0) return;
   const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
-  __shared__ float As[2][DKS][64 + 4];  // [buffer][k][m]
-  __shared__ float Bs[2][DKS][64 + 4];  // [buffer][k][n]
+  // row stride 80 floats: the four k rows a fragment read touches (lanes 16 apart) fall on
+  // different 16-bank groups
+  __shared__ float As[2][DKS][64 + 16];  // [buffer][k][m]
+  __shared__ float Bs[2][DKS][64 + 16];  // [buffer][k][n]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
   const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;

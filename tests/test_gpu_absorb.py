@@ -82,6 +82,14 @@ def test_gram_full_size_and_deterministic():
     eg, ec = relfro(host64(G1), Gr), relfro(host64(C1), Cr)
     say("relfro G, C", eg, ec)
     assert eg <= TOL_G and ec <= TOL_C
+    # element by element: float32 accumulation over 18720 rows stays within 1e-4 of the absolute
+    # sums (and D within 2^-17), so one dropped or misread row of A_loc or A_full (whose products
+    # are a whole 1/18720 of those sums) fails somewhere
+    a_abs, d_abs = np.abs(al.f64), np.abs(af.f64 - al.f64)
+    for got, ref, absum in ((host64(G1), Gr, a_abs.T @ a_abs), (host64(C1), Cr, a_abs.T @ d_abs)):
+        excess = np.abs(got - ref) - 1e-4 * absum
+        say("worst |error| / bound", float(np.max(np.abs(got - ref) / (1e-4 * absum + 1e-30))))
+        assert np.all(excess <= 0), np.unravel_index(np.argmax(excess), excess.shape)
 
 
 def test_gram_rows_past_one_launch():
