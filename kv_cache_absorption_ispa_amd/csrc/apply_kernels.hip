@@ -300,6 +300,241 @@ __global__ __launch_bounds__(256, (NSTG * 4 * PT * RK * 2 <= 80 * 1024) ? 2 : 1)
   }
 }
 
+// R = C W of the absorb on the bf16 matrix cores, at float32 accuracy.  Each float32 operand is
+// carried as three bf16 parts, x = h + m + l exactly (h = bf16(x); the remainder x - h is exact in
+// float32 and has at most 16 significant bits, so m = bf16(x - h) leaves at most 8, which l holds
+// exactly; only values within 2^16 of float32's smallest normal lose low bits).  A product keeps the
+// six terms of order <= 2 (hh, hm, mh, hl, mm, lh); the three it drops (ml, lm, ll) are below 2^-23
+// of it.  The float32 accumulators hold one slab of 64 columns of K; each slab is then added into
+// float64 accumulators, so the long sum over K rounds in float64: the result is at least as accurate
+// as a float32 GEMM's (whose K-long float32 sum rounds at every step), at six bf16 passes
+// (2.5 PFLOP/s) instead of one float32 pass (157.3 TFLOP/s).  (The refinement's residual needs far
+// more than float32 accuracy, about 2^-34 relative to |G| |X| at the conditioning the statistics
+// have, which float32 accumulators cannot hold; it stays on the float64 matrix cores.)
+__device__ __forceinline__ void split3(float x, __bf16& h, __bf16& m, __bf16& l) {
+  h = (__bf16)x;
+  const float r = x - (float)h;
+  m = (__bf16)r;
+  l = (__bf16)(r - (float)m);
+}
+
+// P0, P1, P2 = split3(S), elementwise: S is `count` float32 per batch entry (count % 4 == 0).
+__global__ __launch_bounds__(256) void split3_kernel(const float* __restrict__ S, size_t count, __bf16* P0,
+                                                     __bf16* P1, __bf16* P2, const int32_t* __restrict__ info) {
+  const int b = blockIdx.y;
+  if (info[b] != 0) return;
+  const size_t i = 4 * ((size_t)blockIdx.x * 256 + threadIdx.x);
+  if (i >= count) return;
+  const size_t o = b * count + i;
+  const f32x4 v = *(const f32x4*)(S + o);
+  bf16x4 h, m, l;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    __bf16 he, me, le;
+    split3(v[e], he, me, le);
+    h[e] = he;
+    m[e] = me;
+    l[e] = le;
+  }
+  *(bf16x4*)(P0 + o) = h;
+  *(bf16x4*)(P1 + o) = m;
+  *(bf16x4*)(P2 + o) = l;
+}
+
+// P0, P1, P2 = split3(Y^T): Y is K x N float32 row-major, the planes N x K.
+__global__ __launch_bounds__(256) void split3_t_kernel(const float* __restrict__ Y, int K, int N, __bf16* P0,
+                                                       __bf16* P1, __bf16* P2, const int32_t* __restrict__ info) {
+  const int bk = blockIdx.y, bn = blockIdx.x, b = blockIdx.z;
+  if (info[b] != 0) return;
+  __shared__ float T[SPB][SPB + 1];
+  const size_t kn = (size_t)K * N;
+  const float* src = Y + b * kn + (size_t)bk * SPB * N + bn * SPB;
+  const int tid = threadIdx.x, r0 = tid / 16, c = 4 * (tid % 16);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = r0 + 16 * q;
+    const f32x4 v = *(const f32x4*)(src + (size_t)r * N + c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) T[r][c + e] = v[e];
+  }
+  __syncthreads();
+  const size_t ot = b * kn + (size_t)bn * SPB * K + bk * SPB;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = r0 + 16 * q;  // row of Y^T
+    bf16x4 h, m, l;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      __bf16 he, me, le;
+      split3(T[c + e][r], he, me, le);
+      h[e] = he;
+      m[e] = me;
+      l[e] = le;
+    }
+    const size_t o = ot + (size_t)r * K + c;
+    *(bf16x4*)(P0 + o) = h;
+    *(bf16x4*)(P1 + o) = m;
+    *(bf16x4*)(P2 + o) = l;
+  }
+}
+
+struct Prod6Params {
+  const __bf16* A[3];    // M x K planes (row stride K)
+  const __bf16* B[3];    // N x K planes (row stride K)
+  float* D;              // M x N float32: A B^T
+  int M, N, K, batch;
+  size_t sA, sB, sD;     // batch strides (elements)
+  const int32_t* info;
+};
+
+#ifndef PROD6_NSTG
+#define PROD6_NSTG 2   // stages in the LDS ring (48 KB each)
+#endif
+#ifndef PROD6_FLS
+#define PROD6_FLS 2    // 32-column stages per float64 flush
+#endif
+
+// Same ring as apply3_kernel with six operand planes per stage (RK = 32 columns of K); PT x PT
+// output tile, 4 waves of 64 x 64.  M, N multiples of PT, K of RK * FLS.
+// Tiles in row-major order over (batch, M tiles, N tiles); with fewer workgroups than tiles each
+// workgroup takes tiles gridDim.x apart (a bounded launch leaves compute units to other streams).
+template <int NSTG, int FLS>
+__global__ __launch_bounds__(256, 1) void prod6_kernel(Prod6Params p) {
+  constexpr int RK = 32;
+  constexpr int CPR = RK / 8;
+  constexpr int RPL = 64 / CPR;
+  constexpr int OPS = PT * RK;
+  constexpr int SS = 6 * OPS;   // A0 A1 A2 B0 B1 B2
+  constexpr int NLD = SS / 512;
+  constexpr int WLW = NLD / 4;
+  static_assert(NLD % 4 == 0, "stage loads must split over the waves");
+  __shared__ __attribute__((aligned(1024))) __bf16 S0[SS];
+  __shared__ __attribute__((aligned(1024))) __bf16 S1[SS];
+  __shared__ __attribute__((aligned(1024))) __bf16 S2[NSTG >= 3 ? SS : 8];
+  __bf16* const buf[3] = {S0, S1, S2};
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  const uint32_t K = (uint32_t)p.K;
+  const uint32_t rows_bytes = (uint32_t)PT * K * 2u;
+  const int nst = p.K / RK;
+  const int tn = p.N / PT, tmn = (p.M / PT) * tn;
+  const int ntiles = tmn * p.batch;
+
+  uint32_t gofs[WLW];
+  int lop[WLW], ldst[WLW];
+#pragma unroll
+  for (int j = 0; j < WLW; ++j) {
+    const int g = wave + 4 * j;
+    const int o = g / (PT / RPL), blk = g % (PT / RPL);
+    const int row = blk * RPL + lane / CPR;
+    const int chunk = apply3_slot<RK>(row, lane % CPR);
+    gofs[j] = (uint32_t)row * K * 2u + (uint32_t)chunk * 16u;
+    lop[j] = o;
+    ldst[j] = o * OPS + blk * 512;
+  }
+  auto frag = [&](const __bf16* bb, int o, int r0, int ks) {
+    const int row = r0 + l32;
+    return *(const bf16x8*)(bb + o * OPS + row * RK + 8 * apply3_slot<RK>(row, 2 * ks + hh));
+  };
+
+  for (int t = blockIdx.y * gridDim.x + blockIdx.x + (int)blockIdx.z * tmn; t < ntiles;
+       t += gridDim.x * gridDim.y * gridDim.z) {
+    const int b = t / tmn;
+    const int m0 = (t % tmn) / tn * PT, n0 = (t % tn) * PT;
+    if (p.info[b] != 0) continue;
+    rsrc_t rs[6];
+#pragma unroll
+    for (int o = 0; o < 3; ++o) {
+      rs[o] = make_rsrc(p.A[o] + b * p.sA + (size_t)m0 * K, rows_bytes);
+      rs[3 + o] = make_rsrc(p.B[o] + b * p.sB + (size_t)n0 * K, rows_bytes);
+    }
+    auto load_stage = [&](int st, __bf16* bb) {
+      const uint32_t kofs = (uint32_t)(st * RK) * 2u;
+#pragma unroll
+      for (int j = 0; j < WLW; ++j) load_to_lds(rs[lop[j]], (uint16_t*)(bb + ldst[j]), gofs[j] + kofs);
+    };
+    f32x16 acc[2][2];
+    double acc64[2][2][16];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        acc[i][j] = f32x16{0};
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc64[i][j][v] = 0.0;
+      }
+    auto compute = [&](const __bf16* bb) {
+#pragma unroll
+      for (int ks = 0; ks < RK / 16; ++ks) {
+        bf16x8 a[3][2], bq[3][2];
+#pragma unroll
+        for (int o = 0; o < 3; ++o)
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            a[o][i] = frag(bb, o, wm + 32 * i, ks);
+            bq[o][i] = frag(bb, 3 + o, wn + 32 * i, ks);
+          }
+        // smallest terms first; the four tiles' chains interleave
+        constexpr int TA[6] = {2, 0, 1, 1, 0, 0}, TB[6] = {0, 2, 1, 0, 1, 0};
+#pragma unroll
+        for (int q = 0; q < 6; ++q)
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[TA[q]][i], bq[TB[q]][j], acc[i][j], 0, 0, 0);
+      }
+    };
+    auto flush = [&]() {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc64[i][j][v] += (double)acc[i][j][v];
+          acc[i][j] = f32x16{0};
+        }
+    };
+    constexpr int KEEP = (NSTG - 2) * WLW;
+    constexpr int WAIT_KEEP = 0xF70 | (KEEP & 15) | ((KEEP >> 4) << 14);  // vmcnt(KEEP)
+    const int nstR = (nst + NSTG - 1) / NSTG * NSTG;
+    // the previous tile's last barrier ended every read of the ring
+#pragma unroll
+    for (int k = 0; k + 1 < NSTG; ++k)
+      if (k < nst) load_stage(k, buf[k]);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int st = 0; st < nstR; st += NSTG) {
+#pragma unroll
+      for (int k = 0; k < NSTG; ++k) {
+        const int cur = st + k, nxt = cur + NSTG - 1;
+        if (nxt < nst) load_stage(nxt, buf[(k + NSTG - 1) % NSTG]);
+        if (cur < nst) {
+          compute(buf[k]);
+          if ((cur + 1) % FLS == 0) flush();
+        }
+        if (nxt < nst) __builtin_amdgcn_s_waitcnt(WAIT_KEEP);
+        else __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+      }
+    }
+    // acc64[i][j][v]: row m0 + wm + 32 i + 8 (v / 4) + 4 hh + v % 4, column n0 + wn + 32 j + l32
+    float* D = p.D + b * p.sD;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = m0 + wm + 32 * i + 8 * (v >> 2) + 4 * hh + (v & 3);
+          const int c = n0 + wn + 32 * j + l32;
+          D[(size_t)r * p.N + c] = (float)acc64[i][j][v];
+        }
+  }
+}
+
 }  // namespace
 
 bool apply3_supported(int32_t d, int32_t d_out) { return d % PT == 0 && d_out % PT == 0; }
@@ -351,6 +586,41 @@ ispa_status_t launch_chol_apply3(int32_t d, int32_t d_out, int32_t batch, const 
   hipLaunchKernelGGL((apply3_kernel<KM_UA, false, APPLY3_RK, APPLY3_NSTG>), dim3(d_out / PT, d / PT, batch),
                      dim3(256), 0, s, q);
   return hip_check(hipGetLastError(), "apply3_kernel launch");
+}
+
+ispa_status_t launch_prod6(int32_t M, int32_t N, int32_t K, int32_t batch, const float* A, const float* B, float* D,
+                           void* const asplit[3], void* const bsplit[3], const int32_t* info, hipStream_t s,
+                           int max_wg) {
+  if (M % PT != 0 || N % PT != 0 || K % PT != 0) {
+    set_error("internal: bf16x6 product needs M, N and K multiples of 128");
+    return ISPA_E_INVALID_ARG;
+  }
+  const size_t mk = (size_t)M * K, kn = (size_t)K * N, mn = (size_t)M * N;
+  __bf16* Ap[3] = {(__bf16*)asplit[0], (__bf16*)asplit[1], (__bf16*)asplit[2]};
+  __bf16* Bp[3] = {(__bf16*)bsplit[0], (__bf16*)bsplit[1], (__bf16*)bsplit[2]};
+  hipLaunchKernelGGL(split3_kernel, dim3((unsigned)((mk / 4 + 255) / 256), batch), dim3(256), 0, s, A, mk, Ap[0],
+                     Ap[1], Ap[2], info);
+  ispa_status_t st = hip_check(hipGetLastError(), "split3_kernel launch");
+  if (st != ISPA_OK) return st;
+  hipLaunchKernelGGL(split3_t_kernel, dim3(N / SPB, K / SPB, batch), dim3(256), 0, s, B, K, N, Bp[0], Bp[1], Bp[2],
+                     info);
+  st = hip_check(hipGetLastError(), "split3_t_kernel launch");
+  if (st != ISPA_OK) return st;
+  Prod6Params p{};
+  for (int o = 0; o < 3; ++o) {
+    p.A[o] = Ap[o];
+    p.B[o] = Bp[o];
+  }
+  p.D = D;
+  p.M = M; p.N = N; p.K = K; p.batch = batch;
+  p.sA = mk; p.sB = kn; p.sD = mn;
+  p.info = info;
+  const int tiles = (M / PT) * (N / PT) * batch;
+  if (max_wg > 0 && max_wg < tiles)
+    hipLaunchKernelGGL((prod6_kernel<PROD6_NSTG, PROD6_FLS>), dim3(max_wg, 1, 1), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((prod6_kernel<PROD6_NSTG, PROD6_FLS>), dim3(N / PT, M / PT, batch), dim3(256), 0, s, p);
+  return hip_check(hipGetLastError(), "prod6_kernel launch");
 }
 
 }  // namespace ispa

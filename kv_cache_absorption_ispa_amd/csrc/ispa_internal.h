@@ -99,6 +99,12 @@ ispa_status_t launch_split_lower(int32_t d, int32_t batch, const float* Linv, vo
 ispa_status_t launch_chol_apply3(int32_t d, int32_t d_out, int32_t batch, const void* Lsplit, const void* LTsplit,
                                  const float* Y, void* YTsplit, void* ZTsplit, float* X, const int32_t* info,
                                  hipStream_t s);
+// D = A B (A M x K, B K x N, D M x N; float32, row-major, batched) from three-part bf16 splits of A and
+// B^T, float64-accumulated slabs; M, N, K multiples of 128.  asplit / bsplit: three planes of
+// batch * M * K and batch * K * N bf16 each, scratch.  max_wg > 0 bounds the product's workgroups.
+ispa_status_t launch_prod6(int32_t M, int32_t N, int32_t K, int32_t batch, const float* A, const float* B, float* D,
+                           void* const asplit[3], void* const bsplit[3], const int32_t* info, hipStream_t s,
+                           int max_wg = 0);
 size_t fit_error_workspace_size(int32_t d, int32_t d_out, int32_t batch);
 ispa_status_t launch_fit_error(int32_t d, int32_t d_out, int32_t batch, const float* G, const float* C,
                                const float* E, const float* W, const float* dW, double* eps_abs, double* eps_rel,

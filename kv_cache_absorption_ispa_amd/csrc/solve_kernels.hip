@@ -10,8 +10,8 @@
 //
 // Structure (nb = 64 column panels, right-looking):
 //   M = G + lambda I (lambda scalar or per layer)      (init kernel)
-//   R = C W in float32                                 (GEMM; on the caller's side stream, if given, beside
-//                                                       the factorisation)
+//   R = C W at float32 accuracy                        (bf16 matrix cores, three-part splits; on the caller's
+//                                                       side stream, if given, beside the factorisation)
 //   factor M_00 = L_00 L_00^T and invert L_00        (one workgroup per layer)
 //   for each panel k:
 //     L_ik = M_ik L_kk^-T                             (GEMM, in place)
@@ -55,6 +55,12 @@ constexpr int NB = 64;  // panel width
 // per compute unit, so every unit keeps room for the factorisation's launches.
 #ifndef ISPA_CW_WORKGROUPS
 #define ISPA_CW_WORKGROUPS 256
+#endif
+// Workgroups the bf16 R = C W may hold beside the factorisation (one per compute unit at most; half
+// the chip measured best at d = 5120: 64 -> 15.4 ms per refined solve, 96 -> 12.9, 128 -> 11.5,
+// 160 -> 11.8, 192 -> 12.2, 256 -> 12.9; on the caller's stream before the factorisation, 13.2).
+#ifndef ISPA_CW6_WORKGROUPS
+#define ISPA_CW6_WORKGROUPS 128
 #endif
 // Columns per panel of the blocked trailing update (a multiple of NB).
 #ifndef ISPA_CHOL_PANEL
@@ -490,14 +496,18 @@ __global__ __launch_bounds__(256) void gemm_f64acc_kernel(GemmDParams p) {
 // The same product with 32-deep K slabs: the next slab's operands are loaded into registers while
 // the current one is multiplied from LDS (two LDS buffers, one barrier per slab).
 constexpr int DKS = 32;
-__global__ __launch_bounds__(256) void gemm_f64acc2_kernel(GemmDParams p) {
+#ifndef ISPA_F64_WAVES
+#define ISPA_F64_WAVES 5  // waves per SIMD the register budget allows (five workgroups per compute unit)
+#endif
+__global__ __launch_bounds__(256, ISPA_F64_WAVES) void gemm_f64acc2_kernel(GemmDParams p) {
   const int b = blockIdx.z;
   if (p.info && p.info[b] != 0) return;
   const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
-  // row stride 80 floats: the four k rows a fragment read touches (lanes 16 apart) fall on
-  // different 16-bank groups
-  __shared__ float As[2][DKS][64 + 16];  // [buffer][k][m]
-  __shared__ float Bs[2][DKS][64 + 16];  // [buffer][k][n]
+  // rows of 64 floats with column c of row k stored at c ^ 16 (k % 4): the four k rows a fragment
+  // read touches (lanes 16 apart) fall on different 16-bank groups.  32 KB: five workgroups per
+  // compute unit, so 64 x 64 tiles of a 5120 x 5120 output fill the chip in five whole rounds.
+  __shared__ float As[2][DKS][64];  // [buffer][k][m ^ 16 (k % 4)]
+  __shared__ float Bs[2][DKS][64];  // [buffer][k][n ^ 16 (k % 4)]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
   const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
@@ -521,9 +531,9 @@ __global__ __launch_bounds__(256) void gemm_f64acc2_kernel(GemmDParams p) {
       const int t = tid + 256 * r;
       const int m = t >> 3, kq = t & 7;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) As[buf][4 * kq + e][m] = ra[r][e];
+      for (int e = 0; e < 4; ++e) As[buf][4 * kq + e][m ^ (16 * e)] = ra[r][e];
       const int k = t >> 4, nq = t & 15;
-      *(f32x4*)(&Bs[buf][k][4 * nq]) = rb[r];
+      *(f32x4*)(&Bs[buf][k][(4 * nq) ^ (16 * (k & 3))]) = rb[r];
     }
   };
   f64x4 acc[2][2];
@@ -543,8 +553,8 @@ __global__ __launch_bounds__(256) void gemm_f64acc2_kernel(GemmDParams p) {
       double a[2], bb[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        a[i] = (double)As[buf][4 * kk + g][wm + 16 * i + l16];
-        bb[i] = (double)Bs[buf][4 * kk + g][wn + 16 * i + l16];
+        a[i] = (double)As[buf][4 * kk + g][(wm + 16 * i + l16) ^ (16 * g)];
+        bb[i] = (double)Bs[buf][4 * kk + g][(wn + 16 * i + l16) ^ (16 * g)];
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -783,7 +793,8 @@ size_t absorb_workspace_size(int32_t d, int32_t d_out, int32_t batch) {
   return b * d * d * sizeof(float)          // factor L (lower triangle of M)
          + b * d * d * sizeof(float)        // L^-1
          + b * d * d * sizeof(float)        // intermediate products of the inverse
-         + 3 * b * d * d_out * sizeof(float);  // R = C W, the residual / correction, an intermediate
+         + 3 * b * d * d_out * sizeof(float)   // R = C W, the residual / correction, an intermediate
+         + b * (size_t)d * (d + d_out) * 2;      // third bf16 parts of R = C W's split operands
 }
 
 namespace {
@@ -880,25 +891,39 @@ ispa_status_t launch_absorb(int32_t d, int32_t d_out, int32_t batch, const float
   hipLaunchKernelGGL(init_shift_kernel, dim3((unsigned)((dd / 4 + 255) / 256), batch), dim3(256), 0, s, G, M, Linvf,
                      d, lambda, lam_b, info);
   ISPA_TRY(hip_check(hipGetLastError(), "init_shift_kernel launch"));
-  // R = C W (float32; R's rounding perturbs the solution like the float32 statistics themselves do).
+  // R = C W (at float32 accuracy; R's rounding perturbs the solution like the float32 statistics
+  // themselves do).
   // With a caller-owned side stream it runs there, beside the latency-bound factorisation; for small
   // d it is forked after the first panel steps, since sharing the GPU with it would slow the first
   // diagonal factorisations, which sit on the chain (d = 1536: 1.36 -> 1.33 ms per solve); at
   // d = 5120 it goes first.  Without a side stream it runs on `s` before the factorisation.
+  // Where the factorisation's workspace allows (d, d_out multiples of 128), R = C W runs on the bf16
+  // matrix cores as three-part products with float64-accumulated slabs (at least float32 accuracy; its
+  // splits go to the inverse's scratch, R's neighbours and the workspace tail, none of which the
+  // factorisation touches); otherwise as a float32 GEMM.
+  const bool cw6 = apply3_supported(d, d_out);
   SideJoin joiner;
+  // bounded: hold only some workgroups, leaving compute units to the factorisation beside it
+  auto cw = [&](hipStream_t cs, bool bounded) -> ispa_status_t {
+    if (cw6) {
+      __bf16* tail = (__bf16*)(Zb + (size_t)batch * dn);
+      void* const cs3[3] = {Tb, (__bf16*)Tb + (size_t)batch * dd, tail};
+      void* const ws3[3] = {Rr, (__bf16*)Rr + (size_t)batch * dn, tail + (size_t)batch * dd};
+      return launch_prod6(d, d_out, d, batch, C, W, Rb, cs3, ws3, info, cs, bounded ? ISPA_CW6_WORKGROUPS : 0);
+    }
+    return gemm<false, false>(cs, batch, d, d_out, d, C, d, dd, W, d_out, dn, nullptr, 0, 0, Rb, d_out, dn, 1.f, 0.f,
+                              false, nullptr, 0, 1, 0, 0, 0, 0, nullptr, nullptr, nullptr, 0, 0,
+                              bounded ? ISPA_CW_WORKGROUPS / batch : 0);
+  };
   auto fork_cw = [&]() -> ispa_status_t {
-    if (side == nullptr)
-      return gemm<false, false>(s, batch, d, d_out, d, C, d, dd, W, d_out, dn, nullptr, 0, 0, Rb, d_out, dn, 1.f,
-                                0.f, false, nullptr);
+    if (side == nullptr) return cw(s, false);
     ISPA_TRY(hip_check(hipEventRecord(side->ev_fork, s), "hipEventRecord (fork)"));
     ISPA_TRY(hip_check(hipStreamWaitEvent(side->stream, side->ev_fork, 0), "hipStreamWaitEvent (fork)"));
     joiner.s = s;
     joiner.s2 = side->stream;
     joiner.ev = side->ev_join;
     joiner.armed = true;
-    return gemm<false, false>(side->stream, batch, d, d_out, d, C, d, dd, W, d_out, dn, nullptr, 0, 0, Rb, d_out, dn,
-                              1.f, 0.f, false, nullptr, 0, 1, 0, 0, 0, 0, nullptr, nullptr, nullptr, 0, 0,
-                              d > 2048 ? ISPA_CW_WORKGROUPS / batch : 0);
+    return cw(side->stream, d > 2048);
   };
   const int fork_k = (side != nullptr && d <= 2048) ? 4 : -1;  // panel step before which it is forked (-1: first)
   bool forked = false;

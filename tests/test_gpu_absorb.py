@@ -167,6 +167,43 @@ def test_solve_parity_on_oracle_statistics(d, d_out):
     assert e <= TOL_DW
 
 
+@pytest.mark.parametrize("d,d_out,b", [(2560, 640, 2), (3072, 1024, 1)])
+def test_solve_with_a_side_stream_is_the_single_stream_solve(d, d_out, b):
+    """With a caller-owned side stream and d > 2048, R = C W runs beside the factorisation as a bounded
+    launch whose workgroups loop over the tiles (here more tiles than workgroups, and across the batch);
+    each tile is formed exactly as in the one-stream launch, so dW is the same bit for bit, and within
+    the dW gate of the float64 solve."""
+    Gs, Cs, Ws, refs = [], [], [], []
+    for layer in range(b):
+        al, af = inputs.absorb_rows(13, layer, 4 * d, d, "f32")
+        Gr, Cr = oracle.gram(al.f64, af.f64)
+        W = inputs.normal(13, layer, inputs.LAYER_CHUNK, inputs.T_W, (d, d_out)) * np.float32(d ** -0.5)
+        Gs.append(Gr.astype(np.float32))
+        Cs.append(Cr.astype(np.float32))
+        Ws.append(W)
+        refs.append(oracle.ridge_solve(Gs[-1].astype(np.float64), Cs[-1].astype(np.float64), W.astype(np.float64),
+                                       1e-2))
+    G = torch.from_numpy(np.stack(Gs)).cuda()
+    C = torch.from_numpy(np.stack(Cs)).cuda()
+    W = torch.from_numpy(np.stack(Ws)).cuda()
+    ws = nan_workspace(ispa.ispa_absorb_workspace_size(d, d_out, b))
+    info = torch.full((b,), -7, dtype=torch.int32, device="cuda")
+    dW1 = poisoned((b, d, d_out), torch.float32)
+    dW2 = poisoned((b, d, d_out), torch.float32)
+    ispa.ispa_absorb_solve_ex(G, C, W, 1e-2, dW1, info, workspace=ws, side=ispa.SideStream())
+    torch.cuda.synchronize()
+    assert torch.all(info == 0).item()
+    ws2 = nan_workspace(ispa.ispa_absorb_workspace_size(d, d_out, b))
+    ispa.ispa_absorb_solve_ex(G, C, W, 1e-2, dW2, info, workspace=ws2)
+    torch.cuda.synchronize()
+    assert torch.all(info == 0).item()
+    assert torch.equal(dW1, dW2)
+    for i in range(b):
+        e = relfro(host64(dW1[i]), refs[i])
+        say("layer", i, "dW relfro", e)
+        assert e <= TOL_DW
+
+
 @pytest.mark.parametrize("cfg_name", ["tiny-fp32", "wan1.3b-layer", "wan14b-layer"])
 def test_gram_and_solve_boundary(cfg_name):
     """The absorb at the gram+solve boundary on each layer shape's full warmup row count."""
