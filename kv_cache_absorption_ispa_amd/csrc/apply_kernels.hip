@@ -29,6 +29,15 @@ constexpr int SPB = 64;        // split / transpose block
 #ifndef APPLY3_NSTG
 #define APPLY3_NSTG 3   // stages in the LDS ring
 #endif
+#ifndef APPLY3W_RK
+#define APPLY3W_RK 32   // K columns per stage of the 256-tile products
+#endif
+#ifndef APPLY3W_NSTG
+#define APPLY3W_NSTG 2
+#endif
+#ifndef APPLY3W_MIN_TILES
+#define APPLY3W_MIN_TILES 256
+#endif
 
 __device__ __forceinline__ void split2(float x, __bf16& h, __bf16& l) {
   h = (__bf16)x;
@@ -36,13 +45,14 @@ __device__ __forceinline__ void split2(float x, __bf16& h, __bf16& l) {
 }
 
 // Lh, Ll = split(L^-1) and LTh, LTl = split(L^-T) over the 64 x 64 blocks (bi, bj) of L^-1 with
-// bj <= 2 (bi / 2) + 1: those the 128-row tiles of the two products read (lower: k < m0 + 128;
-// upper, transposed: k >= m0).  Everything they read outside the triangle is zero in L^-1.
+// bj <= 4 (bi / 4) + 3: those the 128- and 256-row tiles of the two products read (lower:
+// k < n0 + tile; upper, transposed: k >= m0).  Everything they read outside the triangle is zero in
+// L^-1.
 __global__ __launch_bounds__(256) void split_lower_kernel(const float* __restrict__ Linv, int d, __bf16* Lh,
                                                           __bf16* Ll, __bf16* LTh, __bf16* LTl,
                                                           const int32_t* __restrict__ info) {
   const int bi = blockIdx.y, bj = blockIdx.x, b = blockIdx.z;
-  if (bj > 2 * (bi / 2) + 1 || info[b] != 0) return;
+  if (bj > 4 * (bi / 4) + 3 || info[b] != 0) return;
   __shared__ float T[SPB][SPB + 1];
   const size_t dd = (size_t)d * d;
   const float* src = Linv + b * dd + (size_t)bi * SPB * d + bj * SPB;
@@ -289,6 +299,172 @@ __global__ __launch_bounds__(256, (NSTG * 4 * PT * RK * 2 <= 80 * 1024) ? 2 : 1)
     float* D = p.D + b * p.sD;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = m0 + wm + 32 * i + 8 * (v >> 2) + 4 * hh + (v & 3);
+          const int c = n0 + wn + 32 * j + l32;
+          D[(size_t)r * p.N + c] = acc[i][j][v];
+        }
+  }
+}
+
+// The same products on 256 x 256 tiles with 8 waves (two per SIMD) of 128 x 64 each: every operand
+// byte staged serves twice the multiplies of a 128 x 128 tile, which halves the operand traffic
+// from the caches that bounds the 128-tile products (about 4 GB per product at d = 5120: 7.7 TB/s).
+// A stage holds RK columns of the four operands (64 KB at RK = 32); M, N multiples of 256.  Each
+// output element sums the same products in the same order as on 128 x 128 tiles, so the two give
+// the same bits.  d = 5120: 515 -> 390 us per product (refined solve 11.56 -> 11.07 ms).
+constexpr int PTW = 256;
+template <int KM, bool OUT_SPLIT, int RK, int NSTG>
+__global__ __launch_bounds__(512) void apply3w_kernel(Apply3Params p) {
+  const int b = blockIdx.z;
+  if (p.info[b] != 0) return;
+  const int m0 = (KM == KM_LB ? blockIdx.x : (KM == KM_LA ? gridDim.y - 1 - blockIdx.y : blockIdx.y)) * PTW;
+  const int n0 = (KM == KM_LB ? gridDim.y - 1 - blockIdx.y : blockIdx.x) * PTW;
+  constexpr int CPR = RK / 8;
+  constexpr int RPL = 64 / CPR;
+  constexpr int OPS = PTW * RK;
+  constexpr int SS = 4 * OPS;
+  constexpr int NLD = SS / 512;
+  constexpr int WLW = NLD / 8;
+  static_assert(NLD % 8 == 0, "stage loads must split over the waves");
+  static_assert(NSTG >= 2 && NSTG <= 4, "ring of two to four stages");
+  __shared__ __attribute__((aligned(1024))) __bf16 S0[SS];
+  __shared__ __attribute__((aligned(1024))) __bf16 S1[SS];
+  __shared__ __attribute__((aligned(1024))) __bf16 S2[NSTG >= 3 ? SS : 8];
+  __shared__ __attribute__((aligned(1024))) __bf16 S3[NSTG >= 4 ? SS : 8];
+  __bf16* const buf[4] = {S0, S1, S2, S3};
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int wm = (wave >> 2) * 128, wn = (wave & 3) * 64;
+  const uint32_t K = (uint32_t)p.K;
+  const uint32_t rows_bytes = (uint32_t)PTW * K * 2u;
+  const rsrc_t rs[4] = {make_rsrc(p.Ah + b * p.sA + (size_t)m0 * K, rows_bytes),
+                        make_rsrc(p.Al + b * p.sA + (size_t)m0 * K, rows_bytes),
+                        make_rsrc(p.Bh + b * p.sB + (size_t)n0 * K, rows_bytes),
+                        make_rsrc(p.Bl + b * p.sB + (size_t)n0 * K, rows_bytes)};
+  const int kb = KM == KM_UA ? m0 : 0;
+  const int ke = KM == KM_LA ? min(p.K, m0 + PTW) : (KM == KM_LB ? min(p.K, n0 + PTW) : p.K);
+  const int nst = (ke - kb) / RK;
+
+  uint32_t gofs[WLW];
+  int lop[WLW], ldst[WLW];
+#pragma unroll
+  for (int j = 0; j < WLW; ++j) {
+    const int g = wave + 8 * j;
+    const int o = g / (PTW / RPL), blk = g % (PTW / RPL);
+    const int row = blk * RPL + lane / CPR;
+    const int chunk = apply3_slot<RK>(row, lane % CPR);
+    gofs[j] = (uint32_t)row * K * 2u + (uint32_t)chunk * 16u;
+    lop[j] = o;
+    ldst[j] = o * OPS + blk * 512;
+  }
+  auto load_stage = [&](int st, __bf16* bb) {
+    const uint32_t kofs = (uint32_t)(kb + st * RK) * 2u;
+#pragma unroll
+    for (int j = 0; j < WLW; ++j) load_to_lds(rs[lop[j]], (uint16_t*)(bb + ldst[j]), gofs[j] + kofs);
+  };
+  auto frag = [&](const __bf16* bb, int o, int r0, int ks) {
+    const int row = r0 + l32;
+    return *(const bf16x8*)(bb + o * OPS + row * RK + 8 * apply3_slot<RK>(row, 2 * ks + hh));
+  };
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{0};
+  auto compute = [&](const __bf16* bb) {
+#pragma unroll
+    for (int ks = 0; ks < RK / 16; ++ks) {
+      bf16x8 ah[4], al[4], bh[2], bl[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ah[i] = frag(bb, 0, wm + 32 * i, ks);
+        al[i] = frag(bb, 1, wm + 32 * i, ks);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        bh[j] = frag(bb, 2, wn + 32 * j, ks);
+        bl[j] = frag(bb, 3, wn + 32 * j, ks);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bh[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bl[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bh[j], acc[i][j], 0, 0, 0);
+    }
+  };
+  constexpr int KEEP = (NSTG - 2) * WLW;
+  constexpr int WAIT_KEEP = 0xF70 | (KEEP & 15) | ((KEEP >> 4) << 14);  // vmcnt(KEEP)
+  const int nstR = (nst + NSTG - 1) / NSTG * NSTG;
+#pragma unroll
+  for (int k = 0; k + 1 < NSTG; ++k)
+    if (k < nst) load_stage(k, buf[k]);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int st = 0; st < nstR; st += NSTG) {
+#pragma unroll
+    for (int k = 0; k < NSTG; ++k) {
+      const int cur = st + k, nxt = cur + NSTG - 1;
+      if (nxt < nst) load_stage(nxt, buf[(k + NSTG - 1) % NSTG]);
+      if (cur < nst) compute(buf[k]);
+      if (nxt < nst) __builtin_amdgcn_s_waitcnt(WAIT_KEEP);
+      else __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+  }
+  // acc[i][j][v]: row m0 + wm + 32 i + 8 (v / 4) + 4 hh + v % 4, column n0 + wn + 32 j + l32
+  if constexpr (OUT_SPLIT) {
+    // through LDS (free after the last barrier): each wave parks one 32 x 64 float32 row of tiles at a
+    // time (8.5 KB; waves 0-6 in the first buffer, wave 7 in the second), then every lane splits 8
+    // consecutive elements of a row and stores 16 bytes of hi and of lo
+    constexpr int TS = 64 + 4;
+    static_assert(7 * 32 * TS * 4 <= SS * 2 && 32 * TS * 4 <= SS * 2, "parked rows fit the buffers");
+    float* T = wave < 7 ? (float*)&S0[0] + wave * 32 * TS : (float*)&S1[0];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) T[(8 * (v >> 2) + 4 * hh + (v & 3)) * TS + 32 * j + l32] = acc[i][j][v];
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int row = (lane >> 3) + 8 * q, c8 = 8 * (lane & 7);
+        const f32x4 x0 = *(const f32x4*)(T + row * TS + c8);
+        const f32x4 x1 = *(const f32x4*)(T + row * TS + c8 + 4);
+        bf16x8 h, l;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          __bf16 he, le;
+          split2(x0[e], he, le);
+          h[e] = he;
+          l[e] = le;
+          split2(x1[e], he, le);
+          h[4 + e] = he;
+          l[4 + e] = le;
+        }
+        const size_t o = b * p.sD + (size_t)(m0 + wm + 32 * i + row) * p.N + n0 + wn + c8;
+        *(bf16x8*)(p.Dh + o) = h;
+        *(bf16x8*)(p.Dl + o) = l;
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+  } else {
+    float* D = p.D + b * p.sD;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -568,13 +744,19 @@ ispa_status_t launch_chol_apply3(int32_t d, int32_t d_out, int32_t batch, const 
   if (st != ISPA_OK) return st;
   // Z^T = Y^T L^-T (A = Y^T, d_out x d; B = L^-1 as rows of k, lower: k <= n), split, row-major:
   // exactly the second product's B operand
+  // 256 x 256 tiles where they still give every compute unit a tile
+  const bool wide = d % PTW == 0 && d_out % PTW == 0 && (size_t)(d / PTW) * (d_out / PTW) * batch >= APPLY3W_MIN_TILES;
   Apply3Params p{};
   p.Ah = YT; p.Al = YT + bdn; p.Bh = L; p.Bl = L + bdd; p.Dh = ZT; p.Dl = ZT + bdn;
   p.M = d_out; p.N = d; p.K = d;
   p.sA = dn; p.sB = dd; p.sD = dn;
   p.info = info;
-  hipLaunchKernelGGL((apply3_kernel<KM_LB, true, APPLY3_RK, APPLY3_NSTG>), dim3(d_out / PT, d / PT, batch),
-                     dim3(256), 0, s, p);
+  if (wide)
+    hipLaunchKernelGGL((apply3w_kernel<KM_LB, true, APPLY3W_RK, APPLY3W_NSTG>), dim3(d_out / PTW, d / PTW, batch),
+                       dim3(512), 0, s, p);
+  else
+    hipLaunchKernelGGL((apply3_kernel<KM_LB, true, APPLY3_RK, APPLY3_NSTG>), dim3(d_out / PT, d / PT, batch),
+                       dim3(256), 0, s, p);
   st = hip_check(hipGetLastError(), "apply3_kernel launch");
   if (st != ISPA_OK) return st;
   // X = L^-T Z
@@ -583,8 +765,12 @@ ispa_status_t launch_chol_apply3(int32_t d, int32_t d_out, int32_t batch, const 
   q.M = d; q.N = d_out; q.K = d;
   q.sA = dd; q.sB = dn; q.sD = dn;
   q.info = info;
-  hipLaunchKernelGGL((apply3_kernel<KM_UA, false, APPLY3_RK, APPLY3_NSTG>), dim3(d_out / PT, d / PT, batch),
-                     dim3(256), 0, s, q);
+  if (wide)
+    hipLaunchKernelGGL((apply3w_kernel<KM_UA, false, APPLY3W_RK, APPLY3W_NSTG>), dim3(d_out / PTW, d / PTW, batch),
+                       dim3(512), 0, s, q);
+  else
+    hipLaunchKernelGGL((apply3_kernel<KM_UA, false, APPLY3_RK, APPLY3_NSTG>), dim3(d_out / PT, d / PT, batch),
+                       dim3(256), 0, s, q);
   return hip_check(hipGetLastError(), "apply3_kernel launch");
 }
 

@@ -301,14 +301,15 @@ def test_batched_solve_with_a_failing_layer(d, bad_col):
         assert torch.equal(Wn[i], W[i] + dW[i])
 
 
-@pytest.mark.parametrize("d,batch", [(384, 1), (1536, 4), (2048, 2)])
+@pytest.mark.parametrize("d,batch", [(384, 1), (1536, 4), (2048, 2), (1536, 8)])
 def test_refinement_reaches_the_float64_solve(d, batch):
     """W is a column permutation scaled by powers of two, so R = C W is exact in float32 and the only
     float32 error left is the factorisation's.  At lambda = 0 (cond ~4e4 at d = 384, ~2e5 at d = 1536)
     the float32 solve is off by ~1e-4; the refinement step (float64-accumulated residual) must bring
     dW to the float64 solve of the same float32 statistics.  The batched d = 1536 case multiplies by
     L^-1 on 128 x 128 tiles, which also read the part above its diagonal blocks (it must be zero
-    whatever the workspace held: the workspaces here start as NaN); the single d = 384 one on 64 x 64."""
+    whatever the workspace held: the workspaces here start as NaN); the single d = 384 one on 64 x 64.
+    Eight d = 1536 layers are enough 256 x 256 tiles for the bf16x3 solves to take them."""
     Gs, Cs, Ws, refs = [], [], [], []
     for layer in range(batch):
         al, af = inputs.absorb_rows(12, layer, max(4 * d, 600), d, "f32")
