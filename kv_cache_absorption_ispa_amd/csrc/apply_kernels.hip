@@ -481,12 +481,13 @@ __global__ __launch_bounds__(512) void apply3w_kernel(Apply3Params p) {
 // float32 and has at most 16 significant bits, so m = bf16(x - h) leaves at most 8, which l holds
 // exactly; only values within 2^16 of float32's smallest normal lose low bits).  A product keeps the
 // six terms of order <= 2 (hh, hm, mh, hl, mm, lh); the three it drops (ml, lm, ll) are below 2^-23
-// of it.  The float32 accumulators hold one slab of 256 columns of K; each slab is then added into
-// float64 accumulators, so the long sum over K rounds in float64: the result is at least as accurate
-// as a float32 GEMM's (whose K-long float32 sum rounds at every step), at six bf16 passes
-// (2.5 PFLOP/s) instead of one float32 pass (157.3 TFLOP/s).  (The refinement's residual needs far
-// more than float32 accuracy, about 2^-34 relative to |G| |X| at the conditioning the statistics
-// have, which float32 accumulators cannot hold; it stays on the float64 matrix cores.)
+// of it, so the result is as accurate as a float32 GEMM's, at six bf16 passes (2.5 PFLOP/s) instead
+// of one float32 pass (157.3 TFLOP/s).  On 256 x 256 tiles (prod6w_kernel, two waves per SIMD) the
+// sum over K accumulates in float32 as in a float32 GEMM; the 128 x 128 kernel (prod6_kernel, one
+// wave per SIMD) adds each 256-column slab into float64 registers instead.  (The refinement's
+// residual needs far more than float32 accuracy, about 2^-34 relative to |G| |X| at the conditioning
+// the statistics have, which float32 accumulators cannot hold; it stays on the float64 matrix
+// cores.)
 __device__ __forceinline__ void split3(float x, __bf16& h, __bf16& m, __bf16& l) {
   h = (__bf16)x;
   const float r = x - (float)h;
@@ -712,6 +713,143 @@ __global__ __launch_bounds__(256, 1) void prod6_kernel(Prod6Params p) {
   }
 }
 
+// The same product on 256 x 256 tiles with 8 waves (two per SIMD) of 128 x 64 each, accumulating in
+// float32 over all of K like a float32 GEMM (its K-long sum rounds in float32; the product terms are
+// still exact to 2^-23).  Without the float64 registers two waves fit each SIMD, and a staged byte
+// serves twice the multiplies of a 128 x 128 tile: at d = 5120 on 128 workgroups beside the
+// factorisation 3.74 -> 2.84 ms (the 128-tile kernel's one wave per SIMD left it at 34 % MFMA-busy
+// on its compute units).  A stage holds RK columns of the six planes (48 KB at RK = 16).  Tiles in
+// row-major order; with fewer workgroups than tiles each takes tiles gridDim.x apart.  M, N
+// multiples of 256, K of RK.
+template <int RK, int NSTG>
+__global__ __launch_bounds__(512) void prod6w_kernel(Prod6Params p) {
+  constexpr int CPR = RK / 8;
+  constexpr int RPL = 64 / CPR;
+  constexpr int OPS = PTW * RK;
+  constexpr int SS = 6 * OPS;   // A0 A1 A2 B0 B1 B2
+  constexpr int NLD = SS / 512;
+  constexpr int WLW = NLD / 8;
+  static_assert(NLD % 8 == 0, "stage loads must split over the waves");
+  static_assert(NSTG >= 2 && NSTG <= 3, "ring of two or three stages");
+  __shared__ __attribute__((aligned(1024))) __bf16 S0[SS];
+  __shared__ __attribute__((aligned(1024))) __bf16 S1[SS];
+  __shared__ __attribute__((aligned(1024))) __bf16 S2[NSTG >= 3 ? SS : 8];
+  __bf16* const buf[3] = {S0, S1, S2};
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int wm = (wave >> 2) * 128, wn = (wave & 3) * 64;
+  const uint32_t K = (uint32_t)p.K;
+  const uint32_t rows_bytes = (uint32_t)PTW * K * 2u;
+  const int nst = p.K / RK;
+  const int tn = p.N / PTW, tmn = (p.M / PTW) * tn;
+  const int ntiles = tmn * p.batch;
+
+  uint32_t gofs[WLW];
+  int lop[WLW], ldst[WLW];
+#pragma unroll
+  for (int j = 0; j < WLW; ++j) {
+    const int g = wave + 8 * j;
+    const int o = g / (PTW / RPL), blk = g % (PTW / RPL);
+    const int row = blk * RPL + lane / CPR;
+    const int chunk = apply3_slot<RK>(row, lane % CPR);
+    gofs[j] = (uint32_t)row * K * 2u + (uint32_t)chunk * 16u;
+    lop[j] = o;
+    ldst[j] = o * OPS + blk * 512;
+  }
+  auto frag = [&](const __bf16* bb, int o, int r0, int ks) {
+    const int row = r0 + l32;
+    return *(const bf16x8*)(bb + o * OPS + row * RK + 8 * apply3_slot<RK>(row, 2 * ks + hh));
+  };
+
+  for (int t = blockIdx.y * gridDim.x + blockIdx.x + (int)blockIdx.z * tmn; t < ntiles;
+       t += gridDim.x * gridDim.y * gridDim.z) {
+    const int b = t / tmn;
+    const int m0 = (t % tmn) / tn * PTW, n0 = (t % tn) * PTW;
+    if (p.info[b] != 0) continue;
+    rsrc_t rs[6];
+#pragma unroll
+    for (int o = 0; o < 3; ++o) {
+      rs[o] = make_rsrc(p.A[o] + b * p.sA + (size_t)m0 * K, rows_bytes);
+      rs[3 + o] = make_rsrc(p.B[o] + b * p.sB + (size_t)n0 * K, rows_bytes);
+    }
+    auto load_stage = [&](int st, __bf16* bb) {
+      const uint32_t kofs = (uint32_t)(st * RK) * 2u;
+#pragma unroll
+      for (int j = 0; j < WLW; ++j) load_to_lds(rs[lop[j]], (uint16_t*)(bb + ldst[j]), gofs[j] + kofs);
+    };
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{0};
+    auto compute = [&](const __bf16* bb) {
+#pragma unroll
+      for (int ks = 0; ks < RK / 16; ++ks) {
+        bf16x8 a[3][4], bq[3][2];
+#pragma unroll
+        for (int o = 0; o < 3; ++o) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) a[o][i] = frag(bb, o, wm + 32 * i, ks);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) bq[o][j] = frag(bb, 3 + o, wn + 32 * j, ks);
+        }
+        // smallest terms first; the eight tiles' chains interleave
+        constexpr int TA[6] = {2, 0, 1, 1, 0, 0}, TB[6] = {0, 2, 1, 0, 1, 0};
+#pragma unroll
+        for (int q = 0; q < 6; ++q)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[TA[q]][i], bq[TB[q]][j], acc[i][j], 0, 0, 0);
+      }
+    };
+    constexpr int KEEP = (NSTG - 2) * WLW;
+    constexpr int WAIT_KEEP = 0xF70 | (KEEP & 15) | ((KEEP >> 4) << 14);  // vmcnt(KEEP)
+    const int nstR = (nst + NSTG - 1) / NSTG * NSTG;
+    // the previous tile's last barrier ended every read of the ring
+#pragma unroll
+    for (int k = 0; k + 1 < NSTG; ++k)
+      if (k < nst) load_stage(k, buf[k]);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int st = 0; st < nstR; st += NSTG) {
+#pragma unroll
+      for (int k = 0; k < NSTG; ++k) {
+        const int cur = st + k, nxt = cur + NSTG - 1;
+        if (nxt < nst) load_stage(nxt, buf[(k + NSTG - 1) % NSTG]);
+        if (cur < nst) compute(buf[k]);
+        if (nxt < nst) __builtin_amdgcn_s_waitcnt(WAIT_KEEP);
+        else __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+      }
+    }
+    // acc[i][j][v]: row m0 + wm + 32 i + 8 (v / 4) + 4 hh + v % 4, column n0 + wn + 32 j + l32
+    float* D = p.D + b * p.sD;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = m0 + wm + 32 * i + 8 * (v >> 2) + 4 * hh + (v & 3);
+          const int c = n0 + wn + 32 * j + l32;
+          D[(size_t)r * p.N + c] = acc[i][j][v];
+        }
+  }
+}
+
+#ifndef PROD6W_RK
+#define PROD6W_RK 16
+#endif
+#ifndef PROD6W_NSTG
+#define PROD6W_NSTG 3
+#endif
+#ifndef PROD6_WIDE
+#define PROD6_WIDE 1
+#endif
+
 }  // namespace
 
 bool apply3_supported(int32_t d, int32_t d_out) { return d % PT == 0 && d_out % PT == 0; }
@@ -802,6 +940,15 @@ ispa_status_t launch_prod6(int32_t M, int32_t N, int32_t K, int32_t batch, const
   p.M = M; p.N = N; p.K = K; p.batch = batch;
   p.sA = mk; p.sB = kn; p.sD = mn;
   p.info = info;
+  // 256 x 256 tiles where there are enough of them to spread over the chip
+  if (PROD6_WIDE && M % PTW == 0 && N % PTW == 0 && (M / PTW) * (N / PTW) * batch >= 128) {
+    const int tiles = (M / PTW) * (N / PTW) * batch;
+    if (max_wg > 0 && max_wg < tiles)
+      hipLaunchKernelGGL((prod6w_kernel<PROD6W_RK, PROD6W_NSTG>), dim3(max_wg, 1, 1), dim3(512), 0, s, p);
+    else
+      hipLaunchKernelGGL((prod6w_kernel<PROD6W_RK, PROD6W_NSTG>), dim3(N / PTW, M / PTW, batch), dim3(512), 0, s, p);
+    return hip_check(hipGetLastError(), "prod6w_kernel launch");
+  }
   const int tiles = (M / PT) * (N / PT) * batch;
   if (max_wg > 0 && max_wg < tiles)
     hipLaunchKernelGGL((prod6_kernel<PROD6_NSTG, PROD6_FLS>), dim3(max_wg, 1, 1), dim3(256), 0, s, p);

@@ -56,11 +56,12 @@ constexpr int NB = 64;  // panel width
 #ifndef ISPA_CW_WORKGROUPS
 #define ISPA_CW_WORKGROUPS 256
 #endif
-// Workgroups the bf16 R = C W may hold beside the factorisation (one per compute unit at most; half
-// the chip measured best at d = 5120: 64 -> 15.4 ms per refined solve, 96 -> 12.9, 128 -> 11.5,
-// 160 -> 11.8, 192 -> 12.2, 256 -> 12.9; on the caller's stream before the factorisation, 13.2).
+// Workgroups the bf16 R = C W may hold beside the factorisation (one per compute unit at most).  On
+// 256 x 256 tiles (8 waves each) at d = 5120, per refined solve on one box: 67 -> 11.13 ms,
+// 80 -> 10.51, 90 -> 10.49, 100 -> 10.57 (its 400 tiles in four whole rounds), 110 -> 10.60;
+// 128 -> 11.2 on another.
 #ifndef ISPA_CW6_WORKGROUPS
-#define ISPA_CW6_WORKGROUPS 128
+#define ISPA_CW6_WORKGROUPS 100
 #endif
 // Columns per panel of the blocked trailing update (a multiple of NB).
 #ifndef ISPA_CHOL_PANEL

@@ -167,12 +167,12 @@ def test_solve_parity_on_oracle_statistics(d, d_out):
     assert e <= TOL_DW
 
 
-@pytest.mark.parametrize("d,d_out,b", [(2560, 640, 2), (3072, 1024, 1)])
+@pytest.mark.parametrize("d,d_out,b", [(2560, 640, 2), (3072, 1024, 1), (2560, 2560, 2)])
 def test_solve_with_a_side_stream_is_the_single_stream_solve(d, d_out, b):
     """With a caller-owned side stream and d > 2048, R = C W runs beside the factorisation as a bounded
-    launch whose workgroups loop over the tiles (here more tiles than workgroups, and across the batch);
-    each tile is formed exactly as in the one-stream launch, so dW is the same bit for bit, and within
-    the dW gate of the float64 solve."""
+    launch whose workgroups loop over the tiles (here more tiles than workgroups, and across the batch;
+    128 x 128 tiles for the first two shapes, 256 x 256 for the last); each tile is formed exactly as in
+    the one-stream launch, so dW is the same bit for bit, and within the dW gate of the float64 solve."""
     Gs, Cs, Ws, refs = [], [], [], []
     for layer in range(b):
         al, af = inputs.absorb_rows(13, layer, 4 * d, d, "f32")
