@@ -308,7 +308,9 @@ size_t ispa_absorb_workspace_size(int32_t d, int32_t d_out, int32_t batch);
  * "Memory-Efficient Inference" (W_new = W + dW).  Computes, per batch entry,
  * M = G + lambda I, M = L L^T (blocked Cholesky, float32), R = C W,
  * L Y = R, L^T dW = Y (through the explicit L^-1), then one refinement
- * step: r = R - (G + lambda I) dW accumulated in float64, dW += M^-1 r.
+ * step: r = R - (G + lambda I) dW formed to ~2^-42 (exact int8 digit-slice
+ * products for d, d_out multiples of 128, else float64 accumulation),
+ * dW += M^-1 r.
  *
  *   G, C [batch, d, d]; W [batch, d, d_out]; dW [batch, d, d_out]; all float32.
  *   W_new [batch, d, d_out] may be NULL or equal to W (in-place absorb).
@@ -519,7 +521,7 @@ ispa_status_t ispa_absorb_solve_lambdas(int32_t d, int32_t d_out, int32_t batch,
                                         const float* W, const float* lambdas, float* dW, float* W_new,
                                         int32_t* info, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Flag of ispa_absorb_solve_ex: skip the float64-residual refinement step. */
+/* Flag of ispa_absorb_solve_ex: skip the refinement step. */
 #define ISPA_ABSORB_NO_REFINE 1
 
 /* A second stream the caller owns, with two events the caller owns, for
@@ -543,8 +545,8 @@ typedef struct {
  * DEVICE array lambdas [batch] when it is non-NULL (else the scalar lambda),
  * flags, and an optional caller-owned side stream (`side`, NULL = everything
  * on `stream`; ispa_absorb_solve and ispa_absorb_solve_lambdas run everything
- * on `stream`).  ISPA_ABSORB_NO_REFINE skips the refinement step (the float64
- * residual and the second pair of triangular products, ~40 % of the solve at
+ * on `stream`).  ISPA_ABSORB_NO_REFINE skips the refinement step (the accurate
+ * residual and the second pair of triangular products, ~25 % of the solve at
  * d = 5120): dW is then the float32 solve, whose error grows like
  * cond(G + lambda I) * 2^-24 instead of reaching the float32 statistics'
  * own accuracy.  Same workspace and errors as ispa_absorb_solve; a `side`

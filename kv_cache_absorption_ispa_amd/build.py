@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libispa.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.hip", "attn_kernels.hip", "gram_kernels.hip", "solve_kernels.hip", "stack_kernels.hip", "fp8_kernels.hip",
-           "apply_kernels.hip"]
+           "apply_kernels.hip", "residual_kernels.hip"]
 
 CFLAGS = [
     "-std=c++17", "-O3", "-fPIC", f"--offload-arch={ARCH}",

@@ -105,6 +105,16 @@ ispa_status_t launch_chol_apply3(int32_t d, int32_t d_out, int32_t batch, const 
 ispa_status_t launch_prod6(int32_t M, int32_t N, int32_t K, int32_t batch, const float* A, const float* B, float* D,
                            void* const asplit[3], void* const bsplit[3], const int32_t* info, hipStream_t s,
                            int max_wg = 0);
+// r = R - G X + gamma X (gamma * gamma_b[b] per layer if gamma_b) from exact int8 digit-slice
+// products of G and X (Ozaki's splitting, 21 int8 products, ~2^-42 relative to the row and column
+// scales); d, d_out multiples of 128.  gplanes / xplanes: six digit planes of batch * d * d and
+// batch * d_out * d bytes; scales: residual_i8_scale_bytes bytes.  All scratch.
+bool residual_i8_supported(int32_t d, int32_t d_out);
+size_t residual_i8_scale_bytes(int32_t d, int32_t d_out, int32_t batch);
+ispa_status_t launch_residual_i8(int32_t d, int32_t d_out, int32_t batch, const float* G, const float* X,
+                                 const float* R, double gamma, const float* gamma_b, float* r,
+                                 void* const gplanes[6], void* const xplanes[6], void* scales, const int32_t* info,
+                                 hipStream_t s);
 size_t fit_error_workspace_size(int32_t d, int32_t d_out, int32_t batch);
 ispa_status_t launch_fit_error(int32_t d, int32_t d_out, int32_t batch, const float* G, const float* C,
                                const float* E, const float* W, const float* dW, double* eps_abs, double* eps_rel,

@@ -19,15 +19,15 @@
 //                                                      block then factors and inverts it)
 //   explicit inverse of L by recursive doubling over block ranges
 //   X = L^-T (L^-1 R)                                  (two triangular GEMMs)
-//   one refinement step: r = R - G X - lambda X in float64,
-//   dW = X + L^-T (L^-1 r).
+//   one refinement step: r = R - G X - lambda X to ~2^-42 (exact int8 digit-slice
+//   products, else float64 accumulation), dW = X + L^-T (L^-1 r).
 // The float32 factorisation alone loses about kappa * 2^-24 (about 1e-3 at the
 // conditioning warmup statistics have, 1e5); the refinement step with a
-// float64 residual brings dW to the accuracy of its float32 inputs.  Forming
-// L^-1 once turns each triangular solve into one GEMM launch instead of one per
-// panel.  The factor, inverse and solve GEMMs run on v_mfma_f32_32x32x2_f32
-// with 64x64 tiles (triangular operands skip their zero blocks); the
-// float64-accumulated products run on v_mfma_f64_16x16x4_f64.  A layer whose pivot
+// residual far more accurate than float32 brings dW to the accuracy of its
+// float32 inputs.  Forming L^-1 once turns each triangular solve into one GEMM
+// launch instead of one per panel.  The factor and inverse GEMMs run on
+// v_mfma_f32_32x32x2_f32 with 64x64 tiles (triangular operands skip their zero
+// blocks); the float64-accumulated products on v_mfma_f64_16x16x4_f64.  A layer whose pivot
 // fails records info = column + 1 and is skipped by later kernels; its dW is
 // set to NaN at the end and its W_new is left alone.
 #include <algorithm>
@@ -60,6 +60,9 @@ constexpr int NB = 64;  // panel width
 // 256 x 256 tiles (8 waves each) at d = 5120, per refined solve on one box: 67 -> 11.13 ms,
 // 80 -> 10.51, 90 -> 10.49, 100 -> 10.57 (its 400 tiles in four whole rounds), 110 -> 10.60;
 // 128 -> 11.2 on another.
+#ifndef ISPA_RESID_I8
+#define ISPA_RESID_I8 1  // the refinement residual from int8 digit slices (else float64 accumulation)
+#endif
 #ifndef ISPA_CW6_WORKGROUPS
 #define ISPA_CW6_WORKGROUPS 100
 #endif
@@ -795,7 +798,8 @@ size_t absorb_workspace_size(int32_t d, int32_t d_out, int32_t batch) {
          + b * d * d * sizeof(float)        // L^-1
          + b * d * d * sizeof(float)        // intermediate products of the inverse
          + 3 * b * d * d_out * sizeof(float)   // R = C W, the residual / correction, an intermediate
-         + b * (size_t)d * (d + d_out) * 2;      // third bf16 parts of R = C W's split operands
+         + b * (size_t)d * (d + d_out) * 2       // third bf16 parts of R = C W's split operands
+         + residual_i8_scale_bytes(d, d_out, batch) + 256;  // the residual's row and column scales
 }
 
 namespace {
@@ -899,9 +903,9 @@ ispa_status_t launch_absorb(int32_t d, int32_t d_out, int32_t batch, const float
   // diagonal factorisations, which sit on the chain (d = 1536: 1.36 -> 1.33 ms per solve); at
   // d = 5120 it goes first.  Without a side stream it runs on `s` before the factorisation.
   // Where the factorisation's workspace allows (d, d_out multiples of 128), R = C W runs on the bf16
-  // matrix cores as three-part products with float64-accumulated slabs (at least float32 accuracy; its
-  // splits go to the inverse's scratch, R's neighbours and the workspace tail, none of which the
-  // factorisation touches); otherwise as a float32 GEMM.
+  // matrix cores as six-term products of three-part splits (float32 accuracy; its splits go to the
+  // inverse's scratch, R's neighbours and the workspace tail, none of which the factorisation
+  // touches); otherwise as a float32 GEMM.
   const bool cw6 = apply3_supported(d, d_out);
   SideJoin joiner;
   // bounded: hold only some workgroups, leaving compute units to the factorisation beside it
@@ -974,7 +978,7 @@ ispa_status_t launch_absorb(int32_t d, int32_t d_out, int32_t batch, const float
   // inv([A 0; B C]) has off-diagonal block -C^-1 (B A^-1); pairs of equal sizes run as one launch.
   ISPA_TRY(invert_lower(s, batch, d, M, Linvf, Tb, info));
   // X = (L L^T)^-1 R.  With the refinement, both solves run on the bf16 matrix cores as three-term
-  // products (about 2^-16 relative per product); the float64-accumulated residual then corrects
+  // products (about 2^-16 relative per product); the accurate residual then corrects
   // the first solve's error and the correction's error is that much smaller again.  L (M) and the
   // doubling scratch (Tb) are free once L^-1 is built and take its splits; Rr (not yet written)
   // takes the split R, Zb the split intermediate.
@@ -990,10 +994,24 @@ ispa_status_t launch_absorb(int32_t d, int32_t d_out, int32_t batch, const float
                        (const float*)nullptr, W_new, dn, (const int32_t*)info);
     return hip_check(hipGetLastError(), "finalize_kernel launch");
   }
-  // refinement: r = R - G X - lambda X accumulated in float64 (the cancellation needs it),
-  // correction = (L L^T)^-1 r
-  ISPA_TRY(gemm_d(s, batch, d, d_out, d, G, d, dd, dW, d_out, dn, Rb, d_out, dn, dW, d_out, dn, nullptr, Rr, d_out,
-                  dn, -1.0, 1.0, lam_b ? -1.0 : -(double)lambda, info, lam_b));
+  // refinement: r = R - G X - lambda X far more accurate than float32 (the cancellation needs it),
+  // correction = (L L^T)^-1 r.  Where supported G X is an exact product of int8 digit slices on the
+  // int8 matrix cores (its planes in the free L^-1, intermediate and tail buffers), else it is
+  // accumulated in float64 on the float64 matrix cores.
+  if (use3 && ISPA_RESID_I8 && residual_i8_supported(d, d_out)) {
+    int8_t* g8 = (int8_t*)Linvf;                    // 4 planes of batch * d * d bytes
+    int8_t* x8 = (int8_t*)Zb;                       // 4 planes of batch * d * d_out bytes
+    int8_t* t8 = (int8_t*)(Zb + (size_t)batch * dn);  // tail: 2 more of each
+    const size_t bdd = (size_t)batch * dd, bdn = (size_t)batch * dn;
+    void* const gp[6] = {g8, g8 + bdd, g8 + 2 * bdd, g8 + 3 * bdd, t8, t8 + bdd};
+    void* const xp[6] = {x8, x8 + bdn, x8 + 2 * bdn, x8 + 3 * bdn, t8 + 2 * bdd, t8 + 2 * bdd + bdn};
+    void* scales = (void*)((((uintptr_t)(t8 + 2 * bdd + 2 * bdn)) + 255) & ~(uintptr_t)255);
+    ISPA_TRY(launch_residual_i8(d, d_out, batch, G, dW, Rb, lam_b ? -1.0 : -(double)lambda, lam_b, Rr, gp, xp,
+                                scales, info, s));
+  } else {
+    ISPA_TRY(gemm_d(s, batch, d, d_out, d, G, d, dd, dW, d_out, dn, Rb, d_out, dn, dW, d_out, dn, nullptr, Rr, d_out,
+                    dn, -1.0, 1.0, lam_b ? -1.0 : -(double)lambda, info, lam_b));
+  }
   if (use3)  // R is no longer needed: its buffer takes the split residual
     ISPA_TRY(launch_chol_apply3(d, d_out, batch, Tb, M, Rr, Rb, Zb, Rr, info, s));
   else
