@@ -308,9 +308,9 @@ size_t ispa_absorb_workspace_size(int32_t d, int32_t d_out, int32_t batch);
  * "Memory-Efficient Inference" (W_new = W + dW).  Computes, per batch entry,
  * M = G + lambda I, M = L L^T (blocked Cholesky, float32), R = C W,
  * L Y = R, L^T dW = Y (through the explicit L^-1), then one refinement
- * step: r = R - (G + lambda I) dW formed to ~2^-42 (exact int8 digit-slice
- * products for d, d_out multiples of 128, else float64 accumulation),
- * dW += M^-1 r.
+ * step: r = R - (G + lambda I) dW formed far beyond float32 accuracy (exact
+ * int8 digit-slice products for d, d_out multiples of 128, else float64
+ * accumulation), dW += M^-1 r.
  *
  *   G, C [batch, d, d]; W [batch, d, d_out]; dW [batch, d, d_out]; all float32.
  *   W_new [batch, d, d_out] may be NULL or equal to W (in-place absorb).

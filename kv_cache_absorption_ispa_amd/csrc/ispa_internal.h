@@ -106,9 +106,10 @@ ispa_status_t launch_prod6(int32_t M, int32_t N, int32_t K, int32_t batch, const
                            void* const asplit[3], void* const bsplit[3], const int32_t* info, hipStream_t s,
                            int max_wg = 0);
 // r = R - G X + gamma X (gamma * gamma_b[b] per layer if gamma_b) from exact int8 digit-slice
-// products of G and X (Ozaki's splitting, 21 int8 products, ~2^-42 relative to the row and column
-// scales); d, d_out multiples of 128.  gplanes / xplanes: six digit planes of batch * d * d and
-// batch * d_out * d bytes; scales: residual_i8_scale_bytes bytes.  All scratch.
+// products of G and X (Ozaki's splitting, five digits, 15 int8 products, ~2^-35 relative to the row
+// and column scales); d, d_out multiples of 128.  gplanes / xplanes: digit planes (the first five
+// used) of batch * d * d and batch * d_out * d bytes; scales: residual_i8_scale_bytes bytes.  All
+// scratch.
 bool residual_i8_supported(int32_t d, int32_t d_out);
 size_t residual_i8_scale_bytes(int32_t d, int32_t d_out, int32_t batch);
 ispa_status_t launch_residual_i8(int32_t d, int32_t d_out, int32_t batch, const float* G, const float* X,

@@ -9,21 +9,26 @@
 // G X is formed as an exact integer product of digit slices (the splitting scheme of Ozaki et al.
 // for accurate matrix products, here on int8 digits with int32 accumulation):
 //  * every row i of G gets a power-of-two scale 2^e_i with |G_ik| < 2^e_i, every column j of X a
-//    scale 2^f_j; the scaled values lie in (-1, 1) and are cut into S = 6 signed 7-bit digits
+//    scale 2^f_j; the scaled values lie in (-1, 1) and are cut into S = 5 signed 7-bit digits
 //    (v -> 128 v, digit = its integer part, v -> the remainder; all exact in float32), so
-//    G_ik = 2^e_i (sum_s a_s,ik 2^(-7(s+1)) + rest) with |rest| < 2^-42;
+//    G_ik = 2^e_i (sum_s a_s,ik 2^(-7(s+1)) + rest) with |rest| < 2^-35;
 //  * G X = 2^(e_i + f_j) sum_{s,t} 2^(-7(s+t+2)) (A_s B_t)_ij; the int8 products A_s B_t are exact
-//    in int32 (|digit| <= 127, at most six products of d terms share one accumulator), and the pairs
-//    with s + t <= 5 are kept (21 products; the dropped ones are below 2^-49 of the scales per term);
-//  * the six diagonal sums s + t = c are combined in float64, scaled, and r = R - G X - lambda X is
+//    in int32 (|digit| <= 127, at most five products of d terms share one accumulator), and the pairs
+//    with s + t <= S - 1 are kept (15 products; each term then within ~2^-35 of the scales' product);
+//  * the S diagonal sums s + t = c are combined in float64, scaled, and r = R - G X - lambda X is
 //    formed in float64 and rounded once to float32.
-// 21 int8 products at 5 POP/s against one float64 product at 78.6 TFLOP/s.
+// 15 int8 products at 5 POP/s against one float64 product at 78.6 TFLOP/s.  Five digits take the
+// refined dW to within 2e-7 to 1e-6 of the float64 solve at cond ~4e4 to 2e5 (six: 4e-8 to 7e-7,
+// 0.42 ms more at d = 5120), far below the float32 statistics' own rounding.
 #include "ispa_internal.h"
 
 namespace ispa {
 namespace {
 
-constexpr int OZ_S = 6;     // 7-bit digits per value
+#ifndef ISPA_OZ_DIGITS
+#define ISPA_OZ_DIGITS 5
+#endif
+constexpr int OZ_S = ISPA_OZ_DIGITS;  // 7-bit digits per value
 constexpr int OZ_T = 128;   // output tile: 8 waves of 64 x 32 (two per SIMD)
 constexpr int OZ_K = 32;    // K per stage: one v_mfma_i32_32x32x32_i8 step
 constexpr int OZ_NSTG = 3;  // stages in the LDS ring (48 KB each)
@@ -38,7 +43,7 @@ __device__ __forceinline__ int scale_exp(float amax) {
   return e;
 }
 
-// the S digits of v in (-1, 1), as bytes: digits 0-3 in lo, 4-5 in hi
+// the S digits of v in (-1, 1), as bytes: digits 0-3 in lo, the rest in hi
 __device__ __forceinline__ void digits(float v, uint32_t& lo, uint32_t& hi) {
   lo = hi = 0;
 #pragma unroll
@@ -185,8 +190,8 @@ struct OzParams {
 __device__ __forceinline__ int oz_slot(int row, int c) { return c ^ ((row >> 3) & 1); }
 
 // r = R - (G X) + gamma X for one 128 x 128 output tile (rows of G: m0.., columns of X: n0..).
-// Per 32-deep K stage the S digit slices of both operands (12 x 128 rows x 32 bytes = 48 KB) go into
-// a ring of LDS buffers by buffer loads into LDS; each of the 8 waves owns 64 x 32 outputs with six
+// Per 32-deep K stage the S digit slices of both operands (2 S x 128 rows x 32 bytes) go into
+// a ring of LDS buffers by buffer loads into LDS; each of the 8 waves owns 64 x 32 outputs with S
 // int32 accumulator sets (one per diagonal s + t), two waves per SIMD.
 __global__ __launch_bounds__(512) void oz_gemm_kernel(OzParams p) {
   const int b = blockIdx.z;
@@ -298,8 +303,8 @@ __global__ __launch_bounds__(512) void oz_gemm_kernel(OzParams p) {
 }  // namespace
 
 bool residual_i8_supported(int32_t d, int32_t d_out) {
-  // int32 accumulators: at most six products of d digit pairs (|digit| <= 127) share one
-  return d % OZ_T == 0 && d_out % OZ_T == 0 && (int64_t)d * 6 * 127 * 127 < ((int64_t)1 << 31);
+  // int32 accumulators: at most S products of d digit pairs (|digit| <= 127) share one
+  return d % OZ_T == 0 && d_out % OZ_T == 0 && (int64_t)d * OZ_S * 127 * 127 < ((int64_t)1 << 31);
 }
 
 size_t residual_i8_scale_bytes(int32_t d, int32_t d_out, int32_t batch) {
@@ -311,7 +316,7 @@ ispa_status_t launch_residual_i8(int32_t d, int32_t d_out, int32_t batch, const 
                                  void* const gplanes[6], void* const xplanes[6], void* scales, const int32_t* info,
                                  hipStream_t s) {
   if (!residual_i8_supported(d, d_out)) {
-    set_error("internal: int8 residual needs d, d_out multiples of 128 and d below 22186");
+    set_error("internal: int8 residual needs d, d_out multiples of 128 and d * 5 * 127^2 below 2^31");
     return ISPA_E_INVALID_ARG;
   }
   Planes GS, XS;

@@ -19,8 +19,8 @@
 //                                                      block then factors and inverts it)
 //   explicit inverse of L by recursive doubling over block ranges
 //   X = L^-T (L^-1 R)                                  (two triangular GEMMs)
-//   one refinement step: r = R - G X - lambda X to ~2^-42 (exact int8 digit-slice
-//   products, else float64 accumulation), dW = X + L^-T (L^-1 r).
+//   one refinement step: r = R - G X - lambda X to ~2^-35 of the scales (exact int8
+//   digit-slice products, else float64 accumulation), dW = X + L^-T (L^-1 r).
 // The float32 factorisation alone loses about kappa * 2^-24 (about 1e-3 at the
 // conditioning warmup statistics have, 1e5); the refinement step with a
 // residual far more accurate than float32 brings dW to the accuracy of its
