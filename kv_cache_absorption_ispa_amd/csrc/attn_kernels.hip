@@ -141,7 +141,7 @@ __device__ __forceinline__ int kv_swizzle(int r) {
 //
 // SK = split mode: the grid is a fixed set of workgroups (one per CU) that
 // share the units' tiles evenly, so no CU idles when the units do not fill the
-// last round; pieces of split units are merged afterwards (sk_fixup_kernel).
+// last wave of workgroups; pieces of split units are merged afterwards (sk_fixup_kernel).
 //
 // KF8 = fp8 keys: Q and K are E4M3 codes and S^T = K Q^T runs on
 // v_mfma_f32_32x32x64_f8f6f4 (twice the bf16 rate, half the K bytes); the
