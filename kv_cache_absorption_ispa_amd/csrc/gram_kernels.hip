@@ -76,7 +76,7 @@ struct GramParams {
 //   PASS_GE: 0 A_loc[:, I]   1 A_loc[:, J]   (EV: 2 D_hi[:, I]   3 D_lo[:, I]   4 D_hi[:, J]   5 D_lo[:, J])
 constexpr int PASS_C = 0, PASS_GE = 1;
 
-template <int PASS, bool EV, int TI_>
+template <int PASS, bool EV, int TI_, int SR = GBK>
 struct GramShape {
   static constexpr int TI = TI_;
   static constexpr int TJ = GT;
@@ -90,7 +90,7 @@ struct GramShape {
     return PASS == PASS_C ? m : (m < 2 ? 0 : ((m == 2 || m == 4) ? 1 : 2));
   }
   __host__ __device__ static constexpr int width(int m) { return side(m) == 0 ? TI : TJ; }
-  __host__ __device__ static constexpr int moff(int m) { return m == 0 ? 0 : moff(m - 1) + GBK * width(m - 1); }
+  __host__ __device__ static constexpr int moff(int m) { return m == 0 ? 0 : moff(m - 1) + SR * width(m - 1); }
   static constexpr int SS = moff(NM);  // elements per stage
 };
 
@@ -106,11 +106,13 @@ __device__ __forceinline__ void upper_tile(int u, int n, int r, int& ti, int& tj
   tj = r * t + u;
 }
 
-// All 256 threads of a workgroup; NSTG stage buffers (2 or 3) in LDS.
-template <int PASS, bool EV, int TI_, int NSTG>
+// All 256 threads of a workgroup; NSTG stage buffers of SR rows each in LDS (SR = 32: two buffers;
+// SR = 16: a ring of four).
+template <int PASS, bool EV, int TI_, int NSTG, int SR = GBK>
 __device__ __forceinline__ void gram_pass(const GramParams& p, const int tile, const int split, uint16_t* s0,
-                                          uint16_t* s1, uint16_t* s2) {
-  using S = GramShape<PASS, EV, TI_>;
+                                          uint16_t* s1, uint16_t* s2, uint16_t* s3 = nullptr) {
+  static_assert((SR == GBK && NSTG == 2) || (SR == 16 && NSTG == 4), "stage shapes");
+  using S = GramShape<PASS, EV, TI_, SR>;
   constexpr int TI = S::TI, TJ = S::TJ, NM = S::NM, WBI = S::WBI, WBJ = S::WBJ;
   constexpr int NWV = 4;
   constexpr int NLD = S::SS / 512;  // 1 KB wave loads per stage
@@ -130,12 +132,12 @@ __device__ __forceinline__ void gram_pass(const GramParams& p, const int tile, c
   const int I0 = ti * TI, J0 = tj * TJ;
   const int64_t r_begin = (int64_t)split * p.rows_per_split;
   const int64_t r_end = min(p.n_rows, r_begin + p.rows_per_split);
-  const int nst = r_end > r_begin ? (int)((r_end - r_begin + GBK - 1) / GBK) : 0;
+  const int nst = r_end > r_begin ? (int)((r_end - r_begin + SR - 1) / SR) : 0;
   const int wi = (wave >> 1) * (TI / 2), wj = (wave & 1) * (TJ / 2);  // wave sub-tile origin
   const uint32_t row_bytes = (uint32_t)p.d * 2u;
   // Buffers start at this split's first row; rows at or past r_end read as 0 (range-checked
   // buffer loads).  The host keeps (rows per launch + 64) * row_bytes <= 2^31, so the byte offsets
-  // of the padding stages (at most 95 rows past the last row) stay far below 2^32.
+  // of the padding stages (at most 111 rows past the last row) stay far below 2^32.
   const uint32_t span = r_end > r_begin ? (uint32_t)(r_end - r_begin) * row_bytes : 0u;
   const rsrc_t rsc[3] = {make_rsrc(p.A + r_begin * p.d, span), make_rsrc(p.Dh + r_begin * p.d, span),
                          make_rsrc(p.Dl + r_begin * p.d, span)};
@@ -161,7 +163,7 @@ __device__ __forceinline__ void gram_pass(const GramParams& p, const int tile, c
     ldst[j] = S::moff(mtx) + li * 512;
   }
   auto load_stage = [&](int st, uint16_t* buf) {
-    const uint32_t sb = (uint32_t)(st * GBK) * row_bytes;
+    const uint32_t sb = (uint32_t)(st * SR) * row_bytes;
 #pragma unroll
     for (int j = 0; j < WLW; ++j) load_to_lds(rsc[lsrc[j]], buf + ldst[j], gofs[j] + sb);
   };
@@ -203,7 +205,7 @@ __device__ __forceinline__ void gram_pass(const GramParams& p, const int tile, c
 
   auto compute = [&](const uint16_t* buf) {
 #pragma unroll
-    for (int ks = 0; ks < GBK / 16; ++ks) {
+    for (int ks = 0; ks < SR / 16; ++ks) {
       if constexpr (PASS == PASS_C) {
         bf16x8 aI[WBI], hJ[WBJ], lJ[WBJ];
 #pragma unroll
@@ -257,35 +259,33 @@ __device__ __forceinline__ void gram_pass(const GramParams& p, const int tile, c
   };
 
   // Stages past r_end read as zeros, so the stage count is rounded up to a multiple of NSTG and the
-  // loop body (one stage per buffer) has no early exit.  With three buffers stage st + 2 is in
-  // flight while stage st is multiplied, and each wait leaves the newest stage's loads outstanding
-  // (vmcnt counts this wave's loads, which complete in order); with two, stage st + 1.
-  constexpr int WAIT_OLDER = 0xF70 | (WLW & 15) | ((WLW >> 4) << 14);  // vmcnt(WLW); expcnt, lgkmcnt free
-  if constexpr (NSTG == 3) {
-    const int nst3 = (nst + 2) / 3 * 3;
-    if (nst3 > 0) {
-      load_stage(0, s0);
-      load_stage(1, s1);
+  // loop body (one stage per buffer) has no early exit.  vmcnt counts this wave's loads, which
+  // complete in order.
+  if constexpr (NSTG == 4) {
+    // Ring of four SR-row buffers: stage st + 3 is loaded while stage st is multiplied, so three
+    // stages are in flight.  Before stage st is read each wave waits for its own loads of it (all
+    // but the two later stages' loads, which complete after it), then the barrier makes every wave's
+    // loads visible and frees the buffer read in the previous stage for the next load.
+    constexpr int NR = 2 * WLW;
+    constexpr int WAIT_RING = 0xF70 | (NR & 15) | ((NR >> 4) << 14);  // vmcnt(2 WLW)
+    uint16_t* const buf[4] = {s0, s1, s2, s3};
+    const int nstr = (nst + 3) / 4 * 4;
+#pragma unroll
+    for (int j = 0; j < 3; ++j) load_stage(j, buf[j]);
+    // The loads run up to three stages past the last one (rows past r_end read as zeros), so every
+    // wait has the same count; the last wait drains them before the workgroup ends.
+    for (int st = 0; st < nstr; st += 4) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        __builtin_amdgcn_s_waitcnt(WAIT_RING);
+        __builtin_amdgcn_s_barrier();
+        load_stage(st + u + 3, buf[(u + 3) & 3]);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(buf[u]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-    __builtin_amdgcn_s_waitcnt(WAIT_OLDER);
-    __syncthreads();
-    for (int st = 0; st < nst3; st += 3) {
-      load_stage(st + 2, s2);
-      compute(s0);
-      __builtin_amdgcn_s_waitcnt(WAIT_OLDER);
-      __syncthreads();
-      const bool more = st + 3 < nst3;
-      if (more) load_stage(st + 3, s0);
-      compute(s1);
-      if (more) __builtin_amdgcn_s_waitcnt(WAIT_OLDER);
-      else __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (more) load_stage(st + 4, s1);
-      compute(s2);
-      if (more) __builtin_amdgcn_s_waitcnt(WAIT_OLDER);
-      else __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-    }
+    __builtin_amdgcn_s_waitcnt(0);
   } else {
     const int nst2 = (nst + 1) / 2 * 2;
     if (nst2 > 0) load_stage(0, s0);
@@ -293,12 +293,18 @@ __device__ __forceinline__ void gram_pass(const GramParams& p, const int tile, c
     __syncthreads();
     for (int st = 0; st < nst2; st += 2) {
       load_stage(st + 1, s1);
+      // keep the next stage's loads ahead of this stage's reads and products: left to itself the
+      // scheduler sinks them to just before the wait below, which then waits out their latency
+      __builtin_amdgcn_sched_barrier(0);
       compute(s0);
+      __builtin_amdgcn_sched_barrier(0);  // and the wait after all of them
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       const bool more = st + 2 < nst2;
       if (more) load_stage(st + 2, s0);
+      __builtin_amdgcn_sched_barrier(0);
       compute(s1);
+      __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
@@ -407,31 +413,43 @@ __global__ __launch_bounds__(256) void gram_finish_kernel(const float* __restric
   }
 }
 
-// One Gram pass per launch (grid: tiles x splits): 256 threads (4 waves, 2 x 2), NSTG stage buffers.
-template <int PASS, bool EV, int TI, int NSTG>
+// Stage shape of the Gram passes: a ring of four 16-row stages, else two 32-row stages (the same
+// LDS either way).
+#ifndef ISPA_GRAM_RING
+#define ISPA_GRAM_RING 1
+#endif
+constexpr int GNS = ISPA_GRAM_RING ? 4 : 2;       // stage buffers
+constexpr int GSR = ISPA_GRAM_RING ? 16 : GBK;    // rows per stage
+
+// One Gram pass per launch (grid: tiles x splits): 256 threads (4 waves, 2 x 2), NSTG stage buffers of
+// SR rows.
+template <int PASS, bool EV, int TI, int NSTG, int SR>
 __global__ __launch_bounds__(256, (PASS == PASS_GE && EV) ? 1 : 2) void gram_bf16_kernel(GramParams p) {
-  constexpr int SS = GramShape<PASS, EV, TI>::SS;
+  constexpr int SS = GramShape<PASS, EV, TI, SR>::SS;
   // the stage buffers as distinct arrays (see the attention kernel: lets the compiler overlap the
   // next stages' loads with this stage's reads)
   __shared__ __attribute__((aligned(1024))) uint16_t s0[SS];
   __shared__ __attribute__((aligned(1024))) uint16_t s1[SS];
-  __shared__ __attribute__((aligned(1024))) uint16_t s2[NSTG == 3 ? SS : 8];
-  gram_pass<PASS, EV, TI, NSTG>(p, blockIdx.x, blockIdx.y, s0, s1, s2);
+  __shared__ __attribute__((aligned(1024))) uint16_t s2[NSTG >= 3 ? SS : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t s3[NSTG >= 4 ? SS : 8];
+  gram_pass<PASS, EV, TI, NSTG, SR>(p, blockIdx.x, blockIdx.y, s0, s1, s2, s3);
 }
 
 // C and G in one launch (without E): workgroups [0, tiles_c * splits) run the C pass, the rest the G
 // pass, so the two fill the GPU together (the G tiles, shorter, come last).
 template <int TIC, int TIG>
 __global__ __launch_bounds__(256, 2) void gram_cg_kernel(GramParams p) {
-  constexpr int SC = GramShape<PASS_C, false, TIC>::SS, SG = GramShape<PASS_GE, false, TIG>::SS;
+  constexpr int SC = GramShape<PASS_C, false, TIC, GSR>::SS, SG = GramShape<PASS_GE, false, TIG, GSR>::SS;
   constexpr int SS = SC > SG ? SC : SG;
   __shared__ __attribute__((aligned(1024))) uint16_t s0[SS];
   __shared__ __attribute__((aligned(1024))) uint16_t s1[SS];
+  __shared__ __attribute__((aligned(1024))) uint16_t s2[GNS >= 3 ? SS : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t s3[GNS >= 4 ? SS : 8];
   const int bid = blockIdx.x, nc = p.tiles_c * p.splits;
   if (bid < nc)
-    gram_pass<PASS_C, false, TIC, 2>(p, bid % p.tiles_c, bid / p.tiles_c, s0, s1, nullptr);
+    gram_pass<PASS_C, false, TIC, GNS, GSR>(p, bid % p.tiles_c, bid / p.tiles_c, s0, s1, s2, s3);
   else
-    gram_pass<PASS_GE, false, TIG, 2>(p, (bid - nc) % p.tiles_ge, (bid - nc) / p.tiles_ge, s0, s1, nullptr);
+    gram_pass<PASS_GE, false, TIG, GNS, GSR>(p, (bid - nc) % p.tiles_ge, (bid - nc) / p.tiles_ge, s0, s1, s2, s3);
 }
 
 // D = A_full - A_loc (exact in float32) as D_hi = bf16(D), D_lo = bf16(D - D_hi); 8 elements per
@@ -637,12 +655,12 @@ ispa_status_t launch_gram(int64_t n_rows, int32_t d, int32_t dtype, const void* 
     if (E) {
       // E needs six staged matrices: its pass runs on its own (one workgroup per CU), after C's
       if (ti == 256)
-        hipLaunchKernelGGL((gram_bf16_kernel<PASS_C, false, 256, 2>), dim3(tiles_c, splits), dim3(256), 0, s, p);
+        hipLaunchKernelGGL((gram_bf16_kernel<PASS_C, false, 256, GNS, GSR>), dim3(tiles_c, splits), dim3(256), 0, s, p);
       else
-        hipLaunchKernelGGL((gram_bf16_kernel<PASS_C, false, 128, 2>), dim3(tiles_c, splits), dim3(256), 0, s, p);
+        hipLaunchKernelGGL((gram_bf16_kernel<PASS_C, false, 128, GNS, GSR>), dim3(tiles_c, splits), dim3(256), 0, s, p);
       ispa_status_t st = hip_check(hipGetLastError(), "gram_bf16_kernel launch (C)");
       if (st != ISPA_OK) return st;
-      hipLaunchKernelGGL((gram_bf16_kernel<PASS_GE, true, GT, 2>), dim3(tiles_ge, splits), dim3(256), 0, s, p);
+      hipLaunchKernelGGL((gram_bf16_kernel<PASS_GE, true, GT, GNS, GSR>), dim3(tiles_ge, splits), dim3(256), 0, s, p);
     } else {
       const dim3 grid((unsigned)((tiles_c + tiles_ge) * splits));
       if (ti == 256 && ti_ge == 256)
