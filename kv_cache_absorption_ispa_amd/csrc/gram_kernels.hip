@@ -203,58 +203,69 @@ __device__ __forceinline__ void gram_pass(const GramParams& p, const int tile, c
       acc1[a][b] = f32x16{0};
     }
 
+  // Operand fragments of one 16-row step: PASS_C: A_I (WBI), D_hi,J (WBJ), D_lo,J (WBJ); PASS_GE: A_I,
+  // A_J, and with EV D_hi,I, D_lo,I, D_hi,J, D_lo,J.
+  constexpr int NF = PASS == PASS_C ? WBI + 2 * WBJ : (EV ? 3 : 1) * (WBI + WBJ);
+  using Frags = bf16x8[NF];
+  auto read = [&](const uint16_t* buf, int ks, Frags& f) {
+#pragma unroll
+    for (int a = 0; a < WBI; ++a) f[a] = frag(buf + S::moff(0), offI[a], ks, TI);
+    if constexpr (PASS == PASS_C) {
+#pragma unroll
+      for (int b = 0; b < WBJ; ++b) {
+        f[WBI + b] = frag(buf + S::moff(1), offJ[b], ks, TJ);
+        f[WBI + WBJ + b] = frag(buf + S::moff(2), offJ[b], ks, TJ);
+      }
+    } else {
+#pragma unroll
+      for (int b = 0; b < WBJ; ++b) f[WBI + b] = frag(buf + S::moff(1), offJ[b], ks, TJ);
+      if constexpr (EV) {
+        constexpr int E0 = WBI + WBJ;
+#pragma unroll
+        for (int a = 0; a < WBI; ++a) {
+          f[E0 + a] = frag(buf + S::moff(2), offI[a], ks, TI);
+          f[E0 + WBI + a] = frag(buf + S::moff(3), offI[a], ks, TI);
+        }
+#pragma unroll
+        for (int b = 0; b < WBJ; ++b) {
+          f[E0 + 2 * WBI + b] = frag(buf + S::moff(4), offJ[b], ks, TJ);
+          f[E0 + 2 * WBI + WBJ + b] = frag(buf + S::moff(5), offJ[b], ks, TJ);
+        }
+      }
+    }
+  };
+  auto mma = [&](const Frags& f) {
+#pragma unroll
+    for (int a = 0; a < WBI; ++a)
+#pragma unroll
+      for (int b = 0; b < WBJ; ++b) {
+        if constexpr (PASS == PASS_C) {
+          acc0[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[a], f[WBI + b], acc0[a][b], 0, 0, 0);
+          acc0[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[a], f[WBI + WBJ + b], acc0[a][b], 0, 0, 0);
+        } else {
+          acc0[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[a], f[WBI + b], acc0[a][b], 0, 0, 0);
+        }
+      }
+    if constexpr (PASS == PASS_GE && EV) {
+      constexpr int E0 = WBI + WBJ;
+#pragma unroll
+      for (int a = 0; a < WBI; ++a)
+#pragma unroll
+        for (int b = 0; b < WBJ; ++b) {
+          const bf16x8 &hI = f[E0 + a], &lI = f[E0 + WBI + a];
+          const bf16x8 &hJ = f[E0 + 2 * WBI + b], &lJ = f[E0 + 2 * WBI + WBJ + b];
+          acc1[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hI, hJ, acc1[a][b], 0, 0, 0);
+          acc1[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hI, lJ, acc1[a][b], 0, 0, 0);
+          acc1[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lI, hJ, acc1[a][b], 0, 0, 0);
+        }
+    }
+  };
   auto compute = [&](const uint16_t* buf) {
 #pragma unroll
     for (int ks = 0; ks < SR / 16; ++ks) {
-      if constexpr (PASS == PASS_C) {
-        bf16x8 aI[WBI], hJ[WBJ], lJ[WBJ];
-#pragma unroll
-        for (int b = 0; b < WBJ; ++b) {
-          hJ[b] = frag(buf + S::moff(1), offJ[b], ks, TJ);
-          lJ[b] = frag(buf + S::moff(2), offJ[b], ks, TJ);
-        }
-#pragma unroll
-        for (int a = 0; a < WBI; ++a) aI[a] = frag(buf + S::moff(0), offI[a], ks, TI);
-#pragma unroll
-        for (int a = 0; a < WBI; ++a)
-#pragma unroll
-          for (int b = 0; b < WBJ; ++b) {
-            acc0[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aI[a], hJ[b], acc0[a][b], 0, 0, 0);
-            acc0[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aI[a], lJ[b], acc0[a][b], 0, 0, 0);
-          }
-      } else {
-        bf16x8 aI[WBI], aJ[WBJ];
-#pragma unroll
-        for (int b = 0; b < WBJ; ++b) aJ[b] = frag(buf + S::moff(1), offJ[b], ks, TJ);
-#pragma unroll
-        for (int a = 0; a < WBI; ++a) aI[a] = frag(buf + S::moff(0), offI[a], ks, TI);
-#pragma unroll
-        for (int a = 0; a < WBI; ++a)
-#pragma unroll
-          for (int b = 0; b < WBJ; ++b)
-            acc0[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aI[a], aJ[b], acc0[a][b], 0, 0, 0);
-        if constexpr (EV) {
-          bf16x8 hI[WBI], lI[WBI], hJ[WBJ], lJ[WBJ];
-#pragma unroll
-          for (int b = 0; b < WBJ; ++b) {
-            hJ[b] = frag(buf + S::moff(4), offJ[b], ks, TJ);
-            lJ[b] = frag(buf + S::moff(5), offJ[b], ks, TJ);
-          }
-#pragma unroll
-          for (int a = 0; a < WBI; ++a) {
-            hI[a] = frag(buf + S::moff(2), offI[a], ks, TI);
-            lI[a] = frag(buf + S::moff(3), offI[a], ks, TI);
-          }
-#pragma unroll
-          for (int a = 0; a < WBI; ++a)
-#pragma unroll
-            for (int b = 0; b < WBJ; ++b) {
-              acc1[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hI[a], hJ[b], acc1[a][b], 0, 0, 0);
-              acc1[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hI[a], lJ[b], acc1[a][b], 0, 0, 0);
-              acc1[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lI[a], hJ[b], acc1[a][b], 0, 0, 0);
-            }
-        }
-      }
+      Frags f;
+      read(buf, ks, f);
+      mma(f);
     }
   };
 
@@ -262,27 +273,40 @@ __device__ __forceinline__ void gram_pass(const GramParams& p, const int tile, c
   // loop body (one stage per buffer) has no early exit.  vmcnt counts this wave's loads, which
   // complete in order.
   if constexpr (NSTG == 4) {
-    // Ring of four SR-row buffers: stage st + 3 is loaded while stage st is multiplied, so three
-    // stages are in flight.  Before stage st is read each wave waits for its own loads of it (all
-    // but the two later stages' loads, which complete after it), then the barrier makes every wave's
-    // loads visible and frees the buffer read in the previous stage for the next load.
-    constexpr int NR = 2 * WLW;
-    constexpr int WAIT_RING = 0xF70 | (NR & 15) | ((NR >> 4) << 14);  // vmcnt(2 WLW)
+    // Ring of four 16-row buffers with the operand fragments double-buffered in registers: step st
+    // loads stage st + 3 (three stages in flight), reads stage st + 1's fragments from LDS and
+    // multiplies stage st's, read one step earlier, so the products never wait for LDS.  At the top
+    // of step st each wave waits for its own loads of stage st + 1 (all but stage st + 2's, which
+    // complete after them); the barrier then makes every wave's loads visible, and every wave has
+    // multiplied stage st - 1, so the buffer it came from takes the next load.
+    constexpr int WAIT_NEXT = 0xF70 | (WLW & 15) | ((WLW >> 4) << 14);      // vmcnt(WLW)
+    constexpr int WAIT_FIRST = 0xF70 | ((2 * WLW) & 15) | (((2 * WLW) >> 4) << 14);  // vmcnt(2 WLW)
     uint16_t* const buf[4] = {s0, s1, s2, s3};
     const int nstr = (nst + 3) / 4 * 4;
+    // The loads run up to three stages past the last one and the reads one (rows past r_end read as
+    // zeros), so every wait has the same count; the last wait drains the loads before the workgroup
+    // ends.
 #pragma unroll
     for (int j = 0; j < 3; ++j) load_stage(j, buf[j]);
-    // The loads run up to three stages past the last one (rows past r_end read as zeros), so every
-    // wait has the same count; the last wait drains them before the workgroup ends.
+    __builtin_amdgcn_s_waitcnt(WAIT_FIRST);
+    __builtin_amdgcn_s_barrier();
+    Frags f0, f1;
+    read(buf[0], 0, f0);
     for (int st = 0; st < nstr; st += 4) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        __builtin_amdgcn_s_waitcnt(WAIT_RING);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(WAIT_NEXT);
         __builtin_amdgcn_s_barrier();
         load_stage(st + u + 3, buf[(u + 3) & 3]);
         __builtin_amdgcn_sched_barrier(0);
-        compute(buf[u]);
-        __builtin_amdgcn_sched_barrier(0);
+        if (u % 2 == 0) {
+          read(buf[(u + 1) & 3], 0, f1);
+          mma(f0);
+        } else {
+          read(buf[(u + 1) & 3], 0, f0);
+          mma(f1);
+        }
       }
     }
     __builtin_amdgcn_s_waitcnt(0);
