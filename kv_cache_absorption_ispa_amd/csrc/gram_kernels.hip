@@ -570,9 +570,12 @@ int64_t gram_block_rows(int d) {
 }
 
 // I extent of the C pass's output tile: 256 where d allows it (a wave then owns 128 x 64), else 128.
-int gram_ti(int d) { return d % 256 == 0 ? 256 : 128; }
+// Without E at d <= 2048 the 128 tiles are twice as many, so fewer row splits fill the GPU and the
+// finish adds fewer partials (d = 1536: 222 tiles in 2 splits, 90 -> 84 us per 4680-row chunk; with
+// E the 256 tiles stay ahead, 139 against 159 us).
+int gram_ti(int d, bool ev) { return (d % 256 == 0 && (ev || d > 2048)) ? 256 : 128; }
 
-int gram_tiles_c(int d) { return (d / gram_ti(d)) * (d / GT); }
+int gram_tiles_c(int d, bool ev) { return (d / gram_ti(d, ev)) * (d / GT); }
 // TI x 128 tiles that reach the upper triangle (G and E pass): sum over I rows of n - r * ti
 int gram_tiles_ge(int d, int ti) {
   const int n = d / GT, r = ti / GT;
@@ -580,7 +583,7 @@ int gram_tiles_ge(int d, int ti) {
   for (int i = 0; i < d / ti; ++i) t += n - r * i;
   return t;
 }
-int gram_ti_ge(int d, bool ev) { return (!ev && d % 256 == 0) ? 256 : 128; }
+int gram_ti_ge(int d, bool ev) { return (!ev && d % 256 == 0 && d > 2048) ? 256 : 128; }
 
 int gram_splits(int64_t n_rows, int tiles) {
   // the most splits that still fit one round of two workgroups on each of the 256 CUs, at least 256
@@ -605,8 +608,8 @@ GramWs gram_ws_layout(int64_t n_rows, int d) {
   w.dbytes = ((size_t)rows * d * 2 + 255) & ~(size_t)255;
   w.dsplit = 0;
   const int64_t r1 = std::max<int64_t>(rows, 1);
-  const int s = std::max(gram_splits(r1, gram_tiles_c(d) + gram_tiles_ge(d, gram_ti_ge(d, false))),
-                         gram_splits(r1, gram_tiles_c(d) + gram_tiles_ge(d, gram_ti_ge(d, true))));
+  const int s = std::max(gram_splits(r1, gram_tiles_c(d, false) + gram_tiles_ge(d, gram_ti_ge(d, false))),
+                         gram_splits(r1, gram_tiles_c(d, true) + gram_tiles_ge(d, gram_ti_ge(d, true))));
   const size_t part_bytes = s > 1 ? (size_t)s * 3 * (size_t)d * d * sizeof(float) : 0;
   w.parts = 2 * w.dbytes;
   w.total = w.parts + part_bytes;
@@ -640,9 +643,9 @@ ispa_status_t launch_gram(int64_t n_rows, int32_t d, int32_t dtype, const void* 
     return ISPA_E_WORKSPACE;
   }
   const GramWs lay = gram_ws_layout(n_rows, d);
-  const int ti = gram_ti(d);
+  const int ti = gram_ti(d, E != nullptr);
   const int ti_ge = gram_ti_ge(d, E != nullptr);
-  const int tiles_c = gram_tiles_c(d), tiles_ge = gram_tiles_ge(d, ti_ge);
+  const int tiles_c = gram_tiles_c(d, E != nullptr), tiles_ge = gram_tiles_ge(d, ti_ge);
   // Rows go in blocks (the D_hi / D_lo workspace holds one); later blocks accumulate.
   const int64_t block_rows = gram_block_rows(d);
   int64_t r0 = 0;
