@@ -821,11 +821,33 @@ ispa_status_t chol_apply(hipStream_t s, int batch, int d, int d_out, const float
 
 // Fill the blocks of L^-1 below its 64x64 diagonal inverses (already in Linvf) by recursive
 // doubling.  Ranges are [start, start+len) in 64-row blocks; each level merges adjacent ranges.
-ispa_status_t invert_lower(hipStream_t s, int batch, int d, const float* L, float* Linvf, float* Tb,
-                           const int32_t* info) {
+// One level of the explicit inverse's recursive doubling for np adjacent pairs of block ranges (A of
+// sa blocks, then C of sc blocks), the first A starting at block a: inv([A 0; B C]) has off-diagonal
+// block -C^-1 (B A^-1).  T (one pair's nC x nA after another, layer stride sT) holds B A^-1.
+ispa_status_t invert_pairs(hipStream_t s, int batch, int d, const float* L, float* Linvf, float* T, size_t sT,
+                           const int32_t* info, int a, int sa, int sc, int np) {
   const size_t dd = (size_t)d * d;
+  const int nA = sa * NB, nC = sc * NB;
+  const size_t a0 = (size_t)a * NB;
+  const size_t pstep = (size_t)(nA + nC) * (d + 1);  // from one pair's corner to the next
+  // T = B A^-1, with B = L[a0+nA : a0+nA+nC, a0 : a0+nA] and A^-1 lower triangular
+  ISPA_TRY((gemm<false, false>(s, batch, nC, nA, nA, L + (a0 + nA) * d + a0, d, dd, Linvf + a0 * d + a0, d, dd,
+                               nullptr, 0, 0, T, nA, sT, 1.f, 0.f, false, info, KM_LOWER_B, np, pstep, pstep, 0,
+                               (size_t)nC * nA)));
+  // off-diagonal block of the inverse: -C^-1 T, with C^-1 lower triangular
+  return gemm<false, false>(s, batch, nC, nA, nC, Linvf + (a0 + nA) * (d + 1), d, dd, T, nA, sT, nullptr, 0, 0,
+                            Linvf + (a0 + nA) * d + a0, d, dd, -1.f, 0.f, false, info, KM_LOWER_A, np, pstep,
+                            (size_t)nC * nA, 0, pstep);
+}
+
+// The doubling's levels over blocks [b0, b0 + nb): ranges merge pairwise, left to right, an odd last
+// range passing a level unchanged; pairs of equal sizes run as one launch.  With emit false nothing
+// is launched and the result is the scratch T needs per layer (floats).
+size_t invert_range(hipStream_t s, int batch, int d, const float* L, float* Linvf, float* T, size_t sT,
+                    const int32_t* info, int b0, int nb, bool emit, ispa_status_t* st) {
   std::vector<std::pair<int, int>> rng;
-  for (int k = 0; k < d / NB; ++k) rng.push_back({k, 1});
+  for (int k = b0; k < b0 + nb; ++k) rng.push_back({k, 1});
+  size_t need = 0;
   while (rng.size() > 1) {
     std::vector<std::pair<int, int>> next;
     size_t i = 0;
@@ -837,24 +859,29 @@ ispa_status_t invert_lower(hipStream_t s, int batch, int d, const float* L, floa
         ++np;
         j += 2;
       }
-      const int nA = sa * NB, nC = sc * NB;
-      const size_t a0 = (size_t)rng[i].first * NB;
-      const size_t pstep = (size_t)(nA + nC) * (d + 1);  // from one pair's corner to the next
-      // T = B A^-1, with B = L[a0+nA : a0+nA+nC, a0 : a0+nA] and A^-1 lower triangular
-      ISPA_TRY((gemm<false, false>(s, batch, nC, nA, nA, L + (a0 + nA) * d + a0, d, dd, Linvf + a0 * d + a0, d, dd,
-                                   nullptr, 0, 0, Tb, nA, dd, 1.f, 0.f, false, info, KM_LOWER_B, np, pstep, pstep, 0,
-                                   (size_t)nC * nA)));
-      // off-diagonal block of the inverse: -C^-1 T, with C^-1 lower triangular
-      ISPA_TRY((gemm<false, false>(s, batch, nC, nA, nC, Linvf + (a0 + nA) * (d + 1), d, dd, Tb, nA, dd, nullptr, 0,
-                                   0, Linvf + (a0 + nA) * d + a0, d, dd, -1.f, 0.f, false, info, KM_LOWER_A, np, pstep,
-                                   (size_t)nC * nA, 0, pstep)));
+      need = std::max(need, (size_t)np * sa * sc * NB * NB);
+      if (emit && *st == ISPA_OK) *st = invert_pairs(s, batch, d, L, Linvf, T, sT, info, rng[i].first, sa, sc, np);
       for (int k = 0; k < np; ++k) next.push_back({rng[i + 2 * k].first, sa + sc});
       i = j;
     }
     if (i < rng.size()) next.push_back(rng[i]);
     rng.swap(next);
   }
-  return ISPA_OK;
+  return need;
+}
+
+// Blocks in the leading range of the doubling's last level (nblk >= 2): the inverse is the leading
+// range's levels, the trailing range's, and one last pair.
+int inverse_split(int nblk) {
+  std::vector<int> sz(nblk, 1);
+  while (sz.size() > 2) {
+    std::vector<int> next;
+    size_t i = 0;
+    for (; i + 1 < sz.size(); i += 2) next.push_back(sz[i] + sz[i + 1]);
+    if (i < sz.size()) next.push_back(sz[i]);
+    sz.swap(next);
+  }
+  return sz.size() == 2 ? sz[0] : nblk;
 }
 
 namespace {
@@ -932,6 +959,22 @@ ispa_status_t launch_absorb(int32_t d, int32_t d_out, int32_t batch, const float
   };
   const int fork_k = (side != nullptr && d <= 2048) ? 4 : -1;  // panel step before which it is forked (-1: first)
   bool forked = false;
+  // The explicit L^-1 by recursive doubling over block ranges (for adjacent ranges A, then C,
+  // inv([A 0; B C]) has off-diagonal block -C^-1 (B A^-1)) in three parts: the levels inside the
+  // leading range of the last level (its P blocks of L are final once the factorisation has factored
+  // block P - 1), those inside the trailing range, and the last pair.  With a side stream the first
+  // part runs there, after R = C W, beside the factorisation's last steps; the trailing part runs on
+  // `s` after the factorisation, in the intermediate buffer Zb (free until the solves) when it is
+  // large enough, and the last pair after both.  Without one, the same launches run in order on `s`.
+  const int inv_p = inverse_split(nblk), inv_q = nblk - inv_p;
+  ispa_status_t inv_st = ISPA_OK;
+  auto inv_lead = [&](hipStream_t st) {
+    invert_range(st, batch, d, M, Linvf, Tb, dd, info, 0, inv_p, true, &inv_st);
+    return inv_st;
+  };
+  const bool inv_q_in_zb =
+      invert_range(s, batch, d, M, Linvf, Zb, dn, info, inv_p, inv_q, false, &inv_st) <= dn;
+  bool inv_lead_forked = false;
   if (fork_k < 0) {
     ISPA_TRY(fork_cw());
     forked = true;
@@ -970,13 +1013,24 @@ ispa_status_t launch_absorb(int32_t d, int32_t d_out, int32_t batch, const float
       ISPA_TRY((gemm<false, true>(s, batch, rest, rest, pe - p0, pan, d, dd, pan, d, dd, trail, d, dd, trail, d, dd,
                                   -1.f, 1.f, true, info, 0, 1, 0, 0, 0, 0, M, Linvf, info, d, k0 + NB)));
     }
+    // block k + 1 is factored: once it is block inv_p - 1, the leading range of L^-1 can be formed
+    // beside the rest of the factorisation (on the side stream, after R = C W, which uses Tb)
+    if (k + 2 == inv_p && forked && side != nullptr && inv_q > 0) {
+      ISPA_TRY(hip_check(hipEventRecord(side->ev_fork, s), "hipEventRecord (fork, inverse)"));
+      ISPA_TRY(hip_check(hipStreamWaitEvent(side->stream, side->ev_fork, 0), "hipStreamWaitEvent (fork, inverse)"));
+      ISPA_TRY(inv_lead(side->stream));
+      inv_lead_forked = true;
+    }
   }
   if (!forked) ISPA_TRY(fork_cw());
-  // join: R = C W is done before the solve reads it
+  if (inv_q > 0 && inv_q_in_zb)
+    ISPA_TRY((invert_range(s, batch, d, M, Linvf, Zb, dn, info, inv_p, inv_q, true, &inv_st), inv_st));
+  // join: R = C W (and the leading range of L^-1) are done before Tb is reused and the solve reads R
   ISPA_TRY(joiner.join());
-  // explicit L^-1 by recursive doubling over block ranges: for adjacent ranges A (first) and C,
-  // inv([A 0; B C]) has off-diagonal block -C^-1 (B A^-1); pairs of equal sizes run as one launch.
-  ISPA_TRY(invert_lower(s, batch, d, M, Linvf, Tb, info));
+  if (!inv_lead_forked) ISPA_TRY(inv_lead(s));
+  if (inv_q > 0 && !inv_q_in_zb)
+    ISPA_TRY((invert_range(s, batch, d, M, Linvf, Tb, dd, info, inv_p, inv_q, true, &inv_st), inv_st));
+  if (inv_q > 0) ISPA_TRY(invert_pairs(s, batch, d, M, Linvf, Tb, dd, info, 0, inv_p, inv_q, 1));
   // X = (L L^T)^-1 R.  With the refinement, both solves run on the bf16 matrix cores as three-term
   // products (about 2^-16 relative per product); the accurate residual then corrects
   // the first solve's error and the correction's error is that much smaller again.  L (M) and the

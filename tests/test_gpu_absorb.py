@@ -92,6 +92,27 @@ def test_gram_full_size_and_deterministic():
         assert np.all(excess <= 0), np.unravel_index(np.argmax(excess), excess.shape)
 
 
+@pytest.mark.parametrize("d,qff", [(2048, False), (2048, True), (2304, False), (2304, True)])
+def test_gram_tile_shapes(d, qff):
+    """Both sides of the tile choice: without E, d <= 2048 runs on 128-row tiles (more tiles, fewer
+    row splits) and d > 2048 on 256-row ones; with E both run on 256-row C tiles.  Two chunks of
+    2340 rows; every entry of G, C (and E) within the float32-accumulation bound of its float64 sum."""
+    say("d, E", d, qff)
+    al, af = inputs.absorb_rows(6, 0, 4680, d, "bf16")
+    G, C, Q = gpu_gram(list(zip(split_rows(al, 2), split_rows(af, 2))), d, qff=qff)
+    Gr, Cr = oracle.gram(al.f64, af.f64)
+    a_abs, d_abs = np.abs(al.f64), np.abs(af.f64 - al.f64)
+    checks = [(host64(G), Gr, a_abs.T @ a_abs), (host64(C), Cr, a_abs.T @ d_abs)]
+    if qff:
+        dd = af.f64 - al.f64
+        checks.append((host64(Q), dd.T @ dd, d_abs.T @ d_abs))
+    for got, ref, absum in checks:
+        excess = np.abs(got - ref) - 1e-4 * absum
+        say("worst |error| / bound", float(np.max(np.abs(got - ref) / (1e-4 * absum + 1e-30))))
+        assert np.all(excess <= 0), np.unravel_index(np.argmax(excess), excess.shape)
+    assert torch.equal(G, G.T)
+
+
 def test_gram_rows_past_one_launch():
     """More rows than one launch block takes (the bf16 split of D = A_full - A_loc is formed for at
     most 32768 rows at a time): the call splits them over blocks, the later ones accumulating.  It
