@@ -17,7 +17,9 @@
 //     L_ik = M_ik L_kk^-T                             (GEMM, in place)
 //     M_ij -= L_ik L_jk^T  (lower tiles only)         (GEMM; the workgroup of the next diagonal
 //                                                      block then factors and inverts it)
-//   explicit inverse of L by recursive doubling over block ranges
+//   explicit inverse of L by recursive doubling over block ranges (the levels inside the leading
+//                                                      range of the last one on the side stream, beside
+//                                                      the factorisation's last steps)
 //   X = L^-T (L^-1 R)                                  (two triangular GEMMs)
 //   one refinement step: r = R - G X - lambda X to ~2^-35 of the scales (exact int8
 //   digit-slice products, else float64 accumulation), dW = X + L^-T (L^-1 r).
