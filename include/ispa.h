@@ -526,12 +526,15 @@ ispa_status_t ispa_absorb_solve_lambdas(int32_t d, int32_t d_out, int32_t batch,
 
 /* A second stream the caller owns, with two events the caller owns, for
  * ispa_absorb_solve_ex: R = C W runs on `stream` beside the factorisation on
- * the call's main stream.  `stream` (hipStream_t) must differ from the main
- * stream and should have the default priority; `ev_fork`, `ev_join`
- * (hipEvent_t, timing may be disabled) are recorded and waited on inside the
- * call: the side stream waits for the main stream's earlier work before R =
- * C W, and the main stream waits for R = C W before the solve reads it, on
- * every return after the fork (error returns included).  Calls that share one
+ * the call's main stream, and after it the leading part of the explicit
+ * inverse of the factor, beside the factorisation's last steps.  `stream`
+ * (hipStream_t) must differ from the main stream and should have the default
+ * priority; `ev_fork`, `ev_join` (hipEvent_t, timing may be disabled) are
+ * recorded and waited on inside the call: the side stream waits for the main
+ * stream's earlier work before R = C W and for the factored blocks before the
+ * inverse's part, and the main stream waits for the side stream's work before
+ * the solve reads it, on every return after the fork (error returns
+ * included).  The result is bitwise the same as without a side stream.  Calls that share one
  * side stream and its events must be enqueued from one host thread at a time
  * (the event record / wait pairs must not interleave). */
 typedef struct {
