@@ -188,12 +188,16 @@ def test_solve_parity_on_oracle_statistics(d, d_out):
     assert e <= TOL_DW
 
 
-@pytest.mark.parametrize("d,d_out,b", [(2560, 640, 2), (3072, 1024, 1), (2560, 2560, 2)])
+@pytest.mark.parametrize("d,d_out,b", [(2560, 640, 2), (3072, 1024, 1), (2560, 2560, 2), (1536, 512, 3), (512, 128, 2),
+                                       (64, 64, 1)])
 def test_solve_with_a_side_stream_is_the_single_stream_solve(d, d_out, b):
-    """With a caller-owned side stream and d > 2048, R = C W runs beside the factorisation as a bounded
-    launch whose workgroups loop over the tiles (here more tiles than workgroups, and across the batch;
-    128 x 128 tiles for the first two shapes, 256 x 256 for the last); each tile is formed exactly as in
-    the one-stream launch, so dW is the same bit for bit, and within the dW gate of the float64 solve."""
+    """With a caller-owned side stream R = C W runs beside the factorisation (for d > 2048 as a bounded
+    launch whose workgroups loop over the tiles: here more tiles than workgroups, and across the batch;
+    128 x 128 tiles for the first two shapes, 256 x 256 for the third), and the explicit inverse's
+    leading levels follow it there once their blocks are factored (d = 2560: 32 of 40 blocks, 3072: 32
+    of 48, 1536: 16 of 24; at d = 512 they come after the factorisation, d = 64 has none).  Each tile
+    is formed exactly as on one stream, so dW is the same bit for bit, and within the dW gate of the
+    float64 solve."""
     Gs, Cs, Ws, refs = [], [], [], []
     for layer in range(b):
         al, af = inputs.absorb_rows(13, layer, 4 * d, d, "f32")
