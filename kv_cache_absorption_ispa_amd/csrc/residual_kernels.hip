@@ -29,7 +29,7 @@ namespace {
 #define ISPA_OZ_DIGITS 5
 #endif
 constexpr int OZ_S = ISPA_OZ_DIGITS;  // 7-bit digits per value
-constexpr int OZ_T = 128;   // output tile: 8 waves of 64 x 32 (two per SIMD)
+constexpr int OZ_T = 128;   // output tile: 8 waves of 32 x 64 (two per SIMD)
 constexpr int OZ_K = 32;    // K per stage: one v_mfma_i32_32x32x32_i8 step
 constexpr int OZ_NSTG = 3;  // stages in the LDS ring (48 KB each)
 typedef int v4i_t __attribute__((ext_vector_type(4)));
@@ -191,7 +191,7 @@ __device__ __forceinline__ int oz_slot(int row, int c) { return c ^ ((row >> 3) 
 
 // r = R - (G X) + gamma X for one 128 x 128 output tile (rows of G: m0.., columns of X: n0..).
 // Per 32-deep K stage the S digit slices of both operands (2 S x 128 rows x 32 bytes) go into
-// a ring of LDS buffers by buffer loads into LDS; each of the 8 waves owns 64 x 32 outputs with S
+// a ring of LDS buffers by buffer loads into LDS; each of the 8 waves owns 32 x 64 outputs with S
 // int32 accumulator sets (one per diagonal s + t), two waves per SIMD.
 __global__ __launch_bounds__(512) void oz_gemm_kernel(OzParams p) {
   const int b = blockIdx.z;
@@ -208,7 +208,7 @@ __global__ __launch_bounds__(512) void oz_gemm_kernel(OzParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
-  const int wi = (wave >> 2) * 64, wj = (wave & 3) * 32;
+  const int wi = (wave >> 1) * 32, wj = (wave & 1) * 64;  // 32 rows x 64 columns per wave
   const uint32_t d = (uint32_t)p.d, n = (uint32_t)p.n;
   const size_t dd = (size_t)d * d, dn = (size_t)d * n;
   // wave load g = wave + 8 j: operand slice o = g / 4 (0..S-1: digits of G, S..2S-1: of X), rows
@@ -242,20 +242,21 @@ __global__ __launch_bounds__(512) void oz_gemm_kernel(OzParams p) {
   for (int c = 0; c < OZ_S; ++c)
 #pragma unroll
     for (int i = 0; i < 2; ++i) acc[c][i] = v16i_t{0};
+  // the row block's digit fragments are read once and kept; each column block's are streamed (15
+  // fragment reads per stage and wave)
   auto compute = [&](const int8_t* bb) {
+    v4i_t a[OZ_S];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      v4i_t a[OZ_S];
+    for (int s = 0; s < OZ_S; ++s) a[s] = frag(bb, s, wi);
 #pragma unroll
-      for (int s = 0; s < OZ_S; ++s) a[s] = frag(bb, s, wi + 32 * i);
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int t = 0; t < OZ_S; ++t) {
-        const v4i_t x = frag(bb, OZ_S + t, wj);
+        const v4i_t x = frag(bb, OZ_S + t, wj + 32 * i);
 #pragma unroll
         for (int s = 0; s + t < OZ_S; ++s)
           acc[s + t][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[s], x, acc[s + t][i], 0, 0, 0);
       }
-    }
   };
   // ring: stage st in buffer st % OZ_NSTG; before the barrier that ends stage st each wave waits
   // until stage st + 1 has landed, leaving the newer stage in flight
@@ -279,15 +280,15 @@ __global__ __launch_bounds__(512) void oz_gemm_kernel(OzParams p) {
       __syncthreads();
     }
   }
-  // acc[c][i][v]: row m0 + wi + 32 i + 8 (v / 4) + 4 hh + v % 4, column n0 + wj + l32
+  // acc[c][i][v]: row m0 + wi + 8 (v / 4) + 4 hh + v % 4, column n0 + wj + 32 i + l32
   const double gb = p.gamma_b ? p.gamma * (double)p.gamma_b[b] : p.gamma;
-  const int j = n0 + wj + l32;
-  const int fj = scale_exp(__uint_as_float(p.xmax[(size_t)b * n + j]));
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 2; ++i) {
+    const int j = n0 + wj + 32 * i + l32;
+    const int fj = scale_exp(__uint_as_float(p.xmax[(size_t)b * n + j]));
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int r = m0 + wi + 32 * i + 8 * (v >> 2) + 4 * hh + (v & 3);
+      const int r = m0 + wi + 8 * (v >> 2) + 4 * hh + (v & 3);
       double sum = 0.0;
 #pragma unroll
       for (int c = OZ_S - 1; c >= 0; --c) sum += ldexp((double)acc[c][i][v], -7 * (c + 2));
@@ -298,6 +299,7 @@ __global__ __launch_bounds__(512) void oz_gemm_kernel(OzParams p) {
       x += gb * (double)p.X[o];
       p.r[o] = (float)x;
     }
+  }
 }
 
 }  // namespace
