@@ -111,7 +111,7 @@ __device__ __forceinline__ void upper_tile(int u, int n, int r, int& ti, int& tj
 template <int PASS, bool EV, int TI_, int NSTG, int SR = GBK>
 __device__ __forceinline__ void gram_pass(const GramParams& p, const int tile, const int split, uint16_t* s0,
                                           uint16_t* s1, uint16_t* s2, uint16_t* s3 = nullptr) {
-  static_assert((SR == GBK && NSTG == 2) || (SR == 16 && NSTG == 4), "stage shapes");
+  static_assert((SR == GBK && NSTG == 2) || (SR == 16 && (NSTG == 3 || NSTG == 4)), "stage shapes");
   using S = GramShape<PASS, EV, TI_, SR>;
   constexpr int TI = S::TI, TJ = S::TJ, NM = S::NM, WBI = S::WBI, WBJ = S::WBJ;
   constexpr int NWV = 4;
@@ -272,7 +272,31 @@ __device__ __forceinline__ void gram_pass(const GramParams& p, const int tile, c
   // Stages past r_end read as zeros, so the stage count is rounded up to a multiple of NSTG and the
   // loop body (one stage per buffer) has no early exit.  vmcnt counts this wave's loads, which
   // complete in order.
-  if constexpr (NSTG == 4) {
+  if constexpr (NSTG == 3) {
+    // Ring of three 16-row buffers without the register double buffer (the E pass: its twelve
+    // fragments twice over would not fit two waves per SIMD): step st loads stage st + 2 and
+    // multiplies stage st, two stages in flight.  At the top of step st each wave waits for its own
+    // loads of stage st (all but stage st + 1's); the barrier makes every wave's loads visible and
+    // frees the buffer stage st - 1 was read from.
+    constexpr int WAIT_CUR = 0xF70 | (WLW & 15) | ((WLW >> 4) << 14);  // vmcnt(WLW)
+    uint16_t* const buf[3] = {s0, s1, s2};
+    const int nstr = (nst + 2) / 3 * 3;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) load_stage(j, buf[j]);
+    // loads run up to two stages past the last one (rows past r_end read as zeros)
+    for (int st = 0; st < nstr; st += 3) {
+#pragma unroll
+      for (int u = 0; u < 3; ++u) {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(WAIT_CUR);
+        __builtin_amdgcn_s_barrier();
+        load_stage(st + u + 2, buf[(u + 2) % 3]);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(buf[u]);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+  } else if constexpr (NSTG == 4) {
     // Ring of four 16-row buffers with the operand fragments double-buffered in registers: step st
     // loads stage st + 3 (three stages in flight), reads stage st + 1's fragments from LDS and
     // multiplies stage st's, read one step earlier, so the products never wait for LDS.  At the top
@@ -444,11 +468,13 @@ __global__ __launch_bounds__(256) void gram_finish_kernel(const float* __restric
 #endif
 constexpr int GNS = ISPA_GRAM_RING ? 4 : 2;       // stage buffers
 constexpr int GSR = ISPA_GRAM_RING ? 16 : GBK;    // rows per stage
+// The E pass (six staged matrices, two accumulator sets): three 16-row stages, two workgroups per CU.
+constexpr int GNS_E = ISPA_GRAM_RING ? 3 : 2;
 
 // One Gram pass per launch (grid: tiles x splits): 256 threads (4 waves, 2 x 2), NSTG stage buffers of
 // SR rows.
 template <int PASS, bool EV, int TI, int NSTG, int SR>
-__global__ __launch_bounds__(256, (PASS == PASS_GE && EV) ? 1 : 2) void gram_bf16_kernel(GramParams p) {
+__global__ __launch_bounds__(256, (PASS == PASS_GE && EV && NSTG != 3) ? 1 : 2) void gram_bf16_kernel(GramParams p) {
   constexpr int SS = GramShape<PASS, EV, TI, SR>::SS;
   // the stage buffers as distinct arrays (see the attention kernel: lets the compiler overlap the
   // next stages' loads with this stage's reads)
@@ -687,7 +713,7 @@ ispa_status_t launch_gram(int64_t n_rows, int32_t d, int32_t dtype, const void* 
         hipLaunchKernelGGL((gram_bf16_kernel<PASS_C, false, 128, GNS, GSR>), dim3(tiles_c, splits), dim3(256), 0, s, p);
       ispa_status_t st = hip_check(hipGetLastError(), "gram_bf16_kernel launch (C)");
       if (st != ISPA_OK) return st;
-      hipLaunchKernelGGL((gram_bf16_kernel<PASS_GE, true, GT, GNS, GSR>), dim3(tiles_ge, splits), dim3(256), 0, s, p);
+      hipLaunchKernelGGL((gram_bf16_kernel<PASS_GE, true, GT, GNS_E, GSR>), dim3(tiles_ge, splits), dim3(256), 0, s, p);
     } else {
       const dim3 grid((unsigned)((tiles_c + tiles_ge) * splits));
       if (ti == 256 && ti_ge == 256)
