@@ -17,22 +17,23 @@
 // accumulator.  E = D_hi^T D_hi + D_hi^T D_lo + D_lo^T D_hi (the D_lo^T D_lo
 // term is below 2^-17 of E).
 //
-// bf16 design (three launches per block of rows):
+// bf16 design (two or three launches per block of rows):
 //  * split pass (HBM-bound): D_hi, D_lo [rows, d] into the workspace;
 //  * Gram kernel, two passes over the rows.  The C pass owns output tiles of TI x 128 (TI = 256
 //    where d allows) and forms C from A_loc[:, I], D_hi[:, J], D_lo[:, J]; the G pass owns the
 //    TI x 128 tiles that reach the upper triangle and forms G (and, in a launch of its own, E) from
 //    A_loc[:, I], A_loc[:, J] (and D_hi, D_lo of both).  Without E both passes run in one launch.
-//    Per 32-row stage (two in flight) the staged matrices go row-major into LDS straight from
-//    global memory (buffer loads into LDS, 16-byte chunks XOR-swizzled by row); MFMA operands need
+//    Through a ring of 16-row stages (two or three in flight) the staged matrices go row-major into
+//    LDS straight from global memory (buffer loads into LDS, 16-byte chunks XOR-swizzled by row); MFMA operands need
 //    8 consecutive rows at one column and come from two transposing LDS reads (ds_read_b64_tr_b16).
 //    Four waves own (TI / 2) x 64 sub-tiles (blocks of v_mfma_f32_32x32x16_bf16): each operand
 //    fragment read from LDS feeds TI / 32 or 4 MFMAs, and one accumulator set per pass keeps two
-//    waves per SIMD.  Rows are split over workgroups when the tiles alone cannot fill the GPU;
-//    every split then stores its partial tile in the workspace;
-//  * finish kernel: adds the partials in split order (bitwise deterministic, no atomics) and
-//    mirrors G and E into the lower triangle through LDS transposes, so both triangles hold the
-//    same bits.
+//    waves per SIMD.  G and E are stored at and above the diagonal and, from the same registers,
+//    at the mirrored positions below it, so both triangles hold the same bits.  Rows are split
+//    over workgroups when the tiles alone cannot fill the GPU; every split then stores its
+//    partial tile in the workspace, and
+//  * a finish kernel adds the partials in split order (bitwise deterministic, no atomics) and
+//    mirrors G and E through LDS transposes.
 #include "ispa_internal.h"
 
 namespace ispa {
@@ -69,8 +70,8 @@ struct GramParams {
 //    else 128) x 128; a wave owns (TI / 2) x 64, so each operand fragment read from LDS feeds
 //    TI / 32 (A side) or 4 (D side) MFMAs, and one accumulator set keeps two waves per SIMD.
 //  * PASS_GE: G = A_loc^T A_loc, and E = D_hi^T D_hi + D_hi^T D_lo + D_lo^T D_hi when EV, on the
-//    128 x 128 tiles on or above the diagonal only (listed compactly, row by row); the finish
-//    kernel mirrors them.
+//    TI x 128 tiles that reach the upper triangle only (listed compactly, row by row), each
+//    element above the diagonal also stored at its mirror position.
 // Staged matrices of a stage, one after the other, each GBK rows, row-major:
 //   PASS_C:  0 A_loc[:, I] (TI)   1 D_hi[:, J]   2 D_lo[:, J]
 //   PASS_GE: 0 A_loc[:, I]   1 A_loc[:, J]   (EV: 2 D_hi[:, I]   3 D_lo[:, I]   4 D_hi[:, J]   5 D_lo[:, J])
@@ -361,9 +362,12 @@ __device__ __forceinline__ void gram_pass(const GramParams& p, const int tile, c
   // ---- epilogue, straight from the accumulators: element v of lane (col, hh) is row
   // 8(v/4) + 4hh + v%4 of its 32 x 32 block, so for each v the 32 lanes of a half-wave cover 32
   // consecutive columns of one row (128-byte stores).  With split rows every split stores its
-  // partial tile; otherwise C is stored everywhere and G, E at and above the diagonal.
-  // gram_finish_kernel then adds the partials in split order and mirrors G and E into the lower
-  // triangle.  Offsets within a d x d matrix fit in 32 bits (d <= 2^15).
+  // partial tile, and gram_finish_kernel adds the partials in split order and mirrors G and E.
+  // Otherwise C is stored everywhere, and G and E at and above the diagonal, each element strictly
+  // above it also at its mirror position: lane (col, hh) holds rows 8q + 4hh .. 8q + 4hh + 3 of its
+  // column, which are 16 consecutive bytes of row `col` of the lower triangle (the 64 lanes of one
+  // store fill 32 bytes of each of 32 rows; the four q fill those rows' 128-byte lines), so both
+  // triangles hold the same bits.  Offsets within a d x d matrix fit in 32 bits (d <= 2^15).
   const uint32_t d = (uint32_t)p.d;
   constexpr int NOUT = PASS == PASS_C ? 1 : (EV ? 2 : 1);
 #pragma unroll
@@ -374,7 +378,7 @@ __device__ __forceinline__ void gram_pass(const GramParams& p, const int tile, c
       X = p.part + ((size_t)split * 3 + m) * (size_t)d * d;
     else
       X = m == 0 ? p.C : (m == 1 ? p.G : p.E);
-    const bool upper_only = p.part == nullptr && m > 0;
+    const bool mirror = p.part == nullptr && m > 0;
 #pragma unroll
     for (int a = 0; a < WBI; ++a)
 #pragma unroll
@@ -382,12 +386,35 @@ __device__ __forceinline__ void gram_pass(const GramParams& p, const int tile, c
         const f32x16& acc = o == 0 ? acc0[a][b] : acc1[a][b];
         const uint32_t c = (uint32_t)(J0 + wj + 32 * b + l32);
         const uint32_t r0 = (uint32_t)(I0 + wi + 32 * a + 4 * hh);
+        if (!mirror) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const uint32_t r = r0 + (uint32_t)(8 * (v >> 2) + (v & 3));
-          if (upper_only && r > c) continue;
-          float* x = X + r * d + c;
-          *x = (p.part == nullptr && p.accumulate) ? *x + acc[v] : acc[v];
+          for (int v = 0; v < 16; ++v) {
+            const uint32_t r = r0 + (uint32_t)(8 * (v >> 2) + (v & 3));
+            float* x = X + r * d + c;
+            *x = (p.part == nullptr && p.accumulate) ? *x + acc[v] : acc[v];
+          }
+        } else {
+          f32x16 val = acc;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const uint32_t r = r0 + (uint32_t)(8 * (v >> 2) + (v & 3));
+            if (r > c) continue;
+            float* x = X + r * d + c;
+            if (p.accumulate) val[v] += *x;
+            *x = val[v];
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t rq = r0 + 8 * q;
+            float* y = X + c * d + rq;
+            if (rq + 3 < c) {
+              *(f32x4*)y = f32x4{val[4 * q], val[4 * q + 1], val[4 * q + 2], val[4 * q + 3]};
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (rq + e < c) y[e] = val[4 * q + e];
+            }
+          }
         }
         // one block at a time: keeps the loads of the accumulate from being hoisted (and held in
         // registers) across the whole tile
@@ -396,66 +423,85 @@ __device__ __forceinline__ void gram_pass(const GramParams& p, const int tile, c
   }
 }
 
-// Completes a Gram call, per 64 x 64 block (bi, bj) of the output: with split rows, C = the C pass's
-// splits_c partials added in split order (plus the old C when accumulating), and for bi <= bj the
-// same for the elements of G and E at and above the diagonal (splits_ge partials); then G and E are
-// mirrored: element (r, c) with r < c is copied to (c, r) through an LDS transpose, so both
-// triangles hold the same bits.
-__global__ __launch_bounds__(256) void gram_finish_kernel(const float* __restrict__ part, int splits_c, int splits_ge,
-                                                          int nmat, float* C, float* G, float* E, int d,
-                                                          int accumulate) {
-  __shared__ float T[64][65];
+// Completes a Gram call with split rows, per 64 x 64 block (bi, bj) of the output: C = the splits'
+// partials added in split order (plus the old C when accumulating), and for bi <= bj the same for
+// the elements of G (and E, NMAT = 3) at and above the diagonal, which are then mirrored: element
+// (r, c) with r < c is copied to (c, r) through an LDS transpose, so both triangles hold the same
+// bits.  A split's loads for all matrices and rows of the thread are issued together, so a block
+// waits out one load latency per split rather than one per row and matrix.
+template <int NMAT>
+__global__ __launch_bounds__(256) void gram_finish_kernel(const float* __restrict__ part, int splits,
+                                                          float* __restrict__ C, float* __restrict__ G,
+                                                          float* __restrict__ E, int d, int accumulate) {
+  __shared__ float T[NMAT - 1][64][65];
   const int bi = blockIdx.y, bj = blockIdx.x;
   const int tid = threadIdx.x;
   const size_t dd = (size_t)d * d;
   const int r_in = tid >> 4, c4 = (tid & 15) * 4;  // thread: rows r_in + 16 k, columns c4 .. c4 + 3
-  if (splits_c > 1) {
+  const bool up = bi <= bj;                        // G and E: the upper blocks carry them
+  size_t o[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const size_t o = (size_t)(bi * 64 + r_in + 16 * k) * d + bj * 64 + c4;
-      f32x4 v = {0.f, 0.f, 0.f, 0.f};
-      for (int s = 0; s < splits_c; ++s) v += *(const f32x4*)(part + (size_t)s * 3 * dd + o);
-      if (accumulate) v += *(const f32x4*)(C + o);
-      *(f32x4*)(C + o) = v;
+  for (int k = 0; k < 4; ++k) o[k] = (size_t)(bi * 64 + r_in + 16 * k) * d + bj * 64 + c4;
+  f32x4 v[NMAT][4];
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[m][k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < splits; ++s) {
+    const float* ps = part + (size_t)s * 3 * dd;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[0][k] += *(const f32x4*)(ps + o[k]);
+    if (up) {
+#pragma unroll
+      for (int m = 1; m < NMAT; ++m)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[m][k] += *(const f32x4*)(ps + m * dd + o[k]);
     }
   }
-  if (bi > bj) return;  // G and E: the upper blocks carry them
-  for (int m = 1; m < nmat; ++m) {
+  if (accumulate) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[0][k] += *(const f32x4*)(C + o[k]);
+    if (up) {
+#pragma unroll
+      for (int m = 1; m < NMAT; ++m)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[m][k] += *(const f32x4*)((m == 1 ? G : E) + o[k]);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) *(f32x4*)(C + o[k]) = v[0][k];
+  if (!up) return;
+#pragma unroll
+  for (int m = 1; m < NMAT; ++m) {
     float* X = m == 1 ? G : E;
-    __syncthreads();
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int r = bi * 64 + r_in + 16 * k, c = bj * 64 + c4;
-      const size_t o = (size_t)r * d + c;
-      f32x4 v;
-      if (splits_ge > 1) {
-        v = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int s = 0; s < splits_ge; ++s) v += *(const f32x4*)(part + ((size_t)s * 3 + m) * dd + o);
-        if (accumulate) v += *(const f32x4*)(X + o);
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (r <= c + e) X[o + e] = v[e];
-      } else {
-        v = *(const f32x4*)(X + o);  // final at and above the diagonal
+      for (int e = 0; e < 4; ++e) {
+        if (r <= c + e) X[o[k] + e] = v[m][k][e];
+        T[m - 1][r_in + 16 * k][c4 + e] = v[m][k][e];
       }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) T[r_in + 16 * k][c4 + e] = v[e];
     }
-    __syncthreads();
-    // transposed: X[bj*64 + rr][bi*64 + cc] = T[cc][rr] for the strictly upper source elements
+  }
+  __syncthreads();
+  // transposed: X[bj*64 + rr][bi*64 + cc] = T[cc][rr] for the strictly upper source elements
+#pragma unroll
+  for (int m = 1; m < NMAT; ++m) {
+    float* X = m == 1 ? G : E;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int rr = r_in + 16 * k;  // row of the mirrored block = column of the source
       const int r = bj * 64 + rr;
       const int c = bi * 64 + c4;
       float* x = X + (size_t)r * d + c;
-      const f32x4 v = {T[c4][rr], T[c4 + 1][rr], T[c4 + 2][rr], T[c4 + 3][rr]};
+      const f32x4 w = {T[m - 1][c4][rr], T[m - 1][c4 + 1][rr], T[m - 1][c4 + 2][rr], T[m - 1][c4 + 3][rr]};
       if (c + 3 < r) {
-        *(f32x4*)x = v;
+        *(f32x4*)x = w;
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (c + e < r) x[e] = v[e];
+          if (c + e < r) x[e] = w[e];
       }
     }
   }
@@ -597,8 +643,9 @@ int64_t gram_block_rows(int d) {
 
 // I extent of the C pass's output tile: 256 where d allows it (a wave then owns 128 x 64), else 128.
 // Without E at d <= 2048 the 128 tiles are twice as many, so fewer row splits fill the GPU and the
-// finish adds fewer partials (d = 1536: 222 tiles in 2 splits, 90 -> 84 us per 4680-row chunk; with
-// E the 256 tiles stay ahead, 139 against 159 us).
+// finish adds fewer partials (d = 1536: 222 tiles in 3 splits at three workgroups per CU, 79 us per
+// 4680-row chunk, against 84 in 2 splits and 90 with 256 tiles; with E the 256 tiles stay ahead,
+// 139 against 159 us).
 int gram_ti(int d, bool ev) { return (d % 256 == 0 && (ev || d > 2048)) ? 256 : 128; }
 
 int gram_tiles_c(int d, bool ev) { return (d / gram_ti(d, ev)) * (d / GT); }
@@ -611,10 +658,17 @@ int gram_tiles_ge(int d, int ti) {
 }
 int gram_ti_ge(int d, bool ev) { return (!ev && d % 256 == 0 && d > 2048) ? 256 : 128; }
 
-int gram_splits(int64_t n_rows, int tiles) {
-  // the most splits that still fit one round of two workgroups on each of the 256 CUs, at least 256
-  // rows per split, at most 8
-  int s = tiles >= 512 ? 1 : 512 / tiles;
+#ifndef ISPA_GRAM_SLOTS128
+#define ISPA_GRAM_SLOTS128 768
+#endif
+// Workgroups of one launch resident at once: two per CU, three for the 128-tile kernel without E
+// (136 VGPRs, 48 KB of LDS).
+int gram_slots(int d, bool ev) { return (!ev && gram_ti(d, ev) == 128 && gram_ti_ge(d, ev) == 128) ? ISPA_GRAM_SLOTS128 : 512; }
+
+int gram_splits(int64_t n_rows, int tiles, int slots) {
+  // the most splits that still fit one round of resident workgroups, at least 256 rows per split,
+  // at most 8
+  int s = tiles >= slots ? 1 : slots / tiles;
   const int64_t max_s = std::max<int64_t>(1, n_rows / 256);
   if (s > max_s) s = (int)max_s;
   if (s > 8) s = 8;
@@ -634,8 +688,8 @@ GramWs gram_ws_layout(int64_t n_rows, int d) {
   w.dbytes = ((size_t)rows * d * 2 + 255) & ~(size_t)255;
   w.dsplit = 0;
   const int64_t r1 = std::max<int64_t>(rows, 1);
-  const int s = std::max(gram_splits(r1, gram_tiles_c(d, false) + gram_tiles_ge(d, gram_ti_ge(d, false))),
-                         gram_splits(r1, gram_tiles_c(d, true) + gram_tiles_ge(d, gram_ti_ge(d, true))));
+  const int s = std::max(gram_splits(r1, gram_tiles_c(d, false) + gram_tiles_ge(d, gram_ti_ge(d, false)), gram_slots(d, false)),
+                         gram_splits(r1, gram_tiles_c(d, true) + gram_tiles_ge(d, gram_ti_ge(d, true)), gram_slots(d, true)));
   const size_t part_bytes = s > 1 ? (size_t)s * 3 * (size_t)d * d * sizeof(float) : 0;
   w.parts = 2 * w.dbytes;
   w.total = w.parts + part_bytes;
@@ -679,7 +733,7 @@ ispa_status_t launch_gram(int64_t n_rows, int32_t d, int32_t dtype, const void* 
     const int64_t nr = std::min(block_rows, n_rows - r0);
     const int acc = (r0 > 0) ? 1 : accumulate;
     const int64_t nr1 = std::max<int64_t>(nr, 1);
-    const int splits = gram_splits(nr1, tiles_c + tiles_ge);
+    const int splits = gram_splits(nr1, tiles_c + tiles_ge, gram_slots(d, E != nullptr));
     GramParams p;
     p.A = (const uint16_t*)A_loc + r0 * d;
     p.Dh = (const uint16_t*)((char*)ws + lay.dsplit);
@@ -723,10 +777,15 @@ ispa_status_t launch_gram(int64_t n_rows, int32_t d, int32_t dtype, const void* 
     }
     ispa_status_t st = hip_check(hipGetLastError(), "gram_bf16_kernel launch");
     if (st != ISPA_OK) return st;
-    hipLaunchKernelGGL(gram_finish_kernel, dim3(d / 64, d / 64), dim3(256), 0, s,
-                       (const float*)((char*)ws + lay.parts), splits, splits, E ? 3 : 2, C, G, E, d, acc);
-    st = hip_check(hipGetLastError(), "gram_finish_kernel launch");
-    if (st != ISPA_OK) return st;
+    if (splits > 1) {  // (one split: the passes stored the final C, G and E, both triangles)
+      const float* part = (const float*)((char*)ws + lay.parts);
+      if (E)
+        hipLaunchKernelGGL(gram_finish_kernel<3>, dim3(d / 64, d / 64), dim3(256), 0, s, part, splits, C, G, E, d, acc);
+      else
+        hipLaunchKernelGGL(gram_finish_kernel<2>, dim3(d / 64, d / 64), dim3(256), 0, s, part, splits, C, G, E, d, acc);
+      st = hip_check(hipGetLastError(), "gram_finish_kernel launch");
+      if (st != ISPA_OK) return st;
+    }
     r0 += nr;
   } while (r0 < n_rows);
   return ISPA_OK;

@@ -92,14 +92,19 @@ def test_gram_full_size_and_deterministic():
         assert np.all(excess <= 0), np.unravel_index(np.argmax(excess), excess.shape)
 
 
-@pytest.mark.parametrize("d,qff", [(2048, False), (2048, True), (2304, False), (2304, True)])
-def test_gram_tile_shapes(d, qff):
+@pytest.mark.parametrize("d,qff,n,n_chunks", [(2048, False, 4680, 2), (2048, True, 4680, 2), (2304, False, 4680, 2),
+                                              (2304, True, 4680, 2), (2304, False, 1000, 4), (2304, True, 1000, 4),
+                                              (1536, True, 4680, 2)])
+def test_gram_tile_shapes(d, qff, n, n_chunks):
     """Both sides of the tile choice: without E, d <= 2048 runs on 128-row tiles (more tiles, fewer
-    row splits) and d > 2048 on 256-row ones; with E both run on 256-row C tiles.  Two chunks of
-    2340 rows; every entry of G, C (and E) within the float32-accumulation bound of its float64 sum."""
-    say("d, E", d, qff)
-    al, af = inputs.absorb_rows(6, 0, 4680, d, "bf16")
-    G, C, Q = gpu_gram(list(zip(split_rows(al, 2), split_rows(af, 2))), d, qff=qff)
+    row splits) and d > 2048 on 256-row ones; with E both run on 256-row C tiles.  Chunks of 2340
+    rows are split over workgroups where the tiles cannot fill the GPU (the finish kernel adds the
+    partials and mirrors G and E: d = 2304 without E, d = 1536 with E); chunks of 250 rows and the
+    other shapes are not (the passes store both triangles themselves).  Every entry of G, C (and E)
+    within the float32-accumulation bound of its float64 sum, G and E exactly symmetric."""
+    say("d, E, rows, chunks", d, qff, n, n_chunks)
+    al, af = inputs.absorb_rows(6, 0, n, d, "bf16")
+    G, C, Q = gpu_gram(list(zip(split_rows(al, n_chunks), split_rows(af, n_chunks))), d, qff=qff)
     Gr, Cr = oracle.gram(al.f64, af.f64)
     a_abs, d_abs = np.abs(al.f64), np.abs(af.f64 - al.f64)
     checks = [(host64(G), Gr, a_abs.T @ a_abs), (host64(C), Cr, a_abs.T @ d_abs)]
@@ -111,6 +116,8 @@ def test_gram_tile_shapes(d, qff):
         say("worst |error| / bound", float(np.max(np.abs(got - ref) / (1e-4 * absum + 1e-30))))
         assert np.all(excess <= 0), np.unravel_index(np.argmax(excess), excess.shape)
     assert torch.equal(G, G.T)
+    if qff:
+        assert torch.equal(Q, Q.T)
 
 
 def test_gram_rows_past_one_launch():
