@@ -33,7 +33,7 @@ constexpr int SPB = 64;        // split / transpose block
 #define APPLY3W_RK 32   // K columns per stage of the 256-tile products
 #endif
 #ifndef APPLY3W_NSTG
-#define APPLY3W_NSTG 2
+#define APPLY3W_NSTG 2  // stages in their ring (64 KB each)
 #endif
 #ifndef APPLY3W_MIN_TILES
 #define APPLY3W_MIN_TILES 256
@@ -178,31 +178,33 @@ __global__ __launch_bounds__(256, (NSTG * 4 * PT * RK * 2 <= 80 * 1024) ? 2 : 1)
   const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
   const uint32_t K = (uint32_t)p.K;
   const uint32_t rows_bytes = (uint32_t)PT * K * 2u;
-  const rsrc_t rs[4] = {make_rsrc(p.Ah + b * p.sA + (size_t)m0 * K, rows_bytes),
-                        make_rsrc(p.Al + b * p.sA + (size_t)m0 * K, rows_bytes),
-                        make_rsrc(p.Bh + b * p.sB + (size_t)n0 * K, rows_bytes),
-                        make_rsrc(p.Bl + b * p.sB + (size_t)n0 * K, rows_bytes)};
   const int kb = KM == KM_UA ? m0 : 0;
   const int ke = KM == KM_LA ? min(p.K, m0 + PT) : (KM == KM_LB ? min(p.K, n0 + PT) : p.K);
   const int nst = (ke - kb) / RK;
 
-  // this wave's loads: wave load g = wave + 4 j is rows RPL * (g % (PT / RPL)) .. of operand g / (PT / RPL)
+  const rsrc_t rs[4] = {make_rsrc(p.Ah + b * p.sA + (size_t)m0 * K, rows_bytes),
+                        make_rsrc(p.Al + b * p.sA + (size_t)m0 * K, rows_bytes),
+                        make_rsrc(p.Bh + b * p.sB + (size_t)n0 * K, rows_bytes),
+                        make_rsrc(p.Bl + b * p.sB + (size_t)n0 * K, rows_bytes)};
+  // this wave's loads: wave load g = wave + 4 j is rows RPL * (g % BPO) .. of operand g / BPO =
+  // 4 j / BPO, known at compile time (a resource indexed at run time costs a waterfall loop per load)
+  constexpr int BPO = PT / RPL;  // wave loads per operand and stage
+  static_assert(BPO % 4 == 0, "a wave's loads of one j share an operand");
   uint32_t gofs[WLW];
-  int lop[WLW], ldst[WLW];
+  int ldst[WLW];
 #pragma unroll
   for (int j = 0; j < WLW; ++j) {
     const int g = wave + 4 * j;
-    const int o = g / (PT / RPL), blk = g % (PT / RPL);
+    const int o = 4 * j / BPO, blk = g % BPO;
     const int row = blk * RPL + lane / CPR;
     const int chunk = apply3_slot<RK>(row, lane % CPR);  // the data chunk that lands in slot lane % CPR
     gofs[j] = (uint32_t)row * K * 2u + (uint32_t)chunk * 16u;
-    lop[j] = o;
     ldst[j] = o * OPS + blk * 512;
   }
   auto load_stage = [&](int st, __bf16* bb) {
     const uint32_t kofs = (uint32_t)(kb + st * RK) * 2u;
 #pragma unroll
-    for (int j = 0; j < WLW; ++j) load_to_lds(rs[lop[j]], (uint16_t*)(bb + ldst[j]), gofs[j] + kofs);
+    for (int j = 0; j < WLW; ++j) load_to_lds(rs[4 * j / BPO], (uint16_t*)(bb + ldst[j]), gofs[j] + kofs);
   };
   // fragment of rows r0 + l32, columns 16 ks + 8 hh .. + 7 of operand o in a stage
   auto frag = [&](const __bf16* bb, int o, int r0, int ks) {
@@ -236,27 +238,32 @@ __global__ __launch_bounds__(256, (NSTG * 4 * PT * RK * 2 <= 80 * 1024) ? 2 : 1)
         }
     }
   };
-  // ring: stage st in buffer st % NSTG (buffers chosen at compile time); before the barrier that ends
-  // stage st each wave waits until stage st + 1 has landed, leaving the NSTG - 2 newer stages in flight
+  // Ring: stage st in buffer st % NSTG (buffers chosen at compile time).  Step st loads stage
+  // st + NSTG - 1 and multiplies stage st, NSTG - 1 stages in flight.  At the top of step st each wave
+  // waits for its own loads of stage st (all but the NSTG - 2 newer stages': vmcnt counts this wave's
+  // loads, which complete in order); the barrier then makes every wave's loads visible and frees the
+  // buffer stage st - 1 was read from.  A plain barrier, not __syncthreads(), whose fence would wait
+  // for the newer stages too.  Every step issues its loads, also past the last stage: they read
+  // columns past ke of the tile's own rows (or zeros past its end) into buffers that are not
+  // multiplied, and the wait after the loop drains them.
   constexpr int KEEP = (NSTG - 2) * WLW;
-  constexpr int WAIT_KEEP = 0xF70 | (KEEP & 15) | ((KEEP >> 4) << 14);  // vmcnt(KEEP)
-  const int nstR = (nst + NSTG - 1) / NSTG * NSTG;  // padding stages load past ke: zeros or unused columns
+  constexpr int WAIT_CUR = 0xF70 | (KEEP & 15) | ((KEEP >> 4) << 14);  // vmcnt(KEEP)
+  const int nstR = (nst + NSTG - 1) / NSTG * NSTG;
 #pragma unroll
-  for (int k = 0; k + 1 < NSTG; ++k)
-    if (k < nst) load_stage(k, buf[k]);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  for (int k = 0; k + 1 < NSTG; ++k) load_stage(k, buf[k]);
   for (int st = 0; st < nstR; st += NSTG) {
 #pragma unroll
-    for (int k = 0; k < NSTG; ++k) {
-      const int cur = st + k, nxt = cur + NSTG - 1;
-      if (nxt < nst) load_stage(nxt, buf[(k + NSTG - 1) % NSTG]);
-      if (cur < nst) compute(buf[k]);
-      if (nxt < nst) __builtin_amdgcn_s_waitcnt(WAIT_KEEP);
-      else __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
+    for (int u = 0; u < NSTG; ++u) {
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(WAIT_CUR);
+      __builtin_amdgcn_s_barrier();
+      load_stage(st + u + NSTG - 1, buf[(u + NSTG - 1) % NSTG]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (st + u < nst) compute(buf[u]);
     }
   }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();  // every wave's products are done before the epilogue reuses the ring
   // acc[i][j][v]: row m0 + wm + 32 i + 8 (v / 4) + 4 hh + v % 4, column n0 + wn + 32 j + l32
   if constexpr (OUT_SPLIT) {
     // through LDS (the ring is free after the last barrier): each wave parks half of its 64 x 64
@@ -342,30 +349,33 @@ __global__ __launch_bounds__(512) void apply3w_kernel(Apply3Params p) {
   const int wm = (wave >> 2) * 128, wn = (wave & 3) * 64;
   const uint32_t K = (uint32_t)p.K;
   const uint32_t rows_bytes = (uint32_t)PTW * K * 2u;
-  const rsrc_t rs[4] = {make_rsrc(p.Ah + b * p.sA + (size_t)m0 * K, rows_bytes),
-                        make_rsrc(p.Al + b * p.sA + (size_t)m0 * K, rows_bytes),
-                        make_rsrc(p.Bh + b * p.sB + (size_t)n0 * K, rows_bytes),
-                        make_rsrc(p.Bl + b * p.sB + (size_t)n0 * K, rows_bytes)};
   const int kb = KM == KM_UA ? m0 : 0;
   const int ke = KM == KM_LA ? min(p.K, m0 + PTW) : (KM == KM_LB ? min(p.K, n0 + PTW) : p.K);
   const int nst = (ke - kb) / RK;
 
+  const rsrc_t rs[4] = {make_rsrc(p.Ah + b * p.sA + (size_t)m0 * K, rows_bytes),
+                        make_rsrc(p.Al + b * p.sA + (size_t)m0 * K, rows_bytes),
+                        make_rsrc(p.Bh + b * p.sB + (size_t)n0 * K, rows_bytes),
+                        make_rsrc(p.Bl + b * p.sB + (size_t)n0 * K, rows_bytes)};
+  // wave load g = wave + 8 j: operand g / BPO = 8 j / BPO, known at compile time (a resource indexed
+  // at run time costs a waterfall loop per load)
+  constexpr int BPO = PTW / RPL;  // wave loads per operand and stage
+  static_assert(BPO % 8 == 0, "a wave's loads of one j share an operand");
   uint32_t gofs[WLW];
-  int lop[WLW], ldst[WLW];
+  int ldst[WLW];
 #pragma unroll
   for (int j = 0; j < WLW; ++j) {
     const int g = wave + 8 * j;
-    const int o = g / (PTW / RPL), blk = g % (PTW / RPL);
+    const int o = 8 * j / BPO, blk = g % BPO;
     const int row = blk * RPL + lane / CPR;
     const int chunk = apply3_slot<RK>(row, lane % CPR);
     gofs[j] = (uint32_t)row * K * 2u + (uint32_t)chunk * 16u;
-    lop[j] = o;
     ldst[j] = o * OPS + blk * 512;
   }
   auto load_stage = [&](int st, __bf16* bb) {
     const uint32_t kofs = (uint32_t)(kb + st * RK) * 2u;
 #pragma unroll
-    for (int j = 0; j < WLW; ++j) load_to_lds(rs[lop[j]], (uint16_t*)(bb + ldst[j]), gofs[j] + kofs);
+    for (int j = 0; j < WLW; ++j) load_to_lds(rs[8 * j / BPO], (uint16_t*)(bb + ldst[j]), gofs[j] + kofs);
   };
   auto frag = [&](const __bf16* bb, int o, int r0, int ks) {
     const int row = r0 + l32;
@@ -405,33 +415,41 @@ __global__ __launch_bounds__(512) void apply3w_kernel(Apply3Params p) {
         for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bh[j], acc[i][j], 0, 0, 0);
     }
   };
+  // Ring: stage st in buffer st % NSTG.  Step st loads stage st + NSTG - 1 and multiplies stage st,
+  // NSTG - 1 stages in flight.  At the top of step st each wave waits for its own loads of stage st
+  // (all but the NSTG - 2 newer stages': vmcnt counts this wave's loads, which complete in order);
+  // the barrier then makes every wave's loads visible and frees the buffer stage st - 1 was read
+  // from.  A plain barrier, not __syncthreads(), whose fence would wait for the newer stages too.
+  // Every step issues its loads, also past the last stage: they read columns past ke of the tile's
+  // own rows (or zeros past its end) into buffers that are not multiplied, and the wait after the
+  // loop drains them.
   constexpr int KEEP = (NSTG - 2) * WLW;
-  constexpr int WAIT_KEEP = 0xF70 | (KEEP & 15) | ((KEEP >> 4) << 14);  // vmcnt(KEEP)
+  constexpr int WAIT_CUR = 0xF70 | (KEEP & 15) | ((KEEP >> 4) << 14);  // vmcnt(KEEP)
   const int nstR = (nst + NSTG - 1) / NSTG * NSTG;
 #pragma unroll
-  for (int k = 0; k + 1 < NSTG; ++k)
-    if (k < nst) load_stage(k, buf[k]);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  for (int k = 0; k + 1 < NSTG; ++k) load_stage(k, buf[k]);
   for (int st = 0; st < nstR; st += NSTG) {
 #pragma unroll
-    for (int k = 0; k < NSTG; ++k) {
-      const int cur = st + k, nxt = cur + NSTG - 1;
-      if (nxt < nst) load_stage(nxt, buf[(k + NSTG - 1) % NSTG]);
-      if (cur < nst) compute(buf[k]);
-      if (nxt < nst) __builtin_amdgcn_s_waitcnt(WAIT_KEEP);
-      else __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
+    for (int u = 0; u < NSTG; ++u) {
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(WAIT_CUR);
+      __builtin_amdgcn_s_barrier();
+      load_stage(st + u + NSTG - 1, buf[(u + NSTG - 1) % NSTG]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (st + u < nst) compute(buf[u]);
     }
   }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();  // every wave's products are done before the epilogue reuses the ring
   // acc[i][j][v]: row m0 + wm + 32 i + 8 (v / 4) + 4 hh + v % 4, column n0 + wn + 32 j + l32
   if constexpr (OUT_SPLIT) {
-    // through LDS (free after the last barrier): each wave parks one 32 x 64 float32 row of tiles at a
-    // time (8.5 KB; waves 0-6 in the first buffer, wave 7 in the second), then every lane splits 8
-    // consecutive elements of a row and stores 16 bytes of hi and of lo
+    // through LDS: each wave parks one 32 x 64 float32 row of tiles at a time (8.5 KB; WPB waves per
+    // ring buffer), then every lane splits 8 consecutive elements of a row and stores 16 bytes of hi
+    // and of lo
     constexpr int TS = 64 + 4;
-    static_assert(7 * 32 * TS * 4 <= SS * 2 && 32 * TS * 4 <= SS * 2, "parked rows fit the buffers");
-    float* T = wave < 7 ? (float*)&S0[0] + wave * 32 * TS : (float*)&S1[0];
+    constexpr int WPB = SS * 2 / (32 * TS * 4);
+    static_assert(WPB * (NSTG < 3 ? NSTG : 3) >= 8, "parked rows fit the first three buffers");
+    float* T = (float*)(wave < WPB ? S0 : (wave < 2 * WPB ? S1 : S2)) + (wave % WPB) * 32 * TS;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -600,16 +618,19 @@ __global__ __launch_bounds__(256, 1) void prod6_kernel(Prod6Params p) {
   const int tn = p.N / PT, tmn = (p.M / PT) * tn;
   const int ntiles = tmn * p.batch;
 
+  // wave load g = wave + 4 j: plane g / BPO = 4 j / BPO, known at compile time (a resource indexed
+  // at run time costs a waterfall loop per load)
+  constexpr int NW = 4, BPO = PT / RPL;
+  static_assert(BPO % NW == 0, "a wave's loads of one j share a plane");
   uint32_t gofs[WLW];
-  int lop[WLW], ldst[WLW];
+  int ldst[WLW];
 #pragma unroll
   for (int j = 0; j < WLW; ++j) {
-    const int g = wave + 4 * j;
-    const int o = g / (PT / RPL), blk = g % (PT / RPL);
+    const int g = wave + NW * j;
+    const int o = NW * j / BPO, blk = g % BPO;
     const int row = blk * RPL + lane / CPR;
     const int chunk = apply3_slot<RK>(row, lane % CPR);
     gofs[j] = (uint32_t)row * K * 2u + (uint32_t)chunk * 16u;
-    lop[j] = o;
     ldst[j] = o * OPS + blk * 512;
   }
   auto frag = [&](const __bf16* bb, int o, int r0, int ks) {
@@ -631,7 +652,7 @@ __global__ __launch_bounds__(256, 1) void prod6_kernel(Prod6Params p) {
     auto load_stage = [&](int st, __bf16* bb) {
       const uint32_t kofs = (uint32_t)(st * RK) * 2u;
 #pragma unroll
-      for (int j = 0; j < WLW; ++j) load_to_lds(rs[lop[j]], (uint16_t*)(bb + ldst[j]), gofs[j] + kofs);
+      for (int j = 0; j < WLW; ++j) load_to_lds(rs[NW * j / BPO], (uint16_t*)(bb + ldst[j]), gofs[j] + kofs);
     };
     f32x16 acc[2][2];
     double acc64[2][2][16];
@@ -745,16 +766,19 @@ __global__ __launch_bounds__(512) void prod6w_kernel(Prod6Params p) {
   const int tn = p.N / PTW, tmn = (p.M / PTW) * tn;
   const int ntiles = tmn * p.batch;
 
+  // wave load g = wave + 8 j: plane g / BPO = 8 j / BPO, known at compile time (a resource indexed
+  // at run time costs a waterfall loop per load)
+  constexpr int NW = 8, BPO = PTW / RPL;
+  static_assert(BPO % NW == 0, "a wave's loads of one j share a plane");
   uint32_t gofs[WLW];
-  int lop[WLW], ldst[WLW];
+  int ldst[WLW];
 #pragma unroll
   for (int j = 0; j < WLW; ++j) {
-    const int g = wave + 8 * j;
-    const int o = g / (PTW / RPL), blk = g % (PTW / RPL);
+    const int g = wave + NW * j;
+    const int o = NW * j / BPO, blk = g % BPO;
     const int row = blk * RPL + lane / CPR;
     const int chunk = apply3_slot<RK>(row, lane % CPR);
     gofs[j] = (uint32_t)row * K * 2u + (uint32_t)chunk * 16u;
-    lop[j] = o;
     ldst[j] = o * OPS + blk * 512;
   }
   auto frag = [&](const __bf16* bb, int o, int r0, int ks) {
@@ -776,7 +800,7 @@ __global__ __launch_bounds__(512) void prod6w_kernel(Prod6Params p) {
     auto load_stage = [&](int st, __bf16* bb) {
       const uint32_t kofs = (uint32_t)(st * RK) * 2u;
 #pragma unroll
-      for (int j = 0; j < WLW; ++j) load_to_lds(rs[lop[j]], (uint16_t*)(bb + ldst[j]), gofs[j] + kofs);
+      for (int j = 0; j < WLW; ++j) load_to_lds(rs[NW * j / BPO], (uint16_t*)(bb + ldst[j]), gofs[j] + kofs);
     };
     f32x16 acc[4][2];
 #pragma unroll
@@ -805,26 +829,29 @@ __global__ __launch_bounds__(512) void prod6w_kernel(Prod6Params p) {
               acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[TA[q]][i], bq[TB[q]][j], acc[i][j], 0, 0, 0);
       }
     };
+    // Ring as in apply3w_kernel: step st loads stage st + NSTG - 1 and multiplies stage st; each wave
+    // waits for its own loads of stage st only, then a plain barrier (a __syncthreads() fence would
+    // wait for the newer stages too).  Loads past the last stage read columns of the tile's own rows
+    // (or zeros past its end) into buffers that are not multiplied.  The previous tile's closing
+    // barrier ended every read of the ring.
     constexpr int KEEP = (NSTG - 2) * WLW;
-    constexpr int WAIT_KEEP = 0xF70 | (KEEP & 15) | ((KEEP >> 4) << 14);  // vmcnt(KEEP)
+    constexpr int WAIT_CUR = 0xF70 | (KEEP & 15) | ((KEEP >> 4) << 14);  // vmcnt(KEEP)
     const int nstR = (nst + NSTG - 1) / NSTG * NSTG;
-    // the previous tile's last barrier ended every read of the ring
 #pragma unroll
-    for (int k = 0; k + 1 < NSTG; ++k)
-      if (k < nst) load_stage(k, buf[k]);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    for (int k = 0; k + 1 < NSTG; ++k) load_stage(k, buf[k]);
     for (int st = 0; st < nstR; st += NSTG) {
 #pragma unroll
-      for (int k = 0; k < NSTG; ++k) {
-        const int cur = st + k, nxt = cur + NSTG - 1;
-        if (nxt < nst) load_stage(nxt, buf[(k + NSTG - 1) % NSTG]);
-        if (cur < nst) compute(buf[k]);
-        if (nxt < nst) __builtin_amdgcn_s_waitcnt(WAIT_KEEP);
-        else __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+      for (int u = 0; u < NSTG; ++u) {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(WAIT_CUR);
+        __builtin_amdgcn_s_barrier();
+        load_stage(st + u + NSTG - 1, buf[(u + NSTG - 1) % NSTG]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (st + u < nst) compute(buf[u]);
       }
     }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // every wave is done with the ring before the next tile's loads
     // acc[i][j][v]: row m0 + wm + 32 i + 8 (v / 4) + 4 hh + v % 4, column n0 + wn + 32 j + l32
     float* D = p.D + b * p.sD;
 #pragma unroll

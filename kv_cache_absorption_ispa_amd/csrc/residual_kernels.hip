@@ -31,7 +31,7 @@ namespace {
 constexpr int OZ_S = ISPA_OZ_DIGITS;  // 7-bit digits per value
 constexpr int OZ_T = 128;   // output tile: 8 waves of 32 x 64 (two per SIMD)
 constexpr int OZ_K = 32;    // K per stage: one v_mfma_i32_32x32x32_i8 step
-constexpr int OZ_NSTG = 3;  // stages in the LDS ring (48 KB each)
+constexpr int OZ_NSTG = 3;  // stages in the LDS ring (40 KB each)
 typedef int v4i_t __attribute__((ext_vector_type(4)));
 typedef int v16i_t __attribute__((ext_vector_type(16)));
 
@@ -258,28 +258,32 @@ __global__ __launch_bounds__(512) void oz_gemm_kernel(OzParams p) {
           acc[s + t][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[s], x, acc[s + t][i], 0, 0, 0);
       }
   };
-  // ring: stage st in buffer st % OZ_NSTG; before the barrier that ends stage st each wave waits
-  // until stage st + 1 has landed, leaving the newer stage in flight
-  constexpr int KEEP = (OZ_NSTG - 2) * WLW;
-  constexpr int WAIT_KEEP = 0xF70 | (KEEP & 15) | ((KEEP >> 4) << 14);  // vmcnt(KEEP)
+  // Ring of three stages, stage st in buffer st % 3: step st loads stage st + 2 and multiplies
+  // stage st, two stages in flight.  At the top of step st each wave waits for its own loads of
+  // stage st (all but stage st + 1's: vmcnt counts this wave's loads, which complete in order); the
+  // barrier then makes every wave's loads visible and frees the buffer stage st - 1 was read from.
+  // A plain barrier, not __syncthreads(), whose fence would wait for stage st + 1's loads as well.
+  // Every step issues its loads, also the (at most four) past the last stage: they read bytes of
+  // the tile's own rows (or zeros past its end) into buffers that are not multiplied, and the wait
+  // after the loop drains them.
+  static_assert(OZ_NSTG == 3, "three-stage ring");
+  constexpr int WAIT_CUR = 0xF70 | (WLW & 15) | ((WLW >> 4) << 14);  // vmcnt(WLW)
   const int nst = p.d / OZ_K;
-  const int nstR = (nst + OZ_NSTG - 1) / OZ_NSTG * OZ_NSTG;
+  const int nstR = (nst + 2) / 3 * 3;
 #pragma unroll
-  for (int k = 0; k + 1 < OZ_NSTG; ++k)
-    if (k < nst) load_stage(k, buf[k]);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int st = 0; st < nstR; st += OZ_NSTG) {
+  for (int k = 0; k < 2; ++k) load_stage(k, buf[k]);
+  for (int st = 0; st < nstR; st += 3) {
 #pragma unroll
-    for (int k = 0; k < OZ_NSTG; ++k) {
-      const int cur = st + k, nxt = cur + OZ_NSTG - 1;
-      if (nxt < nst) load_stage(nxt, buf[(k + OZ_NSTG - 1) % OZ_NSTG]);
-      if (cur < nst) compute(buf[k]);
-      if (nxt < nst) __builtin_amdgcn_s_waitcnt(WAIT_KEEP);
-      else __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
+    for (int u = 0; u < 3; ++u) {
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(WAIT_CUR);
+      __builtin_amdgcn_s_barrier();
+      load_stage(st + u + 2, buf[(u + 2) % 3]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (st + u < nst) compute(buf[u]);
     }
   }
+  __builtin_amdgcn_s_waitcnt(0);
   // acc[c][i][v]: row m0 + wi + 8 (v / 4) + 4 hh + v % 4, column n0 + wj + 32 i + l32
   const double gb = p.gamma_b ? p.gamma * (double)p.gamma_b[b] : p.gamma;
 #pragma unroll
