@@ -72,6 +72,9 @@ constexpr int NB = 64;  // panel width
 #ifndef ISPA_CHOL_PANEL
 #define ISPA_CHOL_PANEL 512
 #endif
+#ifndef ISPA_CHOL_DEFER
+#define ISPA_CHOL_DEFER 1  // defer the panel updates right of the next panel into its steps' launches
+#endif
 constexpr int CP = ISPA_CHOL_PANEL;
 static_assert(CP % 64 == 0, "panel of whole blocks");
 constexpr int SB = NB / 4;     // block column width
@@ -261,6 +264,14 @@ struct GemmParams {
   float* diag_Linv;
   int32_t* diag_info;
   int diag_d, diag_k0;
+  // deferred trailing-update tiles carried by a fused look-ahead launch (one layer only): the
+  // workgroups in grid rows past M / T take lower tiles ex_t0 .. ex_t0 + ex_n - 1 (row-major over
+  // the lower triangle of an ex_nt x ex_nt grid of T x T tiles) of ex_D -= ex_A ex_A^T with depth
+  // ex_K, row stride ex_ld for both.  Slots whose dispatch index is a multiple of 8 (the XCD of
+  // tile (0, 0), whose workgroup then runs the latency-bound factorisation) stay empty.
+  const float* ex_A;
+  float* ex_D;
+  int ex_ld, ex_K, ex_t0, ex_n;
 };
 
 // D = alpha * op(A) op(B) + beta * Cin; op(A) is MxK, op(B) is KxN.
@@ -287,17 +298,15 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
   const int wm = (wave >> 1) * (T / 2), wn = (wave & 1) * (T / 2);
-  const float* A = p.A + b * p.sA + q * p.pA;
-  const float* B = p.B + b * p.sB + q * p.pB;
-  auto run_tile = [&](const int tm, const int tn) {
+  // one output tile: D = alpha * op(A) op(B) + beta * Cin over k in [kb, ke)
+  auto run_tile = [&](const float* A, const float* B, int lda, int ldb, const float* Cin, int ldc, float* D, int ldd,
+                      const int tm, const int tn, const int kb, const int ke) {
   const int m0 = tm * T, n0 = tn * T;
   f32x16 acc[WB][WB];
 #pragma unroll
   for (int i = 0; i < WB; ++i)
 #pragma unroll
     for (int j = 0; j < WB; ++j) acc[i][j] = f32x16{0};
-  const int kb = p.kmode == 2 ? m0 : (p.kmode == 3 ? n0 : 0);
-  const int ke = p.kmode == 1 ? min(p.K, m0 + T) : p.K;
   f32x4 ra[NLD], rb[NLD];
   auto load = [&](int k0) {
 #pragma unroll
@@ -305,17 +314,17 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
       const int t = tid + 256 * r;
       if (!TA) {
         const int m = t / (GKS / 4), kq = t % (GKS / 4);
-        ra[r] = *(const f32x4*)(A + (size_t)(m0 + m) * p.lda + k0 + 4 * kq);
+        ra[r] = *(const f32x4*)(A + (size_t)(m0 + m) * lda + k0 + 4 * kq);
       } else {
         const int k = t / (T / 4), mq = t % (T / 4);
-        ra[r] = *(const f32x4*)(A + (size_t)(k0 + k) * p.lda + m0 + 4 * mq);
+        ra[r] = *(const f32x4*)(A + (size_t)(k0 + k) * lda + m0 + 4 * mq);
       }
       if (TB) {
         const int n = t / (GKS / 4), kq = t % (GKS / 4);
-        rb[r] = *(const f32x4*)(B + (size_t)(n0 + n) * p.ldb + k0 + 4 * kq);
+        rb[r] = *(const f32x4*)(B + (size_t)(n0 + n) * ldb + k0 + 4 * kq);
       } else {
         const int k = t / (T / 4), nq = t % (T / 4);
-        rb[r] = *(const f32x4*)(B + (size_t)(k0 + k) * p.ldb + n0 + 4 * nq);
+        rb[r] = *(const f32x4*)(B + (size_t)(k0 + k) * ldb + n0 + 4 * nq);
       }
     }
   };
@@ -380,8 +389,6 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
     __syncthreads();
     buf ^= 1;
   }
-  const float* Cin = p.Cin ? p.Cin + b * p.sC + q * p.pC : nullptr;
-  float* D = p.D + b * p.sD + q * p.pD;
 #pragma unroll
   for (int i = 0; i < WB; ++i)
 #pragma unroll
@@ -391,20 +398,45 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
         const int r = m0 + wm + 32 * i + 8 * (v >> 2) + 4 * hh + (v & 3);
         const int c = n0 + wn + 32 * j + l32;
         float x = p.alpha * acc[i][j][v];
-        if (Cin && p.beta != 0.f) x = fmaf(p.beta, Cin[(size_t)r * p.ldc + c], x);
-        D[(size_t)r * p.ldd + c] = x;
+        if (Cin && p.beta != 0.f) x = fmaf(p.beta, Cin[(size_t)r * ldc + c], x);
+        D[(size_t)r * ldd + c] = x;
       }
   };
+  const float* A = p.A + b * p.sA + q * p.pA;
+  const float* B = p.B + b * p.sB + q * p.pB;
+  const float* Cin = p.Cin ? p.Cin + b * p.sC + q * p.pC : nullptr;
+  float* D = p.D + b * p.sD + q * p.pD;
+  auto kbeg = [&](int tm, int tn) { return p.kmode == 2 ? tm * T : (p.kmode == 3 ? tn * T : 0); };
+  auto kend = [&](int tm) { return p.kmode == 1 ? min(p.K, tm * T + T) : p.K; };
   if constexpr (PERSIST) {
     // (every slab ends with a barrier, so the LDS is free when the next tile starts)
     const int tiles_n = p.N / T, tiles = (p.M / T) * tiles_n;
-    for (int t = (int)xcd_remap(blockIdx.x, gridDim.x); t < tiles; t += gridDim.x) run_tile(t / tiles_n, t % tiles_n);
+    for (int t = (int)xcd_remap(blockIdx.x, gridDim.x); t < tiles; t += gridDim.x) {
+      const int tm = t / tiles_n, tn = t % tiles_n;
+      run_tile(A, B, p.lda, p.ldb, Cin, p.ldc, D, p.ldd, tm, tn, kbeg(tm, tn), kend(tm));
+    }
     return;
+  }
+  if constexpr (DIAG) {
+    if (p.ex_n > 0 && (int)blockIdx.y >= p.M / T) {
+      // a deferred tile (kmode 0, one layer): skip the slots on the XCD of tile (0, 0)
+      const int lin = (int)(blockIdx.y * gridDim.x + blockIdx.x), prim = (p.M / T) * (int)gridDim.x;
+      if (lin % 8 == 0) return;
+      const int ti = (lin - prim) - ((lin + 7) / 8 - (prim + 7) / 8);
+      if (ti >= p.ex_n) return;
+      const int t = p.ex_t0 + ti;
+      int r = (int)((sqrtf(8.f * (float)t + 1.f) - 1.f) * 0.5f);  // row of the lower-triangle tile t
+      while (r > 0 && r * (r + 1) / 2 > t) --r;
+      while ((r + 1) * (r + 2) / 2 <= t) ++r;
+      const int c = t - r * (r + 1) / 2;
+      run_tile(p.ex_A, p.ex_A, p.ex_ld, p.ex_ld, p.ex_D, p.ex_ld, p.ex_D, p.ex_ld, r, c, 0, p.ex_K);
+      return;
+    }
   }
   // with op(A) lower the last row tiles carry the most K work: dispatch them first
   const int tm = p.kmode == 1 ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y, tn = blockIdx.x;
   if (p.lower_only && tm < tn) return;
-  run_tile(tm, tn);
+  run_tile(A, B, p.lda, p.ldb, Cin, p.ldc, D, p.ldd, tm, tn, kbeg(tm, tn), kend(tm));
   if constexpr (DIAG) {
     if (tm == 0 && tn == 0 && q == 0) {
       // the tile just written holds the next diagonal block: make the stores visible to this
@@ -711,13 +743,21 @@ __global__ __launch_bounds__(256) void trace_lambda_kernel(int d, const float* G
   if (threadIdx.x == 0) lam[b] = (float)((double)scale * red[0] / d);
 }
 
+// Lower 64 x 64 tiles t0 .. t0 + n - 1 of D -= A A^T (A: rows of the tiles, depth K, row stride ld for
+// A and D; tiles row-major over the lower triangle), handed to a fused look-ahead launch.
+struct DeferredTiles {
+  const float* A;
+  float* D;
+  int ld, K, t0, n;
+};
+
 template <bool TA, bool TB>
 ispa_status_t gemm(hipStream_t s, int batch, int M, int N, int K, const float* A, int lda, size_t sA, const float* B,
                    int ldb, size_t sB, const float* Cin, int ldc, size_t sC, float* D, int ldd, size_t sD, float alpha,
                    float beta, bool lower_only, const int32_t* info, int kmode = 0, int npairs = 1,
                    size_t pA = 0, size_t pB = 0, size_t pC = 0, size_t pD = 0, float* diag_M = nullptr,
                    float* diag_Linv = nullptr, int32_t* diag_info = nullptr, int diag_d = 0, int diag_k0 = 0,
-                   int max_wg = 0) {
+                   int max_wg = 0, const DeferredTiles* ex = nullptr) {
   if (M <= 0 || N <= 0 || K <= 0) return ISPA_OK;
   if (K % GKS != 0) {
     set_error("internal: GEMM depth not a multiple of 32");
@@ -736,6 +776,8 @@ ispa_status_t gemm(hipStream_t s, int batch, int M, int N, int K, const float* A
   p.pA = pA; p.pB = pB; p.pC = pC; p.pD = pD;
   p.diag_M = diag_M; p.diag_Linv = diag_Linv; p.diag_info = diag_info;
   p.diag_d = diag_d; p.diag_k0 = diag_k0;
+  p.ex_A = nullptr; p.ex_D = nullptr;
+  p.ex_ld = 0; p.ex_K = 0; p.ex_t0 = 0; p.ex_n = 0;
   // large products use 128x128 tiles (half the operand traffic per FLOP) when they still fill the GPU
   const int z = batch * npairs;
   const bool big = M % 128 == 0 && N % 128 == 0 && (size_t)(M / 128) * (N / 128) * z >= 192;
@@ -744,6 +786,22 @@ ispa_status_t gemm(hipStream_t s, int batch, int M, int N, int K, const float* A
       if (npairs != 1) {
         set_error("internal: fused diagonal factorisation with paired products");
         return ISPA_E_INVALID_ARG;
+      }
+      if (ex != nullptr && ex->n > 0) {
+        if (batch != 1 || kmode != 0 || ex->K % GKS != 0 || M % 64 != 0 || N % 64 != 0) {
+          set_error("internal: deferred tiles on an unsupported launch");
+          return ISPA_E_INVALID_ARG;
+        }
+        p.ex_A = ex->A; p.ex_D = ex->D;
+        p.ex_ld = ex->ld; p.ex_K = ex->K; p.ex_t0 = ex->t0; p.ex_n = ex->n;
+        // slots after the primary grid, the multiples of 8 left empty, until n remain
+        const int nx = N / 64, prim = (M / 64) * nx;
+        int slots = 0;
+        for (int got = 0; got < ex->n; ++slots)
+          if ((prim + slots) % 8 != 0) ++got;
+        const int ey = (slots + nx - 1) / nx;
+        hipLaunchKernelGGL((gemm_f32_kernel<TA, TB, 64, true>), dim3(nx, M / 64 + ey, 1), dim3(256), 0, s, p);
+        return hip_check(hipGetLastError(), "gemm_f32_kernel launch");
       }
       if (big)
         hipLaunchKernelGGL((gemm_f32_kernel<TA, TB, 128, true>), dim3(N / 128, M / 128, z), dim3(256), 0, s, p);
@@ -988,6 +1046,15 @@ ispa_status_t launch_absorb(int32_t d, int32_t d_out, int32_t batch, const float
   // on another stream costs ~15 us of latency here.)
   hipLaunchKernelGGL(potrf_diag_kernel, dim3(batch), dim3(256), 0, s, M, d, 0, Linvf, info);
   ISPA_TRY(hip_check(hipGetLastError(), "potrf_diag_kernel launch"));
+  // Deferred panel updates (one layer, wide trailing matrices): the last step of a CP-column panel
+  // updates only the next panel's columns with all CP columns (K = CP) on the chain; the lower
+  // tiles right of the next panel go to the fused launches of the next panel's steps, in equal
+  // shares, where they fill compute units that otherwise idle while one workgroup factors the next
+  // diagonal block.  They touch only columns the next panel's steps neither read nor write, and
+  // the next panel's own last step (which updates some of the same entries) follows them in
+  // stream order.
+  DeferredTiles pend{};
+  int pend_left = 0;
   for (int k = 0; k + 1 < nblk; ++k) {
     if (k == fork_k) {
       ISPA_TRY(fork_cw());
@@ -1008,12 +1075,38 @@ ispa_status_t launch_absorb(int32_t d, int32_t d_out, int32_t batch, const float
     float* trail = M + (size_t)(k0 + NB) * d + k0 + NB;
     const int p0 = k0 / CP * CP, pe = std::min(d, p0 + CP);
     if (k0 + NB < pe) {
+      DeferredTiles part{};
+      if (pend_left > 0) {  // this step's share of the deferred tiles (the panel's last narrow step takes the rest)
+        const int steps = (pe - k0 - NB) / NB;
+        part = pend;
+        part.t0 = pend.n - pend_left;
+        part.n = (pend_left + steps - 1) / steps;
+        pend_left -= part.n;
+      }
       ISPA_TRY((gemm<false, true>(s, batch, rest, pe - k0 - NB, NB, panel, d, dd, panel, d, dd, trail, d, dd, trail, d,
-                                  dd, -1.f, 1.f, true, info, 0, 1, 0, 0, 0, 0, M, Linvf, info, d, k0 + NB)));
+                                  dd, -1.f, 1.f, true, info, 0, 1, 0, 0, 0, 0, M, Linvf, info, d, k0 + NB, 0, &part)));
     } else {
+      if (pend_left != 0) {
+        set_error("internal: deferred trailing update not consumed");
+        return ISPA_E_INVALID_ARG;
+      }
       const float* pan = M + (size_t)pe * d + p0;  // rows pe.., columns p0 .. pe of L
-      ISPA_TRY((gemm<false, true>(s, batch, rest, rest, pe - p0, pan, d, dd, pan, d, dd, trail, d, dd, trail, d, dd,
-                                  -1.f, 1.f, true, info, 0, 1, 0, 0, 0, 0, M, Linvf, info, d, k0 + NB)));
+      const int far = d - pe - CP;                 // columns right of the next panel
+      if (ISPA_CHOL_DEFER && batch == 1 && far >= 1024) {
+        ISPA_TRY((gemm<false, true>(s, batch, rest, CP, pe - p0, pan, d, dd, pan, d, dd, trail, d, dd, trail, d, dd,
+                                    -1.f, 1.f, true, info, 0, 1, 0, 0, 0, 0, M, Linvf, info, d, k0 + NB)));
+        const int nt = far / 64;
+        pend.A = pan + (size_t)CP * d;
+        pend.D = M + (size_t)(pe + CP) * d + pe + CP;
+        pend.ld = d;
+        pend.K = pe - p0;
+        pend.t0 = 0;
+        pend.n = nt * (nt + 1) / 2;
+        pend_left = pend.n;
+      } else {
+        ISPA_TRY((gemm<false, true>(s, batch, rest, rest, pe - p0, pan, d, dd, pan, d, dd, trail, d, dd, trail, d, dd,
+                                    -1.f, 1.f, true, info, 0, 1, 0, 0, 0, 0, M, Linvf, info, d, k0 + NB)));
+      }
     }
     // block k + 1 is factored: once it is block inv_p - 1, the leading range of L^-1 can be formed
     // beside the rest of the factorisation (on the side stream, after R = C W, which uses Tb)

@@ -333,6 +333,36 @@ def test_batched_solve_with_a_failing_layer(d, bad_col):
         assert torch.equal(Wn[i], W[i] + dW[i])
 
 
+@pytest.mark.parametrize("bad_col", [1030, 1600, 2100])
+def test_one_layer_failing_in_deferred_columns(bad_col):
+    """One layer at d = 2560: the panel updates right of the next 512-column panel are deferred into
+    the next panel's launches (columns 1024.. after panel 0, 1536.. after panel 1).  A zero column of
+    A_loc with lambda = 0 makes the pivot at bad_col exactly zero whichever launch subtracts the
+    earlier panels from it, so info names it, dW is NaN and W_new untouched; the same layer without
+    the zero column matches the oracle."""
+    d = 2560
+    al, af = inputs.absorb_rows(13, 0, 4 * d, d, "f32")
+    W = inputs.normal(13, 0, inputs.LAYER_CHUNK, inputs.T_W, (d, d)) * np.float32(d ** -0.5)
+    raw = al.raw.copy()
+    raw[:, bad_col] = 0
+    Gr, Cr = oracle.gram(raw.astype(np.float64), af.f64)
+    Wt = torch.from_numpy(W).cuda()
+    Wn = Wt.clone()
+    dW, info = gpu_solve(torch.from_numpy(Gr.astype(np.float32)).cuda(), torch.from_numpy(Cr.astype(np.float32)).cuda(),
+                         Wt, 0.0, W_new=Wn)
+    assert info.item() == bad_col + 1
+    assert torch.all(torch.isnan(dW)).item()
+    assert torch.equal(Wn, Wt)
+    Gr, Cr = oracle.gram(al.f64, af.f64)
+    G32, C32 = Gr.astype(np.float32), Cr.astype(np.float32)
+    dW, info = gpu_solve(torch.from_numpy(G32).cuda(), torch.from_numpy(C32).cuda(), Wt, 1e-2)
+    assert info.item() == 0
+    ref = oracle.ridge_solve(G32.astype(np.float64), C32.astype(np.float64), W.astype(np.float64), 1e-2)
+    e = relfro(host64(dW), ref)
+    say("dW relfro", e)
+    assert e <= TOL_DW
+
+
 @pytest.mark.parametrize("d,batch", [(384, 1), (1536, 4), (2048, 2), (1536, 8)])
 def test_refinement_reaches_the_float64_solve(d, batch):
     """W is a column permutation scaled by powers of two, so R = C W is exact in float32 and the only
