@@ -75,6 +75,9 @@ constexpr int NB = 64;  // panel width
 #ifndef ISPA_CHOL_DEFER
 #define ISPA_CHOL_DEFER 1  // defer the panel updates right of the next panel into its steps' launches
 #endif
+#ifndef ISPA_CHOL_DEFER_MIN
+#define ISPA_CHOL_DEFER_MIN 1024  // fewest columns right of the next panel for which that pays
+#endif
 constexpr int CP = ISPA_CHOL_PANEL;
 static_assert(CP % 64 == 0, "panel of whole blocks");
 constexpr int SB = NB / 4;     // block column width
@@ -1092,7 +1095,7 @@ ispa_status_t launch_absorb(int32_t d, int32_t d_out, int32_t batch, const float
       }
       const float* pan = M + (size_t)pe * d + p0;  // rows pe.., columns p0 .. pe of L
       const int far = d - pe - CP;                 // columns right of the next panel
-      if (ISPA_CHOL_DEFER && batch == 1 && far >= 1024) {
+      if (ISPA_CHOL_DEFER && batch == 1 && far >= ISPA_CHOL_DEFER_MIN) {
         ISPA_TRY((gemm<false, true>(s, batch, rest, CP, pe - p0, pan, d, dd, pan, d, dd, trail, d, dd, trail, d, dd,
                                     -1.f, 1.f, true, info, 0, 1, 0, 0, 0, 0, M, Linvf, info, d, k0 + NB)));
         const int nt = far / 64;
