@@ -75,6 +75,9 @@ constexpr int NB = 64;  // panel width
 #ifndef ISPA_CHOL_DEFER
 #define ISPA_CHOL_DEFER 1  // defer the panel updates right of the next panel into its steps' launches
 #endif
+#ifndef ISPA_PAIR_WORKGROUPS
+#define ISPA_PAIR_WORKGROUPS 0  // workgroups the inverse's last-pair product may hold beside the chain (0: all)
+#endif
 #ifndef ISPA_CHOL_DEFER_MIN
 #define ISPA_CHOL_DEFER_MIN 1024  // fewest columns right of the next panel for which that pays
 #endif
@@ -887,16 +890,20 @@ ispa_status_t chol_apply(hipStream_t s, int batch, int d, int d_out, const float
 // One level of the explicit inverse's recursive doubling for np adjacent pairs of block ranges (A of
 // sa blocks, then C of sc blocks), the first A starting at block a: inv([A 0; B C]) has off-diagonal
 // block -C^-1 (B A^-1).  T (one pair's nC x nA after another, layer stride sT) holds B A^-1.
+// part: 0 both products, 1 only T = B A^-1, 2 only the second product (T already formed); at most
+// max_wg workgroups per layer take the first product's tiles (0: no bound).
 ispa_status_t invert_pairs(hipStream_t s, int batch, int d, const float* L, float* Linvf, float* T, size_t sT,
-                           const int32_t* info, int a, int sa, int sc, int np) {
+                           const int32_t* info, int a, int sa, int sc, int np, int part = 0, int max_wg = 0) {
   const size_t dd = (size_t)d * d;
   const int nA = sa * NB, nC = sc * NB;
   const size_t a0 = (size_t)a * NB;
   const size_t pstep = (size_t)(nA + nC) * (d + 1);  // from one pair's corner to the next
   // T = B A^-1, with B = L[a0+nA : a0+nA+nC, a0 : a0+nA] and A^-1 lower triangular
-  ISPA_TRY((gemm<false, false>(s, batch, nC, nA, nA, L + (a0 + nA) * d + a0, d, dd, Linvf + a0 * d + a0, d, dd,
-                               nullptr, 0, 0, T, nA, sT, 1.f, 0.f, false, info, KM_LOWER_B, np, pstep, pstep, 0,
-                               (size_t)nC * nA)));
+  if (part != 2)
+    ISPA_TRY((gemm<false, false>(s, batch, nC, nA, nA, L + (a0 + nA) * d + a0, d, dd, Linvf + a0 * d + a0, d, dd,
+                                 nullptr, 0, 0, T, nA, sT, 1.f, 0.f, false, info, KM_LOWER_B, np, pstep, pstep, 0,
+                                 (size_t)nC * nA, nullptr, nullptr, nullptr, 0, 0, np == 1 ? max_wg : 0)));
+  if (part == 1) return ISPA_OK;
   // off-diagonal block of the inverse: -C^-1 T, with C^-1 lower triangular
   return gemm<false, false>(s, batch, nC, nA, nC, Linvf + (a0 + nA) * (d + 1), d, dd, T, nA, sT, nullptr, 0, 0,
                             Linvf + (a0 + nA) * d + a0, d, dd, -1.f, 0.f, false, info, KM_LOWER_A, np, pstep,
@@ -1037,7 +1044,7 @@ ispa_status_t launch_absorb(int32_t d, int32_t d_out, int32_t batch, const float
   };
   const bool inv_q_in_zb =
       invert_range(s, batch, d, M, Linvf, Zb, dn, info, inv_p, inv_q, false, &inv_st) <= dn;
-  bool inv_lead_forked = false;
+  bool inv_lead_forked = false, pair_left_forked = false;
   if (fork_k < 0) {
     ISPA_TRY(fork_cw());
     forked = true;
@@ -1070,6 +1077,15 @@ ispa_status_t launch_absorb(int32_t d, int32_t d_out, int32_t batch, const float
     // L_ik = M_ik L_kk^-T (in place)
     ISPA_TRY((gemm<false, true>(s, batch, rest, NB, NB, panel, d, dd, Lkk_inv, d, dd, nullptr, 0, 0, panel, d, dd,
                                 1.f, 0.f, false, info)));
+    // the leading block columns of L are final: with the leading range of L^-1 on the side stream, the
+    // last pair's first product T = B A^-1 follows it there (into Tb; the trailing range is in Zb)
+    if (k + 1 == inv_p && inv_lead_forked && inv_q_in_zb) {
+      ISPA_TRY(hip_check(hipEventRecord(side->ev_fork, s), "hipEventRecord (fork, last pair)"));
+      ISPA_TRY(hip_check(hipStreamWaitEvent(side->stream, side->ev_fork, 0), "hipStreamWaitEvent (fork, last pair)"));
+      ISPA_TRY(invert_pairs(side->stream, batch, d, M, Linvf, Tb, dd, info, 0, inv_p, inv_q, 1, 1,
+                            ISPA_PAIR_WORKGROUPS));
+      pair_left_forked = true;
+    }
     // trailing update, lower tiles; tile (0, 0) is diagonal block k + 1, factored in the same launch.
     // Blocks are grouped in panels of CP columns: inside a panel a step updates only the panel's
     // remaining columns (a narrow launch on the chain); the panel's last step updates everything to
@@ -1128,7 +1144,7 @@ ispa_status_t launch_absorb(int32_t d, int32_t d_out, int32_t batch, const float
   if (!inv_lead_forked) ISPA_TRY(inv_lead(s));
   if (inv_q > 0 && !inv_q_in_zb)
     ISPA_TRY((invert_range(s, batch, d, M, Linvf, Tb, dd, info, inv_p, inv_q, true, &inv_st), inv_st));
-  if (inv_q > 0) ISPA_TRY(invert_pairs(s, batch, d, M, Linvf, Tb, dd, info, 0, inv_p, inv_q, 1));
+  if (inv_q > 0) ISPA_TRY(invert_pairs(s, batch, d, M, Linvf, Tb, dd, info, 0, inv_p, inv_q, 1, pair_left_forked ? 2 : 0));
   // X = (L L^T)^-1 R.  With the refinement, both solves run on the bf16 matrix cores as three-term
   // products (about 2^-16 relative per product); the accurate residual then corrects
   // the first solve's error and the correction's error is that much smaller again.  L (M) and the
