@@ -180,7 +180,7 @@ def test_gram_and_solve_when_the_streams_nearly_agree(d, n, scale):
     assert e <= TOL_DW
 
 
-@pytest.mark.parametrize("d,d_out", [(128, 128), (256, 192), (1536, 1536), (2048, 1024), (2560, 640)])
+@pytest.mark.parametrize("d,d_out", [(128, 128), (256, 192), (1536, 1536), (2048, 1024), (2304, 256), (2560, 640)])
 def test_solve_parity_on_oracle_statistics(d, d_out):
     """ispa_absorb_solve alone: G, C are the oracle's (rounded to float32), dW vs the float64 solve."""
     al, af = inputs.absorb_rows(7, 0, max(4 * d, 512), d, "f32")
