@@ -78,6 +78,9 @@ constexpr int NB = 64;  // panel width
 #ifndef ISPA_PAIR_WORKGROUPS
 #define ISPA_PAIR_WORKGROUPS 0  // workgroups the inverse's last-pair product may hold beside the chain (0: all)
 #endif
+#ifndef ISPA_DEFER_SKIP_XCD
+#define ISPA_DEFER_SKIP_XCD 1  // deferred tiles leave the XCD of the factoring workgroup alone
+#endif
 #ifndef ISPA_CHOL_DEFER_MIN
 #define ISPA_CHOL_DEFER_MIN 1024  // fewest columns right of the next panel for which that pays
 #endif
@@ -427,8 +430,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
     if (p.ex_n > 0 && (int)blockIdx.y >= p.M / T) {
       // a deferred tile (kmode 0, one layer): skip the slots on the XCD of tile (0, 0)
       const int lin = (int)(blockIdx.y * gridDim.x + blockIdx.x), prim = (p.M / T) * (int)gridDim.x;
-      if (lin % 8 == 0) return;
-      const int ti = (lin - prim) - ((lin + 7) / 8 - (prim + 7) / 8);
+      if (ISPA_DEFER_SKIP_XCD && lin % 8 == 0) return;
+      const int ti = (lin - prim) - (ISPA_DEFER_SKIP_XCD ? (lin + 7) / 8 - (prim + 7) / 8 : 0);
       if (ti >= p.ex_n) return;
       const int t = p.ex_t0 + ti;
       int r = (int)((sqrtf(8.f * (float)t + 1.f) - 1.f) * 0.5f);  // row of the lower-triangle tile t
@@ -804,7 +807,7 @@ ispa_status_t gemm(hipStream_t s, int batch, int M, int N, int K, const float* A
         const int nx = N / 64, prim = (M / 64) * nx;
         int slots = 0;
         for (int got = 0; got < ex->n; ++slots)
-          if ((prim + slots) % 8 != 0) ++got;
+          if (!ISPA_DEFER_SKIP_XCD || (prim + slots) % 8 != 0) ++got;
         const int ey = (slots + nx - 1) / nx;
         hipLaunchKernelGGL((gemm_f32_kernel<TA, TB, 64, true>), dim3(nx, M / 64 + ey, 1), dim3(256), 0, s, p);
         return hip_check(hipGetLastError(), "gemm_f32_kernel launch");
