@@ -333,6 +333,36 @@ def test_batched_solve_with_a_failing_layer(d, bad_col):
         assert torch.equal(Wn[i], W[i] + dW[i])
 
 
+@pytest.mark.parametrize("d,d_out", [(2560, 640), (3072, 1024)])
+def test_deferred_panel_updates_give_the_batched_bits(d, d_out):
+    """A single layer defers each 512-column panel's updates right of the next panel into the next
+    panel's launches (at least 1024 columns right of it); a batch of layers updates everything to the
+    right of a panel in one launch.  Every entry takes the same products in the same order either
+    way, so the layer alone and the same layer twice in a batch give dW bit for bit alike, within the
+    dW gate of the float64 solve."""
+    al, af = inputs.absorb_rows(14, 0, 4 * d, d, "f32")
+    Gr, Cr = oracle.gram(al.f64, af.f64)
+    G32, C32 = Gr.astype(np.float32), Cr.astype(np.float32)
+    W = inputs.normal(14, 0, inputs.LAYER_CHUNK, inputs.T_W, (d, d_out)) * np.float32(d ** -0.5)
+    G1, C1, W1 = (torch.from_numpy(x).cuda() for x in (G32, C32, W))
+    side = ispa.SideStream()
+    dW1 = poisoned((d, d_out), torch.float32)
+    info1 = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+    ispa.ispa_absorb_solve_ex(G1, C1, W1, 1e-2, dW1, info1, workspace=nan_workspace(
+        ispa.ispa_absorb_workspace_size(d, d_out, 1)), side=side)
+    dW2 = poisoned((2, d, d_out), torch.float32)
+    info2 = torch.full((2,), -7, dtype=torch.int32, device="cuda")
+    ispa.ispa_absorb_solve_ex(torch.stack([G1, G1]), torch.stack([C1, C1]), torch.stack([W1, W1]), 1e-2, dW2, info2,
+                              workspace=nan_workspace(ispa.ispa_absorb_workspace_size(d, d_out, 2)), side=side)
+    torch.cuda.synchronize()
+    assert info1.item() == 0 and torch.all(info2 == 0).item()
+    assert torch.equal(dW2[0], dW1) and torch.equal(dW2[1], dW1)
+    ref = oracle.ridge_solve(G32.astype(np.float64), C32.astype(np.float64), W.astype(np.float64), 1e-2)
+    e = relfro(host64(dW1), ref)
+    say("dW relfro", e)
+    assert e <= TOL_DW
+
+
 @pytest.mark.parametrize("bad_col", [1030, 1600, 2100])
 def test_one_layer_failing_in_deferred_columns(bad_col):
     """One layer at d = 2560: the panel updates right of the next 512-column panel are deferred into
