@@ -100,16 +100,25 @@ constexpr int DIAG_LS_FLOATS = NB * LSTR, DIAG_TS_FLOATS = 32 * 36 + 4;
 
 // Body of the factorisation for layer b; called by all 256 threads of a workgroup, which must not
 // be inside a branch that differs between its waves.  Ls and Xs hold NB * LSTR floats each, Ts
-// DIAG_TS_FLOATS, all 16-byte aligned.
+// DIAG_TS_FLOATS, all 16-byte aligned.  With from_ls the block is read from Ls (written there by
+// the caller before a barrier) instead of from M.
 __device__ __forceinline__ void potrf_diag_block(float* M, int d, int k0, float* Linvf, int32_t* info, int b,
-                                                 float (*Ls)[LSTR], float (*Xs)[LSTR], float (*Ts)[36]) {
+                                                 float (*Ls)[LSTR], float (*Xs)[LSTR], float (*Ts)[36],
+                                                 bool from_ls = false) {
   int& fail_s = *(int*)&Ts[32][0];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   float* Mb = M + (size_t)b * d * d + (size_t)k0 * d + k0;
 
   float a[SB];  // row `lane`, columns SB*wave .. SB*wave+15
-  {
+  if (from_ls) {
+#pragma unroll
+    for (int q = 0; q < SB / 4; ++q) {
+      const f32x4 v = *(const f32x4*)(&Ls[lane][SB * wave + 4 * q]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[4 * q + e] = v[e];
+    }  // (Ls is next written after the barrier below)
+  } else {
     const float* src = Mb + (size_t)lane * d + SB * wave;
 #pragma unroll
     for (int q = 0; q < SB / 4; ++q) {
@@ -308,8 +317,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
   const int l32 = lane & 31, hh = lane >> 5;
   const int wm = (wave >> 1) * (T / 2), wn = (wave & 1) * (T / 2);
   // one output tile: D = alpha * op(A) op(B) + beta * Cin over k in [kb, ke)
+  // With ldsd the tile's leading NB x NB block goes to ldsd (row stride LSTR) instead of D.
   auto run_tile = [&](const float* A, const float* B, int lda, int ldb, const float* Cin, int ldc, float* D, int ldd,
-                      const int tm, const int tn, const int kb, const int ke) {
+                      const int tm, const int tn, const int kb, const int ke, float* ldsd) {
   const int m0 = tm * T, n0 = tn * T;
   f32x16 acc[WB][WB];
 #pragma unroll
@@ -408,7 +418,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
         const int c = n0 + wn + 32 * j + l32;
         float x = p.alpha * acc[i][j][v];
         if (Cin && p.beta != 0.f) x = fmaf(p.beta, Cin[(size_t)r * ldc + c], x);
-        D[(size_t)r * ldd + c] = x;
+        if (ldsd != nullptr && wm + 32 * i < NB && wn + 32 * j < NB)
+          ldsd[(r - m0) * LSTR + (c - n0)] = x;
+        else
+          D[(size_t)r * ldd + c] = x;
       }
   };
   const float* A = p.A + b * p.sA + q * p.pA;
@@ -422,7 +435,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
     const int tiles_n = p.N / T, tiles = (p.M / T) * tiles_n;
     for (int t = (int)xcd_remap(blockIdx.x, gridDim.x); t < tiles; t += gridDim.x) {
       const int tm = t / tiles_n, tn = t % tiles_n;
-      run_tile(A, B, p.lda, p.ldb, Cin, p.ldc, D, p.ldd, tm, tn, kbeg(tm, tn), kend(tm));
+      run_tile(A, B, p.lda, p.ldb, Cin, p.ldc, D, p.ldd, tm, tn, kbeg(tm, tn), kend(tm), nullptr);
     }
     return;
   }
@@ -438,24 +451,26 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
       while (r > 0 && r * (r + 1) / 2 > t) --r;
       while ((r + 1) * (r + 2) / 2 <= t) ++r;
       const int c = t - r * (r + 1) / 2;
-      run_tile(p.ex_A, p.ex_A, p.ex_ld, p.ex_ld, p.ex_D, p.ex_ld, p.ex_D, p.ex_ld, r, c, 0, p.ex_K);
+      run_tile(p.ex_A, p.ex_A, p.ex_ld, p.ex_ld, p.ex_D, p.ex_ld, p.ex_D, p.ex_ld, r, c, 0, p.ex_K, nullptr);
       return;
     }
   }
   // with op(A) lower the last row tiles carry the most K work: dispatch them first
   const int tm = p.kmode == 1 ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y, tn = blockIdx.x;
   if (p.lower_only && tm < tn) return;
-  run_tile(A, B, p.lda, p.ldb, Cin, p.ldc, D, p.ldd, tm, tn, kbeg(tm, tn), kend(tm));
+  // the workgroup of tile (0, 0) of a fused look-ahead launch keeps the next diagonal block (the
+  // tile's leading 64 x 64) in the LDS the multiply no longer needs and factors it from there; its
+  // updated values never go to M, whose block the factorisation overwrites with L (its strict upper
+  // part keeps the values from before this update: nothing reads it)
+  const bool diag_tile = DIAG && tm == 0 && tn == 0 && q == 0;
+  run_tile(A, B, p.lda, p.ldb, Cin, p.ldc, D, p.ldd, tm, tn, kbeg(tm, tn), kend(tm),
+           diag_tile ? &As[0][0][0] : nullptr);
   if constexpr (DIAG) {
-    if (tm == 0 && tn == 0 && q == 0) {
-      // the tile just written holds the next diagonal block: make the stores visible to this
-      // workgroup's loads (the fence also drops stale L1 lines of the tile), then factor it in the
-      // LDS the multiply no longer needs
+    if (diag_tile) {
       __shared__ __attribute__((aligned(16))) float Tx[DIAG_TS_FLOATS / 36 + 1][36];
-      __threadfence();
       __syncthreads();
       potrf_diag_block(p.diag_M, p.diag_d, p.diag_k0, p.diag_Linv, p.diag_info, b, (float(*)[LSTR]) & As[0][0][0],
-                       (float(*)[LSTR]) & Bs[0][0][0], Tx);
+                       (float(*)[LSTR]) & Bs[0][0][0], Tx, true);
     }
   }
 }
