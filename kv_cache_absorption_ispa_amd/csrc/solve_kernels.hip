@@ -43,8 +43,8 @@ namespace {
 
 constexpr int NB = 64;  // panel width
 
-// Cholesky of the NB x NB diagonal block at (k0, k0) of each layer (lower L written in place, the
-// strict upper part of the block left as it is) and its inverse L^-1 into the same block of Linvf
+// Cholesky of the NB x NB diagonal block at (k0, k0) of each layer (lower L written in place, zeros
+// above its diagonal) and its inverse L^-1 into the same block of Linvf
 // (zeros above the diagonal).  info[b] = k0 + j + 1 if the leading minor of order k0 + j + 1 of
 // G + lambda I is not positive definite (LAPACK potrf convention); then nothing is written.
 //
@@ -245,11 +245,9 @@ __device__ __forceinline__ void potrf_diag_block(float* M, int d, int k0, float*
   for (int e = tid; e < NB * NB / 4; e += 256) {
     const int rr = e / (NB / 4), cc = 4 * (e % (NB / 4));
     *(f32x4*)(Xb + (size_t)rr * d + cc) = *(const f32x4*)(&Xs[rr][cc]);
-    if (cc + 3 <= rr) {
-      *(f32x4*)(Mb + (size_t)rr * d + cc) = *(const f32x4*)(&Ls[rr][cc]);
-    } else if (cc <= rr) {
-      for (int q = 0; q <= rr - cc; ++q) Mb[(size_t)rr * d + cc + q] = Ls[rr][cc + q];
-    }
+    // whole rows of L, with the zeros above its diagonal: the strict upper part of a diagonal
+    // block of M is never read
+    *(f32x4*)(Mb + (size_t)rr * d + cc) = *(const f32x4*)(&Ls[rr][cc]);
   }
 }
 
@@ -460,8 +458,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
   if (p.lower_only && tm < tn) return;
   // the workgroup of tile (0, 0) of a fused look-ahead launch keeps the next diagonal block (the
   // tile's leading 64 x 64) in the LDS the multiply no longer needs and factors it from there; its
-  // updated values never go to M, whose block the factorisation overwrites with L (its strict upper
-  // part keeps the values from before this update: nothing reads it)
+  // updated values never go to M, whose block the factorisation overwrites with L
   const bool diag_tile = DIAG && tm == 0 && tn == 0 && q == 0;
   run_tile(A, B, p.lda, p.ldb, Cin, p.ldc, D, p.ldd, tm, tn, kbeg(tm, tn), kend(tm),
            diag_tile ? &As[0][0][0] : nullptr);
